@@ -1,0 +1,253 @@
+"""Benchmark of the DCKV prompt-KV-cache codec on one MI355X.
+
+One step is the whole hot path over one synthetic request: encode of the
+32,768-token prompt (kept-row copy, embedding mean, analysis GEMM with the
+quantiser and the checkerboard passes, escapes, rANS, packing) followed by
+its decode (parse, rANS, mean GEMM with the two dequantisation passes,
+correction MLP, synthesis with RoPE, kept rows).  Inputs are resident in HBM
+before the timed region.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "coded tokens/s (encode, decode) + bf16-KV GB/s at 32K tokens; bytes/token"
+KV_BYTES_PER_TOKEN = 12288
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_work(name: str, N: int, Ca: int, rans_bytes: int):
+    """(bound, algorithmic units per launch, unit) of each timed kernel."""
+    if name == "analysis_gemm":
+        return "mfma", 2.0 * N * Ca * 6144, "flop"
+    if name == "mean_gemm":
+        return "mfma", 2.0 * N * Ca * 2048, "flop"
+    if name == "dequant_gemm":
+        return "mfma", 2.0 * N * 2048 * 2048, "flop"
+    if name == "w1_gemm":
+        return "mfma", 2.0 * N * 256 * 2048, "flop"
+    if name == "synthesis_gemm":
+        return "mfma", 2.0 * N * 6144 * (2048 + 256), "flop"
+    if name in ("rans_encode", "rans_decode"):
+        return "hbm", float(N * Ca + rans_bytes), "byte"
+    return None, 0.0, None
+
+
+def source_sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def cpu_baseline(req_cfg: int, n_rows: int):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    from oracle import codec as ocodec, plan as oplan
+    import dckv_synth as synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i["num_threads"] for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    w = synth.world()
+    req = synth.make_request(req_cfg, n_rows=n_rows)
+    params = w.params()
+    p = oplan.make_plan(np.float32(req.step_scale), w.base_step, w.laplace_scale)
+    t0 = time.perf_counter()
+    enc = ocodec.encode(req.rows, req.token_ids, params, p)
+    t1 = time.perf_counter()
+    ocodec.decode(enc.data, req.token_ids, params, p)
+    t2 = time.perf_counter()
+    return {"value": enc.N / (t2 - t0), "unit": "coded tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": "first %d positions of the 32K workload as one %d-token prompt (%d coded), same seeds "
+                      "and step scale; encode %.2f s + decode %.2f s, numpy float64" % (
+                          n_rows, n_rows, enc.N, t1 - t0, t2 - t1),
+            "encode_tokens_per_s": enc.N / (t1 - t0), "decode_tokens_per_s": enc.N / (t2 - t1)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload index (2 = 32K-token prompt)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=8192)
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import dckv_synth as synth
+    import learned_kv_cache_dckv_amd as dk
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.world()
+    req = synth.make_request(args.config)
+    codec = dk.Codec(w.params(), device=dev)
+    t0 = time.perf_counter()
+    plan = codec.plan(req.step_scale)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    T = req.T
+    rows = torch.from_numpy(req.rows.view(np.int16)).to(dev)
+    tok = torch.from_numpy(req.token_ids.astype(np.int32)).to(dev)
+    max_bytes, ws_bytes = plan.bytes(T)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    buf = torch.empty(max_bytes, dtype=torch.uint8, device=dev)
+    nb = torch.zeros(1, dtype=torch.int64, device=dev)
+    st_e = torch.zeros(1, dtype=torch.int32, device=dev)
+    st_d = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = torch.empty((T, codec.D), dtype=torch.int16, device=dev)
+
+    # first pass: stream size (decode needs the host-side byte count)
+    dk.dckv_encode(plan, rows, tok, buf, nb, st_e, ws)
+    torch.cuda.synchronize()
+    n_bytes = int(nb.item())
+    if int(st_e.item()) != 0 or n_bytes == 0:
+        print("encode failed with status %d" % int(st_e.item()), file=sys.stderr)
+        return 1
+
+    def step():
+        dk.dckv_encode(plan, rows, tok, buf, nb, st_e, ws)
+        dk.dckv_decode(plan, buf, n_bytes, tok, out, st_d, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    dk.dckv_profile_reset()
+    dk.dckv_profile_enable(True)
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(args.steps):
+        step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    dk.dckv_profile_enable(False)
+    kern = {}
+    for name in ("mean_gemm", "analysis_gemm", "fixup", "rans_encode", "scan", "pack", "parse", "rans_decode",
+                 "dequant_gemm", "w1_gemm", "synthesis_gemm"):
+        tot, n = dk.dckv_profile_read(name)
+        if n:
+            kern[name] = {"avg_ms": tot / n, "launches": n}
+    assert int(st_e.item()) == 0 and int(st_d.item()) == 0 and int(nb.item()) == n_bytes
+
+    # encode-only and decode-only rates (profiling off)
+    def timed(fn, k):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        for _ in range(k):
+            fn()
+        b.record(s)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / k
+
+    enc_ms = timed(lambda: dk.dckv_encode(plan, rows, tok, buf, nb, st_e, ws), args.steps)
+    dec_ms = timed(lambda: dk.dckv_decode(plan, buf, n_bytes, tok, out, st_d, ws), args.steps)
+
+    # stream statistics (host side, after timing)
+    data = buf[:n_bytes].cpu().numpy()
+    hdr = data[:64].view(np.uint32)
+    N, Ca, n_groups, n_esc = int(hdr[5]), int(hdr[7]), int(hdr[8]), int(hdr[9])
+    rans_bytes = int(data[56:64].view(np.uint64)[0])
+    kept_bytes = (T - N) * KV_BYTES_PER_TOKEN
+    coded_bytes = n_bytes - 64 - kept_bytes
+    sym = torch.empty(N * Ca, dtype=torch.uint8, device=dev)
+    ne = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    dk.dckv_entropy_decode(plan, buf, n_bytes, T, sym, ne, st, ws)
+    torch.cuda.synchronize()
+    symh = sym.cpu().numpy().reshape(N, Ca)
+    freq = dk.dckv_plan_info(plan)["freq"].astype(np.float64)
+    ok = symh != 255
+    rank = np.broadcast_to(np.arange(Ca)[None, :], symh.shape)
+    modelled_bits = float(np.sum(15.0 - np.log2(freq[rank[ok], symh[ok]])) + 64.0 * n_esc)
+
+    # roofline of the dominant kernel
+    dom = max(kern, key=lambda k: kern[k]["avg_ms"] * kern[k]["launches"])
+    bound, units, unit = kernel_work(dom, N, Ca, rans_bytes)
+    avg_s = kern[dom]["avg_ms"] * 1e-3
+    if unit == "flop":
+        achieved = units / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS}
+    else:
+        achieved = units / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBPS}
+    roof["kernel"] = dom
+    roof["traffic"] = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        ent = tr.get(dom)
+        src = os.path.join(ROOT, "learned_kv_cache_dckv_amd", "csrc", ent["source"]) if ent else None
+        if ent and os.path.exists(src) and source_sha(src) == ent["source_sha"] and ent.get("T") == T:
+            roof["traffic"] = ent["bytes_per_launch"]
+    for k, v in kern.items():
+        b, u, un = kernel_work(k, N, Ca, rans_bytes)
+        if un == "flop":
+            v["tflops"] = u / (v["avg_ms"] * 1e-3) / 1e12
+            v["mfma_frac"] = v["tflops"] / PEAK_BF16_TFLOPS
+        elif un == "byte":
+            v["GBps"] = u / (v["avg_ms"] * 1e-3) / 1e9
+            v["hbm_frac"] = v["GBps"] / PEAK_HBM_GBPS
+
+    res = {
+        "metric": METRIC,
+        "value": N / (ms_step * 1e-3),
+        "unit": "coded tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": req.note, "T": T, "coded_tokens": N, "rate_target_bytes_per_token": req.rate_target,
+                   "step_scale": req.step_scale, "C_a": Ca, "groups": n_groups},
+        "encode_tokens_per_s": N / (enc_ms * 1e-3),
+        "decode_tokens_per_s": N / (dec_ms * 1e-3),
+        "encode_kv_GBps": N * KV_BYTES_PER_TOKEN / (enc_ms * 1e-3) / 1e9,
+        "decode_kv_GBps": N * KV_BYTES_PER_TOKEN / (dec_ms * 1e-3) / 1e9,
+        "encode_ms": enc_ms,
+        "decode_ms": dec_ms,
+        "bytes_per_token": coded_bytes / N,
+        "total_bytes": n_bytes,
+        "ratio_vs_bf16": KV_BYTES_PER_TOKEN / (coded_bytes / N),
+        "stored_over_modelled": coded_bytes * 8.0 / modelled_bits if modelled_bits else None,
+        "n_esc": n_esc,
+        "plan_ms": plan_ms,
+        "workspace_bytes": ws_bytes,
+        "roofline": roof,
+        "kernels": kern,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample_rows)
+    print(json.dumps(res))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,238 @@
+/*
+ * dckv.h - C ABI of the DCKV prompt-KV-cache codec for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The codec follows the DCKV digest page ("DCKV: Learned Transform Coding of
+ * the Prompt KV Cache in Hybrid Language Models", trove.briskstack.com),
+ * section "How it works":
+ *   - each coded token's pre-RoPE keys and values of the full-attention
+ *     layers form one row of D = n_layers * 2 * n_kv_heads * head_dim bf16
+ *     values (6,144 for the paper's model); the first keep_head and the last
+ *     keep_tail positions stay in bf16 (first paragraph);
+ *   - one shared basis projects a row to n_coef = 2,048 coefficients; the
+ *     synthesis side adds one hidden layer of 256 GELU units (Transform);
+ *   - per-component quantisation steps; components whose Laplace scale is
+ *     below 0.05 steps are dropped (Transform);
+ *   - codes are rANS-coded under Laplace distributions; codes beyond +-127
+ *     are escaped at 64 bits each (Coding);
+ *   - even positions take their code means from the token's input embedding,
+ *     odd positions also from both decoded neighbours, so decoding takes two
+ *     parallel passes at any length; token ids are side information, not
+ *     stored (Conditional entropy models);
+ *   - RoPE is reapplied to the keys after decoding (first paragraph).
+ *
+ * Conventions
+ *   - bf16 values are passed as their uint16 bit patterns.
+ *   - Pointers are HIP device pointers unless marked (host).
+ *   - hip_stream is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Every function returns DCKV_OK or a negative dckv_status.  Argument and
+ *     size errors are returned synchronously and nothing is enqueued.  Errors
+ *     that only the device can see are written to the call's device status
+ *     word.  dckv_last_error() gives a message for the last failing call on
+ *     the calling thread.
+ *   - The library never allocates device memory on the encode/decode path:
+ *     the caller passes a workspace of the size dckv_bytes() reports.
+ *   - Only the shapes of the paper's codec are supported by the GPU kernels:
+ *     n_layers = 6, n_kv_heads = 2, head_dim = 256 (D = 6144), n_coef = 2048,
+ *     n_hidden = 256, emb_dim = 2048.  vocab, keep_head, keep_tail and
+ *     rope_theta are free.
+ */
+#ifndef DCKV_H
+#define DCKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dckv_plan_s dckv_plan_t; /* opaque; immutable after dckv_plan() */
+
+typedef enum {
+  DCKV_OK = 0,
+  DCKV_EINVAL = -1,      /* bad argument, or a non-finite coefficient at encode */
+  DCKV_ENOMEM = -2,      /* plan could not allocate its device tables */
+  DCKV_ECAPACITY = -3,   /* stream capacity or workspace too small */
+  DCKV_ECORRUPT = -4,    /* malformed stream, or a rANS group failed its end-state check */
+  DCKV_EPLAN = -5,       /* stream was written under another plan (CRC / C_a mismatch) */
+  DCKV_EHIP = -6,        /* a HIP runtime call failed */
+  DCKV_EUNSUPPORTED = -7 /* shape or size outside what the kernels support */
+} dckv_status;
+
+/* Codec parameters.  Matrices are bf16 row-major device arrays owned by the
+ * caller; they must stay alive and unchanged while any plan made from them
+ * exists.  The three vectors are read on the host during dckv_plan(). */
+typedef struct {
+  int32_t n_layers, n_kv_heads, head_dim;   /* 6, 2, 256 -> D = 6144 */
+  int32_t n_coef, n_hidden, emb_dim, vocab; /* 2048, 256, 2048, any >= 1 */
+  int32_t keep_head, keep_tail;             /* positions kept in bf16: 4, 128 */
+  float rope_theta;                         /* RoPE base, e.g. 1e7 */
+  const uint16_t *analysis;   /* A  [n_coef][D]          y = A x          */
+  const uint16_t *synthesis;  /* S  [D][n_coef]          xhat = S yhat_b + W2 h_b */
+  const uint16_t *w1;         /* W1 [n_hidden][n_coef]   h = GELU(W1 yhat_b) */
+  const uint16_t *w2;         /* W2 [D][n_hidden]        */
+  const uint16_t *embedding;  /* E  [vocab][emb_dim]     the LM's input embedding */
+  const uint16_t *mean_head;  /* H  [n_coef][emb_dim]    mean = H E[tok]  */
+  const float *nbr_weight;    /* (host) a_c [n_coef]: odd mean += a_c (yhat_{j-1,c} + yhat_{j+1,c}) */
+  const float *laplace_scale; /* (host) b_c [n_coef] > 0, Laplace scale of component c */
+  const float *base_step;     /* (host) delta_c [n_coef] > 0, trained quantisation step */
+} dckv_params;
+
+/* ---------------------------------------------------------------------------
+ * Plan: the rate setting.  (DCKV digest, "How it works", Transform and Coding;
+ * "What it claims": one trained codec per rate.)
+ *
+ * step_c = fp32(step_scale * delta_c); s_c = b_c / step_c (float64); component
+ * c is active iff s_c >= 0.05; active components are ranked by ascending c.
+ * For each active component the integer table over the codes -127..127 is the
+ * zero-mean discretised Laplace of scale s_c restricted to +-127 and
+ * renormalised, with 15-bit precision: f_k = 1 + floor(p_k / sum(p) * (2^15 -
+ * 255)), the remainder added to f_0, p_0 = 1 - exp(-0.5/s),
+ * p_k = (exp(-(|k|-0.5)/s) - exp(-(|k|+0.5)/s)) / 2, sum in index order.
+ * The plan CRC is CRC-32 (zlib polynomial) over step (fp32 LE), the active
+ * flags (u8) and the active tables' f (u16 LE, rank order).
+ * --------------------------------------------------------------------------*/
+
+/* Host only, no device needed: the plan's tables into caller buffers.
+ * step_out (host) [n_coef], active_out (host) [n_coef], freq_out (host)
+ * [n_coef][255] (rows 0..C_a-1 filled in rank order; may be NULL),
+ * *c_active and *crc (host).  Returns DCKV_EINVAL for n_coef < 1,
+ * non-positive or non-finite vectors, or a non-positive step_scale. */
+int dckv_plan_tables(const float *base_step, const float *laplace_scale, int32_t n_coef,
+                     float step_scale, float *step_out, uint8_t *active_out,
+                     uint16_t *freq_out, int32_t *c_active, uint32_t *crc);
+
+/* Builds a plan on the current HIP device (synchronous: host tables, then an
+ * upload of about 1 MB).  *out receives the handle; free with dckv_plan_free.
+ * Returns DCKV_EUNSUPPORTED for shapes the kernels do not support. */
+int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **out);
+int dckv_plan_free(dckv_plan_t *plan);
+
+/* Host copies of the plan's tables (any pointer may be NULL). */
+int dckv_plan_info(const dckv_plan_t *plan, float *step_out, uint8_t *active_out,
+                   uint16_t *freq_out, int32_t *c_active, uint32_t *crc);
+
+/* Pure host.  For a request of T tokens: the largest stream an encode can
+ * produce (every code escaped or 16 bits) and the workspace bytes that
+ * dckv_encode / dckv_decode / the entropy stages need. */
+int dckv_bytes(const dckv_plan_t *plan, int64_t T, uint64_t *max_stream_bytes,
+               uint64_t *workspace_bytes);
+
+/* ---------------------------------------------------------------------------
+ * Encode (DCKV digest, "How it works": all bullets; stream layout below).
+ *
+ * rows      [T][D] bf16 pre-RoPE rows, column ((l*2 + kv)*n_kv_heads + h)*head_dim + d
+ *           with kv = 0 for keys.
+ * token_ids [T] int32, each in [0, vocab).
+ * Coded row j is position t = j + keep_head, j = 0..N-1, N = max(T - keep_head -
+ * keep_tail, 0).  y_j = A x_t; mu_j = H E[tok_t] for even j and
+ * H E[tok_t] + a (yhat_{j-1} + yhat_{j+1}) for odd j (yhat_N = 0); the code is
+ * q = rint(fp32(y - mu) / step) (float32, ties to even) for active components,
+ * yhat = mu + q step; |q| > 127 is escaped.  Codes of each (256-token block,
+ * 64 active components) group are coded by an interleaved 32-bit rANS
+ * (16-bit renormalisation, L = 2^16).
+ * stream       output, `capacity` bytes.
+ * stream_bytes (device) u64: the stream's size, or 0 on a device-side error.
+ * status       (device) int32: DCKV_OK, DCKV_EINVAL (non-finite residual),
+ *              DCKV_ECAPACITY (stream larger than capacity, or more escapes
+ *              than the workspace holds).
+ * Asynchronous on hip_stream.  capacity must be at least the fixed part
+ * (header, kept rows and group offsets) or DCKV_ECAPACITY is returned.
+ * --------------------------------------------------------------------------*/
+int dckv_encode(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *token_ids,
+                int64_t T, uint8_t *stream, uint64_t capacity, uint64_t *stream_bytes,
+                int32_t *status, void *workspace, uint64_t workspace_bytes, void *hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode: two checkerboard passes, synthesis with the GELU correction, RoPE.
+ * (DCKV digest, "How it works": Transform, Conditional entropy models, first
+ * paragraph for RoPE.)
+ *
+ * stream, stream_bytes (host u64): a stream from dckv_encode.
+ * token_ids [T] int32: the same ids that were encoded (not stored).
+ * rows_out  [T][D] bf16: every row with RoPE applied to the key columns
+ *           (rotate-half, w_i = theta^(-i/(head_dim/2)), angle t*w_i).
+ * status    (device) int32: DCKV_OK, DCKV_ECORRUPT, DCKV_EPLAN.  On error the
+ *           contents of rows_out are unspecified.
+ * Asynchronous on hip_stream.
+ * --------------------------------------------------------------------------*/
+int dckv_decode(const dckv_plan_t *plan, const uint8_t *stream, uint64_t stream_bytes,
+                const int32_t *token_ids, int64_t T, uint16_t *rows_out, int32_t *status,
+                void *workspace, uint64_t workspace_bytes, void *hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * The lossless stage alone (DCKV digest, "How it works", Coding).
+ *
+ * dckv_entropy_encode: writes the stream for given codes.
+ *   sym        [N][C_a] u8, symbol q+127 per active component (rank order),
+ *              255 at escaped positions;
+ *   esc        [n_esc] records {u32 flat = j*C_a + rank, i32 q}, strictly
+ *              ascending flat, exactly the positions where sym == 255;
+ *   rows       [T][D] bf16, only the kept rows are read;
+ *   stream, capacity, stream_bytes, status as for dckv_encode.
+ * dckv_entropy_decode: parses and rANS-decodes a stream.
+ *   sym_out    [N][C_a] u8 (255 at escaped positions);
+ *   n_esc_out  (device) u32: number of escape records (they are in the stream).
+ *   status     (device) as for dckv_decode.
+ * --------------------------------------------------------------------------*/
+int dckv_entropy_encode(const dckv_plan_t *plan, int64_t T, const uint8_t *sym,
+                        const uint32_t *esc, uint32_t n_esc, const uint16_t *rows,
+                        uint8_t *stream, uint64_t capacity, uint64_t *stream_bytes,
+                        int32_t *status, void *workspace, uint64_t workspace_bytes,
+                        void *hip_stream);
+int dckv_entropy_decode(const dckv_plan_t *plan, const uint8_t *stream, uint64_t stream_bytes,
+                        int64_t T, uint8_t *sym_out, uint32_t *n_esc_out, int32_t *status,
+                        void *workspace, uint64_t workspace_bytes, void *hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Introspection of the workspace after a call (for tests and tools).
+ * Valid until the workspace is reused.  which:
+ *   DCKV_VIEW_SYMBOLS  u8 symbols of the last encode/decode, group-tiled:
+ *                      [G][N256/4][64][4], N256 = 256 * ceil(N/256);
+ *                      symbol (j, rank r) at ((r/64)*(N256/4) + j/4)*256 + (r%64)*4 + j%4
+ *   DCKV_VIEW_YHAT_B   bf16 [N][n_coef] decoded coefficients (row stride n_coef)
+ *   DCKV_VIEW_H_B      bf16 [N][n_hidden] correction hidden units
+ *   DCKV_VIEW_MEAN     fp32 embedding mean H E[tok] of the last encode,
+ *                      [N4/4][C_a4][4], N4 = rows rounded up to the GEMM tile,
+ *                      C_a4 = C_a rounded up to the GEMM tile;
+ *                      element (j, rank r) at ((j/4)*C_a4 + r)*4 + j%4
+ * --------------------------------------------------------------------------*/
+enum { DCKV_VIEW_SYMBOLS = 0, DCKV_VIEW_YHAT_B = 1, DCKV_VIEW_H_B = 2, DCKV_VIEW_MEAN = 3 };
+int dckv_workspace_view(const dckv_plan_t *plan, int64_t T, int32_t which, uint64_t *offset,
+                        uint64_t *bytes, int64_t *row_stride);
+
+/* ---------------------------------------------------------------------------
+ * Kernel timing.  While enabled, every launch of the named kernels is
+ * bracketed by HIP events on the call's stream; dckv_profile_read()
+ * synchronises those events and returns the summed milliseconds and the
+ * number of launches since the last reset.  Kernel names: "mean_gemm",
+ * "analysis_gemm", "rans_encode", "rans_decode", "dequant_gemm", "w1_gemm",
+ * "synthesis_gemm", "fixup", "pack", "parse".
+ * --------------------------------------------------------------------------*/
+int dckv_profile_enable(int32_t on);
+int dckv_profile_reset(void);
+int dckv_profile_read(const char *kernel, double *total_ms, int64_t *launches);
+
+const char *dckv_last_error(void);
+
+/* Stream layout, version 1 (little endian, sections contiguous, no padding):
+ *   0   "DCKV", u16 version = 1, u16 header_bytes = 64
+ *   8   u32 T, keep_head, keep_tail, N, n_coef, C_a, n_groups, n_esc
+ *   40  f32 step_scale, u32 plan_crc
+ *   48  u64 total_bytes, u64 rans_bytes
+ *   64  kept rows, bf16 pre-RoPE, in position order: (T - N) rows of D
+ *   ..  u32 group_offset[n_groups + 1], byte offsets into the rANS section
+ *   ..  n_esc records {u32 flat, i32 q}, ascending flat
+ *   ..  rANS section: group id = b*G + g (b = 256-token block, g = 64-component
+ *       group, G = ceil(C_a/64)), each a sequence of u16 words.
+ * A group's lanes are active ranks 64g..64g+n-1; its encoder starts each lane
+ * at x = 2^16, codes tokens last to first and lanes last to first, emits
+ * x & 0xFFFF and shifts by 16 while x >= f * 2^17, then
+ * x = (x / f) * 2^15 + x % f + cum; it ends by emitting, lanes last to first,
+ * x >> 16 then x & 0xFFFF; the stored words are the emitted ones reversed.
+ * Escaped positions are skipped. */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DCKV_H */

@@ -1,0 +1,327 @@
+"""DCKV prompt-KV-cache codec for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding of ``libdckv.so``: every function here only marshals
+arguments for the C ABI declared in ``include/dckv.h``; every step of encode
+and decode runs in the library's HIP kernels.  PyTorch provides device memory
+and the current HIP stream.
+
+The library must be built first (``python -m learned_kv_cache_dckv_amd.build``);
+importing this package without it raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdckv.so")
+
+OK, EINVAL, ENOMEM, ECAPACITY, ECORRUPT, EPLAN, EHIP, EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6, -7
+STATUS_NAMES = {0: "OK", -1: "EINVAL", -2: "ENOMEM", -3: "ECAPACITY", -4: "ECORRUPT", -5: "EPLAN",
+                -6: "EHIP", -7: "EUNSUPPORTED"}
+VIEW_SYMBOLS, VIEW_YHAT_B, VIEW_H_B, VIEW_MEAN = 0, 1, 2, 3
+
+# every symbol include/dckv.h declares
+EXPORTS = ("dckv_plan_tables", "dckv_plan", "dckv_plan_free", "dckv_plan_info", "dckv_bytes", "dckv_encode",
+           "dckv_decode", "dckv_entropy_encode", "dckv_entropy_decode", "dckv_workspace_view",
+           "dckv_profile_enable", "dckv_profile_reset", "dckv_profile_read", "dckv_last_error")
+
+
+class DckvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s (%d): %s" % (STATUS_NAMES.get(code, "?"), code, msg))
+        self.code = code
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("n_coef", ctypes.c_int32), ("n_hidden", ctypes.c_int32), ("emb_dim", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("keep_head", ctypes.c_int32), ("keep_tail", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float),
+                ("analysis", ctypes.c_void_p), ("synthesis", ctypes.c_void_p), ("w1", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("embedding", ctypes.c_void_p), ("mean_head", ctypes.c_void_p),
+                ("nbr_weight", ctypes.c_void_p), ("laplace_scale", ctypes.c_void_p),
+                ("base_step", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libdckv.so is not built: run `python -m learned_kv_cache_dckv_amd.build` "
+                          "(expected at %s)" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, U64, I64, I32, U32, F = (ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32,
+                                ctypes.c_uint32, ctypes.c_float)
+    sig = {
+        "dckv_plan_tables": [P, P, I32, F, P, P, P, P, P],
+        "dckv_plan": [P, F, P],
+        "dckv_plan_free": [P],
+        "dckv_plan_info": [P, P, P, P, P, P],
+        "dckv_bytes": [P, I64, P, P],
+        "dckv_encode": [P, P, P, I64, P, U64, P, P, P, U64, P],
+        "dckv_decode": [P, P, U64, P, I64, P, P, P, U64, P],
+        "dckv_entropy_encode": [P, I64, P, P, U32, P, P, U64, P, P, P, U64, P],
+        "dckv_entropy_decode": [P, P, U64, I64, P, P, P, P, U64, P],
+        "dckv_workspace_view": [P, I64, I32, P, P, P],
+        "dckv_profile_enable": [I32],
+        "dckv_profile_reset": [],
+        "dckv_profile_read": [ctypes.c_char_p, P, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.dckv_last_error.argtypes = []
+    lib.dckv_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def dckv_last_error() -> str:
+    return (_lib.dckv_last_error() or b"").decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise DckvError(rc, dckv_last_error())
+
+
+def _ptr(x) -> int:
+    """Address of a torch tensor (device) or numpy array (host); None -> 0."""
+    if x is None:
+        return 0
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    return x.data_ptr()
+
+
+def _stream_handle(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _as_bits(t):
+    """bf16 tensor or int16/uint16 bit tensor -> int16 tensor view of the bits."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16)
+    if t.dtype in (torch.int16, torch.uint16):
+        return t.view(torch.int16)
+    raise TypeError("expected bf16 data as torch.bfloat16 or 16-bit integer bits, got %s" % t.dtype)
+
+
+# ---------------------------------------------------------------------------
+# plan
+# ---------------------------------------------------------------------------
+def dckv_plan_tables(base_step, laplace_scale, step_scale: float):
+    """Host-only plan tables: dict(step, active, freq[C_a][255], c_active, crc)."""
+    bs = np.ascontiguousarray(base_step, dtype=np.float32)
+    ls = np.ascontiguousarray(laplace_scale, dtype=np.float32)
+    n = bs.size
+    step = np.empty(n, np.float32)
+    active = np.empty(n, np.uint8)
+    freq = np.empty((n, 255), np.uint16)
+    ca = ctypes.c_int32()
+    crc = ctypes.c_uint32()
+    _check(_lib.dckv_plan_tables(_ptr(bs), _ptr(ls), n, float(step_scale), _ptr(step), _ptr(active), _ptr(freq),
+                                 ctypes.byref(ca), ctypes.byref(crc)))
+    return dict(step=step, active=active.astype(bool), freq=freq[:ca.value].copy(), c_active=ca.value,
+                crc=crc.value)
+
+
+class Codec:
+    """Codec parameters resident in device memory (bf16 matrices as bit tensors)."""
+
+    def __init__(self, params: dict, device="cuda"):
+        import torch
+        self.device = torch.device(device)
+
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(self.device)
+
+        self.analysis = dev(params["analysis"])
+        self.synthesis = dev(params["synthesis"])
+        self.w1 = dev(params["w1"])
+        self.w2 = dev(params["w2"])
+        self.embedding = dev(params["embedding"])
+        self.mean_head = dev(params["mean_head"])
+        self.nbr_weight = np.ascontiguousarray(params["nbr_weight"], dtype=np.float32)
+        self.laplace_scale = np.ascontiguousarray(params["laplace_scale"], dtype=np.float32)
+        self.base_step = np.ascontiguousarray(params["base_step"], dtype=np.float32)
+        self.shape = dict(n_layers=params.get("n_layers", 6), n_kv_heads=params.get("n_kv_heads", 2),
+                          head_dim=params.get("head_dim", 256), keep_head=params.get("keep_head", 4),
+                          keep_tail=params.get("keep_tail", 128), rope_theta=params.get("rope_theta", 1e7))
+        self.n_coef = self.analysis.shape[0]
+        self.D = self.analysis.shape[1]
+        self.n_hidden = self.w1.shape[0]
+        self.vocab, self.emb_dim = self.embedding.shape
+
+    def c_params(self) -> _Params:
+        s = self.shape
+        return _Params(s["n_layers"], s["n_kv_heads"], s["head_dim"], self.n_coef, self.n_hidden, self.emb_dim,
+                       self.vocab, s["keep_head"], s["keep_tail"], float(s["rope_theta"]),
+                       _ptr(self.analysis), _ptr(self.synthesis), _ptr(self.w1), _ptr(self.w2),
+                       _ptr(self.embedding), _ptr(self.mean_head), _ptr(self.nbr_weight),
+                       _ptr(self.laplace_scale), _ptr(self.base_step))
+
+    def plan(self, step_scale: float) -> "Plan":
+        return dckv_plan(self, step_scale)
+
+
+class Plan:
+    def __init__(self, handle: int, codec: Codec, step_scale: float):
+        self.handle = handle
+        self.codec = codec
+        self.step_scale = float(np.float32(step_scale))
+        info = dckv_plan_info(self)
+        self.c_active = info["c_active"]
+        self.crc = info["crc"]
+
+    def free(self):
+        if self.handle:
+            dckv_plan_free(self)
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+    def bytes(self, T: int):
+        return dckv_bytes(self, T)
+
+
+def dckv_plan(codec: Codec, step_scale: float) -> Plan:
+    prm = codec.c_params()
+    h = ctypes.c_void_p()
+    _check(_lib.dckv_plan(ctypes.byref(prm), float(step_scale), ctypes.byref(h)))
+    return Plan(h.value, codec, step_scale)
+
+
+def dckv_plan_free(plan: Plan):
+    h, plan.handle = plan.handle, 0
+    _check(_lib.dckv_plan_free(h))
+
+
+def dckv_plan_info(plan: Plan) -> dict:
+    n = plan.codec.n_coef
+    step = np.empty(n, np.float32)
+    active = np.empty(n, np.uint8)
+    ca = ctypes.c_int32()
+    crc = ctypes.c_uint32()
+    _check(_lib.dckv_plan_info(plan.handle, _ptr(step), _ptr(active), 0, ctypes.byref(ca), ctypes.byref(crc)))
+    freq = np.empty((max(ca.value, 1), 255), np.uint16)
+    _check(_lib.dckv_plan_info(plan.handle, 0, 0, _ptr(freq), None, None))
+    return dict(step=step, active=active.astype(bool), freq=freq[:ca.value], c_active=ca.value, crc=crc.value)
+
+
+def dckv_bytes(plan: Plan, T: int):
+    """(max stream bytes, workspace bytes) for a request of T tokens."""
+    ms = ctypes.c_uint64()
+    ws = ctypes.c_uint64()
+    _check(_lib.dckv_bytes(plan.handle, int(T), ctypes.byref(ms), ctypes.byref(ws)))
+    return ms.value, ws.value
+
+
+def workspace(plan: Plan, T: int):
+    import torch
+    _, ws = dckv_bytes(plan, T)
+    return torch.empty(max(ws, 256), dtype=torch.uint8, device=plan.codec.device)
+
+
+# ---------------------------------------------------------------------------
+# encode / decode
+# ---------------------------------------------------------------------------
+def dckv_encode(plan: Plan, rows, token_ids, stream_buf, stream_bytes, status, ws, stream=None):
+    """Enqueue an encode.  rows [T][D] bf16 (device), token_ids [T] int32,
+    stream_buf uint8 [capacity], stream_bytes int64 [1], status int32 [1]."""
+    T = int(rows.shape[0])
+    rows = _as_bits(rows)
+    _check(_lib.dckv_encode(plan.handle, _ptr(rows), _ptr(token_ids), T, _ptr(stream_buf), stream_buf.numel(),
+                            _ptr(stream_bytes), _ptr(status), _ptr(ws), ws.numel(), _stream_handle(stream)))
+
+
+def dckv_decode(plan: Plan, stream_buf, n_bytes: int, token_ids, rows_out, status, ws, stream=None):
+    """Enqueue a decode into rows_out [T][D] (bf16 or int16 bits)."""
+    T = int(token_ids.shape[0])
+    out = _as_bits(rows_out)
+    _check(_lib.dckv_decode(plan.handle, _ptr(stream_buf), int(n_bytes), _ptr(token_ids), T, _ptr(out),
+                            _ptr(status), _ptr(ws), ws.numel(), _stream_handle(stream)))
+
+
+def dckv_entropy_encode(plan: Plan, T: int, sym, esc, n_esc: int, rows, stream_buf, stream_bytes, status, ws,
+                        stream=None):
+    rows = _as_bits(rows) if rows is not None else None
+    _check(_lib.dckv_entropy_encode(plan.handle, int(T), _ptr(sym), _ptr(esc), int(n_esc), _ptr(rows),
+                                    _ptr(stream_buf), stream_buf.numel(), _ptr(stream_bytes), _ptr(status),
+                                    _ptr(ws), ws.numel(), _stream_handle(stream)))
+
+
+def dckv_entropy_decode(plan: Plan, stream_buf, n_bytes: int, T: int, sym_out, n_esc_out, status, ws,
+                        stream=None):
+    _check(_lib.dckv_entropy_decode(plan.handle, _ptr(stream_buf), int(n_bytes), int(T), _ptr(sym_out),
+                                    _ptr(n_esc_out), _ptr(status), _ptr(ws), ws.numel(), _stream_handle(stream)))
+
+
+def dckv_workspace_view(plan: Plan, T: int, which: int):
+    off = ctypes.c_uint64()
+    nb = ctypes.c_uint64()
+    rs = ctypes.c_int64()
+    _check(_lib.dckv_workspace_view(plan.handle, int(T), int(which), ctypes.byref(off), ctypes.byref(nb),
+                                    ctypes.byref(rs)))
+    return off.value, nb.value, rs.value
+
+
+def dckv_profile_enable(on: bool = True):
+    _check(_lib.dckv_profile_enable(1 if on else 0))
+
+
+def dckv_profile_reset():
+    _check(_lib.dckv_profile_reset())
+
+
+def dckv_profile_read(kernel: str):
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(_lib.dckv_profile_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+# ---------------------------------------------------------------------------
+# convenience (allocating) wrappers
+# ---------------------------------------------------------------------------
+def encode(plan: Plan, rows, token_ids, ws=None, capacity=None):
+    """Encode one request; returns (stream uint8 tensor trimmed to its size, status)."""
+    import torch
+    T = int(rows.shape[0])
+    max_bytes, _ = dckv_bytes(plan, T)
+    cap = int(capacity) if capacity is not None else max_bytes
+    dev = plan.codec.device
+    buf = torch.empty(cap, dtype=torch.uint8, device=dev)
+    nb = torch.zeros(1, dtype=torch.int64, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = workspace(plan, T) if ws is None else ws
+    dckv_encode(plan, rows, token_ids, buf, nb, st, ws)
+    n = int(nb.item())
+    code = int(st.item())
+    return buf[:n], code
+
+
+def decode(plan: Plan, stream_buf, token_ids, ws=None, out=None):
+    """Decode one request; returns (rows bf16 [T][D], status)."""
+    import torch
+    T = int(token_ids.shape[0])
+    dev = plan.codec.device
+    out = torch.empty((T, plan.codec.D), dtype=torch.bfloat16, device=dev) if out is None else out
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = workspace(plan, T) if ws is None else ws
+    dckv_decode(plan, stream_buf, stream_buf.numel(), token_ids, out, st, ws)
+    return out, int(st.item())

@@ -1,0 +1,144 @@
+// C ABI entry points of the DCKV codec: argument checks and the launch
+// sequence of each call.  Every call only enqueues work on the caller's HIP
+// stream; nothing here allocates device memory.
+//
+// Encode (DCKV digest page, "How it works"): kept rows copied verbatim ->
+// embedding mean H E[tok] -> analysis GEMM with the quantiser (even rows, then
+// odd rows with both reconstructed neighbours) -> fix-up of the odd row at
+// each tile edge -> escape ordering -> rANS per group -> group offsets and
+// header -> packing.
+// Decode: parse and validate -> rANS per group -> mean GEMM with the two
+// dequantisation passes -> fix-up -> correction hidden layer -> synthesis with
+// RoPE -> RoPE of the kept rows.
+#include <algorithm>
+#include <cstring>
+
+#include "dckv_internal.h"
+
+using namespace dckv;
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_device(const dckv_plan_t *p) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return set_error(DCKV_EHIP, "no HIP device");
+  if (cur != p->device) return set_error(DCKV_EINVAL, "the current HIP device is not the plan's device");
+  return DCKV_OK;
+}
+
+int common_checks(const dckv_plan_t *p, int64_t T, void *ws, uint64_t ws_bytes, int32_t *status, Geometry &g,
+                  Layout &l) {
+  if (!p) return set_error(DCKV_EINVAL, "null plan");
+  if (T < 0 || T > 0x7FFFFFFF) return set_error(DCKV_EINVAL, "T out of range");
+  if (!status || !aligned(status, 4)) return set_error(DCKV_EINVAL, "status must be a 4-byte aligned device word");
+  if (!ws || !aligned(ws, 256)) return set_error(DCKV_EINVAL, "workspace must be 256-byte aligned");
+  g = geometry(p, T);
+  l = layout(p, g);
+  if ((uint64_t)g.N * (uint64_t)std::max(p->C_a, 1) >= 0xFFFFFFFFull)
+    return set_error(DCKV_EUNSUPPORTED, "request too long for 32-bit escape indices");
+  if (ws_bytes < l.total) return set_error(DCKV_ECAPACITY, "workspace smaller than dckv_bytes() reports");
+  return check_device(p);
+}
+
+int after_launch(const char *what) { return check_hip(hipGetLastError(), what); }
+
+}  // namespace
+
+extern "C" int dckv_encode(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *token_ids, int64_t T,
+                           uint8_t *stream, uint64_t capacity, uint64_t *stream_bytes, int32_t *status,
+                           void *workspace, uint64_t workspace_bytes, void *hip_stream) {
+  Geometry g;
+  Layout l;
+  int rc = common_checks(plan, T, workspace, workspace_bytes, status, g, l);
+  if (rc) return rc;
+  if (T > 0 && (!rows || !aligned(rows, 16) || !token_ids || !aligned(token_ids, 4)))
+    return set_error(DCKV_EINVAL, "rows must be 16-byte aligned, token_ids 4-byte aligned");
+  if (!stream || !aligned(stream, 16) || !stream_bytes || !aligned(stream_bytes, 8))
+    return set_error(DCKV_EINVAL, "stream must be 16-byte aligned and stream_bytes 8-byte aligned");
+  if (capacity < g.fixed_bytes) return set_error(DCKV_ECAPACITY, "capacity below the stream's fixed part");
+  EncodeArgs a{plan, g, l, static_cast<uint8_t *>(workspace), rows, token_ids, stream, capacity,
+               stream_bytes, status, static_cast<hipStream_t>(hip_stream)};
+  launch_init(a);
+  launch_kept_copy(a);
+  launch_mean_gemm(a);
+  launch_analysis_gemm(a);
+  launch_encode_fixup(a);
+  launch_esc_sort(a);
+  launch_rans_encode(a);
+  launch_scan_header(a);
+  launch_pack(a);
+  return after_launch("dckv_encode");
+}
+
+extern "C" int dckv_decode(const dckv_plan_t *plan, const uint8_t *stream, uint64_t stream_bytes,
+                           const int32_t *token_ids, int64_t T, uint16_t *rows_out, int32_t *status,
+                           void *workspace, uint64_t workspace_bytes, void *hip_stream) {
+  Geometry g;
+  Layout l;
+  int rc = common_checks(plan, T, workspace, workspace_bytes, status, g, l);
+  if (rc) return rc;
+  if (T > 0 && (!rows_out || !aligned(rows_out, 16) || !token_ids || !aligned(token_ids, 4)))
+    return set_error(DCKV_EINVAL, "rows_out must be 16-byte aligned, token_ids 4-byte aligned");
+  if (!stream || !aligned(stream, 16)) return set_error(DCKV_EINVAL, "stream must be 16-byte aligned");
+  if (stream_bytes < g.fixed_bytes) return set_error(DCKV_ECORRUPT, "stream shorter than its fixed part");
+  DecodeArgs a{plan, g, l, static_cast<uint8_t *>(workspace), stream, stream_bytes, token_ids, rows_out, status,
+               static_cast<hipStream_t>(hip_stream)};
+  launch_init(a);
+  launch_parse(a);
+  launch_rope_tables(a);
+  launch_rans_decode(a);
+  launch_dequant_gemm(a);
+  launch_decode_fixup(a);
+  launch_w1_gemm(a);
+  launch_synthesis_gemm(a);
+  launch_kept_rope(a);
+  return after_launch("dckv_decode");
+}
+
+extern "C" int dckv_entropy_encode(const dckv_plan_t *plan, int64_t T, const uint8_t *sym, const uint32_t *esc,
+                                   uint32_t n_esc, const uint16_t *rows, uint8_t *stream, uint64_t capacity,
+                                   uint64_t *stream_bytes, int32_t *status, void *workspace,
+                                   uint64_t workspace_bytes, void *hip_stream) {
+  Geometry g;
+  Layout l;
+  int rc = common_checks(plan, T, workspace, workspace_bytes, status, g, l);
+  if (rc) return rc;
+  if (g.N > 0 && plan->C_a > 0 && !sym) return set_error(DCKV_EINVAL, "null symbols");
+  if (n_esc > 0 && (!esc || !aligned(esc, 4))) return set_error(DCKV_EINVAL, "null or misaligned escapes");
+  if ((int64_t)n_esc > g.esc_cap) return set_error(DCKV_ECAPACITY, "more escapes than the workspace holds");
+  if (g.n_kept > 0 && (!rows || !aligned(rows, 16))) return set_error(DCKV_EINVAL, "rows must be 16-byte aligned");
+  if (!stream || !aligned(stream, 16) || !stream_bytes || !aligned(stream_bytes, 8))
+    return set_error(DCKV_EINVAL, "stream must be 16-byte aligned and stream_bytes 8-byte aligned");
+  if (capacity < g.fixed_bytes) return set_error(DCKV_ECAPACITY, "capacity below the stream's fixed part");
+  EncodeArgs a{plan, g, l, static_cast<uint8_t *>(workspace), rows, nullptr, stream, capacity,
+               stream_bytes, status, static_cast<hipStream_t>(hip_stream)};
+  launch_init(a);
+  launch_kept_copy(a);
+  launch_sym_to_tiled(a, sym);
+  launch_load_esc(a, esc, n_esc);
+  launch_rans_encode(a);
+  launch_scan_header(a);
+  launch_pack(a);
+  return after_launch("dckv_entropy_encode");
+}
+
+extern "C" int dckv_entropy_decode(const dckv_plan_t *plan, const uint8_t *stream, uint64_t stream_bytes,
+                                   int64_t T, uint8_t *sym_out, uint32_t *n_esc_out, int32_t *status,
+                                   void *workspace, uint64_t workspace_bytes, void *hip_stream) {
+  Geometry g;
+  Layout l;
+  int rc = common_checks(plan, T, workspace, workspace_bytes, status, g, l);
+  if (rc) return rc;
+  if (g.N > 0 && plan->C_a > 0 && !sym_out) return set_error(DCKV_EINVAL, "null sym_out");
+  if (!stream || !aligned(stream, 16)) return set_error(DCKV_EINVAL, "stream must be 16-byte aligned");
+  if (stream_bytes < g.fixed_bytes) return set_error(DCKV_ECORRUPT, "stream shorter than its fixed part");
+  DecodeArgs a{plan, g, l, static_cast<uint8_t *>(workspace), stream, stream_bytes, nullptr, nullptr, status,
+               static_cast<hipStream_t>(hip_stream)};
+  launch_init(a);
+  launch_parse(a);
+  launch_rans_decode(a);
+  launch_sym_from_tiled(a, sym_out, n_esc_out);
+  return after_launch("dckv_entropy_decode");
+}

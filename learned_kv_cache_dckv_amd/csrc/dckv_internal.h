@@ -1,0 +1,173 @@
+// Internal declarations shared by the host runtime and the HIP kernels of the
+// DCKV codec library.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/dckv.h"
+
+namespace dckv {
+
+// ---- fixed format and kernel constants -----------------------------------
+constexpr int kPrecBits = 15;               // table precision
+constexpr uint32_t kM = 1u << kPrecBits;    // 32768
+constexpr uint32_t kL = 1u << 16;           // rANS lower bound
+constexpr int kNSym = 255;                  // codes -127..127
+constexpr int kEsc = 255;                   // escaped position marker
+constexpr int kBlock = 256;                 // tokens per substream block
+constexpr int kLanes = 64;                  // components per group (one wave)
+constexpr int kBuckets = 128;               // decode lookup buckets per table
+constexpr int kBucketShift = kPrecBits - 7; // slot >> 8 -> bucket
+constexpr int kHeaderBytes = 64;
+constexpr uint16_t kVersion = 1;
+
+// GEMM tiling shared by every transform kernel
+constexpr int kBM = 128;
+constexpr int kBN = 128;
+constexpr int kBK = 64;
+
+// fixed shapes supported by the kernels
+constexpr int kD = 6144;
+constexpr int kC = 2048;
+constexpr int kHid = 256;
+constexpr int kEmb = 2048;
+constexpr int kHeadDim = 256;
+constexpr int kHalf = kHeadDim / 2;
+
+// ---- plan ----------------------------------------------------------------
+struct PlanDev {
+  float *step = nullptr;        // [C]
+  float *nbr = nullptr;         // [C]
+  int32_t *rank = nullptr;      // [C]   rank or -1
+  int32_t *act = nullptr;       // [C_a] component of each rank (padded to a kBN multiple)
+  uint32_t *tab = nullptr;      // [C_a][256]  f | cum << 16
+  uint8_t *bucket = nullptr;    // [C_a][kBuckets] first symbol of each slot bucket
+  double *omega = nullptr;      // [head_dim/2] RoPE frequencies
+};
+
+}  // namespace dckv
+
+struct dckv_plan_s {
+  int n_layers, n_kv_heads, head_dim, D, C, hidden, emb, vocab, keep_head, keep_tail;
+  float rope_theta, step_scale;
+  int C_a, G;
+  uint32_t crc;
+  int device;
+  std::vector<float> step;
+  std::vector<uint8_t> active;
+  std::vector<uint16_t> freq;  // [C_a][255]
+  const uint16_t *A, *S, *W1, *W2, *E, *H;
+  dckv::PlanDev dev;
+  void *dev_block = nullptr;  // one allocation holding every PlanDev array
+};
+
+namespace dckv {
+
+// ---- request geometry and workspace layout --------------------------------
+struct Geometry {
+  int64_t T, N, n_kept;
+  int64_t n_blk, G, n_groups;
+  int64_t N256;       // N rounded up to 256
+  int64_t NM;         // N rounded up to kBM
+  int64_t n_mtiles;   // NM / kBM
+  int64_t Ca4;        // C_a rounded up to kBN
+  int64_t esc_cap;    // escape records the encode workspace holds
+  int64_t rope_hi;    // ceil(T / 256)
+  uint64_t fixed_bytes;  // header + kept rows + group offsets
+};
+
+// control block at the start of every workspace (device)
+struct Ctrl {
+  uint32_t n_esc;        // escapes found (encode) / read (decode)
+  int32_t status;        // sticky first error
+  uint64_t total_bytes;  // stream size (encode)
+  uint64_t rans_bytes;
+  uint64_t esc_off;      // byte offset of the escape section in the stream
+  uint64_t rans_off;     // byte offset of the rANS section in the stream
+  uint64_t offs_off;     // byte offset of the group offsets in the stream
+  uint32_t pad[52];
+};
+static_assert(sizeof(Ctrl) == 256, "ctrl block is 256 bytes");
+
+struct Layout {
+  uint64_t ctrl, sym, mean, esc_raw, esc_sorted, halo_a, halo_b, scratch, gwords, goffs;
+  uint64_t yhat_b, h_b, rope_lo, rope_hi, total;
+};
+
+Geometry geometry(const dckv_plan_t *p, int64_t T);
+Layout layout(const dckv_plan_t *p, const Geometry &g);
+
+// ---- error reporting --------------------------------------------------------
+int set_error(int code, const std::string &msg);
+int check_hip(hipError_t e, const char *what);
+
+// ---- kernel timing ----------------------------------------------------------
+struct KernelTimer {
+  KernelTimer(const char *name, hipStream_t s);
+  ~KernelTimer();
+  const char *name_;
+  hipStream_t s_;
+  hipEvent_t a_ = nullptr, b_ = nullptr;
+};
+
+// ---- launchers (rans.hip / gemm.hip / misc.hip) -----------------------------
+struct EncodeArgs {
+  const dckv_plan_t *p;
+  Geometry g;
+  Layout l;
+  uint8_t *ws;
+  const uint16_t *rows;
+  const int32_t *tok;
+  uint8_t *stream;
+  uint64_t capacity;
+  uint64_t *stream_bytes;
+  int32_t *status;
+  hipStream_t s;
+};
+
+struct DecodeArgs {
+  const dckv_plan_t *p;
+  Geometry g;
+  Layout l;
+  uint8_t *ws;
+  const uint8_t *stream;
+  uint64_t stream_size;
+  const int32_t *tok;
+  uint16_t *rows_out;
+  int32_t *status;
+  hipStream_t s;
+};
+
+// misc.hip
+void launch_init(const EncodeArgs &a);
+void launch_init(const DecodeArgs &a);
+void launch_kept_copy(const EncodeArgs &a);
+void launch_esc_sort(const EncodeArgs &a);
+void launch_finish_status(uint8_t *ws, int32_t *status, uint64_t *stream_bytes, hipStream_t s);
+
+// rans.hip
+void launch_rans_encode(const EncodeArgs &a);
+void launch_scan_header(const EncodeArgs &a);
+void launch_pack(const EncodeArgs &a);
+void launch_parse(const DecodeArgs &a);
+void launch_rans_decode(const DecodeArgs &a);
+void launch_load_esc(const EncodeArgs &a, const uint32_t *esc, uint32_t n_esc);
+void launch_sym_to_tiled(const EncodeArgs &a, const uint8_t *sym);
+void launch_sym_from_tiled(const DecodeArgs &a, uint8_t *sym_out, uint32_t *n_esc_out);
+
+// gemm.hip
+void launch_mean_gemm(const EncodeArgs &a);
+void launch_analysis_gemm(const EncodeArgs &a);
+void launch_encode_fixup(const EncodeArgs &a);
+void launch_rope_tables(const DecodeArgs &a);
+void launch_dequant_gemm(const DecodeArgs &a);
+void launch_decode_fixup(const DecodeArgs &a);
+void launch_w1_gemm(const DecodeArgs &a);
+void launch_synthesis_gemm(const DecodeArgs &a);
+void launch_kept_rope(const DecodeArgs &a);
+
+}  // namespace dckv

@@ -163,9 +163,9 @@ def dequantize(q: np.ndarray, m: np.ndarray, p: Plan, a: np.ndarray) -> np.ndarr
 
 def symbols(q: np.ndarray, p: Plan):
     """Code -> symbol slot (q + 127), 255 for escapes; escape records in flat order."""
-    qa = q[:, p.act_idx]
+    qa = np.ascontiguousarray(q[:, p.act_idx])
     esc = np.abs(qa) > 127
-    sym = np.where(esc, ESC, qa + 127).astype(np.uint8)
+    sym = np.ascontiguousarray(np.where(esc, ESC, qa + 127), dtype=np.uint8)
     jj, rr = np.nonzero(esc)
     flat = jj * p.c_active + rr
     return sym, flat.astype(np.int64), qa[jj, rr].astype(np.int64)
@@ -267,7 +267,7 @@ def decode(data: bytes, tok: np.ndarray, params: dict, p: Plan) -> Decoded:
         esc.reshape(-1)[flat] = True
     sym = rans.decode_all(groups, p.freq, p.cum, N, esc) if N > 0 and p.c_active > 0 else \
         np.full((N, p.c_active), ESC, np.uint8)
-    qa = sym.astype(np.int64) - 127
+    qa = np.ascontiguousarray(sym, dtype=np.int64) - 127
     if len(flat):
         qa.reshape(-1)[flat] = qe
     q = np.zeros((N, C), dtype=np.int64)
