@@ -20,14 +20,14 @@ constexpr int kNSym = 255;                  // codes -127..127
 constexpr int kEsc = 255;                   // escaped position marker
 constexpr int kBlock = 256;                 // tokens per substream block
 constexpr int kLanes = 64;                  // components per group (one wave)
-constexpr int kBuckets = 128;               // decode lookup buckets per table
-constexpr int kBucketShift = kPrecBits - 7; // slot >> 8 -> bucket
+constexpr int kBuckets = 256;               // decode lookup buckets per table (128 slots each)
+constexpr int kBucketShift = kPrecBits - 8; // slot >> 7 -> bucket
 constexpr int kHeaderBytes = 64;
 constexpr uint16_t kVersion = 1;
 
 // GEMM tiling shared by every transform kernel
-constexpr int kBM = 128;
-constexpr int kBN = 128;
+constexpr int kBM = 256;
+constexpr int kBN = 256;
 constexpr int kBK = 64;
 
 // fixed shapes supported by the kernels

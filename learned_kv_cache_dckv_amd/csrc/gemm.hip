@@ -13,21 +13,37 @@
 //     decoding.
 //
 // Every GEMM here is C[m][n] = sum_k A[m][k] * B[n][k] with both operands
-// k-contiguous (token rows times weight rows).  One workgroup of 4 wave64s
-// computes a 128x128 tile; each wave owns a 64x64 sub-tile as 4x4 blocks of
-// v_mfma_f32_16x16x32_bf16.  Operand tiles of 128x64 bf16 are staged through
-// LDS, double buffered, with the next tile's global loads in flight while the
-// current one feeds the matrix cores.
+// k-contiguous (token rows times weight rows).  One workgroup of four wave64s
+// owns a 256x256 tile; each wave a 128x128 sub-tile held as 4x4 blocks of
+// v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane); the 32x32 form
+// keeps the matrix cores busy with a single wave per SIMD.  Operand tiles of
+// 256 rows x 64 k are copied global -> LDS by the direct 16-byte LDS loads of
+// gfx950 (no register staging), double buffered, in an XOR-swizzled layout
+// (16-byte chunk c of row r stored at chunk c ^ (r & 7)) so the fragment reads
+// of 8 consecutive rows hit 8 distinct bank groups.  Workgroups are mapped to
+// tiles so that the tiles of one row band run on the same XCD (the hardware
+// deals workgroups to the 8 XCDs round robin), which keeps a band's token rows
+// in that XCD's L2 while all its weight tiles stream past.
 //
-// Epilogues:
-//   mean       H E[tok] -> fp32, stored in a 4-row-interleaved layout that the
-//              quantiser reads with one 16-byte load per 4 rows
-//   quantise   r = (y - mu) / step, q = rint(r), symbols, escapes; even rows
-//              first, then odd rows with both neighbours (from LDS); the last
-//              odd row of a tile is finished by a small fix-up kernel
+// Lane l of a 32x32 accumulator block holds column l%32 and, in register
+// group g (registers 4g..4g+3), rows 8g + 4*(l/32) .. +3: a quad of 4
+// consecutive rows.  The checkerboard neighbours of a row are in the same
+// quad (rows 4k+1: 4k and 4k+2) or, for row 4k+3, in the first row of the
+// next quad, held by lane l^32 (same group, or the next group / next block).
+// The epilogues work on the accumulators in registers:
+//   mean       H E[tok] -> fp32, stored in the tile-interleaved order the
+//              quantiser reads back (16 bytes per lane per block)
+//   quantise   even rows: r = (y - mu)/step, q = rint(r), yhat = mu + q step;
+//              then odd rows with mu += a (yhat_{j-1} + yhat_{j+1}); the first
+//              row of the lower wave crosses waves through LDS, the last odd
+//              row of a tile is finished by a small fix-up kernel
 //   dequant    yhat = mu + q step in the same two passes -> bf16 yhat_b
-//   w1         GELU(exact erf) -> bf16 h_b
-//   synthesis  RoPE on key heads (rotate-half) -> bf16 rows
+//   w1         exact-erf GELU -> bf16 h_b
+//   synthesis  rotate-half RoPE on key heads; the tile's columns are ordered
+//              so that every pair (d, d+128) sits in one lane and register
+//              of blocks nb and nb+2 -> bf16 rows
+// bf16 outputs go through a per-wave LDS transpose so global stores are
+// 16-byte row segments.
 #include <cmath>
 
 #include "dckv_internal.h"
@@ -37,13 +53,20 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef const void __attribute__((address_space(1))) *gptr_t;
+typedef void __attribute__((address_space(3))) *lptr_t;
 
 constexpr int kThreads = 256;
-constexpr int kLdsStride = kBK + 8;                      // bf16 per staged row (144 B)
-constexpr int kStage = (kBM + kBN) * kLdsStride;         // bf16 per stage
-constexpr int kTileStride = kBM + 4;                     // floats per column of the epilogue tile
-constexpr int kLdsBytes = 2 * kStage * 2 > kBN * kTileStride * 4 ? 2 * kStage * 2 : kBN * kTileStride * 4;
-constexpr float kQLimit = 2147483520.0f;                 // largest float below 2^31
+constexpr int kRowBytes = kBK * 2;                        // 128 B per staged row
+constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 64 KiB per stage
+constexpr int kOutStride = 128 + 8;                       // bf16 per row of a wave's output tile
+constexpr int kOutWaveBytes = 128 * kOutStride * 2;
+constexpr int kXchOff = 4 * kOutWaveBytes;                // row-0 exchange between the two wave rows
+constexpr int kLdsBytes = kXchOff + 2 * 256 * 4;
+static_assert(2 * kStageBytes <= kXchOff, "stages must not overlap the exchange area");
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
+constexpr float kQLimit = 2147483520.0f;  // largest float below 2^31
 
 __device__ __forceinline__ void set_status(int32_t *st, int code) { atomicCAS(st, 0, code); }
 
@@ -58,7 +81,7 @@ __device__ __forceinline__ bool wg_stop(const int32_t *st) {
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// fp32 -> bf16, round to nearest even (finite inputs; NaN kept quiet)
+// fp32 -> bf16, round to nearest even (NaN kept quiet)
 __device__ __forceinline__ uint16_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
@@ -66,97 +89,118 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Operand rows of one tile: 4 rows per thread (tid/8 + 32u), two k-ranges.
-struct Src {
-  const uint16_t *p0[4];
-  const uint16_t *p1[4];
-  int split;  // k-tiles [0, split) from p0, the rest from p1
-};
-
-__device__ __forceinline__ uint4 ld_chunk(const Src &s, int u, int kt, int kc) {
-  const uint16_t *p = kt < s.split ? s.p0[u] + kt * kBK : s.p1[u] + (kt - s.split) * kBK;
-  return *reinterpret_cast<const uint4 *>(p + kc * 8);
+// XCD-aware tile order: workgroup b runs on XCD b % 8; give each XCD a
+// contiguous run of tiles (row-band major) so a band stays in one L2.
+__device__ __forceinline__ void tile_of(int b, int total, int n_nt, int &mt, int &nt) {
+  const int q = total >> 3, r = total & 7, x = b & 7, k = b >> 3;
+  const int t = x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+  mt = t / n_nt;
+  nt = t - mt * n_nt;
 }
 
-__device__ __forceinline__ void mainloop(const Src &A, const Src &B, int KT, f32x4 (&acc)[4][4], uint16_t *lds) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// ---------------------------------------------------------------------------
+// operand staging and the MFMA main loop
+// ---------------------------------------------------------------------------
+struct Operand {
+  const char *base0, *base1;  // two k-ranges (k-tiles [0, split) and the rest)
+  uint32_t rb0, rb1;          // row bytes of each source
+  int split;
+  uint32_t row[8];            // source rows staged by this lane: tile rows wave*64 + 8i + lane/8
+};
+
+__device__ __forceinline__ void stage_tile(const Operand &op, int kt, char *dst_region, int wave, int lane) {
+  const uint32_t chunk = (uint32_t)(((lane & 7) ^ ((lane >> 3) & 7)) << 4);
+  const bool s0 = kt < op.split;
+  const char *base = s0 ? op.base0 : op.base1;
+  const uint32_t rb = s0 ? op.rb0 : op.rb1;
+  const uint32_t ko = (uint32_t)(s0 ? kt : kt - op.split) * kRowBytes + chunk;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const char *src = base + (size_t)op.row[i] * rb + ko;
+    char *dst = dst_region + (wave * 64 + i * 8) * kRowBytes;
+    __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ bf16x8 frag(const char *region, int row, int c) {
+  return *reinterpret_cast<const bf16x8 *>(region + row * kRowBytes + ((c ^ (row & 7)) << 4));
+}
+
+__device__ __forceinline__ void mainloop(const Operand &A, const Operand &B, int KT, f32x16 (&acc)[4][4],
+                                         char *lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int lr = tid >> 3, kc = tid & 7;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint4 ra[4], rb[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    ra[u] = ld_chunk(A, u, 0, kc);
-    rb[u] = ld_chunk(B, u, 0, kc);
-  }
-  {
-    uint16_t *sa = lds, *sb = lds + kBM * kLdsStride;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      *reinterpret_cast<uint4 *>(sa + (lr + 32 * u) * kLdsStride + kc * 8) = ra[u];
-      *reinterpret_cast<uint4 *>(sb + (lr + 32 * u) * kLdsStride + kc * 8) = rb[u];
-    }
-  }
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  stage_tile(A, 0, lds, wave, lane);
+  stage_tile(B, 0, lds + kBM * kRowBytes, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
+    const char *cur = lds + (kt & 1) * kStageBytes;
     if (kt + 1 < KT) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        ra[u] = ld_chunk(A, u, kt + 1, kc);
-        rb[u] = ld_chunk(B, u, kt + 1, kc);
-      }
+      char *nxt = lds + ((kt + 1) & 1) * kStageBytes;
+      stage_tile(A, kt + 1, nxt, wave, lane);
+      stage_tile(B, kt + 1, nxt + kBM * kRowBytes, wave, lane);
     }
-    const uint16_t *sa = lds + cur * kStage;
-    const uint16_t *sb = sa + kBM * kLdsStride;
+    const char *sa = cur, *sb = cur + kBM * kRowBytes;
 #pragma unroll
-    for (int ks = 0; ks < kBK / 32; ++ks) {
-      bf16x8 af[4], bfr[4];
-      const int ko = ks * 32 + (lane >> 4) * 8;
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
+      bf16x8 a[4], b[4];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        af[mb] = *reinterpret_cast<const bf16x8 *>(sa + (wm * 64 + mb * 16 + (lane & 15)) * kLdsStride + ko);
+      for (int mb = 0; mb < 4; ++mb) a[mb] = frag(sa, wm * 128 + mb * 32 + (lane & 31), c);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        bfr[nb] = *reinterpret_cast<const bf16x8 *>(sb + (wn * 64 + nb * 16 + (lane & 15)) * kLdsStride + ko);
+      for (int nb = 0; nb < 4; ++nb) b[nb] = frag(sb, wn * 128 + nb * 32 + (lane & 31), c);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
     }
-    if (kt + 1 < KT) {
-      uint16_t *da = lds + (cur ^ 1) * kStage, *db = da + kBM * kLdsStride;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        *reinterpret_cast<uint4 *>(da + (lr + 32 * u) * kLdsStride + kc * 8) = ra[u];
-        *reinterpret_cast<uint4 *>(db + (lr + 32 * u) * kLdsStride + kc * 8) = rb[u];
-      }
-    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 }
 
-// Accumulators -> LDS tile, column-major: tile[n * kTileStride + m].
-// Lane l of a 16x16 block holds rows 4*(l/16) .. +3 of column l%16.
-__device__ __forceinline__ void acc_to_tile(const f32x4 (&acc)[4][4], float *tile) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int col = wn * 64 + nb * 16 + (lane & 15);
-      const int row = wm * 64 + mb * 16 + (lane >> 4) * 4;
-      *reinterpret_cast<f32x4 *>(tile + col * kTileStride + row) = acc[mb][nb];
+// Row (within the wave tile) of register v of block row mb in this lane.
+__device__ __forceinline__ int acc_row(int mb, int v, int lane) { return mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+
+// ---------------------------------------------------------------------------
+// bf16 output through a per-wave LDS transpose
+// ---------------------------------------------------------------------------
+// The caller writes its 128x128 values (bf16) to the wave's LDS tile with
+// put(); flush_rows() then stores 16-byte row segments: LDS columns [0, 64)
+// go to out[row][col_lo + c], columns [64, 128) to out[row][col_hi + c - 64].
+__device__ __forceinline__ void put(char *wtile, int r, int cc, uint16_t v) {
+  *reinterpret_cast<uint16_t *>(wtile + (r * kOutStride + cc) * 2) = v;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void flush_rows(const char *wtile, uint16_t *out, int64_t ld, int64_t row0, int64_t col_lo,
+                                           int64_t col_hi, int64_t rows_valid) {
+  const int lane = threadIdx.x & 63;
+  const int seg = lane & 15;
+  const int64_t col = seg < 8 ? col_lo + seg * 8 : col_hi + (seg - 8) * 8;
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int r = it * 4 + (lane >> 4);
+    if (row0 + r < rows_valid) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(wtile + (r * kOutStride + seg * 8) * 2);
+      *reinterpret_cast<uint4 *>(out + (size_t)(row0 + r) * ld + col) = v;
     }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// operand row pointers (per thread: rows tid/8 + 32u of the tile)
+// operand setup helpers
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int clamp_tok(const int32_t *tok, int64_t t, int vocab, int32_t *status) {
   int v = tok[t];
@@ -167,44 +211,55 @@ __device__ __forceinline__ int clamp_tok(const int32_t *tok, int64_t t, int voca
   return v;
 }
 
+__device__ __forceinline__ int staged_row(int i) { return (threadIdx.x >> 6) * 64 + i * 8 + ((threadIdx.x & 63) >> 3); }
+
+// tile-interleaved fp32 storage of one 256x256 tile: 64 bytes per lane per block
+__device__ __forceinline__ f32x4 *tiled_ptr(float *base, int64_t tile_id, int wave, int mb, int nb, int lane) {
+  return reinterpret_cast<f32x4 *>(base + ((((tile_id * 4 + wave) * 4 + mb) * 4 + nb) * 64 + lane) * 16);
+}
+
 // ---------------------------------------------------------------------------
 // encode: mean GEMM  m[j][r] = sum_k E[tok_{j+kh}][k] H[act[r]][k]
 // ---------------------------------------------------------------------------
 struct MeanEncP {
   const uint16_t *E, *H;
   const int32_t *tok, *act;
-  float *mean;  // [NM/4][Ca4][4]
-  int64_t N, Ca4;
-  int keep_head, vocab;
+  float *mean;  // tile-interleaved [n_mtiles][n_ntiles][256x256]
+  int64_t N;
+  int n_mt, n_nt, keep_head, vocab;
   int32_t *status;
 };
 
-__global__ __launch_bounds__(kThreads) void k_mean_enc(MeanEncP P) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kLdsBytes];
-  uint16_t *lds = reinterpret_cast<uint16_t *>(lds_raw);
+__global__ __launch_bounds__(kThreads, 1) void k_mean_enc(MeanEncP P) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
   if (wg_stop(P.status)) return;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM;
-  const int n0 = blockIdx.x * kBN;
-  const int lr = threadIdx.x >> 3;
-  Src A, B;
+  int mt, nt;
+  tile_of(blockIdx.x, P.n_mt * P.n_nt, P.n_nt, mt, nt);
+  const int64_t m0 = (int64_t)mt * kBM;
+  const int n0 = nt * kBN;
+  Operand A, B;
+  A.base0 = A.base1 = reinterpret_cast<const char *>(P.E);
+  B.base0 = B.base1 = reinterpret_cast<const char *>(P.H);
+  A.rb0 = A.rb1 = B.rb0 = B.rb1 = kEmb * 2;
   A.split = B.split = kEmb / kBK;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t j = min<int64_t>(m0 + lr + 32 * u, P.N - 1);
-    A.p0[u] = A.p1[u] = P.E + (size_t)clamp_tok(P.tok, P.keep_head + j, P.vocab, P.status) * kEmb;
-    B.p0[u] = B.p1[u] = P.H + (size_t)P.act[n0 + lr + 32 * u] * kEmb;
+  for (int i = 0; i < 8; ++i) {
+    const int64_t j = min<int64_t>(m0 + staged_row(i), P.N - 1);
+    A.row[i] = (uint32_t)clamp_tok(P.tok, P.keep_head + j, P.vocab, P.status);
+    B.row[i] = (uint32_t)P.act[n0 + staged_row(i)];
   }
-  f32x4 acc[4][4];
+  f32x16 acc[4][4];
   mainloop(A, B, kEmb / kBK, acc, lds);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t tid = (int64_t)mt * P.n_nt + nt;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const int64_t row = m0 + wm * 64 + mb * 16 + (lane >> 4) * 4;
-      const int64_t col = n0 + wn * 64 + nb * 16 + (lane & 15);
-      *reinterpret_cast<f32x4 *>(P.mean + ((row >> 2) * P.Ca4 + col) * 4) = acc[mb][nb];
+      f32x4 *dst = tiled_ptr(P.mean, tid, wave, mb, nb, lane);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        dst[g] = f32x4{acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]};
     }
 }
 
@@ -214,24 +269,32 @@ __global__ __launch_bounds__(kThreads) void k_mean_enc(MeanEncP P) {
 struct QuantP {
   const uint16_t *rows, *A;
   const int32_t *act;
-  const float *step, *nbr, *mean;
+  const float *step, *nbr;
+  float *mean;
   uint32_t *sym32;
-  uint32_t *esc_raw;   // {flat, q}
+  uint32_t *esc_raw;  // {flat, q}
   uint8_t *ws;
   float *halo_a, *halo_b;
-  int64_t N, N256, Ca4, esc_cap;
-  int Ca, keep_head, C;
+  int64_t N, N256, esc_cap;
+  int Ca, keep_head, C, n_mt, n_nt;
   int32_t *status;
 };
 
-__device__ __forceinline__ uint32_t quant_one(float d, float step, int64_t j, int r, const QuantP &P, bool &bad,
-                                              float &qf) {
+// r = fp32(d / step) from the reciprocal and one fused correction
+__device__ __forceinline__ float div_step(float d, float step, float inv) {
+  const float q0 = d * inv;
+  const float e = fmaf(-q0, step, d);
+  return fmaf(e, inv, q0);
+}
+
+__device__ __forceinline__ uint32_t quant_one(float d, float step, float inv, int64_t j, int r, const QuantP &P,
+                                              bool &bad, float &qf) {
   if (!isfinite(d)) {
     bad = true;
     qf = 0.f;
     return 127u;
   }
-  qf = fminf(fmaxf(rintf(d / step), -kQLimit), kQLimit);
+  qf = fminf(fmaxf(rintf(div_step(d, step, inv)), -kQLimit), kQLimit);
   const int qi = (int)qf;
   if (qi >= -127 && qi <= 127) return (uint32_t)(qi + 127);
   Ctrl *ct = reinterpret_cast<Ctrl *>(P.ws);
@@ -243,86 +306,135 @@ __device__ __forceinline__ uint32_t quant_one(float d, float step, int64_t j, in
   return (uint32_t)kEsc;
 }
 
-__global__ __launch_bounds__(kThreads) void k_analysis_quant(QuantP P) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kLdsBytes];
-  uint16_t *lds = reinterpret_cast<uint16_t *>(lds_raw);
+__device__ __forceinline__ uint32_t with_byte(uint32_t w, int i, uint32_t s) {
+  return (w & ~(0xFFu << (8 * i))) | (s << (8 * i));
+}
+
+// First row of the quad after the one in register group g of block mb, for
+// the lane that holds this quad: lanes 0..31 find it in lane l+32 (same
+// group), lanes 32..63 in lane l-32 (next group, or group 0 of the next
+// block).  `ext` is used for the wave tile's last quad.  All lanes call this.
+__device__ __forceinline__ float next_quad_row0(const f32x16 (&acc)[4][4], int mb, int nb, int g, float ext, int lane) {
+  const float same = __shfl_xor(acc[mb][nb][4 * g], 32);
+  float nxt;
+  if (g < 3) nxt = __shfl_xor(acc[mb][nb][4 * g + 4], 32);
+  else if (mb < 3) nxt = __shfl_xor(acc[mb + 1 < 4 ? mb + 1 : 3][nb][0], 32);
+  else nxt = ext;
+  return lane < 32 ? same : nxt;
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
   if (wg_stop(P.status)) return;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM;
-  const int n0 = blockIdx.x * kBN;
-  const int lr = threadIdx.x >> 3;
-  Src A, B;
+  int mt, nt;
+  tile_of(blockIdx.x, P.n_mt * P.n_nt, P.n_nt, mt, nt);
+  const int64_t m0 = (int64_t)mt * kBM;
+  const int n0 = nt * kBN;
+  Operand A, B;
+  A.base0 = A.base1 = reinterpret_cast<const char *>(P.rows);
+  B.base0 = B.base1 = reinterpret_cast<const char *>(P.A);
+  A.rb0 = A.rb1 = B.rb0 = B.rb1 = kD * 2;
   A.split = B.split = kD / kBK;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t j = min<int64_t>(m0 + lr + 32 * u, P.N - 1);
-    A.p0[u] = A.p1[u] = P.rows + (size_t)(P.keep_head + j) * kD;
-    B.p0[u] = B.p1[u] = P.A + (size_t)P.act[n0 + lr + 32 * u] * kD;
+  for (int i = 0; i < 8; ++i) {
+    const int64_t j = min<int64_t>(m0 + staged_row(i), P.N - 1);
+    A.row[i] = (uint32_t)(P.keep_head + j);
+    B.row[i] = (uint32_t)P.act[n0 + staged_row(i)];
   }
-  f32x4 acc[4][4];
+  f32x16 acc[4][4];
   mainloop(A, B, kD / kBK, acc, lds);
-  float *tile = reinterpret_cast<float *>(lds_raw);
-  acc_to_tile(acc, tile);
-  __syncthreads();
 
-  const int col = threadIdx.x & 127, half = threadIdx.x >> 7;
-  const int r = n0 + col;
-  const bool rv = r < P.Ca;
-  const int c = P.act[r];
-  const float step = P.step[c], a = P.nbr[c];
-  float *tc = tile + col * kTileStride;
-  const int64_t mt = blockIdx.y;
-  uint32_t symw[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t tid = (int64_t)mt * P.n_nt + nt;
+  const int64_t wrow0 = m0 + wm * 128;  // first row of this wave's tile
+  int r_nb[4];
+  float st_nb[4], inv_nb[4], a_nb[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int r = n0 + wn * 128 + nb * 32 + (lane & 31);
+    const int c = P.act[r];
+    r_nb[nb] = r;
+    st_nb[nb] = P.step[c];
+    inv_nb[nb] = 1.0f / st_nb[nb];
+    a_nb[nb] = P.nbr[c];
+  }
+  uint32_t symw[4][4][4];
   bool bad = false;
   // pass 1: even rows, mu = H E[tok]
-#pragma unroll 4
-  for (int qd = 0; qd < 16; ++qd) {
-    const int rq = half * 64 + qd * 4;
-    const int64_t j0 = m0 + rq;
-    const f32x4 mm = *reinterpret_cast<const f32x4 *>(P.mean + ((j0 >> 2) * P.Ca4 + r) * 4);
-    uint32_t w = 0xFFFFFFFFu;
 #pragma unroll
-    for (int e = 0; e < 4; e += 2) {
-      const int64_t j = j0 + e;
-      if (j < P.N && rv) {
-        float qf;
-        const uint32_t s = quant_one(tc[rq + e] - mm[e], step, j, r, P, bad, qf);
-        tc[rq + e] = mm[e] + qf * step;
-        w = (w & ~(0xFFu << (8 * e))) | (s << (8 * e));
-      } else {
-        tc[rq + e] = 0.f;  // a missing right neighbour counts as zero
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const f32x4 *mp = tiled_ptr(P.mean, tid, wave, mb, nb, lane);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 m4 = mp[g];
+        uint32_t w = 0xFFFFFFFFu;
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const int v = 4 * g + i;
+          const int64_t j = wrow0 + acc_row(mb, v, lane);
+          if (j < P.N && r_nb[nb] < P.Ca) {
+            float qf;
+            const uint32_t sy = quant_one(acc[mb][nb][v] - m4[i], st_nb[nb], inv_nb[nb], j, r_nb[nb], P, bad, qf);
+            acc[mb][nb][v] = m4[i] + qf * st_nb[nb];
+            w = with_byte(w, i, sy);
+          } else {
+            acc[mb][nb][v] = 0.f;  // a missing right neighbour counts as zero
+          }
+        }
+        symw[mb][nb][g] = w;
       }
     }
-    symw[qd] = w;
+  // the first row of each wave row: to the wave above (LDS) and, for the
+  // tile's row 0, to the fix-up of the previous tile (global)
+  float *xch = reinterpret_cast<float *>(lds + kXchOff);
+  if (lane < 32) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      xch[wm * 256 + wn * 128 + nb * 32 + lane] = acc[0][nb][0];
+      if (wm == 0 && r_nb[nb] < P.Ca) P.halo_b[(int64_t)mt * P.C + r_nb[nb]] = acc[0][nb][0];
+    }
   }
   __syncthreads();
-  if (half == 0 && rv) P.halo_b[mt * P.C + r] = tc[0];
+  const bool defer_last = m0 + kBM < P.N;
   // pass 2: odd rows, mu = H E[tok] + a (yhat_{j-1} + yhat_{j+1})
-#pragma unroll 4
-  for (int qd = 0; qd < 16; ++qd) {
-    const int rq = half * 64 + qd * 4;
-    const int64_t j0 = m0 + rq;
-    const f32x4 mm = *reinterpret_cast<const f32x4 *>(P.mean + ((j0 >> 2) * P.Ca4 + r) * 4);
-    uint32_t w = symw[qd];
 #pragma unroll
-    for (int e = 1; e < 4; e += 2) {
-      const int row = rq + e;
-      const int64_t j = j0 + e;
-      if (!(j < P.N && rv)) continue;
-      const float prev = tc[row - 1];
-      uint32_t s;
-      if (row == kBM - 1 && j + 1 < P.N) {
-        P.halo_a[mt * P.C + r] = tc[row] - mm[e] - a * prev;  // finished by the fix-up
-        s = 0u;
-      } else {
-        const float next = row + 1 < kBM ? tc[row + 1] : 0.f;
-        const float mu = mm[e] + a * (prev + next);
-        float qf;
-        s = quant_one(tc[row] - mu, step, j, r, P, bad, qf);
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const f32x4 *mp = tiled_ptr(P.mean, tid, wave, mb, nb, lane);
+      const float ext = wm == 0 ? xch[256 + wn * 128 + nb * 32 + (lane & 31)] : 0.f;
+      const float a = a_nb[nb];
+      const int r = r_nb[nb];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float next3 = next_quad_row0(acc, mb, nb, g, ext, lane);
+        const f32x4 m4 = mp[g];
+        uint32_t w = symw[mb][nb][g];
+        const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
+        const float y0 = acc[mb][nb][4 * g], y2 = acc[mb][nb][4 * g + 2];
+        if (j0 + 1 < P.N && r < P.Ca) {
+          float qf;
+          const float mu = m4[1] + a * (y0 + y2);
+          w = with_byte(w, 1, quant_one(acc[mb][nb][4 * g + 1] - mu, st_nb[nb], inv_nb[nb], j0 + 1, r, P, bad, qf));
+        }
+        if (j0 + 3 < P.N && r < P.Ca) {
+          uint32_t sy;
+          if (wm == 1 && mb == 3 && g == 3 && lane >= 32 && defer_last) {
+            P.halo_a[(int64_t)mt * P.C + r] = acc[mb][nb][4 * g + 3] - m4[3] - a * y2;
+            sy = 0u;  // finished by the fix-up
+          } else {
+            float qf;
+            const float mu = m4[3] + a * (y2 + next3);
+            sy = quant_one(acc[mb][nb][4 * g + 3] - mu, st_nb[nb], inv_nb[nb], j0 + 3, r, P, bad, qf);
+          }
+          w = with_byte(w, 3, sy);
+        }
+        if (j0 < P.N && r < P.Ca) P.sym32[((size_t)(r >> 6) * (P.N256 / 4) + (j0 >> 2)) * 64 + (r & 63)] = w;
       }
-      w = (w & ~(0xFFu << (8 * e))) | (s << (8 * e));
     }
-    if (j0 < P.N && rv) P.sym32[((size_t)(r >> 6) * (P.N256 / 4) + (j0 >> 2)) * 64 + (r & 63)] = w;
-  }
   if (bad) set_status(P.status, DCKV_EINVAL);
 }
 
@@ -339,7 +451,7 @@ __global__ void k_encode_fixup(QuantP P, int64_t n_fix) {
   const float d = P.halo_a[mt * P.C + r] - a * P.halo_b[(mt + 1) * P.C + r];
   bool bad = false;
   float qf;
-  const uint32_t s = quant_one(d, step, j, r, P, bad, qf);
+  const uint32_t s = quant_one(d, step, 1.0f / step, j, r, P, bad, qf);
   uint8_t *sym8 = reinterpret_cast<uint8_t *>(P.sym32);
   sym8[(((size_t)(r >> 6) * (P.N256 / 4) + (j >> 2)) * 64 + (r & 63)) * 4 + (j & 3)] = (uint8_t)s;
   if (bad) set_status(P.status, DCKV_EINVAL);
@@ -358,7 +470,7 @@ struct DeqP {
   uint16_t *yhat_b;  // [NM][C]
   float *halo_a, *halo_b;
   int64_t N, N256;
-  int Ca, keep_head, vocab;
+  int Ca, keep_head, vocab, n_mt, n_nt;
   int32_t *status;
 };
 
@@ -375,107 +487,134 @@ __device__ __forceinline__ int esc_code(const DeqP &P, uint32_t flat) {
   return 0;
 }
 
-__device__ __forceinline__ float code_of(const DeqP &P, uint32_t w, int e, int64_t j, int r) {
-  const uint32_t s = (w >> (8 * e)) & 0xFFu;
+__device__ __forceinline__ float code_of(const DeqP &P, uint32_t w, int i, int64_t j, int r) {
+  const uint32_t s = (w >> (8 * i)) & 0xFFu;
   if (s != (uint32_t)kEsc) return (float)((int)s - 127);
   return (float)esc_code(P, (uint32_t)(j * P.Ca + r));
 }
 
-// row-major bf16 store of a 128x128 LDS tile (column-major floats)
+// bf16 of fn(value) for all 128x128 values of the wave into its LDS tile
+// (identity columns), one element at a time
 template <class F>
-__device__ __forceinline__ void store_tile_rows(const float *tile, uint16_t *out, int64_t ld, int64_t m0, int n0,
-                                                int64_t rows_valid, F &&fn) {
-  const int t = threadIdx.x;
-  const int cg = t & 15;
-  for (int rr = t >> 4; rr < kBM; rr += kThreads / 16) {
-    if (m0 + rr >= rows_valid) break;
-    uint16_t v[8];
+__device__ __forceinline__ void acc_to_wtile(const f32x16 (&acc)[4][4], char *wtile, int lane, F &&fn) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = f2bf(fn(tile[(cg * 8 + e) * kTileStride + rr]));
-    uint4 pk;
-    pk.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
-    pk.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
-    pk.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
-    pk.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
-    *reinterpret_cast<uint4 *>(out + (size_t)(m0 + rr) * ld + n0 + cg * 8) = pk;
-  }
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) put(wtile, acc_row(mb, v, lane), nb * 32 + (lane & 31), f2bf(fn(acc[mb][nb][v])));
 }
 
-__global__ __launch_bounds__(kThreads) void k_dequant(DeqP P) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kLdsBytes];
-  uint16_t *lds = reinterpret_cast<uint16_t *>(lds_raw);
+struct Identity {
+  __device__ float operator()(float x) const { return x; }
+};
+
+__global__ __launch_bounds__(kThreads, 1) void k_dequant(DeqP P) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
   if (wg_stop(P.status)) return;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM;
-  const int n0 = blockIdx.x * kBN;
-  const int lr = threadIdx.x >> 3;
-  Src A, B;
+  int mt, nt;
+  tile_of(blockIdx.x, P.n_mt * P.n_nt, P.n_nt, mt, nt);
+  const int64_t m0 = (int64_t)mt * kBM;
+  const int n0 = nt * kBN;
+  Operand A, B;
+  A.base0 = A.base1 = reinterpret_cast<const char *>(P.E);
+  B.base0 = B.base1 = reinterpret_cast<const char *>(P.H);
+  A.rb0 = A.rb1 = B.rb0 = B.rb1 = kEmb * 2;
   A.split = B.split = kEmb / kBK;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t j = min<int64_t>(m0 + lr + 32 * u, P.N - 1);
-    A.p0[u] = A.p1[u] = P.E + (size_t)clamp_tok(P.tok, P.keep_head + j, P.vocab, P.status) * kEmb;
-    B.p0[u] = B.p1[u] = P.H + (size_t)(n0 + lr + 32 * u) * kEmb;
+  for (int i = 0; i < 8; ++i) {
+    const int64_t j = min<int64_t>(m0 + staged_row(i), P.N - 1);
+    A.row[i] = (uint32_t)clamp_tok(P.tok, P.keep_head + j, P.vocab, P.status);
+    B.row[i] = (uint32_t)(n0 + staged_row(i));
   }
-  f32x4 acc[4][4];
+  f32x16 acc[4][4];
   mainloop(A, B, kEmb / kBK, acc, lds);
-  float *tile = reinterpret_cast<float *>(lds_raw);
-  acc_to_tile(acc, tile);
-  __syncthreads();
 
-  const int col = threadIdx.x & 127, half = threadIdx.x >> 7;
-  const int c = n0 + col;
-  const int r = P.rank[c];
-  const float step = P.step[c], a = P.nbr[c];
-  float *tc = tile + col * kTileStride;
-  const int64_t mt = blockIdx.y;
-  uint32_t symw[16];
-#pragma unroll 4
-  for (int qd = 0; qd < 16; ++qd) {
-    const int rq = half * 64 + qd * 4;
-    const int64_t j0 = m0 + rq;
-    const uint32_t w = (r >= 0 && j0 < P.N)
-                           ? P.sym32[((size_t)(r >> 6) * (P.N256 / 4) + (j0 >> 2)) * 64 + (r & 63)]
-                           : 0x7F7F7F7Fu;  // code 0
-    symw[qd] = w;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t wrow0 = m0 + wm * 128;
+  int r_nb[4], c_nb[4];
+  float st_nb[4], a_nb[4];
 #pragma unroll
-    for (int e = 0; e < 4; e += 2) {
-      const int64_t j = j0 + e;
-      if (j < P.N) {
-        const float q = r >= 0 ? code_of(P, w, e, j, r) : 0.f;
-        tc[rq + e] = tc[rq + e] + q * step;
-      } else {
-        tc[rq + e] = 0.f;
+  for (int nb = 0; nb < 4; ++nb) {
+    const int c = n0 + wn * 128 + nb * 32 + (lane & 31);
+    c_nb[nb] = c;
+    r_nb[nb] = P.rank[c];
+    st_nb[nb] = P.step[c];
+    a_nb[nb] = P.nbr[c];
+  }
+  uint32_t symw[4][4][4];
+  // pass 1: even rows, yhat = mu + q step
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
+        const int r = r_nb[nb];
+        const uint32_t w = (r >= 0 && j0 < P.N)
+                               ? P.sym32[((size_t)(r >> 6) * (P.N256 / 4) + (j0 >> 2)) * 64 + (r & 63)]
+                               : 0x7F7F7F7Fu;  // code 0
+        symw[mb][nb][g] = w;
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const int v = 4 * g + i;
+          if (j0 + i < P.N) {
+            const float q = r >= 0 ? code_of(P, w, i, j0 + i, r) : 0.f;
+            acc[mb][nb][v] = acc[mb][nb][v] + q * st_nb[nb];
+          } else {
+            acc[mb][nb][v] = 0.f;
+          }
+        }
       }
+  float *xch = reinterpret_cast<float *>(lds + kXchOff);
+  if (lane < 32) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      xch[wm * 256 + wn * 128 + nb * 32 + lane] = acc[0][nb][0];
+      if (wm == 0) P.halo_b[(int64_t)mt * kC + c_nb[nb]] = acc[0][nb][0];
     }
   }
   __syncthreads();
-  if (half == 0) P.halo_b[mt * kC + c] = tc[0];
-  // odd rows read only even rows, so they may be overwritten in place
-#pragma unroll 4
-  for (int qd = 0; qd < 16; ++qd) {
-    const int rq = half * 64 + qd * 4;
-    const int64_t j0 = m0 + rq;
-    const uint32_t w = symw[qd];
+  const bool defer_last = m0 + kBM < P.N;
+  // pass 2: odd rows read only even rows, so they are overwritten in place
 #pragma unroll
-    for (int e = 1; e < 4; e += 2) {
-      const int row = rq + e;
-      const int64_t j = j0 + e;
-      if (j >= P.N) {
-        tc[row] = 0.f;
-        continue;
-      }
-      const float q = r >= 0 ? code_of(P, w, e, j, r) : 0.f;
-      const float prev = tc[row - 1];
-      if (row == kBM - 1 && j + 1 < P.N) {
-        P.halo_a[mt * kC + c] = tc[row] + a * prev + q * step;  // finished by the fix-up
-      } else {
-        const float next = row + 1 < kBM ? tc[row + 1] : 0.f;
-        tc[row] = tc[row] + a * (prev + next) + q * step;
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const float ext = wm == 0 ? xch[256 + wn * 128 + nb * 32 + (lane & 31)] : 0.f;
+      const float a = a_nb[nb];
+      const int r = r_nb[nb];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float next3 = next_quad_row0(acc, mb, nb, g, ext, lane);
+        const uint32_t w = symw[mb][nb][g];
+        const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
+        const float y0 = acc[mb][nb][4 * g], y2 = acc[mb][nb][4 * g + 2];
+        if (j0 + 1 < P.N) {
+          const float q = r >= 0 ? code_of(P, w, 1, j0 + 1, r) : 0.f;
+          acc[mb][nb][4 * g + 1] = acc[mb][nb][4 * g + 1] + a * (y0 + y2) + q * st_nb[nb];
+        } else {
+          acc[mb][nb][4 * g + 1] = 0.f;
+        }
+        if (j0 + 3 < P.N) {
+          const float q = r >= 0 ? code_of(P, w, 3, j0 + 3, r) : 0.f;
+          if (wm == 1 && mb == 3 && g == 3 && lane >= 32 && defer_last)
+            P.halo_a[(int64_t)mt * kC + c_nb[nb]] = acc[mb][nb][4 * g + 3] + a * y2 + q * st_nb[nb];
+          else
+            acc[mb][nb][4 * g + 3] = acc[mb][nb][4 * g + 3] + a * (y2 + next3) + q * st_nb[nb];
+        } else {
+          acc[mb][nb][4 * g + 3] = 0.f;
+        }
       }
     }
-  }
-  __syncthreads();
-  store_tile_rows(tile, P.yhat_b, kC, m0, n0, P.N, [](float v) { return v; });
+  // bf16 yhat rows through LDS (the exchange area lies beyond the wave tiles)
+  char *wtile = lds + wave * kOutWaveBytes;
+  acc_to_wtile(acc, wtile, lane, Identity());
+  wave_lds_sync();
+  const int64_t col_lo = n0 + wn * 128;
+  flush_rows(wtile, P.yhat_b, kC, wrow0, col_lo, col_lo + 64, P.N);
 }
 
 __global__ void k_decode_fixup(DeqP P, int64_t n_fix) {
@@ -496,30 +635,34 @@ struct W1P {
   const uint16_t *yhat_b, *W1;
   uint16_t *h_b;  // [NM][256]
   int64_t N;
-  const int32_t *status;
+  int n_mt;
+  int32_t *status;
 };
 
-__global__ __launch_bounds__(kThreads) void k_w1(W1P P) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kLdsBytes];
-  uint16_t *lds = reinterpret_cast<uint16_t *>(lds_raw);
+__global__ __launch_bounds__(kThreads, 1) void k_w1(W1P P) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
   if (wg_stop(P.status)) return;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM;
-  const int n0 = blockIdx.x * kBN;
-  const int lr = threadIdx.x >> 3;
-  Src A, B;
+  int mt, nt;
+  tile_of(blockIdx.x, P.n_mt, 1, mt, nt);
+  const int64_t m0 = (int64_t)mt * kBM;
+  Operand A, B;
+  A.base0 = A.base1 = reinterpret_cast<const char *>(P.yhat_b);
+  B.base0 = B.base1 = reinterpret_cast<const char *>(P.W1);
+  A.rb0 = A.rb1 = B.rb0 = B.rb1 = kC * 2;
   A.split = B.split = kC / kBK;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    A.p0[u] = A.p1[u] = P.yhat_b + (size_t)(m0 + lr + 32 * u) * kC;
-    B.p0[u] = B.p1[u] = P.W1 + (size_t)(n0 + lr + 32 * u) * kC;
+  for (int i = 0; i < 8; ++i) {
+    A.row[i] = (uint32_t)(m0 + staged_row(i));
+    B.row[i] = (uint32_t)staged_row(i);
   }
-  f32x4 acc[4][4];
+  f32x16 acc[4][4];
   mainloop(A, B, kC / kBK, acc, lds);
-  float *tile = reinterpret_cast<float *>(lds_raw);
-  acc_to_tile(acc, tile);
-  __syncthreads();
-  store_tile_rows(tile, P.h_b, kHid, m0, n0, P.N,
-                  [](float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); });
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  char *wtile = lds + wave * kOutWaveBytes;
+  acc_to_wtile(acc, wtile, lane, [](float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); });
+  wave_lds_sync();
+  flush_rows(wtile, P.h_b, kHid, m0 + wm * 128, wn * 128, wn * 128 + 64, P.N);
 }
 
 // ---------------------------------------------------------------------------
@@ -530,80 +673,80 @@ struct SynP {
   const float2 *rope_lo, *rope_hi;  // [256][128], [ceil(T/256)][128]: (cos, sin)
   uint16_t *out;                     // rows_out [T][D]
   int64_t N;
-  int keep_head;
-  const int32_t *status;
+  int keep_head, n_mt, n_nt;
+  int32_t *status;
 };
 
-// GEMM column n of tile nt -> output dim.  Tile nt covers head nt/2 (256
-// dims) and the pair-aligned halves d0 + [0,64) and d0 + 128 + [0,64), with
-// d0 = 64 * (nt % 2), so a rotate-half pair (d, d+128) stays in one tile.
-__device__ __forceinline__ int syn_dim(int nt, int n) {
-  return (nt >> 1) * kHeadDim + (nt & 1) * 64 + n + (n >= 64 ? 64 : 0);
+// Tile nt covers head nt (256 dims).  Wave column half wn, block nb < 2 holds
+// dims 64 wn + 32 nb + [0, 32); block nb + 2 holds the same dims + 128, so a
+// rotate-half pair (d, d + 128) is one lane's register v of blocks nb, nb + 2.
+__device__ __forceinline__ int syn_dim(int n) {
+  const int wn = n >> 7, nb = (n >> 5) & 3, j = n & 31;
+  return (nb >> 1) * 128 + 64 * wn + 32 * (nb & 1) + j;
 }
 
-__global__ __launch_bounds__(kThreads) void k_synthesis(SynP P) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kLdsBytes];
-  uint16_t *lds = reinterpret_cast<uint16_t *>(lds_raw);
+__global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
   if (wg_stop(P.status)) return;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM;
-  const int nt = blockIdx.x;
-  const int lr = threadIdx.x >> 3;
-  Src A, B;
+  int mt, nt;
+  tile_of(blockIdx.x, P.n_mt * P.n_nt, P.n_nt, mt, nt);
+  const int64_t m0 = (int64_t)mt * kBM;
+  const int head = nt;
+  Operand A, B;
+  A.base0 = reinterpret_cast<const char *>(P.yhat_b);
+  A.base1 = reinterpret_cast<const char *>(P.h_b);
+  B.base0 = reinterpret_cast<const char *>(P.S);
+  B.base1 = reinterpret_cast<const char *>(P.W2);
+  A.rb0 = B.rb0 = kC * 2;
+  A.rb1 = B.rb1 = kHid * 2;
   A.split = B.split = kC / kBK;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t j = m0 + lr + 32 * u;
-    A.p0[u] = P.yhat_b + (size_t)j * kC;
-    A.p1[u] = P.h_b + (size_t)j * kHid;
-    const int dim = syn_dim(nt, lr + 32 * u);
-    B.p0[u] = P.S + (size_t)dim * kC;
-    B.p1[u] = P.W2 + (size_t)dim * kHid;
+  for (int i = 0; i < 8; ++i) {
+    A.row[i] = (uint32_t)(m0 + staged_row(i));
+    B.row[i] = (uint32_t)(head * kHeadDim + syn_dim(staged_row(i)));
   }
-  f32x4 acc[4][4];
+  f32x16 acc[4][4];
   mainloop(A, B, (kC + kHid) / kBK, acc, lds);
-  float *tile = reinterpret_cast<float *>(lds_raw);
-  acc_to_tile(acc, tile);
-  __syncthreads();
 
-  const int head = nt >> 1;
-  const bool is_key = (head & 3) < 2;  // per layer: 2 key heads then 2 value heads
-  const int d0 = (nt & 1) * 64;
-  const int t = threadIdx.x;
-  const int pg = t & 7;  // 8 pairs per thread
-  for (int rr = t >> 3; rr < kBM; rr += kThreads / 8) {
-    const int64_t j = m0 + rr;
-    if (j >= P.N) break;
-    const int64_t pos = P.keep_head + j;
-    uint16_t lo_v[8], hi_v[8];
-    if (is_key) {
-      const float2 *tl = P.rope_lo + (size_t)(pos & 255) * kHalf + d0 + pg * 8;
-      const float2 *th = P.rope_hi + (size_t)(pos >> 8) * kHalf + d0 + pg * 8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool is_key = (head & 3) < 2;  // per layer: 2 key heads, then 2 value heads
+  const int64_t wrow0 = m0 + wm * 128;
+  char *wtile = lds + wave * kOutWaveBytes;
+  if (is_key) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 a = tl[e], b = th[e];
-        const float cs = b.x * a.x - b.y * a.y;
-        const float sn = b.y * a.x + b.x * a.y;
-        const float x0 = tile[(pg * 8 + e) * kTileStride + rr];
-        const float x1 = tile[(64 + pg * 8 + e) * kTileStride + rr];
-        lo_v[e] = f2bf(x0 * cs - x1 * sn);
-        hi_v[e] = f2bf(x1 * cs + x0 * sn);
-      }
-    } else {
+    for (int nb = 0; nb < 2; ++nb) {
+      const int f = 64 * wn + 32 * nb + (lane & 31);  // rotary frequency index
+      const float2 w1 = P.rope_lo[kHalf + f];          // (cos w_f, sin w_f): one position step
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        lo_v[e] = f2bf(tile[(pg * 8 + e) * kTileStride + rr]);
-        hi_v[e] = f2bf(tile[(64 + pg * 8 + e) * kTileStride + rr]);
-      }
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          // rows past the end are not stored; their angle is clamped in range
+          const int64_t pos = P.keep_head + min<int64_t>(wrow0 + acc_row(mb, 4 * g, lane), P.N - 1);
+          const float2 a = P.rope_lo[(size_t)(pos & 255) * kHalf + f];
+          const float2 b = P.rope_hi[(size_t)(pos >> 8) * kHalf + f];
+          float cs = b.x * a.x - b.y * a.y;
+          float sn = b.y * a.x + b.x * a.y;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int v = 4 * g + i;
+            const float x0 = acc[mb][nb][v], x1 = acc[mb][nb + 2][v];
+            const int row = acc_row(mb, v, lane);
+            put(wtile, row, nb * 32 + (lane & 31), f2bf(x0 * cs - x1 * sn));
+            put(wtile, row, (nb + 2) * 32 + (lane & 31), f2bf(x1 * cs + x0 * sn));
+            const float c2 = cs * w1.x - sn * w1.y;  // advance the angle by one position
+            sn = sn * w1.x + cs * w1.y;
+            cs = c2;
+          }
+        }
     }
-    uint16_t *o = P.out + (size_t)pos * kD + head * kHeadDim + d0 + pg * 8;
-    uint4 a4, b4;
-    a4.x = lo_v[0] | ((uint32_t)lo_v[1] << 16); a4.y = lo_v[2] | ((uint32_t)lo_v[3] << 16);
-    a4.z = lo_v[4] | ((uint32_t)lo_v[5] << 16); a4.w = lo_v[6] | ((uint32_t)lo_v[7] << 16);
-    b4.x = hi_v[0] | ((uint32_t)hi_v[1] << 16); b4.y = hi_v[2] | ((uint32_t)hi_v[3] << 16);
-    b4.z = hi_v[4] | ((uint32_t)hi_v[5] << 16); b4.w = hi_v[6] | ((uint32_t)hi_v[7] << 16);
-    *reinterpret_cast<uint4 *>(o) = a4;
-    *reinterpret_cast<uint4 *>(o + kHalf) = b4;
+  } else {
+    acc_to_wtile(acc, wtile, lane, Identity());
   }
+  wave_lds_sync();
+  const int64_t hb = (int64_t)head * kHeadDim;
+  flush_rows(wtile, P.out + (size_t)P.keep_head * kD, kD, wrow0, hb + 64 * wn, hb + 128 + 64 * wn, P.N);
 }
 
 // ---------------------------------------------------------------------------
@@ -661,6 +804,15 @@ __global__ void k_kept_rope(const uint8_t *stream, const float2 *lo, const float
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+template <class K, class P>
+static void launch_gemm(K kernel, const char *name, int grid, const P &prm, hipStream_t s) {
+  // dynamic LDS above 64 KiB has to be allowed per kernel
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kLdsBytes);
+  KernelTimer tm(name, s);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), kLdsBytes, s, prm);
+}
+
 void launch_mean_gemm(const EncodeArgs &a) {
   if (a.g.N == 0 || a.p->C_a == 0) return;
   MeanEncP P;
@@ -670,13 +822,12 @@ void launch_mean_gemm(const EncodeArgs &a) {
   P.act = a.p->dev.act;
   P.mean = reinterpret_cast<float *>(a.ws + a.l.mean);
   P.N = a.g.N;
-  P.Ca4 = a.g.Ca4;
+  P.n_mt = (int)a.g.n_mtiles;
+  P.n_nt = (int)(a.g.Ca4 / kBN);
   P.keep_head = a.p->keep_head;
   P.vocab = a.p->vocab;
   P.status = a.status;
-  dim3 grid((unsigned)(a.g.Ca4 / kBN), (unsigned)a.g.n_mtiles);
-  KernelTimer tm("mean_gemm", a.s);
-  hipLaunchKernelGGL(k_mean_enc, grid, dim3(kThreads), 0, a.s, P);
+  launch_gemm(k_mean_enc, "mean_gemm", P.n_mt * P.n_nt, P, a.s);
 }
 
 static QuantP quant_params(const EncodeArgs &a) {
@@ -686,7 +837,7 @@ static QuantP quant_params(const EncodeArgs &a) {
   P.act = a.p->dev.act;
   P.step = a.p->dev.step;
   P.nbr = a.p->dev.nbr;
-  P.mean = reinterpret_cast<const float *>(a.ws + a.l.mean);
+  P.mean = reinterpret_cast<float *>(a.ws + a.l.mean);
   P.sym32 = reinterpret_cast<uint32_t *>(a.ws + a.l.sym);
   P.esc_raw = reinterpret_cast<uint32_t *>(a.ws + a.l.esc_raw);
   P.ws = a.ws;
@@ -694,11 +845,12 @@ static QuantP quant_params(const EncodeArgs &a) {
   P.halo_b = reinterpret_cast<float *>(a.ws + a.l.halo_b);
   P.N = a.g.N;
   P.N256 = a.g.N256;
-  P.Ca4 = a.g.Ca4;
   P.esc_cap = a.g.esc_cap;
   P.Ca = a.p->C_a;
   P.keep_head = a.p->keep_head;
   P.C = a.p->C;
+  P.n_mt = (int)a.g.n_mtiles;
+  P.n_nt = (int)(a.g.Ca4 / kBN);
   P.status = a.status;
   return P;
 }
@@ -706,9 +858,7 @@ static QuantP quant_params(const EncodeArgs &a) {
 void launch_analysis_gemm(const EncodeArgs &a) {
   if (a.g.N == 0 || a.p->C_a == 0) return;
   QuantP P = quant_params(a);
-  dim3 grid((unsigned)(a.g.Ca4 / kBN), (unsigned)a.g.n_mtiles);
-  KernelTimer tm("analysis_gemm", a.s);
-  hipLaunchKernelGGL(k_analysis_quant, grid, dim3(kThreads), 0, a.s, P);
+  launch_gemm(k_analysis_quant, "analysis_gemm", P.n_mt * P.n_nt, P, a.s);
 }
 
 void launch_encode_fixup(const EncodeArgs &a) {
@@ -747,6 +897,8 @@ static DeqP deq_params(const DecodeArgs &a) {
   P.Ca = a.p->C_a;
   P.keep_head = a.p->keep_head;
   P.vocab = a.p->vocab;
+  P.n_mt = (int)a.g.n_mtiles;
+  P.n_nt = kC / kBN;
   P.status = a.status;
   return P;
 }
@@ -754,9 +906,7 @@ static DeqP deq_params(const DecodeArgs &a) {
 void launch_dequant_gemm(const DecodeArgs &a) {
   if (a.g.N == 0) return;
   DeqP P = deq_params(a);
-  dim3 grid((unsigned)(kC / kBN), (unsigned)a.g.n_mtiles);
-  KernelTimer tm("dequant_gemm", a.s);
-  hipLaunchKernelGGL(k_dequant, grid, dim3(kThreads), 0, a.s, P);
+  launch_gemm(k_dequant, "dequant_gemm", P.n_mt * P.n_nt, P, a.s);
 }
 
 void launch_decode_fixup(const DecodeArgs &a) {
@@ -776,10 +926,9 @@ void launch_w1_gemm(const DecodeArgs &a) {
   P.W1 = a.p->W1;
   P.h_b = reinterpret_cast<uint16_t *>(a.ws + a.l.h_b);
   P.N = a.g.N;
+  P.n_mt = (int)a.g.n_mtiles;
   P.status = a.status;
-  dim3 grid((unsigned)(kHid / kBN), (unsigned)a.g.n_mtiles);
-  KernelTimer tm("w1_gemm", a.s);
-  hipLaunchKernelGGL(k_w1, grid, dim3(kThreads), 0, a.s, P);
+  launch_gemm(k_w1, "w1_gemm", P.n_mt, P, a.s);
 }
 
 void launch_synthesis_gemm(const DecodeArgs &a) {
@@ -794,10 +943,10 @@ void launch_synthesis_gemm(const DecodeArgs &a) {
   P.out = a.rows_out;
   P.N = a.g.N;
   P.keep_head = a.p->keep_head;
+  P.n_mt = (int)a.g.n_mtiles;
+  P.n_nt = kD / kBN;
   P.status = a.status;
-  dim3 grid((unsigned)(kD / kBN), (unsigned)a.g.n_mtiles);
-  KernelTimer tm("synthesis_gemm", a.s);
-  hipLaunchKernelGGL(k_synthesis, grid, dim3(kThreads), 0, a.s, P);
+  launch_gemm(k_synthesis, "synthesis_gemm", P.n_mt * P.n_nt, P, a.s);
 }
 
 void launch_kept_rope(const DecodeArgs &a) {

@@ -28,6 +28,7 @@ constexpr int kTabStride = 257;   // u32 per table row in LDS: spreads equal sym
 constexpr int kEncWaves = 16;     // groups (waves) per encoder workgroup, one component group
 constexpr int kDecWaves = 16;
 constexpr int kWordBuf = 1024;    // u16 words cached per decoder wave
+constexpr int kBktStride = kBuckets + 4;  // bytes per bucket row in LDS (65 dwords: rows on distinct banks)
 
 __device__ __forceinline__ void set_status(int32_t *st, int code) { atomicCAS(st, 0, code); }
 
@@ -330,7 +331,7 @@ __device__ __forceinline__ void wave_sync_lds() {
 
 __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
   __shared__ uint32_t tab[kLanes * kTabStride];
-  __shared__ uint8_t bkt[kLanes * kBuckets];
+  __shared__ uint8_t bkt[kLanes * kBktStride];
   __shared__ uint16_t wbuf[kDecWaves][kWordBuf];
   __shared__ unsigned long long ebits[kDecWaves][kBlock];
   const int g = blockIdx.y;
@@ -339,8 +340,10 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
     const int l = idx >> 8, s = idx & 255;
     tab[l * kTabStride + s] = P.tab[(size_t)(kLanes * g + l) * 256 + s];
   }
-  for (int idx = threadIdx.x; idx < n * kBuckets; idx += blockDim.x)
-    bkt[idx] = P.bucket[(size_t)kLanes * g * kBuckets + idx];
+  for (int idx = threadIdx.x; idx < n * kBuckets; idx += blockDim.x) {
+    const int l = idx / kBuckets, bb = idx - l * kBuckets;
+    bkt[l * kBktStride + bb] = P.bucket[(size_t)kLanes * g * kBuckets + idx];
+  }
   __syncthreads();
   if (*P.status != 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -397,7 +400,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
   if (lane_ok) x = (uint32_t)wb[2 * lane] | ((uint32_t)wb[2 * lane + 1] << 16);
   uint32_t ptr = 2u * (uint32_t)n;
   const uint32_t *mytab = tab + lane * kTabStride;
-  const uint8_t *mybkt = bkt + lane * kBuckets;
+  const uint8_t *mybkt = bkt + lane * kBktStride;
   const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   uint32_t *sout = P.sym32 + ((size_t)g * (P.N256 / 4) + (size_t)b * 64) * 64 + lane;
   bool overrun = false;
@@ -409,12 +412,16 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
     bool need = false;
     if (act) {
       const uint32_t slot = x & (kM - 1u);
-      uint32_t sy = mybkt[slot >> kBucketShift];
-      uint32_t e = mytab[sy];
-      while (sy < 254u && (mytab[sy + 1] >> 16) <= slot) {
-        ++sy;
-        e = mytab[sy];
+      // the symbol lies between the first symbols of this bucket and the next
+      const uint32_t bi = slot >> kBucketShift;
+      uint32_t lo = mybkt[bi];
+      uint32_t hi = bi + 1 < (uint32_t)kBuckets ? (uint32_t)mybkt[bi + 1] : (uint32_t)(kNSym - 1);
+      while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        if ((mytab[mid] >> 16) <= slot) lo = mid; else hi = mid - 1;
       }
+      const uint32_t sy = lo;
+      const uint32_t e = mytab[sy];
       x = (e & 0xFFFFu) * (x >> kPrecBits) + slot - (e >> 16);
       s = sy;
       need = x < kL;
