@@ -17,10 +17,14 @@
 // owns a 256x256 tile; each wave a 128x128 sub-tile held as 4x4 blocks of
 // v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane); the 32x32 form
 // keeps the matrix cores busy with a single wave per SIMD.  Operand tiles of
-// 256 rows x 64 k are copied global -> LDS by the direct 16-byte LDS loads of
-// gfx950 (no register staging), double buffered, in an XOR-swizzled layout
-// (16-byte chunk c of row r stored at chunk c ^ (r & 7)) so the fragment reads
-// of 8 consecutive rows hit 8 distinct bank groups.  Workgroups are mapped to
+// 256 rows x 32 k are copied global -> LDS by the direct 16-byte LDS loads of
+// gfx950 (no register staging) into a ring of 4 stages, so three tiles of
+// loads are in flight while one is consumed; a wave waits only for the loads
+// of the tile it is about to read (s_waitcnt vmcnt(n), then a bare barrier).
+// Rows are 64 bytes (4 chunks of 16 B); chunk c of row r is stored at
+// c ^ ((r >> 2) & 3), so the 16 lanes served together by one LDS pass read 16
+// distinct 16-byte bank groups.  Fragments of the next k-step are read from
+// LDS while the current k-step's MFMAs run.  Workgroups are mapped to
 // tiles so that the tiles of one row band run on the same XCD (the hardware
 // deals workgroups to the 8 XCDs round robin), which keeps a band's token rows
 // in that XCD's L2 while all its weight tiles stream past.
@@ -58,13 +62,15 @@ typedef const void __attribute__((address_space(1))) *gptr_t;
 typedef void __attribute__((address_space(3))) *lptr_t;
 
 constexpr int kThreads = 256;
-constexpr int kRowBytes = kBK * 2;                        // 128 B per staged row
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 64 KiB per stage
+constexpr int kStages = 4;
+constexpr int kRowBytes = kBK * 2;                        // 64 B per staged row
+constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 32 KiB per stage
+constexpr int kLoadsPerTile = 8;                          // direct LDS loads per wave per k-tile
 constexpr int kOutStride = 128 + 8;                       // bf16 per row of a wave's output tile
 constexpr int kOutWaveBytes = 128 * kOutStride * 2;
 constexpr int kXchOff = 4 * kOutWaveBytes;                // row-0 exchange between the two wave rows
 constexpr int kLdsBytes = kXchOff + 2 * 256 * 4;
-static_assert(2 * kStageBytes <= kXchOff, "stages must not overlap the exchange area");
+static_assert(kStages * kStageBytes <= kXchOff, "stages must not overlap the exchange area");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
 constexpr float kQLimit = 2147483520.0f;  // largest float below 2^31
 
@@ -105,27 +111,88 @@ struct Operand {
   const char *base0, *base1;  // two k-ranges (k-tiles [0, split) and the rest)
   uint32_t rb0, rb1;          // row bytes of each source
   int split;
-  uint32_t row[8];            // source rows staged by this lane: tile rows wave*64 + 8i + lane/8
+  uint32_t row[4];            // source rows staged by this lane: tile rows wave*64 + 16i + lane/4
 };
 
+// One k-tile of one operand (256 rows x 32 k) into an LDS stage: 4 direct
+// loads per wave, each writing 1 KiB = 16 rows; lane l fills physical chunk
+// l & 3 of row l / 4, which holds logical chunk (l & 3) ^ ((row >> 2) & 3).
 __device__ __forceinline__ void stage_tile(const Operand &op, int kt, char *dst_region, int wave, int lane) {
-  const uint32_t chunk = (uint32_t)(((lane & 7) ^ ((lane >> 3) & 7)) << 4);
+  const uint32_t chunk = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
   const bool s0 = kt < op.split;
   const char *base = s0 ? op.base0 : op.base1;
   const uint32_t rb = s0 ? op.rb0 : op.rb1;
   const uint32_t ko = (uint32_t)(s0 ? kt : kt - op.split) * kRowBytes + chunk;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const char *src = base + (size_t)op.row[i] * rb + ko;
-    char *dst = dst_region + (wave * 64 + i * 8) * kRowBytes;
+    char *dst = dst_region + (wave * 64 + i * 16) * kRowBytes;
     __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
   }
 }
 
 __device__ __forceinline__ bf16x8 frag(const char *region, int row, int c) {
-  return *reinterpret_cast<const bf16x8 *>(region + row * kRowBytes + ((c ^ (row & 7)) << 4));
+  return *reinterpret_cast<const bf16x8 *>(region + row * kRowBytes + ((c ^ ((row >> 2) & 3)) << 4));
 }
 
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+
+__device__ __forceinline__ void read_frags(Frags &f, const char *stage, int ks, int lane, int wm, int wn) {
+  const int c = ks * 2 + (lane >> 5);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) f.a[mb] = frag(stage, wm * 128 + mb * 32 + (lane & 31), c);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) f.b[nb] = frag(stage + kBM * kRowBytes, wn * 128 + nb * 32 + (lane & 31), c);
+}
+
+__device__ __forceinline__ void mma(f32x16 (&acc)[4][4], const Frags &f) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], f.b[nb], acc[mb][nb], 0, 0, 0);
+}
+
+// Wait until at most two k-tiles of this wave's direct loads are still in
+// flight and all of its LDS reads are done, then meet the other waves.
+// s_waitcnt fields: vmcnt[3:0] and [15:14], expcnt[6:4] (7 = no wait),
+// lgkmcnt[11:8] (0 = wait).
+__device__ __forceinline__ void tile_barrier() {
+  constexpr int n = 2 * kLoadsPerTile;
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((n & 15) | 0x70 | ((n >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Instruction order inside one k-step: the 16 MFMAs alternate with the
+// 8 LDS reads of the next k-step and, when given, the 8 direct loads of a
+// later k-tile, so the matrix cores never wait for an LDS round trip.
+// (sched_group_barrier masks: 0x008 MFMA, 0x100 DS read, 0x020 VMEM read.)
+__device__ __forceinline__ void interleave(bool with_loads) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  if (with_loads) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  }
+}
+
+// Ring of kStages LDS stages; k-tile t lives in stage t % kStages.  Every
+// iteration issues the loads of k-tile kt + 3 (clamped to the last tile, so
+// the loop body is uniform and the wait count constant), consumes k-tile kt
+// in two k-steps and, between them, waits for k-tile kt + 1.
+template <bool kPinAcc = true>
 __device__ __forceinline__ void mainloop(const Operand &A, const Operand &B, int KT, f32x16 (&acc)[4][4],
                                          char *lds) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -134,35 +201,57 @@ __device__ __forceinline__ void mainloop(const Operand &A, const Operand &B, int
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-  stage_tile(A, 0, lds, wave, lane);
-  stage_tile(B, 0, lds + kBM * kRowBytes, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const char *cur = lds + (kt & 1) * kStageBytes;
-    if (kt + 1 < KT) {
-      char *nxt = lds + ((kt + 1) & 1) * kStageBytes;
-      stage_tile(A, kt + 1, nxt, wave, lane);
-      stage_tile(B, kt + 1, nxt + kBM * kRowBytes, wave, lane);
-    }
-    const char *sa = cur, *sb = cur + kBM * kRowBytes;
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int c = ks * 2 + (lane >> 5);
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) a[mb] = frag(sa, wm * 128 + mb * 32 + (lane & 31), c);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) b[nb] = frag(sb, wn * 128 + nb * 32 + (lane & 31), c);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  for (int t = 0; t < kStages - 1; ++t) {
+    const int tt = t < KT ? t : KT - 1;
+    stage_tile(A, tt, lds + t * kStageBytes, wave, lane);
+    stage_tile(B, tt, lds + t * kStageBytes + kBM * kRowBytes, wave, lane);
   }
+  tile_barrier();
+  Frags f0, f1;
+  read_frags(f0, lds, 0, lane, wm, wn);
+#pragma unroll 1
+  for (int kt = 0; kt < KT; ++kt) {
+    const char *cur = lds + (kt % kStages) * kStageBytes;
+    // the stage of k-tile kt + 3 held k-tile kt - 1, released by the last barrier
+    char *nxt = lds + ((kt + kStages - 1) % kStages) * kStageBytes;
+    const int tl = kt + kStages - 1 < KT ? kt + kStages - 1 : KT - 1;
+    mma(acc, f0);
+    read_frags(f1, cur, 1, lane, wm, wn);
+    stage_tile(A, tl, nxt, wave, lane);
+    stage_tile(B, tl, nxt + kBM * kRowBytes, wave, lane);
+    interleave(true);
+    tile_barrier();
+    mma(acc, f1);
+    read_frags(f0, lds + ((kt + 1) % kStages) * kStageBytes, 0, lane, wm, wn);
+    interleave(false);
+  }
+  __syncthreads();
+  // The accumulators leave the loop in AGPRs; epilogues copy them to VGPRs one
+  // block at a time (an epilogue that needs them in VGPRs would otherwise have
+  // all 256 copied at the loop exit, and the loop's own registers spilled).
+  if (kPinAcc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+  }
+}
+
+// One accumulator block in VGPRs, copied where it is used.
+__device__ __forceinline__ f32x16 acc_block(const f32x16 (&acc)[4][4], int mb, int nb) {
+  f32x16 b = acc[mb][nb];
+  asm volatile("" : "+v"(b));
+  return b;
+}
+
+// The lane id, opaque to the optimiser: epilogue address arithmetic derived
+// from it cannot be hoisted above the main loop, where it would hold
+// registers for the loop's whole duration.
+__device__ __forceinline__ int epilogue_lane() {
+  int l = threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
+  return l;
 }
 
 // Row (within the wave tile) of register v of block row mb in this lane.
@@ -186,7 +275,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 __device__ __forceinline__ void flush_rows(const char *wtile, uint16_t *out, int64_t ld, int64_t row0, int64_t col_lo,
                                            int64_t col_hi, int64_t rows_valid) {
-  const int lane = threadIdx.x & 63;
+  const int lane = epilogue_lane();
   const int seg = lane & 15;
   const int64_t col = seg < 8 ? col_lo + seg * 8 : col_hi + (seg - 8) * 8;
 #pragma unroll 4
@@ -211,7 +300,8 @@ __device__ __forceinline__ int clamp_tok(const int32_t *tok, int64_t t, int voca
   return v;
 }
 
-__device__ __forceinline__ int staged_row(int i) { return (threadIdx.x >> 6) * 64 + i * 8 + ((threadIdx.x & 63) >> 3); }
+// tile row staged by this lane in load i (0..3), matching stage_tile()
+__device__ __forceinline__ int staged_row(int i) { return (threadIdx.x >> 6) * 64 + i * 16 + ((threadIdx.x & 63) >> 2); }
 
 // tile-interleaved fp32 storage of one 256x256 tile: 64 bytes per lane per block
 __device__ __forceinline__ f32x4 *tiled_ptr(float *base, int64_t tile_id, int wave, int mb, int nb, int lane) {
@@ -243,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mean_enc(MeanEncP P) {
   A.rb0 = A.rb1 = B.rb0 = B.rb1 = kEmb * 2;
   A.split = B.split = kEmb / kBK;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const int64_t j = min<int64_t>(m0 + staged_row(i), P.N - 1);
     A.row[i] = (uint32_t)clamp_tok(P.tok, P.keep_head + j, P.vocab, P.status);
     B.row[i] = (uint32_t)P.act[n0 + staged_row(i)];
@@ -336,13 +426,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   A.rb0 = A.rb1 = B.rb0 = B.rb1 = kD * 2;
   A.split = B.split = kD / kBK;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const int64_t j = min<int64_t>(m0 + staged_row(i), P.N - 1);
     A.row[i] = (uint32_t)(P.keep_head + j);
     B.row[i] = (uint32_t)P.act[n0 + staged_row(i)];
   }
   f32x16 acc[4][4];
-  mainloop(A, B, kD / kBK, acc, lds);
+  mainloop<false>(A, B, kD / kBK, acc, lds);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -496,13 +586,17 @@ __device__ __forceinline__ float code_of(const DeqP &P, uint32_t w, int i, int64
 // bf16 of fn(value) for all 128x128 values of the wave into its LDS tile
 // (identity columns), one element at a time
 template <class F>
-__device__ __forceinline__ void acc_to_wtile(const f32x16 (&acc)[4][4], char *wtile, int lane, F &&fn) {
+__device__ __forceinline__ void acc_to_wtile(const f32x16 (&acc)[4][4], char *wtile, int, F &&fn) {
+  const int lane = epilogue_lane();
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < 4; ++nb) {
+      const f32x16 b = acc_block(acc, mb, nb);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) put(wtile, acc_row(mb, v, lane), nb * 32 + (lane & 31), f2bf(fn(acc[mb][nb][v])));
+      for (int v = 0; v < 16; ++v) put(wtile, acc_row(mb, v, lane), nb * 32 + (lane & 31), f2bf(fn(b[v])));
+      __builtin_amdgcn_sched_barrier(0);  // one block at a time: bounded live ranges
+    }
 }
 
 struct Identity {
@@ -522,7 +616,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dequant(DeqP P) {
   A.rb0 = A.rb1 = B.rb0 = B.rb1 = kEmb * 2;
   A.split = B.split = kEmb / kBK;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const int64_t j = min<int64_t>(m0 + staged_row(i), P.N - 1);
     A.row[i] = (uint32_t)clamp_tok(P.tok, P.keep_head + j, P.vocab, P.status);
     B.row[i] = (uint32_t)(n0 + staged_row(i));
@@ -651,7 +745,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_w1(W1P P) {
   A.rb0 = A.rb1 = B.rb0 = B.rb1 = kC * 2;
   A.split = B.split = kC / kBK;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     A.row[i] = (uint32_t)(m0 + staged_row(i));
     B.row[i] = (uint32_t)staged_row(i);
   }
@@ -701,7 +795,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
   A.rb1 = B.rb1 = kHid * 2;
   A.split = B.split = kC / kBK;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     A.row[i] = (uint32_t)(m0 + staged_row(i));
     B.row[i] = (uint32_t)(head * kHeadDim + syn_dim(staged_row(i)));
   }
@@ -719,7 +813,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
       const int f = 64 * wn + 32 * nb + (lane & 31);  // rotary frequency index
       const float2 w1 = P.rope_lo[kHalf + f];          // (cos w_f, sin w_f): one position step
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb) {
+        const f32x16 blo = acc_block(acc, mb, nb), bhi = acc_block(acc, mb, nb + 2);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           // rows past the end are not stored; their angle is clamped in range
@@ -731,7 +826,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int v = 4 * g + i;
-            const float x0 = acc[mb][nb][v], x1 = acc[mb][nb + 2][v];
+            const float x0 = blo[v], x1 = bhi[v];
             const int row = acc_row(mb, v, lane);
             put(wtile, row, nb * 32 + (lane & 31), f2bf(x0 * cs - x1 * sn));
             put(wtile, row, (nb + 2) * 32 + (lane & 31), f2bf(x1 * cs + x0 * sn));
@@ -740,6 +835,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
             cs = c2;
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   } else {
     acc_to_wtile(acc, wtile, lane, Identity());
