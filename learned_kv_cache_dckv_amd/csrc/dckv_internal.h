@@ -28,7 +28,7 @@ constexpr uint16_t kVersion = 1;
 // GEMM tiling shared by every transform kernel
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kBK = 32;
+constexpr int kBK = 64;
 
 // fixed shapes supported by the kernels
 constexpr int kD = 6144;

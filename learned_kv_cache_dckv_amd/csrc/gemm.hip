@@ -62,10 +62,9 @@ typedef const void __attribute__((address_space(1))) *gptr_t;
 typedef void __attribute__((address_space(3))) *lptr_t;
 
 constexpr int kThreads = 256;
-constexpr int kStages = 4;
-constexpr int kRowBytes = kBK * 2;                        // 64 B per staged row
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 32 KiB per stage
-constexpr int kLoadsPerTile = 8;                          // direct LDS loads per wave per k-tile
+constexpr int kStages = 2;
+constexpr int kRowBytes = kBK * 2;                        // 128 B per staged row
+constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 64 KiB per stage
 constexpr int kOutStride = 128 + 8;                       // bf16 per row of a wave's output tile
 constexpr int kOutWaveBytes = 128 * kOutStride * 2;
 constexpr int kXchOff = 4 * kOutWaveBytes;                // row-0 exchange between the two wave rows
@@ -107,38 +106,69 @@ __device__ __forceinline__ void tile_of(int b, int total, int n_nt, int &mt, int
 // ---------------------------------------------------------------------------
 // operand staging and the MFMA main loop
 // ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
 struct Operand {
-  const char *base0, *base1;  // two k-ranges (k-tiles [0, split) and the rest)
-  uint32_t rb0, rb1;          // row bytes of each source
+  const char *p0, *p1;  // two k-ranges (k-tiles [0, split) and the rest)
+  uint32_t rb0, rb1;    // row bytes of each source
   int split;
-  uint32_t row[4];            // source rows staged by this lane: tile rows wave*64 + 16i + lane/4
+  uint32_t row[8];      // source rows staged by this lane: tile rows wave*64 + 8i + lane/8
 };
 
-// One k-tile of one operand (256 rows x 32 k) into an LDS stage: 4 direct
-// loads per wave, each writing 1 KiB = 16 rows; lane l fills physical chunk
-// l & 3 of row l / 4, which holds logical chunk (l & 3) ^ ((row >> 2) & 3).
-__device__ __forceinline__ void stage_tile(const Operand &op, int kt, char *dst_region, int wave, int lane) {
-  const uint32_t chunk = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+__device__ __forceinline__ void set_sources(Operand &op, const void *p0, uint32_t rb0, const void *p1, uint32_t rb1,
+                                            int split) {
+  op.p0 = reinterpret_cast<const char *>(p0);
+  op.p1 = reinterpret_cast<const char *>(p1);
+  op.rb0 = rb0;
+  op.rb1 = rb1;
+  op.split = split;
+}
+
+// Where the loads of one k-tile of one operand come from: a buffer resource
+// over its source (no stride, full 32-bit range), the k offset (a scalar) and
+// the source's row bytes.  k-tiles at or past KT get a resource with no range,
+// so their loads move no data.
+struct TileSrc {
+  rsrc_t r;
+  uint32_t soff, rb;
+};
+
+__device__ __forceinline__ TileSrc tile_src(const Operand &op, int kt, int KT) {
   const bool s0 = kt < op.split;
-  const char *base = s0 ? op.base0 : op.base1;
-  const uint32_t rb = s0 ? op.rb0 : op.rb1;
-  const uint32_t ko = (uint32_t)(s0 ? kt : kt - op.split) * kRowBytes + chunk;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const char *src = base + (size_t)op.row[i] * rb + ko;
-    char *dst = dst_region + (wave * 64 + i * 16) * kRowBytes;
-    __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
-  }
+  // base and range are wave-uniform: keep them in scalar registers
+  const uint64_t b = reinterpret_cast<uint64_t>(s0 ? op.p0 : op.p1);
+  // (readfirstlane returns int: zero-extend each half, never sign-extend)
+  const uint64_t bu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b) |
+                      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32);
+  const int nrec = __builtin_amdgcn_readfirstlane(kt < KT ? -1 : 0);
+  TileSrc t;
+  t.r = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(bu), (short)0, nrec, 0x00020000);
+  t.rb = s0 ? op.rb0 : op.rb1;
+  t.soff = (uint32_t)(s0 ? kt : kt - op.split) * kRowBytes;
+  return t;
+}
+
+// Direct load i (0..7) of one operand's k-tile (256 rows x 64 k) into its LDS
+// region: each wave stages 64 rows, one load writing 1 KiB = 8 rows of 128
+// bytes, so every load covers whole 128-byte lines.  Lane l fills physical
+// chunk l & 7 of row l / 8, which holds logical chunk (l & 7) ^ ((row >> 1) & 7);
+// for the rows of load i that is (l & 7) ^ (4 (i & 1) + l / 16).
+__device__ __forceinline__ void load_rows(const Operand &op, const TileSrc &t, int i, char *region, int wave, int lane) {
+  const uint32_t c = (uint32_t)(((lane & 7) ^ (((i & 1) << 2) + (lane >> 4))) << 4);
+  const uint32_t voff = op.row[i] * t.rb + c;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(t.r, (lptr_t)(region + (wave * 64 + i * 8) * kRowBytes), 16, voff, t.soff, 0,
+                                           0);
 }
 
 __device__ __forceinline__ bf16x8 frag(const char *region, int row, int c) {
-  return *reinterpret_cast<const bf16x8 *>(region + row * kRowBytes + ((c ^ ((row >> 2) & 3)) << 4));
+  return *reinterpret_cast<const bf16x8 *>(region + row * kRowBytes + ((c ^ ((row >> 1) & 7)) << 4));
 }
 
 struct Frags {
   bf16x8 a[4], b[4];
 };
 
+// Fragments of k-step ks (16 k) of a stage: chunk 2 ks + lane / 32.
 __device__ __forceinline__ void read_frags(Frags &f, const char *stage, int ks, int lane, int wm, int wn) {
   const int c = ks * 2 + (lane >> 5);
 #pragma unroll
@@ -147,84 +177,79 @@ __device__ __forceinline__ void read_frags(Frags &f, const char *stage, int ks, 
   for (int nb = 0; nb < 4; ++nb) f.b[nb] = frag(stage + kBM * kRowBytes, wn * 128 + nb * 32 + (lane & 31), c);
 }
 
-__device__ __forceinline__ void mma(f32x16 (&acc)[4][4], const Frags &f) {
+// One k-step in a fixed instruction order: the 16 MFMAs of fragments f; after
+// each of the first 8, one LDS read of the fragments g of k-step gks of gstage;
+// after every second MFMA, direct load (i / 2) of `load` (a no-op where a
+// k-step issues none).  Spreading the loads keeps the vector memory queue from
+// backing up into the MFMA issue.
+template <class L>
+__device__ __forceinline__ void kstep(f32x16 (&acc)[4][4], const Frags &f, Frags &g, const char *gstage, int gks,
+                                      int lane, int wm, int wn, L &&load) {
+  const int c = gks * 2 + (lane >> 5);
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], f.b[nb], acc[mb][nb], 0, 0, 0);
+  for (int i = 0; i < 16; ++i) {
+    const int mb = i >> 2, nb = i & 3;
+    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], f.b[nb], acc[mb][nb], 0, 0, 0);
+    if (i < 4) g.a[i] = frag(gstage, wm * 128 + i * 32 + (lane & 31), c);
+    else if (i < 8) g.b[i - 4] = frag(gstage + kBM * kRowBytes, wn * 128 + (i - 4) * 32 + (lane & 31), c);
+    if (i & 1) load(i >> 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
-// Wait until at most two k-tiles of this wave's direct loads are still in
-// flight and all of its LDS reads are done, then meet the other waves.
-// s_waitcnt fields: vmcnt[3:0] and [15:14], expcnt[6:4] (7 = no wait),
-// lgkmcnt[11:8] (0 = wait).
+// Wait until at most n of this wave's direct loads are in flight and all of
+// its LDS reads are done, then meet the other waves.  s_waitcnt fields:
+// vmcnt[3:0] and [15:14], expcnt[6:4] (7 = no wait), lgkmcnt[11:8] (0 = wait).
+template <int n>
 __device__ __forceinline__ void tile_barrier() {
-  constexpr int n = 2 * kLoadsPerTile;
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt((n & 15) | 0x70 | ((n >> 4) << 14));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// Instruction order inside one k-step: the 16 MFMAs alternate with the
-// 8 LDS reads of the next k-step and, when given, the 8 direct loads of a
-// later k-tile, so the matrix cores never wait for an LDS round trip.
-// (sched_group_barrier masks: 0x008 MFMA, 0x100 DS read, 0x020 VMEM read.)
-__device__ __forceinline__ void interleave(bool with_loads) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  if (with_loads) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-  } else {
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-  }
-}
-
-// Ring of kStages LDS stages; k-tile t lives in stage t % kStages.  Every
-// iteration issues the loads of k-tile kt + 3 (clamped to the last tile, so
-// the loop body is uniform and the wait count constant), consumes k-tile kt
-// in two k-steps and, between them, waits for k-tile kt + 1.
+// Two LDS stages; k-tile t lives in stage t % 2 and is consumed in four
+// k-steps.  Before the last one, every wave waits for its loads of k-tile
+// kt + 1 and the workgroup meets: k-tile kt + 1 is then visible and stage
+// kt % 2 has been read in full.  The last k-step reads the first fragments of
+// k-tile kt + 1 and issues the A loads of k-tile kt + 2 into the free stage; the
+// first k-step of the next tile issues its B loads.
 template <bool kPinAcc = true>
 __device__ __forceinline__ void mainloop(const Operand &A, const Operand &B, int KT, f32x16 (&acc)[4][4],
                                          char *lds) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index in a scalar register: LDS destinations of the direct loads
+  // (M0) must be wave-uniform
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  {
+    const TileSrc a0 = tile_src(A, 0, KT), b0 = tile_src(B, 0, KT);
 #pragma unroll
-  for (int t = 0; t < kStages - 1; ++t) {
-    const int tt = t < KT ? t : KT - 1;
-    stage_tile(A, tt, lds + t * kStageBytes, wave, lane);
-    stage_tile(B, tt, lds + t * kStageBytes + kBM * kRowBytes, wave, lane);
+    for (int i = 0; i < 8; ++i) load_rows(A, a0, i, lds, wave, lane);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) load_rows(B, b0, i, lds + kBM * kRowBytes, wave, lane);
   }
-  tile_barrier();
+  TileSrc ta = tile_src(A, 1, KT), tb = tile_src(B, 1, KT);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) load_rows(A, ta, i, lds + kStageBytes, wave, lane);
+  tile_barrier<8>();  // k-tile 0 has landed
   Frags f0, f1;
   read_frags(f0, lds, 0, lane, wm, wn);
+  const auto none = [](int) {};
 #pragma unroll 1
   for (int kt = 0; kt < KT; ++kt) {
-    const char *cur = lds + (kt % kStages) * kStageBytes;
-    // the stage of k-tile kt + 3 held k-tile kt - 1, released by the last barrier
-    char *nxt = lds + ((kt + kStages - 1) % kStages) * kStageBytes;
-    const int tl = kt + kStages - 1 < KT ? kt + kStages - 1 : KT - 1;
-    mma(acc, f0);
-    read_frags(f1, cur, 1, lane, wm, wn);
-    stage_tile(A, tl, nxt, wave, lane);
-    stage_tile(B, tl, nxt + kBM * kRowBytes, wave, lane);
-    interleave(true);
-    tile_barrier();
-    mma(acc, f1);
-    read_frags(f0, lds + ((kt + 1) % kStages) * kStageBytes, 0, lane, wm, wn);
-    interleave(false);
+    char *cur = lds + (kt & 1) * kStageBytes;
+    char *nxt = lds + ((kt + 1) & 1) * kStageBytes;
+    kstep(acc, f0, f1, cur, 1, lane, wm, wn, [&](int i) { load_rows(B, tb, i, nxt + kBM * kRowBytes, wave, lane); });
+    kstep(acc, f1, f0, cur, 2, lane, wm, wn, none);
+    kstep(acc, f0, f1, cur, 3, lane, wm, wn, none);
+    tile_barrier<0>();
+    ta = tile_src(A, kt + 2, KT);
+    tb = tile_src(B, kt + 2, KT);
+    kstep(acc, f1, f0, nxt, 0, lane, wm, wn, [&](int i) { load_rows(A, ta, i, cur, wave, lane); });
   }
   __syncthreads();
   // The accumulators leave the loop in AGPRs; epilogues copy them to VGPRs one
@@ -238,13 +263,6 @@ __device__ __forceinline__ void mainloop(const Operand &A, const Operand &B, int
   }
 }
 
-// One accumulator block in VGPRs, copied where it is used.
-__device__ __forceinline__ f32x16 acc_block(const f32x16 (&acc)[4][4], int mb, int nb) {
-  f32x16 b = acc[mb][nb];
-  asm volatile("" : "+v"(b));
-  return b;
-}
-
 // The lane id, opaque to the optimiser: epilogue address arithmetic derived
 // from it cannot be hoisted above the main loop, where it would hold
 // registers for the loop's whole duration.
@@ -253,6 +271,14 @@ __device__ __forceinline__ int epilogue_lane() {
   asm volatile("" : "+v"(l));
   return l;
 }
+
+// One accumulator block in VGPRs, copied where it is used.
+__device__ __forceinline__ f32x16 acc_block(const f32x16 (&acc)[4][4], int mb, int nb) {
+  f32x16 b = acc[mb][nb];
+  asm volatile("" : "+v"(b));
+  return b;
+}
+
 
 // Row (within the wave tile) of register v of block row mb in this lane.
 __device__ __forceinline__ int acc_row(int mb, int v, int lane) { return mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
@@ -300,8 +326,8 @@ __device__ __forceinline__ int clamp_tok(const int32_t *tok, int64_t t, int voca
   return v;
 }
 
-// tile row staged by this lane in load i (0..3), matching stage_tile()
-__device__ __forceinline__ int staged_row(int i) { return (threadIdx.x >> 6) * 64 + i * 16 + ((threadIdx.x & 63) >> 2); }
+// tile row staged by this lane in load i (0..7), matching load_rows()
+__device__ __forceinline__ int staged_row(int i) { return (threadIdx.x >> 6) * 64 + i * 8 + ((threadIdx.x & 63) >> 3); }
 
 // tile-interleaved fp32 storage of one 256x256 tile: 64 bytes per lane per block
 __device__ __forceinline__ f32x4 *tiled_ptr(float *base, int64_t tile_id, int wave, int mb, int nb, int lane) {
@@ -328,12 +354,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_mean_enc(MeanEncP P) {
   const int64_t m0 = (int64_t)mt * kBM;
   const int n0 = nt * kBN;
   Operand A, B;
-  A.base0 = A.base1 = reinterpret_cast<const char *>(P.E);
-  B.base0 = B.base1 = reinterpret_cast<const char *>(P.H);
-  A.rb0 = A.rb1 = B.rb0 = B.rb1 = kEmb * 2;
-  A.split = B.split = kEmb / kBK;
+  set_sources(A, P.E, kEmb * 2, P.E, kEmb * 2, kEmb / kBK);
+  set_sources(B, P.H, kEmb * 2, P.H, kEmb * 2, kEmb / kBK);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const int64_t j = min<int64_t>(m0 + staged_row(i), P.N - 1);
     A.row[i] = (uint32_t)clamp_tok(P.tok, P.keep_head + j, P.vocab, P.status);
     B.row[i] = (uint32_t)P.act[n0 + staged_row(i)];
@@ -421,12 +445,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   const int64_t m0 = (int64_t)mt * kBM;
   const int n0 = nt * kBN;
   Operand A, B;
-  A.base0 = A.base1 = reinterpret_cast<const char *>(P.rows);
-  B.base0 = B.base1 = reinterpret_cast<const char *>(P.A);
-  A.rb0 = A.rb1 = B.rb0 = B.rb1 = kD * 2;
-  A.split = B.split = kD / kBK;
+  set_sources(A, P.rows, kD * 2, P.rows, kD * 2, kD / kBK);
+  set_sources(B, P.A, kD * 2, P.A, kD * 2, kD / kBK);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const int64_t j = min<int64_t>(m0 + staged_row(i), P.N - 1);
     A.row[i] = (uint32_t)(P.keep_head + j);
     B.row[i] = (uint32_t)P.act[n0 + staged_row(i)];
@@ -611,12 +633,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_dequant(DeqP P) {
   const int64_t m0 = (int64_t)mt * kBM;
   const int n0 = nt * kBN;
   Operand A, B;
-  A.base0 = A.base1 = reinterpret_cast<const char *>(P.E);
-  B.base0 = B.base1 = reinterpret_cast<const char *>(P.H);
-  A.rb0 = A.rb1 = B.rb0 = B.rb1 = kEmb * 2;
-  A.split = B.split = kEmb / kBK;
+  set_sources(A, P.E, kEmb * 2, P.E, kEmb * 2, kEmb / kBK);
+  set_sources(B, P.H, kEmb * 2, P.H, kEmb * 2, kEmb / kBK);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const int64_t j = min<int64_t>(m0 + staged_row(i), P.N - 1);
     A.row[i] = (uint32_t)clamp_tok(P.tok, P.keep_head + j, P.vocab, P.status);
     B.row[i] = (uint32_t)(n0 + staged_row(i));
@@ -740,12 +760,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_w1(W1P P) {
   tile_of(blockIdx.x, P.n_mt, 1, mt, nt);
   const int64_t m0 = (int64_t)mt * kBM;
   Operand A, B;
-  A.base0 = A.base1 = reinterpret_cast<const char *>(P.yhat_b);
-  B.base0 = B.base1 = reinterpret_cast<const char *>(P.W1);
-  A.rb0 = A.rb1 = B.rb0 = B.rb1 = kC * 2;
-  A.split = B.split = kC / kBK;
+  set_sources(A, P.yhat_b, kC * 2, P.yhat_b, kC * 2, kC / kBK);
+  set_sources(B, P.W1, kC * 2, P.W1, kC * 2, kC / kBK);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     A.row[i] = (uint32_t)(m0 + staged_row(i));
     B.row[i] = (uint32_t)staged_row(i);
   }
@@ -787,15 +805,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
   const int64_t m0 = (int64_t)mt * kBM;
   const int head = nt;
   Operand A, B;
-  A.base0 = reinterpret_cast<const char *>(P.yhat_b);
-  A.base1 = reinterpret_cast<const char *>(P.h_b);
-  B.base0 = reinterpret_cast<const char *>(P.S);
-  B.base1 = reinterpret_cast<const char *>(P.W2);
-  A.rb0 = B.rb0 = kC * 2;
-  A.rb1 = B.rb1 = kHid * 2;
-  A.split = B.split = kC / kBK;
+  set_sources(A, P.yhat_b, kC * 2, P.h_b, kHid * 2, kC / kBK);
+  set_sources(B, P.S, kC * 2, P.W2, kHid * 2, kC / kBK);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     A.row[i] = (uint32_t)(m0 + staged_row(i));
     B.row[i] = (uint32_t)(head * kHeadDim + syn_dim(staged_row(i)));
   }
