@@ -8,6 +8,19 @@ correction MLP, synthesis with RoPE, kept rows).  Inputs are resident in HBM
 before the timed region.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+HBM traffic of the dominant kernel (the roofline's "traffic") comes from two
+rocprofv3 counter runs of this script, one with FETCH_SIZE and one with
+WRITE_SIZE, each ending with a plain copy of known size
+(--copy-calibration-mib) that scales the counters to bytes:
+
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR_F -o run -- \
+        python bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration-mib 1024
+    rocprofv3 --pmc WRITE_SIZE ... (same, into DIR_W)
+    python bench.py --write-traffic DIR_F DIR_W --copy-calibration-mib 1024
+
+The last command writes profiles/traffic.json (per kernel: bytes per launch,
+and the hash of the kernel's source, so that a changed kernel reports null).
 """
 from __future__ import annotations
 
@@ -47,6 +60,17 @@ def kernel_work(name: str, N: int, Ca: int, rans_bytes: int):
     return None, 0.0, None
 
 
+KERNEL_SOURCES = {  # profile name -> (kernel symbol, source file)
+    "mean_gemm": ("k_mean_enc", "gemm.hip"),
+    "analysis_gemm": ("k_analysis_quant", "gemm.hip"),
+    "dequant_gemm": ("k_dequant", "gemm.hip"),
+    "w1_gemm": ("k_w1", "gemm.hip"),
+    "synthesis_gemm": ("k_synthesis", "gemm.hip"),
+    "rans_encode": ("k_rans_encode", "rans.hip"),
+    "rans_decode": ("k_rans_decode", "rans.hip"),
+}
+
+
 def source_sha(path: str) -> str:
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -72,10 +96,56 @@ def cpu_baseline(req_cfg: int, n_rows: int):
     ocodec.decode(enc.data, req.token_ids, params, p)
     t2 = time.perf_counter()
     return {"value": enc.N / (t2 - t0), "unit": "coded tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": "first %d positions of the 32K workload as one %d-token prompt (%d coded), same seeds "
+            "sample": "first %d positions of the workload as one %d-token prompt (%d coded), same seeds "
                       "and step scale; encode %.2f s + decode %.2f s, numpy float64" % (
                           n_rows, n_rows, enc.N, t1 - t0, t2 - t1),
             "encode_tokens_per_s": enc.N / (t1 - t0), "decode_tokens_per_s": enc.N / (t2 - t1)}
+
+
+def _counter_means(csv_dir: str, counter: str):
+    """Mean value per kernel symbol of one counter, and the largest value of a
+    dispatch outside the library (the calibration copy)."""
+    import csv
+    import glob
+    import re
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % csv_dir)
+    per, other = {}, 0.0
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                m = re.search(r"(k_\w+)", r["Kernel_Name"])
+                if m and "dckv" in r["Kernel_Name"]:
+                    per.setdefault(m.group(1), []).append(v)
+                else:
+                    other = max(other, v)
+    return {k: sum(v) / len(v) for k, v in per.items()}, other
+
+
+def write_traffic(fetch_dir: str, write_dir: str, copy_mib: int, T: int) -> int:
+    fetch, fetch_copy = _counter_means(fetch_dir, "FETCH_SIZE")
+    write, write_copy = _counter_means(write_dir, "WRITE_SIZE")
+    copy_bytes = copy_mib * 1024 * 1024
+    if fetch_copy <= 0 or write_copy <= 0:
+        raise SystemExit("the calibration copy is missing from the counter runs")
+    sf = copy_bytes / (fetch_copy * 1024.0)   # counters are KiB per dispatch
+    sw = copy_bytes / (write_copy * 1024.0)
+    out = {"_calibration": {"copy_bytes": copy_bytes, "fetch_kib": fetch_copy, "write_kib": write_copy,
+                            "fetch_scale": sf, "write_scale": sw}}
+    for name, (sym, src) in KERNEL_SOURCES.items():
+        if sym in fetch and sym in write:
+            fb, wb = fetch[sym] * 1024.0 * sf, write[sym] * 1024.0 * sw
+            out[name] = {"kernel": sym, "source": src,
+                         "source_sha": source_sha(os.path.join(ROOT, "learned_kv_cache_dckv_amd", "csrc", src)),
+                         "T": T, "fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+    return 0
 
 
 def main(argv=None) -> int:
@@ -85,8 +155,16 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload index (2 = 32K-token prompt)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=8192)
+    ap.add_argument("--cpu-sample-rows", type=int, default=32768)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="end with a plain device copy of this many MiB (scale for the traffic counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 counter runs, then exit")
     args = ap.parse_args(argv)
+    if args.write_traffic:
+        import dckv_synth as synth
+        return write_traffic(args.write_traffic[0], args.write_traffic[1], args.copy_calibration_mib or 1024,
+                             synth.CONFIGS[args.config]["T"])
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
         return 2
@@ -243,6 +321,14 @@ def main(argv=None) -> int:
         "kernels": kern,
         "cpu_baseline": None,
     }
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * 1024 * 1024 // 4
+        src_t = torch.ones(n, dtype=torch.int32, device=dev)
+        dst_t = torch.empty(n, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        dst_t.copy_(src_t)  # one elementwise kernel: reads and writes n * 4 bytes
+        torch.cuda.synchronize()
+        del src_t, dst_t
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample_rows)
     print(json.dumps(res))

@@ -94,13 +94,19 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// XCD-aware tile order: workgroup b runs on XCD b % 8; give each XCD a
-// contiguous run of tiles (row-band major) so a band stays in one L2.
+// XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD gets a
+// contiguous run of tile indices.  Tile index t walks column groups of up to 8
+// tiles, row bands inside a group, columns inside a band, so the 32 tiles an
+// XCD runs at once form a 4 x 8 block: per k-tile they read 4 row panels and 8
+// column panels, shared through that XCD's L2.
 __device__ __forceinline__ void tile_of(int b, int total, int n_nt, int &mt, int &nt) {
   const int q = total >> 3, r = total & 7, x = b & 7, k = b >> 3;
   const int t = x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
-  mt = t / n_nt;
-  nt = t - mt * n_nt;
+  const int gw = n_nt < 8 ? n_nt : 8;     // column tiles per group (n_nt is 1..8 or a multiple of 8)
+  const int n_mt = total / n_nt;
+  const int grp = t / (gw * n_mt), rem = t - grp * gw * n_mt;
+  mt = rem / gw;
+  nt = grp * gw + (rem - mt * gw);
 }
 
 // ---------------------------------------------------------------------------

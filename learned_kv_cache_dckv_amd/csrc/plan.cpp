@@ -380,7 +380,7 @@ extern "C" int dckv_workspace_view(const dckv_plan_t *plan, int64_t T, int32_t w
     case DCKV_VIEW_SYMBOLS: o = l.sym; b = (uint64_t)g.G * g.N256 * kLanes; rs = kLanes; break;
     case DCKV_VIEW_YHAT_B: o = l.yhat_b; b = (uint64_t)g.N * plan->C * 2; rs = plan->C; break;
     case DCKV_VIEW_H_B: o = l.h_b; b = (uint64_t)g.N * plan->hidden * 2; rs = plan->hidden; break;
-    case DCKV_VIEW_MEAN: o = l.mean; b = (uint64_t)g.NM * g.Ca4 * 4; rs = g.Ca4; break;
+    case DCKV_VIEW_MEAN: o = l.mean; b = (uint64_t)g.NM * g.Ca4 * 4; rs = 0; break;
     default: return set_error(DCKV_EINVAL, "workspace_view: unknown view");
   }
   if (offset) *offset = o;
