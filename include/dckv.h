@@ -161,6 +161,48 @@ int dckv_decode(const dckv_plan_t *plan, const uint8_t *stream, uint64_t stream_
                 void *workspace, uint64_t workspace_bytes, void *hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * Batches of independent requests in one call (DCKV digest, "How it works":
+ * every request is coded on its own; "Limits": the pages code one request at a
+ * time, so a batch is our extension).
+ *
+ * Each dckv_req describes one request; the array itself is host memory.
+ *   plan         the request's plan (its rate); every plan on the same device
+ *   rows         encode: [T][D] bf16 pre-RoPE rows (device); unused by decode
+ *   token_ids    [T] int32 (device)
+ *   T            the request's length
+ *   stream       encode: output buffer; decode: the request's stream (device)
+ *   capacity     encode: bytes available at stream; decode: the stream's size
+ *   stream_bytes encode: (device) u64 receiving the stream's size (0 on a
+ *                device-side error); unused by decode
+ *   rows_out     decode: [T][D] bf16 output (device); unused by encode
+ *   status       (device) int32 per request, as for dckv_encode / dckv_decode
+ * Every request is checked before anything is enqueued: an argument error in
+ * any request returns its code (dckv_last_error names the request) and
+ * enqueues nothing.  The requests then run in array order on hip_stream and
+ * share one workspace of dckv_bytes_batch() bytes (the largest request's
+ * need); the workspace is owned by the caller and must not be used by other
+ * work on other streams meanwhile.  Each request's results equal those of the
+ * single-request call.
+ * --------------------------------------------------------------------------*/
+typedef struct dckv_req {
+  const dckv_plan_t *plan;
+  const uint16_t *rows;
+  const int32_t *token_ids;
+  int64_t T;
+  uint8_t *stream;
+  uint64_t capacity;
+  uint64_t *stream_bytes;
+  uint16_t *rows_out;
+  int32_t *status;
+} dckv_req;
+
+int dckv_bytes_batch(const dckv_req *reqs, int32_t n, uint64_t *workspace_bytes);
+int dckv_encode_batch(const dckv_req *reqs, int32_t n, void *workspace, uint64_t workspace_bytes,
+                      void *hip_stream);
+int dckv_decode_batch(const dckv_req *reqs, int32_t n, void *workspace, uint64_t workspace_bytes,
+                      void *hip_stream);
+
+/* ---------------------------------------------------------------------------
  * The lossless stage alone (DCKV digest, "How it works", Coding).
  *
  * dckv_entropy_encode: writes the stream for given codes.

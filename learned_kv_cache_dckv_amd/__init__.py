@@ -25,8 +25,9 @@ VIEW_SYMBOLS, VIEW_YHAT_B, VIEW_H_B, VIEW_MEAN = 0, 1, 2, 3
 
 # every symbol include/dckv.h declares
 EXPORTS = ("dckv_plan_tables", "dckv_plan", "dckv_plan_free", "dckv_plan_info", "dckv_bytes", "dckv_encode",
-           "dckv_decode", "dckv_entropy_encode", "dckv_entropy_decode", "dckv_workspace_view",
-           "dckv_profile_enable", "dckv_profile_reset", "dckv_profile_read", "dckv_last_error")
+           "dckv_decode", "dckv_bytes_batch", "dckv_encode_batch", "dckv_decode_batch", "dckv_entropy_encode",
+           "dckv_entropy_decode", "dckv_workspace_view", "dckv_profile_enable", "dckv_profile_reset",
+           "dckv_profile_read", "dckv_last_error")
 
 
 class DckvError(RuntimeError):
@@ -46,6 +47,13 @@ class _Params(ctypes.Structure):
                 ("base_step", ctypes.c_void_p)]
 
 
+class _Req(ctypes.Structure):
+    """One request of a batch call (struct dckv_req)."""
+    _fields_ = [("plan", ctypes.c_void_p), ("rows", ctypes.c_void_p), ("token_ids", ctypes.c_void_p),
+                ("T", ctypes.c_int64), ("stream", ctypes.c_void_p), ("capacity", ctypes.c_uint64),
+                ("stream_bytes", ctypes.c_void_p), ("rows_out", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libdckv.so is not built: run `python -m learned_kv_cache_dckv_amd.build` "
@@ -61,6 +69,9 @@ def _load():
         "dckv_bytes": [P, I64, P, P],
         "dckv_encode": [P, P, P, I64, P, U64, P, P, P, U64, P],
         "dckv_decode": [P, P, U64, P, I64, P, P, P, U64, P],
+        "dckv_bytes_batch": [P, I32, P],
+        "dckv_encode_batch": [P, I32, P, U64, P],
+        "dckv_decode_batch": [P, I32, P, U64, P],
         "dckv_entropy_encode": [P, I64, P, P, U32, P, P, U64, P, P, P, U64, P],
         "dckv_entropy_decode": [P, P, U64, I64, P, P, P, P, U64, P],
         "dckv_workspace_view": [P, I64, I32, P, P, P],
@@ -255,6 +266,49 @@ def dckv_decode(plan: Plan, stream_buf, n_bytes: int, token_ids, rows_out, statu
     out = _as_bits(rows_out)
     _check(_lib.dckv_decode(plan.handle, _ptr(stream_buf), int(n_bytes), _ptr(token_ids), T, _ptr(out),
                             _ptr(status), _ptr(ws), ws.numel(), _stream_handle(stream)))
+
+
+class Request:
+    """One request of a batch call.  Tensors are device tensors; fields a call
+    does not use may be None (rows / stream_bytes for decode, rows_out for
+    encode).  For decode, `capacity` is the stream's size in bytes."""
+
+    def __init__(self, plan: Plan, token_ids, rows=None, stream=None, capacity=None, stream_bytes=None,
+                 rows_out=None, status=None):
+        self.plan, self.token_ids, self.rows, self.stream = plan, token_ids, rows, stream
+        self.capacity = int(stream.numel() if capacity is None and stream is not None else (capacity or 0))
+        self.stream_bytes, self.rows_out, self.status = stream_bytes, rows_out, status
+
+    def c_req(self) -> _Req:
+        T = int(self.token_ids.shape[0])
+        rows = _as_bits(self.rows) if self.rows is not None else None
+        out = _as_bits(self.rows_out) if self.rows_out is not None else None
+        return _Req(self.plan.handle, _ptr(rows), _ptr(self.token_ids), T, _ptr(self.stream), self.capacity,
+                    _ptr(self.stream_bytes), _ptr(out), _ptr(self.status))
+
+
+def _reqs(requests):
+    arr = (_Req * max(len(requests), 1))()
+    for i, r in enumerate(requests):
+        arr[i] = r.c_req()
+    return arr
+
+
+def dckv_bytes_batch(requests) -> int:
+    """Workspace bytes for a batch call over these requests."""
+    ws = ctypes.c_uint64()
+    _check(_lib.dckv_bytes_batch(_reqs(requests), len(requests), ctypes.byref(ws)))
+    return ws.value
+
+
+def dckv_encode_batch(requests, ws, stream=None):
+    """Enqueue the encode of every request, in order, on one stream."""
+    _check(_lib.dckv_encode_batch(_reqs(requests), len(requests), _ptr(ws), ws.numel(), _stream_handle(stream)))
+
+
+def dckv_decode_batch(requests, ws, stream=None):
+    """Enqueue the decode of every request, in order, on one stream."""
+    _check(_lib.dckv_decode_batch(_reqs(requests), len(requests), _ptr(ws), ws.numel(), _stream_handle(stream)))
 
 
 def dckv_entropy_encode(plan: Plan, T: int, sym, esc, n_esc: int, rows, stream_buf, stream_bytes, status, ws,

@@ -11,6 +11,7 @@
 // dequantisation passes -> fix-up -> correction hidden layer -> synthesis with
 // RoPE -> RoPE of the kept rows.
 #include <algorithm>
+#include <cstdio>
 #include <cstring>
 
 #include "dckv_internal.h"
@@ -44,13 +45,10 @@ int common_checks(const dckv_plan_t *p, int64_t T, void *ws, uint64_t ws_bytes, 
 
 int after_launch(const char *what) { return check_hip(hipGetLastError(), what); }
 
-}  // namespace
 
-extern "C" int dckv_encode(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *token_ids, int64_t T,
-                           uint8_t *stream, uint64_t capacity, uint64_t *stream_bytes, int32_t *status,
-                           void *workspace, uint64_t workspace_bytes, void *hip_stream) {
-  Geometry g;
-  Layout l;
+int encode_checks(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *token_ids, int64_t T,
+                  uint8_t *stream, uint64_t capacity, uint64_t *stream_bytes, int32_t *status, void *workspace,
+                  uint64_t workspace_bytes, Geometry &g, Layout &l) {
   int rc = common_checks(plan, T, workspace, workspace_bytes, status, g, l);
   if (rc) return rc;
   if (T > 0 && (!rows || !aligned(rows, 16) || !token_ids || !aligned(token_ids, 4)))
@@ -58,8 +56,10 @@ extern "C" int dckv_encode(const dckv_plan_t *plan, const uint16_t *rows, const 
   if (!stream || !aligned(stream, 16) || !stream_bytes || !aligned(stream_bytes, 8))
     return set_error(DCKV_EINVAL, "stream must be 16-byte aligned and stream_bytes 8-byte aligned");
   if (capacity < g.fixed_bytes) return set_error(DCKV_ECAPACITY, "capacity below the stream's fixed part");
-  EncodeArgs a{plan, g, l, static_cast<uint8_t *>(workspace), rows, token_ids, stream, capacity,
-               stream_bytes, status, static_cast<hipStream_t>(hip_stream)};
+  return DCKV_OK;
+}
+
+void encode_sequence(const EncodeArgs &a) {
   launch_init(a);
   launch_kept_copy(a);
   launch_mean_gemm(a);
@@ -69,22 +69,21 @@ extern "C" int dckv_encode(const dckv_plan_t *plan, const uint16_t *rows, const 
   launch_rans_encode(a);
   launch_scan_header(a);
   launch_pack(a);
-  return after_launch("dckv_encode");
 }
 
-extern "C" int dckv_decode(const dckv_plan_t *plan, const uint8_t *stream, uint64_t stream_bytes,
-                           const int32_t *token_ids, int64_t T, uint16_t *rows_out, int32_t *status,
-                           void *workspace, uint64_t workspace_bytes, void *hip_stream) {
-  Geometry g;
-  Layout l;
+int decode_checks(const dckv_plan_t *plan, const uint8_t *stream, uint64_t stream_bytes, const int32_t *token_ids,
+                  int64_t T, uint16_t *rows_out, int32_t *status, void *workspace, uint64_t workspace_bytes,
+                  Geometry &g, Layout &l) {
   int rc = common_checks(plan, T, workspace, workspace_bytes, status, g, l);
   if (rc) return rc;
   if (T > 0 && (!rows_out || !aligned(rows_out, 16) || !token_ids || !aligned(token_ids, 4)))
     return set_error(DCKV_EINVAL, "rows_out must be 16-byte aligned, token_ids 4-byte aligned");
   if (!stream || !aligned(stream, 16)) return set_error(DCKV_EINVAL, "stream must be 16-byte aligned");
   if (stream_bytes < g.fixed_bytes) return set_error(DCKV_ECORRUPT, "stream shorter than its fixed part");
-  DecodeArgs a{plan, g, l, static_cast<uint8_t *>(workspace), stream, stream_bytes, token_ids, rows_out, status,
-               static_cast<hipStream_t>(hip_stream)};
+  return DCKV_OK;
+}
+
+void decode_sequence(const DecodeArgs &a) {
   launch_init(a);
   launch_parse(a);
   launch_rope_tables(a);
@@ -94,7 +93,97 @@ extern "C" int dckv_decode(const dckv_plan_t *plan, const uint8_t *stream, uint6
   launch_w1_gemm(a);
   launch_synthesis_gemm(a);
   launch_kept_rope(a);
+}
+
+int batch_error(int rc, int32_t i, const char *what) {
+  char msg[160];
+  std::snprintf(msg, sizeof msg, "%s: request %d: %s", what, (int)i, dckv_last_error());
+  return set_error(rc, msg);
+}
+
+}  // namespace
+
+extern "C" int dckv_encode(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *token_ids, int64_t T,
+                           uint8_t *stream, uint64_t capacity, uint64_t *stream_bytes, int32_t *status,
+                           void *workspace, uint64_t workspace_bytes, void *hip_stream) {
+  Geometry g;
+  Layout l;
+  int rc = encode_checks(plan, rows, token_ids, T, stream, capacity, stream_bytes, status, workspace,
+                         workspace_bytes, g, l);
+  if (rc) return rc;
+  encode_sequence(EncodeArgs{plan, g, l, static_cast<uint8_t *>(workspace), rows, token_ids, stream, capacity,
+                             stream_bytes, status, static_cast<hipStream_t>(hip_stream)});
+  return after_launch("dckv_encode");
+}
+
+extern "C" int dckv_decode(const dckv_plan_t *plan, const uint8_t *stream, uint64_t stream_bytes,
+                           const int32_t *token_ids, int64_t T, uint16_t *rows_out, int32_t *status,
+                           void *workspace, uint64_t workspace_bytes, void *hip_stream) {
+  Geometry g;
+  Layout l;
+  int rc = decode_checks(plan, stream, stream_bytes, token_ids, T, rows_out, status, workspace, workspace_bytes,
+                         g, l);
+  if (rc) return rc;
+  decode_sequence(DecodeArgs{plan, g, l, static_cast<uint8_t *>(workspace), stream, stream_bytes, token_ids,
+                             rows_out, status, static_cast<hipStream_t>(hip_stream)});
   return after_launch("dckv_decode");
+}
+
+extern "C" int dckv_bytes_batch(const dckv_req *reqs, int32_t n, uint64_t *workspace_bytes) {
+  if (n < 0 || (n > 0 && !reqs) || !workspace_bytes) return set_error(DCKV_EINVAL, "bytes_batch: bad argument");
+  uint64_t need = 256;
+  for (int32_t i = 0; i < n; ++i) {
+    uint64_t ws = 0;
+    const int rc = dckv_bytes(reqs[i].plan, reqs[i].T, nullptr, &ws);
+    if (rc) return batch_error(rc, i, "bytes_batch");
+    need = std::max(need, ws);
+  }
+  *workspace_bytes = need;
+  return DCKV_OK;
+}
+
+extern "C" int dckv_encode_batch(const dckv_req *reqs, int32_t n, void *workspace, uint64_t workspace_bytes,
+                                 void *hip_stream) {
+  if (n < 0 || (n > 0 && !reqs)) return set_error(DCKV_EINVAL, "encode_batch: bad argument");
+  for (int32_t i = 0; i < n; ++i) {
+    const dckv_req &r = reqs[i];
+    Geometry g;
+    Layout l;
+    const int rc = encode_checks(r.plan, r.rows, r.token_ids, r.T, r.stream, r.capacity, r.stream_bytes, r.status,
+                                 workspace, workspace_bytes, g, l);
+    if (rc) return batch_error(rc, i, "encode_batch");
+    if (i > 0 && r.plan->device != reqs[0].plan->device)
+      return batch_error(DCKV_EINVAL, i, "encode_batch: plans on different devices");
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const dckv_req &r = reqs[i];
+    const Geometry g = geometry(r.plan, r.T);
+    encode_sequence(EncodeArgs{r.plan, g, layout(r.plan, g), static_cast<uint8_t *>(workspace), r.rows, r.token_ids,
+                               r.stream, r.capacity, r.stream_bytes, r.status, static_cast<hipStream_t>(hip_stream)});
+  }
+  return after_launch("dckv_encode_batch");
+}
+
+extern "C" int dckv_decode_batch(const dckv_req *reqs, int32_t n, void *workspace, uint64_t workspace_bytes,
+                                 void *hip_stream) {
+  if (n < 0 || (n > 0 && !reqs)) return set_error(DCKV_EINVAL, "decode_batch: bad argument");
+  for (int32_t i = 0; i < n; ++i) {
+    const dckv_req &r = reqs[i];
+    Geometry g;
+    Layout l;
+    const int rc = decode_checks(r.plan, r.stream, r.capacity, r.token_ids, r.T, r.rows_out, r.status, workspace,
+                                 workspace_bytes, g, l);
+    if (rc) return batch_error(rc, i, "decode_batch");
+    if (i > 0 && r.plan->device != reqs[0].plan->device)
+      return batch_error(DCKV_EINVAL, i, "decode_batch: plans on different devices");
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const dckv_req &r = reqs[i];
+    const Geometry g = geometry(r.plan, r.T);
+    decode_sequence(DecodeArgs{r.plan, g, layout(r.plan, g), static_cast<uint8_t *>(workspace), r.stream,
+                               r.capacity, r.token_ids, r.rows_out, r.status, static_cast<hipStream_t>(hip_stream)});
+  }
+  return after_launch("dckv_decode_batch");
 }
 
 extern "C" int dckv_entropy_encode(const dckv_plan_t *plan, int64_t T, const uint8_t *sym, const uint32_t *esc,
