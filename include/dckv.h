@@ -236,13 +236,15 @@ int dckv_entropy_decode(const dckv_plan_t *plan, const uint8_t *stream, uint64_t
  *   DCKV_VIEW_H_B      bf16 [N][n_hidden] correction hidden units
  *   DCKV_VIEW_MEAN     fp32 embedding mean H E[tok] of the last encode, in
  *                      the order of the GEMM accumulators (row_stride 0: not
- *                      row-major).  With 256x256 tiles, n_nt = C_a rounded up
- *                      to 256, divided by 256: element (j, rank r) has
- *                      tile = (j/256)*n_nt + r/256, w = 2*((j%256)/128) +
- *                      (r%256)/128, mb = (j%128)/32, nb = (r%128)/32,
- *                      lane = (r%32) + 32*((j%8)/4), v = 4*((j%32)/8) + j%4,
- *                      and sits at float index
- *                      ((((tile*4 + w)*4 + mb)*4 + nb)*64 + lane)*16 + v
+ *                      row-major).  With 256x256 tiles and n_nt = C_a rounded
+ *                      up to 256, divided by 256: element (j, rank r) lies in
+ *                      tile = (j/256)*n_nt + r/256, plane p = j%2 (even and odd
+ *                      rows apart), w = 2*((j%256)/128) + (r%256)/128,
+ *                      mb = (j%128)/32, nb = (r%128)/32, lane = (r%32) +
+ *                      32*((j%8)/4), register v = 4*((j%32)/8) + j%4,
+ *                      half h = v/8, element e = 2*((v/4)%2) + (v/2)%2, at
+ *                      float index (tile*2 + p)*32768 +
+ *                      ((((w*4 + mb)*4 + nb)*2 + h)*64 + lane)*4 + e
  * --------------------------------------------------------------------------*/
 enum { DCKV_VIEW_SYMBOLS = 0, DCKV_VIEW_YHAT_B = 1, DCKV_VIEW_H_B = 2, DCKV_VIEW_MEAN = 3 };
 int dckv_workspace_view(const dckv_plan_t *plan, int64_t T, int32_t which, uint64_t *offset,

@@ -335,9 +335,27 @@ __device__ __forceinline__ int clamp_tok(const int32_t *tok, int64_t t, int voca
 // tile row staged by this lane in load i (0..7), matching load_rows()
 __device__ __forceinline__ int staged_row(int i) { return (threadIdx.x >> 6) * 64 + i * 8 + ((threadIdx.x & 63) >> 3); }
 
-// tile-interleaved fp32 storage of one 256x256 tile: 64 bytes per lane per block
-__device__ __forceinline__ f32x4 *tiled_ptr(float *base, int64_t tile_id, int wave, int mb, int nb, int lane) {
-  return reinterpret_cast<f32x4 *>(base + ((((tile_id * 4 + wave) * 4 + mb) * 4 + nb) * 64 + lane) * 16);
+// fp32 embedding mean of one 256x256 tile as two planes of 128 KiB: plane p
+// holds the rows of parity p (the rows one checkerboard pass needs), in the
+// order of the accumulators: [wave][mb][nb][h][lane][4]; element e of half h
+// is accumulator register v = 8h + 4(e >> 1) + 2(e & 1) + p.
+constexpr int kPlaneFloats = 4 * 4 * 4 * 2 * 64 * 4;  // 32768
+__device__ __forceinline__ int plane_off(int wave, int mb, int nb, int h, int lane) {
+  return ((((wave * 4 + mb) * 4 + nb) * 2 + h) * 64 + lane) * 4;
+}
+
+// plane register v (of parity p) -> (half, element)
+__device__ __forceinline__ int plane_h(int v) { return v >> 3; }
+__device__ __forceinline__ int plane_e(int v) { return 2 * ((v >> 2) & 1) + ((v >> 1) & 1); }
+
+// One plane of a tile from global memory into LDS (offset 0): 32 direct loads
+// per wave of 1 KiB each, in the plane's own order.
+__device__ __forceinline__ void plane_to_lds(const float *plane, char *lds, int wave, int lane) {
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int off = wave * (kPlaneFloats / 4) + k * 256;  // floats
+    __builtin_amdgcn_global_load_lds((gptr_t)(plane + off + lane * 4), (lptr_t)(lds + off * 4), 16, 0, 0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -346,7 +364,7 @@ __device__ __forceinline__ f32x4 *tiled_ptr(float *base, int64_t tile_id, int wa
 struct MeanEncP {
   const uint16_t *E, *H;
   const int32_t *tok, *act;
-  float *mean;  // tile-interleaved [n_mtiles][n_ntiles][256x256]
+  float *mean;  // [n_mtiles][n_ntiles][2 planes][32768], see plane_off()
   int64_t N;
   int n_mt, n_nt, keep_head, vocab;
   int32_t *status;
@@ -376,10 +394,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_mean_enc(MeanEncP P) {
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      f32x4 *dst = tiled_ptr(P.mean, tid, wave, mb, nb, lane);
+      const f32x16 b = acc_block(acc, mb, nb);
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        dst[g] = f32x4{acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]};
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float *plane = P.mean + (tid * 2 + p) * kPlaneFloats;
+          const int v = 8 * h + p;
+          *reinterpret_cast<f32x4 *>(plane + plane_off(wave, mb, nb, h, lane)) = f32x4{b[v], b[v + 2], b[v + 4], b[v + 6]};
+        }
     }
 }
 
@@ -479,24 +502,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   }
   uint32_t symw[4][4][4];
   bool bad = false;
-  // pass 1: even rows, mu = H E[tok]
+  // pass 1: even rows, mu = H E[tok], from the even-row plane staged in LDS
+  plane_to_lds(P.mean + (tid * 2 + 0) * kPlaneFloats, lds, wave, lane);
+  __syncthreads();  // (waits for this wave's loads, then for every wave's)
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const f32x4 *mp = tiled_ptr(P.mean, tid, wave, mb, nb, lane);
+      f32x4 mh[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) mh[h] = *reinterpret_cast<const f32x4 *>(lds + plane_off(wave, mb, nb, h, lane) * 4);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 m4 = mp[g];
         uint32_t w = 0xFFFFFFFFu;
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
           const int v = 4 * g + i;
+          const float m = mh[plane_h(v)][plane_e(v)];
           const int64_t j = wrow0 + acc_row(mb, v, lane);
           if (j < P.N && r_nb[nb] < P.Ca) {
             float qf;
-            const uint32_t sy = quant_one(acc[mb][nb][v] - m4[i], st_nb[nb], inv_nb[nb], j, r_nb[nb], P, bad, qf);
-            acc[mb][nb][v] = m4[i] + qf * st_nb[nb];
+            const uint32_t sy = quant_one(acc[mb][nb][v] - m, st_nb[nb], inv_nb[nb], j, r_nb[nb], P, bad, qf);
+            acc[mb][nb][v] = m + qf * st_nb[nb];
             w = with_byte(w, i, sy);
           } else {
             acc[mb][nb][v] = 0.f;  // a missing right neighbour counts as zero
@@ -517,35 +544,41 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   }
   __syncthreads();
   const bool defer_last = m0 + kBM < P.N;
-  // pass 2: odd rows, mu = H E[tok] + a (yhat_{j-1} + yhat_{j+1})
+  // pass 2: odd rows, mu = H E[tok] + a (yhat_{j-1} + yhat_{j+1}), from the
+  // odd-row plane (the barrier above also ended every wave's pass 1 reads)
+  plane_to_lds(P.mean + (tid * 2 + 1) * kPlaneFloats, lds, wave, lane);
+  __syncthreads();
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const f32x4 *mp = tiled_ptr(P.mean, tid, wave, mb, nb, lane);
+      f32x4 mh[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) mh[h] = *reinterpret_cast<const f32x4 *>(lds + plane_off(wave, mb, nb, h, lane) * 4);
       const float ext = wm == 0 ? xch[256 + wn * 128 + nb * 32 + (lane & 31)] : 0.f;
       const float a = a_nb[nb];
       const int r = r_nb[nb];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float next3 = next_quad_row0(acc, mb, nb, g, ext, lane);
-        const f32x4 m4 = mp[g];
+        const float m1 = mh[plane_h(4 * g + 1)][plane_e(4 * g + 1)];
+        const float m3 = mh[plane_h(4 * g + 3)][plane_e(4 * g + 3)];
         uint32_t w = symw[mb][nb][g];
         const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
         const float y0 = acc[mb][nb][4 * g], y2 = acc[mb][nb][4 * g + 2];
         if (j0 + 1 < P.N && r < P.Ca) {
           float qf;
-          const float mu = m4[1] + a * (y0 + y2);
+          const float mu = m1 + a * (y0 + y2);
           w = with_byte(w, 1, quant_one(acc[mb][nb][4 * g + 1] - mu, st_nb[nb], inv_nb[nb], j0 + 1, r, P, bad, qf));
         }
         if (j0 + 3 < P.N && r < P.Ca) {
           uint32_t sy;
           if (wm == 1 && mb == 3 && g == 3 && lane >= 32 && defer_last) {
-            P.halo_a[(int64_t)mt * P.C + r] = acc[mb][nb][4 * g + 3] - m4[3] - a * y2;
+            P.halo_a[(int64_t)mt * P.C + r] = acc[mb][nb][4 * g + 3] - m3 - a * y2;
             sy = 0u;  // finished by the fix-up
           } else {
             float qf;
-            const float mu = m4[3] + a * (y2 + next3);
+            const float mu = m3 + a * (y2 + next3);
             sy = quant_one(acc[mb][nb][4 * g + 3] - mu, st_nb[nb], inv_nb[nb], j0 + 3, r, P, bad, qf);
           }
           w = with_byte(w, 3, sy);
@@ -664,19 +697,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_dequant(DeqP P) {
     a_nb[nb] = P.nbr[c];
   }
   uint32_t symw[4][4][4];
-  // pass 1: even rows, yhat = mu + q step
+  // pass 1: even rows, yhat = mu + q step.  The 16 symbol words of a block
+  // row are loaded together, ahead of their use.
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
         const int r = r_nb[nb];
-        const uint32_t w = (r >= 0 && j0 < P.N)
-                               ? P.sym32[((size_t)(r >> 6) * (P.N256 / 4) + (j0 >> 2)) * 64 + (r & 63)]
-                               : 0x7F7F7F7Fu;  // code 0
-        symw[mb][nb][g] = w;
+        symw[mb][nb][g] = (r >= 0 && j0 < P.N)
+                              ? P.sym32[((size_t)(r >> 6) * (P.N256 / 4) + (j0 >> 2)) * 64 + (r & 63)]
+                              : 0x7F7F7F7Fu;  // code 0
+      }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
+        const int r = r_nb[nb];
+        const uint32_t w = symw[mb][nb][g];
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
           const int v = 4 * g + i;
@@ -688,6 +729,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_dequant(DeqP P) {
           }
         }
       }
+  }
   float *xch = reinterpret_cast<float *>(lds + kXchOff);
   if (lane < 32) {
 #pragma unroll
