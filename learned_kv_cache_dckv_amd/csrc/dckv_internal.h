@@ -29,6 +29,7 @@ constexpr uint16_t kVersion = 1;
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kBK = 64;
+constexpr int kEscLdsMax = 2048;  // escape records a dequantisation tile keeps in LDS
 
 // fixed shapes supported by the kernels
 constexpr int kD = 6144;
@@ -89,13 +90,14 @@ struct Ctrl {
   uint64_t esc_off;      // byte offset of the escape section in the stream
   uint64_t rans_off;     // byte offset of the rANS section in the stream
   uint64_t offs_off;     // byte offset of the group offsets in the stream
-  uint32_t pad[52];
+  uint32_t n_esc_tiles[2];  // decode: dequantisation tiles with escapes, per kind (records in LDS / not)
+  uint32_t pad[50];
 };
 static_assert(sizeof(Ctrl) == 256, "ctrl block is 256 bytes");
 
 struct Layout {
   uint64_t ctrl, sym, mean, esc_raw, esc_sorted, halo_a, halo_b, scratch, gwords, goffs;
-  uint64_t yhat_b, h_b, rope_lo, rope_hi, total;
+  uint64_t yhat_b, h_b, rope_lo, rope_hi, esc_tiles, esc_rows, esc_list, total;
 };
 
 Geometry geometry(const dckv_plan_t *p, int64_t T);
@@ -112,6 +114,21 @@ struct KernelTimer {
   const char *name_;
   hipStream_t s_;
   hipEvent_t a_ = nullptr, b_ = nullptr;
+};
+
+// ---- a second stream for work that may run beside the caller's ---------------
+// One library-owned stream per device (default priority, non-blocking).  The
+// constructor makes it wait for the work already enqueued on `parent`; join()
+// makes `parent` wait for the work enqueued on it since.  If a HIP call fails,
+// stream() is `parent` itself and the work simply runs in order.
+class SideStream {
+ public:
+  explicit SideStream(hipStream_t parent);
+  hipStream_t stream() const { return side_; }
+  void join();
+
+ private:
+  hipStream_t parent_, side_;
 };
 
 // ---- launchers (rans.hip / gemm.hip / misc.hip) -----------------------------

@@ -68,7 +68,8 @@ constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 64 KiB per stage
 constexpr int kOutStride = 128 + 8;                       // bf16 per row of a wave's output tile
 constexpr int kOutWaveBytes = 128 * kOutStride * 2;
 constexpr int kXchOff = 4 * kOutWaveBytes;                // row-0 exchange between the two wave rows
-constexpr int kLdsBytes = kXchOff + 2 * 256 * 4;
+constexpr int kEscLdsOff = kXchOff + 2 * 256 * 4;         // escape records of a dequantisation tile
+constexpr int kLdsBytes = kEscLdsOff + kEscLdsMax * 8;
 static_assert(kStages * kStageBytes <= kXchOff, "stages must not overlap the exchange area");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
 constexpr float kQLimit = 2147483520.0f;  // largest float below 2^31
@@ -620,28 +621,52 @@ struct DeqP {
   const uint8_t *ws;
   uint16_t *yhat_b;  // [NM][C]
   float *halo_a, *halo_b;
+  const uint32_t *esc_tiles;  // [n_mt][n_nt]: 0 no escaped code, 1 escapes (records fit in LDS), 2 more
+  const uint32_t *esc_rows;   // [n_mt][2]: index range of the escapes of a row tile
+  const uint32_t *esc_list;   // [2][n_mt * n_nt]: tiles of escape kinds 1 and 2
   int64_t N, N256;
   int Ca, keep_head, vocab, n_mt, n_nt;
   int32_t *status;
 };
 
-__device__ __forceinline__ int esc_code(const DeqP &P, uint32_t flat) {
-  const Ctrl *ct = reinterpret_cast<const Ctrl *>(P.ws);
-  const uint32_t *esc = reinterpret_cast<const uint32_t *>(P.stream + ct->esc_off);
-  uint32_t lo = 0, hi = ct->n_esc;
+// Escape records {flat, q} of the tile's rows, sorted by flat: in LDS
+// (address space 3) or, when too many, in the stream (address space 1).  The
+// typed pointer tells the compiler the records cannot alias the accumulators.
+template <int kAS>
+struct EscRecs {
+  const uint32_t __attribute__((address_space(kAS))) *rec;
+  uint32_t n;
+};
+
+// The code of an escaped position: binary search of its flat index.  Out of
+// line, so that the fully unrolled epilogue stays small (its accumulators
+// then stay in registers); it runs only at escaped positions.
+template <int kAS>
+__device__ __noinline__ int esc_code(int32_t *status, const uint32_t __attribute__((address_space(kAS))) *rec,
+                                     uint32_t n, uint32_t flat) {
+  uint32_t lo = 0, hi = n;
   while (lo < hi) {
     const uint32_t mid = (lo + hi) >> 1;
-    if (esc[2 * mid] < flat) lo = mid + 1; else hi = mid;
+    if (rec[2 * mid] < flat) lo = mid + 1; else hi = mid;
   }
-  if (lo < ct->n_esc && esc[2 * lo] == flat) return (int)esc[2 * lo + 1];
-  set_status(const_cast<int32_t *>(P.status), DCKV_ECORRUPT);
+  if (lo < n && rec[2 * lo] == flat) return (int)rec[2 * lo + 1];
+  set_status(status, DCKV_ECORRUPT);
   return 0;
 }
 
-__device__ __forceinline__ float code_of(const DeqP &P, uint32_t w, int i, int64_t j, int r) {
+// Code of byte i of a symbol word.  Tiles without escapes (kMode 0) take the
+// slot as it is; tiles with escapes look escaped codes up in their records.
+template <int kMode>
+struct EscOf {
+  typedef EscRecs<kMode == 2 ? 1 : 3> type;
+};
+
+template <int kMode>
+__device__ __forceinline__ float code_of(const DeqP &P, const typename EscOf<kMode>::type &E, uint32_t w, int i,
+                                         int64_t j, int r) {
   const uint32_t s = (w >> (8 * i)) & 0xFFu;
-  if (s != (uint32_t)kEsc) return (float)((int)s - 127);
-  return (float)esc_code(P, (uint32_t)(j * P.Ca + r));
+  if (kMode == 0 || s != (uint32_t)kEsc) return (float)((int)s - 127);
+  return (float)esc_code(P.status, E.rec, E.n, (uint32_t)(j * P.Ca + r));
 }
 
 // bf16 of fn(value) for all 128x128 values of the wave into its LDS tile
@@ -664,11 +689,138 @@ struct Identity {
   __device__ float operator()(float x) const { return x; }
 };
 
-__global__ __launch_bounds__(kThreads, 1) void k_dequant(DeqP P) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  if (wg_stop(P.status)) return;
-  int mt, nt;
-  tile_of(blockIdx.x, P.n_mt * P.n_nt, P.n_nt, mt, nt);
+// Epilogue of the dequantisation GEMM: the two checkerboard passes on the
+// accumulators (mu = H E[tok]) and the bf16 rows of yhat.
+template <int kMode>
+__device__ __forceinline__ void dequant_epilogue(const DeqP &P, const typename EscOf<kMode>::type &E,
+                                                 const f32x16 (&acc)[4][4], char *lds, int mt, int64_t m0, int n0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t wrow0 = m0 + wm * 128;
+  const bool defer_last = m0 + kBM < P.N;
+  float *xch = reinterpret_cast<float *>(lds + kXchOff);
+  char *wtile = lds + wave * kOutWaveBytes;
+
+  // The epilogue works one 32x32 block (16 values per lane) at a time, down
+  // each block column: pass 1 (even rows) of block mb + 1, then pass 2 (odd
+  // rows) of block mb, whose last quad needs the first row of block mb + 1.
+  // Symbol words of a block are loaded one block ahead.
+  auto load_words = [&](int mb, int r, uint32_t (&w)[4]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
+      w[g] = (r >= 0 && j0 < P.N) ? P.sym32[((size_t)(r >> 6) * (P.N256 / 4) + (j0 >> 2)) * 64 + (r & 63)]
+                                  : 0x7F7F7F7Fu;  // code 0
+    }
+  };
+  // pass 1: yhat = mu + q step on the even rows; rows past the end are zero
+  auto pass1 = [&](f32x16 &b, const uint32_t (&w)[4], int mb, int r, float st) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        if (j0 + i < P.N) {
+          const float q = r >= 0 ? code_of<kMode>(P, E, w[g], i, j0 + i, r) : 0.f;
+          b[4 * g + i] = b[4 * g + i] + q * st;
+        } else {
+          b[4 * g + i] = 0.f;
+        }
+      }
+    }
+  };
+  // pass 2: yhat = mu + a (yhat_{j-1} + yhat_{j+1}) + q step on the odd rows;
+  // `nx` is the next block (its first row follows this block's last quad)
+  auto pass2 = [&](f32x16 &b, const f32x16 &nx, float ext, const uint32_t (&w)[4], int mb, int r, int c, float st,
+                   float a) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // first row of the next quad: lanes < 32 find it in lane + 32 (same
+      // group), lanes >= 32 in lane - 32 (next group, or the next block)
+      const float same = __shfl_xor(b[4 * g], 32);
+      const float nxt = g < 3 ? __shfl_xor(b[4 * g + 4], 32) : (mb < 3 ? __shfl_xor(nx[0], 32) : ext);
+      const float next3 = lane < 32 ? same : nxt;
+      const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
+      const float y0 = b[4 * g], y2 = b[4 * g + 2];
+      if (j0 + 1 < P.N) {
+        const float q = r >= 0 ? code_of<kMode>(P, E, w[g], 1, j0 + 1, r) : 0.f;
+        b[4 * g + 1] = b[4 * g + 1] + a * (y0 + y2) + q * st;
+      } else {
+        b[4 * g + 1] = 0.f;
+      }
+      if (j0 + 3 < P.N) {
+        const float q = r >= 0 ? code_of<kMode>(P, E, w[g], 3, j0 + 3, r) : 0.f;
+        if (wm == 1 && mb == 3 && g == 3 && lane >= 32 && defer_last)
+          P.halo_a[(int64_t)mt * kC + c] = b[4 * g + 3] + a * y2 + q * st;  // finished by the fix-up
+        else
+          b[4 * g + 3] = b[4 * g + 3] + a * (y2 + next3) + q * st;
+      } else {
+        b[4 * g + 3] = 0.f;
+      }
+    }
+  };
+
+  // row 0 of every wave tile, after pass 1: to the wave above (LDS) and, for
+  // the tile's row 0, to the fix-up of the previous tile (global)
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int c = n0 + wn * 128 + nb * 32 + (lane & 31);
+    const int r = P.rank[c];
+    uint32_t w[4];
+    load_words(0, r, w);
+    f32x16 b = acc_block(acc, 0, nb);
+    pass1(b, w, 0, r, P.step[c]);
+    if (lane < 32) {
+      xch[wm * 256 + wn * 128 + nb * 32 + lane] = b[0];
+      if (wm == 0) P.halo_b[(int64_t)mt * kC + c] = b[0];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int c = n0 + wn * 128 + nb * 32 + (lane & 31);
+    const int r = P.rank[c];
+    const float st = P.step[c], a = P.nbr[c];
+    const float ext = wm == 0 ? xch[256 + wn * 128 + nb * 32 + (lane & 31)] : 0.f;
+    uint32_t w_cur[4], w_nxt[4];
+    load_words(0, r, w_cur);
+    f32x16 cur = acc_block(acc, 0, nb);
+    pass1(cur, w_cur, 0, r, st);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      f32x16 nxt = cur;
+      if (mb < 3) {
+        load_words(mb + 1, r, w_nxt);
+        nxt = acc_block(acc, mb + 1, nb);
+        pass1(nxt, w_nxt, mb + 1, r, st);
+      }
+      pass2(cur, nxt, ext, w_cur, mb, r, c, st, a);
+      // bf16 yhat of this block into the wave's LDS tile
+#pragma unroll
+      for (int v = 0; v < 16; ++v) put(wtile, acc_row(mb, v, lane), nb * 32 + (lane & 31), f2bf(cur[v]));
+      __builtin_amdgcn_sched_barrier(0);
+      if (mb < 3) {
+        cur = nxt;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) w_cur[g] = w_nxt[g];
+      }
+    }
+  }
+  // bf16 yhat rows from LDS (the exchange area lies beyond the wave tiles)
+  wave_lds_sync();
+  const int64_t col_lo = n0 + wn * 128;
+  flush_rows(wtile, P.yhat_b, kC, wrow0, col_lo, col_lo + 64, P.N);
+}
+
+// Three instances, one per kind of tile (marked while parsing): 0 no escaped
+// code, 1 escapes whose records fit in LDS, 2 more records than that.  Kind 0
+// walks the whole grid and skips escape tiles; kinds 1 and 2 take their tiles
+// from the parser's lists, one per workgroup, and the surplus workgroups
+// return at once.  Every tile is computed once, and the escape-free instance
+// keeps a register allocation of its own.
+// One dequantisation tile: the mean GEMM and its epilogue.
+template <int kMode>
+__device__ __forceinline__ void dequant_tile(const DeqP &P, char *lds, int mt, int nt) {
   const int64_t m0 = (int64_t)mt * kBM;
   const int n0 = nt * kBN;
   Operand A, B;
@@ -682,101 +834,47 @@ __global__ __launch_bounds__(kThreads, 1) void k_dequant(DeqP P) {
   }
   f32x16 acc[4][4];
   mainloop(A, B, kEmb / kBK, acc, lds);
+  typename EscOf<kMode>::type E{nullptr, 0u};
+  if (kMode != 0) {
+    // the escape records of this tile's rows
+    const Ctrl *ct = reinterpret_cast<const Ctrl *>(P.ws);
+    const uint32_t lo = P.esc_rows[2 * mt], hi = P.esc_rows[2 * mt + 1];
+    const uint32_t *grec = reinterpret_cast<const uint32_t *>(P.stream + ct->esc_off) + 2ull * lo;
+    E.n = hi - lo;
+    if (kMode == 1) {
+      uint32_t *lrec = reinterpret_cast<uint32_t *>(lds + kEscLdsOff);
+      for (uint32_t i = threadIdx.x; i < 2 * E.n; i += kThreads) lrec[i] = grec[i];
+      __syncthreads();
+      E.rec = (decltype(E.rec))(lrec);
+    } else {
+      E.rec = (decltype(E.rec))(grec);
+    }
+  }
+  dequant_epilogue<kMode>(P, E, acc, lds, mt, m0, n0);
+}
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t wrow0 = m0 + wm * 128;
-  int r_nb[4], c_nb[4];
-  float st_nb[4], a_nb[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int c = n0 + wn * 128 + nb * 32 + (lane & 31);
-    c_nb[nb] = c;
-    r_nb[nb] = P.rank[c];
-    st_nb[nb] = P.step[c];
-    a_nb[nb] = P.nbr[c];
+// Three instances, one per kind of tile (marked while parsing): 0 no escaped
+// code, 1 escapes whose records fit in LDS, 2 more records than that.  Kind 0
+// walks the whole grid and skips escape tiles; kinds 1 and 2 take their tiles
+// from the parser's lists, one per workgroup, and the surplus workgroups
+// return at once.  Every tile is computed once, and the escape-free instance
+// keeps a register allocation of its own.
+template <int kMode>
+__global__ __launch_bounds__(kThreads, 1) void k_dequant(DeqP P) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  int mt, nt;
+  if (kMode == 0) {
+    tile_of(blockIdx.x, P.n_mt * P.n_nt, P.n_nt, mt, nt);
+    if (P.esc_tiles[mt * P.n_nt + nt] != 0u) return;
+  } else {
+    const Ctrl *ct = reinterpret_cast<const Ctrl *>(P.ws);
+    if (blockIdx.x >= ct->n_esc_tiles[kMode - 1]) return;
+    const uint32_t tile = P.esc_list[(kMode - 1) * (P.n_mt * P.n_nt) + blockIdx.x];
+    mt = (int)(tile / P.n_nt);
+    nt = (int)(tile - (uint32_t)mt * P.n_nt);
   }
-  uint32_t symw[4][4][4];
-  // pass 1: even rows, yhat = mu + q step.  The 16 symbol words of a block
-  // row are loaded together, ahead of their use.
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
-        const int r = r_nb[nb];
-        symw[mb][nb][g] = (r >= 0 && j0 < P.N)
-                              ? P.sym32[((size_t)(r >> 6) * (P.N256 / 4) + (j0 >> 2)) * 64 + (r & 63)]
-                              : 0x7F7F7F7Fu;  // code 0
-      }
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
-        const int r = r_nb[nb];
-        const uint32_t w = symw[mb][nb][g];
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const int v = 4 * g + i;
-          if (j0 + i < P.N) {
-            const float q = r >= 0 ? code_of(P, w, i, j0 + i, r) : 0.f;
-            acc[mb][nb][v] = acc[mb][nb][v] + q * st_nb[nb];
-          } else {
-            acc[mb][nb][v] = 0.f;
-          }
-        }
-      }
-  }
-  float *xch = reinterpret_cast<float *>(lds + kXchOff);
-  if (lane < 32) {
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      xch[wm * 256 + wn * 128 + nb * 32 + lane] = acc[0][nb][0];
-      if (wm == 0) P.halo_b[(int64_t)mt * kC + c_nb[nb]] = acc[0][nb][0];
-    }
-  }
-  __syncthreads();
-  const bool defer_last = m0 + kBM < P.N;
-  // pass 2: odd rows read only even rows, so they are overwritten in place
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const float ext = wm == 0 ? xch[256 + wn * 128 + nb * 32 + (lane & 31)] : 0.f;
-      const float a = a_nb[nb];
-      const int r = r_nb[nb];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float next3 = next_quad_row0(acc, mb, nb, g, ext, lane);
-        const uint32_t w = symw[mb][nb][g];
-        const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
-        const float y0 = acc[mb][nb][4 * g], y2 = acc[mb][nb][4 * g + 2];
-        if (j0 + 1 < P.N) {
-          const float q = r >= 0 ? code_of(P, w, 1, j0 + 1, r) : 0.f;
-          acc[mb][nb][4 * g + 1] = acc[mb][nb][4 * g + 1] + a * (y0 + y2) + q * st_nb[nb];
-        } else {
-          acc[mb][nb][4 * g + 1] = 0.f;
-        }
-        if (j0 + 3 < P.N) {
-          const float q = r >= 0 ? code_of(P, w, 3, j0 + 3, r) : 0.f;
-          if (wm == 1 && mb == 3 && g == 3 && lane >= 32 && defer_last)
-            P.halo_a[(int64_t)mt * kC + c_nb[nb]] = acc[mb][nb][4 * g + 3] + a * y2 + q * st_nb[nb];
-          else
-            acc[mb][nb][4 * g + 3] = acc[mb][nb][4 * g + 3] + a * (y2 + next3) + q * st_nb[nb];
-        } else {
-          acc[mb][nb][4 * g + 3] = 0.f;
-        }
-      }
-    }
-  // bf16 yhat rows through LDS (the exchange area lies beyond the wave tiles)
-  char *wtile = lds + wave * kOutWaveBytes;
-  acc_to_wtile(acc, wtile, lane, Identity());
-  wave_lds_sync();
-  const int64_t col_lo = n0 + wn * 128;
-  flush_rows(wtile, P.yhat_b, kC, wrow0, col_lo, col_lo + 64, P.N);
+  if (wg_stop(P.status)) return;
+  dequant_tile<kMode>(P, lds, mt, nt);
 }
 
 __global__ void k_decode_fixup(DeqP P, int64_t n_fix) {
@@ -1050,6 +1148,9 @@ static DeqP deq_params(const DecodeArgs &a) {
   P.yhat_b = reinterpret_cast<uint16_t *>(a.ws + a.l.yhat_b);
   P.halo_a = reinterpret_cast<float *>(a.ws + a.l.halo_a);
   P.halo_b = reinterpret_cast<float *>(a.ws + a.l.halo_b);
+  P.esc_tiles = reinterpret_cast<const uint32_t *>(a.ws + a.l.esc_tiles);
+  P.esc_rows = reinterpret_cast<const uint32_t *>(a.ws + a.l.esc_rows);
+  P.esc_list = reinterpret_cast<const uint32_t *>(a.ws + a.l.esc_list);
   P.N = a.g.N;
   P.N256 = a.g.N256;
   P.Ca = a.p->C_a;
@@ -1064,7 +1165,14 @@ static DeqP deq_params(const DecodeArgs &a) {
 void launch_dequant_gemm(const DecodeArgs &a) {
   if (a.g.N == 0) return;
   DeqP P = deq_params(a);
-  launch_gemm(k_dequant, "dequant_gemm", P.n_mt * P.n_nt, P, a.s);
+  // the tiles with escaped codes (few, slower) run on a side stream, beside
+  // the escape-free tiles on the caller's stream; the caller's stream then
+  // waits for both
+  SideStream side(a.s);
+  launch_gemm(k_dequant<1>, "dequant_gemm_esc", P.n_mt * P.n_nt, P, side.stream());
+  launch_gemm(k_dequant<2>, "dequant_gemm_esc", P.n_mt * P.n_nt, P, side.stream());
+  launch_gemm(k_dequant<0>, "dequant_gemm", P.n_mt * P.n_nt, P, a.s);
+  side.join();
 }
 
 void launch_decode_fixup(const DecodeArgs &a) {

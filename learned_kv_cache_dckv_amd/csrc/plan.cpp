@@ -345,6 +345,9 @@ Layout dckv::layout(const dckv_plan_t *p, const Geometry &g) {
   // decode-only region (overlaps the encode-only one)
   off = shared_end;
   l.yhat_b = take((uint64_t)g.NM * p->C * 2);
+  l.esc_tiles = take((uint64_t)g.n_mtiles * (p->C / kBN) * 4);
+  l.esc_rows = take((uint64_t)g.n_mtiles * 2 * 4);
+  l.esc_list = take((uint64_t)g.n_mtiles * (p->C / kBN) * 2 * 4);
   l.h_b = take((uint64_t)g.NM * p->hidden * 2);
   l.rope_lo = take(256ull * kHalf * 8);
   l.rope_hi = take((uint64_t)g.rope_hi * kHalf * 8);
@@ -421,6 +424,44 @@ void drain_locked(ProfState &s) {
   s.pending.clear();
 }
 }  // namespace
+
+// ---- side streams -------------------------------------------------------------
+namespace {
+
+std::mutex g_side_mu;
+hipStream_t g_side[64] = {};
+
+// order `to` after the work enqueued so far on `from`
+bool stream_wait(hipStream_t to, hipStream_t from) {
+  hipEvent_t e;
+  if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return false;
+  const bool ok = hipEventRecord(e, from) == hipSuccess && hipStreamWaitEvent(to, e, 0) == hipSuccess;
+  (void)hipEventDestroy(e);  // released once the wait has been satisfied
+  return ok;
+}
+
+}  // namespace
+
+SideStream::SideStream(hipStream_t parent) : parent_(parent), side_(parent) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
+  hipStream_t s;
+  {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    if (!g_side[dev] && hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking) != hipSuccess) {
+      g_side[dev] = nullptr;
+      return;
+    }
+    s = g_side[dev];
+  }
+  if (stream_wait(s, parent)) side_ = s;
+}
+
+void SideStream::join() {
+  if (side_ == parent_) return;
+  if (!stream_wait(parent_, side_)) (void)hipStreamSynchronize(side_);
+  side_ = parent_;
+}
 
 KernelTimer::KernelTimer(const char *name, hipStream_t s) : name_(name), s_(s) {
   ProfState &st = prof();

@@ -141,10 +141,14 @@ def test_codec_escapes_and_outliers():
 
 
 def test_codec_many_escapes_use_global_sort():
+    # more than 4096 escapes: the encoder sorts them in global memory, and row
+    # tiles hold more escape records than the decoder keeps in LDS
     rows, tok = synth.random_rows(132 + 600, seed=78)
     rows = bf16.from_f64(bf16.to_f64(rows) * 60.0)
-    data, enc, plan, p = _run_case(rows, tok, synth.step_scale_for(400.0), check_rows=False, min_agree=0.99)
+    data, enc, plan, p = _run_case(rows, tok, synth.step_scale_for(400.0), min_agree=0.99)
     assert len(enc.esc_flat) > 4096
+    per_row_tile = np.bincount(enc.esc_flat // p.c_active // 256)
+    assert per_row_tile.max() > 2048
 
 
 def test_codec_with_dropped_components():
