@@ -10,6 +10,18 @@
 namespace dckv {
 namespace {
 
+// The kept rows (first keep_head and last keep_tail positions) into the
+// stream, verbatim and in position order: one workgroup per row, 16-byte
+// vectors (rows and stream are 16-byte aligned, rows are D * 2 bytes).
+__global__ __launch_bounds__(256) void k_kept_copy(const uint16_t *rows, uint8_t *dst, int64_t D, int64_t head_n,
+                                                   int64_t tail_row0) {
+  const int64_t k = blockIdx.x;
+  const int64_t src_row = k < head_n ? k : tail_row0 + (k - head_n);
+  const uint4 *src = reinterpret_cast<const uint4 *>(rows + src_row * D);
+  uint4 *out = reinterpret_cast<uint4 *>(dst + k * D * 2);
+  for (int64_t i = threadIdx.x; i < D / 8; i += blockDim.x) out[i] = src[i];
+}
+
 __global__ void k_init(uint8_t *ws, int32_t *status, uint64_t *stream_bytes) {
   if (threadIdx.x == 0) {
     Ctrl *ct = reinterpret_cast<Ctrl *>(ws);
@@ -90,14 +102,10 @@ void launch_init(const DecodeArgs &a) {
 }
 
 void launch_kept_copy(const EncodeArgs &a) {
+  if (a.g.n_kept == 0) return;
   const int64_t head_n = std::min<int64_t>(a.p->keep_head, a.g.T);
-  const size_t row = (size_t)a.p->D * 2;
-  uint8_t *dst = a.stream + kHeaderBytes;
-  if (head_n > 0) (void)hipMemcpyAsync(dst, a.rows, head_n * row, hipMemcpyDeviceToDevice, a.s);
-  const int64_t tail_n = a.g.n_kept - head_n;
-  if (tail_n > 0)
-    (void)hipMemcpyAsync(dst + head_n * row, a.rows + (size_t)(a.p->keep_head + a.g.N) * a.p->D, tail_n * row,
-                         hipMemcpyDeviceToDevice, a.s);
+  hipLaunchKernelGGL(k_kept_copy, dim3((unsigned)a.g.n_kept), dim3(256), 0, a.s, a.rows, a.stream + kHeaderBytes,
+                     (int64_t)a.p->D, head_n, (int64_t)a.p->keep_head + a.g.N);
 }
 
 void launch_esc_sort(const EncodeArgs &a) {

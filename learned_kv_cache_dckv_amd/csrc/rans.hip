@@ -373,13 +373,19 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
     const int l = idx >> 8, s = idx & 255;
     tab[l * kTabStride + s] = P.tab[(size_t)(kLanes * g + l) * 256 + s];
   }
-  for (int idx = threadIdx.x; idx < n * kBuckets; idx += blockDim.x) {
-    const int l = idx / kBuckets, bb = idx - l * kBuckets;
-    bkt[l * kBktStride + bb] = P.bucket[(size_t)kLanes * g * kBuckets + idx];
+  for (int idx = threadIdx.x; idx < n * (kBuckets + 1); idx += blockDim.x) {
+    // bucket row of lane l: first symbol of each slot bucket, then the last
+    // symbol as the upper bound of the last bucket
+    const int l = idx / (kBuckets + 1), bb = idx - l * (kBuckets + 1);
+    bkt[l * kBktStride + bb] =
+        bb < kBuckets ? P.bucket[(size_t)kLanes * g * kBuckets + (size_t)l * kBuckets + bb] : (uint8_t)(kNSym - 1);
   }
   __syncthreads();
   if (*P.status != 0) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // per-wave values are kept in scalar registers: the step loop is uniform,
+  // and lanes that decode nothing at a step take the same path with their
+  // results discarded
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t b = (int64_t)blockIdx.x * kDecWaves + wave;
   if (b >= P.n_blk) return;
   const Ctrl *ct = reinterpret_cast<const Ctrl *>(P.ws);
@@ -411,6 +417,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
       uint32_t mid = (lo2 + hi2) >> 1;
       if ((uint64_t)esc[2 * mid] < f_hi) lo2 = mid + 1; else hi2 = mid;
     }
+    lo = __builtin_amdgcn_readfirstlane(lo);
+    lo2 = __builtin_amdgcn_readfirstlane(lo2);
     if (lo2 > lo) {
       has_esc = true;
       for (int i = lane; i < kBlock; i += 64) ebits[wave][i] = 0ull;
@@ -434,31 +442,31 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
   uint32_t ptr = 2u * (uint32_t)n;
   const uint32_t *mytab = tab + lane * kTabStride;
   const uint8_t *mybkt = bkt + lane * kBktStride;
-  const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   uint32_t *sout = P.sym32 + ((size_t)g * (P.N256 / 4) + (size_t)b * 64) * 64 + lane;
   bool overrun = false;
   uint32_t acc = 0xFFFFFFFFu;
   for (int i = 0; i < Lb; ++i) {
     bool act = lane_ok;
-    if (has_esc && ((ebits[wave][i] >> lane) & 1ull)) act = false;
-    uint32_t s = (uint32_t)kEsc;
-    bool need = false;
-    if (act) {
-      const uint32_t slot = x & (kM - 1u);
-      // the symbol lies between the first symbols of this bucket and the next
-      const uint32_t bi = slot >> kBucketShift;
-      uint32_t lo = mybkt[bi];
-      uint32_t hi = bi + 1 < (uint32_t)kBuckets ? (uint32_t)mybkt[bi + 1] : (uint32_t)(kNSym - 1);
-      while (lo < hi) {
-        const uint32_t mid = (lo + hi + 1) >> 1;
-        if ((mytab[mid] >> 16) <= slot) lo = mid; else hi = mid - 1;
-      }
-      const uint32_t sy = lo;
-      const uint32_t e = mytab[sy];
-      x = (e & 0xFFFFu) * (x >> kPrecBits) + slot - (e >> 16);
-      s = sy;
-      need = x < kL;
+    if (has_esc) act = act && !((ebits[wave][i] >> lane) & 1ull);
+    const uint32_t slot = x & (kM - 1u);
+    // the symbol lies between the first symbols of this bucket and the next;
+    // search while any lane's range holds more than one symbol
+    const uint32_t bi = slot >> kBucketShift;
+    uint32_t lo = mybkt[bi];
+    uint32_t hi = act ? (uint32_t)mybkt[bi + 1] : lo;
+    while (__ballot(lo < hi)) {
+      const uint32_t mid = (lo + hi + 1) >> 1;
+      const bool up = (mytab[mid] >> 16) <= slot;
+      const bool open = lo < hi;
+      lo = open && up ? mid : lo;
+      hi = open && !up ? mid - 1 : hi;
     }
+    const uint32_t e = mytab[lo];
+    // f * (x >> 15) < 2^32: f <= 2^15 and x >> 15 < 2^17 (24-bit multiply)
+    const uint32_t xd = __umul24(e & 0xFFFFu, x >> kPrecBits) + slot - (e >> 16);
+    x = act ? xd : x;
+    const uint32_t s = act ? lo : (uint32_t)kEsc;
+    const bool need = act && x < kL;
     const uint64_t mask = __ballot(need);
     const uint32_t cnt = (uint32_t)__popcll(mask);
     if (cnt) {
@@ -468,11 +476,13 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
         for (uint32_t k = lane; k < kWordBuf && base + k < W; k += 64) wb[k] = wsrc[base + k];
         wave_sync_lds();
       }
-      if (need) {
-        const uint32_t idx = ptr + (uint32_t)__popcll(mask & lower);
-        if (idx < W && idx - base < (uint32_t)kWordBuf) x = (x << 16) | wb[idx - base];
-        else overrun = true;
-      }
+      const uint32_t before = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+      const uint32_t idx = ptr + before;
+      const bool ok = idx < W && idx - base < (uint32_t)kWordBuf;
+      const uint32_t wv = wb[ok ? idx - base : 0u];
+      x = need && ok ? (x << 16) | wv : x;
+      overrun = overrun || (need && !ok);
       ptr += cnt;
     }
     const int k = i & 3;
