@@ -1,11 +1,13 @@
 """Benchmark of the DCKV prompt-KV-cache codec on one MI355X.
 
 One step is the whole hot path over one synthetic request: encode of the
-32,768-token prompt (kept-row copy, embedding mean, analysis GEMM with the
-quantiser and the checkerboard passes, escapes, rANS, packing) followed by
-its decode (parse, rANS, mean GEMM with the two dequantisation passes,
-correction MLP, synthesis with RoPE, kept rows).  Inputs are resident in HBM
-before the timed region.  Prints one JSON line.
+32,768-token prompt (kept-row copy, analysis GEMM with the quantiser and the
+checkerboard passes, its means gathered from the plan's embedding-mean table,
+escapes, rANS, packing) followed by its decode (parse, rANS, the two
+dequantisation passes over the table's means, correction MLP, synthesis with
+RoPE, kept rows).  Inputs are resident in HBM before the timed region; the
+plan (with its table) is built before it, once per rate.  Prints one JSON
+line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 
@@ -47,10 +49,9 @@ def kernel_work(name: str, N: int, Ca: int, rans_bytes: int):
     """(bound, algorithmic units per launch, unit) of each timed kernel."""
     if name == "analysis_gemm":
         return "mfma", 2.0 * N * Ca * 6144, "flop"
-    if name == "mean_gemm":
-        return "mfma", 2.0 * N * Ca * 2048, "flop"
-    if name == "dequant_gemm":
-        return "mfma", 2.0 * N * 2048 * 2048, "flop"
+    if name == "dequant":
+        # per coded row: its table row of means (fp32), its symbols, its bf16 output
+        return "hbm", float(N) * (2048 * 4 + Ca + 2048 * 2), "byte"
     if name == "w1_gemm":
         return "mfma", 2.0 * N * 256 * 2048, "flop"
     if name == "synthesis_gemm":
@@ -61,9 +62,8 @@ def kernel_work(name: str, N: int, Ca: int, rans_bytes: int):
 
 
 KERNEL_SOURCES = {  # profile name -> (kernel symbol, source file)
-    "mean_gemm": ("k_mean_enc", "gemm.hip"),
     "analysis_gemm": ("k_analysis_quant", "gemm.hip"),
-    "dequant_gemm": ("k_dequant", "gemm.hip"),
+    "dequant": ("k_dequant", "gemm.hip"),
     "w1_gemm": ("k_w1", "gemm.hip"),
     "synthesis_gemm": ("k_synthesis", "gemm.hip"),
     "rans_encode": ("k_rans_encode", "rans.hip"),
@@ -220,8 +220,8 @@ def main(argv=None) -> int:
     ms_step = e0.elapsed_time(e1) / args.steps
     dk.dckv_profile_enable(False)
     kern = {}
-    for name in ("mean_gemm", "analysis_gemm", "fixup", "rans_encode", "scan", "pack", "parse", "rans_decode",
-                 "dequant_gemm", "dequant_gemm_esc", "w1_gemm", "synthesis_gemm"):
+    for name in ("analysis_gemm", "fixup", "rans_encode", "scan", "pack", "parse", "rans_decode",
+                 "dequant", "w1_gemm", "synthesis_gemm"):
         tot, n = dk.dckv_profile_read(name)
         if n:
             kern[name] = {"avg_ms": tot / n, "launches": n}

@@ -61,7 +61,8 @@ typedef enum {
 
 /* Codec parameters.  Matrices are bf16 row-major device arrays owned by the
  * caller; they must stay alive and unchanged while any plan made from them
- * exists.  The three vectors are read on the host during dckv_plan(). */
+ * exists (embedding and mean_head are read only by dckv_plan()).  The three
+ * vectors are read on the host during dckv_plan(). */
 typedef struct {
   int32_t n_layers, n_kv_heads, head_dim;   /* 6, 2, 256 -> D = 6144 */
   int32_t n_coef, n_hidden, emb_dim, vocab; /* 2048, 256, 2048, any >= 1 */
@@ -102,15 +103,30 @@ int dckv_plan_tables(const float *base_step, const float *laplace_scale, int32_t
                      float step_scale, float *step_out, uint8_t *active_out,
                      uint16_t *freq_out, int32_t *c_active, uint32_t *crc);
 
-/* Builds a plan on the current HIP device (synchronous: host tables, then an
- * upload of about 1 MB).  *out receives the handle; free with dckv_plan_free.
- * Returns DCKV_EUNSUPPORTED for shapes the kernels do not support. */
+/* Builds a plan on the current HIP device, synchronously: host tables, an
+ * upload of about 1 MB, and the embedding-mean table (below), which the plan
+ * allocates (vocab * n_coef * 4 bytes: 256 MiB for a 32,768-token vocabulary)
+ * and computes with one GEMM on the null stream.  *out receives the handle;
+ * free with dckv_plan_free.  Returns DCKV_EUNSUPPORTED for shapes the kernels
+ * do not support, DCKV_ENOMEM when an allocation fails. */
 int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **out);
 int dckv_plan_free(dckv_plan_t *plan);
 
 /* Host copies of the plan's tables (any pointer may be NULL). */
 int dckv_plan_info(const dckv_plan_t *plan, float *step_out, uint8_t *active_out,
                    uint16_t *freq_out, int32_t *c_active, uint32_t *crc);
+
+/* The plan's embedding-mean table (DCKV digest, "How it works", Conditional
+ * entropy models: the code means of a position come from its token's input
+ * embedding).  The mean of every coefficient depends on the token id alone,
+ * so the plan holds it for the whole vocabulary:
+ *   table[v][i] = sum_k E[v][k] * H[col_component[i]][k]   (fp32, bf16 inputs)
+ * for v < vocab, row stride n_coef floats, where the columns are the active
+ * components in rank order, then the dropped ones in ascending order.
+ * *table (device, owned by the plan, valid until dckv_plan_free), *rows (host)
+ * = vocab, col_component (host) [n_coef]; any pointer may be NULL. */
+int dckv_plan_mean_table(const dckv_plan_t *plan, const float **table, int64_t *rows,
+                         int32_t *col_component);
 
 /* Pure host.  For a request of T tokens: the largest stream an encode can
  * produce (every code escaped or 16 bits) and the workspace bytes that
@@ -234,19 +250,8 @@ int dckv_entropy_decode(const dckv_plan_t *plan, const uint8_t *stream, uint64_t
  *                      symbol (j, rank r) at ((r/64)*(N256/4) + j/4)*256 + (r%64)*4 + j%4
  *   DCKV_VIEW_YHAT_B   bf16 [N][n_coef] decoded coefficients (row stride n_coef)
  *   DCKV_VIEW_H_B      bf16 [N][n_hidden] correction hidden units
- *   DCKV_VIEW_MEAN     fp32 embedding mean H E[tok] of the last encode, in
- *                      the order of the GEMM accumulators (row_stride 0: not
- *                      row-major).  With 256x256 tiles and n_nt = C_a rounded
- *                      up to 256, divided by 256: element (j, rank r) lies in
- *                      tile = (j/256)*n_nt + r/256, plane p = j%2 (even and odd
- *                      rows apart), w = 2*((j%256)/128) + (r%256)/128,
- *                      mb = (j%128)/32, nb = (r%128)/32, lane = (r%32) +
- *                      32*((j%8)/4), register v = 4*((j%32)/8) + j%4,
- *                      half h = v/8, element e = 2*((v/4)%2) + (v/2)%2, at
- *                      float index (tile*2 + p)*32768 +
- *                      ((((w*4 + mb)*4 + nb)*2 + h)*64 + lane)*4 + e
  * --------------------------------------------------------------------------*/
-enum { DCKV_VIEW_SYMBOLS = 0, DCKV_VIEW_YHAT_B = 1, DCKV_VIEW_H_B = 2, DCKV_VIEW_MEAN = 3 };
+enum { DCKV_VIEW_SYMBOLS = 0, DCKV_VIEW_YHAT_B = 1, DCKV_VIEW_H_B = 2 };
 int dckv_workspace_view(const dckv_plan_t *plan, int64_t T, int32_t which, uint64_t *offset,
                         uint64_t *bytes, int64_t *row_stride);
 
@@ -254,9 +259,9 @@ int dckv_workspace_view(const dckv_plan_t *plan, int64_t T, int32_t which, uint6
  * Kernel timing.  While enabled, every launch of the named kernels is
  * bracketed by HIP events on the call's stream; dckv_profile_read()
  * synchronises those events and returns the summed milliseconds and the
- * number of launches since the last reset.  Kernel names: "mean_gemm",
- * "analysis_gemm", "rans_encode", "rans_decode", "dequant_gemm", "w1_gemm",
- * "synthesis_gemm", "fixup", "pack", "parse".
+ * number of launches since the last reset.  Kernel names:
+ * "analysis_gemm", "rans_encode", "rans_decode", "dequant", "w1_gemm",
+ * "synthesis_gemm", "fixup", "scan", "pack", "parse".
  * --------------------------------------------------------------------------*/
 int dckv_profile_enable(int32_t on);
 int dckv_profile_reset(void);

@@ -5,7 +5,7 @@ arguments for the C ABI declared in ``include/dckv.h``; every step of encode
 and decode runs in the library's HIP kernels.  PyTorch provides device memory
 and the current HIP stream.
 
-The library must be built first (``python -m learned_kv_cache_dckv_amd.build``);
+The library must be built first (``python learned_kv_cache_dckv_amd/build.py``);
 importing this package without it raises ImportError.
 """
 from __future__ import annotations
@@ -21,10 +21,11 @@ LIB_PATH = os.path.join(_HERE, "libdckv.so")
 OK, EINVAL, ENOMEM, ECAPACITY, ECORRUPT, EPLAN, EHIP, EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6, -7
 STATUS_NAMES = {0: "OK", -1: "EINVAL", -2: "ENOMEM", -3: "ECAPACITY", -4: "ECORRUPT", -5: "EPLAN",
                 -6: "EHIP", -7: "EUNSUPPORTED"}
-VIEW_SYMBOLS, VIEW_YHAT_B, VIEW_H_B, VIEW_MEAN = 0, 1, 2, 3
+VIEW_SYMBOLS, VIEW_YHAT_B, VIEW_H_B = 0, 1, 2
 
 # every symbol include/dckv.h declares
-EXPORTS = ("dckv_plan_tables", "dckv_plan", "dckv_plan_free", "dckv_plan_info", "dckv_bytes", "dckv_encode",
+EXPORTS = ("dckv_plan_tables", "dckv_plan", "dckv_plan_free", "dckv_plan_info", "dckv_plan_mean_table",
+           "dckv_bytes", "dckv_encode",
            "dckv_decode", "dckv_bytes_batch", "dckv_encode_batch", "dckv_decode_batch", "dckv_entropy_encode",
            "dckv_entropy_decode", "dckv_workspace_view", "dckv_profile_enable", "dckv_profile_reset",
            "dckv_profile_read", "dckv_last_error")
@@ -56,7 +57,7 @@ class _Req(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libdckv.so is not built: run `python -m learned_kv_cache_dckv_amd.build` "
+        raise ImportError("libdckv.so is not built: run `python learned_kv_cache_dckv_amd/build.py` "
                           "(expected at %s)" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     P, U64, I64, I32, U32, F = (ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32,
@@ -66,6 +67,7 @@ def _load():
         "dckv_plan": [P, F, P],
         "dckv_plan_free": [P],
         "dckv_plan_info": [P, P, P, P, P, P],
+        "dckv_plan_mean_table": [P, P, P, P],
         "dckv_bytes": [P, I64, P, P],
         "dckv_encode": [P, P, P, I64, P, U64, P, P, P, U64, P],
         "dckv_decode": [P, P, U64, P, I64, P, P, P, U64, P],
@@ -232,6 +234,34 @@ def dckv_plan_info(plan: Plan) -> dict:
     freq = np.empty((max(ca.value, 1), 255), np.uint16)
     _check(_lib.dckv_plan_info(plan.handle, 0, 0, _ptr(freq), None, None))
     return dict(step=step, active=active.astype(bool), freq=freq[:ca.value], c_active=ca.value, crc=crc.value)
+
+
+def dckv_plan_mean_table(plan: Plan):
+    """(device address of the table, rows, col_component[n_coef]): the plan's
+    embedding-mean table, fp32 [rows][n_coef]."""
+    tab = ctypes.c_void_p()
+    rows = ctypes.c_int64()
+    cols = np.empty(plan.codec.n_coef, np.int32)
+    _check(_lib.dckv_plan_mean_table(plan.handle, ctypes.byref(tab), ctypes.byref(rows), _ptr(cols)))
+    return tab.value or 0, rows.value, cols
+
+
+class _DeviceArray:
+    """A device address with shape and dtype, for torch.as_tensor (no copy)."""
+
+    def __init__(self, addr: int, shape, typestr: str):
+        self.__cuda_array_interface__ = {"shape": tuple(shape), "typestr": typestr, "data": (int(addr), False),
+                                         "version": 2, "strides": None}
+
+
+def mean_table(plan: Plan):
+    """The plan's embedding-mean table as a torch float32 tensor [vocab][n_coef]
+    sharing the plan's memory (read only; valid while the plan lives), and
+    col_component: the component of each column."""
+    import torch
+    addr, rows, cols = dckv_plan_mean_table(plan)
+    t = torch.as_tensor(_DeviceArray(addr, (rows, plan.codec.n_coef), "<f4"), device=plan.codec.device)
+    return t, cols
 
 
 def dckv_bytes(plan: Plan, T: int):

@@ -1,6 +1,9 @@
 """Builds libdckv.so (HIP kernels + host runtime) for gfx950 with hipcc.
 
-    python -m learned_kv_cache_dckv_amd.build
+    python learned_kv_cache_dckv_amd/build.py
+
+Run as a script (or loaded by file path): importing the package itself needs
+the built library.
 
 Every source is compiled on each call (no up-to-date check), in parallel, and
 linked into ``learned_kv_cache_dckv_amd/libdckv.so`` in the source tree.

@@ -62,7 +62,6 @@ int encode_checks(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *
 void encode_sequence(const EncodeArgs &a) {
   launch_init(a);
   launch_kept_copy(a);
-  launch_mean_gemm(a);
   launch_analysis_gemm(a);
   launch_encode_fixup(a);
   launch_esc_sort(a);
@@ -88,8 +87,7 @@ void decode_sequence(const DecodeArgs &a) {
   launch_parse(a);
   launch_rope_tables(a);
   launch_rans_decode(a);
-  launch_dequant_gemm(a);
-  launch_decode_fixup(a);
+  launch_dequant(a);
   launch_w1_gemm(a);
   launch_synthesis_gemm(a);
   launch_kept_rope(a);

@@ -29,7 +29,6 @@ constexpr uint16_t kVersion = 1;
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kBK = 64;
-constexpr int kEscLdsMax = 2048;  // escape records a dequantisation tile keeps in LDS
 
 // fixed shapes supported by the kernels
 constexpr int kD = 6144;
@@ -45,6 +44,8 @@ struct PlanDev {
   float *nbr = nullptr;         // [C]
   int32_t *rank = nullptr;      // [C]   rank or -1
   int32_t *act = nullptr;       // [C_a] component of each rank (padded to a kBN multiple)
+  int32_t *perm = nullptr;      // [C]   component of each mean-table column: ranks, then dropped
+  int32_t *colpos = nullptr;    // [C]   mean-table column of each component
   uint32_t *tab = nullptr;      // [C_a][256]  f | cum << 16
   uint8_t *bucket = nullptr;    // [C_a][kBuckets] first symbol of each slot bucket
   double *omega = nullptr;      // [head_dim/2] RoPE frequencies
@@ -64,6 +65,9 @@ struct dckv_plan_s {
   const uint16_t *A, *S, *W1, *W2, *E, *H;
   dckv::PlanDev dev;
   void *dev_block = nullptr;  // one allocation holding every PlanDev array
+  // embedding-mean table [vocab][C] fp32: column i of row v is
+  // sum_k E[v][k] H[perm[i]][k] (its own allocation)
+  float *mtab = nullptr;
 };
 
 namespace dckv {
@@ -90,14 +94,13 @@ struct Ctrl {
   uint64_t esc_off;      // byte offset of the escape section in the stream
   uint64_t rans_off;     // byte offset of the rANS section in the stream
   uint64_t offs_off;     // byte offset of the group offsets in the stream
-  uint32_t n_esc_tiles[2];  // decode: dequantisation tiles with escapes, per kind (records in LDS / not)
-  uint32_t pad[50];
+  uint32_t pad[52];
 };
 static_assert(sizeof(Ctrl) == 256, "ctrl block is 256 bytes");
 
 struct Layout {
-  uint64_t ctrl, sym, mean, esc_raw, esc_sorted, halo_a, halo_b, scratch, gwords, goffs;
-  uint64_t yhat_b, h_b, rope_lo, rope_hi, esc_tiles, esc_rows, esc_list, total;
+  uint64_t ctrl, sym, esc_raw, esc_sorted, halo_a, halo_b, scratch, gwords, goffs;
+  uint64_t yhat_b, h_b, rope_lo, rope_hi, esc_rows, total;
 };
 
 Geometry geometry(const dckv_plan_t *p, int64_t T);
@@ -114,21 +117,6 @@ struct KernelTimer {
   const char *name_;
   hipStream_t s_;
   hipEvent_t a_ = nullptr, b_ = nullptr;
-};
-
-// ---- a second stream for work that may run beside the caller's ---------------
-// One library-owned stream per device (default priority, non-blocking).  The
-// constructor makes it wait for the work already enqueued on `parent`; join()
-// makes `parent` wait for the work enqueued on it since.  If a HIP call fails,
-// stream() is `parent` itself and the work simply runs in order.
-class SideStream {
- public:
-  explicit SideStream(hipStream_t parent);
-  hipStream_t stream() const { return side_; }
-  void join();
-
- private:
-  hipStream_t parent_, side_;
 };
 
 // ---- launchers (rans.hip / gemm.hip / misc.hip) -----------------------------
@@ -177,12 +165,11 @@ void launch_sym_to_tiled(const EncodeArgs &a, const uint8_t *sym);
 void launch_sym_from_tiled(const DecodeArgs &a, uint8_t *sym_out, uint32_t *n_esc_out);
 
 // gemm.hip
-void launch_mean_gemm(const EncodeArgs &a);
+int build_mean_table(dckv_plan_t *p);  // at plan time: fills p->mtab, synchronous
 void launch_analysis_gemm(const EncodeArgs &a);
 void launch_encode_fixup(const EncodeArgs &a);
 void launch_rope_tables(const DecodeArgs &a);
-void launch_dequant_gemm(const DecodeArgs &a);
-void launch_decode_fixup(const DecodeArgs &a);
+void launch_dequant(const DecodeArgs &a);
 void launch_w1_gemm(const DecodeArgs &a);
 void launch_synthesis_gemm(const DecodeArgs &a);
 void launch_kept_rope(const DecodeArgs &a);

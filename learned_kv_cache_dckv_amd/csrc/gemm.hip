@@ -17,35 +17,38 @@
 // owns a 256x256 tile; each wave a 128x128 sub-tile held as 4x4 blocks of
 // v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane); the 32x32 form
 // keeps the matrix cores busy with a single wave per SIMD.  Operand tiles of
-// 256 rows x 32 k are copied global -> LDS by the direct 16-byte LDS loads of
-// gfx950 (no register staging) into a ring of 4 stages, so three tiles of
-// loads are in flight while one is consumed; a wave waits only for the loads
-// of the tile it is about to read (s_waitcnt vmcnt(n), then a bare barrier).
-// Rows are 64 bytes (4 chunks of 16 B); chunk c of row r is stored at
-// c ^ ((r >> 2) & 3), so the 16 lanes served together by one LDS pass read 16
-// distinct 16-byte bank groups.  Fragments of the next k-step are read from
-// LDS while the current k-step's MFMAs run.  Workgroups are mapped to
-// tiles so that the tiles of one row band run on the same XCD (the hardware
-// deals workgroups to the 8 XCDs round robin), which keeps a band's token rows
-// in that XCD's L2 while all its weight tiles stream past.
+// 256 rows x 64 k (whole 128-byte lines) are copied global -> LDS by the
+// direct 16-byte LDS loads of gfx950 (no register staging) into two stages;
+// one barrier per k-tile.  Chunk c of row r is stored at c ^ ((r >> 1) & 7),
+// so the 16 lanes served together by one LDS pass read 16 distinct 16-byte
+// bank groups.  Fragments of the next k-step are read from LDS while the
+// current k-step's MFMAs run.  Workgroups are mapped to tiles so that the
+// tiles one XCD runs at once share their operand panels in that XCD's L2.
 //
 // Lane l of a 32x32 accumulator block holds column l%32 and, in register
 // group g (registers 4g..4g+3), rows 8g + 4*(l/32) .. +3: a quad of 4
 // consecutive rows.  The checkerboard neighbours of a row are in the same
 // quad (rows 4k+1: 4k and 4k+2) or, for row 4k+3, in the first row of the
 // next quad, held by lane l^32 (same group, or the next group / next block).
-// The epilogues work on the accumulators in registers:
-//   mean       H E[tok] -> fp32, stored in the tile-interleaved order the
-//              quantiser reads back (16 bytes per lane per block)
-//   quantise   even rows: r = (y - mu)/step, q = rint(r), yhat = mu + q step;
-//              then odd rows with mu += a (yhat_{j-1} + yhat_{j+1}); the first
-//              row of the lower wave crosses waves through LDS, the last odd
-//              row of a tile is finished by a small fix-up kernel
-//   dequant    yhat = mu + q step in the same two passes -> bf16 yhat_b
-//   w1         exact-erf GELU -> bf16 h_b
-//   synthesis  rotate-half RoPE on key heads; the tile's columns are ordered
-//              so that every pair (d, d+128) sits in one lane and register
-//              of blocks nb and nb+2 -> bf16 rows
+//
+// The embedding mean H E[tok] depends on the token id alone, so the plan
+// holds it for the whole vocabulary (computed once by k_mean_table, fp32).
+// The kernels:
+//   mean table  H E[v] for every token id v -> fp32 [vocab][C], columns in the
+//               plan's rank order (active components, then dropped ones)
+//   quantise    analysis GEMM; epilogue: even rows r = (y - mu)/step,
+//               q = rint(r), yhat = mu + q step; then odd rows with
+//               mu += a (yhat_{j-1} + yhat_{j+1}); mu rows are gathered from
+//               the table into LDS one parity at a time; the first row of the
+//               lower wave crosses waves through LDS, the last odd row of a
+//               tile is finished by a small fix-up kernel
+//   dequant     no GEMM: yhat = mu + q step in the same two passes, streamed
+//               row by row from the table, the codes and the escape records
+//               -> bf16 yhat_b
+//   w1          exact-erf GELU -> bf16 h_b
+//   synthesis   rotate-half RoPE on key heads; the tile's columns are ordered
+//               so that every pair (d, d+128) sits in one lane and register
+//               of blocks nb and nb+2 -> bf16 rows
 // bf16 outputs go through a per-wave LDS transpose so global stores are
 // 16-byte row segments.
 #include <cmath>
@@ -58,6 +61,8 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef const void __attribute__((address_space(1))) *gptr_t;
 typedef void __attribute__((address_space(3))) *lptr_t;
 
@@ -68,9 +73,10 @@ constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 64 KiB per stage
 constexpr int kOutStride = 128 + 8;                       // bf16 per row of a wave's output tile
 constexpr int kOutWaveBytes = 128 * kOutStride * 2;
 constexpr int kXchOff = 4 * kOutWaveBytes;                // row-0 exchange between the two wave rows
-constexpr int kEscLdsOff = kXchOff + 2 * 256 * 4;         // escape records of a dequantisation tile
-constexpr int kLdsBytes = kEscLdsOff + kEscLdsMax * 8;
+constexpr int kLdsBytes = kXchOff + 2 * 256 * 4;
+constexpr int kMeanRowFloats = 256 + 16;                  // LDS row of staged means (see mean_rows_to_lds)
 static_assert(kStages * kStageBytes <= kXchOff, "stages must not overlap the exchange area");
+static_assert(128 * kMeanRowFloats * 4 <= kXchOff, "staged means must not overlap the exchange area");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
 constexpr float kQLimit = 2147483520.0f;  // largest float below 2^31
 
@@ -336,74 +342,46 @@ __device__ __forceinline__ int clamp_tok(const int32_t *tok, int64_t t, int voca
 // tile row staged by this lane in load i (0..7), matching load_rows()
 __device__ __forceinline__ int staged_row(int i) { return (threadIdx.x >> 6) * 64 + i * 8 + ((threadIdx.x & 63) >> 3); }
 
-// fp32 embedding mean of one 256x256 tile as two planes of 128 KiB: plane p
-// holds the rows of parity p (the rows one checkerboard pass needs), in the
-// order of the accumulators: [wave][mb][nb][h][lane][4]; element e of half h
-// is accumulator register v = 8h + 4(e >> 1) + 2(e & 1) + p.
-constexpr int kPlaneFloats = 4 * 4 * 4 * 2 * 64 * 4;  // 32768
-__device__ __forceinline__ int plane_off(int wave, int mb, int nb, int h, int lane) {
-  return ((((wave * 4 + mb) * 4 + nb) * 2 + h) * 64 + lane) * 4;
-}
-
-// plane register v (of parity p) -> (half, element)
-__device__ __forceinline__ int plane_h(int v) { return v >> 3; }
-__device__ __forceinline__ int plane_e(int v) { return 2 * ((v >> 2) & 1) + ((v >> 1) & 1); }
-
-// One plane of a tile from global memory into LDS (offset 0): 32 direct loads
-// per wave of 1 KiB each, in the plane's own order.
-__device__ __forceinline__ void plane_to_lds(const float *plane, char *lds, int wave, int lane) {
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const int off = wave * (kPlaneFloats / 4) + k * 256;  // floats
-    __builtin_amdgcn_global_load_lds((gptr_t)(plane + off + lane * 4), (lptr_t)(lds + off * 4), 16, 0, 0);
-  }
-}
-
 // ---------------------------------------------------------------------------
-// encode: mean GEMM  m[j][r] = sum_k E[tok_{j+kh}][k] H[act[r]][k]
+// plan time: embedding-mean table  mtab[v][i] = sum_k E[v][k] H[perm[i]][k]
 // ---------------------------------------------------------------------------
-struct MeanEncP {
+struct MeanTabP {
   const uint16_t *E, *H;
-  const int32_t *tok, *act;
-  float *mean;  // [n_mtiles][n_ntiles][2 planes][32768], see plane_off()
-  int64_t N;
-  int n_mt, n_nt, keep_head, vocab;
-  int32_t *status;
+  const int32_t *perm;
+  float *mtab;  // [vocab][kC]
+  int vocab, n_mt, n_nt;
 };
 
-__global__ __launch_bounds__(kThreads, 1) void k_mean_enc(MeanEncP P) {
+__global__ __launch_bounds__(kThreads, 1) void k_mean_table(MeanTabP P) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  if (wg_stop(P.status)) return;
   int mt, nt;
   tile_of(blockIdx.x, P.n_mt * P.n_nt, P.n_nt, mt, nt);
-  const int64_t m0 = (int64_t)mt * kBM;
+  const int m0 = mt * kBM;
   const int n0 = nt * kBN;
   Operand A, B;
   set_sources(A, P.E, kEmb * 2, P.E, kEmb * 2, kEmb / kBK);
   set_sources(B, P.H, kEmb * 2, P.H, kEmb * 2, kEmb / kBK);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int64_t j = min<int64_t>(m0 + staged_row(i), P.N - 1);
-    A.row[i] = (uint32_t)clamp_tok(P.tok, P.keep_head + j, P.vocab, P.status);
-    B.row[i] = (uint32_t)P.act[n0 + staged_row(i)];
+    A.row[i] = (uint32_t)min(m0 + staged_row(i), P.vocab - 1);
+    B.row[i] = (uint32_t)P.perm[n0 + staged_row(i)];
   }
   f32x16 acc[4][4];
   mainloop(A, B, kEmb / kBK, acc, lds);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t tid = (int64_t)mt * P.n_nt + nt;
+  const int lane = epilogue_lane(), wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const f32x16 b = acc_block(acc, mb, nb);
+      const int col = n0 + wn * 128 + nb * 32 + (lane & 31);
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float *plane = P.mean + (tid * 2 + p) * kPlaneFloats;
-          const int v = 8 * h + p;
-          *reinterpret_cast<f32x4 *>(plane + plane_off(wave, mb, nb, h, lane)) = f32x4{b[v], b[v + 2], b[v + 4], b[v + 6]};
-        }
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * 128 + acc_row(mb, v, lane);
+        if (row < P.vocab) P.mtab[(size_t)row * kC + col] = b[v];
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -412,17 +390,41 @@ __global__ __launch_bounds__(kThreads, 1) void k_mean_enc(MeanEncP P) {
 // ---------------------------------------------------------------------------
 struct QuantP {
   const uint16_t *rows, *A;
-  const int32_t *act;
+  const int32_t *act, *tok;
   const float *step, *nbr;
-  float *mean;
+  const float *mtab;  // [vocab][kC] embedding means, columns in rank order
   uint32_t *sym32;
   uint32_t *esc_raw;  // {flat, q}
   uint8_t *ws;
   float *halo_a, *halo_b;
   int64_t N, N256, esc_cap;
-  int Ca, keep_head, C, n_mt, n_nt;
+  int Ca, keep_head, C, n_mt, n_nt, vocab;
   int32_t *status;
 };
+
+// The means of the tile rows of one parity p into LDS (offset 0): slot i
+// (0..127) holds tile row 2i + p, i.e. columns [n0, n0 + 256) of the table row
+// of that row's token, 1 KiB, with kMeanRowFloats floats per slot, so rows
+// two slots apart (tile rows 4 apart, read together by the two half-waves)
+// fall in opposite halves of the LDS banks.  Each wave stages 32 slots with
+// one direct 16-byte load per slot; the token of slot k is read out of lane k.
+__device__ __forceinline__ void mean_rows_to_lds(const QuantP &P, int64_t m0, int n0, int p, char *lds, int lane) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t j = min<int64_t>(m0 + 2 * (wave * 32 + (lane & 31)) + p, P.N - 1);
+  const int v = clamp_tok(P.tok, P.keep_head + j, P.vocab, P.status);
+  const float *col = P.mtab + n0 + lane * 4;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int row = __builtin_amdgcn_readlane(v, k);
+    __builtin_amdgcn_global_load_lds((gptr_t)(col + (size_t)row * kC),
+                                     (lptr_t)(lds + (wave * 32 + k) * kMeanRowFloats * 4), 16, 0, 0);
+  }
+}
+
+// staged mean of tile row `trow` (of the parity staged), tile column `tcol`
+__device__ __forceinline__ float mean_at(const char *lds, int trow, int tcol) {
+  return reinterpret_cast<const float *>(lds)[(trow >> 1) * kMeanRowFloats + tcol];
+}
 
 // r = fp32(d / step) from the reciprocal and one fused correction
 __device__ __forceinline__ float div_step(float d, float step, float inv) {
@@ -488,7 +490,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t tid = (int64_t)mt * P.n_nt + nt;
   const int64_t wrow0 = m0 + wm * 128;  // first row of this wave's tile
   int r_nb[4];
   float st_nb[4], inv_nb[4], a_nb[4];
@@ -503,23 +504,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   }
   uint32_t symw[4][4][4];
   bool bad = false;
-  // pass 1: even rows, mu = H E[tok], from the even-row plane staged in LDS
-  plane_to_lds(P.mean + (tid * 2 + 0) * kPlaneFloats, lds, wave, lane);
+  // pass 1: even rows, mu = H E[tok], from the even rows' means staged in LDS
+  mean_rows_to_lds(P, m0, n0, 0, lds, lane);
   __syncthreads();  // (waits for this wave's loads, then for every wave's)
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      f32x4 mh[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) mh[h] = *reinterpret_cast<const f32x4 *>(lds + plane_off(wave, mb, nb, h, lane) * 4);
+      const int tcol = wn * 128 + nb * 32 + (lane & 31);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint32_t w = 0xFFFFFFFFu;
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
           const int v = 4 * g + i;
-          const float m = mh[plane_h(v)][plane_e(v)];
+          const float m = mean_at(lds, wm * 128 + acc_row(mb, v, lane), tcol);
           const int64_t j = wrow0 + acc_row(mb, v, lane);
           if (j < P.N && r_nb[nb] < P.Ca) {
             float qf;
@@ -546,24 +545,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   __syncthreads();
   const bool defer_last = m0 + kBM < P.N;
   // pass 2: odd rows, mu = H E[tok] + a (yhat_{j-1} + yhat_{j+1}), from the
-  // odd-row plane (the barrier above also ended every wave's pass 1 reads)
-  plane_to_lds(P.mean + (tid * 2 + 1) * kPlaneFloats, lds, wave, lane);
+  // odd rows' means (the barrier above also ended every wave's pass 1 reads)
+  mean_rows_to_lds(P, m0, n0, 1, lds, lane);
   __syncthreads();
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      f32x4 mh[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) mh[h] = *reinterpret_cast<const f32x4 *>(lds + plane_off(wave, mb, nb, h, lane) * 4);
+      const int tcol = wn * 128 + nb * 32 + (lane & 31);
       const float ext = wm == 0 ? xch[256 + wn * 128 + nb * 32 + (lane & 31)] : 0.f;
       const float a = a_nb[nb];
       const int r = r_nb[nb];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float next3 = next_quad_row0(acc, mb, nb, g, ext, lane);
-        const float m1 = mh[plane_h(4 * g + 1)][plane_e(4 * g + 1)];
-        const float m3 = mh[plane_h(4 * g + 3)][plane_e(4 * g + 3)];
+        const float m1 = mean_at(lds, wm * 128 + acc_row(mb, 4 * g + 1, lane), tcol);
+        const float m3 = mean_at(lds, wm * 128 + acc_row(mb, 4 * g + 3, lane), tcol);
         uint32_t w = symw[mb][nb][g];
         const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
         const float y0 = acc[mb][nb][4 * g], y2 = acc[mb][nb][4 * g + 2];
@@ -610,67 +607,157 @@ __global__ void k_encode_fixup(QuantP P, int64_t n_fix) {
 }
 
 // ---------------------------------------------------------------------------
-// decode: mean GEMM over all components + two dequantisation passes
+// decode: two dequantisation passes, streamed (no GEMM: the means come from
+// the plan's table)
 // ---------------------------------------------------------------------------
 struct DeqP {
-  const uint16_t *E, *H;
-  const int32_t *tok, *rank;
+  const float *mtab;          // [vocab][kC] embedding means
+  const int32_t *tok, *rank, *colpos;
   const float *step, *nbr;
-  const uint32_t *sym32;
-  const uint8_t *stream;
+  const uint32_t *sym32;      // [G][N256/4][64]: symbols of 4 consecutive rows per word
+  const uint8_t *stream;      // escape records {flat, q}, ascending flat, at the offset the parser found
   const uint8_t *ws;
-  uint16_t *yhat_b;  // [NM][C]
-  float *halo_a, *halo_b;
-  const uint32_t *esc_tiles;  // [n_mt][n_nt]: 0 no escaped code, 1 escapes (records fit in LDS), 2 more
-  const uint32_t *esc_rows;   // [n_mt][2]: index range of the escapes of a row tile
-  const uint32_t *esc_list;   // [2][n_mt * n_nt]: tiles of escape kinds 1 and 2
+  const uint32_t *esc_rows;   // [256-row tiles][2]: index range of each tile's records
+  uint16_t *yhat_b;           // [NM][kC]
   int64_t N, N256;
-  int Ca, keep_head, vocab, n_mt, n_nt;
+  int Ca, keep_head, vocab;
   int32_t *status;
 };
 
-// Escape records {flat, q} of the tile's rows, sorted by flat: in LDS
-// (address space 3) or, when too many, in the stream (address space 1).  The
-// typed pointer tells the compiler the records cannot alias the accumulators.
-template <int kAS>
-struct EscRecs {
-  const uint32_t __attribute__((address_space(kAS))) *rec;
-  uint32_t n;
-};
+constexpr int kDeqThreads = 256;
+constexpr int kDeqRows = 8;  // rows per thread: two quads (row quads share a symbol word)
 
-// The code of an escaped position: binary search of its flat index.  Out of
-// line, so that the fully unrolled epilogue stays small (its accumulators
-// then stay in registers); it runs only at escaped positions.
-template <int kAS>
-__device__ __noinline__ int esc_code(int32_t *status, const uint32_t __attribute__((address_space(kAS))) *rec,
-                                     uint32_t n, uint32_t flat) {
-  uint32_t lo = 0, hi = n;
+// A load through a global (address space 1) pointer.
+template <class T>
+__device__ __forceinline__ T gload(const T *p) {
+  return *(const T __attribute__((address_space(1))) *)p;
+}
+
+// The code of escaped position (j, rank r): binary search of its flat index
+// among the escape records of its 256-row tile (found by the parser).
+__device__ __forceinline__ int esc_search(const DeqP &P, int j, int r) {
+  const uint32_t flat = (uint32_t)j * (uint32_t)P.Ca + (uint32_t)r;
+  const uint32_t *rec = reinterpret_cast<const uint32_t *>(P.stream + gload(&reinterpret_cast<const Ctrl *>(P.ws)->esc_off));
+  uint32_t lo = gload(P.esc_rows + 2 * (j >> 8)), hi = gload(P.esc_rows + 2 * (j >> 8) + 1);
+  const uint32_t end = hi;
   while (lo < hi) {
     const uint32_t mid = (lo + hi) >> 1;
-    if (rec[2 * mid] < flat) lo = mid + 1; else hi = mid;
+    if (gload(rec + 2 * mid) < flat) lo = mid + 1; else hi = mid;
   }
-  if (lo < n && rec[2 * lo] == flat) return (int)rec[2 * lo + 1];
-  set_status(status, DCKV_ECORRUPT);
+  if (lo < end && gload(rec + 2 * lo) == flat) return (int)gload(rec + 2 * lo + 1);
+  set_status(P.status, DCKV_ECORRUPT);
   return 0;
 }
 
-// Code of byte i of a symbol word.  Tiles without escapes (kMode 0) take the
-// slot as it is; tiles with escapes look escaped codes up in their records.
-template <int kMode>
-struct EscOf {
-  typedef EscRecs<kMode == 2 ? 1 : 3> type;
-};
-
-template <int kMode>
-__device__ __forceinline__ float code_of(const DeqP &P, const typename EscOf<kMode>::type &E, uint32_t w, int i,
-                                         int64_t j, int r) {
-  const uint32_t s = (w >> (8 * i)) & 0xFFu;
-  if (kMode == 0 || s != (uint32_t)kEsc) return (float)((int)s - 127);
-  return (float)esc_code(P.status, E.rec, E.n, (uint32_t)(j * P.Ca + r));
+// Thread t of grid row y owns components c0 .. c0+3 (c0 = 4 (256 y + t)) of
+// rows j0 .. j0+7 (j0 = 8 x), plus the first row j0+8 of the next rows, which
+// the last odd row needs.  Every load is issued up front: the 9 rows' tokens
+// and means (a 16-byte load per row), and three symbol words per component
+// (rows j0..j0+3, j0+4..j0+7, j0+8..).  Pass 1 gives the even rows
+// (yhat = mu + q step), pass 2 the odd rows (mu += a (yhat_{j-1} +
+// yhat_{j+1})); rows past the end count as zero.  kDense: no dropped
+// component, so component = rank = table column.
+template <bool kDense>
+__global__ __launch_bounds__(kDeqThreads) void k_dequant(DeqP P) {
+  if (gload(P.status) != 0) return;
+  const int c0 = (blockIdx.y * kDeqThreads + threadIdx.x) * 4;
+  const int j0 = blockIdx.x * kDeqRows;
+  const int N = (int)P.N;
+  const size_t n_quads = (size_t)(P.N256 / 4);
+  float st[4], a[4];
+  int r[4], col[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    st[k] = gload(P.step + c0 + k);
+    a[k] = gload(P.nbr + c0 + k);
+    r[k] = kDense ? c0 + k : gload(P.rank + c0 + k);
+    col[k] = kDense ? c0 + k : gload(P.colpos + c0 + k);
+  }
+  // symbol words of the three quads (code 0 where dropped or past the end)
+  uint32_t w[3][4];
+#pragma unroll
+  for (int qq = 0; qq < 3; ++qq) {
+    const size_t q = (size_t)(j0 >> 2) + qq;
+    if (j0 + 4 * qq < N) {
+      if (kDense) {
+        const u32x4 x = gload(reinterpret_cast<const u32x4 *>(P.sym32 + ((size_t)(c0 >> 6) * n_quads + q) * 64 + (c0 & 63)));
+        w[qq][0] = x.x; w[qq][1] = x.y; w[qq][2] = x.z; w[qq][3] = x.w;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          w[qq][k] = r[k] >= 0 ? gload(P.sym32 + ((size_t)(r[k] >> 6) * n_quads + q) * 64 + (r[k] & 63)) : 0x7F7F7F7Fu;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[qq][k] = 0x7F7F7F7Fu;
+    }
+  }
+  // means of the 9 rows (0 past the end)
+  float m[kDeqRows + 1][4];
+#pragma unroll
+  for (int i = 0; i <= kDeqRows; ++i) {
+    if (j0 + i < N) {
+      int v = gload(P.tok + P.keep_head + j0 + i);
+      if (v < 0 || v >= P.vocab) {
+        set_status(P.status, DCKV_EINVAL);
+        v = 0;
+      }
+      const float *row = P.mtab + (size_t)v * kC;
+      if (kDense) {
+        const f32x4 x = gload(reinterpret_cast<const f32x4 *>(row + c0));
+        m[i][0] = x.x; m[i][1] = x.y; m[i][2] = x.z; m[i][3] = x.w;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m[i][k] = gload(row + col[k]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m[i][k] = 0.f;
+    }
+  }
+  // codes; escaped positions (symbol 255) are looked up, one at a time
+  float q[kDeqRows + 1][4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t em = 0;
+#pragma unroll
+    for (int i = 0; i <= kDeqRows; ++i) {
+      const uint32_t sy = (w[i >> 2][k] >> (8 * (i & 3))) & 0xFFu;
+      q[i][k] = (float)((int)sy - 127);
+      if (sy == (uint32_t)kEsc && j0 + i < N) em |= 1u << i;
+    }
+    while (em) {
+      const int i = __builtin_ctz(em);
+      em &= em - 1;
+      const float val = (float)esc_search(P, j0 + i, r[k]);
+#pragma unroll
+      for (int ii = 0; ii <= kDeqRows; ++ii)
+        if (ii == i) q[ii][k] = val;
+    }
+  }
+  // pass 1: even rows (row j0+8 too); pass 2: odd rows
+  float y[kDeqRows + 1][4];
+#pragma unroll
+  for (int i = 0; i <= kDeqRows; i += 2)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) y[i][k] = j0 + i < N ? m[i][k] + q[i][k] * st[k] : 0.f;
+#pragma unroll
+  for (int i = 1; i < kDeqRows; i += 2)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) y[i][k] = m[i][k] + a[k] * (y[i - 1][k] + y[i + 1][k]) + q[i][k] * st[k];
+#pragma unroll
+  for (int i = 0; i < kDeqRows; ++i) {
+    if (j0 + i < N) {
+      u32x2 o;
+      o.x = (uint32_t)f2bf(y[i][0]) | ((uint32_t)f2bf(y[i][1]) << 16);
+      o.y = (uint32_t)f2bf(y[i][2]) | ((uint32_t)f2bf(y[i][3]) << 16);
+      *(u32x2 __attribute__((address_space(1))) *)(P.yhat_b + (size_t)(j0 + i) * kC + c0) = o;
+    }
+  }
 }
 
 // bf16 of fn(value) for all 128x128 values of the wave into its LDS tile
-// (identity columns), one element at a time
+// (identity columns), one accumulator block at a time
 template <class F>
 __device__ __forceinline__ void acc_to_wtile(const f32x16 (&acc)[4][4], char *wtile, int, F &&fn) {
   const int lane = epilogue_lane();
@@ -688,205 +775,6 @@ __device__ __forceinline__ void acc_to_wtile(const f32x16 (&acc)[4][4], char *wt
 struct Identity {
   __device__ float operator()(float x) const { return x; }
 };
-
-// Epilogue of the dequantisation GEMM: the two checkerboard passes on the
-// accumulators (mu = H E[tok]) and the bf16 rows of yhat.
-template <int kMode>
-__device__ __forceinline__ void dequant_epilogue(const DeqP &P, const typename EscOf<kMode>::type &E,
-                                                 const f32x16 (&acc)[4][4], char *lds, int mt, int64_t m0, int n0) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t wrow0 = m0 + wm * 128;
-  const bool defer_last = m0 + kBM < P.N;
-  float *xch = reinterpret_cast<float *>(lds + kXchOff);
-  char *wtile = lds + wave * kOutWaveBytes;
-
-  // The epilogue works one 32x32 block (16 values per lane) at a time, down
-  // each block column: pass 1 (even rows) of block mb + 1, then pass 2 (odd
-  // rows) of block mb, whose last quad needs the first row of block mb + 1.
-  // Symbol words of a block are loaded one block ahead.
-  auto load_words = [&](int mb, int r, uint32_t (&w)[4]) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
-      w[g] = (r >= 0 && j0 < P.N) ? P.sym32[((size_t)(r >> 6) * (P.N256 / 4) + (j0 >> 2)) * 64 + (r & 63)]
-                                  : 0x7F7F7F7Fu;  // code 0
-    }
-  };
-  // pass 1: yhat = mu + q step on the even rows; rows past the end are zero
-  auto pass1 = [&](f32x16 &b, const uint32_t (&w)[4], int mb, int r, float st) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
-#pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        if (j0 + i < P.N) {
-          const float q = r >= 0 ? code_of<kMode>(P, E, w[g], i, j0 + i, r) : 0.f;
-          b[4 * g + i] = b[4 * g + i] + q * st;
-        } else {
-          b[4 * g + i] = 0.f;
-        }
-      }
-    }
-  };
-  // pass 2: yhat = mu + a (yhat_{j-1} + yhat_{j+1}) + q step on the odd rows;
-  // `nx` is the next block (its first row follows this block's last quad)
-  auto pass2 = [&](f32x16 &b, const f32x16 &nx, float ext, const uint32_t (&w)[4], int mb, int r, int c, float st,
-                   float a) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      // first row of the next quad: lanes < 32 find it in lane + 32 (same
-      // group), lanes >= 32 in lane - 32 (next group, or the next block)
-      const float same = __shfl_xor(b[4 * g], 32);
-      const float nxt = g < 3 ? __shfl_xor(b[4 * g + 4], 32) : (mb < 3 ? __shfl_xor(nx[0], 32) : ext);
-      const float next3 = lane < 32 ? same : nxt;
-      const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
-      const float y0 = b[4 * g], y2 = b[4 * g + 2];
-      if (j0 + 1 < P.N) {
-        const float q = r >= 0 ? code_of<kMode>(P, E, w[g], 1, j0 + 1, r) : 0.f;
-        b[4 * g + 1] = b[4 * g + 1] + a * (y0 + y2) + q * st;
-      } else {
-        b[4 * g + 1] = 0.f;
-      }
-      if (j0 + 3 < P.N) {
-        const float q = r >= 0 ? code_of<kMode>(P, E, w[g], 3, j0 + 3, r) : 0.f;
-        if (wm == 1 && mb == 3 && g == 3 && lane >= 32 && defer_last)
-          P.halo_a[(int64_t)mt * kC + c] = b[4 * g + 3] + a * y2 + q * st;  // finished by the fix-up
-        else
-          b[4 * g + 3] = b[4 * g + 3] + a * (y2 + next3) + q * st;
-      } else {
-        b[4 * g + 3] = 0.f;
-      }
-    }
-  };
-
-  // row 0 of every wave tile, after pass 1: to the wave above (LDS) and, for
-  // the tile's row 0, to the fix-up of the previous tile (global)
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int c = n0 + wn * 128 + nb * 32 + (lane & 31);
-    const int r = P.rank[c];
-    uint32_t w[4];
-    load_words(0, r, w);
-    f32x16 b = acc_block(acc, 0, nb);
-    pass1(b, w, 0, r, P.step[c]);
-    if (lane < 32) {
-      xch[wm * 256 + wn * 128 + nb * 32 + lane] = b[0];
-      if (wm == 0) P.halo_b[(int64_t)mt * kC + c] = b[0];
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int c = n0 + wn * 128 + nb * 32 + (lane & 31);
-    const int r = P.rank[c];
-    const float st = P.step[c], a = P.nbr[c];
-    const float ext = wm == 0 ? xch[256 + wn * 128 + nb * 32 + (lane & 31)] : 0.f;
-    uint32_t w_cur[4], w_nxt[4];
-    load_words(0, r, w_cur);
-    f32x16 cur = acc_block(acc, 0, nb);
-    pass1(cur, w_cur, 0, r, st);
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      f32x16 nxt = cur;
-      if (mb < 3) {
-        load_words(mb + 1, r, w_nxt);
-        nxt = acc_block(acc, mb + 1, nb);
-        pass1(nxt, w_nxt, mb + 1, r, st);
-      }
-      pass2(cur, nxt, ext, w_cur, mb, r, c, st, a);
-      // bf16 yhat of this block into the wave's LDS tile
-#pragma unroll
-      for (int v = 0; v < 16; ++v) put(wtile, acc_row(mb, v, lane), nb * 32 + (lane & 31), f2bf(cur[v]));
-      __builtin_amdgcn_sched_barrier(0);
-      if (mb < 3) {
-        cur = nxt;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) w_cur[g] = w_nxt[g];
-      }
-    }
-  }
-  // bf16 yhat rows from LDS (the exchange area lies beyond the wave tiles)
-  wave_lds_sync();
-  const int64_t col_lo = n0 + wn * 128;
-  flush_rows(wtile, P.yhat_b, kC, wrow0, col_lo, col_lo + 64, P.N);
-}
-
-// Three instances, one per kind of tile (marked while parsing): 0 no escaped
-// code, 1 escapes whose records fit in LDS, 2 more records than that.  Kind 0
-// walks the whole grid and skips escape tiles; kinds 1 and 2 take their tiles
-// from the parser's lists, one per workgroup, and the surplus workgroups
-// return at once.  Every tile is computed once, and the escape-free instance
-// keeps a register allocation of its own.
-// One dequantisation tile: the mean GEMM and its epilogue.
-template <int kMode>
-__device__ __forceinline__ void dequant_tile(const DeqP &P, char *lds, int mt, int nt) {
-  const int64_t m0 = (int64_t)mt * kBM;
-  const int n0 = nt * kBN;
-  Operand A, B;
-  set_sources(A, P.E, kEmb * 2, P.E, kEmb * 2, kEmb / kBK);
-  set_sources(B, P.H, kEmb * 2, P.H, kEmb * 2, kEmb / kBK);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t j = min<int64_t>(m0 + staged_row(i), P.N - 1);
-    A.row[i] = (uint32_t)clamp_tok(P.tok, P.keep_head + j, P.vocab, P.status);
-    B.row[i] = (uint32_t)(n0 + staged_row(i));
-  }
-  f32x16 acc[4][4];
-  mainloop(A, B, kEmb / kBK, acc, lds);
-  typename EscOf<kMode>::type E{nullptr, 0u};
-  if (kMode != 0) {
-    // the escape records of this tile's rows
-    const Ctrl *ct = reinterpret_cast<const Ctrl *>(P.ws);
-    const uint32_t lo = P.esc_rows[2 * mt], hi = P.esc_rows[2 * mt + 1];
-    const uint32_t *grec = reinterpret_cast<const uint32_t *>(P.stream + ct->esc_off) + 2ull * lo;
-    E.n = hi - lo;
-    if (kMode == 1) {
-      uint32_t *lrec = reinterpret_cast<uint32_t *>(lds + kEscLdsOff);
-      for (uint32_t i = threadIdx.x; i < 2 * E.n; i += kThreads) lrec[i] = grec[i];
-      __syncthreads();
-      E.rec = (decltype(E.rec))(lrec);
-    } else {
-      E.rec = (decltype(E.rec))(grec);
-    }
-  }
-  dequant_epilogue<kMode>(P, E, acc, lds, mt, m0, n0);
-}
-
-// Three instances, one per kind of tile (marked while parsing): 0 no escaped
-// code, 1 escapes whose records fit in LDS, 2 more records than that.  Kind 0
-// walks the whole grid and skips escape tiles; kinds 1 and 2 take their tiles
-// from the parser's lists, one per workgroup, and the surplus workgroups
-// return at once.  Every tile is computed once, and the escape-free instance
-// keeps a register allocation of its own.
-template <int kMode>
-__global__ __launch_bounds__(kThreads, 1) void k_dequant(DeqP P) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  int mt, nt;
-  if (kMode == 0) {
-    tile_of(blockIdx.x, P.n_mt * P.n_nt, P.n_nt, mt, nt);
-    if (P.esc_tiles[mt * P.n_nt + nt] != 0u) return;
-  } else {
-    const Ctrl *ct = reinterpret_cast<const Ctrl *>(P.ws);
-    if (blockIdx.x >= ct->n_esc_tiles[kMode - 1]) return;
-    const uint32_t tile = P.esc_list[(kMode - 1) * (P.n_mt * P.n_nt) + blockIdx.x];
-    mt = (int)(tile / P.n_nt);
-    nt = (int)(tile - (uint32_t)mt * P.n_nt);
-  }
-  if (wg_stop(P.status)) return;
-  dequant_tile<kMode>(P, lds, mt, nt);
-}
-
-__global__ void k_decode_fixup(DeqP P, int64_t n_fix) {
-  if (*P.status != 0) return;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n_fix * kC) return;
-  const int64_t mt = i / kC;
-  const int c = (int)(i - mt * kC);
-  const int64_t j = (mt + 1) * kBM - 1;
-  const float y = P.halo_a[mt * kC + c] + P.nbr[c] * P.halo_b[(mt + 1) * kC + c];
-  P.yhat_b[(size_t)j * kC + c] = f2bf(y);
-}
 
 // ---------------------------------------------------------------------------
 // decode: correction hidden layer h = GELU(W1 yhat_b)
@@ -1069,21 +957,24 @@ static void launch_gemm(K kernel, const char *name, int grid, const P &prm, hipS
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), kLdsBytes, s, prm);
 }
 
-void launch_mean_gemm(const EncodeArgs &a) {
-  if (a.g.N == 0 || a.p->C_a == 0) return;
-  MeanEncP P;
-  P.E = a.p->E;
-  P.H = a.p->H;
-  P.tok = a.tok;
-  P.act = a.p->dev.act;
-  P.mean = reinterpret_cast<float *>(a.ws + a.l.mean);
-  P.N = a.g.N;
-  P.n_mt = (int)a.g.n_mtiles;
-  P.n_nt = (int)(a.g.Ca4 / kBN);
-  P.keep_head = a.p->keep_head;
-  P.vocab = a.p->vocab;
-  P.status = a.status;
-  launch_gemm(k_mean_enc, "mean_gemm", P.n_mt * P.n_nt, P, a.s);
+int build_mean_table(dckv_plan_t *p) {
+  MeanTabP P;
+  P.E = p->E;
+  P.H = p->H;
+  P.perm = p->dev.perm;
+  P.mtab = p->mtab;
+  P.vocab = p->vocab;
+  P.n_mt = (p->vocab + kBM - 1) / kBM;
+  P.n_nt = kC / kBN;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev != p->device)
+    return set_error(DCKV_EHIP, "plan: the current device changed while building the plan");
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k_mean_table),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  hipLaunchKernelGGL(k_mean_table, dim3(P.n_mt * P.n_nt), dim3(kThreads), kLdsBytes, 0, P);
+  int rc = check_hip(hipGetLastError(), "plan: mean table launch");
+  if (rc) return rc;
+  return check_hip(hipStreamSynchronize(0), "plan: mean table");
 }
 
 static QuantP quant_params(const EncodeArgs &a) {
@@ -1091,9 +982,10 @@ static QuantP quant_params(const EncodeArgs &a) {
   P.rows = a.rows;
   P.A = a.p->A;
   P.act = a.p->dev.act;
+  P.tok = a.tok;
   P.step = a.p->dev.step;
   P.nbr = a.p->dev.nbr;
-  P.mean = reinterpret_cast<float *>(a.ws + a.l.mean);
+  P.mtab = a.p->mtab;
   P.sym32 = reinterpret_cast<uint32_t *>(a.ws + a.l.sym);
   P.esc_raw = reinterpret_cast<uint32_t *>(a.ws + a.l.esc_raw);
   P.ws = a.ws;
@@ -1107,6 +999,7 @@ static QuantP quant_params(const EncodeArgs &a) {
   P.C = a.p->C;
   P.n_mt = (int)a.g.n_mtiles;
   P.n_nt = (int)(a.g.Ca4 / kBN);
+  P.vocab = a.p->vocab;
   P.status = a.status;
   return P;
 }
@@ -1134,55 +1027,32 @@ void launch_rope_tables(const DecodeArgs &a) {
                      reinterpret_cast<float2 *>(a.ws + a.l.rope_hi), a.g.rope_hi);
 }
 
-static DeqP deq_params(const DecodeArgs &a) {
+void launch_dequant(const DecodeArgs &a) {
+  if (a.g.N == 0) return;
   DeqP P;
-  P.E = a.p->E;
-  P.H = a.p->H;
+  P.mtab = a.p->mtab;
   P.tok = a.tok;
   P.rank = a.p->dev.rank;
+  P.colpos = a.p->dev.colpos;
   P.step = a.p->dev.step;
   P.nbr = a.p->dev.nbr;
   P.sym32 = reinterpret_cast<const uint32_t *>(a.ws + a.l.sym);
   P.stream = a.stream;
   P.ws = a.ws;
-  P.yhat_b = reinterpret_cast<uint16_t *>(a.ws + a.l.yhat_b);
-  P.halo_a = reinterpret_cast<float *>(a.ws + a.l.halo_a);
-  P.halo_b = reinterpret_cast<float *>(a.ws + a.l.halo_b);
-  P.esc_tiles = reinterpret_cast<const uint32_t *>(a.ws + a.l.esc_tiles);
   P.esc_rows = reinterpret_cast<const uint32_t *>(a.ws + a.l.esc_rows);
-  P.esc_list = reinterpret_cast<const uint32_t *>(a.ws + a.l.esc_list);
+  P.yhat_b = reinterpret_cast<uint16_t *>(a.ws + a.l.yhat_b);
   P.N = a.g.N;
   P.N256 = a.g.N256;
   P.Ca = a.p->C_a;
   P.keep_head = a.p->keep_head;
   P.vocab = a.p->vocab;
-  P.n_mt = (int)a.g.n_mtiles;
-  P.n_nt = kC / kBN;
   P.status = a.status;
-  return P;
-}
-
-void launch_dequant_gemm(const DecodeArgs &a) {
-  if (a.g.N == 0) return;
-  DeqP P = deq_params(a);
-  // the tiles with escaped codes (few, slower) run on a side stream, beside
-  // the escape-free tiles on the caller's stream; the caller's stream then
-  // waits for both
-  SideStream side(a.s);
-  launch_gemm(k_dequant<1>, "dequant_gemm_esc", P.n_mt * P.n_nt, P, side.stream());
-  launch_gemm(k_dequant<2>, "dequant_gemm_esc", P.n_mt * P.n_nt, P, side.stream());
-  launch_gemm(k_dequant<0>, "dequant_gemm", P.n_mt * P.n_nt, P, a.s);
-  side.join();
-}
-
-void launch_decode_fixup(const DecodeArgs &a) {
-  if (a.g.N == 0) return;
-  const int64_t n_fix = (a.g.N - 1) / kBM;
-  if (n_fix <= 0) return;
-  DeqP P = deq_params(a);
-  const int64_t work = n_fix * kC;
-  KernelTimer tm("fixup", a.s);
-  hipLaunchKernelGGL(k_decode_fixup, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, a.s, P, n_fix);
+  const dim3 grid((unsigned)((a.g.N + kDeqRows - 1) / kDeqRows), kC / (4 * kDeqThreads));
+  KernelTimer tm("dequant", a.s);
+  if (a.p->C_a == kC)
+    hipLaunchKernelGGL(k_dequant<true>, grid, dim3(kDeqThreads), 0, a.s, P);
+  else
+    hipLaunchKernelGGL(k_dequant<false>, grid, dim3(kDeqThreads), 0, a.s, P);
 }
 
 void launch_w1_gemm(const DecodeArgs &a) {

@@ -208,6 +208,16 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
     act[r] = h.act[r];
   }
   for (int r = Ca; r < Ca_pad; ++r) act[r] = Ca > 0 ? h.act[Ca - 1] : 0;
+  // mean-table columns: the active components in rank order, then the
+  // dropped ones in ascending order
+  std::vector<int32_t> perm(C), colpos(C);
+  {
+    int i = 0;
+    for (int r = 0; r < Ca; ++r) perm[i++] = h.act[r];
+    for (int c = 0; c < C; ++c)
+      if (rank[c] < 0) perm[i++] = c;
+    for (int k = 0; k < C; ++k) colpos[perm[k]] = k;
+  }
   std::vector<uint32_t> tab((size_t)std::max(Ca, 1) * 256, 0);
   std::vector<uint8_t> bucket((size_t)std::max(Ca, 1) * kBuckets, 0);
   for (int r = 0; r < Ca; ++r) {
@@ -241,6 +251,7 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
     return o;
   };
   const size_t o_step = take(C * 4), o_nbr = take(C * 4), o_rank = take(C * 4), o_act = take(Ca_pad * 4);
+  const size_t o_perm = take(C * 4), o_colpos = take(C * 4);
   const size_t o_tab = take(tab.size() * 4), o_bucket = take(bucket.size()), o_omega = take(kHalf * 8);
   void *blk = nullptr;
   if (hipMalloc(&blk, off) != hipSuccess) {
@@ -252,6 +263,8 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
   std::memcpy(&img[o_nbr], p->nbr_weight, C * 4);
   std::memcpy(&img[o_rank], rank.data(), C * 4);
   std::memcpy(&img[o_act], act.data(), Ca_pad * 4);
+  std::memcpy(&img[o_perm], perm.data(), C * 4);
+  std::memcpy(&img[o_colpos], colpos.data(), C * 4);
   std::memcpy(&img[o_tab], tab.data(), tab.size() * 4);
   std::memcpy(&img[o_bucket], bucket.data(), bucket.size());
   std::memcpy(&img[o_omega], omega.data(), kHalf * 8);
@@ -266,9 +279,26 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
   pl->dev.nbr = reinterpret_cast<float *>(b + o_nbr);
   pl->dev.rank = reinterpret_cast<int32_t *>(b + o_rank);
   pl->dev.act = reinterpret_cast<int32_t *>(b + o_act);
+  pl->dev.perm = reinterpret_cast<int32_t *>(b + o_perm);
+  pl->dev.colpos = reinterpret_cast<int32_t *>(b + o_colpos);
   pl->dev.tab = reinterpret_cast<uint32_t *>(b + o_tab);
   pl->dev.bucket = b + o_bucket;
   pl->dev.omega = reinterpret_cast<double *>(b + o_omega);
+  // the embedding-mean table: H E[v] for every token id, once per plan
+  void *mtab = nullptr;
+  if (hipMalloc(&mtab, (size_t)pl->vocab * C * 4) != hipSuccess) {
+    (void)hipFree(blk);
+    delete pl;
+    return set_error(DCKV_ENOMEM, "plan: hipMalloc of the embedding-mean table failed");
+  }
+  pl->mtab = static_cast<float *>(mtab);
+  rc = build_mean_table(pl);
+  if (rc) {
+    (void)hipFree(mtab);
+    (void)hipFree(blk);
+    delete pl;
+    return rc;
+  }
   *out = pl;
   return DCKV_OK;
 }
@@ -281,6 +311,10 @@ extern "C" int dckv_plan_free(dckv_plan_t *plan) {
     (void)hipGetDevice(&cur);
     (void)hipSetDevice(plan->device);
     rc = check_hip(hipFree(plan->dev_block), "plan_free");
+    if (plan->mtab) {
+      const int rc2 = check_hip(hipFree(plan->mtab), "plan_free");
+      if (rc == DCKV_OK) rc = rc2;
+    }
     (void)hipSetDevice(cur);
   }
   delete plan;
@@ -295,6 +329,21 @@ extern "C" int dckv_plan_info(const dckv_plan_t *plan, float *step_out, uint8_t 
   if (freq_out) std::memcpy(freq_out, plan->freq.data(), plan->freq.size() * 2);
   if (c_active) *c_active = plan->C_a;
   if (crc) *crc = plan->crc;
+  return DCKV_OK;
+}
+
+extern "C" int dckv_plan_mean_table(const dckv_plan_t *plan, const float **table, int64_t *rows,
+                                    int32_t *col_component) {
+  if (!plan) return set_error(DCKV_EINVAL, "plan_mean_table: null plan");
+  if (table) *table = plan->mtab;
+  if (rows) *rows = plan->vocab;
+  if (col_component) {
+    int i = 0;
+    for (int c = 0; c < plan->C; ++c)
+      if (plan->active[c]) col_component[i++] = c;
+    for (int c = 0; c < plan->C; ++c)
+      if (!plan->active[c]) col_component[i++] = c;
+  }
   return DCKV_OK;
 }
 
@@ -333,7 +382,6 @@ Layout dckv::layout(const dckv_plan_t *p, const Geometry &g) {
   l.halo_b = take((uint64_t)g.n_mtiles * p->C * 4);
   const uint64_t shared_end = off;
   // encode-only region
-  l.mean = take((uint64_t)g.NM * g.Ca4 * 4);
   uint64_t cap2 = 1;
   while (cap2 < (uint64_t)g.esc_cap) cap2 <<= 1;
   l.esc_raw = take(cap2 * 8);  // room for the bitonic sort's power-of-two padding
@@ -345,9 +393,7 @@ Layout dckv::layout(const dckv_plan_t *p, const Geometry &g) {
   // decode-only region (overlaps the encode-only one)
   off = shared_end;
   l.yhat_b = take((uint64_t)g.NM * p->C * 2);
-  l.esc_tiles = take((uint64_t)g.n_mtiles * (p->C / kBN) * 4);
   l.esc_rows = take((uint64_t)g.n_mtiles * 2 * 4);
-  l.esc_list = take((uint64_t)g.n_mtiles * (p->C / kBN) * 2 * 4);
   l.h_b = take((uint64_t)g.NM * p->hidden * 2);
   l.rope_lo = take(256ull * kHalf * 8);
   l.rope_hi = take((uint64_t)g.rope_hi * kHalf * 8);
@@ -383,7 +429,6 @@ extern "C" int dckv_workspace_view(const dckv_plan_t *plan, int64_t T, int32_t w
     case DCKV_VIEW_SYMBOLS: o = l.sym; b = (uint64_t)g.G * g.N256 * kLanes; rs = kLanes; break;
     case DCKV_VIEW_YHAT_B: o = l.yhat_b; b = (uint64_t)g.N * plan->C * 2; rs = plan->C; break;
     case DCKV_VIEW_H_B: o = l.h_b; b = (uint64_t)g.N * plan->hidden * 2; rs = plan->hidden; break;
-    case DCKV_VIEW_MEAN: o = l.mean; b = (uint64_t)g.NM * g.Ca4 * 4; rs = 0; break;
     default: return set_error(DCKV_EINVAL, "workspace_view: unknown view");
   }
   if (offset) *offset = o;
@@ -424,44 +469,6 @@ void drain_locked(ProfState &s) {
   s.pending.clear();
 }
 }  // namespace
-
-// ---- side streams -------------------------------------------------------------
-namespace {
-
-std::mutex g_side_mu;
-hipStream_t g_side[64] = {};
-
-// order `to` after the work enqueued so far on `from`
-bool stream_wait(hipStream_t to, hipStream_t from) {
-  hipEvent_t e;
-  if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return false;
-  const bool ok = hipEventRecord(e, from) == hipSuccess && hipStreamWaitEvent(to, e, 0) == hipSuccess;
-  (void)hipEventDestroy(e);  // released once the wait has been satisfied
-  return ok;
-}
-
-}  // namespace
-
-SideStream::SideStream(hipStream_t parent) : parent_(parent), side_(parent) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
-  hipStream_t s;
-  {
-    std::lock_guard<std::mutex> lk(g_side_mu);
-    if (!g_side[dev] && hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking) != hipSuccess) {
-      g_side[dev] = nullptr;
-      return;
-    }
-    s = g_side[dev];
-  }
-  if (stream_wait(s, parent)) side_ = s;
-}
-
-void SideStream::join() {
-  if (side_ == parent_) return;
-  if (!stream_wait(parent_, side_)) (void)hipStreamSynchronize(side_);
-  side_ = parent_;
-}
 
 KernelTimer::KernelTimer(const char *name, hipStream_t s) : name_(name), s_(s) {
   ProfState &st = prof();

@@ -245,12 +245,8 @@ struct ParseP {
   int32_t *status;
   uint32_t T, keep_head, keep_tail, N, n_coef, Ca, crc, n_groups;
   uint64_t kept_bytes;
-  const int32_t *act;     // component of each rank
-  uint32_t *esc_tiles;    // [row tiles][n_coef / 256]: 1 where a tile holds an escape
   uint32_t *esc_rows;     // [row tiles][2]: index range of the escapes of a 256-row tile
-  uint32_t *esc_list;     // [2][n_tiles]: the tiles of each escape kind
-  uint32_t n_tiles;
-  uint32_t esc_lds_max;   // escape records a dequantisation tile holds in LDS
+  uint32_t n_row_tiles;
 };
 
 __global__ __launch_bounds__(256) void k_parse(ParseP P) {
@@ -259,7 +255,7 @@ __global__ __launch_bounds__(256) void k_parse(ParseP P) {
   __shared__ uint64_t s_esc_off, s_rans_off, s_rans_bytes;
   __shared__ uint32_t s_n_esc;
   const int t = threadIdx.x;
-  for (uint32_t i = t; i < P.n_tiles; i += blockDim.x) P.esc_tiles[i] = 0u;
+  for (uint32_t i = t; i < 2 * P.n_row_tiles; i += blockDim.x) P.esc_rows[i] = 0u;  // no records
   if (t == 0) {
     bad = 0;
     plan_bad = 0;
@@ -301,11 +297,8 @@ __global__ __launch_bounds__(256) void k_parse(ParseP P) {
       if ((uint64_t)f >= lim) {
         my_bad = 1;
       } else {
-        // the (256-row, 256-component) tile of the dequantisation that holds
-        // it, and the first / one-past-last escape of its 256-row tile
-        const uint32_t j = f / P.Ca, c = (uint32_t)P.act[f - j * P.Ca];
-        const uint32_t mt = j >> 8;
-        P.esc_tiles[mt * (P.n_coef >> 8) + (c >> 8)] = 1u;
+        // the first / one-past-last escape of its 256-row tile
+        const uint32_t mt = (f / P.Ca) >> 8;
         if (i == 0 || (esc[2 * i - 2] / P.Ca) >> 8 != mt) P.esc_rows[2 * mt] = i;
         if (i + 1 == s_n_esc || (esc[2 * i + 2] / P.Ca) >> 8 != mt) P.esc_rows[2 * mt + 1] = i + 1;
       }
@@ -314,24 +307,8 @@ __global__ __launch_bounds__(256) void k_parse(ParseP P) {
     if (my_bad) atomicOr(&bad, 1);
   }
   __syncthreads();
-  // tiles of row tiles with more escape records than the dequantisation keeps
-  // in LDS are searched in the stream instead (kind 2); both kinds are also
-  // listed, so that their workgroups can be launched first
-  __shared__ uint32_t s_cnt[2];
-  if (t < 2) s_cnt[t] = 0u;
-  __syncthreads();
-  for (uint32_t i = t; i < P.n_tiles; i += blockDim.x) {
-    const uint32_t mt = i / (P.n_coef >> 8);
-    if (!P.esc_tiles[i]) continue;
-    const uint32_t kind = P.esc_rows[2 * mt + 1] - P.esc_rows[2 * mt] > P.esc_lds_max ? 2u : 1u;
-    P.esc_tiles[i] = kind;
-    P.esc_list[(kind - 1) * P.n_tiles + atomicAdd(&s_cnt[kind - 1], 1u)] = i;
-  }
-  __syncthreads();
   if (t == 0) {
     Ctrl *ct = ctrl_of(P.ws);
-    ct->n_esc_tiles[0] = bad || plan_bad ? 0u : s_cnt[0];
-    ct->n_esc_tiles[1] = bad || plan_bad ? 0u : s_cnt[1];
     if (plan_bad) set_status(P.status, DCKV_EPLAN);
     else if (bad) set_status(P.status, DCKV_ECORRUPT);
     ct->n_esc = bad || plan_bad ? 0 : s_n_esc;
@@ -620,12 +597,8 @@ void launch_parse(const DecodeArgs &a) {
   P.crc = a.p->crc;
   P.n_groups = (uint32_t)a.g.n_groups;
   P.kept_bytes = (uint64_t)a.g.n_kept * a.p->D * 2;
-  P.act = a.p->dev.act;
-  P.esc_tiles = reinterpret_cast<uint32_t *>(a.ws + a.l.esc_tiles);
   P.esc_rows = reinterpret_cast<uint32_t *>(a.ws + a.l.esc_rows);
-  P.esc_list = reinterpret_cast<uint32_t *>(a.ws + a.l.esc_list);
-  P.n_tiles = (uint32_t)(a.g.n_mtiles * (a.p->C / kBN));
-  P.esc_lds_max = kEscLdsMax;
+  P.n_row_tiles = (uint32_t)a.g.n_mtiles;
   KernelTimer tm("parse", a.s);
   hipLaunchKernelGGL(k_parse, dim3(1), dim3(256), 0, a.s, P);
 }

@@ -1,0 +1,66 @@
+"""The plan's embedding-mean table on the GPU against the oracle.
+
+The code means of a position come from its token's input embedding (DCKV
+digest, "How it works", Conditional entropy models); the mean of every
+coefficient depends on the token id alone, so the plan holds H E[v] for the
+whole vocabulary.  Bars:
+  - columns: the active components in rank order, then the dropped ones in
+    ascending order (a permutation of all components);
+  - sampled rows (first, last, seeded random ids) within relative L2 1e-5 of
+    the oracle's float64 mean of the same bf16 inputs (fp32 accumulation over
+    2,048 bf16 products), every row on its own;
+  - the same with dropped components, whose columns follow the active ones.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import dckv_synth as synth
+from oracle import codec as ocodec
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+def _check_plan(plan, params, p):
+    dk = gu.dk()
+    tab, cols = dk.mean_table(plan)
+    vocab, C = tab.shape
+    assert vocab == params["embedding"].shape[0] and C == p.step.size
+    # column order
+    assert np.array_equal(np.sort(cols), np.arange(C))
+    assert np.array_equal(cols[:p.c_active], p.act_idx)
+    assert np.array_equal(cols[p.c_active:], np.flatnonzero(~p.active))
+    rng = np.random.default_rng(31)
+    ids = np.unique(np.concatenate([[0, 1, 255, 256, vocab - 1], rng.choice(vocab, size=64, replace=False)]))
+    got = tab[ids].cpu().numpy().astype(np.float64)
+    want = ocodec.embedding_mean(params, ids)[:, cols]
+    for n, v in enumerate(ids):
+        e = gu.rel_l2(got[n], want[n])
+        assert e <= TOL, (int(v), e)
+    gu.say("  %d table rows, worst rel %.3g" % (len(ids), max(gu.rel_l2(got[n], want[n]) for n in range(len(ids)))))
+
+
+def test_mean_table_matches_oracle():
+    params = synth.world().params()
+    g = synth.step_scale_for(220.0)
+    plan = gu.device_codec().plan(g)
+    gu.say("mean table, C_a = %d" % plan.c_active)
+    _check_plan(plan, params, gu.oracle_plan(params, g))
+
+
+def test_mean_table_with_dropped_components():
+    w = synth.world()
+    rng = np.random.default_rng(5)
+    scale = w.laplace_scale.copy()
+    scale[rng.choice(2048, size=77, replace=False)] = 1e-5
+    params = gu.params_with_scales(scale)
+    g = synth.step_scale_for(220.0)
+    p = gu.oracle_plan(params, g)
+    plan = gu.codec_with_scales(scale).plan(g)
+    assert plan.c_active == p.c_active < 2048
+    gu.say("mean table, C_a = %d" % plan.c_active)
+    _check_plan(plan, params, p)
