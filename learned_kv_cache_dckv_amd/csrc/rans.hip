@@ -32,6 +32,41 @@ constexpr int kBktStride = kBuckets + 4;  // bytes per bucket row in LDS (65 dwo
 
 __device__ __forceinline__ void set_status(int32_t *st, int code) { atomicCAS(st, 0, code); }
 
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// A load through a global (address space 1) pointer.
+template <class T>
+__device__ __forceinline__ T gload(const T *p) {
+  return *(const T __attribute__((address_space(1))) *)p;
+}
+
+// The tables of component group g into LDS: n rows of 256 u32 (LDS row stride
+// kTabStride), contiguous in the plan.  Every thread issues its 16-byte loads
+// before its first LDS write, so the copy costs one memory latency.
+template <int kThreads>
+__device__ __forceinline__ void stage_tab(uint32_t *tab, const uint32_t *gtab, int g, int n) {
+  constexpr int kPer = kLanes * 256 / 4 / kThreads;  // 16-byte pieces per thread
+  static_assert(kPer * kThreads * 4 == kLanes * 256, "whole pieces");
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(gtab + (size_t)kLanes * g * 256);
+  u32x4 v[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int pc = threadIdx.x + i * kThreads;  // row pc / 64, entries 4 (pc % 64) ..
+    if ((pc >> 6) < n) v[i] = gload(src + pc);
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int pc = threadIdx.x + i * kThreads;
+    if ((pc >> 6) < n) {
+      uint32_t *d = tab + (pc >> 6) * kTabStride + (pc & 63) * 4;
+      d[0] = v[i].x;
+      d[1] = v[i].y;
+      d[2] = v[i].z;
+      d[3] = v[i].w;
+    }
+  }
+}
+
 __device__ __forceinline__ Ctrl *ctrl_of(uint8_t *ws) { return reinterpret_cast<Ctrl *>(ws); }
 
 // x / f and x % f for 1 <= f < 2^15 and x < f * 2^17 (so x / f < 2^17): a
@@ -65,10 +100,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(EncP P) {
   __shared__ uint32_t tab[kLanes * kTabStride];
   const int g = blockIdx.y;
   const int n = min(kLanes, P.Ca - kLanes * g);
-  for (int idx = threadIdx.x; idx < n * 256; idx += blockDim.x) {
-    const int l = idx >> 8, s = idx & 255;
-    tab[l * kTabStride + s] = P.tab[(size_t)(kLanes * g + l) * 256 + s];
-  }
+  stage_tab<kEncWaves * 64>(tab, P.tab, g, n);
   __syncthreads();
   if (*P.status != 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -83,11 +115,29 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(EncP P) {
   const uint64_t higher = lane == 63 ? 0ull : (~0ull << (lane + 1));
   uint32_t x = kL;
   uint32_t cnt = 0;
+  // symbol words in chunks of 8 quads, last chunk first; the words of the
+  // next chunk are loaded while this one is coded
   const int nq = (Lb + 3) >> 2;
-  uint32_t wnext = lane_ok ? sw[(size_t)(nq - 1) * 64] : 0xFFFFFFFFu;
-  for (int qd = nq - 1; qd >= 0; --qd) {
-    const uint32_t w = wnext;
-    if (qd > 0) wnext = lane_ok ? sw[(size_t)(qd - 1) * 64] : 0xFFFFFFFFu;
+  const int nch = (nq + 7) >> 3;
+  uint32_t wq[8], wn[8];
+  auto load_chunk = [&](int ch, uint32_t (&w)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int qd = ch * 8 + u;
+      w[u] = lane_ok && qd < nq ? gload(sw + (size_t)qd * 64) : 0xFFFFFFFFu;
+    }
+  };
+  load_chunk(nch - 1, wn);
+  for (int ch = nch - 1; ch >= 0; --ch) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) wq[u] = wn[u];
+    if (ch > 0) load_chunk(ch - 1, wn);
+#pragma unroll
+    for (int u = 7; u >= 0; --u) {
+    const int qd = ch * 8 + u;
+    if (qd >= nq) continue;
+    const uint32_t w = wq[u];
+#pragma unroll
     for (int k = 3; k >= 0; --k) {
       const int i = qd * 4 + k;
       if (i >= Lb) continue;
@@ -107,6 +157,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(EncP P) {
         divmod_small(x, f, q, r);
         x = (q << kPrecBits) + r + c;
       }
+    }
     }
   }
   if (lane_ok) {
@@ -327,6 +378,7 @@ struct DecP {
   const uint8_t *bucket;
   const uint8_t *stream;
   const uint8_t *ws;
+  const uint32_t *esc_rows;  // [blocks][2]: index range of each block's escape records (from the parser)
   uint32_t *sym32;
   int64_t N, N256, n_blk;
   int Ca, G;
@@ -346,16 +398,22 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
   __shared__ unsigned long long ebits[kDecWaves][kBlock];
   const int g = blockIdx.y;
   const int n = min(kLanes, P.Ca - kLanes * g);
-  for (int idx = threadIdx.x; idx < n * 256; idx += blockDim.x) {
-    const int l = idx >> 8, s = idx & 255;
-    tab[l * kTabStride + s] = P.tab[(size_t)(kLanes * g + l) * 256 + s];
-  }
-  for (int idx = threadIdx.x; idx < n * (kBuckets + 1); idx += blockDim.x) {
+  stage_tab<kDecWaves * 64>(tab, P.tab, g, n);
+  {
     // bucket row of lane l: first symbol of each slot bucket, then the last
-    // symbol as the upper bound of the last bucket
-    const int l = idx / (kBuckets + 1), bb = idx - l * (kBuckets + 1);
-    bkt[l * kBktStride + bb] =
-        bb < kBuckets ? P.bucket[(size_t)kLanes * g * kBuckets + (size_t)l * kBuckets + bb] : (uint8_t)(kNSym - 1);
+    // symbol as the upper bound of the last bucket; one 16-byte piece per
+    // thread
+    static_assert(kDecWaves * 64 * 16 == kLanes * kBuckets, "one piece per thread");
+    const int pc = threadIdx.x, l = pc >> 4;
+    if (l < n) {
+      const u32x4 v = gload(reinterpret_cast<const u32x4 *>(P.bucket + (size_t)kLanes * g * kBuckets) + pc);
+      uint32_t *d = reinterpret_cast<uint32_t *>(bkt + l * kBktStride + (pc & 15) * 16);
+      d[0] = v.x;
+      d[1] = v.y;
+      d[2] = v.z;
+      d[3] = v.w;
+    }
+    if (pc < n) bkt[pc * kBktStride + kBuckets] = (uint8_t)(kNSym - 1);
   }
   __syncthreads();
   if (*P.status != 0) return;
@@ -379,23 +437,12 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
     return;
   }
   // escape positions of this group
-  const uint32_t n_esc = ct->n_esc;
   const uint32_t *esc = reinterpret_cast<const uint32_t *>(P.stream + ct->esc_off);
   bool has_esc = false;
-  if (n_esc) {
-    const uint64_t f_lo = (uint64_t)kBlock * b * P.Ca, f_hi = ((uint64_t)kBlock * b + Lb) * P.Ca;
-    uint32_t lo = 0, hi = n_esc;  // lower_bound(f_lo)
-    while (lo < hi) {
-      uint32_t mid = (lo + hi) >> 1;
-      if ((uint64_t)esc[2 * mid] < f_lo) lo = mid + 1; else hi = mid;
-    }
-    uint32_t lo2 = lo, hi2 = n_esc;  // lower_bound(f_hi)
-    while (lo2 < hi2) {
-      uint32_t mid = (lo2 + hi2) >> 1;
-      if ((uint64_t)esc[2 * mid] < f_hi) lo2 = mid + 1; else hi2 = mid;
-    }
-    lo = __builtin_amdgcn_readfirstlane(lo);
-    lo2 = __builtin_amdgcn_readfirstlane(lo2);
+  {
+    // the block's records, as the parser found them (a block is 256 rows)
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(gload(P.esc_rows + 2 * b));
+    const uint32_t lo2 = __builtin_amdgcn_readfirstlane(gload(P.esc_rows + 2 * b + 1));
     if (lo2 > lo) {
       has_esc = true;
       for (int i = lane; i < kBlock; i += 64) ebits[wave][i] = 0ull;
@@ -410,9 +457,22 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
       wave_sync_lds();
     }
   }
-  // word window [base, base + kWordBuf)
+  // word window [base, base + kWordBuf); the first window's loads are all
+  // issued before the first LDS write
   uint32_t base = 0;
-  for (uint32_t k = lane; k < min(W, (uint32_t)kWordBuf); k += 64) wb[k] = wsrc[k];
+  {
+    uint16_t v[kWordBuf / 64];
+#pragma unroll
+    for (int i = 0; i < kWordBuf / 64; ++i) {
+      const uint32_t k = (uint32_t)lane + 64u * i;
+      if (k < W) v[i] = gload(wsrc + k);
+    }
+#pragma unroll
+    for (int i = 0; i < kWordBuf / 64; ++i) {
+      const uint32_t k = (uint32_t)lane + 64u * i;
+      if (k < W) wb[k] = v[i];
+    }
+  }
   wave_sync_lds();
   uint32_t x = kL;
   if (lane_ok) x = (uint32_t)wb[2 * lane] | ((uint32_t)wb[2 * lane + 1] << 16);
@@ -610,6 +670,7 @@ void launch_rans_decode(const DecodeArgs &a) {
   P.bucket = a.p->dev.bucket;
   P.stream = a.stream;
   P.ws = a.ws;
+  P.esc_rows = reinterpret_cast<const uint32_t *>(a.ws + a.l.esc_rows);
   P.sym32 = reinterpret_cast<uint32_t *>(a.ws + a.l.sym);
   P.N = a.g.N;
   P.N256 = a.g.N256;

@@ -121,3 +121,108 @@ def oracle_stream_from_symbols(rows, T, params, p, sym, flat, qe) -> bytes:
                        c_active=p.c_active, n_groups=n_blk * G, n_esc=len(flat), step_scale=float(p.step_scale),
                        plan_crc=p.crc, total_bytes=0, rans_bytes=0)
     return ostream.write(h, rows[kept_t], groups, flat, qe)
+
+
+# ---------------------------------------------------------------------------
+# full-size checks on sampled rows (the oracle computes them one by one)
+# ---------------------------------------------------------------------------
+def full_codes(sym, flat, qe, act_idx, C):
+    """Codes [N][C] (int32, dropped components 0) from symbols and escapes."""
+    qa = np.ascontiguousarray(sym, dtype=np.int32) - 127
+    if len(flat):
+        qa.reshape(-1)[flat] = qe
+    q = np.zeros((sym.shape[0], C), dtype=np.int32)
+    q[:, act_idx] = qa
+    return q
+
+
+def sample_rows(N: int, rows_coded: np.ndarray, seed: int = 4242, n_random: int = 48, n_outliers: int = 12):
+    """Tile and block edges, the first and last rows, the rows of largest norm
+    (outliers, when the workload has them) and seeded random rows."""
+    fixed = [0, 1, 2, 3, 126, 127, 128, 129, 254, 255, 256, 257, 511, 512, 513, 32767, 32768,
+             N - 4, N - 3, N - 2, N - 1]
+    rng = np.random.default_rng(seed)
+    rand = rng.choice(N, size=min(n_random, N), replace=False)
+    norms = np.concatenate([np.linalg.norm(bf16.to_f64(rows_coded[i:i + 4096]), axis=1)
+                            for i in range(0, N, 4096)])
+    outl = np.argsort(norms)[-n_outliers:]
+    js = np.unique(np.concatenate([np.array([j for j in fixed if 0 <= j < N]), rand, outl]))
+    return js.astype(np.int64)
+
+
+def check_sampled_rows(rows, tok, T, params, p, sym_g, flat_g, qe_g, js, out_rows=None, yhat_view=None):
+    """Codes and decoded rows of sampled coded rows js against the oracle.
+
+    The oracle's float64 transform and its float32 quantisation decision,
+    with the GPU's even-row codes as the odd rows' neighbours (as the decoder
+    has them), must give the GPU's codes up to certified ties; the oracle's
+    two-pass dequantisation, correction, synthesis and RoPE of the GPU's codes
+    must match the GPU's rows (and the yhat_b view, if given) within the
+    float bar, in aggregate and row by row.
+    """
+    sh = ocodec.shape_of(params)
+    N, _, coded_t = ocodec.split_positions(T, sh.keep_head, sh.keep_tail)
+    C = p.step.size
+    act = p.active
+    qg = full_codes(sym_g, flat_g, qe_g, p.act_idx, C)
+    A = bf16.to_f64(params["analysis"])
+    y = bf16.to_f64(rows[coded_t[js]]) @ A.T
+    need = np.unique(np.concatenate([js, js[js % 2 == 1] - 1, js[(js % 2 == 1) & (js + 1 < N)] + 1]))
+    m_need = ocodec.embedding_mean(params, tok[coded_t[need]])
+    pos = {int(j): i for i, j in enumerate(need)}
+    step = p.step.astype(np.float64)
+    a64 = params["nbr_weight"].astype(np.float64)
+    mu = np.empty((len(js), C))
+    for n, j in enumerate(js):
+        m = m_need[pos[int(j)]].copy()
+        if j % 2 == 1:
+            nb = m_need[pos[int(j - 1)]] + qg[j - 1] * step
+            if j + 1 < N:
+                nb = nb + m_need[pos[int(j + 1)]] + qg[j + 1] * step
+            m = m + a64 * nb
+        mu[n] = m
+    res = (y - mu) / step
+    d = (y - mu)[:, act]
+    qo = ocodec._decide(d, p.step[act])
+    qs = qg[js][:, act].astype(np.int64)
+    agree = float(np.mean(qo == qs))
+    say("  sampled codes agree %.7f (%d codes)" % (agree, qo.size))
+    assert agree >= SYMBOL_AGREEMENT
+    for n, k in np.argwhere(qo != qs):
+        # a disagreement is a tie within float32 accuracy of the residual
+        rr = res[n, act][k]
+        tie = 0.5 * (qo[n, k] + qs[n, k])
+        tol = 2.0 ** -17 * (abs(y[n, act][k]) + abs(mu[n, act][k])) / p.step[act][k] + 1e-4
+        assert abs(qo[n, k] - qs[n, k]) == 1 and abs(rr - tie) <= tol, (js[n], k, rr, qo[n, k], qs[n, k])
+    yhat = mu + qg[js] * step[None, :]
+    yb_bits = bf16.from_f64(yhat)
+    if yhat_view is not None:
+        e1 = rel_l2(bf16.to_f64(yhat_view[js]), bf16.to_f64(yb_bits))
+        say("  sampled yhat_b rel %.3g (bit-equal %.5f)" % (e1, np.mean(yhat_view[js] == yb_bits)))
+        assert e1 <= REL_L2_TOL
+    if out_rows is None:
+        return
+    yb = bf16.to_f64(yb_bits)
+    hb = bf16.to_f64(bf16.from_f64(ocodec.gelu(yb @ bf16.to_f64(params["w1"]).T)))
+    xhat = yb @ bf16.to_f64(params["synthesis"]).T + hb @ bf16.to_f64(params["w2"]).T
+    want = bf16.from_f64(ocodec.rope(xhat, coded_t[js], sh))
+    got = out_rows[coded_t[js]]
+    e3 = rel_l2(bf16.to_f64(got), bf16.to_f64(want))
+    say("  sampled rows rel %.3g (bit-equal %.5f)" % (e3, np.mean(got == want)))
+    assert e3 <= REL_L2_TOL
+    for n in range(len(js)):
+        assert rel_l2(bf16.to_f64(got[n]), bf16.to_f64(want[n])) <= 4 * REL_L2_TOL, js[n]
+
+
+def check_kept_rows(rows, T, params, out_rows):
+    """Kept rows: RoPE'd keys within the float bar, values and row 0 bit-identical."""
+    sh = ocodec.shape_of(params)
+    _, kept_t, _ = ocodec.split_positions(T, sh.keep_head, sh.keep_tail)
+    if not len(kept_t):
+        return
+    want = bf16.from_f64(ocodec.rope(bf16.to_f64(rows[kept_t]), kept_t, sh))
+    got = out_rows[kept_t]
+    assert rel_l2(bf16.to_f64(got), bf16.to_f64(want)) <= REL_L2_TOL
+    vcols = np.concatenate([np.arange(l * 1024 + 512, l * 1024 + 1024) for l in range(sh.n_layers)])
+    assert np.array_equal(got[:, vcols], rows[kept_t][:, vcols])
+    assert np.array_equal(out_rows[0], rows[0])
