@@ -93,12 +93,15 @@ __device__ __forceinline__ bool wg_stop(const int32_t *st) {
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet)
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even: the conversion instruction of gfx950
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+// two fp32 -> two bf16 in one word (a in the low half), one instruction
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD gets a
@@ -300,10 +303,20 @@ __device__ __forceinline__ int acc_row(int mb, int v, int lane) { return mb * 32
 // bf16 output through a per-wave LDS transpose
 // ---------------------------------------------------------------------------
 // The caller writes its 128x128 values (bf16) to the wave's LDS tile with
-// put(); flush_rows() then stores 16-byte row segments: LDS columns [0, 64)
-// go to out[row][col_lo + c], columns [64, 128) to out[row][col_hi + c - 64].
-__device__ __forceinline__ void put(char *wtile, int r, int cc, uint16_t v) {
-  *reinterpret_cast<uint16_t *>(wtile + (r * kOutStride + cc) * 2) = v;
+// put_rows2(); flush_rows() then stores 16-byte row segments: LDS columns
+// [0, 64) go to out[row][col_lo + c], columns [64, 128) to
+// out[row][col_hi + c - 64].
+
+// Rows r and r + 1 of this lane's column tcol (y0, y1) into the wave's LDS
+// tile as 32-bit pairs of adjacent columns: lanes l and l ^ 1 hold columns
+// tcol and tcol ^ 1 of the same rows and swap one value (a DPP quad
+// permute); the even lane then writes row r, the odd lane row r + 1.
+__device__ __forceinline__ void put_rows2(char *wtile, int r, int tcol, float y0, float y1, int lane) {
+  const bool odd = lane & 1;
+  const float send = odd ? y0 : y1;
+  const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
+  const float a = odd ? recv : y0, b = odd ? y1 : recv;
+  *reinterpret_cast<uint32_t *>(wtile + ((r + (odd ? 1 : 0)) * kOutStride + (tcol & ~1)) * 2) = pack_bf16x2(a, b);
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -452,23 +465,6 @@ __device__ __forceinline__ uint32_t quant_one(float d, float step, float inv, in
   return (uint32_t)kEsc;
 }
 
-__device__ __forceinline__ uint32_t with_byte(uint32_t w, int i, uint32_t s) {
-  return (w & ~(0xFFu << (8 * i))) | (s << (8 * i));
-}
-
-// First row of the quad after the one in register group g of block mb, for
-// the lane that holds this quad: lanes 0..31 find it in lane l+32 (same
-// group), lanes 32..63 in lane l-32 (next group, or group 0 of the next
-// block).  `ext` is used for the wave tile's last quad.  All lanes call this.
-__device__ __forceinline__ float next_quad_row0(const f32x16 (&acc)[4][4], int mb, int nb, int g, float ext, int lane) {
-  const float same = __shfl_xor(acc[mb][nb][4 * g], 32);
-  float nxt;
-  if (g < 3) nxt = __shfl_xor(acc[mb][nb][4 * g + 4], 32);
-  else if (mb < 3) nxt = __shfl_xor(acc[mb + 1 < 4 ? mb + 1 : 3][nb][0], 32);
-  else nxt = ext;
-  return lane < 32 ? same : nxt;
-}
-
 __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   if (wg_stop(P.status)) return;
@@ -486,60 +482,133 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
     B.row[i] = (uint32_t)P.act[n0 + staged_row(i)];
   }
   f32x16 acc[4][4];
-  mainloop<false>(A, B, kD / kBK, acc, lds);
+  mainloop(A, B, kD / kBK, acc, lds);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // The epilogue works one 32x32 accumulator block at a time: its 8 means of
+  // one parity are read from LDS together, every value is decided without a
+  // branch, and escapes (rare) take one branch per block.  The even rows'
+  // symbols wait for pass 2 packed two quads per register.
+  const int lane = epilogue_lane(), wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t wrow0 = m0 + wm * 128;  // first row of this wave's tile
-  int r_nb[4];
-  float st_nb[4], inv_nb[4], a_nb[4];
+  const int N = (int)P.N;
+  const int wrow0 = (int)m0 + wm * 128;  // first row of this wave's tile
+  Ctrl *ct = reinterpret_cast<Ctrl *>(P.ws);
+  // bit 31 set once a difference is not finite: its exponent field plus one
+  // unit carries into the sign bit only when the field is all ones
+  uint32_t nonfin = 0u;
+
+  // One value: d = y - mu, valid = 1 for a coded row and active rank, else 0.
+  // Returns the symbol (255 when escaped, 0xFF when not valid), sets qi, the
+  // escape bit (1 for an escaped valid value) and yhat (0 when not valid).
+  // Flags are integer arithmetic, so no lane mask stays alive.
+  auto code = [&](float d, float m, float st, float inv, uint32_t valid, int &qi, uint32_t &esc, float &yhat) {
+    nonfin |= (__float_as_uint(d) & 0x7F800000u) + 0x00800000u;
+    const float qf = fminf(fmaxf(rintf(div_step(d, st, inv)), -kQLimit), kQLimit);
+    qi = (int)qf;
+    const uint32_t s = (uint32_t)(qi + 127);
+    const uint32_t out = s > 254u ? 1u : 0u;       // 1: beyond +-127 (s wraps for q < -127)
+    const uint32_t om = 0u - out, vm = valid - 1u;  // all ones when escaped / not valid
+    esc = out & valid;
+    yhat = (m + qf * st) * (float)valid;
+    return (((s & ~om) | om) | vm) & 0xFFu;
+  };
+  // valid for the row of register v of block mb (of an active rank)
+  auto valid_v = [&](int ln, int mb, int v, uint32_t rvalid) {
+    return rvalid & ((uint32_t)(wrow0 + 4 * (ln >> 5) - N + mb * 32 + 8 * (v >> 2) + (v & 3)) >> 31);
+  };
+  // the staged mean of register v of block (mb, nb): a per-lane base plus a
+  // constant offset (tile row = wm 128 + 4 (lane / 32) + constant, all even
+  // but the constant's low bit)
+  auto mean = [&](int ln, int mb, int nb, int v) {
+    const float *mbase =
+        reinterpret_cast<const float *>(lds) + (wm * 64 + 2 * (ln >> 5)) * kMeanRowFloats + wn * 128 + (ln & 31);
+    return mbase[(mb * 16 + 4 * (v >> 2) + ((v & 3) >> 1)) * kMeanRowFloats + nb * 32];
+  };
+  // symbol words: quad (wrow0 / 4 + lane / 32 + 8 mb + 2 g) of rank r
+  auto sym_at = [&](int ln, int mb, int nb, int g) {
+    return P.sym32 + ((size_t)(wrow0 >> 2) + (ln >> 5)) * 64 +
+           (size_t)(((n0 + wn * 128) >> 6) + (nb >> 1)) * (size_t)(P.N256 / 4) * 64 + (ln & 31) + (nb & 1) * 32 +
+           (mb * 8 + 2 * g) * 64;
+  };
+  // escape records of the values of one parity of a block (bit e: register 2e + par)
+  const uint32_t esc_cap = (uint32_t)min<int64_t>(P.esc_cap, 0x7FFFFFFF);
+  auto escapes = [&](uint32_t em, const int (&qi)[8], int par, int mb, int r) {
+    const int ln = epilogue_lane();
+    uint32_t idx = atomicAdd(&ct->n_esc, (uint32_t)__builtin_popcount(em));
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int r = n0 + wn * 128 + nb * 32 + (lane & 31);
-    const int c = P.act[r];
-    r_nb[nb] = r;
-    st_nb[nb] = P.step[c];
-    inv_nb[nb] = 1.0f / st_nb[nb];
-    a_nb[nb] = P.nbr[c];
-  }
-  uint32_t symw[4][4][4];
-  bool bad = false;
+    for (int e = 0; e < 8; ++e) {
+      if (em & (1u << e)) {
+        const uint32_t j = (uint32_t)(wrow0 + acc_row(mb, 2 * e + par, ln));
+        if (idx < esc_cap) {
+          P.esc_raw[2 * idx] = j * (uint32_t)P.Ca + (uint32_t)r;
+          P.esc_raw[2 * idx + 1] = (uint32_t)qi[e];
+        }
+        ++idx;
+      }
+    }
+  };
+
   // pass 1: even rows, mu = H E[tok], from the even rows' means staged in LDS
   mean_rows_to_lds(P, m0, n0, 0, lds, lane);
   __syncthreads();  // (waits for this wave's loads, then for every wave's)
+  // the lane's column of each block column nb: rank, step, 1 / step, a
+  int r_nb[4];
+  float st_nb[4], inv_nb[4], a_nb[4];
+  uint32_t rv_nb[4];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int nb = 0; nb < 4; ++nb) {
+    r_nb[nb] = n0 + wn * 128 + nb * 32 + (lane & 31);
+    const int c = P.act[r_nb[nb]];
+    st_nb[nb] = P.step[c];
+    inv_nb[nb] = 1.0f / st_nb[nb];
+    a_nb[nb] = P.nbr[c];
+    rv_nb[nb] = (uint32_t)(r_nb[nb] - P.Ca) >> 31;
+  }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const int tcol = wn * 128 + nb * 32 + (lane & 31);
+      const int r = r_nb[nb];
+      const float st = st_nb[nb], inv = inv_nb[nb];
+      const uint32_t rvalid = rv_nb[nb];
+      const int ln = lane;
+      f32x16 b = acc_block(acc, mb, nb);
+      float m[8];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint32_t w = 0xFFFFFFFFu;
+      for (int e = 0; e < 8; ++e) m[e] = mean(ln, mb, nb, 2 * e);
+      int qi[8];
+      uint32_t em = 0, w = 0;
 #pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const int v = 4 * g + i;
-          const float m = mean_at(lds, wm * 128 + acc_row(mb, v, lane), tcol);
-          const int64_t j = wrow0 + acc_row(mb, v, lane);
-          if (j < P.N && r_nb[nb] < P.Ca) {
-            float qf;
-            const uint32_t sy = quant_one(acc[mb][nb][v] - m, st_nb[nb], inv_nb[nb], j, r_nb[nb], P, bad, qf);
-            acc[mb][nb][v] = m + qf * st_nb[nb];
-            w = with_byte(w, i, sy);
-          } else {
-            acc[mb][nb][v] = 0.f;  // a missing right neighbour counts as zero
-          }
+      for (int e = 0; e < 8; ++e) {
+        const int v = 2 * e;
+        uint32_t esc;
+        float yh;
+        const uint32_t sy = code(b[v] - m[e], m[e], st, inv, valid_v(ln, mb, v, rvalid), qi[e], esc, yh);
+        b[v] = yh;  // a missing right neighbour counts as zero
+        em |= esc << e;
+        // the quad's word with its even rows (bytes 0 and 2); pass 2 adds the odd ones
+        w |= sy << (16 * (e & 1));
+        if (e & 1) {
+          if (valid_v(ln, mb, v - 2, rvalid)) *sym_at(ln, mb, nb, e >> 1) = w | 0xFF00FF00u;
+          w = 0;
         }
-        symw[mb][nb][g] = w;
       }
+      if (em) escapes(em, qi, 0, mb, r);
+      acc[mb][nb] = b;
+      asm volatile("" : "+a"(acc[mb][nb]));  // back to the accumulator registers
+      asm volatile("" : "+v"(nonfin));       // this block's values are folded in here
+      __builtin_amdgcn_sched_barrier(0);
     }
+  }
   // the first row of each wave row: to the wave above (LDS) and, for the
   // tile's row 0, to the fix-up of the previous tile (global)
   float *xch = reinterpret_cast<float *>(lds + kXchOff);
   if (lane < 32) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
+      const int r = n0 + wn * 128 + nb * 32 + lane;
       xch[wm * 256 + wn * 128 + nb * 32 + lane] = acc[0][nb][0];
-      if (wm == 0 && r_nb[nb] < P.Ca) P.halo_b[(int64_t)mt * P.C + r_nb[nb]] = acc[0][nb][0];
+      if (wm == 0 && r < P.Ca) P.halo_b[(int64_t)mt * P.C + r] = acc[0][nb][0];
     }
   }
   __syncthreads();
@@ -549,43 +618,72 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   mean_rows_to_lds(P, m0, n0, 1, lds, lane);
   __syncthreads();
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const int tcol = wn * 128 + nb * 32 + (lane & 31);
-      const float ext = wm == 0 ? xch[256 + wn * 128 + nb * 32 + (lane & 31)] : 0.f;
-      const float a = a_nb[nb];
       const int r = r_nb[nb];
+      const float st = st_nb[nb], inv = inv_nb[nb], a = a_nb[nb];
+      const uint32_t rvalid = rv_nb[nb];
+      const float ext = wm == 0 && mb == 3 ? xch[256 + wn * 128 + nb * 32 + (lane & 31)] : 0.f;
+      const int ln = lane;
+      const f32x16 b = acc_block(acc, mb, nb);
+      const float nx0 = mb < 3 ? acc[mb + 1][nb][0] : 0.f;  // the next block's first row
+      float m[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[e] = mean(ln, mb, nb, 2 * e + 1);
+      int qi[8];
+      uint32_t em = 0;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float next3 = next_quad_row0(acc, mb, nb, g, ext, lane);
-        const float m1 = mean_at(lds, wm * 128 + acc_row(mb, 4 * g + 1, lane), tcol);
-        const float m3 = mean_at(lds, wm * 128 + acc_row(mb, 4 * g + 3, lane), tcol);
-        uint32_t w = symw[mb][nb][g];
-        const int64_t j0 = wrow0 + acc_row(mb, 4 * g, lane);
-        const float y0 = acc[mb][nb][4 * g], y2 = acc[mb][nb][4 * g + 2];
-        if (j0 + 1 < P.N && r < P.Ca) {
-          float qf;
-          const float mu = m1 + a * (y0 + y2);
-          w = with_byte(w, 1, quant_one(acc[mb][nb][4 * g + 1] - mu, st_nb[nb], inv_nb[nb], j0 + 1, r, P, bad, qf));
+        // the first row of the next quad: lanes < 32 hold it in lane + 32
+        // (same group), lanes >= 32 in lane - 32 (next group or next block)
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(b[4 * g]),
+                                                         __float_as_uint(g < 3 ? b[4 * g + 4] : nx0), false, false);
+        float next3 = __uint_as_float(lane < 32 ? sw[1] : sw[0]);
+        if (g == 3 && mb == 3 && lane >= 32) next3 = ext;
+        const float y0 = b[4 * g], y2 = b[4 * g + 2];
+        // bytes 1 and 3 of the quad's word (pass 1 wrote 0 and 2): byte
+        // stores, so that no load waits behind this pass's stores
+        uint32_t w = 0u;
+        {
+          const float mu = m[2 * g] + a * (y0 + y2);
+          uint32_t esc;
+          float yh;
+          const uint32_t sy = code(b[4 * g + 1] - mu, mu, st, inv, valid_v(ln, mb, 4 * g + 1, rvalid), qi[2 * g], esc,
+                                   yh);
+          em |= esc << (2 * g);
+          w |= sy << 8;
         }
-        if (j0 + 3 < P.N && r < P.Ca) {
-          uint32_t sy;
-          if (wm == 1 && mb == 3 && g == 3 && lane >= 32 && defer_last) {
-            P.halo_a[(int64_t)mt * P.C + r] = acc[mb][nb][4 * g + 3] - m3 - a * y2;
-            sy = 0u;  // finished by the fix-up
-          } else {
-            float qf;
-            const float mu = m3 + a * (y2 + next3);
-            sy = quant_one(acc[mb][nb][4 * g + 3] - mu, st_nb[nb], inv_nb[nb], j0 + 3, r, P, bad, qf);
+        {
+          // the tile's last odd row waits for the next tile's first row
+          const bool deferred = wm == 1 && mb == 3 && g == 3 && lane >= 32 && defer_last;
+          const uint32_t valid = valid_v(ln, mb, 4 * g + 3, rvalid);
+          const float mu = m[2 * g + 1] + a * (y2 + next3);
+          uint32_t esc;
+          float yh;
+          uint32_t sy = code(b[4 * g + 3] - mu, mu, st, inv, valid, qi[2 * g + 1], esc, yh);
+          if (deferred) {
+            if (valid) P.halo_a[(int64_t)mt * P.C + r] = b[4 * g + 3] - m[2 * g + 1] - a * y2;
+            sy = valid ? 0u : 0xFFu;  // finished by the fix-up
+            esc = 0u;
           }
-          w = with_byte(w, 3, sy);
+          em |= esc << (2 * g + 1);
+          w |= sy << 24;
         }
-        if (j0 < P.N && r < P.Ca) P.sym32[((size_t)(r >> 6) * (P.N256 / 4) + (j0 >> 2)) * 64 + (r & 63)] = w;
+        if (valid_v(ln, mb, 4 * g, rvalid)) {
+          uint8_t *wb = reinterpret_cast<uint8_t *>(sym_at(ln, mb, nb, g));
+          wb[1] = (uint8_t)(w >> 8);
+          wb[3] = (uint8_t)(w >> 24);
+        }
       }
+      if (em) escapes(em, qi, 1, mb, r);
+      asm volatile("" : "+v"(nonfin));
+      __builtin_amdgcn_sched_barrier(0);
     }
-  if (bad) set_status(P.status, DCKV_EINVAL);
+  }
+  if (nonfin >> 31) set_status(P.status, DCKV_EINVAL);
 }
+
 
 // last odd row of every row tile whose right neighbour is in the next tile
 __global__ void k_encode_fixup(QuantP P, int64_t n_fix) {
@@ -749,8 +847,8 @@ __global__ __launch_bounds__(kDeqThreads) void k_dequant(DeqP P) {
   for (int i = 0; i < kDeqRows; ++i) {
     if (j0 + i < N) {
       u32x2 o;
-      o.x = (uint32_t)f2bf(y[i][0]) | ((uint32_t)f2bf(y[i][1]) << 16);
-      o.y = (uint32_t)f2bf(y[i][2]) | ((uint32_t)f2bf(y[i][3]) << 16);
+      o.x = pack_bf16x2(y[i][0], y[i][1]);
+      o.y = pack_bf16x2(y[i][2], y[i][3]);
       *(u32x2 __attribute__((address_space(1))) *)(P.yhat_b + (size_t)(j0 + i) * kC + c0) = o;
     }
   }
@@ -767,7 +865,8 @@ __device__ __forceinline__ void acc_to_wtile(const f32x16 (&acc)[4][4], char *wt
     for (int nb = 0; nb < 4; ++nb) {
       const f32x16 b = acc_block(acc, mb, nb);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) put(wtile, acc_row(mb, v, lane), nb * 32 + (lane & 31), f2bf(fn(b[v])));
+      for (int v = 0; v < 16; v += 2)
+        put_rows2(wtile, acc_row(mb, v, lane), nb * 32 + (lane & 31), fn(b[v]), fn(b[v + 1]), lane);
       __builtin_amdgcn_sched_barrier(0);  // one block at a time: bounded live ranges
     }
 }
@@ -855,33 +954,56 @@ __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
   const int64_t wrow0 = m0 + wm * 128;
   char *wtile = lds + wave * kOutWaveBytes;
   if (is_key) {
+    // Angles: the lane's first row from the tables (position p = 256 hi +
+    // lo), every other row by rotating it through 32 (block), 8 (register
+    // group) and 1 (row) positions, whose cos / sin are rows 32, 8 and 1 of
+    // the low table.  All table loads are issued before the first rotation.
+    // A lane whose first row is past the end stores nothing; its position
+    // is clamped only to stay inside the tables.
+    const int64_t p0 = P.keep_head + min<int64_t>(wrow0 + 4 * (lane >> 5), P.N - 1);
+    float2 ta[2], tb[2], r1[2], r8[2], r32[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int f = 64 * wn + 32 * nb + (lane & 31);  // rotary frequency index
-      const float2 w1 = P.rope_lo[kHalf + f];          // (cos w_f, sin w_f): one position step
+      ta[nb] = P.rope_lo[(size_t)(p0 & 255) * kHalf + f];
+      tb[nb] = P.rope_hi[(size_t)(p0 >> 8) * kHalf + f];
+      r1[nb] = P.rope_lo[1 * kHalf + f];
+      r8[nb] = P.rope_lo[8 * kHalf + f];
+      r32[nb] = P.rope_lo[32 * kHalf + f];
+    }
+    auto rot = [](float &c, float &s, float2 r) {
+      const float c2 = c * r.x - s * r.y;
+      s = s * r.x + c * r.y;
+      c = c2;
+    };
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int tc0 = nb * 32 + (lane & 31), tc1 = (nb + 2) * 32 + (lane & 31);
+      float c_mb = tb[nb].x * ta[nb].x - tb[nb].y * ta[nb].y;
+      float s_mb = tb[nb].y * ta[nb].x + tb[nb].x * ta[nb].y;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const f32x16 blo = acc_block(acc, mb, nb), bhi = acc_block(acc, mb, nb + 2);
+        float c_g = c_mb, s_g = s_mb;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          // rows past the end are not stored; their angle is clamped in range
-          const int64_t pos = P.keep_head + min<int64_t>(wrow0 + acc_row(mb, 4 * g, lane), P.N - 1);
-          const float2 a = P.rope_lo[(size_t)(pos & 255) * kHalf + f];
-          const float2 b = P.rope_hi[(size_t)(pos >> 8) * kHalf + f];
-          float cs = b.x * a.x - b.y * a.y;
-          float sn = b.y * a.x + b.x * a.y;
+          float cs = c_g, sn = s_g;
+          float o0[4], o1[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int v = 4 * g + i;
-            const float x0 = blo[v], x1 = bhi[v];
-            const int row = acc_row(mb, v, lane);
-            put(wtile, row, nb * 32 + (lane & 31), f2bf(x0 * cs - x1 * sn));
-            put(wtile, row, (nb + 2) * 32 + (lane & 31), f2bf(x1 * cs + x0 * sn));
-            const float c2 = cs * w1.x - sn * w1.y;  // advance the angle by one position
-            sn = sn * w1.x + cs * w1.y;
-            cs = c2;
+            o0[i] = blo[v] * cs - bhi[v] * sn;
+            o1[i] = bhi[v] * cs + blo[v] * sn;
+            if (i < 3) rot(cs, sn, r1[nb]);
           }
+          const int row = acc_row(mb, 4 * g, lane);
+          put_rows2(wtile, row, tc0, o0[0], o0[1], lane);
+          put_rows2(wtile, row + 2, tc0, o0[2], o0[3], lane);
+          put_rows2(wtile, row, tc1, o1[0], o1[1], lane);
+          put_rows2(wtile, row + 2, tc1, o1[2], o1[3], lane);
+          if (g < 3) rot(c_g, s_g, r8[nb]);
         }
+        if (mb < 3) rot(c_mb, s_mb, r32[nb]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
