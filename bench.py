@@ -221,7 +221,7 @@ def main(argv=None) -> int:
     dk.dckv_profile_enable(False)
     kern = {}
     for name in ("analysis_gemm", "fixup", "rans_encode", "scan", "pack", "parse", "rans_decode",
-                 "dequant", "w1_gemm", "synthesis_gemm"):
+                 "dequant", "w1_gemm", "w1_gelu", "synthesis_gemm"):
         tot, n = dk.dckv_profile_read(name)
         if n:
             kern[name] = {"avg_ms": tot / n, "launches": n}

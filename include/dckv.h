@@ -261,7 +261,7 @@ int dckv_workspace_view(const dckv_plan_t *plan, int64_t T, int32_t which, uint6
  * synchronises those events and returns the summed milliseconds and the
  * number of launches since the last reset.  Kernel names:
  * "analysis_gemm", "rans_encode", "rans_decode", "dequant", "w1_gemm",
- * "synthesis_gemm", "fixup", "scan", "pack", "parse".
+ * "w1_gelu", "synthesis_gemm", "fixup", "scan", "pack", "parse".
  * --------------------------------------------------------------------------*/
 int dckv_profile_enable(int32_t on);
 int dckv_profile_reset(void);

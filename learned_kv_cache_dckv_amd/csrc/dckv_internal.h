@@ -100,7 +100,7 @@ static_assert(sizeof(Ctrl) == 256, "ctrl block is 256 bytes");
 
 struct Layout {
   uint64_t ctrl, sym, esc_raw, esc_sorted, halo_a, halo_b, scratch, gwords, goffs;
-  uint64_t yhat_b, h_b, rope_lo, rope_hi, esc_rows, total;
+  uint64_t yhat_b, h_b, w1_part, rope_lo, rope_hi, esc_rows, total;
 };
 
 Geometry geometry(const dckv_plan_t *p, int64_t T);

@@ -880,34 +880,69 @@ struct Identity {
 // ---------------------------------------------------------------------------
 struct W1P {
   const uint16_t *yhat_b, *W1;
-  uint16_t *h_b;  // [NM][256]
-  int64_t N;
+  float *part;       // [2][NM][256]: the products over each half of the coefficients
+  uint16_t *h_b;     // [NM][256]
+  int64_t N, NM;
   int n_mt;
   int32_t *status;
 };
 
+// W1 yhat_b as two half-K products (coefficients [0, 1024) and [1024, 2048)):
+// 256-row tiles times 2 halves fill twice as many CUs as whole-K tiles; the
+// halves are added (one fp32 addition, so the order does not matter) by
+// k_w1_gelu.
 __global__ __launch_bounds__(kThreads, 1) void k_w1(W1P P) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   if (wg_stop(P.status)) return;
-  int mt, nt;
-  tile_of(blockIdx.x, P.n_mt, 1, mt, nt);
+  int mt, kh;
+  tile_of(blockIdx.x, P.n_mt * 2, 2, mt, kh);
   const int64_t m0 = (int64_t)mt * kBM;
   Operand A, B;
-  set_sources(A, P.yhat_b, kC * 2, P.yhat_b, kC * 2, kC / kBK);
-  set_sources(B, P.W1, kC * 2, P.W1, kC * 2, kC / kBK);
+  set_sources(A, P.yhat_b + kh * (kC / 2), kC * 2, P.yhat_b + kh * (kC / 2), kC * 2, kC / 2 / kBK);
+  set_sources(B, P.W1 + kh * (kC / 2), kC * 2, P.W1 + kh * (kC / 2), kC * 2, kC / 2 / kBK);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     A.row[i] = (uint32_t)(m0 + staged_row(i));
     B.row[i] = (uint32_t)staged_row(i);
   }
   f32x16 acc[4][4];
-  mainloop(A, B, kC / kBK, acc, lds);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  mainloop(A, B, kC / 2 / kBK, acc, lds);
+  const int lane = epilogue_lane(), wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  char *wtile = lds + wave * kOutWaveBytes;
-  acc_to_wtile(acc, wtile, lane, [](float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); });
-  wave_lds_sync();
-  flush_rows(wtile, P.h_b, kHid, m0 + wm * 128, wn * 128, wn * 128 + 64, P.N);
+  float *part = P.part + ((size_t)kh * P.NM + m0 + wm * 128) * kHid + wn * 128 + (lane & 31);
+  const int rows_left = (int)min<int64_t>(P.N - (m0 + wm * 128), 128);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const f32x16 b = acc_block(acc, mb, nb);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = acc_row(mb, v, lane);
+        if (row < rows_left) part[(size_t)row * kHid + nb * 32] = b[v];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// h_b = bf16(GELU(part0 + part1)), exact-erf GELU; 4 hidden units per thread
+__global__ __launch_bounds__(256) void k_w1_gelu(W1P P) {
+  if (*P.status != 0) return;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (row, 4-unit group)
+  if (i >= P.N * (kHid / 4)) return;
+  const size_t o = (size_t)i * 4;
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(P.part + o);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(P.part + (size_t)P.NM * kHid + o);
+  float h[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float u = a[k] + b[k];
+    h[k] = 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
+  }
+  u32x2 w;
+  w.x = pack_bf16x2(h[0], h[1]);
+  w.y = pack_bf16x2(h[2], h[3]);
+  *reinterpret_cast<u32x2 *>(P.h_b + o) = w;
 }
 
 // ---------------------------------------------------------------------------
@@ -1182,11 +1217,16 @@ void launch_w1_gemm(const DecodeArgs &a) {
   W1P P;
   P.yhat_b = reinterpret_cast<const uint16_t *>(a.ws + a.l.yhat_b);
   P.W1 = a.p->W1;
+  P.part = reinterpret_cast<float *>(a.ws + a.l.w1_part);
   P.h_b = reinterpret_cast<uint16_t *>(a.ws + a.l.h_b);
   P.N = a.g.N;
+  P.NM = a.g.NM;
   P.n_mt = (int)a.g.n_mtiles;
   P.status = a.status;
-  launch_gemm(k_w1, "w1_gemm", P.n_mt, P, a.s);
+  launch_gemm(k_w1, "w1_gemm", P.n_mt * 2, P, a.s);
+  const int64_t work = a.g.N * (kHid / 4);
+  KernelTimer tm("w1_gelu", a.s);
+  hipLaunchKernelGGL(k_w1_gelu, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, a.s, P);
 }
 
 void launch_synthesis_gemm(const DecodeArgs &a) {

@@ -395,6 +395,7 @@ Layout dckv::layout(const dckv_plan_t *p, const Geometry &g) {
   l.yhat_b = take((uint64_t)g.NM * p->C * 2);
   l.esc_rows = take((uint64_t)g.n_mtiles * 2 * 4);
   l.h_b = take((uint64_t)g.NM * p->hidden * 2);
+  l.w1_part = take(2ull * g.NM * p->hidden * 4);
   l.rope_lo = take(256ull * kHalf * 8);
   l.rope_hi = take((uint64_t)g.rope_hi * kHalf * 8);
   const uint64_t dec_end = off;
