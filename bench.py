@@ -148,6 +148,35 @@ def write_traffic(fetch_dir: str, write_dir: str, copy_mib: int, T: int) -> int:
     return 0
 
 
+def vendor_gemm(N: int, steps: int) -> int:
+    """The vendor library's plain bf16 GEMMs (torch.matmul: hipBLASLt) on the
+    codec's GEMM shapes, for comparison with the fused kernels' main loops.
+    Operands are random; B is stored transposed-contiguous (k-major)."""
+    import torch
+    dev = torch.device("cuda:0")
+    shapes = [("analysis", N, 2048, 6144), ("w1", N, 256, 2048), ("synthesis", N, 6144, 2304),
+              ("mean_table", 32768, 2048, 2048)]
+    out = {}
+    for name, m, n, k in shapes:
+        a = torch.randn(m, k, device=dev).to(torch.bfloat16)
+        bt = torch.randn(k, n, device=dev).to(torch.bfloat16)
+        for _ in range(3):
+            c = a @ bt
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            c = a @ bt
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        out[name] = {"M": m, "N": n, "K": k, "ms": ms, "tflops": tf, "frac": tf / PEAK_BF16_TFLOPS}
+        del a, bt, c
+    print(json.dumps({"vendor_gemm": out, "blas": str(torch.backends.cuda.preferred_blas_library())}))
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,7 +189,13 @@ def main(argv=None) -> int:
                     help="end with a plain device copy of this many MiB (scale for the traffic counters)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 counter runs, then exit")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time the vendor library's plain GEMMs on the same shapes, then exit")
     args = ap.parse_args(argv)
+    if args.vendor_gemm:
+        import dckv_synth as synth
+        T = synth.CONFIGS[args.config]["T"]
+        return vendor_gemm(T - 132, args.steps)
     if args.write_traffic:
         import dckv_synth as synth
         return write_traffic(args.write_traffic[0], args.write_traffic[1], args.copy_calibration_mib or 1024,
