@@ -308,16 +308,21 @@ __device__ __forceinline__ int acc_row(int mb, int v, int lane) { return mb * 32
 // out[row][col_hi + c - 64].
 
 // Rows r and r + 1 of this lane's column tcol (y0, y1) into the wave's LDS
-// tile as 32-bit pairs of adjacent columns: lanes l and l ^ 1 hold columns
-// tcol and tcol ^ 1 of the same rows and swap one value (a DPP quad
-// permute); the even lane then writes row r, the odd lane row r + 1.
-__device__ __forceinline__ void put_rows2(char *wtile, int r, int tcol, float y0, float y1, int lane) {
-  const bool odd = lane & 1;
-  const float send = odd ? y0 : y1;
-  const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
-  const float a = odd ? recv : y0, b = odd ? y1 : recv;
-  *reinterpret_cast<uint32_t *>(wtile + ((r + (odd ? 1 : 0)) * kOutStride + (tcol & ~1)) * 2) = pack_bf16x2(a, b);
+// tile: one conversion packs both, then the low half goes to row r and the
+// high half to row r + 1 (two 16-bit LDS stores; the two half-waves, rows 4
+// apart, write disjoint bank ranges).
+// wbase is the lane's origin in the tile (row 4 (lane / 32), column lane % 32),
+// crow and ccol compile-time offsets, so both stores use immediate offsets.
+__device__ __forceinline__ char *wtile_base(char *wtile, int lane) {
+  return wtile + ((4 * (lane >> 5)) * kOutStride + (lane & 31)) * 2;
 }
+__device__ __forceinline__ void put_rows2(char *wbase, int crow, int ccol, float y0, float y1) {
+  const uint32_t pk = pack_bf16x2(y0, y1);
+  *reinterpret_cast<uint16_t *>(wbase + (crow * kOutStride + ccol) * 2) = (uint16_t)pk;
+  *reinterpret_cast<uint16_t *>(wbase + ((crow + 1) * kOutStride + ccol) * 2) = (uint16_t)(pk >> 16);
+}
+// the constant part of acc_row(): row of register v of block mb without the lane term
+__device__ __forceinline__ constexpr int acc_crow(int mb, int v) { return mb * 32 + 8 * (v >> 2) + (v & 3); }
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -506,7 +511,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
     const float qf = fminf(fmaxf(rintf(div_step(d, st, inv)), -kQLimit), kQLimit);
     qi = (int)qf;
     const uint32_t s = (uint32_t)(qi + 127);
-    const uint32_t out = s > 254u ? 1u : 0u;       // 1: beyond +-127 (s wraps for q < -127)
+    const uint32_t out = (uint32_t)(127 - max(qi, -qi)) >> 31;  // 1: beyond +-127 (|q| < 2^31 after the clamp)
     const uint32_t om = 0u - out, vm = valid - 1u;  // all ones when escaped / not valid
     esc = out & valid;
     yhat = (m + qf * st) * (float)valid;
@@ -858,15 +863,14 @@ __global__ __launch_bounds__(kDeqThreads) void k_dequant(DeqP P) {
 // (identity columns), one accumulator block at a time
 template <class F>
 __device__ __forceinline__ void acc_to_wtile(const f32x16 (&acc)[4][4], char *wtile, int, F &&fn) {
-  const int lane = epilogue_lane();
+  char *wbase = wtile_base(wtile, epilogue_lane());
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const f32x16 b = acc_block(acc, mb, nb);
 #pragma unroll
-      for (int v = 0; v < 16; v += 2)
-        put_rows2(wtile, acc_row(mb, v, lane), nb * 32 + (lane & 31), fn(b[v]), fn(b[v + 1]), lane);
+      for (int v = 0; v < 16; v += 2) put_rows2(wbase, acc_crow(mb, v), nb * 32, fn(b[v]), fn(b[v + 1]));
       __builtin_amdgcn_sched_barrier(0);  // one block at a time: bounded live ranges
     }
 }
@@ -1011,9 +1015,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
       s = s * r.x + c * r.y;
       c = c2;
     };
+    char *wbase = wtile_base(wtile, lane);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const int tc0 = nb * 32 + (lane & 31), tc1 = (nb + 2) * 32 + (lane & 31);
       float c_mb = tb[nb].x * ta[nb].x - tb[nb].y * ta[nb].y;
       float s_mb = tb[nb].y * ta[nb].x + tb[nb].x * ta[nb].y;
 #pragma unroll
@@ -1031,11 +1035,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
             o1[i] = bhi[v] * cs + blo[v] * sn;
             if (i < 3) rot(cs, sn, r1[nb]);
           }
-          const int row = acc_row(mb, 4 * g, lane);
-          put_rows2(wtile, row, tc0, o0[0], o0[1], lane);
-          put_rows2(wtile, row + 2, tc0, o0[2], o0[3], lane);
-          put_rows2(wtile, row, tc1, o1[0], o1[1], lane);
-          put_rows2(wtile, row + 2, tc1, o1[2], o1[3], lane);
+          const int crow = acc_crow(mb, 4 * g);
+          put_rows2(wbase, crow, nb * 32, o0[0], o0[1]);
+          put_rows2(wbase, crow + 2, nb * 32, o0[2], o0[3]);
+          put_rows2(wbase, crow, (nb + 2) * 32, o1[0], o1[1]);
+          put_rows2(wbase, crow + 2, (nb + 2) * 32, o1[2], o1[3]);
           if (g < 3) rot(c_g, s_g, r8[nb]);
         }
         if (mb < 3) rot(c_mb, s_mb, r32[nb]);
