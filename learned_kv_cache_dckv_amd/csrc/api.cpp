@@ -60,11 +60,9 @@ int encode_checks(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *
 }
 
 void encode_sequence(const EncodeArgs &a) {
-  launch_init(a);
-  launch_kept_copy(a);
+  launch_start_encode(a);
   launch_analysis_gemm(a);
   launch_encode_fixup(a);
-  launch_esc_sort(a);
   launch_rans_encode(a);
   launch_scan_header(a);
   launch_pack(a);
@@ -83,14 +81,11 @@ int decode_checks(const dckv_plan_t *plan, const uint8_t *stream, uint64_t strea
 }
 
 void decode_sequence(const DecodeArgs &a) {
-  launch_init(a);
-  launch_parse(a);
-  launch_rope_tables(a);
+  launch_parse(a, true);
   launch_rans_decode(a);
   launch_dequant(a);
-  launch_w1_gemm(a);
+  launch_w1_gemm(a);  // also RoPE on the kept rows
   launch_synthesis_gemm(a);
-  launch_kept_rope(a);
 }
 
 int batch_error(int rc, int32_t i, const char *what) {
@@ -201,8 +196,7 @@ extern "C" int dckv_entropy_encode(const dckv_plan_t *plan, int64_t T, const uin
   if (capacity < g.fixed_bytes) return set_error(DCKV_ECAPACITY, "capacity below the stream's fixed part");
   EncodeArgs a{plan, g, l, static_cast<uint8_t *>(workspace), rows, nullptr, stream, capacity,
                stream_bytes, status, static_cast<hipStream_t>(hip_stream)};
-  launch_init(a);
-  launch_kept_copy(a);
+  launch_start_encode(a);
   launch_sym_to_tiled(a, sym);
   launch_load_esc(a, esc, n_esc);
   launch_rans_encode(a);
@@ -223,8 +217,7 @@ extern "C" int dckv_entropy_decode(const dckv_plan_t *plan, const uint8_t *strea
   if (stream_bytes < g.fixed_bytes) return set_error(DCKV_ECORRUPT, "stream shorter than its fixed part");
   DecodeArgs a{plan, g, l, static_cast<uint8_t *>(workspace), stream, stream_bytes, nullptr, nullptr, status,
                static_cast<hipStream_t>(hip_stream)};
-  launch_init(a);
-  launch_parse(a);
+  launch_parse(a, false);
   launch_rans_decode(a);
   launch_sym_from_tiled(a, sym_out, n_esc_out);
   return after_launch("dckv_entropy_decode");

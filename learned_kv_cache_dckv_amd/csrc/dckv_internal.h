@@ -148,17 +148,13 @@ struct DecodeArgs {
 };
 
 // misc.hip
-void launch_init(const EncodeArgs &a);
-void launch_init(const DecodeArgs &a);
-void launch_kept_copy(const EncodeArgs &a);
-void launch_esc_sort(const EncodeArgs &a);
-void launch_finish_status(uint8_t *ws, int32_t *status, uint64_t *stream_bytes, hipStream_t s);
+void launch_start_encode(const EncodeArgs &a);  // control words, status, kept rows
 
 // rans.hip
 void launch_rans_encode(const EncodeArgs &a);
 void launch_scan_header(const EncodeArgs &a);
 void launch_pack(const EncodeArgs &a);
-void launch_parse(const DecodeArgs &a);
+void launch_parse(const DecodeArgs &a, bool with_rope);  // control words, status, parse, RoPE tables
 void launch_rans_decode(const DecodeArgs &a);
 void launch_load_esc(const EncodeArgs &a, const uint32_t *esc, uint32_t n_esc);
 void launch_sym_to_tiled(const EncodeArgs &a, const uint8_t *sym);
@@ -168,10 +164,9 @@ void launch_sym_from_tiled(const DecodeArgs &a, uint8_t *sym_out, uint32_t *n_es
 int build_mean_table(dckv_plan_t *p);  // at plan time: fills p->mtab, synchronous
 void launch_analysis_gemm(const EncodeArgs &a);
 void launch_encode_fixup(const EncodeArgs &a);
-void launch_rope_tables(const DecodeArgs &a);
 void launch_dequant(const DecodeArgs &a);
 void launch_w1_gemm(const DecodeArgs &a);
 void launch_synthesis_gemm(const DecodeArgs &a);
-void launch_kept_rope(const DecodeArgs &a);
+
 
 }  // namespace dckv

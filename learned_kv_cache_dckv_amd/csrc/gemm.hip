@@ -879,6 +879,30 @@ struct Identity {
   __device__ float operator()(float x) const { return x; }
 };
 
+// kept row k: RoPE on the key columns of the verbatim row in the stream
+__device__ __forceinline__ void kept_rope_row(int64_t k, const uint8_t *stream, const float2 *lo, const float2 *hi,
+                                              uint16_t *out, int64_t head_n, int64_t tail_pos0) {
+  const int64_t pos = k < head_n ? k : tail_pos0 + (k - head_n);
+  const uint16_t *src = reinterpret_cast<const uint16_t *>(stream + kHeaderBytes) + (size_t)k * kD;
+  uint16_t *dst = out + (size_t)pos * kD;
+  for (int i = threadIdx.x; i < kD / 2; i += blockDim.x) {
+    // i enumerates (head, d) with d < 128: the pair (d, d + 128) of every head
+    const int head = i / kHalf, d = i % kHalf;
+    const int base = head * kHeadDim;
+    const float x0 = bf2f(src[base + d]), x1 = bf2f(src[base + d + kHalf]);
+    if ((head & 3) < 2) {
+      const float2 a = lo[(size_t)(pos & 255) * kHalf + d], b = hi[(size_t)(pos >> 8) * kHalf + d];
+      const float cs = b.x * a.x - b.y * a.y;
+      const float sn = b.y * a.x + b.x * a.y;
+      dst[base + d] = f2bf(x0 * cs - x1 * sn);
+      dst[base + d + kHalf] = f2bf(x1 * cs + x0 * sn);
+    } else {
+      dst[base + d] = src[base + d];
+      dst[base + d + kHalf] = src[base + d + kHalf];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // decode: correction hidden layer h = GELU(W1 yhat_b)
 // ---------------------------------------------------------------------------
@@ -889,6 +913,12 @@ struct W1P {
   int64_t N, NM;
   int n_mt;
   int32_t *status;
+  // kept rows, RoPE'd by the GELU kernel's last n_kept workgroups
+  const uint8_t *stream;
+  const float2 *rope_lo, *rope_hi;
+  uint16_t *out;
+  int64_t n_kept, head_n, tail_pos0;
+  unsigned gelu_blocks;
 };
 
 // W1 yhat_b as two half-K products (coefficients [0, 1024) and [1024, 2048)):
@@ -929,9 +959,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_w1(W1P P) {
     }
 }
 
-// h_b = bf16(GELU(part0 + part1)), exact-erf GELU; 4 hidden units per thread
+// h_b = bf16(GELU(part0 + part1)), exact-erf GELU; 4 hidden units per thread.
+// Workgroups past the GELU ones apply RoPE to one kept row each (the RoPE
+// tables are written by the parse kernel, which runs first).
 __global__ __launch_bounds__(256) void k_w1_gelu(W1P P) {
   if (*P.status != 0) return;
+  if (blockIdx.x >= P.gelu_blocks) {
+    kept_rope_row(blockIdx.x - P.gelu_blocks, P.stream, P.rope_lo, P.rope_hi, P.out, P.head_n, P.tail_pos0);
+    return;
+  }
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (row, 4-unit group)
   if (i >= P.N * (kHid / 4)) return;
   const size_t o = (size_t)i * 4;
@@ -1054,55 +1090,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
   flush_rows(wtile, P.out + (size_t)P.keep_head * kD, kD, wrow0, hb + 64 * wn, hb + 128 + 64 * wn, P.N);
 }
 
-// ---------------------------------------------------------------------------
-// RoPE angle tables: cos/sin of u*w_i (u < 256) and of 256*v*w_i, in float64
-// ---------------------------------------------------------------------------
-__global__ void k_rope_tables(const double *omega, float2 *lo, float2 *hi, int64_t n_hi) {
-  const int64_t n = (256 + n_hi) * kHalf;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t u = i / kHalf;
-    const int k = (int)(i - u * kHalf);
-    double ang;
-    float2 *dst;
-    if (u < 256) {
-      ang = (double)u * omega[k];
-      dst = lo + u * kHalf + k;
-    } else {
-      ang = (double)((u - 256) * 256) * omega[k];
-      dst = hi + (u - 256) * kHalf + k;
-    }
-    double s, c;
-    sincos(ang, &s, &c);
-    *dst = make_float2((float)c, (float)s);
-  }
-}
-
-// kept rows: RoPE on key columns of the verbatim rows in the stream
-__global__ void k_kept_rope(const uint8_t *stream, const float2 *lo, const float2 *hi, uint16_t *out,
-                            int64_t n_kept, int64_t head_n, int64_t tail_pos0, const int32_t *status) {
-  if (*status != 0) return;
-  const int64_t k = blockIdx.x;
-  if (k >= n_kept) return;
-  const int64_t pos = k < head_n ? k : tail_pos0 + (k - head_n);
-  const uint16_t *src = reinterpret_cast<const uint16_t *>(stream + kHeaderBytes) + (size_t)k * kD;
-  uint16_t *dst = out + (size_t)pos * kD;
-  for (int i = threadIdx.x; i < kD / 2; i += blockDim.x) {
-    // i enumerates (head, d) with d < 128: the pair (d, d + 128) of every head
-    const int head = i / kHalf, d = i % kHalf;
-    const int base = head * kHeadDim;
-    const float x0 = bf2f(src[base + d]), x1 = bf2f(src[base + d + kHalf]);
-    if ((head & 3) < 2) {
-      const float2 a = lo[(size_t)(pos & 255) * kHalf + d], b = hi[(size_t)(pos >> 8) * kHalf + d];
-      const float cs = b.x * a.x - b.y * a.y;
-      const float sn = b.y * a.x + b.x * a.y;
-      dst[base + d] = f2bf(x0 * cs - x1 * sn);
-      dst[base + d + kHalf] = f2bf(x1 * cs + x0 * sn);
-    } else {
-      dst[base + d] = src[base + d];
-      dst[base + d + kHalf] = src[base + d + kHalf];
-    }
-  }
-}
 
 }  // namespace
 
@@ -1181,13 +1168,6 @@ void launch_encode_fixup(const EncodeArgs &a) {
   hipLaunchKernelGGL(k_encode_fixup, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, a.s, P, n_fix);
 }
 
-void launch_rope_tables(const DecodeArgs &a) {
-  const int64_t n = (256 + a.g.rope_hi) * kHalf;
-  hipLaunchKernelGGL(k_rope_tables, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0, a.s,
-                     a.p->dev.omega, reinterpret_cast<float2 *>(a.ws + a.l.rope_lo),
-                     reinterpret_cast<float2 *>(a.ws + a.l.rope_hi), a.g.rope_hi);
-}
-
 void launch_dequant(const DecodeArgs &a) {
   if (a.g.N == 0) return;
   DeqP P;
@@ -1217,7 +1197,7 @@ void launch_dequant(const DecodeArgs &a) {
 }
 
 void launch_w1_gemm(const DecodeArgs &a) {
-  if (a.g.N == 0) return;
+  if (a.g.N == 0 && a.g.n_kept == 0) return;
   W1P P;
   P.yhat_b = reinterpret_cast<const uint16_t *>(a.ws + a.l.yhat_b);
   P.W1 = a.p->W1;
@@ -1227,10 +1207,17 @@ void launch_w1_gemm(const DecodeArgs &a) {
   P.NM = a.g.NM;
   P.n_mt = (int)a.g.n_mtiles;
   P.status = a.status;
-  launch_gemm(k_w1, "w1_gemm", P.n_mt * 2, P, a.s);
-  const int64_t work = a.g.N * (kHid / 4);
+  P.stream = a.stream;
+  P.rope_lo = reinterpret_cast<const float2 *>(a.ws + a.l.rope_lo);
+  P.rope_hi = reinterpret_cast<const float2 *>(a.ws + a.l.rope_hi);
+  P.out = a.rows_out;
+  P.n_kept = a.g.n_kept;
+  P.head_n = std::min<int64_t>(a.p->keep_head, a.g.T);
+  P.tail_pos0 = a.p->keep_head + a.g.N;
+  P.gelu_blocks = (unsigned)((a.g.N * (kHid / 4) + 255) / 256);
+  if (a.g.N) launch_gemm(k_w1, "w1_gemm", P.n_mt * 2, P, a.s);
   KernelTimer tm("w1_gelu", a.s);
-  hipLaunchKernelGGL(k_w1_gelu, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, a.s, P);
+  hipLaunchKernelGGL(k_w1_gelu, dim3(P.gelu_blocks + (unsigned)a.g.n_kept), dim3(256), 0, a.s, P);
 }
 
 void launch_synthesis_gemm(const DecodeArgs &a) {
@@ -1249,16 +1236,6 @@ void launch_synthesis_gemm(const DecodeArgs &a) {
   P.n_nt = kD / kBN;
   P.status = a.status;
   launch_gemm(k_synthesis, "synthesis_gemm", P.n_mt * P.n_nt, P, a.s);
-}
-
-void launch_kept_rope(const DecodeArgs &a) {
-  if (a.g.n_kept == 0) return;
-  const int64_t head_n = std::min<int64_t>(a.p->keep_head, a.g.T);
-  const int64_t tail_pos0 = a.p->keep_head + a.g.N;
-  hipLaunchKernelGGL(k_kept_rope, dim3((unsigned)a.g.n_kept), dim3(256), 0, a.s, a.stream,
-                     reinterpret_cast<const float2 *>(a.ws + a.l.rope_lo),
-                     reinterpret_cast<const float2 *>(a.ws + a.l.rope_hi), a.rows_out, a.g.n_kept, head_n,
-                     tail_pos0, a.status);
 }
 
 }  // namespace dckv

@@ -171,7 +171,68 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(EncP P) {
 // ---------------------------------------------------------------------------
 // group-size scan, group offsets, header, final size
 // ---------------------------------------------------------------------------
+// Escapes (codes beyond +-127, 64 bits each) are found out of order by the
+// quantiser tiles; the stream stores them by ascending flat index
+// j * C_a + rank, so the scan's workgroup first sorts the (usually few)
+// records with a bitonic network, in LDS up to kSortLds records, else in
+// place in global memory.
+constexpr int kSortLds = 4096;
+
+__device__ __forceinline__ void bitonic(unsigned long long *a, uint32_t n_pow2) {
+  for (uint32_t k = 2; k <= n_pow2; k <<= 1) {
+    for (uint32_t j = k >> 1; j > 0; j >>= 1) {
+      for (uint32_t i = threadIdx.x; i < n_pow2; i += blockDim.x) {
+        const uint32_t l = i ^ j;
+        if (l > i) {
+          const unsigned long long x = a[i], y = a[l];
+          const bool up = (i & k) == 0;
+          if ((x > y) == up) {
+            a[i] = y;
+            a[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// esc_raw holds {flat, q} pairs in arrival order; esc_sorted receives them by
+// ascending flat.  esc_raw has room for the padded power-of-two count.  All
+// threads of the workgroup call this.
+__device__ __forceinline__ void sort_escapes(const uint8_t *ws, uint32_t *esc_raw, uint32_t *esc_sorted,
+                                             int64_t esc_cap, unsigned long long *keys) {
+  const Ctrl *ct = reinterpret_cast<const Ctrl *>(ws);
+  const uint32_t n = (uint32_t)min<int64_t>(ct->n_esc, esc_cap);
+  if (n == 0) return;
+  uint32_t p2 = 1;
+  while (p2 < n) p2 <<= 1;
+  unsigned long long *a;
+  unsigned long long *g = reinterpret_cast<unsigned long long *>(esc_raw);
+  if (p2 <= (uint32_t)kSortLds) {
+    a = keys;
+    for (uint32_t i = threadIdx.x; i < p2; i += blockDim.x)
+      a[i] = i < n ? (((unsigned long long)esc_raw[2 * i]) << 32) | esc_raw[2 * i + 1] : ~0ull;
+  } else {
+    // in place in global memory: keys overwrite the pairs they were made from
+    a = g;
+    for (uint32_t i = threadIdx.x; i < p2; i += blockDim.x) {
+      unsigned long long v = ~0ull;
+      if (i < n) v = (((unsigned long long)esc_raw[2 * i]) << 32) | esc_raw[2 * i + 1];
+      a[i] = v;  // element i occupies exactly the bytes of pair i
+    }
+  }
+  __syncthreads();
+  bitonic(a, p2);
+  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const unsigned long long v = a[i];
+    esc_sorted[2 * i] = (uint32_t)(v >> 32);
+    esc_sorted[2 * i + 1] = (uint32_t)v;
+  }
+}
+
 struct ScanP {
+  uint32_t *esc_raw, *esc_sorted;
   const uint32_t *gwords;
   uint64_t *goffs;        // word offsets [n_groups + 1]
   uint8_t *ws;
@@ -187,7 +248,10 @@ struct ScanP {
 
 __global__ __launch_bounds__(1024) void k_scan_header(ScanP P) {
   __shared__ uint64_t part[1024];
+  __shared__ unsigned long long keys[kSortLds];
   const int t = threadIdx.x;
+  if (*P.status == 0) sort_escapes(P.ws, P.esc_raw, P.esc_sorted, P.esc_cap, keys);
+  __syncthreads();
   const int64_t ng = P.n_groups;
   const int64_t per = (ng + 1023) / 1024;
   const int64_t lo = min<int64_t>(ng, t * per), hi = min<int64_t>(ng, lo + per);
@@ -294,6 +358,12 @@ struct ParseP {
   uint64_t size;
   uint8_t *ws;
   int32_t *status;
+  // RoPE angle tables, built by the workgroups after the first (none when
+  // n_rope is 0): lo[u][i] = (cos, sin)(u w_i), u < 256; hi[v][i] = the same
+  // of 256 v w_i; in float64, rounded once
+  const double *omega;
+  float2 *rope_lo, *rope_hi;
+  int64_t rope_hi_n;
   uint32_t T, keep_head, keep_tail, N, n_coef, Ca, crc, n_groups;
   uint64_t kept_bytes;
   uint32_t *esc_rows;     // [row tiles][2]: index range of the escapes of a 256-row tile
@@ -306,6 +376,36 @@ __global__ __launch_bounds__(256) void k_parse(ParseP P) {
   __shared__ uint64_t s_esc_off, s_rans_off, s_rans_bytes;
   __shared__ uint32_t s_n_esc;
   const int t = threadIdx.x;
+  if (blockIdx.x > 0) {
+    const int64_t n = (256 + P.rope_hi_n) * kHalf;
+    for (int64_t i = (int64_t)(blockIdx.x - 1) * blockDim.x + t; i < n; i += (int64_t)(gridDim.x - 1) * blockDim.x) {
+      const int64_t u = i / kHalf;
+      const int k = (int)(i - u * kHalf);
+      double ang;
+      float2 *dst;
+      if (u < 256) {
+        ang = (double)u * P.omega[k];
+        dst = P.rope_lo + u * kHalf + k;
+      } else {
+        ang = (double)((u - 256) * 256) * P.omega[k];
+        dst = P.rope_hi + (u - 256) * kHalf + k;
+      }
+      double sn, cs;
+      sincos(ang, &sn, &cs);
+      *dst = make_float2((float)cs, (float)sn);
+    }
+    return;
+  }
+  if (t == 0) {  // the call's control words and status start clear
+    Ctrl *ct = ctrl_of(P.ws);
+    ct->n_esc = 0;
+    ct->status = 0;
+    ct->total_bytes = 0;
+    ct->rans_bytes = 0;
+    ct->esc_off = ct->rans_off = ct->offs_off = 0;
+    *P.status = 0;
+  }
+  __syncthreads();
   for (uint32_t i = t; i < 2 * P.n_row_tiles; i += blockDim.x) P.esc_rows[i] = 0u;  // no records
   if (t == 0) {
     bad = 0;
@@ -565,10 +665,12 @@ __global__ void k_sym_from_tiled(const uint32_t *sym32, uint8_t *sym, int64_t N,
   }
 }
 
-__global__ void k_load_esc(const uint32_t *esc, uint32_t n_esc, uint32_t *esc_sorted, uint8_t *ws) {
+// the caller's records into the raw list (the scan's sort leaves their
+// ascending order as it is)
+__global__ void k_load_esc(const uint32_t *esc, uint32_t n_esc, uint32_t *esc_raw, uint8_t *ws) {
   if (blockIdx.x == 0 && threadIdx.x == 0) ctrl_of(ws)->n_esc = n_esc;
   for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < 2 * n_esc; i += gridDim.x * blockDim.x)
-    esc_sorted[i] = esc[i];
+    esc_raw[i] = esc[i];
 }
 
 __global__ void k_copy_n_esc(const uint8_t *ws, uint32_t *n_esc_out, const int32_t *status) {
@@ -605,6 +707,8 @@ void launch_rans_encode(const EncodeArgs &a) {
 
 void launch_scan_header(const EncodeArgs &a) {
   ScanP P;
+  P.esc_raw = reinterpret_cast<uint32_t *>(a.ws + a.l.esc_raw);
+  P.esc_sorted = reinterpret_cast<uint32_t *>(a.ws + a.l.esc_sorted);
   P.gwords = reinterpret_cast<const uint32_t *>(a.ws + a.l.gwords);
   P.goffs = reinterpret_cast<uint64_t *>(a.ws + a.l.goffs);
   P.ws = a.ws;
@@ -642,7 +746,7 @@ void launch_pack(const EncodeArgs &a) {
   hipLaunchKernelGGL(k_pack, dim3(grid), dim3(256), 0, a.s, P);
 }
 
-void launch_parse(const DecodeArgs &a) {
+void launch_parse(const DecodeArgs &a, bool with_rope) {
   ParseP P;
   P.stream = a.stream;
   P.size = a.stream_size;
@@ -659,8 +763,14 @@ void launch_parse(const DecodeArgs &a) {
   P.kept_bytes = (uint64_t)a.g.n_kept * a.p->D * 2;
   P.esc_rows = reinterpret_cast<uint32_t *>(a.ws + a.l.esc_rows);
   P.n_row_tiles = (uint32_t)a.g.n_mtiles;
+  P.omega = a.p->dev.omega;
+  P.rope_lo = reinterpret_cast<float2 *>(a.ws + a.l.rope_lo);
+  P.rope_hi = reinterpret_cast<float2 *>(a.ws + a.l.rope_hi);
+  P.rope_hi_n = a.g.rope_hi;
+  const int64_t n_rope = with_rope ? (256 + a.g.rope_hi) * kHalf : 0;
+  const unsigned rope_blocks = (unsigned)std::min<int64_t>((n_rope + 255) / 256, 4096);
   KernelTimer tm("parse", a.s);
-  hipLaunchKernelGGL(k_parse, dim3(1), dim3(256), 0, a.s, P);
+  hipLaunchKernelGGL(k_parse, dim3(1 + rope_blocks), dim3(256), 0, a.s, P);
 }
 
 void launch_rans_decode(const DecodeArgs &a) {
@@ -701,7 +811,7 @@ void launch_sym_from_tiled(const DecodeArgs &a, uint8_t *sym_out, uint32_t *n_es
 
 void launch_load_esc(const EncodeArgs &a, const uint32_t *esc, uint32_t n_esc) {
   hipLaunchKernelGGL(k_load_esc, dim3(grid_for(2 * (int64_t)n_esc)), dim3(256), 0, a.s, esc, n_esc,
-                     reinterpret_cast<uint32_t *>(a.ws + a.l.esc_sorted), a.ws);
+                     reinterpret_cast<uint32_t *>(a.ws + a.l.esc_raw), a.ws);
 }
 
 }  // namespace dckv
