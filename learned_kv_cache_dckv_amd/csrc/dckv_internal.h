@@ -46,6 +46,7 @@ struct PlanDev {
   int32_t *act = nullptr;       // [C_a] component of each rank (padded to a kBN multiple)
   int32_t *perm = nullptr;      // [C]   component of each mean-table column: ranks, then dropped
   int32_t *colpos = nullptr;    // [C]   mean-table column of each component
+  float *qcol = nullptr;        // [C_a padded][4] step, 1/step (0 past C_a), neighbour weight, 0 of each rank
   uint32_t *tab = nullptr;      // [C_a][256]  f | cum << 16
   uint8_t *bucket = nullptr;    // [C_a][kBuckets] first symbol of each slot bucket
   double *omega = nullptr;      // [head_dim/2] RoPE frequencies

@@ -74,9 +74,7 @@ constexpr int kOutStride = 128 + 8;                       // bf16 per row of a w
 constexpr int kOutWaveBytes = 128 * kOutStride * 2;
 constexpr int kXchOff = 4 * kOutWaveBytes;                // row-0 exchange between the two wave rows
 constexpr int kLdsBytes = kXchOff + 2 * 256 * 4;
-constexpr int kMeanRowFloats = 256 + 16;                  // LDS row of staged means (see mean_rows_to_lds)
 static_assert(kStages * kStageBytes <= kXchOff, "stages must not overlap the exchange area");
-static_assert(128 * kMeanRowFloats * 4 <= kXchOff, "staged means must not overlap the exchange area");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
 constexpr float kQLimit = 2147483520.0f;  // largest float below 2^31
 
@@ -89,6 +87,12 @@ __device__ __forceinline__ bool wg_stop(const int32_t *st) {
   if (threadIdx.x == 0) s_stop = *reinterpret_cast<const volatile int32_t *>(st);
   __syncthreads();
   return s_stop != 0;
+}
+
+// A load through a global (address space 1) pointer.
+template <class T>
+__device__ __forceinline__ T gload(const T *p) {
+  return *(const T __attribute__((address_space(1))) *)p;
 }
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -296,6 +300,14 @@ __device__ __forceinline__ f32x16 acc_block(const f32x16 (&acc)[4][4], int mb, i
 }
 
 
+// Register v of an accumulator block, read out of its AGPR in place (the
+// block is not copied to VGPRs as a whole).
+__device__ __forceinline__ float acc_get(const f32x16 &b, int v) {
+  float x;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(b[v]));
+  return x;
+}
+
 // Row (within the wave tile) of register v of block row mb in this lane.
 __device__ __forceinline__ int acc_row(int mb, int v, int lane) { return mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
@@ -410,39 +422,16 @@ struct QuantP {
   const uint16_t *rows, *A;
   const int32_t *act, *tok;
   const float *step, *nbr;
+  const float *qcol;  // [C_a padded][4]: step, 1 / step (0 past C_a), a, 0 of each rank
   const float *mtab;  // [vocab][kC] embedding means, columns in rank order
   uint32_t *sym32;
   uint32_t *esc_raw;  // {flat, q}
   uint8_t *ws;
   float *halo_a, *halo_b;
   int64_t N, N256, esc_cap;
-  int Ca, keep_head, C, n_mt, n_nt, vocab;
+  int Ca, keep_head, C, n_mt, n_nt, vocab, T;
   int32_t *status;
 };
-
-// The means of the tile rows of one parity p into LDS (offset 0): slot i
-// (0..127) holds tile row 2i + p, i.e. columns [n0, n0 + 256) of the table row
-// of that row's token, 1 KiB, with kMeanRowFloats floats per slot, so rows
-// two slots apart (tile rows 4 apart, read together by the two half-waves)
-// fall in opposite halves of the LDS banks.  Each wave stages 32 slots with
-// one direct 16-byte load per slot; the token of slot k is read out of lane k.
-__device__ __forceinline__ void mean_rows_to_lds(const QuantP &P, int64_t m0, int n0, int p, char *lds, int lane) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t j = min<int64_t>(m0 + 2 * (wave * 32 + (lane & 31)) + p, P.N - 1);
-  const int v = clamp_tok(P.tok, P.keep_head + j, P.vocab, P.status);
-  const float *col = P.mtab + n0 + lane * 4;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const int row = __builtin_amdgcn_readlane(v, k);
-    __builtin_amdgcn_global_load_lds((gptr_t)(col + (size_t)row * kC),
-                                     (lptr_t)(lds + (wave * 32 + k) * kMeanRowFloats * 4), 16, 0, 0);
-  }
-}
-
-// staged mean of tile row `trow` (of the parity staged), tile column `tcol`
-__device__ __forceinline__ float mean_at(const char *lds, int trow, int tcol) {
-  return reinterpret_cast<const float *>(lds)[(trow >> 1) * kMeanRowFloats + tcol];
-}
 
 // r = fp32(d / step) from the reciprocal and one fused correction
 __device__ __forceinline__ float div_step(float d, float step, float inv) {
@@ -470,6 +459,33 @@ __device__ __forceinline__ uint32_t quant_one(float d, float step, float inv, in
   return (uint32_t)kEsc;
 }
 
+// A buffer resource over [p, p + bytes) with a wave-uniform base: loads past
+// the end return 0 and stores past it are dropped.
+__device__ __forceinline__ rsrc_t span_rsrc(const void *p, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(p);
+  const uint64_t bu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b) |
+                      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(bu), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
+}
+
+// Meet the other waves once this wave's LDS accesses are done; vector memory
+// operations stay in flight (s_waitcnt: vmcnt 63, expcnt 7, lgkmcnt 0).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// four integer-valued floats in [0, 255] -> the bytes of one word
+__device__ __forceinline__ uint32_t pack_u8x4(float a, float b, float c, float d) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_u8_f32(a, 0, 0u);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(b, 1, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(c, 2, w);
+  return __builtin_amdgcn_cvt_pk_u8_f32(d, 3, w);
+}
+
 __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   if (wg_stop(P.status)) return;
@@ -486,57 +502,88 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
     A.row[i] = (uint32_t)(P.keep_head + j);
     B.row[i] = (uint32_t)P.act[n0 + staged_row(i)];
   }
-  f32x16 acc[4][4];
-  mainloop(A, B, kD / kBK, acc, lds);
-
-  // The epilogue works one 32x32 accumulator block at a time: its 8 means of
-  // one parity are read from LDS together, every value is decided without a
-  // branch, and escapes (rare) take one branch per block.  The even rows'
-  // symbols wait for pass 2 packed two quads per register.
-  const int lane = epilogue_lane(), wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int N = (int)P.N;
   const int wrow0 = (int)m0 + wm * 128;  // first row of this wave's tile
-  Ctrl *ct = reinterpret_cast<Ctrl *>(P.ws);
-  // bit 31 set once a difference is not finite: its exponent field plus one
-  // unit carries into the sign bit only when the field is all ones
-  uint32_t nonfin = 0u;
+  // Loaded before the main loop, whose duration hides their latency: the
+  // token ids of the wave's 128 rows (rows lane and 64 + lane; rows past the
+  // request read 0) and the quantiser constants of the lane's four columns.
+  uint32_t tk[2];
+  {
+    const int l0 = threadIdx.x & 63;
+    const rsrc_t tr = span_rsrc(P.tok + P.keep_head, (uint32_t)(P.T - P.keep_head) * 4u);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) tk[i] = __builtin_amdgcn_raw_buffer_load_b32(tr, (uint32_t)(wrow0 + 64 * i + l0) * 4u, 0, 0);
+  }
+  f32x4 qc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    qc[nb] = gload(reinterpret_cast<const f32x4 *>(P.qcol) + n0 + wn * 128 + nb * 32 + (threadIdx.x & 31));
+  f32x16 acc[4][4];
+  mainloop(A, B, kD / kBK, acc, lds);
 
-  // One value: d = y - mu, valid = 1 for a coded row and active rank, else 0.
-  // Returns the symbol (255 when escaped, 0xFF when not valid), sets qi, the
-  // escape bit (1 for an escaped valid value) and yhat (0 when not valid).
-  // Flags are integer arithmetic, so no lane mask stays alive.
-  auto code = [&](float d, float m, float st, float inv, uint32_t valid, int &qi, uint32_t &esc, float &yhat) {
-    nonfin |= (__float_as_uint(d) & 0x7F800000u) + 0x00800000u;
-    const float qf = fminf(fmaxf(rintf(div_step(d, st, inv)), -kQLimit), kQLimit);
-    qi = (int)qf;
-    const uint32_t s = (uint32_t)(qi + 127);
-    const uint32_t out = (uint32_t)(127 - max(qi, -qi)) >> 31;  // 1: beyond +-127 (|q| < 2^31 after the clamp)
-    const uint32_t om = 0u - out, vm = valid - 1u;  // all ones when escaped / not valid
-    esc = out & valid;
-    yhat = (m + qf * st) * (float)valid;
-    return (((s & ~om) | om) | vm) & 0xFFu;
+  // The epilogue works one 32x32 accumulator block at a time.  Each value
+  // first takes a short path that assumes a coded row, an active rank, a
+  // finite difference and no escape; a block where any of that fails (rare)
+  // is decided again in full.  The means of a block are loaded four blocks
+  // ahead, straight from the table into registers.  The even rows' symbols
+  // wait in registers for pass 2, which writes whole symbol words.
+  const int lane = epilogue_lane();
+  Ctrl *ct = reinterpret_cast<Ctrl *>(P.ws);
+  // LDS after the main loop: per wave, the token ids of its rows ordered
+  // [lane / 32][mb][parity][e] (the 8 rows of one parity of a block row and
+  // lane half, register 2e + parity, are 32 contiguous bytes), then the even
+  // rows' yhat of its 16 blocks [block][e / 4][lane] (16 bytes each)
+  int32_t *ltok = reinterpret_cast<int32_t *>(lds) + wave * 128;
+  f32x4 *lyh = reinterpret_cast<f32x4 *>(lds + 4 * 512) + wave * 16 * 2 * 64;
+  static_assert(4 * 512 + 4 * 16 * 2 * 64 * 16 <= kXchOff, "epilogue LDS must not overlap the exchange area");
+  {
+    uint32_t tmax = 0u;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int R = 64 * i + lane;  // wave row: mb = R / 32, quad row q, half h, kk
+      const int mb = R >> 5, q = (R >> 3) & 3, h = (R >> 2) & 1, kk = R & 3;
+      ltok[((h * 4 + mb) * 2 + (kk & 1)) * 8 + 2 * q + (kk >> 1)] = (int32_t)tk[i];
+      // token ids of coded rows must be in range (the table reads of any id
+      // stay inside the table's buffer range)
+      tmax = max(tmax, wrow0 + R < N ? tk[i] : 0u);
+    }
+    if (tmax >= (uint32_t)P.vocab) set_status(P.status, DCKV_EINVAL);
+  }
+  const rsrc_t mr = span_rsrc(P.mtab, (uint32_t)P.vocab * (uint32_t)(kC * 4));
+  const uint32_t colb = (uint32_t)(n0 + wn * 128 + (lane & 31)) * 4u;
+  // block row br = 4 parity + mb (0..7); its tokens are read from LDS one
+  // block row before its means are requested, which is one block row before
+  // they are used
+  int tq[2][8];
+  auto read_tok = [&](int br) {
+    const int4 *src = reinterpret_cast<const int4 *>(ltok + (((lane >> 5) * 4 + (br & 3)) * 2 + (br >> 2)) * 8);
+    const int4 t0 = src[0], t1 = src[1];
+    int *d = tq[br & 1];
+    d[0] = t0.x; d[1] = t0.y; d[2] = t0.z; d[3] = t0.w;
+    d[4] = t1.x; d[5] = t1.y; d[6] = t1.z; d[7] = t1.w;
   };
-  // valid for the row of register v of block mb (of an active rank)
-  auto valid_v = [&](int ln, int mb, int v, uint32_t rvalid) {
-    return rvalid & ((uint32_t)(wrow0 + 4 * (ln >> 5) - N + mb * 32 + 8 * (v >> 2) + (v & 3)) >> 31);
+  constexpr int kAhead = 4;
+  float mq[kAhead][8];
+  // means of block k of the 32 in epilogue order (block row k / 4, nb = k % 4)
+  auto issue = [&](int k) {
+    const int nb = k & 3;
+    const int *t = tq[(k >> 2) & 1];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      mq[k % kAhead][e] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(mr, ((uint32_t)t[e] << 13) + colb + nb * 128, 0, 0));
   };
-  // the staged mean of register v of block (mb, nb): a per-lane base plus a
-  // constant offset (tile row = wm 128 + 4 (lane / 32) + constant, all even
-  // but the constant's low bit)
-  auto mean = [&](int ln, int mb, int nb, int v) {
-    const float *mbase =
-        reinterpret_cast<const float *>(lds) + (wm * 64 + 2 * (ln >> 5)) * kMeanRowFloats + wn * 128 + (ln & 31);
-    return mbase[(mb * 16 + 4 * (v >> 2) + ((v & 3) >> 1)) * kMeanRowFloats + nb * 32];
-  };
-  // symbol words: quad (wrow0 / 4 + lane / 32 + 8 mb + 2 g) of rank r
-  auto sym_at = [&](int ln, int mb, int nb, int g) {
-    return P.sym32 + ((size_t)(wrow0 >> 2) + (ln >> 5)) * 64 +
-           (size_t)(((n0 + wn * 128) >> 6) + (nb >> 1)) * (size_t)(P.N256 / 4) * 64 + (ln & 31) + (nb & 1) * 32 +
-           (mb * 8 + 2 * g) * 64;
-  };
-  // escape records of the values of one parity of a block (bit e: register 2e + par)
+  static_assert(kC * 4 == 1 << 13, "table row bytes");
+  read_tok(0);
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) issue(k);
+  read_tok(1);
+
+  uint32_t nonfin = 0u;  // 1 once a coded value's difference is not finite
   const uint32_t esc_cap = (uint32_t)min<int64_t>(P.esc_cap, 0x7FFFFFFF);
+  // escape records of the values of one parity of a block (bit e: register 2e + par)
   auto escapes = [&](uint32_t em, const int (&qi)[8], int par, int mb, int r) {
     const int ln = epilogue_lane();
     uint32_t idx = atomicAdd(&ct->n_esc, (uint32_t)__builtin_popcount(em));
@@ -553,140 +600,156 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
     }
   };
 
-  // pass 1: even rows, mu = H E[tok], from the even rows' means staged in LDS
-  mean_rows_to_lds(P, m0, n0, 0, lds, lane);
-  __syncthreads();  // (waits for this wave's loads, then for every wave's)
-  // the lane's column of each block column nb: rank, step, 1 / step, a
-  int r_nb[4];
-  float st_nb[4], inv_nb[4], a_nb[4];
-  uint32_t rv_nb[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    r_nb[nb] = n0 + wn * 128 + nb * 32 + (lane & 31);
-    const int c = P.act[r_nb[nb]];
-    st_nb[nb] = P.step[c];
-    inv_nb[nb] = 1.0f / st_nb[nb];
-    a_nb[nb] = P.nbr[c];
-    rv_nb[nb] = (uint32_t)(r_nb[nb] - P.Ca) >> 31;
-  }
+  // pass 1: even rows, mu = H E[tok]; yhat to LDS, symbols kept for pass 2
+  uint32_t ev[4][4][2];  // [mb][nb][g / 2]: byte 2 (g % 2) + i = symbol of row 4g + 2i
+  float *xch = reinterpret_cast<float *>(lds + kXchOff);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
+    const bool edge = wrow0 + mb * 32 + 32 > N;  // rows past N in this block row
+    read_tok(mb + 2);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const int r = r_nb[nb];
-      const float st = st_nb[nb], inv = inv_nb[nb];
-      const uint32_t rvalid = rv_nb[nb];
-      const int ln = lane;
-      f32x16 b = acc_block(acc, mb, nb);
-      float m[8];
+      const int k = mb * 4 + nb;
+      const float st = qc[nb].x, inv = qc[nb].y;
+      float x[8], m[8], f[8], yh[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m[e] = mean(ln, mb, nb, 2 * e);
-      int qi[8];
-      uint32_t em = 0, w = 0;
+      for (int e = 0; e < 8; ++e) m[e] = mq[k % kAhead][e];
+      if (k + kAhead < 32) issue(k + kAhead);  // into the slot just read
+      float dsum = 0.f, amax = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int v = 2 * e;
-        uint32_t esc;
-        float yh;
-        const uint32_t sy = code(b[v] - m[e], m[e], st, inv, valid_v(ln, mb, v, rvalid), qi[e], esc, yh);
-        b[v] = yh;  // a missing right neighbour counts as zero
-        em |= esc << e;
-        // the quad's word with its even rows (bytes 0 and 2); pass 2 adds the odd ones
-        w |= sy << (16 * (e & 1));
-        if (e & 1) {
-          if (valid_v(ln, mb, v - 2, rvalid)) *sym_at(ln, mb, nb, e >> 1) = w | 0xFF00FF00u;
-          w = 0;
-        }
+        x[e] = acc_get(acc[mb][nb], 2 * e);
+        const float d = x[e] - m[e];
+        dsum += d;
+        const float qf = rintf(div_step(d, st, inv));
+        amax = fmaxf(amax, fabsf(qf));
+        yh[e] = m[e] + qf * st;
+        f[e] = qf + 127.f;
       }
-      if (em) escapes(em, qi, 0, mb, r);
-      acc[mb][nb] = b;
-      asm volatile("" : "+a"(acc[mb][nb]));  // back to the accumulator registers
-      asm volatile("" : "+v"(nonfin));       // this block's values are folded in here
+      if (edge || !(amax < 127.5f) || !isfinite(dsum)) {
+        const int r = n0 + wn * 128 + nb * 32 + (lane & 31);
+        int qi[8];
+        uint32_t em = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool valid = r < P.Ca && wrow0 + acc_row(mb, 2 * e, lane) < N;
+          const float d = x[e] - m[e];
+          if (valid && !isfinite(d)) nonfin = 1u;
+          const float qf = fminf(fmaxf(rintf(div_step(d, st, inv)), -kQLimit), kQLimit);
+          qi[e] = (int)qf;
+          const bool esc = valid && (qi[e] > 127 || qi[e] < -127);
+          em |= (uint32_t)esc << e;
+          f[e] = valid && !esc ? qf + 127.f : 255.f;
+          yh[e] = valid ? m[e] + qf * st : 0.f;  // a missing right neighbour counts as zero
+        }
+        if (em) escapes(em, qi, 0, mb, r);
+      }
+      ev[mb][nb][0] = pack_u8x4(f[0], f[1], f[2], f[3]);
+      ev[mb][nb][1] = pack_u8x4(f[4], f[5], f[6], f[7]);
+      lyh[(k * 2) * 64 + lane] = f32x4{yh[0], yh[1], yh[2], yh[3]};
+      lyh[(k * 2 + 1) * 64 + lane] = f32x4{yh[4], yh[5], yh[6], yh[7]};
+      if (mb == 0 && lane < 32) {
+        // the first row of each wave row: to the wave above (LDS) and, for
+        // the tile's row 0, to the fix-up of the previous tile (global)
+        const int r = n0 + wn * 128 + nb * 32 + lane;
+        xch[wm * 256 + wn * 128 + nb * 32 + lane] = yh[0];
+        if (wm == 0 && r < P.Ca) P.halo_b[(int64_t)mt * P.C + r] = yh[0];
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // the first row of each wave row: to the wave above (LDS) and, for the
-  // tile's row 0, to the fix-up of the previous tile (global)
-  float *xch = reinterpret_cast<float *>(lds + kXchOff);
-  if (lane < 32) {
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int r = n0 + wn * 128 + nb * 32 + lane;
-      xch[wm * 256 + wn * 128 + nb * 32 + lane] = acc[0][nb][0];
-      if (wm == 0 && r < P.Ca) P.halo_b[(int64_t)mt * P.C + r] = acc[0][nb][0];
-    }
-  }
-  __syncthreads();
+  lds_barrier();
   const bool defer_last = m0 + kBM < P.N;
-  // pass 2: odd rows, mu = H E[tok] + a (yhat_{j-1} + yhat_{j+1}), from the
-  // odd rows' means (the barrier above also ended every wave's pass 1 reads)
-  mean_rows_to_lds(P, m0, n0, 1, lds, lane);
-  __syncthreads();
+  // symbol words: one buffer per 64-rank group, holding the quads of rows < N
+  // only (a group past C_a holds none)
+  rsrc_t symr[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int grp = ((n0 + wn * 128) >> 6) + i;
+    symr[i] = span_rsrc(P.sym32 + (size_t)grp * (size_t)(P.N256 / 4) * 64,
+                        grp * 64 < P.Ca ? (uint32_t)((N + 3) >> 2) * 256u : 0u);
+  }
+  const uint32_t sbase = (uint32_t)((((wrow0 >> 2) + (lane >> 5)) * 64 + (lane & 31)) * 4);
+  // pass 2: odd rows, mu = H E[tok] + a (yhat_{j-1} + yhat_{j+1})
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
+    const bool edge = wrow0 + mb * 32 + 32 > N;
+    if (mb < 2) read_tok(mb + 6);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const int r = r_nb[nb];
-      const float st = st_nb[nb], inv = inv_nb[nb], a = a_nb[nb];
-      const uint32_t rvalid = rv_nb[nb];
-      const float ext = wm == 0 && mb == 3 ? xch[256 + wn * 128 + nb * 32 + (lane & 31)] : 0.f;
-      const int ln = lane;
-      const f32x16 b = acc_block(acc, mb, nb);
-      const float nx0 = mb < 3 ? acc[mb + 1][nb][0] : 0.f;  // the next block's first row
-      float m[8];
+      const int k = 16 + mb * 4 + nb;
+      float x[8], m[8], mu[8], f[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m[e] = mean(ln, mb, nb, 2 * e + 1);
-      int qi[8];
-      uint32_t em = 0;
+      for (int e = 0; e < 8; ++e) m[e] = mq[k % kAhead][e];
+      if (k + kAhead < 32) issue(k + kAhead);  // into the slot just read
+      const f32x4 ya = lyh[((k - 16) * 2) * 64 + lane], yb = lyh[((k - 16) * 2 + 1) * 64 + lane];
+      const float yv[8] = {ya.x, ya.y, ya.z, ya.w, yb.x, yb.y, yb.z, yb.w};  // yhat of register 2e
+      const float st = qc[nb].x, inv = qc[nb].y, a = qc[nb].z;
+      const float ext = wm == 0 && mb == 3 ? xch[256 + wn * 128 + nb * 32 + (lane & 31)] : 0.f;
+      const float nx0 = mb < 3 ? lyh[((k - 12) * 2) * 64 + lane].x : 0.f;  // the next block's first row
+      // the tile's last odd row (register 15 of lanes >= 32 in the last
+      // block row of the lower wave) waits for the next tile's first row
+      const bool dfr = mb == 3 && wm == 1 && defer_last;
+      const bool dlane = dfr && lane >= 32;
+      float dsum = 0.f, amax = 0.f, y2_last = 0.f;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        const float y0 = yv[2 * g], y2 = yv[2 * g + 1];
         // the first row of the next quad: lanes < 32 hold it in lane + 32
         // (same group), lanes >= 32 in lane - 32 (next group or next block)
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(b[4 * g]),
-                                                         __float_as_uint(g < 3 ? b[4 * g + 4] : nx0), false, false);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(y0),
+                                                         __float_as_uint(g < 3 ? yv[2 * g + 2] : nx0), false, false);
         float next3 = __uint_as_float(lane < 32 ? sw[1] : sw[0]);
         if (g == 3 && mb == 3 && lane >= 32) next3 = ext;
-        const float y0 = b[4 * g], y2 = b[4 * g + 2];
-        // bytes 1 and 3 of the quad's word (pass 1 wrote 0 and 2): byte
-        // stores, so that no load waits behind this pass's stores
-        uint32_t w = 0u;
-        {
-          const float mu = m[2 * g] + a * (y0 + y2);
-          uint32_t esc;
-          float yh;
-          const uint32_t sy = code(b[4 * g + 1] - mu, mu, st, inv, valid_v(ln, mb, 4 * g + 1, rvalid), qi[2 * g], esc,
-                                   yh);
-          em |= esc << (2 * g);
-          w |= sy << 8;
-        }
-        {
-          // the tile's last odd row waits for the next tile's first row
-          const bool deferred = wm == 1 && mb == 3 && g == 3 && lane >= 32 && defer_last;
-          const uint32_t valid = valid_v(ln, mb, 4 * g + 3, rvalid);
-          const float mu = m[2 * g + 1] + a * (y2 + next3);
-          uint32_t esc;
-          float yh;
-          uint32_t sy = code(b[4 * g + 3] - mu, mu, st, inv, valid, qi[2 * g + 1], esc, yh);
-          if (deferred) {
-            if (valid) P.halo_a[(int64_t)mt * P.C + r] = b[4 * g + 3] - m[2 * g + 1] - a * y2;
-            sy = valid ? 0u : 0xFFu;  // finished by the fix-up
-            esc = 0u;
-          }
-          em |= esc << (2 * g + 1);
-          w |= sy << 24;
-        }
-        if (valid_v(ln, mb, 4 * g, rvalid)) {
-          uint8_t *wb = reinterpret_cast<uint8_t *>(sym_at(ln, mb, nb, g));
-          wb[1] = (uint8_t)(w >> 8);
-          wb[3] = (uint8_t)(w >> 24);
+        if (g == 3) y2_last = y2;
+        x[2 * g] = acc_get(acc[mb][nb], 4 * g + 1);
+        x[2 * g + 1] = acc_get(acc[mb][nb], 4 * g + 3);
+        mu[2 * g] = m[2 * g] + a * (y0 + y2);
+        mu[2 * g + 1] = m[2 * g + 1] + a * (y2 + next3);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int e = 2 * g + i;
+          const float d = x[e] - mu[e];
+          dsum += d;
+          const float qf = rintf(div_step(d, st, inv));
+          amax = fmaxf(amax, e == 7 && dlane ? 0.f : fabsf(qf));
+          f[e] = qf + 127.f;
         }
       }
-      if (em) escapes(em, qi, 1, mb, r);
-      asm volatile("" : "+v"(nonfin));
+      const int r = n0 + wn * 128 + nb * 32 + (lane & 31);
+      if (edge || !(amax < 127.5f) || !isfinite(dsum)) {
+        int qi[8];
+        uint32_t em = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool valid = r < P.Ca && wrow0 + acc_row(mb, 2 * e + 1, lane) < N;
+          const bool deferred = e == 7 && dlane;  // decided by the fix-up
+          const float d = x[e] - mu[e];
+          if (valid && !deferred && !isfinite(d)) nonfin = 1u;
+          const float qf = fminf(fmaxf(rintf(div_step(d, st, inv)), -kQLimit), kQLimit);
+          qi[e] = (int)qf;
+          const bool esc = valid && !deferred && (qi[e] > 127 || qi[e] < -127);
+          em |= (uint32_t)esc << e;
+          f[e] = valid && !esc ? qf + 127.f : 255.f;
+        }
+        if (em) escapes(em, qi, 1, mb, r);
+      }
+      if (dlane) {
+        f[7] = 0.f;  // finished by the fix-up
+        if (r < P.Ca) P.halo_a[(int64_t)mt * P.C + r] = x[7] - m[7] - a * y2_last;
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint32_t o = __builtin_amdgcn_cvt_pk_u8_f32(f[2 * g], 1, 0u);
+        o = __builtin_amdgcn_cvt_pk_u8_f32(f[2 * g + 1], 3, o);
+        const uint32_t w = __builtin_amdgcn_perm(ev[mb][nb][g >> 1], o, (g & 1) ? 0x03070106u : 0x03050104u);
+        __builtin_amdgcn_raw_buffer_store_b32(w, symr[nb >> 1], sbase + (uint32_t)((nb & 1) * 128 + mb * 2048 + g * 512),
+                                              0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  if (nonfin >> 31) set_status(P.status, DCKV_EINVAL);
+  if (nonfin) set_status(P.status, DCKV_EINVAL);
 }
 
 
@@ -730,11 +793,6 @@ struct DeqP {
 constexpr int kDeqThreads = 256;
 constexpr int kDeqRows = 8;  // rows per thread: two quads (row quads share a symbol word)
 
-// A load through a global (address space 1) pointer.
-template <class T>
-__device__ __forceinline__ T gload(const T *p) {
-  return *(const T __attribute__((address_space(1))) *)p;
-}
 
 // The code of escaped position (j, rank r): binary search of its flat index
 // among the escape records of its 256-row tile (found by the parser).
@@ -1133,6 +1191,7 @@ static QuantP quant_params(const EncodeArgs &a) {
   P.tok = a.tok;
   P.step = a.p->dev.step;
   P.nbr = a.p->dev.nbr;
+  P.qcol = a.p->dev.qcol;
   P.mtab = a.p->mtab;
   P.sym32 = reinterpret_cast<uint32_t *>(a.ws + a.l.sym);
   P.esc_raw = reinterpret_cast<uint32_t *>(a.ws + a.l.esc_raw);
@@ -1148,6 +1207,7 @@ static QuantP quant_params(const EncodeArgs &a) {
   P.n_mt = (int)a.g.n_mtiles;
   P.n_nt = (int)(a.g.Ca4 / kBN);
   P.vocab = a.p->vocab;
+  P.T = (int)a.g.T;
   P.status = a.status;
   return P;
 }

@@ -240,6 +240,14 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
       bucket[(size_t)r * kBuckets + b] = (uint8_t)s;
     }
   }
+  // quantiser constants of each rank: step, 1 / step (0 past C_a), neighbour weight
+  std::vector<float> qcol((size_t)Ca_pad * 4, 0.f);
+  for (int r = 0; r < Ca_pad; ++r) {
+    const int c = act[r];
+    qcol[4 * r] = h.step[c];
+    qcol[4 * r + 1] = r < Ca ? 1.0f / h.step[c] : 0.f;
+    qcol[4 * r + 2] = p->nbr_weight[c];
+  }
   std::vector<double> omega(kHalf);
   for (int i = 0; i < kHalf; ++i) omega[i] = std::pow((double)pl->rope_theta, -(double)i / (double)kHalf);
 
@@ -251,7 +259,7 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
     return o;
   };
   const size_t o_step = take(C * 4), o_nbr = take(C * 4), o_rank = take(C * 4), o_act = take(Ca_pad * 4);
-  const size_t o_perm = take(C * 4), o_colpos = take(C * 4);
+  const size_t o_perm = take(C * 4), o_colpos = take(C * 4), o_qcol = take(qcol.size() * 4);
   const size_t o_tab = take(tab.size() * 4), o_bucket = take(bucket.size()), o_omega = take(kHalf * 8);
   void *blk = nullptr;
   if (hipMalloc(&blk, off) != hipSuccess) {
@@ -265,6 +273,7 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
   std::memcpy(&img[o_act], act.data(), Ca_pad * 4);
   std::memcpy(&img[o_perm], perm.data(), C * 4);
   std::memcpy(&img[o_colpos], colpos.data(), C * 4);
+  std::memcpy(&img[o_qcol], qcol.data(), qcol.size() * 4);
   std::memcpy(&img[o_tab], tab.data(), tab.size() * 4);
   std::memcpy(&img[o_bucket], bucket.data(), bucket.size());
   std::memcpy(&img[o_omega], omega.data(), kHalf * 8);
@@ -281,6 +290,7 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
   pl->dev.act = reinterpret_cast<int32_t *>(b + o_act);
   pl->dev.perm = reinterpret_cast<int32_t *>(b + o_perm);
   pl->dev.colpos = reinterpret_cast<int32_t *>(b + o_colpos);
+  pl->dev.qcol = reinterpret_cast<float *>(b + o_qcol);
   pl->dev.tab = reinterpret_cast<uint32_t *>(b + o_tab);
   pl->dev.bucket = b + o_bucket;
   pl->dev.omega = reinterpret_cast<double *>(b + o_omega);
