@@ -262,8 +262,12 @@ int dckv_workspace_view(const dckv_plan_t *plan, int64_t T, int32_t which, uint6
  * number of launches since the last reset.  Kernel names:
  * "analysis_gemm", "rans_encode", "rans_decode", "dequant", "w1_gemm",
  * "w1_gelu", "synthesis_gemm", "fixup", "scan", "pack", "parse".
+ * dckv_profile_only() restricts the timing to one kernel name (NULL or ""
+ * restores all), so that a timed run carries two events per launch of that
+ * kernel and none elsewhere.
  * --------------------------------------------------------------------------*/
 int dckv_profile_enable(int32_t on);
+int dckv_profile_only(const char *kernel);
 int dckv_profile_reset(void);
 int dckv_profile_read(const char *kernel, double *total_ms, int64_t *launches);
 

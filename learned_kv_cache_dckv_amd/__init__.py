@@ -27,7 +27,7 @@ VIEW_SYMBOLS, VIEW_YHAT_B, VIEW_H_B = 0, 1, 2
 EXPORTS = ("dckv_plan_tables", "dckv_plan", "dckv_plan_free", "dckv_plan_info", "dckv_plan_mean_table",
            "dckv_bytes", "dckv_encode",
            "dckv_decode", "dckv_bytes_batch", "dckv_encode_batch", "dckv_decode_batch", "dckv_entropy_encode",
-           "dckv_entropy_decode", "dckv_workspace_view", "dckv_profile_enable", "dckv_profile_reset",
+           "dckv_entropy_decode", "dckv_workspace_view", "dckv_profile_enable", "dckv_profile_only", "dckv_profile_reset",
            "dckv_profile_read", "dckv_last_error")
 
 
@@ -78,6 +78,7 @@ def _load():
         "dckv_entropy_decode": [P, P, U64, I64, P, P, P, P, U64, P],
         "dckv_workspace_view": [P, I64, I32, P, P, P],
         "dckv_profile_enable": [I32],
+        "dckv_profile_only": [ctypes.c_char_p],
         "dckv_profile_reset": [],
         "dckv_profile_read": [ctypes.c_char_p, P, P],
     }
@@ -366,6 +367,10 @@ def dckv_workspace_view(plan: Plan, T: int, which: int):
 
 def dckv_profile_enable(on: bool = True):
     _check(_lib.dckv_profile_enable(1 if on else 0))
+
+
+def dckv_profile_only(kernel=None):
+    _check(_lib.dckv_profile_only(kernel.encode() if kernel else None))
 
 
 def dckv_profile_reset():

@@ -455,6 +455,7 @@ namespace {
 struct ProfState {
   std::mutex mu;
   bool on = false;
+  std::string only;  // time only this kernel (empty: all)
   struct Pending {
     std::string name;
     hipEvent_t a, b;
@@ -484,6 +485,10 @@ void drain_locked(ProfState &s) {
 KernelTimer::KernelTimer(const char *name, hipStream_t s) : name_(name), s_(s) {
   ProfState &st = prof();
   if (!st.on) return;
+  {
+    std::lock_guard<std::mutex> g(st.mu);
+    if (!st.only.empty() && st.only != name) return;
+  }
   if (hipEventCreate(&a_) != hipSuccess || hipEventCreate(&b_) != hipSuccess) {
     a_ = b_ = nullptr;
     return;
@@ -502,6 +507,13 @@ KernelTimer::~KernelTimer() {
 
 extern "C" int dckv_profile_enable(int32_t on) {
   prof().on = on != 0;
+  return DCKV_OK;
+}
+
+extern "C" int dckv_profile_only(const char *kernel) {
+  ProfState &s = prof();
+  std::lock_guard<std::mutex> g(s.mu);
+  s.only = kernel ? kernel : "";
   return DCKV_OK;
 }
 

@@ -491,6 +491,76 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The symbols of one wave's rows: step i pops the symbol of row i from each
+// lane's state (bucket of the slot, then a binary search while any lane's
+// bucket holds more than one symbol), then renormalises the lanes that need
+// it with the next words of the interleaved stream, in lane order.  kPlain:
+// every lane is a coded component and the block has no escapes, so no lane
+// is ever skipped.  The word window is read modulo its size: a valid stream
+// never leaves it (it slides before it would), and a corrupt one ends with
+// ptr != W or a final state != L, which the caller reports.
+template <bool kPlain>
+__device__ __forceinline__ void decode_rows(uint32_t &x, uint32_t &ptr, uint32_t &base, uint32_t W, int Lb, int lane,
+                                            bool lane_ok, const unsigned long long *ebits, const uint32_t *mytab,
+                                            const uint8_t *mybkt, uint16_t *wb, const uint16_t *wsrc,
+                                            uint32_t *sout) {
+  auto step = [&](int i) -> uint32_t {
+    bool act = true;
+    if (!kPlain) {
+      act = lane_ok;
+      if (ebits) act = act && !((ebits[i] >> lane) & 1ull);
+    }
+    const uint32_t slot = x & (kM - 1u);
+    const uint32_t bi = slot >> kBucketShift;
+    uint32_t lo = mybkt[bi];
+    uint32_t hi = mybkt[bi + 1];
+    if (!kPlain) hi = act ? hi : lo;
+    while (__ballot(lo < hi)) {
+      const uint32_t mid = (lo + hi + 1) >> 1;
+      const bool up = (mytab[mid] >> 16) <= slot;
+      const bool open = lo < hi;
+      lo = open && up ? mid : lo;
+      hi = open && !up ? mid - 1 : hi;
+    }
+    const uint32_t e = mytab[lo];
+    // f * (x >> 15) < 2^32: f <= 2^15 and x >> 15 < 2^17 (24-bit multiply)
+    const uint32_t xd = __umul24(e & 0xFFFFu, x >> kPrecBits) + slot - (e >> 16);
+    x = act ? xd : x;
+    const bool need = act && x < kL;
+    const uint64_t mask = __ballot(need);
+    if (mask) {
+      const uint32_t cnt = (uint32_t)__popcll(mask);
+      if (ptr + cnt > base + kWordBuf && base + kWordBuf < W) {  // slide the window
+        base = ptr;
+        wave_sync_lds();
+        for (uint32_t k = lane; k < kWordBuf && base + k < W; k += 64) wb[k] = wsrc[base + k];
+        wave_sync_lds();
+      }
+      const uint32_t before = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+      const uint32_t wv = wb[(ptr - base + before) & (kWordBuf - 1u)];
+      x = need ? (x << 16) | wv : x;
+      ptr += cnt;
+    }
+    return act ? lo : (uint32_t)kEsc;
+  };
+  const int nq = Lb >> 2;
+#pragma unroll 1
+  for (int q = 0; q < nq; ++q) {
+    uint32_t w = step(4 * q);
+    w |= step(4 * q + 1) << 8;
+    w |= step(4 * q + 2) << 16;
+    w |= step(4 * q + 3) << 24;
+    if (kPlain || lane_ok) sout[(size_t)q * 64] = w;
+  }
+  if (Lb & 3) {  // the last, partial quad: rows past the block read as escapes
+    uint32_t w = 0xFFFFFFFFu;
+#pragma unroll 1
+    for (int k = 0; k < (Lb & 3); ++k) w = (w & ~(0xFFu << (8 * k))) | (step(4 * nq + k) << (8 * k));
+    if (kPlain || lane_ok) sout[(size_t)nq * 64] = w;
+  }
+}
+
 __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
   __shared__ uint32_t tab[kLanes * kTabStride];
   __shared__ uint8_t bkt[kLanes * kBktStride];
@@ -580,56 +650,12 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
   const uint32_t *mytab = tab + lane * kTabStride;
   const uint8_t *mybkt = bkt + lane * kBktStride;
   uint32_t *sout = P.sym32 + ((size_t)g * (P.N256 / 4) + (size_t)b * 64) * 64 + lane;
-  bool overrun = false;
-  uint32_t acc = 0xFFFFFFFFu;
-  for (int i = 0; i < Lb; ++i) {
-    bool act = lane_ok;
-    if (has_esc) act = act && !((ebits[wave][i] >> lane) & 1ull);
-    const uint32_t slot = x & (kM - 1u);
-    // the symbol lies between the first symbols of this bucket and the next;
-    // search while any lane's range holds more than one symbol
-    const uint32_t bi = slot >> kBucketShift;
-    uint32_t lo = mybkt[bi];
-    uint32_t hi = act ? (uint32_t)mybkt[bi + 1] : lo;
-    while (__ballot(lo < hi)) {
-      const uint32_t mid = (lo + hi + 1) >> 1;
-      const bool up = (mytab[mid] >> 16) <= slot;
-      const bool open = lo < hi;
-      lo = open && up ? mid : lo;
-      hi = open && !up ? mid - 1 : hi;
-    }
-    const uint32_t e = mytab[lo];
-    // f * (x >> 15) < 2^32: f <= 2^15 and x >> 15 < 2^17 (24-bit multiply)
-    const uint32_t xd = __umul24(e & 0xFFFFu, x >> kPrecBits) + slot - (e >> 16);
-    x = act ? xd : x;
-    const uint32_t s = act ? lo : (uint32_t)kEsc;
-    const bool need = act && x < kL;
-    const uint64_t mask = __ballot(need);
-    const uint32_t cnt = (uint32_t)__popcll(mask);
-    if (cnt) {
-      if (ptr + cnt > base + kWordBuf && base + kWordBuf < W) {  // slide the window
-        base = ptr;
-        wave_sync_lds();
-        for (uint32_t k = lane; k < kWordBuf && base + k < W; k += 64) wb[k] = wsrc[base + k];
-        wave_sync_lds();
-      }
-      const uint32_t before = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-      const uint32_t idx = ptr + before;
-      const bool ok = idx < W && idx - base < (uint32_t)kWordBuf;
-      const uint32_t wv = wb[ok ? idx - base : 0u];
-      x = need && ok ? (x << 16) | wv : x;
-      overrun = overrun || (need && !ok);
-      ptr += cnt;
-    }
-    const int k = i & 3;
-    acc = (acc & ~(0xFFu << (8 * k))) | (s << (8 * k));
-    if (k == 3 || i == Lb - 1) {
-      if (lane_ok) sout[(size_t)(i >> 2) * 64] = acc;
-      acc = 0xFFFFFFFFu;
-    }
-  }
-  const bool lane_bad = overrun || (lane_ok && x != kL);
+  const unsigned long long *eb = ebits[wave];
+  if (!has_esc && n == kLanes)
+    decode_rows<true>(x, ptr, base, W, Lb, lane, true, eb, mytab, mybkt, wb, wsrc, sout);
+  else
+    decode_rows<false>(x, ptr, base, W, Lb, lane, lane_ok, has_esc ? eb : nullptr, mytab, mybkt, wb, wsrc, sout);
+  const bool lane_bad = lane_ok && x != kL;
   if (__ballot(lane_bad) != 0ull || ptr != W) {
     if (lane == 0) set_status(P.status, DCKV_ECORRUPT);
   }
