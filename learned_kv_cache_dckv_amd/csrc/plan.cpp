@@ -227,7 +227,8 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
       tab[(size_t)r * 256 + s] = (uint32_t)f[s] | (cum << 16);
       cum += f[s];
     }
-    tab[(size_t)r * 256 + 255] = 0;  // unused
+    // entry 255 (escape) codes as the identity in the encoder: f = 2^15, cum 0
+    tab[(size_t)r * 256 + 255] = kM;
     // first symbol whose slot range contains the bucket's first slot
     int s = 0;
     uint32_t c0 = 0;

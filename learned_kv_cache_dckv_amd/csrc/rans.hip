@@ -69,23 +69,6 @@ __device__ __forceinline__ void stage_tab(uint32_t *tab, const uint32_t *gtab, i
 
 __device__ __forceinline__ Ctrl *ctrl_of(uint8_t *ws) { return reinterpret_cast<Ctrl *>(ws); }
 
-// x / f and x % f for 1 <= f < 2^15 and x < f * 2^17 (so x / f < 2^17): a
-// float reciprocal estimate is within one of the quotient, then one exact
-// integer correction step.
-__device__ __forceinline__ void divmod_small(uint32_t x, uint32_t f, uint32_t &q, uint32_t &r) {
-  const float est = (float)x * __builtin_amdgcn_rcpf((float)f);
-  q = (uint32_t)est;
-  int32_t rr = (int32_t)(x - q * f);
-  if (rr < 0) {
-    q -= 1;
-    rr += (int32_t)f;
-  } else if (rr >= (int32_t)f) {
-    q += 1;
-    rr -= (int32_t)f;
-  }
-  r = (uint32_t)rr;
-}
-
 struct EncP {
   const uint32_t *tab;     // [C_a][256]
   const uint32_t *sym32;   // tiled symbols
@@ -111,53 +94,60 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(EncP P) {
   const uint32_t *sw = P.sym32 + ((size_t)g * (P.N256 / 4) + (size_t)b * 64) * 64 + lane;
   uint16_t *out = P.scratch + (size_t)gid * (kLanes * (kBlock + 2));
   const bool lane_ok = lane < n;
-  const uint32_t *mytab = tab + lane * kTabStride;
-  const uint64_t higher = lane == 63 ? 0ull : (~0ull << (lane + 1));
+  // Escapes code as the identity: table entry 255 is f = 2^15, cum = 0, so
+  // the state never emits and x / f * 2^15 + x % f = x.  Lanes past C_a code
+  // escapes only, through lane 0's table row.
+  const uint32_t *mytab = tab + (lane_ok ? lane : 0) * kTabStride;
   uint32_t x = kL;
   uint32_t cnt = 0;
+  auto enc = [&](uint32_t s) {
+    const uint32_t e = mytab[s];
+    const uint32_t f = e & 0xFFFFu, c = e >> 16;
+    const bool emit = (x >> 17) >= f;  // x >= f 2^17 (f = 2^15 never emits)
+    const uint64_t mask = __ballot(emit);
+    if (mask) {
+      // the emitting lanes write in descending lane order
+      const uint32_t tot = (uint32_t)__popcll(mask);
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+      if (emit) out[cnt + tot - 1u - below] = (uint16_t)(x & 0xFFFFu);
+      x = emit ? x >> 16 : x;
+      cnt += tot;
+    }
+    // x / f within one from a float reciprocal (x < f 2^17), then corrected
+    const uint32_t q0 = (uint32_t)((float)x * __builtin_amdgcn_rcpf((float)f));
+    int32_t r = (int32_t)(x - __umul24(q0, f));
+    const uint32_t neg = (uint32_t)r >> 31;
+    r += neg ? (int32_t)f : 0;
+    const uint32_t big = r >= (int32_t)f;
+    r -= big ? (int32_t)f : 0;
+    x = ((q0 - neg + big) << kPrecBits) + (uint32_t)r + c;
+  };
   // symbol words in chunks of 8 quads, last chunk first; the words of the
-  // next chunk are loaded while this one is coded
+  // next chunk are loaded while this one is coded (every quad of the block
+  // is in the buffer; quads past the last are not coded)
   const int nq = (Lb + 3) >> 2;
   const int nch = (nq + 7) >> 3;
+  // rows past the block in its last quad code as escapes
+  const uint32_t tail = (Lb & 3) ? 0xFFFFFFFFu << (8 * (Lb & 3)) : 0u;
   uint32_t wq[8], wn[8];
   auto load_chunk = [&](int ch, uint32_t (&w)[8]) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int qd = ch * 8 + u;
-      w[u] = lane_ok && qd < nq ? gload(sw + (size_t)qd * 64) : 0xFFFFFFFFu;
-    }
+    for (int u = 0; u < 8; ++u) w[u] = gload(sw + (size_t)(ch * 8 + u) * 64);
   };
   load_chunk(nch - 1, wn);
+#pragma unroll 1
   for (int ch = nch - 1; ch >= 0; --ch) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) wq[u] = wn[u];
+    for (int u = 0; u < 8; ++u) wq[u] = lane_ok ? wn[u] : 0xFFFFFFFFu;
     if (ch > 0) load_chunk(ch - 1, wn);
 #pragma unroll
     for (int u = 7; u >= 0; --u) {
-    const int qd = ch * 8 + u;
-    if (qd >= nq) continue;
-    const uint32_t w = wq[u];
+      const int qd = ch * 8 + u;
+      if (qd >= nq) continue;
+      const uint32_t w = wq[u] | (qd == nq - 1 ? tail : 0u);
 #pragma unroll
-    for (int k = 3; k >= 0; --k) {
-      const int i = qd * 4 + k;
-      if (i >= Lb) continue;
-      const uint32_t s = (w >> (8 * k)) & 0xFFu;
-      const bool act = s != (uint32_t)kEsc;
-      const uint32_t e = act ? mytab[s] : 0u;
-      const uint32_t f = e & 0xFFFFu, c = e >> 16;
-      const bool emit = act && (x >= (f << 17));
-      const uint64_t mask = __ballot(emit);
-      if (emit) {
-        out[cnt + __popcll(mask & higher)] = (uint16_t)(x & 0xFFFFu);
-        x >>= 16;
-      }
-      cnt += (uint32_t)__popcll(mask);
-      if (act) {
-        uint32_t q, r;
-        divmod_small(x, f, q, r);
-        x = (q << kPrecBits) + r + c;
-      }
-    }
+      for (int k = 3; k >= 0; --k) enc((w >> (8 * k)) & 0xFFu);
     }
   }
   if (lane_ok) {
