@@ -38,10 +38,10 @@
 //               plan's rank order (active components, then dropped ones)
 //   quantise    analysis GEMM; epilogue: even rows r = (y - mu)/step,
 //               q = rint(r), yhat = mu + q step; then odd rows with
-//               mu += a (yhat_{j-1} + yhat_{j+1}); mu rows are gathered from
-//               the table into LDS one parity at a time; the first row of the
-//               lower wave crosses waves through LDS, the last odd row of a
-//               tile is finished by a small fix-up kernel
+//               mu += a (yhat_{j-1} + yhat_{j+1}); mu comes from the table
+//               straight into registers, four accumulator blocks ahead; the
+//               first row of the lower wave crosses waves through LDS, the
+//               last odd row of a tile is finished by a small fix-up kernel
 //   dequant     no GEMM: yhat = mu + q step in the same two passes, streamed
 //               row by row from the table, the codes and the escape records
 //               -> bf16 yhat_b
