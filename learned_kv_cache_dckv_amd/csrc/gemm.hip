@@ -234,9 +234,16 @@ __device__ __forceinline__ void tile_barrier() {
 // kt % 2 has been read in full.  The last k-step reads the first fragments of
 // k-tile kt + 1 and issues the A loads of k-tile kt + 2 into the free stage; the
 // first k-step of the next tile issues its B loads.
-template <bool kPinAcc = true>
+struct NoSide {
+  __device__ void operator()(int) const {}
+};
+
+// kPeel > 0: the first kPeel k-tiles are unrolled and call side(8 kt + i),
+// i = 0..7, spread over their third k-step (work with compile-time indices,
+// such as stores of registers held from a previous tile); needs KT >= kPeel.
+template <bool kPinAcc = true, int kPeel = 0, class S = NoSide>
 __device__ __forceinline__ void mainloop(const Operand &A, const Operand &B, int KT, f32x16 (&acc)[4][4],
-                                         char *lds) {
+                                         char *lds, S &&side = S()) {
   // the wave index in a scalar register: LDS destinations of the direct loads
   // (M0) must be wave-uniform
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -259,18 +266,21 @@ __device__ __forceinline__ void mainloop(const Operand &A, const Operand &B, int
   Frags f0, f1;
   read_frags(f0, lds, 0, lane, wm, wn);
   const auto none = [](int) {};
-#pragma unroll 1
-  for (int kt = 0; kt < KT; ++kt) {
+  auto body = [&](int kt, auto &&sidek) {
     char *cur = lds + (kt & 1) * kStageBytes;
     char *nxt = lds + ((kt + 1) & 1) * kStageBytes;
     kstep(acc, f0, f1, cur, 1, lane, wm, wn, [&](int i) { load_rows(B, tb, i, nxt + kBM * kRowBytes, wave, lane); });
-    kstep(acc, f1, f0, cur, 2, lane, wm, wn, none);
+    kstep(acc, f1, f0, cur, 2, lane, wm, wn, sidek);
     kstep(acc, f0, f1, cur, 3, lane, wm, wn, none);
     tile_barrier<0>();
     ta = tile_src(A, kt + 2, KT);
     tb = tile_src(B, kt + 2, KT);
     kstep(acc, f1, f0, nxt, 0, lane, wm, wn, [&](int i) { load_rows(A, ta, i, cur, wave, lane); });
-  }
+  };
+#pragma unroll
+  for (int kt = 0; kt < kPeel; ++kt) body(kt, [&](int i) { side(8 * kt + i); });
+#pragma unroll 1
+  for (int kt = kPeel; kt < KT; ++kt) body(kt, none);
   __syncthreads();
   // The accumulators leave the loop in AGPRs; epilogues copy them to VGPRs one
   // block at a time (an epilogue that needs them in VGPRs would otherwise have
@@ -1063,91 +1073,162 @@ __device__ __forceinline__ int syn_dim(int n) {
   return (nb >> 1) * 128 + 64 * wn + 32 * (nb & 1) + j;
 }
 
+// Rows r, r + 1 of this lane's column j (y0, y1) -> one word of a row and two
+// adjacent columns: lanes l and l ^ 1 (columns j, j ^ 1) swap their packed
+// pairs with a DPP quad permute; the even lane keeps row r (columns j, j + 1),
+// the odd lane row r + 1 (columns j - 1, j).  sel is the lane's v_perm
+// selector (0x05040100 on even lanes, 0x03020706 on odd ones).
+__device__ __forceinline__ uint32_t row_pair_word(float y0, float y1, uint32_t sel) {
+  const uint32_t pk = pack_bf16x2(y0, y1);
+  const uint32_t sw = (uint32_t)__builtin_amdgcn_mov_dpp((int)pk, 0xB1, 0xF, 0xF, false);
+  return __builtin_amdgcn_perm(sw, pk, sel);
+}
+
+// Word p of a wave's packed output tile: p = ((mb 4 + nb) 4 + g) 2 + h holds
+// tile row acc_crow(mb, 4g + 2h) + 4 (lane / 32) + lane % 2 and the columns
+// (lane % 32) & ~1 and + 1 of block nb.  Its byte offset from the wave's
+// origin (row 0, first column of the wave's half of the head), without the
+// lane's part; block nb holds head dims (nb / 2) 128 + 32 (nb % 2) + [0, 32).
+__device__ __forceinline__ constexpr uint32_t pend_off(int p) {
+  return (uint32_t)((acc_crow(p >> 5, 4 * ((p >> 1) & 3) + 2 * (p & 1)) * kD + ((p >> 3) & 3) / 2 * 128 +
+                     32 * (((p >> 3) & 3) & 1)) * 2);
+}
+
+// Persistent: each workgroup takes tiles b, b + grid, ...  Of the 128 x 128
+// bf16 outputs of a wave (128 words per lane), kSynDefer words per lane stay
+// in registers after the epilogue and are stored during the first k-tiles of
+// the next tile's main loop, so that the stores of all CUs do not come at the
+// same moment (the rest, as many as the registers left by the main loop do
+// not hold, are stored at once); the last tile's words are stored at the end.  A buffer resource per tile ends at the
+// last coded row, so stores of rows past N are dropped.
+constexpr int kSynDefer = 96;             // words held over (the rest are stored at once)
+constexpr int kSynPeel = kSynDefer / 8;    // k-tiles that store them, 8 each
+static_assert((kC + kHid) / kBK >= kSynPeel, "synthesis main loop shorter than the store spread");
+
 __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   if (wg_stop(P.status)) return;
-  int mt, nt;
-  tile_of(blockIdx.x, P.n_mt * P.n_nt, P.n_nt, mt, nt);
-  const int64_t m0 = (int64_t)mt * kBM;
-  const int head = nt;
-  Operand A, B;
-  set_sources(A, P.yhat_b, kC * 2, P.h_b, kHid * 2, kC / kBK);
-  set_sources(B, P.S, kC * 2, P.W2, kHid * 2, kC / kBK);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    A.row[i] = (uint32_t)(m0 + staged_row(i));
-    B.row[i] = (uint32_t)(head * kHeadDim + syn_dim(staged_row(i)));
-  }
-  f32x16 acc[4][4];
-  mainloop(A, B, (kC + kHid) / kBK, acc, lds);
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const bool is_key = (head & 3) < 2;  // per layer: 2 key heads, then 2 value heads
-  const int64_t wrow0 = m0 + wm * 128;
-  char *wtile = lds + wave * kOutWaveBytes;
-  if (is_key) {
-    // Angles: the lane's first row from the tables (position p = 256 hi +
-    // lo), every other row by rotating it through 32 (block), 8 (register
-    // group) and 1 (row) positions, whose cos / sin are rows 32, 8 and 1 of
-    // the low table.  All table loads are issued before the first rotation.
-    // A lane whose first row is past the end stores nothing; its position
-    // is clamped only to stay inside the tables.
-    const int64_t p0 = P.keep_head + min<int64_t>(wrow0 + 4 * (lane >> 5), P.N - 1);
-    float2 ta[2], tb[2], r1[2], r8[2], r32[2];
+  const int total = P.n_mt * P.n_nt;
+  uint32_t pend[kSynDefer];
+  rsrc_t pr;          // the tile of the words
+  uint32_t lb = 0u, sel = 0u;
+  bool have = false;  // wave-uniform
+  auto store_pend = [&](int p) {
+    __builtin_amdgcn_raw_buffer_store_b32(pend[p], pr, lb + pend_off(p), 0, 0);
+  };
+  // word p of this tile: held over, or stored now
+  auto put = [&](int p, uint32_t w) {
+    if (p < kSynDefer)
+      pend[p] = w;
+    else
+      __builtin_amdgcn_raw_buffer_store_b32(w, pr, lb + pend_off(p), 0, 0);
+  };
+#pragma unroll 1
+  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+    int mt, nt;
+    tile_of(t, total, P.n_nt, mt, nt);
+    const int64_t m0 = (int64_t)mt * kBM;
+    const int head = nt;
+    Operand A, B;
+    set_sources(A, P.yhat_b, kC * 2, P.h_b, kHid * 2, kC / kBK);
+    set_sources(B, P.S, kC * 2, P.W2, kHid * 2, kC / kBK);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int f = 64 * wn + 32 * nb + (lane & 31);  // rotary frequency index
-      ta[nb] = P.rope_lo[(size_t)(p0 & 255) * kHalf + f];
-      tb[nb] = P.rope_hi[(size_t)(p0 >> 8) * kHalf + f];
-      r1[nb] = P.rope_lo[1 * kHalf + f];
-      r8[nb] = P.rope_lo[8 * kHalf + f];
-      r32[nb] = P.rope_lo[32 * kHalf + f];
+    for (int i = 0; i < 8; ++i) {
+      A.row[i] = (uint32_t)(m0 + staged_row(i));
+      B.row[i] = (uint32_t)(head * kHeadDim + syn_dim(staged_row(i)));
     }
-    auto rot = [](float &c, float &s, float2 r) {
-      const float c2 = c * r.x - s * r.y;
-      s = s * r.x + c * r.y;
-      c = c2;
-    };
-    char *wbase = wtile_base(wtile, lane);
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float c_mb = tb[nb].x * ta[nb].x - tb[nb].y * ta[nb].y;
-      float s_mb = tb[nb].y * ta[nb].x + tb[nb].x * ta[nb].y;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const f32x16 blo = acc_block(acc, mb, nb), bhi = acc_block(acc, mb, nb + 2);
-        float c_g = c_mb, s_g = s_mb;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float cs = c_g, sn = s_g;
-          float o0[4], o1[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int v = 4 * g + i;
-            o0[i] = blo[v] * cs - bhi[v] * sn;
-            o1[i] = bhi[v] * cs + blo[v] * sn;
-            if (i < 3) rot(cs, sn, r1[nb]);
-          }
-          const int crow = acc_crow(mb, 4 * g);
-          put_rows2(wbase, crow, nb * 32, o0[0], o0[1]);
-          put_rows2(wbase, crow + 2, nb * 32, o0[2], o0[3]);
-          put_rows2(wbase, crow, (nb + 2) * 32, o1[0], o1[1]);
-          put_rows2(wbase, crow + 2, (nb + 2) * 32, o1[2], o1[3]);
-          if (g < 3) rot(c_g, s_g, r8[nb]);
-        }
-        if (mb < 3) rot(c_mb, s_mb, r32[nb]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  } else {
-    acc_to_wtile(acc, wtile, lane, Identity());
-  }
-  wave_lds_sync();
-  const int64_t hb = (int64_t)head * kHeadDim;
-  flush_rows(wtile, P.out + (size_t)P.keep_head * kD, kD, wrow0, hb + 64 * wn, hb + 128 + 64 * wn, P.N);
-}
+    f32x16 acc[4][4];
+    if (have)
+      mainloop<true, kSynPeel>(A, B, (kC + kHid) / kBK, acc, lds, store_pend);
+    else
+      mainloop(A, B, (kC + kHid) / kBK, acc, lds);
 
+    const int lane = epilogue_lane();
+    const bool is_key = (head & 3) < 2;  // per layer: 2 key heads, then 2 value heads
+    const int64_t wrow0 = m0 + wm * 128;
+    // this tile's words: rows from keep_head + wrow0, columns from the
+    // wave's half of the head
+    {
+      const int64_t r0 = P.keep_head + wrow0;
+      const int64_t rows = max<int64_t>(0, P.N - wrow0);
+      pr = span_rsrc(P.out + (size_t)r0 * kD + (size_t)head * kHeadDim + 64 * wn,
+                     (uint32_t)min<int64_t>(rows * kD * 2, 0x7FFFFFFF));
+      lb = (uint32_t)(((4 * (lane >> 5) + (lane & 1)) * kD + ((lane & 31) & ~1)) * 2);
+      sel = (lane & 1) ? 0x03020706u : 0x05040100u;
+    }
+    if (is_key) {
+      // Angles: the lane's first row from the tables (position p = 256 hi +
+      // lo), every other row by rotating it through 32 (block), 8 (register
+      // group) and 1 (row) positions, whose cos / sin are rows 32, 8 and 1 of
+      // the low table.  All table loads are issued before the first rotation.
+      // The position of a lane whose first row is past the end is clamped
+      // only to stay inside the tables (its words are dropped).
+      const int64_t p0 = P.keep_head + min<int64_t>(wrow0 + 4 * (lane >> 5), P.N - 1);
+      float2 ta[2], tb[2], r1[2], r8[2], r32[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int f = 64 * wn + 32 * nb + (lane & 31);  // rotary frequency index
+        ta[nb] = P.rope_lo[(size_t)(p0 & 255) * kHalf + f];
+        tb[nb] = P.rope_hi[(size_t)(p0 >> 8) * kHalf + f];
+        r1[nb] = P.rope_lo[1 * kHalf + f];
+        r8[nb] = P.rope_lo[8 * kHalf + f];
+        r32[nb] = P.rope_lo[32 * kHalf + f];
+      }
+      auto rot = [](float &c, float &s, float2 r) {
+        const float c2 = c * r.x - s * r.y;
+        s = s * r.x + c * r.y;
+        c = c2;
+      };
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float c_mb = tb[nb].x * ta[nb].x - tb[nb].y * ta[nb].y;
+        float s_mb = tb[nb].y * ta[nb].x + tb[nb].x * ta[nb].y;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          float c_g = c_mb, s_g = s_mb;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float cs = c_g, sn = s_g;
+            float o0[4], o1[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int v = 4 * g + i;
+              const float lo = acc_get(acc[mb][nb], v), hi = acc_get(acc[mb][nb + 2], v);
+              o0[i] = lo * cs - hi * sn;
+              o1[i] = hi * cs + lo * sn;
+              if (i < 3) rot(cs, sn, r1[nb]);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              put(((mb * 4 + nb) * 4 + g) * 2 + h, row_pair_word(o0[2 * h], o0[2 * h + 1], sel));
+              put(((mb * 4 + nb + 2) * 4 + g) * 2 + h, row_pair_word(o1[2 * h], o1[2 * h + 1], sel));
+            }
+            if (g < 3) rot(c_g, s_g, r8[nb]);
+          }
+          if (mb < 3) rot(c_mb, s_mb, r32[nb]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            put((mb * 4 + nb) * 8 + q, row_pair_word(acc_get(acc[mb][nb], 2 * q), acc_get(acc[mb][nb], 2 * q + 1), sel));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    have = true;
+  }
+  if (have) {
+#pragma unroll
+    for (int p = 0; p < kSynDefer; ++p) store_pend(p);
+  }
+}
 
 }  // namespace
 
@@ -1295,7 +1376,17 @@ void launch_synthesis_gemm(const DecodeArgs &a) {
   P.n_mt = (int)a.g.n_mtiles;
   P.n_nt = kD / kBN;
   P.status = a.status;
-  launch_gemm(k_synthesis, "synthesis_gemm", P.n_mt * P.n_nt, P, a.s);
+  // persistent: one workgroup per CU at most
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      n_cu = n;
+    else
+      n_cu = 256;
+  }
+  launch_gemm(k_synthesis, "synthesis_gemm", std::min(P.n_mt * P.n_nt, n_cu), P, a.s);
 }
 
 }  // namespace dckv
