@@ -9,7 +9,12 @@ RoPE, kept rows).  Inputs are resident in HBM before the timed region; the
 plan (with its table) is built before it, once per rate.  Prints one JSON
 line.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--codec linear]
+
+--codec linear measures the linear codec (the same codec without the
+synthesis-side GELU correction); --rate-ladder instead prints, for each rate
+setting of the mixed-rate batch workload and both codecs, the 32K request's
+bytes/token, stored/modelled ratio and encode/decode rates (one JSON line).
 
 HBM traffic of the dominant kernel (the roofline's "traffic") comes from two
 rocprofv3 counter runs of this script, one with FETCH_SIZE and one with
@@ -148,6 +153,78 @@ def write_traffic(fetch_dir: str, write_dir: str, copy_mib: int, T: int) -> int:
     return 0
 
 
+def codec_params(w, codec: str) -> dict:
+    p = dict(w.params())
+    if codec == "linear":  # no correction: decode is xhat = S yhat_b
+        p.pop("w1")
+        p.pop("w2")
+    return p
+
+
+def rate_ladder(cfg: int, steps: int) -> int:
+    """Bytes/token, stored/modelled and rates at each rate of the mixed batch."""
+    import torch
+    import dckv_synth as synth
+    import learned_kv_cache_dckv_amd as dk
+    dev = torch.device("cuda:0")
+    w = synth.world()
+    req = synth.make_request(cfg)
+    T = req.T
+    rows = torch.from_numpy(req.rows.view(np.int16)).to(dev)
+    tok = torch.from_numpy(req.token_ids.astype(np.int32)).to(dev)
+    s = torch.cuda.current_stream()
+    out_rows = torch.empty((T, 6144), dtype=torch.int16, device=dev)
+    res = []
+    for codec_name in ("dckv", "linear"):
+        codec = dk.Codec(codec_params(w, codec_name), device=dev)
+        for rate in synth.CONFIGS[4]["rates"]:
+            plan = codec.plan(synth.step_scale_for(rate))
+            max_bytes, ws_bytes = plan.bytes(T)
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            buf = torch.empty(max_bytes, dtype=torch.uint8, device=dev)
+            nb = torch.zeros(1, dtype=torch.int64, device=dev)
+            st = torch.zeros(1, dtype=torch.int32, device=dev)
+            dk.dckv_encode(plan, rows, tok, buf, nb, st, ws)
+            torch.cuda.synchronize()
+            n_bytes = int(nb.item())
+            assert int(st.item()) == 0
+
+            def timed(fn):
+                fn()
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(s)
+                for _ in range(steps):
+                    fn()
+                b.record(s)
+                torch.cuda.synchronize()
+                return a.elapsed_time(b) / steps
+
+            enc_ms = timed(lambda: dk.dckv_encode(plan, rows, tok, buf, nb, st, ws))
+            dec_ms = timed(lambda: dk.dckv_decode(plan, buf, n_bytes, tok, out_rows, st, ws))
+            assert int(st.item()) == 0
+            data = buf[:n_bytes].cpu().numpy()
+            hdr = data[:64].view(np.uint32)
+            N, Ca, n_esc = int(hdr[5]), int(hdr[7]), int(hdr[9])
+            coded = n_bytes - 64 - (T - N) * KV_BYTES_PER_TOKEN
+            sym = torch.empty(max(N * Ca, 1), dtype=torch.uint8, device=dev)
+            ne = torch.zeros(1, dtype=torch.int32, device=dev)
+            dk.dckv_entropy_decode(plan, buf, n_bytes, T, sym, ne, st, ws)
+            torch.cuda.synchronize()
+            symh = sym[:N * Ca].cpu().numpy().reshape(N, Ca)
+            freq = dk.dckv_plan_info(plan)["freq"].astype(np.float64)
+            ok = symh != 255
+            rank = np.broadcast_to(np.arange(Ca)[None, :], symh.shape)
+            modelled = float(np.sum(15.0 - np.log2(freq[rank[ok], symh[ok]])) + 64.0 * n_esc)
+            res.append({"codec": codec_name, "rate_target_bytes_per_token": rate, "C_a": Ca,
+                        "bytes_per_token": coded / N, "stored_over_modelled": coded * 8.0 / modelled,
+                        "n_esc": n_esc, "encode_tokens_per_s": N / (enc_ms * 1e-3),
+                        "decode_tokens_per_s": N / (dec_ms * 1e-3)})
+            del plan, ws, buf
+    print(json.dumps({"workload": req.note, "T": T, "steps": steps, "rate_ladder": res}))
+    return 0
+
+
 def vendor_gemm(N: int, steps: int) -> int:
     """The vendor library's plain bf16 GEMMs (torch.matmul: hipBLASLt) on the
     codec's GEMM shapes, for comparison with the fused kernels' main loops.
@@ -191,11 +268,17 @@ def main(argv=None) -> int:
                     help="write profiles/traffic.json from two rocprofv3 counter runs, then exit")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="time the vendor library's plain GEMMs on the same shapes, then exit")
+    ap.add_argument("--codec", choices=("dckv", "linear"), default="dckv",
+                    help="linear: the codec without the GELU correction")
+    ap.add_argument("--rate-ladder", action="store_true",
+                    help="bytes/token and rates at each rate setting, both codecs, then exit")
     args = ap.parse_args(argv)
     if args.vendor_gemm:
         import dckv_synth as synth
         T = synth.CONFIGS[args.config]["T"]
         return vendor_gemm(T - 132, args.steps)
+    if args.rate_ladder:
+        return rate_ladder(args.config, args.steps)
     if args.write_traffic:
         import dckv_synth as synth
         return write_traffic(args.write_traffic[0], args.write_traffic[1], args.copy_calibration_mib or 1024,
@@ -212,7 +295,7 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     w = synth.world()
     req = synth.make_request(args.config)
-    codec = dk.Codec(w.params(), device=dev)
+    codec = dk.Codec(codec_params(w, args.codec), device=dev)
     t0 = time.perf_counter()
     plan = codec.plan(req.step_scale)
     plan_ms = (time.perf_counter() - t0) * 1e3
@@ -351,7 +434,8 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": req.note, "T": T, "coded_tokens": N, "rate_target_bytes_per_token": req.rate_target,
+        "config": {"workload": req.note, "codec": args.codec, "T": T, "coded_tokens": N,
+                   "rate_target_bytes_per_token": req.rate_target,
                    "step_scale": req.step_scale, "C_a": Ca, "groups": n_groups},
         "encode_tokens_per_s": N / (enc_ms * 1e-3),
         "decode_tokens_per_s": N / (dec_ms * 1e-3),

@@ -71,7 +71,8 @@ typedef struct {
   const uint16_t *analysis;   /* A  [n_coef][D]          y = A x          */
   const uint16_t *synthesis;  /* S  [D][n_coef]          xhat = S yhat_b + W2 h_b */
   const uint16_t *w1;         /* W1 [n_hidden][n_coef]   h = GELU(W1 yhat_b) */
-  const uint16_t *w2;         /* W2 [D][n_hidden]        */
+  const uint16_t *w2;         /* W2 [D][n_hidden]        (w1 = w2 = NULL: the
+                                 linear codec, xhat = S yhat_b; streams are the same) */
   const uint16_t *embedding;  /* E  [vocab][emb_dim]     the LM's input embedding */
   const uint16_t *mean_head;  /* H  [n_coef][emb_dim]    mean = H E[tok]  */
   const float *nbr_weight;    /* (host) a_c [n_coef]: odd mean += a_c (yhat_{j-1,c} + yhat_{j+1,c}) */

@@ -163,8 +163,10 @@ class Codec:
 
         self.analysis = dev(params["analysis"])
         self.synthesis = dev(params["synthesis"])
-        self.w1 = dev(params["w1"])
-        self.w2 = dev(params["w2"])
+        # without w1 / w2: the linear codec (no correction on the synthesis side)
+        self.linear = params.get("w1") is None
+        self.w1 = None if self.linear else dev(params["w1"])
+        self.w2 = None if self.linear else dev(params["w2"])
         self.embedding = dev(params["embedding"])
         self.mean_head = dev(params["mean_head"])
         self.nbr_weight = np.ascontiguousarray(params["nbr_weight"], dtype=np.float32)
@@ -175,7 +177,7 @@ class Codec:
                           keep_tail=params.get("keep_tail", 128), rope_theta=params.get("rope_theta", 1e7))
         self.n_coef = self.analysis.shape[0]
         self.D = self.analysis.shape[1]
-        self.n_hidden = self.w1.shape[0]
+        self.n_hidden = 256 if self.linear else self.w1.shape[0]
         self.vocab, self.emb_dim = self.embedding.shape
 
     def c_params(self) -> _Params:

@@ -1062,6 +1062,7 @@ struct SynP {
   uint16_t *out;                     // rows_out [T][D]
   int64_t N;
   int keep_head, n_mt, n_nt;
+  int KT;                            // k-tiles: 36 with the correction, 32 for the linear codec
   int32_t *status;
 };
 
@@ -1103,7 +1104,7 @@ __device__ __forceinline__ constexpr uint32_t pend_off(int p) {
 // last coded row, so stores of rows past N are dropped.
 constexpr int kSynDefer = 96;             // words held over (the rest are stored at once)
 constexpr int kSynPeel = kSynDefer / 8;    // k-tiles that store them, 8 each
-static_assert((kC + kHid) / kBK >= kSynPeel, "synthesis main loop shorter than the store spread");
+static_assert(kC / kBK >= kSynPeel, "synthesis main loop shorter than the store spread");
 
 __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -1141,9 +1142,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
     }
     f32x16 acc[4][4];
     if (have)
-      mainloop<true, kSynPeel>(A, B, (kC + kHid) / kBK, acc, lds, store_pend);
+      mainloop<true, kSynPeel>(A, B, P.KT, acc, lds, store_pend);
     else
-      mainloop(A, B, (kC + kHid) / kBK, acc, lds);
+      mainloop(A, B, P.KT, acc, lds);
 
     const int lane = epilogue_lane();
     const bool is_key = (head & 3) < 2;  // per layer: 2 key heads, then 2 value heads
@@ -1355,8 +1356,10 @@ void launch_w1_gemm(const DecodeArgs &a) {
   P.n_kept = a.g.n_kept;
   P.head_n = std::min<int64_t>(a.p->keep_head, a.g.T);
   P.tail_pos0 = a.p->keep_head + a.g.N;
-  P.gelu_blocks = (unsigned)((a.g.N * (kHid / 4) + 255) / 256);
-  if (a.g.N) launch_gemm(k_w1, "w1_gemm", P.n_mt * 2, P, a.s);
+  // the linear codec (no correction) launches the kept rows only
+  P.gelu_blocks = a.p->W1 ? (unsigned)((a.g.N * (kHid / 4) + 255) / 256) : 0u;
+  if (P.gelu_blocks + a.g.n_kept == 0) return;
+  if (a.g.N && a.p->W1) launch_gemm(k_w1, "w1_gemm", P.n_mt * 2, P, a.s);
   KernelTimer tm("w1_gelu", a.s);
   hipLaunchKernelGGL(k_w1_gelu, dim3(P.gelu_blocks + (unsigned)a.g.n_kept), dim3(256), 0, a.s, P);
 }
@@ -1375,6 +1378,7 @@ void launch_synthesis_gemm(const DecodeArgs &a) {
   P.keep_head = a.p->keep_head;
   P.n_mt = (int)a.g.n_mtiles;
   P.n_nt = kD / kBN;
+  P.KT = (kC + (a.p->W1 ? kHid : 0)) / kBK;
   P.status = a.status;
   // persistent: one workgroup per CU at most
   static int n_cu = 0;

@@ -161,8 +161,9 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
   if (p->vocab < 1 || p->keep_head < 0 || p->keep_tail < 0 || !(p->rope_theta > 0.0f) ||
       !std::isfinite(p->rope_theta))
     return set_error(DCKV_EINVAL, "plan: bad vocab, keep sizes or rope_theta");
-  if (!p->analysis || !p->synthesis || !p->w1 || !p->w2 || !p->embedding || !p->mean_head || !p->nbr_weight)
+  if (!p->analysis || !p->synthesis || !p->embedding || !p->mean_head || !p->nbr_weight)
     return set_error(DCKV_EINVAL, "plan: null parameter pointer");
+  if (!p->w1 != !p->w2) return set_error(DCKV_EINVAL, "plan: w1 and w2 are both given or both null");
   for (int c = 0; c < p->n_coef; ++c)
     if (!std::isfinite(p->nbr_weight[c])) return set_error(DCKV_EINVAL, "plan: non-finite nbr_weight");
   HostTables h;

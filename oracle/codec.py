@@ -28,6 +28,10 @@ Readings taken where the pages are silent (each is used below):
     w_i = theta^(-i/(head_dim/2)), angle t*w_i in float64) on the key columns;
     output bf16.  Kept rows get the same RoPE, so the output is a uniform
     post-RoPE cache.
+  * The linear codec (Evidence section, which compares its stored payload
+    with DCKV's) is read as the same codec without the nonlinear correction:
+    params without "w1" / "w2" decode to xhat = S yhat_b.  Encoding does not
+    involve the correction, so both codecs write the same stream.
 """
 from __future__ import annotations
 
@@ -273,18 +277,22 @@ def decode(data: bytes, tok: np.ndarray, params: dict, p: Plan) -> Decoded:
     q = np.zeros((N, C), dtype=np.int64)
     q[:, p.act_idx] = qa
     out = np.zeros((T, D), dtype=np.uint16)
-    hid = params["w1"].shape[0]
+    linear = params.get("w1") is None
+    hid = 0 if linear else params["w1"].shape[0]
     if N > 0:
         m = embedding_mean(params, tok[coded_t])
         yhat = dequantize(q, m, p, params["nbr_weight"])
         yb_bits = bf16.from_f64(yhat)
         yb = bf16.to_f64(yb_bits)
-        W1 = bf16.to_f64(params["w1"])
-        hb_bits = bf16.from_f64(gelu(yb @ W1.T))
-        hb = bf16.to_f64(hb_bits)
         S = bf16.to_f64(params["synthesis"])
-        W2 = bf16.to_f64(params["w2"])
-        xhat = yb @ S.T + hb @ W2.T
+        xhat = yb @ S.T
+        if linear:
+            hb_bits = np.zeros((N, 0), np.uint16)
+        else:
+            W1 = bf16.to_f64(params["w1"])
+            hb_bits = bf16.from_f64(gelu(yb @ W1.T))
+            W2 = bf16.to_f64(params["w2"])
+            xhat = xhat + bf16.to_f64(hb_bits) @ W2.T
         out[coded_t] = bf16.from_f64(rope(xhat, coded_t, sh))
     else:
         yhat = np.zeros((0, C))

@@ -425,6 +425,28 @@ def test_end_to_end_closed_form_error_bound():
     assert np.all(err <= bound + slack)
 
 
+def test_linear_codec_drops_exactly_the_correction():
+    """The linear codec (no w1 / w2) writes the same stream and decodes to the
+    DCKV reconstruction minus W2 h_b: the pre-RoPE difference equals W2 h_b
+    computed here from the DCKV decode's own h_b."""
+    prm = tiny_params(seed=21, n_coef=8, head_dim=8, n_layers=1, n_kv_heads=1, keep_head=1, keep_tail=2)
+    lin = {k: v for k, v in prm.items() if k not in ("w1", "w2")}
+    pl = P.make_plan(np.float32(0.3), prm["base_step"], prm["laplace_scale"])
+    rows, tok = tiny_rows(prm, 30, seed=4)
+    enc = codec.encode(rows, tok, prm, pl)
+    assert codec.encode(rows, tok, lin, pl).data == enc.data
+    full = codec.decode(enc.data, tok, prm, pl)
+    part = codec.decode(enc.data, tok, lin, pl)
+    assert np.array_equal(part.yhat_b, full.yhat_b)
+    assert part.h_b.shape[1] == 0
+    corr = bf16.to_f64(full.h_b) @ bf16.to_f64(prm["w2"]).T
+    assert np.max(np.abs(corr)) > 1e-3  # the correction is not trivially zero here
+    np.testing.assert_allclose(full.xhat - part.xhat, corr, rtol=1e-12, atol=1e-12)
+    # kept rows do not depend on the codec
+    _, kept_t, _ = codec.split_positions(30, 1, 2)
+    assert np.array_equal(full.rows[kept_t], part.rows[kept_t])
+
+
 # ----------------------------------------------------------------------------
 # stream validation
 # ----------------------------------------------------------------------------
