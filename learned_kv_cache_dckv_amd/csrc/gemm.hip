@@ -49,8 +49,8 @@
 //   synthesis   rotate-half RoPE on key heads; the tile's columns are ordered
 //               so that every pair (d, d+128) sits in one lane and register
 //               of blocks nb and nb+2 -> bf16 rows
-// bf16 outputs go through a per-wave LDS transpose so global stores are
-// 16-byte row segments.
+// Synthesis is persistent: a wave keeps most of its bf16 output tile in
+// registers and stores it during the next tile's main loop.
 #include <cmath>
 
 #include "dckv_internal.h"
@@ -70,9 +70,11 @@ constexpr int kThreads = 256;
 constexpr int kStages = 2;
 constexpr int kRowBytes = kBK * 2;                        // 128 B per staged row
 constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 64 KiB per stage
-constexpr int kOutStride = 128 + 8;                       // bf16 per row of a wave's output tile
-constexpr int kOutWaveBytes = 128 * kOutStride * 2;
-constexpr int kXchOff = 4 * kOutWaveBytes;                // row-0 exchange between the two wave rows
+// after the main loop the quantiser reuses LDS for its token ids (512 B per
+// wave) and its even rows' yhat (32 KiB per wave); the row-0 exchange between
+// the two wave rows sits above both
+constexpr int kQuantEpiBytes = 4 * 512 + 4 * 16 * 2 * 64 * 16;
+constexpr int kXchOff = kQuantEpiBytes > kStages * kStageBytes ? kQuantEpiBytes : kStages * kStageBytes;
 constexpr int kLdsBytes = kXchOff + 2 * 256 * 4;
 static_assert(kStages * kStageBytes <= kXchOff, "stages must not overlap the exchange area");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
@@ -321,28 +323,6 @@ __device__ __forceinline__ float acc_get(const f32x16 &b, int v) {
 // Row (within the wave tile) of register v of block row mb in this lane.
 __device__ __forceinline__ int acc_row(int mb, int v, int lane) { return mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
-// ---------------------------------------------------------------------------
-// bf16 output through a per-wave LDS transpose
-// ---------------------------------------------------------------------------
-// The caller writes its 128x128 values (bf16) to the wave's LDS tile with
-// put_rows2(); flush_rows() then stores 16-byte row segments: LDS columns
-// [0, 64) go to out[row][col_lo + c], columns [64, 128) to
-// out[row][col_hi + c - 64].
-
-// Rows r and r + 1 of this lane's column tcol (y0, y1) into the wave's LDS
-// tile: one conversion packs both, then the low half goes to row r and the
-// high half to row r + 1 (two 16-bit LDS stores; the two half-waves, rows 4
-// apart, write disjoint bank ranges).
-// wbase is the lane's origin in the tile (row 4 (lane / 32), column lane % 32),
-// crow and ccol compile-time offsets, so both stores use immediate offsets.
-__device__ __forceinline__ char *wtile_base(char *wtile, int lane) {
-  return wtile + ((4 * (lane >> 5)) * kOutStride + (lane & 31)) * 2;
-}
-__device__ __forceinline__ void put_rows2(char *wbase, int crow, int ccol, float y0, float y1) {
-  const uint32_t pk = pack_bf16x2(y0, y1);
-  *reinterpret_cast<uint16_t *>(wbase + (crow * kOutStride + ccol) * 2) = (uint16_t)pk;
-  *reinterpret_cast<uint16_t *>(wbase + ((crow + 1) * kOutStride + ccol) * 2) = (uint16_t)(pk >> 16);
-}
 // the constant part of acc_row(): row of register v of block mb without the lane term
 __device__ __forceinline__ constexpr int acc_crow(int mb, int v) { return mb * 32 + 8 * (v >> 2) + (v & 3); }
 
@@ -352,20 +332,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ void flush_rows(const char *wtile, uint16_t *out, int64_t ld, int64_t row0, int64_t col_lo,
-                                           int64_t col_hi, int64_t rows_valid) {
-  const int lane = epilogue_lane();
-  const int seg = lane & 15;
-  const int64_t col = seg < 8 ? col_lo + seg * 8 : col_hi + (seg - 8) * 8;
-#pragma unroll 4
-  for (int it = 0; it < 32; ++it) {
-    const int r = it * 4 + (lane >> 4);
-    if (row0 + r < rows_valid) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(wtile + (r * kOutStride + seg * 8) * 2);
-      *reinterpret_cast<uint4 *>(out + (size_t)(row0 + r) * ld + col) = v;
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // operand setup helpers
@@ -547,7 +513,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   // rows' yhat of its 16 blocks [block][e / 4][lane] (16 bytes each)
   int32_t *ltok = reinterpret_cast<int32_t *>(lds) + wave * 128;
   f32x4 *lyh = reinterpret_cast<f32x4 *>(lds + 4 * 512) + wave * 16 * 2 * 64;
-  static_assert(4 * 512 + 4 * 16 * 2 * 64 * 16 <= kXchOff, "epilogue LDS must not overlap the exchange area");
+  static_assert(4 * 512 + 4 * 16 * 2 * 64 * 16 <= kQuantEpiBytes, "epilogue LDS must not overlap the exchange area");
   {
     uint32_t tmax = 0u;
 #pragma unroll
@@ -927,25 +893,6 @@ __global__ __launch_bounds__(kDeqThreads) void k_dequant(DeqP P) {
   }
 }
 
-// bf16 of fn(value) for all 128x128 values of the wave into its LDS tile
-// (identity columns), one accumulator block at a time
-template <class F>
-__device__ __forceinline__ void acc_to_wtile(const f32x16 (&acc)[4][4], char *wtile, int, F &&fn) {
-  char *wbase = wtile_base(wtile, epilogue_lane());
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const f32x16 b = acc_block(acc, mb, nb);
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) put_rows2(wbase, acc_crow(mb, v), nb * 32, fn(b[v]), fn(b[v + 1]));
-      __builtin_amdgcn_sched_barrier(0);  // one block at a time: bounded live ranges
-    }
-}
-
-struct Identity {
-  __device__ float operator()(float x) const { return x; }
-};
 
 // kept row k: RoPE on the key columns of the verbatim row in the stream
 __device__ __forceinline__ void kept_rope_row(int64_t k, const uint8_t *stream, const float2 *lo, const float2 *hi,
@@ -1062,7 +1009,6 @@ struct SynP {
   uint16_t *out;                     // rows_out [T][D]
   int64_t N;
   int keep_head, n_mt, n_nt;
-  int KT;                            // k-tiles: 36 with the correction, 32 for the linear codec
   int32_t *status;
 };
 
@@ -1106,6 +1052,7 @@ constexpr int kSynDefer = 96;             // words held over (the rest are store
 constexpr int kSynPeel = kSynDefer / 8;    // k-tiles that store them, 8 each
 static_assert(kC / kBK >= kSynPeel, "synthesis main loop shorter than the store spread");
 
+template <int KT>  // k-tiles: 36 with the correction, 32 for the linear codec
 __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   if (wg_stop(P.status)) return;
@@ -1142,9 +1089,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
     }
     f32x16 acc[4][4];
     if (have)
-      mainloop<true, kSynPeel>(A, B, P.KT, acc, lds, store_pend);
+      mainloop<true, kSynPeel>(A, B, KT, acc, lds, store_pend);
     else
-      mainloop(A, B, P.KT, acc, lds);
+      mainloop(A, B, KT, acc, lds);
 
     const int lane = epilogue_lane();
     const bool is_key = (head & 3) < 2;  // per layer: 2 key heads, then 2 value heads
@@ -1378,7 +1325,6 @@ void launch_synthesis_gemm(const DecodeArgs &a) {
   P.keep_head = a.p->keep_head;
   P.n_mt = (int)a.g.n_mtiles;
   P.n_nt = kD / kBN;
-  P.KT = (kC + (a.p->W1 ? kHid : 0)) / kBK;
   P.status = a.status;
   // persistent: one workgroup per CU at most
   static int n_cu = 0;
@@ -1390,7 +1336,11 @@ void launch_synthesis_gemm(const DecodeArgs &a) {
     else
       n_cu = 256;
   }
-  launch_gemm(k_synthesis, "synthesis_gemm", std::min(P.n_mt * P.n_nt, n_cu), P, a.s);
+  const int grid = std::min(P.n_mt * P.n_nt, n_cu);
+  if (a.p->W1)
+    launch_gemm(k_synthesis<(kC + kHid) / kBK>, "synthesis_gemm", grid, P, a.s);
+  else
+    launch_gemm(k_synthesis<kC / kBK>, "synthesis_gemm", grid, P, a.s);
 }
 
 }  // namespace dckv
