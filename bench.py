@@ -225,6 +225,70 @@ def rate_ladder(cfg: int, steps: int) -> int:
     return 0
 
 
+def fit_bench(cfg: int, n: int, steps: int, cpu: bool) -> int:
+    """The closed-form fit of the conditional models on n calibration rows
+    (the first coded rows of the workload), GPU against the oracle."""
+    import torch
+    import dckv_synth as synth
+    import learned_kv_cache_dckv_amd as dk
+    dev = torch.device("cuda:0")
+    w = synth.world()
+    req = synth.make_request(cfg, n_rows=n + 4)
+    rows_h = np.ascontiguousarray(req.rows[4:4 + n])
+    tok_h = np.ascontiguousarray(req.token_ids[4:4 + n].astype(np.int32))
+    codec = dk.Codec(w.params(), device=dev)
+    rows = torch.from_numpy(rows_h.view(np.int16)).to(dev)
+    tok = torch.from_numpy(tok_h).to(dev)
+    ridge = 1e-3
+    H = torch.empty((2048, 2048), dtype=torch.float32, device=dev)
+    Hb = torch.empty((2048, 2048), dtype=torch.int16, device=dev)
+    a = torch.empty(2048, dtype=torch.float32, device=dev)
+    b = torch.empty(2048, dtype=torch.float32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(dk.dckv_fit_bytes(n), dtype=torch.uint8, device=dev)
+
+    def run():
+        dk.dckv_fit(codec, rows, tok, ridge, H, Hb, a, b, st, ws)
+
+    run()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        run()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert int(st.item()) == 0
+    dk.dckv_profile_reset()
+    dk.dckv_profile_only("fit_gemm")
+    dk.dckv_profile_enable(True)
+    run()
+    torch.cuda.synchronize()
+    dk.dckv_profile_enable(False)
+    dk.dckv_profile_only(None)
+    gemm_ms, launches = dk.dckv_profile_read("fit_gemm")
+    C = D = 2048
+    gemm_flop = 2.0 * n * 6144 * C + 2.0 * D * D * n + 2.0 * D * C * 2 * n + 2.0 * n * D * C
+    solve_flop = D ** 3 / 3.0 + 2.0 * D * D * C
+    res = {"metric": "closed-form fit of the conditional models (ms per fit)", "n_rows": n, "ridge": ridge,
+           "ms": ms, "gemm_ms": gemm_ms, "gemm_launches": launches,
+           "gemm_tflops": gemm_flop / (gemm_ms * 1e-3) / 1e12,
+           "gemm_frac": gemm_flop / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "solve_and_rest_ms": ms - gemm_ms, "solve_gflop": solve_flop / 1e9, "cpu_baseline": None}
+    if cpu:
+        from oracle import fit as ofit
+        t0 = time.perf_counter()
+        f = ofit.fit(rows_h, tok_h, w.params(), ridge)
+        cpu_s = time.perf_counter() - t0
+        rel = float(np.linalg.norm(H.cpu().numpy() - f.H) / np.linalg.norm(f.H))
+        res["cpu_baseline"] = {"ms": cpu_s * 1e3, "kind": "oracle", "cores": len(os.sched_getaffinity(0)),
+                               "sample": "the same %d rows, numpy float64" % n, "H_rel_l2": rel}
+    print(json.dumps(res))
+    return 0
+
+
 def vendor_gemm(N: int, steps: int) -> int:
     """The vendor library's plain bf16 GEMMs (torch.matmul: hipBLASLt) on the
     codec's GEMM shapes, for comparison with the fused kernels' main loops.
@@ -270,6 +334,8 @@ def main(argv=None) -> int:
                     help="time the vendor library's plain GEMMs on the same shapes, then exit")
     ap.add_argument("--codec", choices=("dckv", "linear"), default="dckv",
                     help="linear: the codec without the GELU correction")
+    ap.add_argument("--fit", type=int, default=0, metavar="N_ROWS",
+                    help="time the closed-form fit of the conditional models on N_ROWS calibration rows, then exit")
     ap.add_argument("--rate-ladder", action="store_true",
                     help="bytes/token and rates at each rate setting, both codecs, then exit")
     args = ap.parse_args(argv)
@@ -277,6 +343,8 @@ def main(argv=None) -> int:
         import dckv_synth as synth
         T = synth.CONFIGS[args.config]["T"]
         return vendor_gemm(T - 132, args.steps)
+    if args.fit:
+        return fit_bench(args.config, args.fit, args.steps, not args.no_cpu_baseline)
     if args.rate_ladder:
         return rate_ladder(args.config, args.steps)
     if args.write_traffic:

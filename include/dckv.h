@@ -272,6 +272,34 @@ int dckv_profile_only(const char *kernel);
 int dckv_profile_reset(void);
 int dckv_profile_read(const char *kernel, double *total_ms, int64_t *launches);
 
+/* ---------------------------------------------------------------------------
+ * Closed-form fit of the conditional models to a trained codec (DCKV digest,
+ * Evidence: fitting them in closed form recovers a saving close to joint
+ * training).  The page names no estimator; these are the plainest closed
+ * forms for the models of "How it works", Conditional entropy models:
+ *   - calibration: n consecutive coded rows x_j [n][D] (bf16) of one prompt
+ *     with their token ids; y_j = A x_j, e_j = E[tok_j];
+ *   - mean head, ridge least squares over all rows:
+ *       H^T = (E^T E + ridge * n * I)^-1 E^T Y   -> mean_head_out, fp32
+ *     [n_coef][emb_dim] (may be NULL) and mean_head_bf16_out, its bf16
+ *     rounding, the form a plan takes (may be NULL);
+ *   - with m_j = bf16(H) e_j and, for odd j, s_j = y_{j-1} + y_{j+1}
+ *     (y_n = 0): nbr_weight_out[c] = sum r s / sum s^2 over the odd rows,
+ *     r = y - m (0 if sum s^2 = 0);
+ *   - laplace_scale_out[c] = mean over all rows of |y - mu|, mu = m, plus
+ *     a s on odd rows (the Laplace maximum-likelihood scale).
+ * Outputs are device arrays.  Uses analysis and embedding of p (its other
+ * pointers may be NULL).  The fit runs in fp32 on bf16 MFMA products
+ * (E^T Y keeps 16 mantissa bits of Y) with a blocked Cholesky solve; a Gram
+ * matrix plus ridge that is not positive definite, or a token id outside
+ * [0, vocab), sets *status to DCKV_EINVAL.  The workspace (dckv_fit_bytes)
+ * is about 28 KiB per calibration row plus 42 MiB.  2 <= n <= 2^22.
+ * --------------------------------------------------------------------------*/
+int dckv_fit_bytes(int64_t n, uint64_t *workspace_bytes);
+int dckv_fit(const dckv_params *p, const uint16_t *rows, const int32_t *token_ids, int64_t n, float ridge,
+             float *mean_head_out, uint16_t *mean_head_bf16_out, float *nbr_weight_out, float *laplace_scale_out,
+             int32_t *status, void *workspace, uint64_t workspace_bytes, void *hip_stream);
+
 const char *dckv_last_error(void);
 
 /* Stream layout, version 1 (little endian, sections contiguous, no padding):

@@ -28,7 +28,7 @@ EXPORTS = ("dckv_plan_tables", "dckv_plan", "dckv_plan_free", "dckv_plan_info", 
            "dckv_bytes", "dckv_encode",
            "dckv_decode", "dckv_bytes_batch", "dckv_encode_batch", "dckv_decode_batch", "dckv_entropy_encode",
            "dckv_entropy_decode", "dckv_workspace_view", "dckv_profile_enable", "dckv_profile_only", "dckv_profile_reset",
-           "dckv_profile_read", "dckv_last_error")
+           "dckv_profile_read", "dckv_fit_bytes", "dckv_fit", "dckv_last_error")
 
 
 class DckvError(RuntimeError):
@@ -81,6 +81,8 @@ def _load():
         "dckv_profile_only": [ctypes.c_char_p],
         "dckv_profile_reset": [],
         "dckv_profile_read": [ctypes.c_char_p, P, P],
+        "dckv_fit_bytes": [I64, P],
+        "dckv_fit": [P, P, P, I64, F, P, P, P, P, P, P, U64, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -356,6 +358,39 @@ def dckv_entropy_decode(plan: Plan, stream_buf, n_bytes: int, T: int, sym_out, n
                         stream=None):
     _check(_lib.dckv_entropy_decode(plan.handle, _ptr(stream_buf), int(n_bytes), int(T), _ptr(sym_out),
                                     _ptr(n_esc_out), _ptr(status), _ptr(ws), ws.numel(), _stream_handle(stream)))
+
+
+def dckv_fit_bytes(n: int) -> int:
+    v = ctypes.c_uint64()
+    _check(_lib.dckv_fit_bytes(int(n), ctypes.byref(v)))
+    return v.value
+
+
+def dckv_fit(codec: "Codec", rows, token_ids, ridge: float, mean_head_out, mean_head_bf16_out, nbr_weight_out,
+             laplace_scale_out, status, ws, stream=None):
+    n = int(token_ids.shape[0])
+    prm = codec.c_params()
+    _check(_lib.dckv_fit(ctypes.byref(prm), _ptr(rows), _ptr(token_ids), n, float(ridge), _ptr(mean_head_out),
+                         _ptr(mean_head_bf16_out), _ptr(nbr_weight_out), _ptr(laplace_scale_out), _ptr(status),
+                         _ptr(ws), ws.numel(), _stream_handle(stream)))
+
+
+def fit(codec: "Codec", rows, token_ids, ridge: float):
+    """Closed-form fit of the conditional models from calibration rows (device
+    bf16 bits [n][D]) and token ids (device int32 [n]); returns (mean head fp32
+    [n_coef][emb], its bf16 bits, neighbour weights, Laplace scales, status)."""
+    import torch
+    dev = codec.device
+    n = int(token_ids.shape[0])
+    H = torch.empty((codec.n_coef, codec.emb_dim), dtype=torch.float32, device=dev)
+    Hb = torch.empty((codec.n_coef, codec.emb_dim), dtype=torch.int16, device=dev)
+    a = torch.empty(codec.n_coef, dtype=torch.float32, device=dev)
+    b = torch.empty(codec.n_coef, dtype=torch.float32, device=dev)
+    st = torch.full((1,), 777, dtype=torch.int32, device=dev)
+    ws = torch.empty(dckv_fit_bytes(n), dtype=torch.uint8, device=dev)
+    dckv_fit(codec, rows, token_ids, ridge, H, Hb, a, b, st, ws)
+    torch.cuda.synchronize()
+    return H, Hb, a, b, int(st.item())
 
 
 def dckv_workspace_view(plan: Plan, T: int, which: int):

@@ -2,15 +2,18 @@
 // sequence of each call.  Every call only enqueues work on the caller's HIP
 // stream; nothing here allocates device memory.
 //
-// Encode (DCKV digest page, "How it works"): kept rows copied verbatim ->
-// embedding mean H E[tok] -> analysis GEMM with the quantiser (even rows, then
-// odd rows with both reconstructed neighbours) -> fix-up of the odd row at
-// each tile edge -> escape ordering -> rANS per group -> group offsets and
-// header -> packing.
-// Decode: parse and validate -> rANS per group -> mean GEMM with the two
-// dequantisation passes -> fix-up -> correction hidden layer -> synthesis with
-// RoPE -> RoPE of the kept rows.
+// Encode (DCKV digest page, "How it works"): control words and kept rows ->
+// analysis GEMM with the quantiser (means from the plan's embedding-mean
+// table; even rows, then odd rows with both reconstructed neighbours;
+// escape records) -> fix-up of the odd row at each tile edge -> rANS per
+// group -> escape sort, group offsets and header -> packing.
+// Decode: parse and validate (and the RoPE tables) -> rANS per group -> the
+// two dequantisation passes -> correction hidden layer (and RoPE of the kept
+// rows) -> synthesis with RoPE.
+// Fit (DCKV digest page, Evidence): the closed-form fit of the conditional
+// models from calibration rows.
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 
@@ -221,4 +224,53 @@ extern "C" int dckv_entropy_decode(const dckv_plan_t *plan, const uint8_t *strea
   launch_rans_decode(a);
   launch_sym_from_tiled(a, sym_out, n_esc_out);
   return after_launch("dckv_entropy_decode");
+}
+
+extern "C" int dckv_fit_bytes(int64_t n, uint64_t *workspace_bytes) {
+  if (n < 2 || n > (int64_t)1 << 22) return set_error(DCKV_EINVAL, "fit: n must be in [2, 2^22]");
+  if (!workspace_bytes) return set_error(DCKV_EINVAL, "fit: null workspace_bytes");
+  *workspace_bytes = fit_layout(n).total;
+  return DCKV_OK;
+}
+
+extern "C" int dckv_fit(const dckv_params *p, const uint16_t *rows, const int32_t *token_ids, int64_t n, float ridge,
+                        float *mean_head_out, uint16_t *mean_head_bf16_out, float *nbr_weight_out,
+                        float *laplace_scale_out, int32_t *status, void *workspace, uint64_t workspace_bytes,
+                        void *hip_stream) {
+  if (!p) return set_error(DCKV_EINVAL, "fit: null params");
+  if (p->n_layers != 6 || p->n_kv_heads != 2 || p->head_dim != kHeadDim || p->n_coef != kC || p->emb_dim != kEmb)
+    return set_error(DCKV_EUNSUPPORTED,
+                     "fit: the kernels support n_layers=6, n_kv_heads=2, head_dim=256, n_coef=2048, emb_dim=2048");
+  if (!p->analysis || !p->embedding || p->vocab < 1) return set_error(DCKV_EINVAL, "fit: null analysis or embedding");
+  uint64_t need = 0;
+  int rc = dckv_fit_bytes(n, &need);
+  if (rc) return rc;
+  if (!rows || !aligned(rows, 16) || !token_ids || !aligned(token_ids, 4))
+    return set_error(DCKV_EINVAL, "fit: rows must be 16-byte aligned, token_ids 4-byte aligned");
+  if (!(ridge >= 0.0f) || !std::isfinite(ridge)) return set_error(DCKV_EINVAL, "fit: ridge must be finite and >= 0");
+  if (!nbr_weight_out || !laplace_scale_out || !aligned(nbr_weight_out, 4) || !aligned(laplace_scale_out, 4))
+    return set_error(DCKV_EINVAL, "fit: null or misaligned nbr_weight_out / laplace_scale_out");
+  if ((mean_head_out && !aligned(mean_head_out, 4)) || (mean_head_bf16_out && !aligned(mean_head_bf16_out, 2)))
+    return set_error(DCKV_EINVAL, "fit: misaligned mean head output");
+  if (!status || !aligned(status, 4)) return set_error(DCKV_EINVAL, "fit: status must be a 4-byte aligned device word");
+  if (!workspace || !aligned(workspace, 256)) return set_error(DCKV_EINVAL, "fit: workspace must be 256-byte aligned");
+  if (workspace_bytes < need) return set_error(DCKV_ECAPACITY, "fit: workspace smaller than dckv_fit_bytes()");
+  FitArgs a;
+  a.l = fit_layout(n);
+  a.ws = static_cast<uint8_t *>(workspace);
+  a.rows = rows;
+  a.A = p->analysis;
+  a.E = p->embedding;
+  a.tok = token_ids;
+  a.n = n;
+  a.vocab = p->vocab;
+  a.ridge = ridge;
+  a.H_out = mean_head_out;
+  a.Hb_out = mean_head_bf16_out;
+  a.a_out = nbr_weight_out;
+  a.b_out = laplace_scale_out;
+  a.status = status;
+  a.s = static_cast<hipStream_t>(hip_stream);
+  fit_sequence(a);
+  return after_launch("dckv_fit");
 }

@@ -163,6 +163,45 @@ void launch_sym_from_tiled(const DecodeArgs &a, uint8_t *sym_out, uint32_t *n_es
 
 // gemm.hip
 int build_mean_table(dckv_plan_t *p);  // at plan time: fills p->mtab, synchronous
+
+// C[m][n] = sum_k A[m][k] B[n][k], bf16 operands (k contiguous), fp32 output.
+// k-tiles [0, split) read a0 / b0, the rest a1 / b1 (row bytes lda*, ldb*);
+// A's row m is arow[m] when arow is set.  K = 64 KT; N a multiple of 8 tiles
+// of 256 or at most 8 of them (the tile order's grouping).
+struct GemmF32Args {
+  const uint16_t *a0, *a1, *b0, *b1;
+  uint32_t lda0, lda1, ldb0, ldb1;
+  int split, KT;
+  const int32_t *arow;
+  int M, N;
+  float *c;
+  int64_t ldc;
+  int n_mt, n_nt;  // set by the launcher
+};
+void launch_gemm_f32(const GemmF32Args &args, hipStream_t s);
+
+// fit.hip: the closed-form fit of the conditional models
+constexpr int kFitChunks = 64;  // row chunks of the per-component sums
+struct FitLayout {
+  int64_t n_pad = 0;  // n rounded up to 64 (the inner dimension of the Gram products)
+  uint64_t Y = 0, M = 0, Yhi = 0, Ylo = 0, Et = 0, G = 0, R = 0, Hb = 0, tokc = 0, part = 0, dg = 0, linv = 0, total = 0;
+};
+FitLayout fit_layout(int64_t n);
+struct FitArgs {
+  FitLayout l;
+  uint8_t *ws;
+  const uint16_t *rows, *A, *E;
+  const int32_t *tok;
+  int64_t n;
+  int vocab;
+  float ridge;
+  float *H_out;       // may be null
+  uint16_t *Hb_out;   // may be null
+  float *a_out, *b_out;
+  int32_t *status;
+  hipStream_t s;
+};
+void fit_sequence(const FitArgs &a);
 void launch_analysis_gemm(const EncodeArgs &a);
 void launch_encode_fixup(const EncodeArgs &a);
 void launch_dequant(const DecodeArgs &a);

@@ -392,6 +392,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_mean_table(MeanTabP P) {
 }
 
 // ---------------------------------------------------------------------------
+// fit: C[m][n] = sum_k A[m][k] B[n][k] with fp32 output (bf16 operands, two
+// k-ranges per operand, optional row gather for A)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_f32(GemmF32Args P) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  int mt, nt;
+  tile_of(blockIdx.x, P.n_mt * P.n_nt, P.n_nt, mt, nt);
+  const int m0 = mt * kBM, n0 = nt * kBN;
+  Operand A, B;
+  set_sources(A, P.a0, P.lda0, P.a1, P.lda1, P.split);
+  set_sources(B, P.b0, P.ldb0, P.b1, P.ldb1, P.split);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = min(m0 + staged_row(i), P.M - 1);
+    A.row[i] = (uint32_t)(P.arow ? P.arow[m] : m);
+    B.row[i] = (uint32_t)min(n0 + staged_row(i), P.N - 1);
+  }
+  f32x16 acc[4][4];
+  mainloop(A, B, P.KT, acc, lds);
+  const int lane = epilogue_lane(), wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int col = n0 + wn * 128 + nb * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * 128 + acc_row(mb, v, lane);
+        if (row < P.M && col < P.N) P.c[(size_t)row * P.ldc + col] = acc_get(acc[mb][nb], v);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // encode: analysis GEMM + quantiser (two checkerboard passes)
 // ---------------------------------------------------------------------------
 struct QuantP {
@@ -1190,6 +1226,13 @@ static void launch_gemm(K kernel, const char *name, int grid, const P &prm, hipS
                             kLdsBytes);
   KernelTimer tm(name, s);
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), kLdsBytes, s, prm);
+}
+
+void launch_gemm_f32(const GemmF32Args &args, hipStream_t s) {
+  GemmF32Args P = args;
+  P.n_mt = (P.M + kBM - 1) / kBM;
+  P.n_nt = (P.N + kBN - 1) / kBN;
+  launch_gemm(k_gemm_f32, "fit_gemm", P.n_mt * P.n_nt, P, s);
 }
 
 int build_mean_table(dckv_plan_t *p) {

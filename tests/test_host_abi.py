@@ -67,3 +67,20 @@ def test_plan_tables_rejects_bad_input():
         dk.dckv_plan_tables(np.array([1.0, -1.0], np.float32), np.ones(2, np.float32), 0.1)
     with pytest.raises(dk.DckvError):
         dk.dckv_plan_tables(np.ones(2, np.float32), np.array([1.0, np.nan], np.float32), 0.1)
+
+
+def test_fit_workspace_size_and_bounds():
+    dk = _lib()
+    with pytest.raises(dk.DckvError):
+        dk.dckv_fit_bytes(1)
+    with pytest.raises(dk.DckvError):
+        dk.dckv_fit_bytes((1 << 22) + 1)
+    # per row: fp32 coefficients and means (16 KiB), two bf16 halves of the
+    # coefficients and the gathered embeddings (12 KiB), the checked id; fixed:
+    # Gram and right-hand sides (32 MiB), bf16 head (8 MiB), partial sums,
+    # the diagonal
+    n = 4096
+    got = dk.dckv_fit_bytes(n)
+    per_row = 2048 * 4 * 2 + 2048 * 2 * 3 + 4
+    fixed = 2048 * 2048 * 4 * 2 + 2048 * 2048 * 2 + 64 * 2 * 2048 * 8 + 2048 * 4
+    assert fixed + per_row * n <= got <= fixed + per_row * n + 11 * 256
