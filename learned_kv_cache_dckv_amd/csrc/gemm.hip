@@ -39,7 +39,7 @@
 //   quantise    analysis GEMM; epilogue: even rows r = (y - mu)/step,
 //               q = rint(r), yhat = mu + q step; then odd rows with
 //               mu += a (yhat_{j-1} + yhat_{j+1}); mu comes from the table
-//               straight into registers, four accumulator blocks ahead; the
+//               straight into registers, six accumulator blocks ahead; the
 //               first row of the lower wave crosses waves through LDS, the
 //               last odd row of a tile is finished by a small fix-up kernel
 //   dequant     no GEMM: yhat = mu + q step in the same two passes, streamed
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   // The epilogue works one 32x32 accumulator block at a time.  Each value
   // first takes a short path that assumes a coded row, an active rank, a
   // finite difference and no escape; a block where any of that fails (rare)
-  // is decided again in full.  The means of a block are loaded four blocks
+  // is decided again in full.  The means of a block are loaded six blocks
   // ahead, straight from the table into registers.  The even rows' symbols
   // wait in registers for pass 2, which writes whole symbol words.
   const int lane = epilogue_lane();
@@ -565,9 +565,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   }
   const rsrc_t mr = span_rsrc(P.mtab, (uint32_t)P.vocab * (uint32_t)(kC * 4));
   const uint32_t colb = (uint32_t)(n0 + wn * 128 + (lane & 31)) * 4u;
-  // block row br = 4 parity + mb (0..7); its tokens are read from LDS one
-  // block row before its means are requested, which is one block row before
-  // they are used
+  // block row br = 4 parity + mb (0..7); its tokens are read from LDS two
+  // block rows before it (at least two blocks before its first means are
+  // requested, kAhead blocks before they are used)
   int tq[2][8];
   auto read_tok = [&](int br) {
     const int4 *src = reinterpret_cast<const int4 *>(ltok + (((lane >> 5) * 4 + (br & 3)) * 2 + (br >> 2)) * 8);
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
     d[0] = t0.x; d[1] = t0.y; d[2] = t0.z; d[3] = t0.w;
     d[4] = t1.x; d[5] = t1.y; d[6] = t1.z; d[7] = t1.w;
   };
-  constexpr int kAhead = 4;
+  constexpr int kAhead = 6;
   float mq[kAhead][8];
   // means of block k of the 32 in epilogue order (block row k / 4, nb = k % 4)
   auto issue = [&](int k) {
@@ -589,9 +589,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   };
   static_assert(kC * 4 == 1 << 13, "table row bytes");
   read_tok(0);
+  read_tok(1);
 #pragma unroll
   for (int k = 0; k < kAhead; ++k) issue(k);
-  read_tok(1);
 
   uint32_t nonfin = 0u;  // 1 once a coded value's difference is not finite
   const uint32_t esc_cap = (uint32_t)min<int64_t>(P.esc_cap, 0x7FFFFFFF);
