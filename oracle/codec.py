@@ -234,6 +234,14 @@ def rope(x: np.ndarray, t: np.ndarray, sh: Shape) -> np.ndarray:
     return out
 
 
+def unrope(x: np.ndarray, t: np.ndarray, sh: Shape) -> np.ndarray:
+    """The inverse of rope(): the key columns rotated back by the angles of
+    positions t (float64).  Encoding a post-RoPE cache takes its rows through
+    this first (first paragraph of "How it works": keys are coded before
+    RoPE)."""
+    return rope(x, -np.asarray(t, dtype=np.float64), sh)
+
+
 @dataclass
 class Decoded:
     rows: np.ndarray     # uint16 bf16 [T][D]

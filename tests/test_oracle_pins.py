@@ -393,6 +393,24 @@ def test_rope_closed_forms():
             np.testing.assert_allclose(n0, n1, rtol=1e-12)
 
 
+def test_unrope_inverts_rope_and_leaves_values():
+    prm = tiny_params(seed=14, n_layers=2, n_kv_heads=2, head_dim=8)
+    sh = codec.shape_of(prm)
+    rng = np.random.default_rng(5)
+    x = rng.normal(0, 1, (9, sh.D))
+    t = np.arange(100, 109)
+    np.testing.assert_allclose(codec.unrope(codec.rope(x, t, sh), t, sh), x, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(codec.rope(codec.unrope(x, t, sh), t, sh), x, rtol=0, atol=1e-12)
+    u = codec.unrope(x, t, sh)
+    # value columns are untouched; the rotation keeps each key pair's norm
+    for l in range(2):
+        vb = (l * 2 + 1) * 2 * 8
+        np.testing.assert_array_equal(u[:, vb:vb + 16], x[:, vb:vb + 16])
+        kb = l * 2 * 2 * 8
+        pairs = lambda a: a[:, kb:kb + 4] ** 2 + a[:, kb + 4:kb + 8] ** 2
+        np.testing.assert_allclose(pairs(u), pairs(x), rtol=1e-12)
+
+
 def test_matmul_orientation_against_triple_loop():
     prm = tiny_params(seed=12, n_coef=4, head_dim=2, n_layers=1, n_kv_heads=1)
     X = np.random.default_rng(0).standard_normal((3, 4))
