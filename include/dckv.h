@@ -178,6 +178,30 @@ int dckv_decode(const dckv_plan_t *plan, const uint8_t *stream, uint64_t stream_
                 void *workspace, uint64_t workspace_bytes, void *hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * dckv_decode_heads: dckv_decode into the attention layers' cache layout
+ * instead of rows.  kv_out (host array of 2 * n_layers device pointers):
+ * kv_out[2 l + kv] (kv = 0 keys, 1 values) receives a bf16 [n_kv_heads][T]
+ * [head_dim] matrix, the columns ((l 2 + kv) n_kv_heads + h) head_dim + d of
+ * every decoded row (keys with RoPE reapplied).  Same values as dckv_decode;
+ * each matrix 16-byte aligned, caller-owned.  (The cache-layout integration
+ * next to the hot path: the decoded cache lands where the attention reads it.)
+ * --------------------------------------------------------------------------*/
+int dckv_decode_heads(const dckv_plan_t *plan, const uint8_t *stream, uint64_t stream_bytes,
+                      const int32_t *token_ids, int64_t T, uint16_t *const *kv_out, int32_t *status,
+                      void *workspace, uint64_t workspace_bytes, void *hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * dckv_unrope: the inverse of the RoPE that dckv_decode reapplies, so that a
+ * post-RoPE cache can be encoded (DCKV digest, "How it works", first
+ * paragraph: keys are coded before RoPE).  rows_in [T][D] bf16 at positions
+ * 0..T-1 -> rows_out [T][D]: on the key columns (x0, x1) = (p0 c + p1 s,
+ * p1 c - p0 s) for the pair (d, d + head_dim/2) at angle t w_d, computed in
+ * fp64 and rounded once to bf16; value columns copied.  rows_out may equal
+ * rows_in.  4-byte aligned device arrays.  Asynchronous on hip_stream.
+ * --------------------------------------------------------------------------*/
+int dckv_unrope(const dckv_plan_t *plan, const uint16_t *rows_in, int64_t T, uint16_t *rows_out, void *hip_stream);
+
+/* ---------------------------------------------------------------------------
  * Batches of independent requests in one call (DCKV digest, "How it works":
  * every request is coded on its own; "Limits": the pages code one request at a
  * time, so a batch is our extension).

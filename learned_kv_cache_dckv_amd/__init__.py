@@ -26,7 +26,7 @@ VIEW_SYMBOLS, VIEW_YHAT_B, VIEW_H_B = 0, 1, 2
 # every symbol include/dckv.h declares
 EXPORTS = ("dckv_plan_tables", "dckv_plan", "dckv_plan_free", "dckv_plan_info", "dckv_plan_mean_table",
            "dckv_bytes", "dckv_encode",
-           "dckv_decode", "dckv_bytes_batch", "dckv_encode_batch", "dckv_decode_batch", "dckv_entropy_encode",
+           "dckv_decode", "dckv_decode_heads", "dckv_unrope", "dckv_bytes_batch", "dckv_encode_batch", "dckv_decode_batch", "dckv_entropy_encode",
            "dckv_entropy_decode", "dckv_workspace_view", "dckv_profile_enable", "dckv_profile_only", "dckv_profile_reset",
            "dckv_profile_read", "dckv_fit_bytes", "dckv_fit", "dckv_last_error")
 
@@ -71,6 +71,8 @@ def _load():
         "dckv_bytes": [P, I64, P, P],
         "dckv_encode": [P, P, P, I64, P, U64, P, P, P, U64, P],
         "dckv_decode": [P, P, U64, P, I64, P, P, P, U64, P],
+        "dckv_decode_heads": [P, P, U64, P, I64, P, P, P, U64, P],
+        "dckv_unrope": [P, P, I64, P, P],
         "dckv_bytes_batch": [P, I32, P],
         "dckv_encode_batch": [P, I32, P, U64, P],
         "dckv_decode_batch": [P, I32, P, U64, P],
@@ -358,6 +360,34 @@ def dckv_entropy_decode(plan: Plan, stream_buf, n_bytes: int, T: int, sym_out, n
                         stream=None):
     _check(_lib.dckv_entropy_decode(plan.handle, _ptr(stream_buf), int(n_bytes), int(T), _ptr(sym_out),
                                     _ptr(n_esc_out), _ptr(status), _ptr(ws), ws.numel(), _stream_handle(stream)))
+
+
+def dckv_decode_heads(plan: Plan, stream_buf, n_bytes: int, token_ids, kv_out, status, ws, stream=None):
+    """kv_out: 2 * n_layers device tensors [n_kv_heads][T][head_dim] (bf16 bits)."""
+    arr = (ctypes.c_void_p * len(kv_out))(*[_ptr(t) for t in kv_out])
+    _check(_lib.dckv_decode_heads(plan.handle, _ptr(stream_buf), int(n_bytes), _ptr(token_ids),
+                                  int(token_ids.shape[0]), arr, _ptr(status), _ptr(ws), ws.numel(),
+                                  _stream_handle(stream)))
+
+
+def decode_heads(plan: Plan, stream_buf, token_ids, ws=None):
+    """Decode into the attention layers' cache layout: returns (list of
+    2 * n_layers tensors [n_kv_heads][T][head_dim] (int16 bf16 bits), status)."""
+    import torch
+    T = int(token_ids.shape[0])
+    dev = plan.codec.device
+    s = plan.codec.shape
+    kv = [torch.empty((s["n_kv_heads"], T, s["head_dim"]), dtype=torch.int16, device=dev)
+          for _ in range(2 * s["n_layers"])]
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = workspace(plan, T) if ws is None else ws
+    dckv_decode_heads(plan, stream_buf, stream_buf.numel(), token_ids, kv, st, ws)
+    return kv, int(st.item())
+
+
+def dckv_unrope(plan: Plan, rows_in, rows_out, stream=None):
+    _check(_lib.dckv_unrope(plan.handle, _ptr(rows_in), int(rows_in.shape[0]), _ptr(rows_out),
+                            _stream_handle(stream)))
 
 
 def dckv_fit_bytes(n: int) -> int:

@@ -125,6 +125,28 @@ extern "C" int dckv_decode(const dckv_plan_t *plan, const uint8_t *stream, uint6
   return after_launch("dckv_decode");
 }
 
+extern "C" int dckv_decode_heads(const dckv_plan_t *plan, const uint8_t *stream, uint64_t stream_bytes,
+                                 const int32_t *token_ids, int64_t T, uint16_t *const *kv_out, int32_t *status,
+                                 void *workspace, uint64_t workspace_bytes, void *hip_stream) {
+  Geometry g;
+  Layout l;
+  if (!kv_out) return set_error(DCKV_EINVAL, "decode_heads: null kv_out");
+  KvHeads h;
+  for (int i = 0; i < 12; ++i) {
+    h.p[i] = kv_out[i];
+    if (T > 0 && (!h.p[i] || !aligned(h.p[i], 16)))
+      return set_error(DCKV_EINVAL, "decode_heads: every kv_out matrix must be a 16-byte aligned device pointer");
+  }
+  // rows_out is not used; pass a placeholder that satisfies the shared checks
+  int rc = decode_checks(plan, stream, stream_bytes, token_ids, T, h.p[0], status, workspace, workspace_bytes, g, l);
+  if (rc) return rc;
+  DecodeArgs a{plan, g, l, static_cast<uint8_t *>(workspace), stream, stream_bytes, token_ids, nullptr, status,
+               static_cast<hipStream_t>(hip_stream)};
+  a.heads = &h;
+  decode_sequence(a);
+  return after_launch("dckv_decode_heads");
+}
+
 extern "C" int dckv_bytes_batch(const dckv_req *reqs, int32_t n, uint64_t *workspace_bytes) {
   if (n < 0 || (n > 0 && !reqs) || !workspace_bytes) return set_error(DCKV_EINVAL, "bytes_batch: bad argument");
   uint64_t need = 256;
@@ -273,4 +295,16 @@ extern "C" int dckv_fit(const dckv_params *p, const uint16_t *rows, const int32_
   a.s = static_cast<hipStream_t>(hip_stream);
   fit_sequence(a);
   return after_launch("dckv_fit");
+}
+
+extern "C" int dckv_unrope(const dckv_plan_t *plan, const uint16_t *rows_in, int64_t T, uint16_t *rows_out,
+                           void *hip_stream) {
+  if (!plan) return set_error(DCKV_EINVAL, "unrope: null plan");
+  if (T < 0 || T > 0x7FFFFFFF) return set_error(DCKV_EINVAL, "unrope: T out of range");
+  if (T > 0 && (!rows_in || !rows_out || !aligned(rows_in, 4) || !aligned(rows_out, 4)))
+    return set_error(DCKV_EINVAL, "unrope: rows must be 4-byte aligned device pointers");
+  int rc = check_device(plan);
+  if (rc) return rc;
+  launch_unrope(plan, rows_in, rows_out, T, static_cast<hipStream_t>(hip_stream));
+  return after_launch("dckv_unrope");
 }

@@ -135,6 +135,13 @@ struct EncodeArgs {
   hipStream_t s;
 };
 
+// Decoded rows either as rows_out [T][D], or per attention layer: for layer
+// l and kv (0 keys, 1 values), heads[2 l + kv] -> [n_kv_heads][T][head_dim]
+// (head h of the row's column block (2 l + kv) 2 + h).
+struct KvHeads {
+  uint16_t *p[12];
+};
+
 struct DecodeArgs {
   const dckv_plan_t *p;
   Geometry g;
@@ -146,10 +153,12 @@ struct DecodeArgs {
   uint16_t *rows_out;
   int32_t *status;
   hipStream_t s;
+  const KvHeads *heads = nullptr;  // set: the per-layer layout, rows_out unused
 };
 
 // misc.hip
 void launch_start_encode(const EncodeArgs &a);  // control words, status, kept rows
+void launch_unrope(const dckv_plan_t *p, const uint16_t *in, uint16_t *out, int64_t T, hipStream_t s);
 
 // rans.hip
 void launch_rans_encode(const EncodeArgs &a);

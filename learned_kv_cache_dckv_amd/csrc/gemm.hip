@@ -930,26 +930,51 @@ __global__ __launch_bounds__(kDeqThreads) void k_dequant(DeqP P) {
 }
 
 
+// Where decoded rows go: rows [T][D] (rows set) or the per-layer head
+// matrices (heads[2 l + kv] -> [2][T][head_dim]).
+struct OutRows {
+  uint16_t *rows;
+  uint16_t *heads[12];
+  int64_t T;
+  // element (position pos, head, 0) of the output
+  __device__ __forceinline__ uint16_t *at(int64_t pos, int head) const {
+    return rows ? rows + (size_t)pos * kD + head * kHeadDim
+                : heads[head >> 1] + ((size_t)(head & 1) * T + pos) * kHeadDim;
+  }
+};
+
+static OutRows out_rows(const DecodeArgs &a) {
+  OutRows o{};
+  o.T = a.g.T;
+  if (a.heads) {
+    o.rows = nullptr;
+    for (int i = 0; i < 12; ++i) o.heads[i] = a.heads->p[i];
+  } else {
+    o.rows = a.rows_out;
+  }
+  return o;
+}
+
 // kept row k: RoPE on the key columns of the verbatim row in the stream
 __device__ __forceinline__ void kept_rope_row(int64_t k, const uint8_t *stream, const float2 *lo, const float2 *hi,
-                                              uint16_t *out, int64_t head_n, int64_t tail_pos0) {
+                                              const OutRows &out, int64_t head_n, int64_t tail_pos0) {
   const int64_t pos = k < head_n ? k : tail_pos0 + (k - head_n);
   const uint16_t *src = reinterpret_cast<const uint16_t *>(stream + kHeaderBytes) + (size_t)k * kD;
-  uint16_t *dst = out + (size_t)pos * kD;
   for (int i = threadIdx.x; i < kD / 2; i += blockDim.x) {
     // i enumerates (head, d) with d < 128: the pair (d, d + 128) of every head
     const int head = i / kHalf, d = i % kHalf;
     const int base = head * kHeadDim;
+    uint16_t *dst = out.at(pos, head);
     const float x0 = bf2f(src[base + d]), x1 = bf2f(src[base + d + kHalf]);
     if ((head & 3) < 2) {
       const float2 a = lo[(size_t)(pos & 255) * kHalf + d], b = hi[(size_t)(pos >> 8) * kHalf + d];
       const float cs = b.x * a.x - b.y * a.y;
       const float sn = b.y * a.x + b.x * a.y;
-      dst[base + d] = f2bf(x0 * cs - x1 * sn);
-      dst[base + d + kHalf] = f2bf(x1 * cs + x0 * sn);
+      dst[d] = f2bf(x0 * cs - x1 * sn);
+      dst[d + kHalf] = f2bf(x1 * cs + x0 * sn);
     } else {
-      dst[base + d] = src[base + d];
-      dst[base + d + kHalf] = src[base + d + kHalf];
+      dst[d] = src[base + d];
+      dst[d + kHalf] = src[base + d + kHalf];
     }
   }
 }
@@ -967,7 +992,7 @@ struct W1P {
   // kept rows, RoPE'd by the GELU kernel's last n_kept workgroups
   const uint8_t *stream;
   const float2 *rope_lo, *rope_hi;
-  uint16_t *out;
+  OutRows out;
   int64_t n_kept, head_n, tail_pos0;
   unsigned gelu_blocks;
 };
@@ -1042,7 +1067,7 @@ __global__ __launch_bounds__(256) void k_w1_gelu(W1P P) {
 struct SynP {
   const uint16_t *yhat_b, *h_b, *S, *W2;
   const float2 *rope_lo, *rope_hi;  // [256][128], [ceil(T/256)][128]: (cos, sin)
-  uint16_t *out;                     // rows_out [T][D]
+  OutRows out;
   int64_t N;
   int keep_head, n_mt, n_nt;
   int32_t *status;
@@ -1072,8 +1097,9 @@ __device__ __forceinline__ uint32_t row_pair_word(float y0, float y1, uint32_t s
 // (lane % 32) & ~1 and + 1 of block nb.  Its byte offset from the wave's
 // origin (row 0, first column of the wave's half of the head), without the
 // lane's part; block nb holds head dims (nb / 2) 128 + 32 (nb % 2) + [0, 32).
+template <int kLd>  // row stride of the output (kD for rows, kHeadDim for head matrices)
 __device__ __forceinline__ constexpr uint32_t pend_off(int p) {
-  return (uint32_t)((acc_crow(p >> 5, 4 * ((p >> 1) & 3) + 2 * (p & 1)) * kD + ((p >> 3) & 3) / 2 * 128 +
+  return (uint32_t)((acc_crow(p >> 5, 4 * ((p >> 1) & 3) + 2 * (p & 1)) * kLd + ((p >> 3) & 3) / 2 * 128 +
                      32 * (((p >> 3) & 3) & 1)) * 2);
 }
 
@@ -1088,8 +1114,11 @@ constexpr int kSynDefer = 96;             // words held over (the rest are store
 constexpr int kSynPeel = kSynDefer / 8;    // k-tiles that store them, 8 each
 static_assert(kC / kBK >= kSynPeel, "synthesis main loop shorter than the store spread");
 
-template <int KT>  // k-tiles: 36 with the correction, 32 for the linear codec
+// KT: k-tiles, 36 with the correction, 32 for the linear codec; kHeads: the
+// per-layer head matrices as the output
+template <int KT, bool kHeads>
 __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
+  constexpr int kLd = kHeads ? kHeadDim : kD;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   if (wg_stop(P.status)) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1100,14 +1129,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
   uint32_t lb = 0u, sel = 0u;
   bool have = false;  // wave-uniform
   auto store_pend = [&](int p) {
-    __builtin_amdgcn_raw_buffer_store_b32(pend[p], pr, lb + pend_off(p), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(pend[p], pr, lb + pend_off<kLd>(p), 0, 0);
   };
   // word p of this tile: held over, or stored now
   auto put = [&](int p, uint32_t w) {
     if (p < kSynDefer)
       pend[p] = w;
     else
-      __builtin_amdgcn_raw_buffer_store_b32(w, pr, lb + pend_off(p), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(w, pr, lb + pend_off<kLd>(p), 0, 0);
   };
 #pragma unroll 1
   for (int t = blockIdx.x; t < total; t += gridDim.x) {
@@ -1137,9 +1166,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
     {
       const int64_t r0 = P.keep_head + wrow0;
       const int64_t rows = max<int64_t>(0, P.N - wrow0);
-      pr = span_rsrc(P.out + (size_t)r0 * kD + (size_t)head * kHeadDim + 64 * wn,
-                     (uint32_t)min<int64_t>(rows * kD * 2, 0x7FFFFFFF));
-      lb = (uint32_t)(((4 * (lane >> 5) + (lane & 1)) * kD + ((lane & 31) & ~1)) * 2);
+      pr = span_rsrc(P.out.at(r0, head) + 64 * wn, (uint32_t)min<int64_t>(rows * kLd * 2, 0x7FFFFFFF));
+      lb = (uint32_t)(((4 * (lane >> 5) + (lane & 1)) * kLd + ((lane & 31) & ~1)) * 2);
       sel = (lane & 1) ? 0x03020706u : 0x05040100u;
     }
     if (is_key) {
@@ -1342,7 +1370,7 @@ void launch_w1_gemm(const DecodeArgs &a) {
   P.stream = a.stream;
   P.rope_lo = reinterpret_cast<const float2 *>(a.ws + a.l.rope_lo);
   P.rope_hi = reinterpret_cast<const float2 *>(a.ws + a.l.rope_hi);
-  P.out = a.rows_out;
+  P.out = out_rows(a);
   P.n_kept = a.g.n_kept;
   P.head_n = std::min<int64_t>(a.p->keep_head, a.g.T);
   P.tail_pos0 = a.p->keep_head + a.g.N;
@@ -1363,7 +1391,7 @@ void launch_synthesis_gemm(const DecodeArgs &a) {
   P.W2 = a.p->W2;
   P.rope_lo = reinterpret_cast<const float2 *>(a.ws + a.l.rope_lo);
   P.rope_hi = reinterpret_cast<const float2 *>(a.ws + a.l.rope_hi);
-  P.out = a.rows_out;
+  P.out = out_rows(a);
   P.N = a.g.N;
   P.keep_head = a.p->keep_head;
   P.n_mt = (int)a.g.n_mtiles;
@@ -1380,10 +1408,18 @@ void launch_synthesis_gemm(const DecodeArgs &a) {
       n_cu = 256;
   }
   const int grid = std::min(P.n_mt * P.n_nt, n_cu);
-  if (a.p->W1)
-    launch_gemm(k_synthesis<(kC + kHid) / kBK>, "synthesis_gemm", grid, P, a.s);
-  else
-    launch_gemm(k_synthesis<kC / kBK>, "synthesis_gemm", grid, P, a.s);
+  constexpr int kFull = (kC + kHid) / kBK, kLin = kC / kBK;
+  if (a.heads) {
+    if (a.p->W1)
+      launch_gemm(k_synthesis<kFull, true>, "synthesis_gemm", grid, P, a.s);
+    else
+      launch_gemm(k_synthesis<kLin, true>, "synthesis_gemm", grid, P, a.s);
+  } else {
+    if (a.p->W1)
+      launch_gemm(k_synthesis<kFull, false>, "synthesis_gemm", grid, P, a.s);
+    else
+      launch_gemm(k_synthesis<kLin, false>, "synthesis_gemm", grid, P, a.s);
+  }
 }
 
 }  // namespace dckv
