@@ -289,6 +289,35 @@ def fit_bench(cfg: int, n: int, steps: int, cpu: bool) -> int:
     return 0
 
 
+def unrope_bench(cfg: int, steps: int) -> int:
+    """The inverse RoPE over the workload's rows (a post-RoPE cache back to
+    pre-RoPE rows): HBM-bound, 2 x T x 12,288 bytes per call."""
+    import torch
+    import dckv_synth as synth
+    import learned_kv_cache_dckv_amd as dk
+    dev = torch.device("cuda:0")
+    req = synth.make_request(cfg)
+    codec = dk.Codec(synth.world().params(), device=dev)
+    plan = codec.plan(req.step_scale)
+    src = torch.from_numpy(req.rows.view(np.int16)).to(dev)
+    dst = torch.empty_like(src)
+    dk.dckv_unrope(plan, src, dst)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    for _ in range(steps):
+        dk.dckv_unrope(plan, src, dst)
+    b.record(s)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    nbytes = 2.0 * req.T * KV_BYTES_PER_TOKEN
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": "inverse RoPE of a post-RoPE cache (GB/s)", "workload": req.note, "T": req.T,
+                      "ms": ms, "GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS}))
+    return 0
+
+
 def vendor_gemm(N: int, steps: int) -> int:
     """The vendor library's plain bf16 GEMMs (torch.matmul: hipBLASLt) on the
     codec's GEMM shapes, for comparison with the fused kernels' main loops.
@@ -336,6 +365,10 @@ def main(argv=None) -> int:
                     help="linear: the codec without the GELU correction")
     ap.add_argument("--fit", type=int, default=0, metavar="N_ROWS",
                     help="time the closed-form fit of the conditional models on N_ROWS calibration rows, then exit")
+    ap.add_argument("--unrope", action="store_true",
+                    help="time the inverse RoPE over the workload's rows, then exit")
+    ap.add_argument("--layout", choices=("rows", "heads"), default="rows",
+                    help="heads: decode into the per-layer [n_kv_heads][T][head_dim] matrices")
     ap.add_argument("--rate-ladder", action="store_true",
                     help="bytes/token and rates at each rate setting, both codecs, then exit")
     args = ap.parse_args(argv)
@@ -343,6 +376,8 @@ def main(argv=None) -> int:
         import dckv_synth as synth
         T = synth.CONFIGS[args.config]["T"]
         return vendor_gemm(T - 132, args.steps)
+    if args.unrope:
+        return unrope_bench(args.config, args.steps)
     if args.fit:
         return fit_bench(args.config, args.fit, args.steps, not args.no_cpu_baseline)
     if args.rate_ladder:
@@ -386,9 +421,21 @@ def main(argv=None) -> int:
         print("encode failed with status %d" % int(st_e.item()), file=sys.stderr)
         return 1
 
+    kv_out = None
+    if args.layout == "heads":
+        sh = codec.shape
+        kv_out = [torch.empty((sh["n_kv_heads"], T, sh["head_dim"]), dtype=torch.int16, device=dev)
+                  for _ in range(2 * sh["n_layers"])]
+
+    def decode_call():
+        if kv_out is None:
+            dk.dckv_decode(plan, buf, n_bytes, tok, out, st_d, ws)
+        else:
+            dk.dckv_decode_heads(plan, buf, n_bytes, tok, kv_out, st_d, ws)
+
     def step():
         dk.dckv_encode(plan, rows, tok, buf, nb, st_e, ws)
-        dk.dckv_decode(plan, buf, n_bytes, tok, out, st_d, ws)
+        decode_call()
 
     s = torch.cuda.current_stream()
     names = ("analysis_gemm", "fixup", "rans_encode", "scan", "pack", "parse", "rans_decode",
@@ -440,7 +487,7 @@ def main(argv=None) -> int:
         return a.elapsed_time(b) / k
 
     enc_ms = timed(lambda: dk.dckv_encode(plan, rows, tok, buf, nb, st_e, ws), args.steps)
-    dec_ms = timed(lambda: dk.dckv_decode(plan, buf, n_bytes, tok, out, st_d, ws), args.steps)
+    dec_ms = timed(decode_call, args.steps)
 
     # stream statistics (host side, after timing)
     data = buf[:n_bytes].cpu().numpy()
@@ -502,7 +549,7 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": req.note, "codec": args.codec, "T": T, "coded_tokens": N,
+        "config": {"workload": req.note, "codec": args.codec, "layout": args.layout, "T": T, "coded_tokens": N,
                    "rate_target_bytes_per_token": req.rate_target,
                    "step_scale": req.step_scale, "C_a": Ca, "groups": n_groups},
         "encode_tokens_per_s": N / (enc_ms * 1e-3),
