@@ -289,6 +289,91 @@ def fit_bench(cfg: int, n: int, steps: int, cpu: bool) -> int:
     return 0
 
 
+def training_rate_bench(cfg: int, steps: int, cpu: bool) -> int:
+    """The training rate (additive-noise likelihood, straight-through
+    reconstruction and the rate's gradients) of one prompt, by default the
+    4,096-token prompt a training sample holds.  The rate kernel moves 24
+    algorithmic bytes per coded coefficient (reads y, the noise and the
+    embedding mean; writes the reconstruction and two gradients); the
+    transform before it is the 6,144 -> 2,048 GEMM with fp32 output."""
+    import torch
+    import dckv_synth as synth
+    import learned_kv_cache_dckv_amd as dk
+    dev = torch.device("cuda:0")
+    req = synth.make_request(cfg)
+    T, C = req.T, 2048
+    N = T - 132
+    codec = dk.Codec(synth.world().params(), device=dev)
+    plan = codec.plan(req.step_scale)
+    u_h = synth.rate_noise(N, C, seed=cfg)
+    rows = torch.from_numpy(req.rows.view(np.int16)).to(dev)
+    tok = torch.from_numpy(req.token_ids.astype(np.int32)).to(dev)
+    u = torch.from_numpy(u_h).to(dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    bits, yhat, gy, gm = (torch.empty(N, **f32), torch.empty((N, C), **f32), torch.empty((N, C), **f32),
+                          torch.empty((N, C), **f32))
+    ga, gb = torch.empty(C, **f32), torch.empty(C, **f32)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(dk.dckv_rate_bytes(plan, T), dtype=torch.uint8, device=dev)
+
+    def run():
+        dk.dckv_rate_forward(plan, rows, tok, u, bits, yhat, gy, gm, ga, gb, st, ws)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        run()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kern = {}
+    for name in ("rate", "fit_gemm"):
+        dk.dckv_profile_reset()
+        dk.dckv_profile_only(name)
+        dk.dckv_profile_enable(True)
+        for _ in range(steps):
+            run()
+        torch.cuda.synchronize()
+        dk.dckv_profile_enable(False)
+        dk.dckv_profile_only(None)
+        tot, n = dk.dckv_profile_read(name)
+        kern[name] = tot / max(n, 1)
+    rate_bytes = 24.0 * N * C
+    gemm_flop = 2.0 * N * 6144 * C
+    gbps = rate_bytes / (kern["rate"] * 1e-3) / 1e9
+    tf = gemm_flop / (kern["fit_gemm"] * 1e-3) / 1e12
+    res = {"metric": "training rate forward + gradients (coded tokens/s)", "value": N / (ms * 1e-3),
+           "unit": "coded tokens/s", "workload": req.note, "T": T, "coded_tokens": N, "ms": ms,
+           "step_scale": req.step_scale, "bits_per_token": float(bits.mean().item()),
+           "kernels": {"rate": {"avg_ms": kern["rate"], "GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS,
+                                "algorithmic_bytes": rate_bytes},
+                       "transform_gemm": {"avg_ms": kern["fit_gemm"], "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}},
+           "cpu_baseline": None}
+    if cpu:
+        from oracle import rate as orate
+        w = synth.world()
+        t0 = time.perf_counter()
+        y, m = orate.coefficients(req.rows, req.token_ids, w.params())
+        r = orate.rate_forward(y, m, _oracle_plan(w, req.step_scale), w.nbr_weight, w.laplace_scale, u_h)
+        cpu_s = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": N / cpu_s, "unit": "coded tokens/s", "kind": "oracle",
+                               "cores": len(os.sched_getaffinity(0)),
+                               "sample": "the same %d-token prompt, numpy float64" % T,
+                               "bits_rel": float(abs(bits.sum().item() - r.total) / r.total)}
+    print(json.dumps(res))
+    return 0
+
+
+def _oracle_plan(w, g):
+    from oracle import plan as oplan
+    return oplan.make_plan(np.float32(g), w.base_step, w.laplace_scale)
+
+
 def unrope_bench(cfg: int, steps: int) -> int:
     """The inverse RoPE over the workload's rows (a post-RoPE cache back to
     pre-RoPE rows): HBM-bound, 2 x T x 12,288 bytes per call."""
@@ -369,6 +454,9 @@ def main(argv=None) -> int:
                     help="time the inverse RoPE over the workload's rows, then exit")
     ap.add_argument("--layout", choices=("rows", "heads"), default="rows",
                     help="heads: decode into the per-layer [n_kv_heads][T][head_dim] matrices")
+    ap.add_argument("--training-rate", action="store_true",
+                    help="time the training rate and its gradients on the workload (default: the 4,096-token "
+                         "prompt), then exit")
     ap.add_argument("--rate-ladder", action="store_true",
                     help="bytes/token and rates at each rate setting, both codecs, then exit")
     args = ap.parse_args(argv)
@@ -380,6 +468,9 @@ def main(argv=None) -> int:
         return unrope_bench(args.config, args.steps)
     if args.fit:
         return fit_bench(args.config, args.fit, args.steps, not args.no_cpu_baseline)
+    if args.training_rate:
+        cfg = args.config if "--config" in (argv or sys.argv) else 1
+        return training_rate_bench(cfg, args.steps, not args.no_cpu_baseline)
     if args.rate_ladder:
         return rate_ladder(args.config, args.steps)
     if args.write_traffic:

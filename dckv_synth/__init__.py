@@ -311,3 +311,10 @@ def random_rows(T: int, seed: int, gain: float = 1.0):
     if gain != 1.0:
         rows = to_bf16_bits(bf16_bits_to_f32(rows) * np.float32(gain))
     return rows, tok
+
+
+def rate_noise(n_rows: int, n_coef: int, seed: int) -> np.ndarray:
+    """Uniform noise in [-1/2, 1/2) steps, float32 [n_rows][n_coef] (the
+    additive noise of the training rate, drawn by the caller)."""
+    rng = np.random.default_rng(np.random.SeedSequence([CODEC_SEED, 77, int(seed)]))
+    return (rng.random((n_rows, n_coef), dtype=np.float32) - np.float32(0.5)).astype(np.float32)

@@ -324,6 +324,46 @@ int dckv_fit(const dckv_params *p, const uint16_t *rows, const int32_t *token_id
              float *mean_head_out, uint16_t *mean_head_bf16_out, float *nbr_weight_out, float *laplace_scale_out,
              int32_t *status, void *workspace, uint64_t workspace_bytes, void *hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * Training rate: the code length of additive-noise coefficients and its
+ * gradients (DCKV digest page, "How it works", Training bullet: the rate is
+ * computed with additive noise, the reconstruction from rounded values whose
+ * gradient passes straight through).  The distortion term of the training
+ * loss needs the language model and is not part of this call.
+ *
+ * For coded row j (position t = j + keep_head, 0 <= j < N) and component c,
+ * with the plan's step D_c, its Laplace scale b_c (the params' laplace_scale)
+ * and s = b_c / D_c:
+ *   y = A x_t (fp32 accumulation of bf16 products); m = H E[tok_t];
+ *   mu = m for even j, m + a (yhat_{j-1} + yhat_{j+1}) for odd j (yhat_N = 0);
+ *   yhat = mu + rint(fp32(y - mu) / D) D, the codec's two-pass reconstruction;
+ *   t = (y - mu) / D + noise[j][c];
+ *   bits = -log2(F_s(t + 1/2) - F_s(t - 1/2)), F_s the zero-mean Laplace CDF.
+ * Dropped components (the plan's drop rule) have bits 0, yhat = mu and zero
+ * gradients.  R is the sum of bits over rows and active components; with the
+ * straight-through rule (d yhat / d y = 1, d yhat / d mu = 0):
+ *   bits_out    [N]     fp32  per-token sum of bits
+ *   yhat_out    [N][C]  fp32  reconstruction (components in natural order)
+ *   grad_y      [N][C]  fp32  dR/dy, including the even rows' share in their
+ *                             odd neighbours' means
+ *   grad_mean   [N][C]  fp32  dR/dm (for the mean head's gradient)
+ *   grad_nbr    [C]     fp32  dR/da
+ *   grad_scale  [C]     fp32  dR/db
+ * rows [T][D] bf16 pre-RoPE (16-byte aligned) and token_ids [T] are those of
+ * dckv_encode; noise [N][C] fp32 is the caller's uniform draw in steps,
+ * normally in [-1/2, 1/2).  All outputs and the workspace are caller-owned
+ * device memory (4-byte aligned, workspace 256-byte aligned, at least
+ * dckv_rate_bytes); nothing is allocated.  Arguments are checked
+ * synchronously (negative return, nothing enqueued); a non-finite y - mu or a
+ * token id outside [0, vocab) sets *status to DCKV_EINVAL on the device.
+ * The workspace is about 8.3 KiB per coded row.
+ * --------------------------------------------------------------------------*/
+int dckv_rate_bytes(const dckv_plan_t *plan, int64_t T, uint64_t *workspace_bytes);
+int dckv_rate_forward(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *token_ids, int64_t T,
+                      const float *noise, float *bits_out, float *yhat_out, float *grad_y, float *grad_mean,
+                      float *grad_nbr, float *grad_scale, int32_t *status, void *workspace,
+                      uint64_t workspace_bytes, void *hip_stream);
+
 const char *dckv_last_error(void);
 
 /* Stream layout, version 1 (little endian, sections contiguous, no padding):

@@ -28,7 +28,8 @@ EXPORTS = ("dckv_plan_tables", "dckv_plan", "dckv_plan_free", "dckv_plan_info", 
            "dckv_bytes", "dckv_encode",
            "dckv_decode", "dckv_decode_heads", "dckv_unrope", "dckv_bytes_batch", "dckv_encode_batch", "dckv_decode_batch", "dckv_entropy_encode",
            "dckv_entropy_decode", "dckv_workspace_view", "dckv_profile_enable", "dckv_profile_only", "dckv_profile_reset",
-           "dckv_profile_read", "dckv_fit_bytes", "dckv_fit", "dckv_last_error")
+           "dckv_profile_read", "dckv_fit_bytes", "dckv_fit", "dckv_rate_bytes", "dckv_rate_forward",
+           "dckv_last_error")
 
 
 class DckvError(RuntimeError):
@@ -85,6 +86,8 @@ def _load():
         "dckv_profile_read": [ctypes.c_char_p, P, P],
         "dckv_fit_bytes": [I64, P],
         "dckv_fit": [P, P, P, I64, F, P, P, P, P, P, P, U64, P],
+        "dckv_rate_bytes": [P, I64, P],
+        "dckv_rate_forward": [P, P, P, I64, P, P, P, P, P, P, P, P, P, U64, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -421,6 +424,45 @@ def fit(codec: "Codec", rows, token_ids, ridge: float):
     dckv_fit(codec, rows, token_ids, ridge, H, Hb, a, b, st, ws)
     torch.cuda.synchronize()
     return H, Hb, a, b, int(st.item())
+
+
+def dckv_rate_bytes(plan: Plan, T: int) -> int:
+    v = ctypes.c_uint64()
+    _check(_lib.dckv_rate_bytes(plan.handle, int(T), ctypes.byref(v)))
+    return v.value
+
+
+def dckv_rate_forward(plan: Plan, rows, token_ids, noise, bits_out, yhat_out, grad_y, grad_mean, grad_nbr,
+                      grad_scale, status, ws, stream=None):
+    _check(_lib.dckv_rate_forward(plan.handle, _ptr(rows), _ptr(token_ids), int(token_ids.shape[0]), _ptr(noise),
+                                  _ptr(bits_out), _ptr(yhat_out), _ptr(grad_y), _ptr(grad_mean), _ptr(grad_nbr),
+                                  _ptr(grad_scale), _ptr(status), _ptr(ws), ws.numel(), _stream_handle(stream)))
+
+
+def rate_forward(plan: Plan, rows, token_ids, noise, ws=None):
+    """Training rate of one request (device bf16 row bits [T][D], int32 token
+    ids [T], fp32 noise [N][n_coef] in steps); returns a dict of device
+    tensors: bits [N], yhat, grad_y, grad_mean [N][n_coef], grad_nbr,
+    grad_scale [n_coef], and the status."""
+    import torch
+    dev = rows.device
+    T = int(token_ids.shape[0])
+    c = plan.codec
+    N = max(T - c.shape["keep_head"] - c.shape["keep_tail"], 0)
+    out = dict(bits=torch.empty(N, dtype=torch.float32, device=dev),
+               yhat=torch.empty((N, c.n_coef), dtype=torch.float32, device=dev),
+               grad_y=torch.empty((N, c.n_coef), dtype=torch.float32, device=dev),
+               grad_mean=torch.empty((N, c.n_coef), dtype=torch.float32, device=dev),
+               grad_nbr=torch.empty(c.n_coef, dtype=torch.float32, device=dev),
+               grad_scale=torch.empty(c.n_coef, dtype=torch.float32, device=dev))
+    st = torch.full((1,), 777, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = torch.empty(dckv_rate_bytes(plan, T), dtype=torch.uint8, device=dev)
+    dckv_rate_forward(plan, rows, token_ids, noise, out["bits"], out["yhat"], out["grad_y"], out["grad_mean"],
+                      out["grad_nbr"], out["grad_scale"], st, ws)
+    torch.cuda.synchronize()
+    out["status"] = int(st.item())
+    return out
 
 
 def dckv_workspace_view(plan: Plan, T: int, which: int):

@@ -22,7 +22,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdckv.so")
 ARCH = os.environ.get("DCKV_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["plan.cpp", "api.cpp", "misc.hip", "rans.hip", "gemm.hip", "fit.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "misc.hip", "rans.hip", "gemm.hip", "fit.hip", "rate.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-Wall", "-Wno-unused-function",
           "-Wno-unused-variable", "-Wno-unused-result", "-Wno-pass-failed",

@@ -297,6 +297,59 @@ extern "C" int dckv_fit(const dckv_params *p, const uint16_t *rows, const int32_
   return after_launch("dckv_fit");
 }
 
+extern "C" int dckv_rate_bytes(const dckv_plan_t *plan, int64_t T, uint64_t *workspace_bytes) {
+  if (!plan) return set_error(DCKV_EINVAL, "rate: null plan");
+  if (T < 0 || T > ((int64_t)1 << 22) + plan->keep_head + plan->keep_tail)
+    return set_error(DCKV_EINVAL, "rate: T out of range (at most 2^22 coded rows)");
+  if (!workspace_bytes) return set_error(DCKV_EINVAL, "rate: null workspace_bytes");
+  *workspace_bytes = rate_layout(geometry(plan, T).N).total;
+  return DCKV_OK;
+}
+
+extern "C" int dckv_rate_forward(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *token_ids, int64_t T,
+                                 const float *noise, float *bits_out, float *yhat_out, float *grad_y,
+                                 float *grad_mean, float *grad_nbr, float *grad_scale, int32_t *status,
+                                 void *workspace, uint64_t workspace_bytes, void *hip_stream) {
+  uint64_t need = 0;
+  int rc = dckv_rate_bytes(plan, T, &need);
+  if (rc) return rc;
+  if (plan->n_kv_heads != 2 || plan->head_dim != kHeadDim || plan->D != kD || plan->C != kC || plan->emb != kEmb)
+    return set_error(DCKV_EUNSUPPORTED, "rate: the kernels support D=6144, n_coef=2048, emb_dim=2048");
+  const int64_t N = geometry(plan, T).N;
+  if (N > 0) {
+    if (!rows || !aligned(rows, 16) || !token_ids || !aligned(token_ids, 4))
+      return set_error(DCKV_EINVAL, "rate: rows must be 16-byte aligned, token_ids 4-byte aligned");
+    const void *per_row[] = {noise, bits_out, yhat_out, grad_y, grad_mean};
+    for (const void *q : per_row)
+      if (!q || !aligned(q, 4)) return set_error(DCKV_EINVAL, "rate: null or misaligned per-row array");
+  }
+  if (!grad_nbr || !grad_scale || !aligned(grad_nbr, 4) || !aligned(grad_scale, 4))
+    return set_error(DCKV_EINVAL, "rate: null or misaligned grad_nbr / grad_scale");
+  if (!status || !aligned(status, 4)) return set_error(DCKV_EINVAL, "rate: status must be a 4-byte aligned device word");
+  if (!workspace || !aligned(workspace, 256)) return set_error(DCKV_EINVAL, "rate: workspace must be 256-byte aligned");
+  if (workspace_bytes < need) return set_error(DCKV_ECAPACITY, "rate: workspace smaller than dckv_rate_bytes()");
+  rc = check_device(plan);
+  if (rc) return rc;
+  RateArgs a;
+  a.p = plan;
+  a.l = rate_layout(N);
+  a.ws = static_cast<uint8_t *>(workspace);
+  a.rows = rows;
+  a.tok = token_ids;
+  a.noise = noise;
+  a.N = N;
+  a.bits = bits_out;
+  a.yhat = yhat_out;
+  a.grad_y = grad_y;
+  a.grad_mean = grad_mean;
+  a.grad_nbr = grad_nbr;
+  a.grad_scale = grad_scale;
+  a.status = status;
+  a.s = static_cast<hipStream_t>(hip_stream);
+  rate_sequence(a);
+  return after_launch("dckv_rate_forward");
+}
+
 extern "C" int dckv_unrope(const dckv_plan_t *plan, const uint16_t *rows_in, int64_t T, uint16_t *rows_out,
                            void *hip_stream) {
   if (!plan) return set_error(DCKV_EINVAL, "unrope: null plan");

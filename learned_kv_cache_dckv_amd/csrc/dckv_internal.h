@@ -47,6 +47,7 @@ struct PlanDev {
   int32_t *perm = nullptr;      // [C]   component of each mean-table column: ranks, then dropped
   int32_t *colpos = nullptr;    // [C]   mean-table column of each component
   float *qcol = nullptr;        // [C_a padded][4] step, 1/step (0 past C_a), neighbour weight, 0 of each rank
+  float *scale = nullptr;       // [C]   Laplace scale b of each component
   uint32_t *tab = nullptr;      // [C_a][256]  f | cum << 16
   uint8_t *bucket = nullptr;    // [C_a][kBuckets] first symbol of each slot bucket
   double *omega = nullptr;      // [head_dim/2] RoPE frequencies
@@ -211,6 +212,26 @@ struct FitArgs {
   hipStream_t s;
 };
 void fit_sequence(const FitArgs &a);
+
+// rate.hip: the training rate (additive-noise likelihood) and its gradients
+struct RateLayout {
+  int64_t chunks = 0;  // row chunks of the per-component sums
+  uint64_t Y = 0, bits_part = 0, ga_part = 0, gb_part = 0, total = 0;
+};
+RateLayout rate_layout(int64_t N);
+struct RateArgs {
+  const dckv_plan_t *p;
+  RateLayout l;
+  uint8_t *ws;
+  const uint16_t *rows;
+  const int32_t *tok;
+  const float *noise;
+  int64_t N;
+  float *bits, *yhat, *grad_y, *grad_mean, *grad_nbr, *grad_scale;
+  int32_t *status;
+  hipStream_t s;
+};
+void rate_sequence(const RateArgs &a);
 void launch_analysis_gemm(const EncodeArgs &a);
 void launch_encode_fixup(const EncodeArgs &a);
 void launch_dequant(const DecodeArgs &a);

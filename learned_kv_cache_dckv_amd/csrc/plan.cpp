@@ -261,7 +261,7 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
     return o;
   };
   const size_t o_step = take(C * 4), o_nbr = take(C * 4), o_rank = take(C * 4), o_act = take(Ca_pad * 4);
-  const size_t o_perm = take(C * 4), o_colpos = take(C * 4), o_qcol = take(qcol.size() * 4);
+  const size_t o_perm = take(C * 4), o_colpos = take(C * 4), o_qcol = take(qcol.size() * 4), o_scale = take(C * 4);
   const size_t o_tab = take(tab.size() * 4), o_bucket = take(bucket.size()), o_omega = take(kHalf * 8);
   void *blk = nullptr;
   if (hipMalloc(&blk, off) != hipSuccess) {
@@ -276,6 +276,7 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
   std::memcpy(&img[o_perm], perm.data(), C * 4);
   std::memcpy(&img[o_colpos], colpos.data(), C * 4);
   std::memcpy(&img[o_qcol], qcol.data(), qcol.size() * 4);
+  std::memcpy(&img[o_scale], p->laplace_scale, C * 4);
   std::memcpy(&img[o_tab], tab.data(), tab.size() * 4);
   std::memcpy(&img[o_bucket], bucket.data(), bucket.size());
   std::memcpy(&img[o_omega], omega.data(), kHalf * 8);
@@ -293,6 +294,7 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
   pl->dev.perm = reinterpret_cast<int32_t *>(b + o_perm);
   pl->dev.colpos = reinterpret_cast<int32_t *>(b + o_colpos);
   pl->dev.qcol = reinterpret_cast<float *>(b + o_qcol);
+  pl->dev.scale = reinterpret_cast<float *>(b + o_scale);
   pl->dev.tab = reinterpret_cast<uint32_t *>(b + o_tab);
   pl->dev.bucket = b + o_bucket;
   pl->dev.omega = reinterpret_cast<double *>(b + o_omega);
