@@ -186,6 +186,9 @@ struct GemmF32Args {
   int M, N;
   float *c;
   int64_t ldc;
+  // ksplit > 1 (single-source operands, KT a multiple of ksplit): slice ks of
+  // the k range goes to c + ks * M * ldc, for the caller to add up
+  int ksplit;
   int n_mt, n_nt;  // set by the launcher
 };
 void launch_gemm_f32(const GemmF32Args &args, hipStream_t s);
@@ -215,8 +218,11 @@ void fit_sequence(const FitArgs &a);
 
 // rate.hip: the training rate (additive-noise likelihood) and its gradients
 struct RateLayout {
-  int64_t chunks = 0;  // row chunks of the per-component sums
-  uint64_t Y = 0, bits_part = 0, ga_part = 0, gb_part = 0, total = 0;
+  int64_t chunks = 0;  // row chunks of the rate kernel
+  int64_t parts = 0;   // partial rows of the per-component sums (one per chunk)
+  int ksplit = 1;      // k-slices of the transform (partial coefficient sets)
+  int64_t n_seg = 0;   // first-stage segments of those sums
+  uint64_t Y = 0, bits_part = 0, ga_part = 0, gb_part = 0, flags = 0, ga_seg = 0, gb_seg = 0, flags2 = 0, total = 0;
 };
 RateLayout rate_layout(int64_t N);
 struct RateArgs {

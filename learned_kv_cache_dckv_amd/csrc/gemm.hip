@@ -398,11 +398,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_mean_table(MeanTabP P) {
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_f32(GemmF32Args P) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int mt, nt;
-  tile_of(blockIdx.x, P.n_mt * P.n_nt, P.n_nt, mt, nt);
+  // k-slice ks of ksplit (single-source operands): k-tiles [ks KT, (ks + 1) KT)
+  // into the output slice c + ks M ldc
+  const int tiles = P.n_mt * P.n_nt;
+  const int ks = blockIdx.x / tiles;
+  tile_of(blockIdx.x - ks * tiles, tiles, P.n_nt, mt, nt);
+  const int KT = P.KT / P.ksplit;
+  const size_t koff = (size_t)ks * KT * kRowBytes;
+  const int split = P.ksplit > 1 ? KT : P.split;
   const int m0 = mt * kBM, n0 = nt * kBN;
   Operand A, B;
-  set_sources(A, P.a0, P.lda0, P.a1, P.lda1, P.split);
-  set_sources(B, P.b0, P.ldb0, P.b1, P.ldb1, P.split);
+  set_sources(A, reinterpret_cast<const char *>(P.a0) + koff, P.lda0, reinterpret_cast<const char *>(P.a1) + koff,
+              P.lda1, split);
+  set_sources(B, reinterpret_cast<const char *>(P.b0) + koff, P.ldb0, reinterpret_cast<const char *>(P.b1) + koff,
+              P.ldb1, split);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int m = min(m0 + staged_row(i), P.M - 1);
@@ -410,9 +419,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_f32(GemmF32Args P) {
     B.row[i] = (uint32_t)min(n0 + staged_row(i), P.N - 1);
   }
   f32x16 acc[4][4];
-  mainloop(A, B, P.KT, acc, lds);
+  mainloop(A, B, KT, acc, lds);
   const int lane = epilogue_lane(), wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  float *const cs = P.c + (size_t)ks * P.M * P.ldc;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -421,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_f32(GemmF32Args P) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = m0 + wm * 128 + acc_row(mb, v, lane);
-        if (row < P.M && col < P.N) P.c[(size_t)row * P.ldc + col] = acc_get(acc[mb][nb], v);
+        if (row < P.M && col < P.N) cs[(size_t)row * P.ldc + col] = acc_get(acc[mb][nb], v);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1260,7 +1270,8 @@ void launch_gemm_f32(const GemmF32Args &args, hipStream_t s) {
   GemmF32Args P = args;
   P.n_mt = (P.M + kBM - 1) / kBM;
   P.n_nt = (P.N + kBN - 1) / kBN;
-  launch_gemm(k_gemm_f32, "fit_gemm", P.n_mt * P.n_nt, P, s);
+  if (P.ksplit < 1) P.ksplit = 1;
+  launch_gemm(k_gemm_f32, "fit_gemm", P.n_mt * P.n_nt * P.ksplit, P, s);
 }
 
 int build_mean_table(dckv_plan_t *p) {

@@ -15,33 +15,35 @@
 //   dR/db   = sum over j of gamma_j / D.
 // Dropped components: bits 0, yhat = mu, no gradient.
 //
-// Work split: the coefficients y = A x come from the fp32-output GEMM; one
-// thread per component walks a chunk of rows in order, so the neighbour terms
-// are register carries (two halo rows before the chunk and one after it are
-// recomputed).  Per-token bits are wave sums written as partials and added in
-// a fixed order; the per-component sums are per-chunk partials in fp64.
+// Work split: the coefficients y = A x come from the fp32-output GEMM (split
+// over k into partial sets when its tiles alone would not fill the chip); one
+// thread per component codes a chunk of rows held in registers, so the
+// neighbour terms are register reads (two halo rows before the chunk and one after it are
+// recomputed).  Per-token bits are column-block sums written as partials and
+// added in a fixed order; the per-component sums are per-chunk partials in fp64,
+// reduced by a last kernel that also sets the status.
 #include "dckv_internal.h"
 
 namespace dckv {
 namespace {
 
-constexpr int kRateRows = 32;    // rows per chunk (even)
+constexpr int kRateRows = 16;    // rows per chunk (even)
 constexpr int kRateCols = 256;   // components per workgroup
-constexpr int kRateWaves = kC / 64;  // wave partials per row
+constexpr int kRateParts = kC / kRateCols;  // column-block partials per row
 
 struct RateP {
-  const float *Y;        // [N][C] coefficients
+  const float *Y;        // [ksplit][N][C] partial coefficients
   const float *mtab;     // [vocab][C] embedding means, plan column order
   const int32_t *tok;    // [T]
   const float *noise;    // [N][C]
   const float *step, *nbr, *scale;
   const int32_t *rank, *colpos;
   float *yhat, *gy, *gm;  // [N][C]
-  float *bits_part;       // [kRateWaves][N]
-  double *ga_part, *gb_part;  // [chunks][C]
-  int32_t *status;
-  int64_t N;
-  int keep_head, vocab;
+  float *bits_part;       // [kRateParts][N]
+  float *ga_part, *gb_part;   // [chunks][C] per-chunk sums (fp64 inside a chunk)
+  int32_t *flags;             // [chunks][C / kRateCols] a bad input seen
+  int64_t N, chunks;          // chunks of kRateRows rows
+  int keep_head, vocab, ksplit;  // ksplit 1 or 2
 };
 
 struct Col {
@@ -78,53 +80,48 @@ __device__ __forceinline__ void rate_of(float t, const Col &k, Out &o) {
   }
 }
 
-struct Row {
-  float y, m, u;
-};
-
-__device__ __forceinline__ Row load_row(const RateP &P, int64_t j, int c, const Col &k, bool &bad) {
-  Row r;
-  const int64_t o = j * kC + c;
-  r.y = P.Y[o];
-  r.u = P.noise[o];
-  int v = P.tok[j + P.keep_head];
-  if ((unsigned)v >= (unsigned)P.vocab) {
-    bad = true;
-    v = 0;
-  }
-  r.m = P.mtab[(int64_t)v * kC + k.col];
-  return r;
+__device__ __forceinline__ float wave_sum16(float v) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
 }
 
 // reconstruction and rate of one row given its conditional mean
-__device__ __forceinline__ Out code_row(const Row &r, float mu, const Col &k, bool &bad) {
+__device__ __forceinline__ Out code_row(float y, float u, float mu, const Col &k, bool &bad) {
   Out o;
   if (!k.act) {
     o.yhat = mu;
     o.beta = o.gamma = o.bits = 0.f;
     return o;
   }
-  const float d = r.y - mu;
+  const float d = y - mu;
   if (!isfinite(d)) bad = true;
   const float rr = __fdiv_rn(d, k.step);
   const float q = fminf(fmaxf(rintf(rr), -2147483520.0f), 2147483520.0f);
   o.yhat = fmaf(q, k.step, mu);
-  rate_of(rr + r.u, k, o);
+  rate_of(rr + u, k, o);
   return o;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
+constexpr int kWin = kRateRows + 3;  // window rows j0 - 2 .. j0 + kRateRows
 
-__global__ __launch_bounds__(256) void k_rate(RateP P) {
-  const int c = blockIdx.x * kRateCols + threadIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wv = c >> 6;
-  const int64_t j0 = (int64_t)blockIdx.y * kRateRows;
-  const int64_t j1 = min(j0 + kRateRows, P.N);
+// Workgroup (column block, chunk of kRateRows rows from j0): every load of the
+// chunk's window is issued first (token ids, then coefficients, noise and
+// means), the rows are coded in registers, and the per-token bits of the
+// block's columns are summed through LDS.
+__global__ __launch_bounds__(kRateCols) void k_rate(RateP P) {
+  __shared__ float lb[kRateRows * kRateCols];
+  // workgroups are dealt to the 8 XCDs in turn; give each XCD a contiguous
+  // range of (chunk, column block) pairs, so that it reads whole rows and the
+  // halo rows of its chunks are mostly in its own L2
+  const int total = (int)gridDim.x, x = blockIdx.x & 7, kk = blockIdx.x >> 3;
+  const int q8 = total >> 3, r8 = total & 7;
+  const int t = x < r8 ? x * (q8 + 1) + kk : r8 * (q8 + 1) + (x - r8) * q8 + kk;
+  const int cb = t % kRateParts, chunk = t / kRateParts;
+  const int lt = threadIdx.x;
+  const int c = cb * kRateCols + lt;
+  const int64_t j0 = (int64_t)chunk * kRateRows;
+  const int64_t base = j0 - 2;
   Col k;
   k.step = P.step[c];
   k.a = P.nbr[c];
@@ -134,105 +131,227 @@ __global__ __launch_bounds__(256) void k_rate(RateP P) {
   k.inv_s_l2 = kLog2e / k.s;
   k.k0 = 1.f - log2f(-expm1f(-1.f / k.s));
   k.g0 = 1.f / expm1f(1.f / k.s);
+  const float inv_d = 1.f / k.step;
   bool bad = false;
   double ga = 0.0, gb = 0.0;
-  const float inv_d = 1.f / k.step;
-
-  // the first even row, and the odd row before it (its dR/dm feeds the chain)
-  const Row r0 = load_row(P, j0, c, k, bad);
-  Out oe = code_row(r0, r0.m, k, bad);
-  float gm_prev = 0.f;  // dR/dm of row j0 - 1
-  if (j0 >= 2) {
-    const Row rp = load_row(P, j0 - 2, c, k, bad);
-    const Out op = code_row(rp, rp.m, k, bad);
-    const Row ro = load_row(P, j0 - 1, c, k, bad);
-    const Out oo = code_row(ro, fmaf(k.a, op.yhat + oe.yhat, ro.m), k, bad);
-    gm_prev = -oo.beta * inv_d;
-  }
-  for (int64_t e = j0; e < j1; e += 2) {
-    const int64_t o = e + 1;
-    Out on = {0.f, 0.f, 0.f, 0.f};     // the odd row e + 1
-    Out onext = {0.f, 0.f, 0.f, 0.f};  // the next even row e + 2
-    bool have_next = false;
-    if (o < P.N) {
-      if (e + 2 < P.N) {
-        const Row rn = load_row(P, e + 2, c, k, bad);
-        onext = code_row(rn, rn.m, k, bad);
-        have_next = true;
+  int tk[kWin];
+#pragma unroll
+  for (int r = 0; r < kWin; ++r) {
+    const int64_t j = base + r;
+    int v = 0;
+    if (j >= 0 && j < P.N) {
+      v = P.tok[j + P.keep_head];
+      if ((unsigned)v >= (unsigned)P.vocab) {
+        bad = true;
+        v = 0;
       }
-      const Row ro = load_row(P, o, c, k, bad);
-      const float nb = oe.yhat + (have_next ? onext.yhat : 0.f);
-      const float mu = fmaf(k.a, nb, ro.m);
-      on = code_row(ro, mu, k, bad);
-      const float gmo = -on.beta * inv_d;
-      ga += (double)gmo * (double)nb;
-      gb += (double)on.gamma * (double)inv_d;
+    }
+    tk[r] = v;
+  }
+  // (the second partial set is added only after every load is in flight)
+  float ys[kWin], y2[kWin], us[kWin], ms[kWin];
+  const bool two = P.ksplit > 1;
+  const int64_t NC = P.N * kC;
+#pragma unroll
+  for (int r = 0; r < kWin; ++r) {
+    const int64_t j = base + r;
+    ys[r] = y2[r] = us[r] = ms[r] = 0.f;
+    if (j >= 0 && j < P.N) {
+      const int64_t o = j * kC + c;
+      ys[r] = P.Y[o];
+      if (two) y2[r] = P.Y[NC + o];
+      us[r] = P.noise[o];
+      ms[r] = P.mtab[(int64_t)tk[r] * kC + k.col];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kWin; ++r) ys[r] += y2[r];
+  // even window rows 2i (rows past N reconstruct to 0: the missing neighbour)
+  Out ev[kRateRows / 2 + 2];
+#pragma unroll
+  for (int i = 0; i < kRateRows / 2 + 2; ++i) {
+    const int64_t j = base + 2 * i;
+    ev[i] = Out{0.f, 0.f, 0.f, 0.f};
+    if (j >= 0 && j < P.N) ev[i] = code_row(ys[2 * i], us[2 * i], ms[2 * i], k, bad);
+  }
+  // odd window rows 2i + 1, with the neighbours' reconstruction in their means
+  Out od[kRateRows / 2 + 1];
+  float nbs[kRateRows / 2 + 1];
+#pragma unroll
+  for (int i = 0; i < kRateRows / 2 + 1; ++i) {
+    const int64_t j = base + 2 * i + 1;
+    nbs[i] = ev[i].yhat + ev[i + 1].yhat;
+    od[i] = Out{0.f, 0.f, 0.f, 0.f};
+    if (j >= 0 && j < P.N) od[i] = code_row(ys[2 * i + 1], us[2 * i + 1], fmaf(k.a, nbs[i], ms[2 * i + 1]), k, bad);
+  }
+#pragma unroll
+  for (int i = 1; i <= kRateRows / 2; ++i) {
+    const int64_t e = base + 2 * i, o = e + 1;
+    const int le = 2 * i - 2;
+    float be = 0.f, bo = 0.f;
+    if (e < P.N) {
+      const int64_t eo = e * kC + c;
+      P.yhat[eo] = ev[i].yhat;
+      // the even row's reconstruction feeds the means of rows e - 1 and e + 1
+      P.gy[eo] = fmaf(k.a, -(od[i - 1].beta + od[i].beta) * inv_d, ev[i].beta * inv_d);
+      P.gm[eo] = -ev[i].beta * inv_d;
+      gb += (double)ev[i].gamma * (double)inv_d;
+      be = ev[i].bits;
+    }
+    if (o < P.N) {
       const int64_t oo = o * kC + c;
-      P.yhat[oo] = on.yhat;
-      P.gy[oo] = on.beta * inv_d;
+      const float gmo = -od[i].beta * inv_d;
+      P.yhat[oo] = od[i].yhat;
+      P.gy[oo] = od[i].beta * inv_d;
       P.gm[oo] = gmo;
+      ga += (double)gmo * (double)nbs[i];
+      gb += (double)od[i].gamma * (double)inv_d;
+      bo = od[i].bits;
     }
-    // the even row: its reconstruction feeds the means of rows e - 1 and e + 1
-    const float gme = -oe.beta * inv_d;
-    const float gm_next = -on.beta * inv_d;
-    const int64_t eo = e * kC + c;
-    P.yhat[eo] = oe.yhat;
-    P.gy[eo] = fmaf(k.a, gm_prev + gm_next, oe.beta * inv_d);
-    P.gm[eo] = gme;
-    gb += (double)oe.gamma * (double)inv_d;
-    const float be = wave_sum(oe.bits);
-    const float bo = wave_sum(on.bits);
-    if (lane == 0) {
-      P.bits_part[wv * P.N + e] = be;
-      if (o < P.N) P.bits_part[wv * P.N + o] = bo;
+    lb[le * kRateCols + lt] = be;
+    lb[(le + 1) * kRateCols + lt] = bo;
+  }
+  __syncthreads();
+  // per-token bits of this block's columns: 16 lanes per row, 16 columns each
+  {
+    const int row = lt >> 4, part = lt & 15;
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < kRateCols / 16; ++q) sum += lb[row * kRateCols + q * 16 + part];
+    sum = wave_sum16(sum);
+    if (part == 0 && j0 + row < P.N) P.bits_part[cb * P.N + j0 + row] = sum;
+  }
+  P.ga_part[(int64_t)chunk * kC + c] = (float)ga;
+  P.gb_part[(int64_t)chunk * kC + c] = (float)gb;
+  const int any = __syncthreads_or(bad ? 1 : 0);
+  if (lt == 0) P.flags[t] = any;
+}
+
+constexpr int kParCols = 64;              // components per reduction workgroup (one wave's row)
+constexpr int kParGroups = 256 / kParCols;  // partial rows summed side by side
+constexpr int kParSeg = 64;               // partial rows per first-stage workgroup
+
+// The reductions after k_rate, by workgroup:
+//   [0, nb)            per-token bits of 256 rows: the column-block partials in
+//                      a fixed order; and the OR of the bad-input flags of the
+//                      chunks those rows fall in
+//   [nb, nb + C/64 S)  first stage of dR/da and dR/db: 64 components x one
+//                      segment of kParSeg partial rows, summed by 4 groups
+//                      (row i in group i % 4) in fp64, then the groups in order
+struct FinishP {
+  const float *bits_part;
+  const float *ga_part, *gb_part;
+  double *ga_seg, *gb_seg;  // [S][C]
+  const int32_t *flags;
+  int32_t *flags2;          // [nb]
+  float *bits, *ga, *gb;
+  int32_t *status;
+  int64_t N, parts, n_flags;
+  int nb, n_seg;
+};
+
+__global__ __launch_bounds__(256) void k_rate_finish(FinishP P) {
+  __shared__ double sa[kParGroups][kParCols], sb[kParGroups][kParCols];
+  const int b = blockIdx.x;
+  if (b < P.nb) {
+    const int64_t j = (int64_t)b * 256 + threadIdx.x;
+    if (j < P.N) {
+      float s = 0.f;
+      for (int w = 0; w < kRateParts; ++w) s += P.bits_part[w * P.N + j];
+      P.bits[j] = s;
     }
-    gm_prev = gm_next;
-    oe = onext;
+    // flags of chunks [16 b, 16 b + 16): (chunk, column block) pairs at t = 8 chunk + cb
+    const int64_t f = (int64_t)b * (256 / kRateRows) * kRateParts + threadIdx.x;
+    const int any = __syncthreads_or(threadIdx.x < (256 / kRateRows) * kRateParts && f < P.n_flags ? P.flags[f] : 0);
+    if (threadIdx.x == 0) P.flags2[b] = any;
+    return;
   }
-  P.ga_part[(int64_t)blockIdx.y * kC + c] = ga;
-  P.gb_part[(int64_t)blockIdx.y * kC + c] = gb;
-  if (bad) *P.status = DCKV_EINVAL;
-}
-
-// per-token bits: the wave partials in a fixed order
-__global__ __launch_bounds__(256) void k_rate_bits(const float *part, int64_t N, float *bits) {
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (j >= N) return;
-  float s = 0.f;
-  for (int w = 0; w < kRateWaves; ++w) s += part[w * N + j];
-  bits[j] = s;
-}
-
-// per-component sums over the chunks
-__global__ __launch_bounds__(256) void k_rate_params(const double *ga_part, const double *gb_part, int chunks,
-                                                     float *ga, float *gb) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  double a = 0.0, b = 0.0;
-  for (int i = 0; i < chunks; ++i) {
-    a += ga_part[(int64_t)i * kC + c];
-    b += gb_part[(int64_t)i * kC + c];
+  const int bb = b - P.nb;
+  const int cg = bb % (kC / kParCols), seg = bb / (kC / kParCols);
+  const int col = threadIdx.x % kParCols, grp = threadIdx.x / kParCols;
+  const int c = cg * kParCols + col;
+  const int64_t lo = (int64_t)seg * kParSeg, hi = min(lo + kParSeg, P.parts);
+  double a = 0.0, g = 0.0;
+  for (int64_t i = lo + grp; i < hi; i += kParGroups) {
+    a += P.ga_part[i * kC + c];
+    g += P.gb_part[i * kC + c];
   }
-  ga[c] = (float)a;
-  gb[c] = (float)b;
+  sa[grp][col] = a;
+  sb[grp][col] = g;
+  __syncthreads();
+  if (threadIdx.x < kParCols) {
+    double ta = 0.0, tb = 0.0;
+    for (int k = 0; k < kParGroups; ++k) {
+      ta += sa[k][threadIdx.x];
+      tb += sb[k][threadIdx.x];
+    }
+    P.ga_seg[(int64_t)seg * kC + c] = ta;
+    P.gb_seg[(int64_t)seg * kC + c] = tb;
+  }
 }
 
-__global__ void k_rate_clear_status(int32_t *status) { *status = 0; }
+// Second stage: workgroups [0, C / 64) add the segments of 64 components (4
+// groups, segment i in group i % 4, then the groups in order); workgroup C / 64
+// sets the status: EINVAL if any k_rate workgroup saw a bad input.
+__global__ __launch_bounds__(256) void k_rate_finish2(FinishP P) {
+  __shared__ double sa[kParGroups][kParCols], sb[kParGroups][kParCols];
+  if (blockIdx.x < kC / kParCols) {
+    const int col = threadIdx.x % kParCols, grp = threadIdx.x / kParCols;
+    const int c = blockIdx.x * kParCols + col;
+    double a = 0.0, g = 0.0;
+    for (int i = grp; i < P.n_seg; i += kParGroups) {
+      a += P.ga_seg[(int64_t)i * kC + c];
+      g += P.gb_seg[(int64_t)i * kC + c];
+    }
+    sa[grp][col] = a;
+    sb[grp][col] = g;
+    __syncthreads();
+    if (threadIdx.x < kParCols) {
+      double ta = 0.0, tb = 0.0;
+      for (int k = 0; k < kParGroups; ++k) {
+        ta += sa[k][threadIdx.x];
+        tb += sb[k][threadIdx.x];
+      }
+      P.ga[c] = (float)ta;
+      P.gb[c] = (float)tb;
+    }
+    return;
+  }
+  int any = 0;
+  for (int i = threadIdx.x; i < P.nb; i += 256) any |= P.flags2[i];
+  any = __syncthreads_or(any);
+  if (threadIdx.x == 0) *P.status = any ? DCKV_EINVAL : 0;
+}
+
+// k-slices of the transform: two when its tiles fill at most half of the 256
+// compute units (k_rate adds at most two partial sets)
+int rate_ksplit(int64_t N) {
+  const int64_t tiles = ((N + kBM - 1) / kBM) * (kC / kBN);
+  return tiles * 2 <= 256 ? 2 : 1;
+}
 
 }  // namespace
 
 RateLayout rate_layout(int64_t N) {
   RateLayout l;
   l.chunks = (N + kRateRows - 1) / kRateRows;
+  l.parts = l.chunks;
+  l.ksplit = rate_ksplit(N);
   uint64_t off = 0;
   auto take = [&](uint64_t bytes) {
     const uint64_t o = off;
     off = (off + bytes + 255) & ~(uint64_t)255;
     return o;
   };
-  l.Y = take((uint64_t)N * kC * 4);
-  l.bits_part = take((uint64_t)kRateWaves * N * 4);
-  l.ga_part = take((uint64_t)l.chunks * kC * 8);
-  l.gb_part = take((uint64_t)l.chunks * kC * 8);
+  l.Y = take((uint64_t)l.ksplit * N * kC * 4);
+  l.bits_part = take((uint64_t)kRateParts * N * 4);
+  l.ga_part = take((uint64_t)l.parts * kC * 4);
+  l.gb_part = take((uint64_t)l.parts * kC * 4);
+  l.flags = take((uint64_t)l.parts * (kC / kRateCols) * 4);
+  l.n_seg = (l.parts + kParSeg - 1) / kParSeg;
+  l.ga_seg = take((uint64_t)l.n_seg * kC * 8);
+  l.gb_seg = take((uint64_t)l.n_seg * kC * 8);
+  l.flags2 = take((uint64_t)(N + 255) / 256 * 4);
   l.total = std::max<uint64_t>(off, 256);
   return l;
 }
@@ -240,10 +359,9 @@ RateLayout rate_layout(int64_t N) {
 void rate_sequence(const RateArgs &a) {
   const dckv_plan_t *p = a.p;
   const hipStream_t s = a.s;
-  hipLaunchKernelGGL(k_rate_clear_status, dim3(1), dim3(1), 0, s, a.status);
   const RateLayout &l = a.l;
-  double *ga_part = reinterpret_cast<double *>(a.ws + l.ga_part);
-  double *gb_part = reinterpret_cast<double *>(a.ws + l.gb_part);
+  float *ga_part = reinterpret_cast<float *>(a.ws + l.ga_part);
+  float *gb_part = reinterpret_cast<float *>(a.ws + l.gb_part);
   if (a.N > 0) {
     float *Y = reinterpret_cast<float *>(a.ws + l.Y);
     GemmF32Args g{};
@@ -257,6 +375,7 @@ void rate_sequence(const RateArgs &a) {
     g.N = kC;
     g.c = Y;
     g.ldc = kC;
+    g.ksplit = l.ksplit;
     launch_gemm_f32(g, s);
     RateP P;
     P.Y = Y;
@@ -274,18 +393,37 @@ void rate_sequence(const RateArgs &a) {
     P.bits_part = reinterpret_cast<float *>(a.ws + l.bits_part);
     P.ga_part = ga_part;
     P.gb_part = gb_part;
-    P.status = a.status;
+    P.flags = reinterpret_cast<int32_t *>(a.ws + l.flags);
     P.N = a.N;
     P.keep_head = p->keep_head;
     P.vocab = p->vocab;
+    P.ksplit = l.ksplit;
+    P.chunks = l.chunks;
     {
       KernelTimer tm("rate", s);
-      hipLaunchKernelGGL(k_rate, dim3(kC / kRateCols, (unsigned)l.chunks), dim3(kRateCols), 0, s, P);
+      hipLaunchKernelGGL(k_rate, dim3((unsigned)(l.chunks * kRateParts)), dim3(kRateCols), 0, s, P);
     }
-    hipLaunchKernelGGL(k_rate_bits, dim3((unsigned)((a.N + 255) / 256)), dim3(256), 0, s, P.bits_part, a.N, a.bits);
   }
-  hipLaunchKernelGGL(k_rate_params, dim3(kC / 256), dim3(256), 0, s, ga_part, gb_part, (int)l.chunks, a.grad_nbr,
-                     a.grad_scale);
+  FinishP F;
+  F.bits_part = reinterpret_cast<const float *>(a.ws + l.bits_part);
+  F.ga_part = ga_part;
+  F.gb_part = gb_part;
+  F.flags = reinterpret_cast<const int32_t *>(a.ws + l.flags);
+  F.bits = a.bits;
+  F.ga = a.grad_nbr;
+  F.gb = a.grad_scale;
+  F.status = a.status;
+  F.N = a.N;
+  F.parts = l.parts;
+  F.n_flags = l.parts * (kC / kRateCols);
+  F.nb = (int)((a.N + 255) / 256);
+  F.n_seg = (int)l.n_seg;
+  F.ga_seg = reinterpret_cast<double *>(a.ws + l.ga_seg);
+  F.gb_seg = reinterpret_cast<double *>(a.ws + l.gb_seg);
+  F.flags2 = reinterpret_cast<int32_t *>(a.ws + l.flags2);
+  const unsigned g1 = (unsigned)(F.nb + (kC / kParCols) * l.n_seg);
+  if (g1 > 0) hipLaunchKernelGGL(k_rate_finish, dim3(g1), dim3(256), 0, s, F);
+  hipLaunchKernelGGL(k_rate_finish2, dim3(kC / kParCols + 1), dim3(256), 0, s, F);
 }
 
 }  // namespace dckv
