@@ -30,7 +30,8 @@ Readings taken where the pages are silent:
     alone is the training rate).
   * Outputs are the total R = sum of bits and its gradients with respect to
     the coefficients y, the embedding means m, the neighbour weights a and the
-    Laplace scales b.  Steps are held fixed.
+    Laplace scales b, and through y = A x and m = H e those with respect to
+    the analysis matrix A and the mean head H.  Steps are held fixed.
 """
 from __future__ import annotations
 
@@ -167,3 +168,20 @@ def coefficients(rows: np.ndarray, tok: np.ndarray, params: dict):
     X = bf16.to_f64(rows[coded_t])
     y = X @ bf16.to_f64(params["analysis"]).T
     return y, ocodec.embedding_mean(params, tok[coded_t])
+
+
+def weight_grads(rows: np.ndarray, tok: np.ndarray, params: dict, r: Rate):
+    """Gradients of the total rate with respect to the analysis matrix and the
+    mean head: y_j = A x_j and m_j = H e_j (e_j the token's input embedding)
+    give dR/dA = sum_j (dR/dy_j) x_j^T and dR/dH = sum_j (dR/dm_j) e_j^T over
+    the coded rows (float64 [C][D] and [C][emb])."""
+    sh = ocodec.shape_of(params)
+    T = rows.shape[0]
+    N, _, coded_t = ocodec.split_positions(T, sh.keep_head, sh.keep_tail)
+    C, D = params["analysis"].shape
+    emb = params["embedding"].shape[1]
+    if N == 0:
+        return np.zeros((C, D)), np.zeros((C, emb))
+    X = bf16.to_f64(rows[coded_t])
+    E = bf16.to_f64(params["embedding"][np.asarray(tok[coded_t], dtype=np.int64)])
+    return r.g_y.T @ X, r.g_m.T @ E

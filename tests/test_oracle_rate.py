@@ -180,3 +180,44 @@ def test_edge_cases():
     rows, tok = tiny_rows(params, 3, seed=2)
     y0, m0 = rate.coefficients(rows, tok, params)
     assert y0.shape == (0, 8)
+
+
+@pytest.mark.parametrize("N", [5, 6])
+def test_weight_gradients_match_finite_differences(N):
+    """dR/dA and dR/dH against central differences of the total rate through the
+    whole forward (y = A x, m = H e recomputed from the perturbed matrix), with
+    the reconstruction held at its straight-through value."""
+    from oracle import bf16
+    params, p, rows, tok, y, m, u = _tiny_request(N, seed=21 + N)
+    a, b = params["nbr_weight"], params["laplace_scale"]
+    r = rate.rate_forward(y, m, p, a, b, u)
+    shift = r.yhat - y
+    gA, gH = rate.weight_grads(rows, tok, params, r)
+    A = bf16.to_f64(params["analysis"])
+    H = bf16.to_f64(params["mean_head"])
+    sh = ocodec.shape_of(params)
+    _, _, coded_t = ocodec.split_positions(rows.shape[0], sh.keep_head, sh.keep_tail)
+    X = bf16.to_f64(rows[coded_t])
+    Eg = bf16.to_f64(params["embedding"][tok[coded_t].astype(np.int64)])
+
+    def total(A2, H2):
+        y2 = X @ A2.T
+        m2 = Eg @ H2.T
+        return rate.rate_terms(y2, m2, y2 + shift, p, a, b, u).total
+
+    h = 1e-6
+    fA = np.zeros_like(A)
+    for c in range(A.shape[0]):
+        for d in range(A.shape[1]):
+            e = np.zeros_like(A)
+            e[c, d] = h
+            fA[c, d] = (total(A + e, H) - total(A - e, H)) / (2 * h)
+    fH = np.zeros_like(H)
+    for c in range(H.shape[0]):
+        for k in range(H.shape[1]):
+            e = np.zeros_like(H)
+            e[c, k] = h
+            fH[c, k] = (total(A, H + e) - total(A, H - e)) / (2 * h)
+    np.testing.assert_allclose(gA, fA, rtol=0, atol=3e-6 * np.max(np.abs(gA)))
+    np.testing.assert_allclose(gH, fH, rtol=0, atol=3e-6 * np.max(np.abs(gH)))
+    assert np.all(gA[~p.active] == 0) and np.all(gH[~p.active] == 0)
