@@ -343,6 +343,24 @@ def training_rate_bench(cfg: int, steps: int, cpu: bool) -> int:
         dk.dckv_profile_only(None)
         tot, n = dk.dckv_profile_read(name)
         kern[name] = tot / max(n, 1)
+    # the weight gradients of the same call's outputs
+    gA, gH = torch.empty((C, 6144), **f32), torch.empty((C, 2048), **f32)
+    wsb = torch.empty(dk.dckv_rate_backward_bytes(plan, T), dtype=torch.uint8, device=dev)
+
+    def run_bwd():
+        dk.dckv_rate_backward(plan, rows, tok, gy, gm, gA, gH, st, wsb)
+
+    for _ in range(3):
+        run_bwd()
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    e0.record(s)
+    for _ in range(steps):
+        run_bwd()
+    e1.record(s)
+    torch.cuda.synchronize()
+    bwd_ms = e0.elapsed_time(e1) / steps
+    bwd_flop = 2.0 * N * C * (6144 + 2048)  # dR/dA and dR/dH, once per product
     rate_bytes = 24.0 * N * C
     gemm_flop = 2.0 * N * 6144 * C
     gbps = rate_bytes / (kern["rate"] * 1e-3) / 1e9
@@ -353,6 +371,9 @@ def training_rate_bench(cfg: int, steps: int, cpu: bool) -> int:
            "kernels": {"rate": {"avg_ms": kern["rate"], "GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS,
                                 "algorithmic_bytes": rate_bytes},
                        "transform_gemm": {"avg_ms": kern["fit_gemm"], "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}},
+           "weight_gradients": {"ms": bwd_ms, "tflops": bwd_flop / (bwd_ms * 1e-3) / 1e12,
+                                "note": "dR/dA and dR/dH; the gradients enter as two bf16 halves, so the "
+                                        "MFMA work is twice these flops"},
            "cpu_baseline": None}
     if cpu:
         from oracle import rate as orate

@@ -131,7 +131,10 @@ int dckv_plan_mean_table(const dckv_plan_t *plan, const float **table, int64_t *
 
 /* Pure host.  For a request of T tokens: the largest stream an encode can
  * produce (every code escaped or 16 bits) and the workspace bytes that
- * dckv_encode / dckv_decode / the entropy stages need. */
+ * dckv_encode / dckv_decode / the entropy stages need.  T <= 2^18 positions:
+ * the kernels address each [T][D] operand through 32-bit byte offsets, so
+ * longer requests return DCKV_EUNSUPPORTED (here and in every call that
+ * takes T). */
 int dckv_bytes(const dckv_plan_t *plan, int64_t T, uint64_t *max_stream_bytes,
                uint64_t *workspace_bytes);
 
@@ -317,7 +320,7 @@ int dckv_profile_read(const char *kernel, double *total_ms, int64_t *launches);
  * (E^T Y keeps 16 mantissa bits of Y) with a blocked Cholesky solve; a Gram
  * matrix plus ridge that is not positive definite, or a token id outside
  * [0, vocab), sets *status to DCKV_EINVAL.  The workspace (dckv_fit_bytes)
- * is about 28 KiB per calibration row plus 42 MiB.  2 <= n <= 2^22.
+ * is about 28 KiB per calibration row plus 42 MiB.  2 <= n <= 2^18.
  * --------------------------------------------------------------------------*/
 int dckv_fit_bytes(int64_t n, uint64_t *workspace_bytes);
 int dckv_fit(const dckv_params *p, const uint16_t *rows, const int32_t *token_ids, int64_t n, float ridge,
@@ -356,13 +359,32 @@ int dckv_fit(const dckv_params *p, const uint16_t *rows, const int32_t *token_id
  * dckv_rate_bytes); nothing is allocated.  Arguments are checked
  * synchronously (negative return, nothing enqueued); a non-finite y - mu or a
  * token id outside [0, vocab) sets *status to DCKV_EINVAL on the device.
- * The workspace is about 8.3 KiB per coded row.
+ * The workspace is about 8.3 KiB per coded row (16.3 KiB up to 4,096 coded
+ * rows, where the transform is split in two k ranges).  T <= 2^18.
  * --------------------------------------------------------------------------*/
 int dckv_rate_bytes(const dckv_plan_t *plan, int64_t T, uint64_t *workspace_bytes);
 int dckv_rate_forward(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *token_ids, int64_t T,
                       const float *noise, float *bits_out, float *yhat_out, float *grad_y, float *grad_mean,
                       float *grad_nbr, float *grad_scale, int32_t *status, void *workspace,
                       uint64_t workspace_bytes, void *hip_stream);
+
+/* Weight gradients through the codec's transforms (same passage): with
+ * y_j = A x_j and m_j = H e_j (x_j the coded row at t = j + keep_head, e_j the
+ * input embedding of its token),
+ *   grad_analysis  [n_coef][D]     fp32  = sum_j grad_y[j] x_j^T
+ *   grad_mean_head [n_coef][emb]   fp32  = sum_j grad_mean[j] e_j^T
+ * over the N coded rows.  grad_y and grad_mean ([N][n_coef] fp32) are any
+ * upstream gradients, e.g. dckv_rate_forward's, plus a distortion term's.
+ * The products run on the bf16 MFMA with fp32 accumulation; the gradients
+ * enter as two bf16 halves (16 mantissa bits), rows and embeddings are exact.
+ * Caller-owned device memory throughout (rows 16-byte, the rest 4-byte
+ * aligned, workspace 256-byte aligned and at least dckv_rate_backward_bytes,
+ * about 32 KiB per coded row); a token id outside [0, vocab) sets *status to
+ * DCKV_EINVAL.  T <= 2^18. */
+int dckv_rate_backward_bytes(const dckv_plan_t *plan, int64_t T, uint64_t *workspace_bytes);
+int dckv_rate_backward(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *token_ids, int64_t T,
+                       const float *grad_y, const float *grad_mean, float *grad_analysis, float *grad_mean_head,
+                       int32_t *status, void *workspace, uint64_t workspace_bytes, void *hip_stream);
 
 const char *dckv_last_error(void);
 

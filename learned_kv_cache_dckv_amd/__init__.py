@@ -29,7 +29,7 @@ EXPORTS = ("dckv_plan_tables", "dckv_plan", "dckv_plan_free", "dckv_plan_info", 
            "dckv_decode", "dckv_decode_heads", "dckv_unrope", "dckv_bytes_batch", "dckv_encode_batch", "dckv_decode_batch", "dckv_entropy_encode",
            "dckv_entropy_decode", "dckv_workspace_view", "dckv_profile_enable", "dckv_profile_only", "dckv_profile_reset",
            "dckv_profile_read", "dckv_fit_bytes", "dckv_fit", "dckv_rate_bytes", "dckv_rate_forward",
-           "dckv_last_error")
+           "dckv_rate_backward_bytes", "dckv_rate_backward", "dckv_last_error")
 
 
 class DckvError(RuntimeError):
@@ -88,6 +88,8 @@ def _load():
         "dckv_fit": [P, P, P, I64, F, P, P, P, P, P, P, U64, P],
         "dckv_rate_bytes": [P, I64, P],
         "dckv_rate_forward": [P, P, P, I64, P, P, P, P, P, P, P, P, P, U64, P],
+        "dckv_rate_backward_bytes": [P, I64, P],
+        "dckv_rate_backward": [P, P, P, I64, P, P, P, P, P, P, U64, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -463,6 +465,35 @@ def rate_forward(plan: Plan, rows, token_ids, noise, ws=None):
     torch.cuda.synchronize()
     out["status"] = int(st.item())
     return out
+
+
+def dckv_rate_backward_bytes(plan: Plan, T: int) -> int:
+    v = ctypes.c_uint64()
+    _check(_lib.dckv_rate_backward_bytes(plan.handle, int(T), ctypes.byref(v)))
+    return v.value
+
+
+def dckv_rate_backward(plan: Plan, rows, token_ids, grad_y, grad_mean, grad_analysis, grad_mean_head, status, ws,
+                       stream=None):
+    _check(_lib.dckv_rate_backward(plan.handle, _ptr(rows), _ptr(token_ids), int(token_ids.shape[0]), _ptr(grad_y),
+                                   _ptr(grad_mean), _ptr(grad_analysis), _ptr(grad_mean_head), _ptr(status),
+                                   _ptr(ws), ws.numel(), _stream_handle(stream)))
+
+
+def rate_backward(plan: Plan, rows, token_ids, grad_y, grad_mean, ws=None):
+    """Weight gradients (dR/dA [n_coef][D], dR/dH [n_coef][emb], fp32 device
+    tensors) for upstream gradients grad_y, grad_mean [N][n_coef]; and the status."""
+    import torch
+    dev = rows.device
+    c = plan.codec
+    gA = torch.empty((c.n_coef, c.D), dtype=torch.float32, device=dev)
+    gH = torch.empty((c.n_coef, c.emb_dim), dtype=torch.float32, device=dev)
+    st = torch.full((1,), 777, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = torch.empty(dckv_rate_backward_bytes(plan, int(token_ids.shape[0])), dtype=torch.uint8, device=dev)
+    dckv_rate_backward(plan, rows, token_ids, grad_y, grad_mean, gA, gH, st, ws)
+    torch.cuda.synchronize()
+    return gA, gH, int(st.item())
 
 
 def dckv_workspace_view(plan: Plan, T: int, which: int):

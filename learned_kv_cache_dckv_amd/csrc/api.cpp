@@ -36,6 +36,7 @@ int common_checks(const dckv_plan_t *p, int64_t T, void *ws, uint64_t ws_bytes, 
                   Layout &l) {
   if (!p) return set_error(DCKV_EINVAL, "null plan");
   if (T < 0 || T > 0x7FFFFFFF) return set_error(DCKV_EINVAL, "T out of range");
+  if (T > kMaxRows) return set_error(DCKV_EUNSUPPORTED, "T above 2^18 positions (32-bit operand offsets)");
   if (!status || !aligned(status, 4)) return set_error(DCKV_EINVAL, "status must be a 4-byte aligned device word");
   if (!ws || !aligned(ws, 256)) return set_error(DCKV_EINVAL, "workspace must be 256-byte aligned");
   g = geometry(p, T);
@@ -249,7 +250,7 @@ extern "C" int dckv_entropy_decode(const dckv_plan_t *plan, const uint8_t *strea
 }
 
 extern "C" int dckv_fit_bytes(int64_t n, uint64_t *workspace_bytes) {
-  if (n < 2 || n > (int64_t)1 << 22) return set_error(DCKV_EINVAL, "fit: n must be in [2, 2^22]");
+  if (n < 2 || n > kMaxRows) return set_error(DCKV_EINVAL, "fit: n must be in [2, 2^18]");
   if (!workspace_bytes) return set_error(DCKV_EINVAL, "fit: null workspace_bytes");
   *workspace_bytes = fit_layout(n).total;
   return DCKV_OK;
@@ -299,8 +300,7 @@ extern "C" int dckv_fit(const dckv_params *p, const uint16_t *rows, const int32_
 
 extern "C" int dckv_rate_bytes(const dckv_plan_t *plan, int64_t T, uint64_t *workspace_bytes) {
   if (!plan) return set_error(DCKV_EINVAL, "rate: null plan");
-  if (T < 0 || T > ((int64_t)1 << 22) + plan->keep_head + plan->keep_tail)
-    return set_error(DCKV_EINVAL, "rate: T out of range (at most 2^22 coded rows)");
+  if (T < 0 || T > kMaxRows) return set_error(DCKV_EINVAL, "rate: T out of range (at most 2^18 positions)");
   if (!workspace_bytes) return set_error(DCKV_EINVAL, "rate: null workspace_bytes");
   *workspace_bytes = rate_layout(geometry(plan, T).N).total;
   return DCKV_OK;
@@ -348,6 +348,57 @@ extern "C" int dckv_rate_forward(const dckv_plan_t *plan, const uint16_t *rows, 
   a.s = static_cast<hipStream_t>(hip_stream);
   rate_sequence(a);
   return after_launch("dckv_rate_forward");
+}
+
+extern "C" int dckv_rate_backward_bytes(const dckv_plan_t *plan, int64_t T, uint64_t *workspace_bytes) {
+  if (!plan) return set_error(DCKV_EINVAL, "rate backward: null plan");
+  if (T < 0 || T > kMaxRows) return set_error(DCKV_EINVAL, "rate backward: T out of range (at most 2^18 positions)");
+  if (!workspace_bytes) return set_error(DCKV_EINVAL, "rate backward: null workspace_bytes");
+  *workspace_bytes = rate_bwd_layout(geometry(plan, T).N).total;
+  return DCKV_OK;
+}
+
+extern "C" int dckv_rate_backward(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *token_ids,
+                                  int64_t T, const float *grad_y, const float *grad_mean, float *grad_analysis,
+                                  float *grad_mean_head, int32_t *status, void *workspace, uint64_t workspace_bytes,
+                                  void *hip_stream) {
+  uint64_t need = 0;
+  int rc = dckv_rate_backward_bytes(plan, T, &need);
+  if (rc) return rc;
+  if (plan->D != kD || plan->C != kC || plan->emb != kEmb)
+    return set_error(DCKV_EUNSUPPORTED, "rate backward: the kernels support D=6144, n_coef=2048, emb_dim=2048");
+  const int64_t N = geometry(plan, T).N;
+  if (N > 0) {
+    if (!rows || !aligned(rows, 16) || !token_ids || !aligned(token_ids, 4))
+      return set_error(DCKV_EINVAL, "rate backward: rows must be 16-byte aligned, token_ids 4-byte aligned");
+    if (!grad_y || !grad_mean || !aligned(grad_y, 4) || !aligned(grad_mean, 4))
+      return set_error(DCKV_EINVAL, "rate backward: null or misaligned grad_y / grad_mean");
+  }
+  if (!grad_analysis || !grad_mean_head || !aligned(grad_analysis, 4) || !aligned(grad_mean_head, 4))
+    return set_error(DCKV_EINVAL, "rate backward: null or misaligned grad_analysis / grad_mean_head");
+  if (!status || !aligned(status, 4))
+    return set_error(DCKV_EINVAL, "rate backward: status must be a 4-byte aligned device word");
+  if (!workspace || !aligned(workspace, 256))
+    return set_error(DCKV_EINVAL, "rate backward: workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return set_error(DCKV_ECAPACITY, "rate backward: workspace smaller than dckv_rate_backward_bytes()");
+  rc = check_device(plan);
+  if (rc) return rc;
+  RateBwdArgs a;
+  a.p = plan;
+  a.l = rate_bwd_layout(N);
+  a.ws = static_cast<uint8_t *>(workspace);
+  a.rows = rows;
+  a.tok = token_ids;
+  a.grad_y = grad_y;
+  a.grad_mean = grad_mean;
+  a.N = N;
+  a.grad_A = grad_analysis;
+  a.grad_H = grad_mean_head;
+  a.status = status;
+  a.s = static_cast<hipStream_t>(hip_stream);
+  rate_bwd_sequence(a);
+  return after_launch("dckv_rate_backward");
 }
 
 extern "C" int dckv_unrope(const dckv_plan_t *plan, const uint16_t *rows_in, int64_t T, uint16_t *rows_out,

@@ -32,6 +32,10 @@ constexpr int kBK = 64;
 
 // fixed shapes supported by the kernels
 constexpr int kD = 6144;
+// Positions of one request (and calibration rows of a fit): the GEMMs address
+// each operand through one buffer resource with 32-bit byte offsets, so a
+// [rows][6,144] bf16 operand must stay below 4 GiB; 2^18 rows is 3 GiB.
+constexpr int64_t kMaxRows = (int64_t)1 << 18;
 constexpr int kC = 2048;
 constexpr int kHid = 256;
 constexpr int kEmb = 2048;
@@ -192,6 +196,8 @@ struct GemmF32Args {
   int n_mt, n_nt;  // set by the launcher
 };
 void launch_gemm_f32(const GemmF32Args &args, hipStream_t s);
+// two independent products in one launch (the second's workgroups follow the first's)
+void launch_gemm_f32_pair(const GemmF32Args &a, const GemmF32Args &b, hipStream_t s);
 
 // fit.hip: the closed-form fit of the conditional models
 constexpr int kFitChunks = 64;  // row chunks of the per-component sums
@@ -215,6 +221,13 @@ struct FitArgs {
   hipStream_t s;
 };
 void fit_sequence(const FitArgs &a);
+// shared with the rate's weight gradients: clear a status word; gather E[tok]
+// transposed to [emb][n_pad] bf16 (EINVAL for a bad id); split fp32 [n][C]
+// into transposed bf16 high and low halves [C][n_pad] (zero past n)
+void launch_clear_status(int32_t *status, hipStream_t s);
+void launch_gather_t(const uint16_t *E, const int32_t *tok, int64_t n, int64_t n_pad, int vocab, uint16_t *Et,
+                     int32_t *tokc, int32_t *status, hipStream_t s);
+void launch_split_t(const float *Y, int64_t n, int64_t n_pad, uint16_t *hi, uint16_t *lo, hipStream_t s);
 
 // rate.hip: the training rate (additive-noise likelihood) and its gradients
 struct RateLayout {
@@ -238,6 +251,25 @@ struct RateArgs {
   hipStream_t s;
 };
 void rate_sequence(const RateArgs &a);
+// the weight gradients dR/dA = G_y^T X and dR/dH = G_m^T E[tok]
+struct RateBwdLayout {
+  int64_t n_pad = 0;  // N rounded up to 64 (the inner dimension)
+  uint64_t gy_hi = 0, gy_lo = 0, gm_hi = 0, gm_lo = 0, Xt = 0, Et = 0, tokc = 0, total = 0;
+};
+RateBwdLayout rate_bwd_layout(int64_t N);
+struct RateBwdArgs {
+  const dckv_plan_t *p;
+  RateBwdLayout l;
+  uint8_t *ws;
+  const uint16_t *rows;
+  const int32_t *tok;
+  const float *grad_y, *grad_mean;
+  int64_t N;
+  float *grad_A, *grad_H;
+  int32_t *status;
+  hipStream_t s;
+};
+void rate_bwd_sequence(const RateBwdArgs &a);
 void launch_analysis_gemm(const EncodeArgs &a);
 void launch_encode_fixup(const EncodeArgs &a);
 void launch_dequant(const DecodeArgs &a);

@@ -284,6 +284,20 @@ __global__ void k_fit_ab_reduce(const double *part, int chunks, int64_t n, float
 
 }  // namespace
 
+void launch_clear_status(int32_t *status, hipStream_t s) {
+  hipLaunchKernelGGL(k_fit_clear_status, dim3(1), dim3(1), 0, s, status);
+}
+
+void launch_gather_t(const uint16_t *E, const int32_t *tok, int64_t n, int64_t n_pad, int vocab, uint16_t *Et,
+                     int32_t *tokc, int32_t *status, hipStream_t s) {
+  hipLaunchKernelGGL(k_fit_gather_t, dim3((unsigned)(n_pad / 64), kEmb / 64), dim3(256), 0, s, E, tok, n, n_pad,
+                     vocab, Et, tokc, status);
+}
+
+void launch_split_t(const float *Y, int64_t n, int64_t n_pad, uint16_t *hi, uint16_t *lo, hipStream_t s) {
+  hipLaunchKernelGGL(k_fit_split_t, dim3((unsigned)(n_pad / 64), kC / 64), dim3(256), 0, s, Y, n, n_pad, hi, lo);
+}
+
 FitLayout fit_layout(int64_t n) {
   FitLayout l;
   l.n_pad = (n + 63) / 64 * 64;

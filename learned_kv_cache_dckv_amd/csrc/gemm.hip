@@ -395,14 +395,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_mean_table(MeanTabP P) {
 // fit: C[m][n] = sum_k A[m][k] B[n][k] with fp32 output (bf16 operands, two
 // k-ranges per operand, optional row gather for A)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_f32(GemmF32Args P) {
+// Two independent products may share one launch (workgroups [0, blocks0) do
+// the first), so that small ones fill the chip together.
+struct GemmF32Pair {
+  GemmF32Args g0, g1;
+  int blocks0;
+};
+
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_f32(GemmF32Pair PP) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
+  const bool second = (int)blockIdx.x >= PP.blocks0;
+  const GemmF32Args &P = second ? PP.g1 : PP.g0;
+  const int bid = second ? (int)blockIdx.x - PP.blocks0 : (int)blockIdx.x;
   int mt, nt;
   // k-slice ks of ksplit (single-source operands): k-tiles [ks KT, (ks + 1) KT)
   // into the output slice c + ks M ldc
   const int tiles = P.n_mt * P.n_nt;
-  const int ks = blockIdx.x / tiles;
-  tile_of(blockIdx.x - ks * tiles, tiles, P.n_nt, mt, nt);
+  const int ks = bid / tiles;
+  tile_of(bid - ks * tiles, tiles, P.n_nt, mt, nt);
   const int KT = P.KT / P.ksplit;
   const size_t koff = (size_t)ks * KT * kRowBytes;
   const int split = P.ksplit > 1 ? KT : P.split;
@@ -1266,12 +1276,28 @@ static void launch_gemm(K kernel, const char *name, int grid, const P &prm, hipS
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), kLdsBytes, s, prm);
 }
 
-void launch_gemm_f32(const GemmF32Args &args, hipStream_t s) {
-  GemmF32Args P = args;
+static int prepare_f32(GemmF32Args &P) {
   P.n_mt = (P.M + kBM - 1) / kBM;
   P.n_nt = (P.N + kBN - 1) / kBN;
   if (P.ksplit < 1) P.ksplit = 1;
-  launch_gemm(k_gemm_f32, "fit_gemm", P.n_mt * P.n_nt * P.ksplit, P, s);
+  return P.n_mt * P.n_nt * P.ksplit;
+}
+
+void launch_gemm_f32(const GemmF32Args &args, hipStream_t s) {
+  GemmF32Pair PP;
+  PP.g0 = args;
+  PP.blocks0 = prepare_f32(PP.g0);
+  PP.g1 = PP.g0;
+  launch_gemm(k_gemm_f32, "fit_gemm", PP.blocks0, PP, s);
+}
+
+void launch_gemm_f32_pair(const GemmF32Args &a, const GemmF32Args &b, hipStream_t s) {
+  GemmF32Pair PP;
+  PP.g0 = a;
+  PP.g1 = b;
+  PP.blocks0 = prepare_f32(PP.g0);
+  const int blocks1 = prepare_f32(PP.g1);
+  launch_gemm(k_gemm_f32, "fit_gemm", PP.blocks0 + blocks1, PP, s);
 }
 
 int build_mean_table(dckv_plan_t *p) {

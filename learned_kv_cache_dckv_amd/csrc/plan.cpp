@@ -421,6 +421,7 @@ extern "C" int dckv_bytes(const dckv_plan_t *plan, int64_t T, uint64_t *max_stre
                           uint64_t *workspace_bytes) {
   if (!plan) return set_error(DCKV_EINVAL, "bytes: null plan");
   if (T < 0 || T > (int64_t)0x7FFFFFFF) return set_error(DCKV_EINVAL, "bytes: T out of range");
+  if (T > kMaxRows) return set_error(DCKV_EUNSUPPORTED, "bytes: T above 2^18 positions (32-bit operand offsets)");
   Geometry g = geometry(plan, T);
   // a coded position costs at most one 16-bit word or one 8-byte escape record;
   // each substream adds a two-word flush

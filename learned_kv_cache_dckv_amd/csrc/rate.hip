@@ -330,7 +330,95 @@ int rate_ksplit(int64_t N) {
   return tiles * 2 <= 256 ? 2 : 1;
 }
 
+// Xt[d][j] = rows[keep_head + j][d] for j < N, 0 for N <= j < n_pad (bf16,
+// transposed through a 64 x 64 LDS tile)
+__global__ __launch_bounds__(256) void k_rate_rows_t(const uint16_t *X, int64_t N, int64_t n_pad, uint16_t *Xt) {
+  __shared__ uint16_t t[64][65];
+  const int64_t j0 = (int64_t)blockIdx.x * 64;
+  const int d0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t j = j0 + r;
+    t[r][tx] = j < N ? X[j * kD + d0 + tx] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) Xt[(int64_t)(d0 + r) * n_pad + j0 + tx] = t[tx][r];
+}
+
+__global__ __launch_bounds__(256) void k_rate_zero(float *p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
+}
+
 }  // namespace
+
+RateBwdLayout rate_bwd_layout(int64_t N) {
+  RateBwdLayout l;
+  l.n_pad = (N + 63) / 64 * 64;
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t o = off;
+    off = (off + bytes + 255) & ~(uint64_t)255;
+    return o;
+  };
+  const uint64_t np = (uint64_t)l.n_pad;
+  l.gy_hi = take(np * kC * 2);
+  l.gy_lo = take(np * kC * 2);
+  l.gm_hi = take(np * kC * 2);
+  l.gm_lo = take(np * kC * 2);
+  l.Xt = take(np * kD * 2);
+  l.Et = take(np * kEmb * 2);
+  l.tokc = take(np * 4);
+  l.total = std::max<uint64_t>(off, 256);
+  return l;
+}
+
+// dR/dA[c][d] = sum_j G_y[j][c] x_j[d] and dR/dH[c][e] = sum_j G_m[j][c] E[tok_j][e]
+// on the fp32-output MFMA GEMM: the gradients enter as transposed bf16 high and
+// low halves (16 mantissa bits) over two k ranges against the same transposed
+// bf16 rows / gathered embeddings, so the products of the halves add up.
+void rate_bwd_sequence(const RateBwdArgs &a) {
+  const dckv_plan_t *p = a.p;
+  const hipStream_t s = a.s;
+  const RateBwdLayout &l = a.l;
+  launch_clear_status(a.status, s);
+  if (a.N == 0) {  // (a fill kernel, not a memset: the sequence may be captured in a graph)
+    hipLaunchKernelGGL(k_rate_zero, dim3(1024), dim3(256), 0, s, a.grad_A, (int64_t)kC * kD);
+    hipLaunchKernelGGL(k_rate_zero, dim3(256), dim3(256), 0, s, a.grad_H, (int64_t)kC * kEmb);
+    return;
+  }
+  const int64_t np = l.n_pad;
+  uint16_t *gy_hi = reinterpret_cast<uint16_t *>(a.ws + l.gy_hi), *gy_lo = reinterpret_cast<uint16_t *>(a.ws + l.gy_lo);
+  uint16_t *gm_hi = reinterpret_cast<uint16_t *>(a.ws + l.gm_hi), *gm_lo = reinterpret_cast<uint16_t *>(a.ws + l.gm_lo);
+  uint16_t *Xt = reinterpret_cast<uint16_t *>(a.ws + l.Xt), *Et = reinterpret_cast<uint16_t *>(a.ws + l.Et);
+  int32_t *tokc = reinterpret_cast<int32_t *>(a.ws + l.tokc);
+  launch_split_t(a.grad_y, a.N, np, gy_hi, gy_lo, s);
+  launch_split_t(a.grad_mean, a.N, np, gm_hi, gm_lo, s);
+  hipLaunchKernelGGL(k_rate_rows_t, dim3((unsigned)(np / 64), kD / 64), dim3(256), 0, s,
+                     a.rows + (size_t)p->keep_head * kD, a.N, np, Xt);
+  launch_gather_t(p->E, a.tok + p->keep_head, a.N, np, p->vocab, Et, tokc, a.status, s);
+  GemmF32Args g{};
+  g.a0 = gy_hi;
+  g.a1 = gy_lo;
+  g.lda0 = g.lda1 = (uint32_t)(np * 2);
+  g.b0 = g.b1 = Xt;
+  g.ldb0 = g.ldb1 = (uint32_t)(np * 2);
+  g.split = (int)(np / kBK);
+  g.KT = 2 * g.split;
+  g.arow = nullptr;
+  g.M = kC;
+  g.N = kD;
+  g.c = a.grad_A;
+  g.ldc = kD;
+  GemmF32Args h = g;
+  h.a0 = gm_hi;
+  h.a1 = gm_lo;
+  h.b0 = h.b1 = Et;
+  h.N = kEmb;
+  h.c = a.grad_H;
+  h.ldc = kEmb;
+  // 192 + 64 tiles of the same depth: one launch fills the 256 compute units
+  launch_gemm_f32_pair(g, h, s);
+}
 
 RateLayout rate_layout(int64_t N) {
   RateLayout l;

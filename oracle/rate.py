@@ -175,6 +175,11 @@ def weight_grads(rows: np.ndarray, tok: np.ndarray, params: dict, r: Rate):
     mean head: y_j = A x_j and m_j = H e_j (e_j the token's input embedding)
     give dR/dA = sum_j (dR/dy_j) x_j^T and dR/dH = sum_j (dR/dm_j) e_j^T over
     the coded rows (float64 [C][D] and [C][emb])."""
+    return weight_grads_of(rows, tok, params, r.g_y, r.g_m)
+
+
+def weight_grads_of(rows: np.ndarray, tok: np.ndarray, params: dict, g_y: np.ndarray, g_m: np.ndarray):
+    """The same products for any upstream gradients g_y, g_m [N][C]."""
     sh = ocodec.shape_of(params)
     T = rows.shape[0]
     N, _, coded_t = ocodec.split_positions(T, sh.keep_head, sh.keep_tail)
@@ -184,4 +189,4 @@ def weight_grads(rows: np.ndarray, tok: np.ndarray, params: dict, r: Rate):
         return np.zeros((C, D)), np.zeros((C, emb))
     X = bf16.to_f64(rows[coded_t])
     E = bf16.to_f64(params["embedding"][np.asarray(tok[coded_t], dtype=np.int64)])
-    return r.g_y.T @ X, r.g_m.T @ E
+    return np.asarray(g_y, np.float64).T @ X, np.asarray(g_m, np.float64).T @ E

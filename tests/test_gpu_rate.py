@@ -1,5 +1,7 @@
 """The training rate (additive-noise likelihood, straight-through
-reconstruction) and its gradients on the GPU against the oracle.
+reconstruction) and its gradients on the GPU against the oracle, and the
+weight gradients through the transforms (dR/dA, dR/dH) for seeded upstream
+gradients, within their derived elementwise bound.
 
 Workloads: the 512-token and 4,096-token prompts (a training sample is a
 4,096-token prompt) with seeded uniform noise, plus edge cases: no coded rows,
@@ -172,3 +174,67 @@ def test_rate_status_of_bad_inputs():
     bad_rows[4 + 5, 100] = 0x7F80  # +inf
     assert _gpu_rate(plan, bad_rows, tok, u)["status"] == -1  # EINVAL
     assert _gpu_rate(plan, rows, tok, u)["status"] == 0
+
+
+def _check_weight_grads(params, rows, tok, gy, gm, gA, gH, label):
+    """Elementwise bound: the gradients enter as two bf16 halves (relative
+    error 2^-16) and the products accumulate in fp32 over K = 2 n_pad terms, so
+    |error| <= (2^-16 + K 2^-24) times the product of the magnitudes."""
+    wA, wH = orate.weight_grads_of(rows, tok, params, gy, gm)
+    sh = ocodec.shape_of(params)
+    N = rows.shape[0] - sh.keep_head - sh.keep_tail
+    K = 2 * ((N + 63) // 64 * 64)
+    f = 2.0 ** -16 + K * 2.0 ** -24
+    # |g|^T |x|: the rows' magnitudes (bf16 values are exact in float64)
+    _, _, coded_t = ocodec.split_positions(rows.shape[0], sh.keep_head, sh.keep_tail)
+    X = np.abs(orate.bf16.to_f64(rows[coded_t]))
+    Eg = np.abs(orate.bf16.to_f64(params["embedding"][tok[coded_t].astype(np.int64)]))
+    bA = f * (np.abs(gy).T @ X)
+    bH = f * (np.abs(gm).T @ Eg)
+    for name, got, want, bar in (("dA", gA, wA, bA), ("dH", gH, wH, bH)):
+        e = np.abs(got.astype(np.float64) - want)
+        rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+        gu.say("  %s: %s rel L2 %.3g, worst %.3g of the bound" % (label, name, rel, float(np.max(e / bar))))
+        assert np.all(e <= bar), name
+
+
+@pytest.mark.parametrize("cfg", [0, 1], ids=["tiny-512", "prompt-4k"])
+def test_rate_weight_gradients(cfg):
+    import torch
+    req = synth.make_request(cfg)
+    params = synth.world().params()
+    plan = gu.device_codec().plan(req.step_scale)
+    N = req.T - 132
+    rng = np.random.default_rng(300 + cfg)
+    gy = (rng.standard_normal((N, 2048)) * rng.uniform(0.1, 30.0, 2048)).astype(np.float32)
+    gm = (-gy + rng.standard_normal((N, 2048)).astype(np.float32)).astype(np.float32)
+    gA, gH, st = gu.dk().rate_backward(plan, gu.rows_dev(req.rows), gu.to_dev(req.token_ids.astype(np.int32)),
+                                       gu.to_dev(gy), gu.to_dev(gm))
+    assert st == 0
+    _check_weight_grads(params, req.rows, req.token_ids, gy, gm, gA.cpu().numpy(), gH.cpu().numpy(), "cfg%d" % cfg)
+
+
+def test_rate_weight_gradients_edges():
+    g = synth.step_scale_for(220.0)
+    plan = gu.device_codec().plan(g)
+    params = synth.world().params()
+    # no coded rows: zero gradients
+    rows, tok = synth.random_rows(100, seed=5)
+    gA, gH, st = gu.dk().rate_backward(plan, gu.rows_dev(rows), gu.to_dev(tok.astype(np.int32)),
+                                       gu.to_dev(np.zeros((0, 2048), np.float32)),
+                                       gu.to_dev(np.zeros((0, 2048), np.float32)))
+    assert st == 0 and not gA.any().item() and not gH.any().item()
+    # a ragged count (one row past a multiple of 64) and a bad token id
+    rows, tok = synth.random_rows(132 + 65, seed=6)
+    rng = np.random.default_rng(6)
+    gy = rng.standard_normal((65, 2048)).astype(np.float32)
+    gm = rng.standard_normal((65, 2048)).astype(np.float32)
+    gA, gH, st = gu.dk().rate_backward(plan, gu.rows_dev(rows), gu.to_dev(tok.astype(np.int32)), gu.to_dev(gy),
+                                       gu.to_dev(gm))
+    assert st == 0
+    _check_weight_grads(params, rows, tok, gy, gm, gA.cpu().numpy(), gH.cpu().numpy(), "N65")
+    bad = tok.copy()
+    bad[4 + 64] = -3
+    _, _, st = gu.dk().rate_backward(plan, gu.rows_dev(rows), gu.to_dev(bad.astype(np.int32)), gu.to_dev(gy),
+                                     gu.to_dev(gm))
+    assert st == -1  # EINVAL

@@ -74,7 +74,7 @@ def test_fit_workspace_size_and_bounds():
     with pytest.raises(dk.DckvError):
         dk.dckv_fit_bytes(1)
     with pytest.raises(dk.DckvError):
-        dk.dckv_fit_bytes((1 << 22) + 1)
+        dk.dckv_fit_bytes((1 << 18) + 1)
     # per row: fp32 coefficients and means (16 KiB), two bf16 halves of the
     # coefficients and the gathered embeddings (12 KiB), the checked id; fixed:
     # Gram and right-hand sides (32 MiB), bf16 head (8 MiB), partial sums,
