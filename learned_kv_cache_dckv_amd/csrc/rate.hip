@@ -10,18 +10,23 @@
 //   bits = -log2(F_s(t + 1/2) - F_s(t - 1/2)),  F_s the zero-mean Laplace CDF
 // and, with beta = d bits / dt and gamma = d bits / ds,
 //   dR/dm_j = -beta_j / D
-//   dR/dy_j = beta_j / D + [j even] a (dR/dm_{j-1} + dR/dm_{j+1})  (odd rows)
+//   dR/dy_j = beta_j / D, plus a (dR/dm_{j-1} + dR/dm_{j+1}) on even rows
+//             (their reconstruction is in the odd neighbours' means)
 //   dR/da   = sum over odd j of dR/dm_j (yhat_{j-1} + yhat_{j+1})
 //   dR/db   = sum over j of gamma_j / D.
-// Dropped components: bits 0, yhat = mu, no gradient.
+// Dropped components: bits 0, yhat = mu, no gradient.  Through y = A x and
+// m = H e the weight gradients are dR/dA = sum_j dR/dy_j x_j^T and
+// dR/dH = sum_j dR/dm_j e_j^T.
 //
 // Work split: the coefficients y = A x come from the fp32-output GEMM (split
-// over k into partial sets when its tiles alone would not fill the chip); one
-// thread per component codes a chunk of rows held in registers, so the
-// neighbour terms are register reads (two halo rows before the chunk and one after it are
-// recomputed).  Per-token bits are column-block sums written as partials and
-// added in a fixed order; the per-component sums are per-chunk partials in fp64,
-// reduced by a last kernel that also sets the status.
+// over k into two partial sets when its tiles alone would not fill the chip);
+// one thread per component codes a chunk of rows held in registers, so the
+// neighbour terms are register reads (the two rows before the chunk and the
+// one after it are recomputed).  Per-token bits are column-block sums written
+// as partials and added in a fixed order; the per-component sums are fp64
+// within a chunk, stored per chunk and added in fp64 by two reduction kernels,
+// the second of which also sets the status.  The weight gradients are two
+// MFMA products over the token dimension in one launch.
 #include "dckv_internal.h"
 
 namespace dckv {
