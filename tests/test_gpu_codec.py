@@ -214,3 +214,20 @@ def test_codec_status_codes():
     bad[20] ^= 2  # N
     _, st = gu.gpu_decode(plan, bytes(bad), tok)
     assert st == dk.ECORRUPT
+
+
+def test_request_length_cap():
+    """Requests above 2^18 positions (a [T][6,144] bf16 operand past 3 GiB, where
+    32-bit operand offsets end) are refused before anything is enqueued."""
+    dk = gu.dk()
+    plan = gu.device_codec().plan(synth.step_scale_for(220.0))
+    max_bytes, ws = dk.dckv_bytes(plan, 1 << 18)
+    assert max_bytes > 0 and ws > 0
+    with pytest.raises(dk.DckvError) as e:
+        dk.dckv_bytes(plan, (1 << 18) + 1)
+    assert e.value.code == dk.EUNSUPPORTED
+    with pytest.raises(dk.DckvError):
+        dk.dckv_rate_bytes(plan, (1 << 18) + 1)
+    with pytest.raises(dk.DckvError):
+        dk.dckv_rate_backward_bytes(plan, (1 << 18) + 1)
+    assert dk.dckv_rate_bytes(plan, 1 << 18) > 0
