@@ -377,8 +377,9 @@ int dckv_rate_forward(const dckv_plan_t *plan, const uint16_t *rows, const int32
  * upstream gradients, e.g. dckv_rate_forward's, plus a distortion term's.
  * The products run on the bf16 MFMA with fp32 accumulation; the gradients
  * enter as two bf16 halves (16 mantissa bits), rows and embeddings are exact.
- * Caller-owned device memory throughout (rows 16-byte, the rest 4-byte
- * aligned, workspace 256-byte aligned and at least dckv_rate_backward_bytes,
+ * Caller-owned device memory throughout (rows, grad_y and grad_mean 16-byte,
+ * the outputs 4-byte aligned, workspace 256-byte aligned and at least
+ * dckv_rate_backward_bytes,
  * about 32 KiB per coded row); a token id outside [0, vocab) sets *status to
  * DCKV_EINVAL.  T <= 2^18. */
 int dckv_rate_backward_bytes(const dckv_plan_t *plan, int64_t T, uint64_t *workspace_bytes);

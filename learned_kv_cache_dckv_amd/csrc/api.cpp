@@ -371,8 +371,8 @@ extern "C" int dckv_rate_backward(const dckv_plan_t *plan, const uint16_t *rows,
   if (N > 0) {
     if (!rows || !aligned(rows, 16) || !token_ids || !aligned(token_ids, 4))
       return set_error(DCKV_EINVAL, "rate backward: rows must be 16-byte aligned, token_ids 4-byte aligned");
-    if (!grad_y || !grad_mean || !aligned(grad_y, 4) || !aligned(grad_mean, 4))
-      return set_error(DCKV_EINVAL, "rate backward: null or misaligned grad_y / grad_mean");
+    if (!grad_y || !grad_mean || !aligned(grad_y, 16) || !aligned(grad_mean, 16))
+      return set_error(DCKV_EINVAL, "rate backward: grad_y / grad_mean must be 16-byte aligned");
   }
   if (!grad_analysis || !grad_mean_head || !aligned(grad_analysis, 4) || !aligned(grad_mean_head, 4))
     return set_error(DCKV_EINVAL, "rate backward: null or misaligned grad_analysis / grad_mean_head");

@@ -33,48 +33,70 @@ __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint
 
 __global__ void k_fit_clear_status(int32_t *status) { *status = 0; }
 
+// The transposes below move 64 x 64 tiles through LDS with 8- or 16-byte
+// accesses: 16 threads cover one 64-element row, 16 rows per pass.
+
 // Et[e][j] = E[tok_j][e] for j < n, 0 for n <= j < n_pad (bf16, transposed);
 // an id outside [0, vocab) sets EINVAL and reads as 0; tokc receives the
 // checked ids (row indices of the later gather GEMM)
-__global__ void k_fit_gather_t(const uint16_t *E, const int32_t *tok, int64_t n, int64_t n_pad, int vocab,
-                               uint16_t *Et, int32_t *tokc, int32_t *status) {
-  __shared__ uint16_t t[64][65];
-  const int j0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 256 threads: 4 rows at a time
-  for (int r = ty; r < 64; r += 4) {
-    const int64_t j = j0 + r;
-    uint16_t v = 0;
+__global__ __launch_bounds__(256) void k_fit_gather_t(const uint16_t *E, const int32_t *tok, int64_t n,
+                                                      int64_t n_pad, int vocab, uint16_t *Et, int32_t *tokc,
+                                                      int32_t *status) {
+  __shared__ uint16_t t[64][72];
+  const int64_t j0 = (int64_t)blockIdx.x * 64;
+  const int e0 = blockIdx.y * 64;
+  const int q = threadIdx.x & 15, r = threadIdx.x >> 4;
+  for (int p = 0; p < 4; ++p) {
+    const int jr = r + 16 * p;
+    const int64_t j = j0 + jr;
+    uint2 v = make_uint2(0u, 0u);
     if (j < n) {
       int id = tok[j];
       if (id < 0 || id >= vocab) {
         atomicCAS(status, 0, DCKV_EINVAL);
         id = 0;
       }
-      v = E[(size_t)id * kEmb + e0 + tx];
-      if (blockIdx.y == 0 && tx == 0) tokc[j] = id;
+      v = *reinterpret_cast<const uint2 *>(E + (size_t)id * kEmb + e0 + 4 * q);
+      if (blockIdx.y == 0 && q == 0) tokc[j] = id;
     }
-    t[r][tx] = v;
+    *reinterpret_cast<uint2 *>(&t[jr][4 * q]) = v;
   }
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) Et[(size_t)(e0 + r) * n_pad + j0 + tx] = t[tx][r];
+  for (int p = 0; p < 4; ++p) {
+    const int er = r + 16 * p;
+    const uint32_t a = (uint32_t)t[4 * q][er] | ((uint32_t)t[4 * q + 1][er] << 16);
+    const uint32_t b = (uint32_t)t[4 * q + 2][er] | ((uint32_t)t[4 * q + 3][er] << 16);
+    *reinterpret_cast<uint2 *>(Et + (size_t)(e0 + er) * n_pad + j0 + 4 * q) = make_uint2(a, b);
+  }
 }
 
 // Yt_hi[c][j] = bf16(Y[j][c]), Yt_lo[c][j] = bf16(Y[j][c] - Yt_hi), zero for j >= n
-__global__ void k_fit_split_t(const float *Y, int64_t n, int64_t n_pad, uint16_t *hi, uint16_t *lo) {
-  __shared__ float t[64][65];
-  const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
-    const int64_t j = j0 + r;
-    t[r][tx] = j < n ? Y[(size_t)j * kC + c0 + tx] : 0.f;
+__global__ __launch_bounds__(256) void k_fit_split_t(const float *Y, int64_t n, int64_t n_pad, uint16_t *hi,
+                                                     uint16_t *lo) {
+  __shared__ float t[64][68];
+  const int64_t j0 = (int64_t)blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  const int q = threadIdx.x & 15, r = threadIdx.x >> 4;
+  for (int p = 0; p < 4; ++p) {
+    const int jr = r + 16 * p;
+    const int64_t j = j0 + jr;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (j < n) v = *reinterpret_cast<const float4 *>(Y + (size_t)j * kC + c0 + 4 * q);
+    *reinterpret_cast<float4 *>(&t[jr][4 * q]) = v;
   }
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) {
-    const float y = t[tx][r];
-    const uint16_t h = f2bf(y);
-    const size_t o = (size_t)(c0 + r) * n_pad + j0 + tx;
-    hi[o] = h;
-    lo[o] = f2bf(y - bf2f(h));
+  for (int p = 0; p < 4; ++p) {
+    const int cr = r + 16 * p;
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float y = t[4 * q + i][cr];
+      h[i] = f2bf(y);
+      l[i] = f2bf(y - bf2f((uint16_t)h[i]));
+    }
+    const size_t o = (size_t)(c0 + cr) * n_pad + j0 + 4 * q;
+    *reinterpret_cast<uint2 *>(hi + o) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    *reinterpret_cast<uint2 *>(lo + o) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
   }
 }
 

@@ -336,18 +336,27 @@ int rate_ksplit(int64_t N) {
 }
 
 // Xt[d][j] = rows[keep_head + j][d] for j < N, 0 for N <= j < n_pad (bf16,
-// transposed through a 64 x 64 LDS tile)
+// transposed through a 64 x 64 LDS tile with 8-byte accesses: 16 threads per
+// 64-element row, 16 rows per pass)
 __global__ __launch_bounds__(256) void k_rate_rows_t(const uint16_t *X, int64_t N, int64_t n_pad, uint16_t *Xt) {
-  __shared__ uint16_t t[64][65];
+  __shared__ uint16_t t[64][72];
   const int64_t j0 = (int64_t)blockIdx.x * 64;
   const int d0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
-    const int64_t j = j0 + r;
-    t[r][tx] = j < N ? X[j * kD + d0 + tx] : (uint16_t)0;
+  const int q = threadIdx.x & 15, r = threadIdx.x >> 4;
+  for (int p = 0; p < 4; ++p) {
+    const int jr = r + 16 * p;
+    const int64_t j = j0 + jr;
+    uint2 v = make_uint2(0u, 0u);
+    if (j < N) v = *reinterpret_cast<const uint2 *>(X + j * kD + d0 + 4 * q);
+    *reinterpret_cast<uint2 *>(&t[jr][4 * q]) = v;
   }
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) Xt[(int64_t)(d0 + r) * n_pad + j0 + tx] = t[tx][r];
+  for (int p = 0; p < 4; ++p) {
+    const int dr = r + 16 * p;
+    const uint32_t a = (uint32_t)t[4 * q][dr] | ((uint32_t)t[4 * q + 1][dr] << 16);
+    const uint32_t b = (uint32_t)t[4 * q + 2][dr] | ((uint32_t)t[4 * q + 3][dr] << 16);
+    *reinterpret_cast<uint2 *>(Xt + (int64_t)(d0 + dr) * n_pad + j0 + 4 * q) = make_uint2(a, b);
+  }
 }
 
 __global__ __launch_bounds__(256) void k_rate_zero(float *p, int64_t n) {
