@@ -247,20 +247,26 @@ __global__ __launch_bounds__(1024) void k_scan_header(ScanP P) {
   const int64_t lo = min<int64_t>(ng, t * per), hi = min<int64_t>(ng, lo + per);
   uint64_t s = 0;
   for (int64_t i = lo; i < hi; ++i) s += P.gwords[i];
-  part[t] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
-    uint64_t v = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
+  // inclusive scan: within each wave by shuffles, then the 16 wave totals
+  const int lane = t & 63, wv = t >> 6;
+  uint64_t incl = s;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
   }
-  uint64_t run = part[t] - s;
+  if (lane == 63) part[wv] = incl;
+  __syncthreads();
+  uint64_t before = 0;
+  for (int w = 0; w < wv; ++w) before += part[w];
+  uint64_t all = 0;
+  for (int w = 0; w < 16; ++w) all += part[w];
+  uint64_t run = before + incl - s;
   for (int64_t i = lo; i < hi; ++i) {
     P.goffs[i] = run;
     run += P.gwords[i];
   }
-  const uint64_t total_words = part[1023];
+  const uint64_t total_words = all;
   if (t == 0) P.goffs[ng] = total_words;
   Ctrl *ct = ctrl_of(P.ws);
   const uint32_t n_esc = ct->n_esc;
