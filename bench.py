@@ -371,6 +371,11 @@ def training_rate_bench(cfg: int, steps: int, cpu: bool) -> int:
            "kernels": {"rate": {"avg_ms": kern["rate"], "GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS,
                                 "algorithmic_bytes": rate_bytes},
                        "transform_gemm": {"avg_ms": kern["fit_gemm"], "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}},
+           "roofline": ({"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / PEAK_BF16_TFLOPS, "kernel": "transform_gemm", "traffic": None}
+                        if kern["fit_gemm"] >= kern["rate"] else
+                        {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": gbps / PEAK_HBM_GBPS, "kernel": "rate", "traffic": None}),
            "weight_gradients": {"ms": bwd_ms, "tflops": bwd_flop / (bwd_ms * 1e-3) / 1e12,
                                 "note": "dR/dA and dR/dH; the gradients enter as two bf16 halves, so the "
                                         "MFMA work is twice these flops"},
