@@ -373,7 +373,8 @@ void fit_sequence(const FitArgs &a) {
   g.ldc = kC;
   launch_gemm_f32(g, s);
   hipLaunchKernelGGL(k_fit_split_t, dim3((unsigned)(np / 64), kC / 64), dim3(256), 0, s, Y, n, np, Yhi, Ylo);
-  // G = Et Et^T
+  // G = Et Et^T and R = Et [Yhi | Ylo]^T (= E^T Y with 16 mantissa bits of Y):
+  // independent, 64 tiles each, so one launch
   g.a0 = g.a1 = Et;
   g.lda0 = g.lda1 = (uint32_t)(np * 2);
   g.b0 = g.b1 = Et;
@@ -383,16 +384,16 @@ void fit_sequence(const FitArgs &a) {
   g.N = kEmb;
   g.c = G;
   g.ldc = kEmb;
-  launch_gemm_f32(g, s);
-  // R = Et [Yhi | Ylo]^T (= E^T Y with 16 mantissa bits of Y)
-  g.b0 = Yhi;
-  g.b1 = Ylo;
-  g.KT = (int)(2 * np / kBK);
-  g.split = (int)(np / kBK);
-  g.N = kC;
-  g.c = R;
-  g.ldc = kC;
-  launch_gemm_f32(g, s);
+  GemmF32Args gr = g;
+  gr.b0 = Yhi;
+  gr.b1 = Ylo;
+  gr.KT = (int)(2 * np / kBK);
+  gr.split = (int)(np / kBK);
+  gr.N = kC;
+  gr.c = R;
+  gr.ldc = kC;
+  launch_gemm_f32_pair(g, gr, s);
+  g = gr;
   float *dg = reinterpret_cast<float *>(ws + l.dg);
   float *linv = reinterpret_cast<float *>(ws + l.linv);
   hipLaunchKernelGGL(k_fit_add_diag, dim3(kEmb / 256), dim3(256), 0, s, G, a.ridge * (float)n, dg);
