@@ -35,7 +35,15 @@
  *   - Only the shapes of the paper's codec are supported by the GPU kernels:
  *     n_layers = 6, n_kv_heads = 2, head_dim = 256 (D = 6144), n_coef = 2048,
  *     n_hidden = 256, emb_dim = 2048.  vocab, keep_head, keep_tail and
- *     rope_theta are free.
+ *     rope_theta are free.  A request holds at most 2^18 positions.
+ *   - The encode and decode calls issue no memset and no host
+ *     synchronisation, so they can be captured in a HIP graph.
+ *
+ * Entry points, in the order below: plan (tables, creation, inspection,
+ * mean table); sizing; encode; decode (rows, or the per-layer head
+ * matrices); inverse RoPE of a post-RoPE cache; batches; the lossless stage
+ * alone; workspace views and kernel timing; the closed-form fit of the
+ * conditional models; the training rate and its gradients.
  */
 #ifndef DCKV_H
 #define DCKV_H
