@@ -304,6 +304,17 @@ def make_request(cfg: int, index: int = 0, T: int | None = None, n_rows: int | N
                    note=note)
 
 
+RATE_CALIB_ROWS = 4096
+
+
+def calibration_sample(n_rows: int = RATE_CALIB_ROWS):
+    """Rows and token ids of the held-out sample the rate ladder is calibrated
+    on: the row model with a seed of its own (neither a workload nor the batch
+    the basis and scales were fitted on)."""
+    w = world()
+    return _draw_rows(w, n_rows, np.random.SeedSequence([CODEC_SEED, 1]))
+
+
 def random_rows(T: int, seed: int, gain: float = 1.0):
     """Rows and token ids from the row model with an arbitrary seed (edge-case tests)."""
     w = world()
