@@ -13,8 +13,9 @@
  *     synthesis side adds one hidden layer of 256 GELU units (Transform);
  *   - per-component quantisation steps; components whose Laplace scale is
  *     below 0.05 steps are dropped (Transform);
- *   - codes are rANS-coded under Laplace distributions; codes beyond +-127
- *     are escaped at 64 bits each (Coding);
+ *   - the codes go through a rANS coder with discretised-Laplace symbol
+ *     models; a code outside [-127, 127] is stored as a 64-bit record
+ *     instead (Coding);
  *   - even positions take their code means from the token's input embedding,
  *     odd positions also from both decoded neighbours, so decoding takes two
  *     parallel passes at any length; token ids are side information, not
@@ -34,8 +35,8 @@
  *     the caller passes a workspace of the size dckv_bytes() reports.
  *   - Only the shapes of the paper's codec are supported by the GPU kernels:
  *     n_layers = 6, n_kv_heads = 2, head_dim = 256 (D = 6144), n_coef = 2048,
- *     n_hidden = 256, emb_dim = 2048.  vocab, keep_head, keep_tail and
- *     rope_theta are free.  A request holds at most 2^18 positions.
+ *     n_hidden = 256, emb_dim = 2048.  keep_head, keep_tail and rope_theta
+ *     are free, vocab is below 2^19.  A request holds at most 2^18 positions.
  *   - The encode and decode calls issue no memset and no host
  *     synchronisation, so they can be captured in a HIP graph.
  *
@@ -73,7 +74,7 @@ typedef enum {
  * vectors are read on the host during dckv_plan(). */
 typedef struct {
   int32_t n_layers, n_kv_heads, head_dim;   /* 6, 2, 256 -> D = 6144 */
-  int32_t n_coef, n_hidden, emb_dim, vocab; /* 2048, 256, 2048, any >= 1 */
+  int32_t n_coef, n_hidden, emb_dim, vocab; /* 2048, 256, 2048, 1 .. 2^19 - 1 */
   int32_t keep_head, keep_tail;             /* positions kept in bf16: 4, 128 */
   float rope_theta;                         /* RoPE base, e.g. 1e7 */
   const uint16_t *analysis;   /* A  [n_coef][D]          y = A x          */
@@ -117,7 +118,8 @@ int dckv_plan_tables(const float *base_step, const float *laplace_scale, int32_t
  * allocates (vocab * n_coef * 4 bytes: 256 MiB for a 32,768-token vocabulary)
  * and computes with one GEMM on the null stream.  *out receives the handle;
  * free with dckv_plan_free.  Returns DCKV_EUNSUPPORTED for shapes the kernels
- * do not support, DCKV_ENOMEM when an allocation fails. */
+ * do not support (vocab above 2^19 - 1 among them: the encoder addresses the
+ * mean table with 32-bit byte offsets), DCKV_ENOMEM when an allocation fails. */
 int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **out);
 int dckv_plan_free(dckv_plan_t *plan);
 
@@ -138,11 +140,15 @@ int dckv_plan_mean_table(const dckv_plan_t *plan, const float **table, int64_t *
                          int32_t *col_component);
 
 /* Pure host.  For a request of T tokens: the largest stream an encode can
- * produce (every code escaped or 16 bits) and the workspace bytes that
+ * produce and the workspace bytes that
  * dckv_encode / dckv_decode / the entropy stages need.  T <= 2^18 positions:
  * the kernels address each [T][D] operand through 32-bit byte offsets, so
  * longer requests return DCKV_EUNSUPPORTED (here and in every call that
- * takes T). */
+ * takes T).  The workspace holds max(4096, N * C_a / 16) escape records
+ * (6.25 % of the coded positions); an encode that finds more sets
+ * DCKV_ECAPACITY.  So the largest stream is the fixed part plus, per coded
+ * position, one 16-bit word or (for at most that many) one 8-byte record,
+ * plus a 32-bit flush per substream. */
 int dckv_bytes(const dckv_plan_t *plan, int64_t T, uint64_t *max_stream_bytes,
                uint64_t *workspace_bytes);
 

@@ -37,6 +37,10 @@ constexpr int kD = 6144;
 // [rows][6,144] bf16 operand must stay below 4 GiB; 2^18 rows is 3 GiB.
 constexpr int64_t kMaxRows = (int64_t)1 << 18;
 constexpr int kC = 2048;
+// The encoder reads a token's row of the embedding-mean table (n_coef fp32 =
+// 8 KiB) through a buffer resource with 32-bit byte offsets, so the table's
+// vocab * 8 KiB must stay below 4 GiB.
+constexpr int kMaxVocab = (1 << 19) - 1;
 constexpr int kHid = 256;
 constexpr int kEmb = 2048;
 constexpr int kHeadDim = 256;

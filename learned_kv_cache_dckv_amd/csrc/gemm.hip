@@ -9,8 +9,8 @@
 //   - Conditional entropy models: even positions take their code means from
 //     the prompt token's input embedding, odd positions also from the decoded
 //     coefficients of both neighbours (a 1-D checkerboard, two passes);
-//   - first paragraph: keys are taken before RoPE, which is reapplied after
-//     decoding.
+//   - first paragraph: the codec sees the keys without their rotary position
+//     embedding, and the decoder rotates them again at the end.
 //
 // Every GEMM here is C[m][n] = sum_k A[m][k] * B[n][k] with both operands
 // k-contiguous (token rows times weight rows).  One workgroup of four wave64s

@@ -158,6 +158,8 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
     return set_error(DCKV_EUNSUPPORTED,
                      "plan: the kernels support n_layers=6, n_kv_heads=2, head_dim=256, n_coef=2048, "
                      "n_hidden=256, emb_dim=2048");
+  if (p->vocab > kMaxVocab)
+    return set_error(DCKV_EUNSUPPORTED, "plan: vocab above 2^19 - 1 (the mean table is addressed with 32-bit offsets)");
   if (p->vocab < 1 || p->keep_head < 0 || p->keep_tail < 0 || !(p->rope_theta > 0.0f) ||
       !std::isfinite(p->rope_theta))
     return set_error(DCKV_EINVAL, "plan: bad vocab, keep sizes or rope_theta");
@@ -424,12 +426,14 @@ extern "C" int dckv_bytes(const dckv_plan_t *plan, int64_t T, uint64_t *max_stre
   if (T > kMaxRows) return set_error(DCKV_EUNSUPPORTED, "bytes: T above 2^18 positions (32-bit operand offsets)");
   Geometry g = geometry(plan, T);
   // a coded position costs at most one 16-bit word or one 8-byte escape record;
-  // each substream adds a two-word flush
+  // each substream adds a two-word flush.  An encode refuses more escapes than
+  // the workspace holds (esc_cap, DCKV_ECAPACITY), so at most esc_cap records.
   const uint64_t symbols = (uint64_t)g.N * plan->C_a;
   const uint64_t rans_max = 2ull * symbols + 4ull * (uint64_t)g.n_blk * plan->C_a;
   if (rans_max >= 0xFFFFFFFFull || symbols >= 0xFFFFFFFFull)
     return set_error(DCKV_EUNSUPPORTED, "bytes: request too long for 32-bit stream offsets");
-  if (max_stream_bytes) *max_stream_bytes = g.fixed_bytes + 8ull * symbols + 4ull * g.n_blk * plan->C_a;
+  const uint64_t esc_max = std::min<uint64_t>((uint64_t)g.esc_cap, symbols);
+  if (max_stream_bytes) *max_stream_bytes = g.fixed_bytes + rans_max + 6ull * esc_max;
   if (workspace_bytes) *workspace_bytes = layout(plan, g).total;
   return DCKV_OK;
 }

@@ -3,9 +3,10 @@
 // stream parser.
 //
 // Source: DCKV digest page ("DCKV: Learned Transform Coding of the Prompt KV
-// Cache in Hybrid Language Models"), "How it works", Coding bullet: codes are
-// rANS-coded on the GPU under Laplace distributions and codes beyond +-127
-// are escaped at 64 bits each.  Coder parameters and layout are this
+// Cache in Hybrid Language Models"), "How it works", Coding bullet: the
+// integer codes go through an asymmetric-numeral-system coder whose symbol
+// model is a discretised Laplace, and a code outside [-127, 127] leaves that
+// coder and travels as a 64-bit record.  Coder parameters and layout are this
 // library's own (stream version 1): 32-bit state, L = 2^16, 16-bit words,
 // 15-bit tables, one group = one wave64 whose lanes are the group's
 // components.

@@ -1,6 +1,7 @@
 // The rate term of codec training and its gradients (DCKV digest page, "How
-// it works", Training bullet: code length computed with additive noise,
-// reconstruction from rounded values with a straight-through gradient).
+// it works", Training bullet: the rate is the code length of coefficients
+// perturbed by uniform noise; the reconstruction uses the quantised values,
+// and its gradient bypasses the rounding).
 //
 // For coded row j and active component c, with step D, Laplace scale b,
 // s = b / D, neighbour weight a and embedding mean m:

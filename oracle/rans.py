@@ -1,7 +1,8 @@
 """Interleaved 32-bit rANS over (component, 256-token block) substreams.
 
-Source: DCKV digest page, "How it works", Coding bullet (codes are rANS-coded
-under Laplace distributions; codes beyond +-127 are escaped at 64 bits each).
+Source: DCKV digest page, "How it works", Coding bullet (an asymmetric-numeral
+coder over discretised-Laplace symbol models; a code outside [-127, 127] is
+stored as a 64-bit record instead).
 The pages fix neither the coder's parameters nor a byte format; the readings
 taken here are:
   * state x is 32 bits, renormalisation moves 16-bit words, L = 2^16, table

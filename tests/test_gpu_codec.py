@@ -216,6 +216,27 @@ def test_codec_status_codes():
     assert st == dk.ECORRUPT
 
 
+def test_codec_escape_overflow_is_ecapacity():
+    """More escapes than the workspace holds (max(4096, N C_a / 16) records)
+    set ECAPACITY and a zero stream size; the stream bound dckv_bytes reports
+    is consistent with that cap."""
+    import torch
+    dk = gu.dk()
+    plan = gu.device_codec().plan(synth.step_scale_for(220.0))
+    T = 132 + 600
+    rows, tok = synth.random_rows(T, seed=81, gain=2000.0)
+    max_bytes, _ = dk.dckv_bytes(plan, T)
+    N, Ca = T - 132, plan.c_active
+    n_blk = (N + 255) // 256
+    fixed = 64 + 132 * 12288 + 4 * (n_blk * ((Ca + 63) // 64) + 1)
+    cap = max(4096, N * Ca // 16)
+    assert max_bytes == fixed + 2 * N * Ca + 4 * n_blk * Ca + 6 * cap
+    gu.say("encode with about 3/4 of the codes escaped")
+    s, st = dk.encode(plan, gu.rows_dev(rows), gu.to_dev(tok.astype(np.int32)))
+    torch.cuda.synchronize()
+    assert st == dk.ECAPACITY and s.numel() == 0
+
+
 def test_request_length_cap():
     """Requests above 2^18 positions (a [T][6,144] bf16 operand past 3 GiB, where
     32-bit operand offsets end) are refused before anything is enqueued."""

@@ -3,7 +3,8 @@ head matrices, and the inverse RoPE that takes a post-RoPE cache back to the
 pre-RoPE rows the codec codes (DCKV digest, "How it works", first paragraph).
 
 Bars: dckv_decode_heads gives exactly the values of dckv_decode (bit for bit,
-kept rows included, rows past N untouched in neither layout); dckv_unrope
+kept rows included, rows past N untouched in neither layout) and is within the
+rows' bar of the oracle's decode of the same stream; dckv_unrope
 equals the oracle's float64 inverse rotation rounded once to bf16 on every
 value, in place or not, and takes a decode's post-RoPE output back to the
 oracle's pre-RoPE reconstruction within the rows' bar plus one bf16 rounding.
@@ -48,6 +49,14 @@ def test_decode_heads_equals_decode(case):
     got = _heads_to_rows(kv, len(tok))
     gu.say("%s: T=%d heads layout equal %s" % (case, len(tok), np.array_equal(got, want)))
     assert np.array_equal(got, want)
+    # and against the oracle's decode of the same stream, kept rows included
+    params = synth.world().params()
+    p = gu.oracle_plan(params, g)
+    dec = ocodec.decode(data, tok, params, p)
+    e = gu.rel_l2(bf16.to_f64(got), bf16.to_f64(dec.rows))
+    gu.say("  heads layout vs oracle decode: rel %.3g" % e)
+    assert e <= gu.REL_L2_TOL
+    gu.check_kept_rows(rows, len(tok), params, got)
 
 
 def test_unrope_matches_oracle_and_inverts_decode_rope():

@@ -80,6 +80,18 @@ def _check(params, p, rows, tok, u, got, label):
     gu.say("  %s: N=%d codes agree %.7f" % (label, N, agree))
     assert agree >= gu.SYMBOL_AGREEMENT
     r = orate.rate_forward(y, m, p, a, b, u, q=qg)
+    # odd rows: the oracle's float32 decision around the means the GPU's even
+    # codes give (as the decoder would have them); every disagreement is a
+    # certified tie
+    mu_o = r.mu[1::2][:, act]
+    qo_o = ocodec._decide(y[1::2][:, act] - mu_o, p.step[act])
+    qg_o = qg[1::2][:, act]
+    res_o = (y[1::2][:, act] - mu_o) / step[act][None, :]
+    yy_o = np.abs(y[1::2][:, act]) + np.abs(mu_o)
+    for n, k in np.argwhere(qo_o != qg_o):
+        tie = 0.5 * (qo_o[n, k] + qg_o[n, k])
+        tol = 2.0 ** -17 * yy_o[n, k] / step[act][k] + 1e-4
+        assert abs(qo_o[n, k] - qg_o[n, k]) == 1 and abs(res_o[n, k] - tie) <= tol, (label, 2 * n + 1, k)
     if N:
         eb = np.max(np.abs(got["bits"] - r.bits_tok) / np.maximum(r.bits_tok, 1.0))
         gu.say("  %s: bits/token %.1f, worst rel %.3g" % (label, float(np.mean(r.bits_tok)), eb))

@@ -84,3 +84,19 @@ def test_fit_workspace_size_and_bounds():
     per_row = 2048 * 4 * 2 + 2048 * 2 * 3 + 4
     fixed = 2048 * 2048 * 4 * 2 + 2048 * 2048 * 2 + 64 * 2 * 2048 * 8 + 2048 * 4 + 32 * 64 * 64 * 4
     assert fixed + per_row * n <= got <= fixed + per_row * n + 12 * 256
+
+
+def test_plan_rejects_vocab_beyond_32bit_mean_table_offsets():
+    """A vocabulary of 2^19 rows would make the mean table 4 GiB, past the
+    encoder's 32-bit offsets: the plan refuses it before touching a device."""
+    import ctypes
+    dk = _lib()
+    n = 2048
+    vec = np.ones(n, np.float32)
+    for vocab, want in ((1 << 19, dk.EUNSUPPORTED), ((1 << 19) + 7, dk.EUNSUPPORTED)):
+        prm = dk._Params(6, 2, 256, n, 256, 2048, vocab, 4, 128, 1e7,
+                         8, 8, 8, 8, 8, 8, vec.ctypes.data, vec.ctypes.data, vec.ctypes.data)
+        h = ctypes.c_void_p()
+        rc = dk.lib().dckv_plan(ctypes.byref(prm), 0.1, ctypes.byref(h))
+        assert rc == want and not h.value
+        assert "vocab" in dk.dckv_last_error()
