@@ -178,6 +178,23 @@ int dckv_encode(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *to
                 int32_t *status, void *workspace, uint64_t workspace_bytes, void *hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * dckv_encode_noalloc: dckv_encode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and errors as dckv_encode, minus
+ * the workspace: the library keeps a 72 MiB static device array per GPU it
+ * runs on (held until the process ends), which covers a request of up to
+ * 8,192 positions under any plan; a longer request returns DCKV_ECAPACITY
+ * and enqueues nothing.  The call allocates nothing and issues no memset (the
+ * kernels initialise what they read).  Every call on one GPU shares that
+ * GPU's array and it keeps the last call's contents: calls that overlap on
+ * one GPU (other streams, other threads) race and must be serialised by the
+ * caller.  The first call on a device looks up the array's address there.
+ * --------------------------------------------------------------------------*/
+int dckv_encode_noalloc(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *token_ids,
+                        int64_t T, uint8_t *stream, uint64_t capacity, uint64_t *stream_bytes,
+                        int32_t *status, void *hip_stream);
+
+/* ---------------------------------------------------------------------------
  * Decode: two checkerboard passes, synthesis with the GELU correction, RoPE.
  * (DCKV digest, "How it works": Transform, Conditional entropy models, first
  * paragraph for RoPE.)

@@ -25,7 +25,7 @@ VIEW_SYMBOLS, VIEW_YHAT_B, VIEW_H_B = 0, 1, 2
 
 # every symbol include/dckv.h declares
 EXPORTS = ("dckv_plan_tables", "dckv_plan", "dckv_plan_free", "dckv_plan_info", "dckv_plan_mean_table",
-           "dckv_bytes", "dckv_encode",
+           "dckv_bytes", "dckv_encode", "dckv_encode_noalloc",
            "dckv_decode", "dckv_decode_heads", "dckv_unrope", "dckv_bytes_batch", "dckv_encode_batch", "dckv_decode_batch", "dckv_entropy_encode",
            "dckv_entropy_decode", "dckv_workspace_view", "dckv_profile_enable", "dckv_profile_only", "dckv_profile_reset",
            "dckv_profile_read", "dckv_fit_bytes", "dckv_fit", "dckv_rate_bytes", "dckv_rate_forward",
@@ -71,6 +71,7 @@ def _load():
         "dckv_plan_mean_table": [P, P, P, P],
         "dckv_bytes": [P, I64, P, P],
         "dckv_encode": [P, P, P, I64, P, U64, P, P, P, U64, P],
+        "dckv_encode_noalloc": [P, P, P, I64, P, U64, P, P, P],
         "dckv_decode": [P, P, U64, P, I64, P, P, P, U64, P],
         "dckv_decode_heads": [P, P, U64, P, I64, P, P, P, U64, P],
         "dckv_unrope": [P, P, I64, P, P],
@@ -300,6 +301,15 @@ def dckv_encode(plan: Plan, rows, token_ids, stream_buf, stream_bytes, status, w
     rows = _as_bits(rows)
     _check(_lib.dckv_encode(plan.handle, _ptr(rows), _ptr(token_ids), T, _ptr(stream_buf), stream_buf.numel(),
                             _ptr(stream_bytes), _ptr(status), _ptr(ws), ws.numel(), _stream_handle(stream)))
+
+
+def dckv_encode_noalloc(plan: Plan, rows, token_ids, stream_buf, stream_bytes, status, stream=None):
+    """Enqueue an encode that uses the library's own static scratch instead of a
+    workspace (requests up to 8,192 positions)."""
+    T = int(rows.shape[0])
+    rows = _as_bits(rows)
+    _check(_lib.dckv_encode_noalloc(plan.handle, _ptr(rows), _ptr(token_ids), T, _ptr(stream_buf),
+                                    stream_buf.numel(), _ptr(stream_bytes), _ptr(status), _stream_handle(stream)))
 
 
 def dckv_decode(plan: Plan, stream_buf, n_bytes: int, token_ids, rows_out, status, ws, stream=None):

@@ -16,6 +16,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "dckv_internal.h"
 
@@ -32,8 +33,9 @@ int check_device(const dckv_plan_t *p) {
   return DCKV_OK;
 }
 
+// encode_only: the workspace need only hold what the encode kernels touch
 int common_checks(const dckv_plan_t *p, int64_t T, void *ws, uint64_t ws_bytes, int32_t *status, Geometry &g,
-                  Layout &l) {
+                  Layout &l, bool encode_only = false) {
   if (!p) return set_error(DCKV_EINVAL, "null plan");
   if (T < 0 || T > 0x7FFFFFFF) return set_error(DCKV_EINVAL, "T out of range");
   if (T > kMaxRows) return set_error(DCKV_EUNSUPPORTED, "T above 2^18 positions (32-bit operand offsets)");
@@ -43,7 +45,8 @@ int common_checks(const dckv_plan_t *p, int64_t T, void *ws, uint64_t ws_bytes, 
   l = layout(p, g);
   if ((uint64_t)g.N * (uint64_t)std::max(p->C_a, 1) >= 0xFFFFFFFFull)
     return set_error(DCKV_EUNSUPPORTED, "request too long for 32-bit escape indices");
-  if (ws_bytes < l.total) return set_error(DCKV_ECAPACITY, "workspace smaller than dckv_bytes() reports");
+  if (ws_bytes < (encode_only ? l.enc_total : l.total))
+    return set_error(DCKV_ECAPACITY, "workspace smaller than dckv_bytes() reports");
   return check_device(p);
 }
 
@@ -52,8 +55,8 @@ int after_launch(const char *what) { return check_hip(hipGetLastError(), what); 
 
 int encode_checks(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *token_ids, int64_t T,
                   uint8_t *stream, uint64_t capacity, uint64_t *stream_bytes, int32_t *status, void *workspace,
-                  uint64_t workspace_bytes, Geometry &g, Layout &l) {
-  int rc = common_checks(plan, T, workspace, workspace_bytes, status, g, l);
+                  uint64_t workspace_bytes, Geometry &g, Layout &l, bool encode_only = false) {
+  int rc = common_checks(plan, T, workspace, workspace_bytes, status, g, l, encode_only);
   if (rc) return rc;
   if (T > 0 && (!rows || !aligned(rows, 16) || !token_ids || !aligned(token_ids, 4)))
     return set_error(DCKV_EINVAL, "rows must be 16-byte aligned, token_ids 4-byte aligned");
@@ -411,4 +414,68 @@ extern "C" int dckv_unrope(const dckv_plan_t *plan, const uint16_t *rows_in, int
   if (rc) return rc;
   launch_unrope(plan, rows_in, rows_out, T, static_cast<hipStream_t>(hip_stream));
   return after_launch("dckv_unrope");
+}
+
+// ---------------------------------------------------------------------------
+// Encode without any allocation: the workspace is a file-scope device array.
+// Every device the library runs on holds its own copy of the array until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it only names a stand-in): the device address of each device's copy
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is used.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr uint64_t kNoAllocScratchBytes = 72ull << 20;
+constexpr int kNoAllocMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kNoAllocMaxDevices] = {};
+
+// The calling thread's current device must be `dev`.
+int scratch_address(int dev, void **out) {
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return set_error(DCKV_EUNSUPPORTED, "encode_noalloc: device index too large");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return check_hip(e != hipSuccess ? e : hipErrorInvalidSymbol, "encode_noalloc: scratch address");
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return DCKV_OK;
+}
+}  // namespace
+
+extern "C" int dckv_encode_noalloc(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *token_ids, int64_t T,
+                                   uint8_t *stream, uint64_t capacity, uint64_t *stream_bytes, int32_t *status,
+                                   void *hip_stream) {
+  if (!plan) return set_error(DCKV_EINVAL, "encode_noalloc: null plan");
+  if (T < 0 || T > kMaxRows) return set_error(DCKV_EINVAL, "encode_noalloc: T out of range");
+  int rc = check_device(plan);
+  if (rc) return rc;
+  const Geometry g0 = geometry(plan, T);
+  const Layout l0 = layout(plan, g0);
+  if (l0.enc_total > kNoAllocScratchBytes) {
+    char msg[200];
+    std::snprintf(msg, sizeof msg,
+                  "encode_noalloc: a %lld-position request needs %llu bytes of scratch; the library holds %llu "
+                  "(every plan fits up to 8,192 positions); use dckv_encode with a workspace",
+                  (long long)T, (unsigned long long)l0.enc_total, (unsigned long long)kNoAllocScratchBytes);
+    return set_error(DCKV_ECAPACITY, msg);
+  }
+  void *ws = nullptr;
+  rc = scratch_address(plan->device, &ws);
+  if (rc) return rc;
+  Geometry g;
+  Layout l;
+  rc = encode_checks(plan, rows, token_ids, T, stream, capacity, stream_bytes, status, ws, kNoAllocScratchBytes, g,
+                     l, /*encode_only=*/true);
+  if (rc) return rc;
+  encode_sequence(EncodeArgs{plan, g, l, static_cast<uint8_t *>(ws), rows, token_ids, stream, capacity, stream_bytes,
+                             status, static_cast<hipStream_t>(hip_stream)});
+  return after_launch("dckv_encode_noalloc");
 }

@@ -415,6 +415,7 @@ Layout dckv::layout(const dckv_plan_t *p, const Geometry &g) {
   l.rope_lo = take(256ull * kHalf * 8);
   l.rope_hi = take((uint64_t)g.rope_hi * kHalf * 8);
   const uint64_t dec_end = off;
+  l.enc_total = enc_end;
   l.total = std::max(enc_end, dec_end);
   return l;
 }
