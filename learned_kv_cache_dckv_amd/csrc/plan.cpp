@@ -222,26 +222,42 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
     for (int k = 0; k < C; ++k) colpos[perm[k]] = k;
   }
   std::vector<uint32_t> tab((size_t)std::max(Ca, 1) * 256, 0);
-  std::vector<uint8_t> bucket((size_t)std::max(Ca, 1) * kBuckets, 0);
+  std::vector<float> rcp((size_t)std::max(Ca, 1) * 256, 0.f);
+  std::vector<uint16_t> bucket((size_t)std::max(Ca, 1) * kBuckets, 0);
   for (int r = 0; r < Ca; ++r) {
     uint32_t cum = 0;
     const uint16_t *f = &h.freq[(size_t)r * kNSym];
+    std::vector<uint32_t> cumv(kNSym + 1, 0);
     for (int s = 0; s < kNSym; ++s) {
       tab[(size_t)r * 256 + s] = (uint32_t)f[s] | (cum << 16);
+      cumv[s] = cum;
       cum += f[s];
     }
+    cumv[kNSym] = cum;
     // entry 255 (escape) codes as the identity in the encoder: f = 2^15, cum 0
     tab[(size_t)r * 256 + 255] = kM;
-    // first symbol whose slot range contains the bucket's first slot
+    // the encoder's reciprocal of f, scaled down by (1 - 2^-21) before its
+    // rounding to fp32: fp32(x) * rcp then never exceeds x / f and stays above
+    // x / f - 1 for x < 2^32, so the quotient needs one upward correction at most
+    for (int s = 0; s < 256; ++s) {
+      const uint32_t fs = tab[(size_t)r * 256 + s] & 0xFFFFu;
+      rcp[(size_t)r * 256 + s] = (float)((1.0 / (double)fs) * (1.0 - std::ldexp(1.0, -21)));
+    }
+    // decoder buckets of 2^kBucketShift slots: lo = symbol of the bucket's
+    // first slot; split = offset (in the bucket) where symbol lo + 1 starts
+    // when the bucket holds exactly two symbols, kSplitPure when it holds
+    // one, kSplitSearch when it holds three or more
     int s = 0;
-    uint32_t c0 = 0;
     for (int b = 0; b < kBuckets; ++b) {
-      const uint32_t slot = (uint32_t)b << kBucketShift;
-      while (c0 + f[s] <= slot) {
-        c0 += f[s];
-        ++s;
-      }
-      bucket[(size_t)r * kBuckets + b] = (uint8_t)s;
+      const uint32_t first = (uint32_t)b << kBucketShift, last = first + (1u << kBucketShift) - 1u;
+      while (cumv[s + 1] <= first) ++s;
+      int e = s;
+      while (cumv[e + 1] <= last) ++e;
+      uint32_t split;
+      if (e == s) split = kSplitPure;
+      else if (e == s + 1) split = cumv[s + 1] - first;
+      else split = kSplitSearch;
+      bucket[(size_t)r * kBuckets + b] = (uint16_t)(s | (split << 8));
     }
   }
   // quantiser constants of each rank: step, 1 / step (0 past C_a), neighbour weight
@@ -264,7 +280,8 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
   };
   const size_t o_step = take(C * 4), o_nbr = take(C * 4), o_rank = take(C * 4), o_act = take(Ca_pad * 4);
   const size_t o_perm = take(C * 4), o_colpos = take(C * 4), o_qcol = take(qcol.size() * 4), o_scale = take(C * 4);
-  const size_t o_tab = take(tab.size() * 4), o_bucket = take(bucket.size()), o_omega = take(kHalf * 8);
+  const size_t o_tab = take(tab.size() * 4), o_rcp = take(rcp.size() * 4), o_bucket = take(bucket.size() * 2);
+  const size_t o_omega = take(kHalf * 8);
   void *blk = nullptr;
   if (hipMalloc(&blk, off) != hipSuccess) {
     delete pl;
@@ -280,7 +297,8 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
   std::memcpy(&img[o_qcol], qcol.data(), qcol.size() * 4);
   std::memcpy(&img[o_scale], p->laplace_scale, C * 4);
   std::memcpy(&img[o_tab], tab.data(), tab.size() * 4);
-  std::memcpy(&img[o_bucket], bucket.data(), bucket.size());
+  std::memcpy(&img[o_rcp], rcp.data(), rcp.size() * 4);
+  std::memcpy(&img[o_bucket], bucket.data(), bucket.size() * 2);
   std::memcpy(&img[o_omega], omega.data(), kHalf * 8);
   if (hipMemcpy(blk, img.data(), off, hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(blk);
@@ -298,7 +316,8 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
   pl->dev.qcol = reinterpret_cast<float *>(b + o_qcol);
   pl->dev.scale = reinterpret_cast<float *>(b + o_scale);
   pl->dev.tab = reinterpret_cast<uint32_t *>(b + o_tab);
-  pl->dev.bucket = b + o_bucket;
+  pl->dev.rcp = reinterpret_cast<float *>(b + o_rcp);
+  pl->dev.bucket = reinterpret_cast<uint16_t *>(b + o_bucket);
   pl->dev.omega = reinterpret_cast<double *>(b + o_omega);
   // the embedding-mean table: H E[v] for every token id, once per plan
   void *mtab = nullptr;

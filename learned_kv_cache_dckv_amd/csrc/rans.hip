@@ -29,7 +29,6 @@ constexpr int kTabStride = 257;   // u32 per table row in LDS: spreads equal sym
 constexpr int kEncWaves = 16;     // groups (waves) per encoder workgroup, one component group
 constexpr int kDecWaves = 16;
 constexpr int kWordBuf = 1024;    // u16 words cached per decoder wave
-constexpr int kBktStride = kBuckets + 4;  // bytes per bucket row in LDS (65 dwords: rows on distinct banks)
 
 __device__ __forceinline__ void set_status(int32_t *st, int code) { atomicCAS(st, 0, code); }
 
@@ -72,6 +71,7 @@ __device__ __forceinline__ Ctrl *ctrl_of(uint8_t *ws) { return reinterpret_cast<
 
 struct EncP {
   const uint32_t *tab;     // [C_a][256]
+  const float *rcp;        // [C_a][256] scaled reciprocals of f
   const uint32_t *sym32;   // tiled symbols
   uint16_t *scratch;       // [n_groups][64 * 258]
   uint32_t *gwords;        // [n_groups]
@@ -82,9 +82,11 @@ struct EncP {
 
 __global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(EncP P) {
   __shared__ uint32_t tab[kLanes * kTabStride];
+  __shared__ uint32_t rcpt[kLanes * kTabStride];  // fp32 bits of the scaled reciprocal of each f
   const int g = blockIdx.y;
   const int n = min(kLanes, P.Ca - kLanes * g);
   stage_tab<kEncWaves * 64>(tab, P.tab, g, n);
+  stage_tab<kEncWaves * 64>(rcpt, reinterpret_cast<const uint32_t *>(P.rcp), g, n);
   __syncthreads();
   if (*P.status != 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -99,10 +101,15 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(EncP P) {
   // the state never emits and x / f * 2^15 + x % f = x.  Lanes past C_a code
   // escapes only, through lane 0's table row.
   const uint32_t *mytab = tab + (lane_ok ? lane : 0) * kTabStride;
+  const float *myrcp = reinterpret_cast<const float *>(rcpt) + (lane_ok ? lane : 0) * kTabStride;
   uint32_t x = kL;
   uint32_t cnt = 0;
-  auto enc = [&](uint32_t s) {
-    const uint32_t e = mytab[s];
+  // One coding step of symbol entry (e, rf) = (f | cum << 16, scaled 1/f).
+  // q0 = trunc(fp32(x) rf) is floor(x / f) or one less (the reciprocal is
+  // scaled down so that the fp32 roundings never push it above), so
+  // x' = q M + (x - q f) + cum = (q0 << 15) + r0 + cum, plus M - f when
+  // r0 = x - q0 f is still >= f.
+  auto enc = [&](uint32_t e, float rf) {
     const uint32_t f = e & 0xFFFFu, c = e >> 16;
     const bool emit = (x >> 17) >= f;  // x >= f 2^17 (f = 2^15 never emits)
     const uint64_t mask = __ballot(emit);
@@ -115,14 +122,10 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(EncP P) {
       x = emit ? x >> 16 : x;
       cnt += tot;
     }
-    // x / f within one from a float reciprocal (x < f 2^17), then corrected
-    const uint32_t q0 = (uint32_t)((float)x * __builtin_amdgcn_rcpf((float)f));
-    int32_t r = (int32_t)(x - __umul24(q0, f));
-    const uint32_t neg = (uint32_t)r >> 31;
-    r += neg ? (int32_t)f : 0;
-    const uint32_t big = r >= (int32_t)f;
-    r -= big ? (int32_t)f : 0;
-    x = ((q0 - neg + big) << kPrecBits) + (uint32_t)r + c;
+    const uint32_t q0 = (uint32_t)((float)x * rf);
+    const uint32_t r0 = x - __umul24(q0, f);
+    const uint32_t xn = (q0 << kPrecBits) + r0 + c;
+    x = xn + (r0 >= f ? kM - f : 0u);
   };
   // symbol words in chunks of 8 quads, last chunk first; the words of the
   // next chunk are loaded while this one is coded (every quad of the block
@@ -147,8 +150,17 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(EncP P) {
       const int qd = ch * 8 + u;
       if (qd >= nq) continue;
       const uint32_t w = wq[u] | (qd == nq - 1 ? tail : 0u);
+      // the quad's four table entries are read before its first step
+      uint32_t e[4];
+      float rf[4];
 #pragma unroll
-      for (int k = 3; k >= 0; --k) enc((w >> (8 * k)) & 0xFFu);
+      for (int k = 3; k >= 0; --k) {
+        const uint32_t s = (w >> (8 * k)) & 0xFFu;
+        e[k] = mytab[s];
+        rf[k] = myrcp[s];
+      }
+#pragma unroll
+      for (int k = 3; k >= 0; --k) enc(e[k], rf[k]);
     }
   }
   if (lane_ok) {
@@ -472,7 +484,7 @@ __global__ __launch_bounds__(256) void k_parse(ParseP P) {
 // ---------------------------------------------------------------------------
 struct DecP {
   const uint32_t *tab;
-  const uint8_t *bucket;
+  const uint16_t *bucket;
   const uint8_t *stream;
   const uint8_t *ws;
   const uint32_t *esc_rows;  // [blocks][2]: index range of each block's escape records (from the parser)
@@ -488,38 +500,52 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Lane q's copy of a per-lane 64-bit value (q wave-uniform).
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int q) {
+  return (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, q) |
+         ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), q) << 32);
+}
+
 // The symbols of one wave's rows: step i pops the symbol of row i from each
-// lane's state (bucket of the slot, then a binary search while any lane's
-// bucket holds more than one symbol), then renormalises the lanes that need
-// it with the next words of the interleaved stream, in lane order.  kPlain:
-// every lane is a coded component and the block has no escapes, so no lane
-// is ever skipped.  The word window is read modulo its size: a valid stream
-// never leaves it (it slides before it would), and a corrupt one ends with
-// ptr != W or a final state != L, which the caller reports.
+// lane's state, then renormalises the lanes that need it with the next words
+// of the interleaved stream, in lane order.  The symbol of a slot comes from
+// its bucket: lo, or lo + 1 from the bucket's split offset on; only buckets of
+// three or more symbols take a binary search over the cumulative table (rare:
+// a wave enters it only while one of its lanes sits in such a bucket).
+// kPlain: every lane is a coded component and the block has no escapes, so no
+// lane is ever skipped; otherwise lane l of row 4 q + k is skipped when bit l
+// of lane q's esc[k] is set.  The word window is read modulo its size: a
+// valid stream never leaves it (it slides before it would), and a corrupt one
+// ends with ptr != W or a final state != L, which the caller reports.
 template <bool kPlain>
 __device__ __forceinline__ void decode_rows(uint32_t &x, uint32_t &ptr, uint32_t &base, uint32_t W, int Lb, int lane,
-                                            bool lane_ok, const unsigned long long *ebits, const uint32_t *mytab,
-                                            const uint8_t *mybkt, uint16_t *wb, const uint16_t *wsrc,
-                                            uint32_t *sout) {
-  auto step = [&](int i) -> uint32_t {
+                                            bool lane_ok, bool has_esc, const uint64_t (&esc)[4],
+                                            const uint32_t *mytab, const uint16_t *mybkt, uint16_t *wb,
+                                            const uint16_t *wsrc, uint32_t *sout) {
+  // emask: the row's escaped lanes (bit l set: lane l is skipped)
+  auto step = [&](uint64_t emask) -> uint32_t {
     bool act = true;
-    if (!kPlain) {
-      act = lane_ok;
-      if (ebits) act = act && !((ebits[i] >> lane) & 1ull);
-    }
+    if (!kPlain) act = lane_ok && !((emask >> lane) & 1ull);
     const uint32_t slot = x & (kM - 1u);
     const uint32_t bi = slot >> kBucketShift;
-    uint32_t lo = mybkt[bi];
-    uint32_t hi = mybkt[bi + 1];
-    if (!kPlain) hi = act ? hi : lo;
-    while (__ballot(lo < hi)) {
-      const uint32_t mid = (lo + hi + 1) >> 1;
-      const bool up = (mytab[mid] >> 16) <= slot;
-      const bool open = lo < hi;
-      lo = open && up ? mid : lo;
-      hi = open && !up ? mid - 1 : hi;
+    const uint32_t be = mybkt[bi];
+    const uint32_t split = be >> 8;
+    uint32_t s = (be & 0xFFu) + ((slot & ((1u << kBucketShift) - 1u)) >= split ? 1u : 0u);
+    const bool srch = act && split == kSplitSearch;
+    if (__ballot(srch)) {
+      // candidates lo .. the first symbol of the next bucket
+      uint32_t lo = s, hi = s;
+      if (srch) hi = bi + 1 < (uint32_t)kBuckets ? (uint32_t)(mybkt[bi + 1] & 0xFFu) : (uint32_t)(kNSym - 1);
+      while (__ballot(lo < hi)) {
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        const bool up = (mytab[mid] >> 16) <= slot;
+        const bool open = lo < hi;
+        lo = open && up ? mid : lo;
+        hi = open && !up ? mid - 1 : hi;
+      }
+      s = lo;
     }
-    const uint32_t e = mytab[lo];
+    const uint32_t e = mytab[s];
     // f * (x >> 15) < 2^32: f <= 2^15 and x >> 15 < 2^17 (24-bit multiply)
     const uint32_t xd = __umul24(e & 0xFFFFu, x >> kPrecBits) + slot - (e >> 16);
     x = act ? xd : x;
@@ -530,7 +556,7 @@ __device__ __forceinline__ void decode_rows(uint32_t &x, uint32_t &ptr, uint32_t
       if (ptr + cnt > base + kWordBuf && base + kWordBuf < W) {  // slide the window
         base = ptr;
         wave_sync_lds();
-        for (uint32_t k = lane; k < kWordBuf && base + k < W; k += 64) wb[k] = wsrc[base + k];
+        for (uint32_t k2 = lane; k2 < kWordBuf && base + k2 < W; k2 += 64) wb[k2] = wsrc[base + k2];
         wave_sync_lds();
       }
       const uint32_t before = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -539,48 +565,53 @@ __device__ __forceinline__ void decode_rows(uint32_t &x, uint32_t &ptr, uint32_t
       x = need ? (x << 16) | wv : x;
       ptr += cnt;
     }
-    return act ? lo : (uint32_t)kEsc;
+    return act ? s : (uint32_t)kEsc;
+  };
+  // the escaped lanes of row 4 q + k (lane q's esc[k]; k is a constant at
+  // every call, so esc stays in registers)
+  auto em = [&](int q, int k) -> uint64_t {
+    return (!kPlain && has_esc) ? readlane64(esc[k], q) : 0ull;
   };
   const int nq = Lb >> 2;
 #pragma unroll 1
   for (int q = 0; q < nq; ++q) {
-    uint32_t w = step(4 * q);
-    w |= step(4 * q + 1) << 8;
-    w |= step(4 * q + 2) << 16;
-    w |= step(4 * q + 3) << 24;
+    uint32_t w = step(em(q, 0));
+    w |= step(em(q, 1)) << 8;
+    w |= step(em(q, 2)) << 16;
+    w |= step(em(q, 3)) << 24;
     if (kPlain || lane_ok) sout[(size_t)q * 64] = w;
   }
   if (Lb & 3) {  // the last, partial quad: rows past the block read as escapes
     uint32_t w = 0xFFFFFFFFu;
-#pragma unroll 1
-    for (int k = 0; k < (Lb & 3); ++k) w = (w & ~(0xFFu << (8 * k))) | (step(4 * nq + k) << (8 * k));
+    if ((Lb & 3) > 0) w = (w & ~0xFFu) | step(em(nq, 0));
+    if ((Lb & 3) > 1) w = (w & ~0xFF00u) | (step(em(nq, 1)) << 8);
+    if ((Lb & 3) > 2) w = (w & ~0xFF0000u) | (step(em(nq, 2)) << 16);
     if (kPlain || lane_ok) sout[(size_t)nq * 64] = w;
   }
 }
 
 __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
   __shared__ uint32_t tab[kLanes * kTabStride];
-  __shared__ uint8_t bkt[kLanes * kBktStride];
-  __shared__ uint16_t wbuf[kDecWaves][kWordBuf];
-  __shared__ unsigned long long ebits[kDecWaves][kBlock];
+  __shared__ uint16_t bkt[kLanes * kBuckets];
+  __shared__ __attribute__((aligned(16))) uint16_t wbuf[kDecWaves][kWordBuf];
   const int g = blockIdx.y;
   const int n = min(kLanes, P.Ca - kLanes * g);
   stage_tab<kDecWaves * 64>(tab, P.tab, g, n);
   {
-    // bucket row of lane l: first symbol of each slot bucket, then the last
-    // symbol as the upper bound of the last bucket; one 16-byte piece per
-    // thread
-    static_assert(kDecWaves * 64 * 16 == kLanes * kBuckets, "one piece per thread");
-    const int pc = threadIdx.x, l = pc >> 4;
-    if (l < n) {
-      const u32x4 v = gload(reinterpret_cast<const u32x4 *>(P.bucket + (size_t)kLanes * g * kBuckets) + pc);
-      uint32_t *d = reinterpret_cast<uint32_t *>(bkt + l * kBktStride + (pc & 15) * 16);
-      d[0] = v.x;
-      d[1] = v.y;
-      d[2] = v.z;
-      d[3] = v.w;
+    // bucket rows: 512 bytes per lane, two 16-byte pieces per thread
+    static_assert(kDecWaves * 64 * 2 * 16 == kLanes * kBuckets * 2, "two pieces per thread");
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(P.bucket + (size_t)kLanes * g * kBuckets);
+    u32x4 v[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int pc = threadIdx.x + i * kDecWaves * 64;  // row pc / 32
+      if ((pc >> 5) < n) v[i] = gload(src + pc);
     }
-    if (pc < n) bkt[pc * kBktStride + kBuckets] = (uint8_t)(kNSym - 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int pc = threadIdx.x + i * kDecWaves * 64;
+      if ((pc >> 5) < n) reinterpret_cast<u32x4 *>(bkt)[pc] = v[i];
+    }
   }
   __syncthreads();
   if (*P.status != 0) return;
@@ -603,24 +634,32 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
     if (lane == 0) set_status(P.status, DCKV_ECORRUPT);
     return;
   }
-  // escape positions of this group
-  const uint32_t *esc = reinterpret_cast<const uint32_t *>(P.stream + ct->esc_off);
+  // escape positions of this group: a bitmap of the block's 256 rows, built
+  // in the word buffer (2 KiB) and then held in registers, rows 4 l .. 4 l + 3
+  // by lane l
+  uint64_t esc[4] = {0ull, 0ull, 0ull, 0ull};
   bool has_esc = false;
   {
+    const uint32_t *erec = reinterpret_cast<const uint32_t *>(P.stream + ct->esc_off);
     // the block's records, as the parser found them (a block is 256 rows)
     const uint32_t lo = __builtin_amdgcn_readfirstlane(gload(P.esc_rows + 2 * b));
     const uint32_t lo2 = __builtin_amdgcn_readfirstlane(gload(P.esc_rows + 2 * b + 1));
     if (lo2 > lo) {
       has_esc = true;
-      for (int i = lane; i < kBlock; i += 64) ebits[wave][i] = 0ull;
+      unsigned long long *eb = reinterpret_cast<unsigned long long *>(wb);
+      static_assert(kWordBuf * 2 >= kBlock * 8, "the bitmap fits in the word buffer");
+      for (int i = lane; i < kBlock; i += 64) eb[i] = 0ull;
       wave_sync_lds();
       for (uint32_t e = lo + lane; e < lo2; e += 64) {
-        const uint64_t f = esc[2 * e];
+        const uint64_t f = erec[2 * e];
         const uint64_t jj = f / (uint64_t)P.Ca;
         const int r = (int)(f - jj * (uint64_t)P.Ca);
         if (r >= kLanes * g && r < kLanes * g + n)
-          atomicOr(&ebits[wave][(int)(jj - (uint64_t)kBlock * b)], 1ull << (r - kLanes * g));
+          atomicOr(&eb[(int)(jj - (uint64_t)kBlock * b)], 1ull << (r - kLanes * g));
       }
+      wave_sync_lds();
+#pragma unroll
+      for (int k = 0; k < 4; ++k) esc[k] = eb[4 * lane + k];
       wave_sync_lds();
     }
   }
@@ -645,13 +684,12 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
   if (lane_ok) x = (uint32_t)wb[2 * lane] | ((uint32_t)wb[2 * lane + 1] << 16);
   uint32_t ptr = 2u * (uint32_t)n;
   const uint32_t *mytab = tab + lane * kTabStride;
-  const uint8_t *mybkt = bkt + lane * kBktStride;
+  const uint16_t *mybkt = bkt + lane * kBuckets;
   uint32_t *sout = P.sym32 + ((size_t)g * (P.N256 / 4) + (size_t)b * 64) * 64 + lane;
-  const unsigned long long *eb = ebits[wave];
   if (!has_esc && n == kLanes)
-    decode_rows<true>(x, ptr, base, W, Lb, lane, true, eb, mytab, mybkt, wb, wsrc, sout);
+    decode_rows<true>(x, ptr, base, W, Lb, lane, true, false, esc, mytab, mybkt, wb, wsrc, sout);
   else
-    decode_rows<false>(x, ptr, base, W, Lb, lane, lane_ok, has_esc ? eb : nullptr, mytab, mybkt, wb, wsrc, sout);
+    decode_rows<false>(x, ptr, base, W, Lb, lane, lane_ok, has_esc, esc, mytab, mybkt, wb, wsrc, sout);
   const bool lane_bad = lane_ok && x != kL;
   if (__ballot(lane_bad) != 0ull || ptr != W) {
     if (lane == 0) set_status(P.status, DCKV_ECORRUPT);
@@ -714,6 +752,7 @@ void launch_rans_encode(const EncodeArgs &a) {
   if (a.g.n_groups == 0) return;
   EncP P;
   P.tab = a.p->dev.tab;
+  P.rcp = a.p->dev.rcp;
   P.sym32 = reinterpret_cast<const uint32_t *>(a.ws + a.l.sym);
   P.scratch = reinterpret_cast<uint16_t *>(a.ws + a.l.scratch);
   P.gwords = reinterpret_cast<uint32_t *>(a.ws + a.l.gwords);
