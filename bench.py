@@ -92,7 +92,11 @@ def cpu_baseline(req_cfg: int, n_rows: int):
     except Exception:
         cores = len(os.sched_getaffinity(0))
     w = synth.world()
-    req = synth.make_request(req_cfg, n_rows=n_rows)
+    if synth.CONFIGS[req_cfg].get("n_requests"):
+        n_rows = min(n_rows, synth.CONFIGS[req_cfg]["T"])
+        req = synth.make_request(req_cfg, index=0, T=n_rows)
+    else:
+        req = synth.make_request(req_cfg, n_rows=n_rows)
     params = w.params()
     p = oplan.make_plan(np.float32(req.step_scale), w.base_step, w.laplace_scale)
     t0 = time.perf_counter()
@@ -100,11 +104,14 @@ def cpu_baseline(req_cfg: int, n_rows: int):
     t1 = time.perf_counter()
     ocodec.decode(enc.data, req.token_ids, params, p)
     t2 = time.perf_counter()
+    model, blas = _host_info()
+    what = ("request 0 of the batch (its first %d positions)" % n_rows if synth.CONFIGS[req_cfg].get("n_requests")
+            else "first %d positions of the workload as one %d-token prompt" % (n_rows, n_rows))
     return {"value": enc.N / (t2 - t0), "unit": "coded tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": "first %d positions of the workload as one %d-token prompt (%d coded), same seeds "
-                      "and step scale; encode %.2f s + decode %.2f s, numpy float64" % (
-                          n_rows, n_rows, enc.N, t1 - t0, t2 - t1),
-            "encode_tokens_per_s": enc.N / (t1 - t0), "decode_tokens_per_s": enc.N / (t2 - t1)}
+            "sample": "%s (%d coded), same seeds and step scale; encode %.2f s + decode %.2f s, numpy float64" % (
+                what, enc.N, t1 - t0, t2 - t1),
+            "encode_tokens_per_s": enc.N / (t1 - t0), "decode_tokens_per_s": enc.N / (t2 - t1),
+            "cpu_model": model, "blas": blas}
 
 
 def _counter_means(csv_dir: str, counter: str):
@@ -507,6 +514,33 @@ def main(argv=None) -> int:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
         return 2
 
+    return codec_bench(args)
+
+
+def _host_info():
+    """CPU model and the BLAS numpy uses (for the CPU baseline's record)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = "%s %s" % (b.get("name", "?"), b.get("version", ""))
+    except Exception:
+        pass
+    return model.strip(), blas.strip()
+
+
+def codec_bench(args) -> int:
+    """Encode + decode of the workload: one request through dckv_encode /
+    dckv_decode, or the batch workload's requests through the batch calls."""
     import torch
     import dckv_synth as synth
     import learned_kv_cache_dckv_amd as dk
@@ -514,48 +548,82 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = synth.world()
-    req = synth.make_request(args.config)
+    batch = synth.CONFIGS[args.config].get("n_requests", 0) > 0
+    if batch:
+        reqs = [synth.make_request(args.config, index=i) for i in range(synth.CONFIGS[args.config]["n_requests"])]
+    else:
+        reqs = [synth.make_request(args.config)]
     codec = dk.Codec(codec_params(w, args.codec), device=dev)
     t0 = time.perf_counter()
-    plan = codec.plan(req.step_scale)
+    plans = {}
+    for r in reqs:
+        if r.step_scale not in plans:
+            plans[r.step_scale] = codec.plan(r.step_scale)
     plan_ms = (time.perf_counter() - t0) * 1e3
-    T = req.T
-    rows = torch.from_numpy(req.rows.view(np.int16)).to(dev)
-    tok = torch.from_numpy(req.token_ids.astype(np.int32)).to(dev)
-    max_bytes, ws_bytes = plan.bytes(T)
+    R = []  # per request: device tensors and buffers
+    for r in reqs:
+        plan = plans[r.step_scale]
+        max_bytes, ws_bytes = plan.bytes(r.T)
+        R.append(dict(req=r, plan=plan, T=r.T, ws_bytes=ws_bytes,
+                      rows=torch.from_numpy(r.rows.view(np.int16)).to(dev),
+                      tok=torch.from_numpy(r.token_ids.astype(np.int32)).to(dev),
+                      buf=torch.empty(max_bytes, dtype=torch.uint8, device=dev),
+                      nb=torch.zeros(1, dtype=torch.int64, device=dev),
+                      st_e=torch.zeros(1, dtype=torch.int32, device=dev),
+                      st_d=torch.zeros(1, dtype=torch.int32, device=dev),
+                      out=torch.empty((r.T, codec.D), dtype=torch.int16, device=dev)))
+    if batch:
+        enc_reqs = [dk.Request(x["plan"], x["tok"], rows=x["rows"], stream=x["buf"], stream_bytes=x["nb"],
+                               status=x["st_e"]) for x in R]
+        ws_bytes = dk.dckv_bytes_batch(enc_reqs)
+    else:
+        ws_bytes = R[0]["ws_bytes"]
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    buf = torch.empty(max_bytes, dtype=torch.uint8, device=dev)
-    nb = torch.zeros(1, dtype=torch.int64, device=dev)
-    st_e = torch.zeros(1, dtype=torch.int32, device=dev)
-    st_d = torch.zeros(1, dtype=torch.int32, device=dev)
-    out = torch.empty((T, codec.D), dtype=torch.int16, device=dev)
 
-    # first pass: stream size (decode needs the host-side byte count)
-    dk.dckv_encode(plan, rows, tok, buf, nb, st_e, ws)
+    def encode_all():
+        if batch:
+            dk.dckv_encode_batch(enc_reqs, ws)
+        else:
+            x = R[0]
+            dk.dckv_encode(x["plan"], x["rows"], x["tok"], x["buf"], x["nb"], x["st_e"], ws)
+
+    # first pass: stream sizes (decode needs the host-side byte counts)
+    encode_all()
     torch.cuda.synchronize()
-    n_bytes = int(nb.item())
-    if int(st_e.item()) != 0 or n_bytes == 0:
-        print("encode failed with status %d" % int(st_e.item()), file=sys.stderr)
-        return 1
+    for x in R:
+        x["n_bytes"] = int(x["nb"].item())
+        if int(x["st_e"].item()) != 0 or x["n_bytes"] == 0:
+            print("encode failed with status %d" % int(x["st_e"].item()), file=sys.stderr)
+            return 1
 
     kv_out = None
     if args.layout == "heads":
+        if batch:
+            print("bench.py: --layout heads times one request", file=sys.stderr)
+            return 2
         sh = codec.shape
-        kv_out = [torch.empty((sh["n_kv_heads"], T, sh["head_dim"]), dtype=torch.int16, device=dev)
+        kv_out = [torch.empty((sh["n_kv_heads"], R[0]["T"], sh["head_dim"]), dtype=torch.int16, device=dev)
                   for _ in range(2 * sh["n_layers"])]
+    if batch:
+        dec_reqs = [dk.Request(x["plan"], x["tok"], stream=x["buf"], capacity=x["n_bytes"], rows_out=x["out"],
+                               status=x["st_d"]) for x in R]
 
-    def decode_call():
-        if kv_out is None:
-            dk.dckv_decode(plan, buf, n_bytes, tok, out, st_d, ws)
+    def decode_all():
+        if batch:
+            dk.dckv_decode_batch(dec_reqs, ws)
+        elif kv_out is None:
+            x = R[0]
+            dk.dckv_decode(x["plan"], x["buf"], x["n_bytes"], x["tok"], x["out"], x["st_d"], ws)
         else:
-            dk.dckv_decode_heads(plan, buf, n_bytes, tok, kv_out, st_d, ws)
+            x = R[0]
+            dk.dckv_decode_heads(x["plan"], x["buf"], x["n_bytes"], x["tok"], kv_out, x["st_d"], ws)
 
     def step():
-        dk.dckv_encode(plan, rows, tok, buf, nb, st_e, ws)
-        decode_call()
+        encode_all()
+        decode_all()
 
     s = torch.cuda.current_stream()
-    names = ("analysis_gemm", "fixup", "rans_encode", "scan", "pack", "parse", "rans_decode",
+    names = ("start", "analysis_gemm", "fixup", "rans_encode", "scan", "pack", "parse", "rans_decode",
              "dequant", "w1_gemm", "w1_gelu", "synthesis_gemm")
 
     def profiled(k, only=None):
@@ -577,7 +645,7 @@ def main(argv=None) -> int:
         for name in names:
             tot, n = dk.dckv_profile_read(name)
             if n:
-                res[name] = {"avg_ms": tot / n, "launches": n}
+                res[name] = {"avg_ms": tot / n, "launches": n, "launches_per_step": n / k}
         return a.elapsed_time(b) / k, res
 
     for _ in range(args.warmup):
@@ -587,7 +655,8 @@ def main(argv=None) -> int:
     _, calib = profiled(max(2, min(args.steps, 5)))
     dom = max(calib, key=lambda k: calib[k]["avg_ms"] * calib[k]["launches"])
     ms_step, dom_t = profiled(args.steps, only=dom)
-    assert int(st_e.item()) == 0 and int(st_d.item()) == 0 and int(nb.item()) == n_bytes
+    for x in R:
+        assert int(x["st_e"].item()) == 0 and int(x["st_d"].item()) == 0 and int(x["nb"].item()) == x["n_bytes"]
     # per-kernel breakdown (events on every kernel; not the timed region)
     _, kern = profiled(args.steps)
     kern[dom] = dict(dom_t[dom])
@@ -603,29 +672,48 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         return a.elapsed_time(b) / k
 
-    enc_ms = timed(lambda: dk.dckv_encode(plan, rows, tok, buf, nb, st_e, ws), args.steps)
-    dec_ms = timed(decode_call, args.steps)
+    enc_ms = timed(encode_all, args.steps)
+    dec_ms = timed(decode_all, args.steps)
 
-    # stream statistics (host side, after timing)
-    data = buf[:n_bytes].cpu().numpy()
-    hdr = data[:64].view(np.uint32)
-    N, Ca, n_groups, n_esc = int(hdr[5]), int(hdr[7]), int(hdr[8]), int(hdr[9])
-    rans_bytes = int(data[56:64].view(np.uint64)[0])
-    kept_bytes = (T - N) * KV_BYTES_PER_TOKEN
-    coded_bytes = n_bytes - 64 - kept_bytes
-    sym = torch.empty(N * Ca, dtype=torch.uint8, device=dev)
-    ne = torch.zeros(1, dtype=torch.int32, device=dev)
-    st = torch.zeros(1, dtype=torch.int32, device=dev)
-    dk.dckv_entropy_decode(plan, buf, n_bytes, T, sym, ne, st, ws)
-    torch.cuda.synchronize()
-    symh = sym.cpu().numpy().reshape(N, Ca)
-    freq = dk.dckv_plan_info(plan)["freq"].astype(np.float64)
-    ok = symh != 255
-    rank = np.broadcast_to(np.arange(Ca)[None, :], symh.shape)
-    modelled_bits = float(np.sum(15.0 - np.log2(freq[rank[ok], symh[ok]])) + 64.0 * n_esc)
+    # stream statistics (host side, after timing), summed over the requests
+    N_tot = coded_tot = n_esc_tot = groups_tot = total_bytes = 0
+    modelled_bits = 0.0
+    Ca = None
+    rans_tot = 0
+    for x in R:
+        n_bytes, T, plan = x["n_bytes"], x["T"], x["plan"]
+        data = x["buf"][:n_bytes].cpu().numpy()
+        hdr = data[:64].view(np.uint32)
+        N, Ca, n_groups, n_esc = int(hdr[5]), int(hdr[7]), int(hdr[8]), int(hdr[9])
+        rans_tot += int(data[56:64].view(np.uint64)[0])
+        coded_tot += n_bytes - 64 - (T - N) * KV_BYTES_PER_TOKEN
+        N_tot += N
+        n_esc_tot += n_esc
+        groups_tot += n_groups
+        total_bytes += n_bytes
+        sym = torch.empty(N * Ca, dtype=torch.uint8, device=dev)
+        ne = torch.zeros(1, dtype=torch.int32, device=dev)
+        st = torch.zeros(1, dtype=torch.int32, device=dev)
+        wse = torch.empty(x["ws_bytes"], dtype=torch.uint8, device=dev)
+        dk.dckv_entropy_decode(plan, x["buf"], n_bytes, T, sym, ne, st, wse)
+        torch.cuda.synchronize()
+        symh = sym.cpu().numpy().reshape(N, Ca)
+        freq = dk.dckv_plan_info(plan)["freq"].astype(np.float64)
+        ok = symh != 255
+        rank = np.broadcast_to(np.arange(Ca)[None, :], symh.shape)
+        modelled_bits += float(np.sum(15.0 - np.log2(freq[rank[ok], symh[ok]])) + 64.0 * n_esc)
+        del sym, wse
+
+    # algorithmic work of a kernel per launch: the step's total over its
+    # launches per step (a transform launch covers one request, a stream-stage
+    # launch all of them)
+    def work(name, v):
+        b_, u_, un_ = kernel_work(name, N_tot, Ca, rans_tot)
+        per = v.get("launches_per_step") or 1.0
+        return b_, u_ / per, un_
 
     # roofline of the dominant kernel (its time from the timed region)
-    bound, units, unit = kernel_work(dom, N, Ca, rans_bytes)
+    bound, units, unit = work(dom, kern[dom])
     avg_s = kern[dom]["avg_ms"] * 1e-3
     if unit == "flop":
         achieved = units / avg_s / 1e12
@@ -637,25 +725,51 @@ def main(argv=None) -> int:
                 "frac": achieved / PEAK_HBM_GBPS}
     roof["kernel"] = dom
     roof["traffic"] = None
-    if os.path.exists(TRAFFIC_FILE):
+    T0 = R[0]["T"]
+    if os.path.exists(TRAFFIC_FILE) and not batch:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         ent = tr.get(dom)
         src = os.path.join(ROOT, "learned_kv_cache_dckv_amd", "csrc", ent["source"]) if ent else None
-        if ent and os.path.exists(src) and source_sha(src) == ent["source_sha"] and ent.get("T") == T:
+        if ent and os.path.exists(src) and source_sha(src) == ent["source_sha"] and ent.get("T") == T0:
             roof["traffic"] = ent["bytes_per_launch"]
     for k, v in kern.items():
-        b, u, un = kernel_work(k, N, Ca, rans_bytes)
-        if un == "flop":
-            v["tflops"] = u / (v["avg_ms"] * 1e-3) / 1e12
+        b_, u_, un_ = work(k, v)
+        if un_ == "flop":
+            v["tflops"] = u_ / (v["avg_ms"] * 1e-3) / 1e12
             v["mfma_frac"] = v["tflops"] / PEAK_BF16_TFLOPS
-        elif un == "byte":
-            v["GBps"] = u / (v["avg_ms"] * 1e-3) / 1e9
+        elif un_ == "byte":
+            v["GBps"] = u_ / (v["avg_ms"] * 1e-3) / 1e9
             v["hbm_frac"] = v["GBps"] / PEAK_HBM_GBPS
 
+    pm = {}
+    seen = set()
+    plan_tab = mean_tab = 0
+    for p_ in plans.values():
+        m = dk.dckv_plan_memory(p_)
+        plan_tab += m["table_bytes"]
+        key = dk.dckv_plan_mean_table(p_)[0]
+        if key not in seen:
+            seen.add(key)
+            mean_tab += m["mean_table_bytes"]
+    pm = {"plans": len(plans), "plan_tables_bytes": plan_tab, "mean_tables": len(seen),
+          "mean_table_bytes": mean_tab, "workspace_bytes": ws_bytes,
+          "total_MiB": (plan_tab + mean_tab + ws_bytes) / 2 ** 20,
+          "pages_added_peak_MiB": 182, "note": "the pages report +182 MiB peak GPU memory for the codec "
+                                               "(their model, one request at a time); context, not a target"}
+    if batch:
+        workload = {"workload": synth.CONFIGS[args.config]["name"], "requests": len(R),
+                    "T_per_request": R[0]["T"], "rates_bytes_per_token": sorted({x["req"].rate_target for x in R}),
+                    "step_scales": sorted(plans.keys())}
+    else:
+        r0 = R[0]["req"]
+        workload = {"workload": r0.note, "T": r0.T, "rate_target_bytes_per_token": r0.rate_target,
+                    "step_scale": r0.step_scale}
+    workload.update({"codec": args.codec, "layout": args.layout, "coded_tokens": N_tot, "C_a": Ca,
+                     "groups": groups_tot})
     res = {
         "metric": METRIC,
-        "value": N / (ms_step * 1e-3),
+        "value": N_tot / (ms_step * 1e-3),
         "unit": "coded tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -666,22 +780,21 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": req.note, "codec": args.codec, "layout": args.layout, "T": T, "coded_tokens": N,
-                   "rate_target_bytes_per_token": req.rate_target,
-                   "step_scale": req.step_scale, "C_a": Ca, "groups": n_groups},
-        "encode_tokens_per_s": N / (enc_ms * 1e-3),
-        "decode_tokens_per_s": N / (dec_ms * 1e-3),
-        "encode_kv_GBps": N * KV_BYTES_PER_TOKEN / (enc_ms * 1e-3) / 1e9,
-        "decode_kv_GBps": N * KV_BYTES_PER_TOKEN / (dec_ms * 1e-3) / 1e9,
+        "config": workload,
+        "encode_tokens_per_s": N_tot / (enc_ms * 1e-3),
+        "decode_tokens_per_s": N_tot / (dec_ms * 1e-3),
+        "encode_kv_GBps": N_tot * KV_BYTES_PER_TOKEN / (enc_ms * 1e-3) / 1e9,
+        "decode_kv_GBps": N_tot * KV_BYTES_PER_TOKEN / (dec_ms * 1e-3) / 1e9,
         "encode_ms": enc_ms,
         "decode_ms": dec_ms,
-        "bytes_per_token": coded_bytes / N,
-        "total_bytes": n_bytes,
-        "ratio_vs_bf16": KV_BYTES_PER_TOKEN / (coded_bytes / N),
-        "stored_over_modelled": coded_bytes * 8.0 / modelled_bits if modelled_bits else None,
-        "n_esc": n_esc,
+        "bytes_per_token": coded_tot / N_tot,
+        "total_bytes": total_bytes,
+        "ratio_vs_bf16": KV_BYTES_PER_TOKEN / (coded_tot / N_tot),
+        "stored_over_modelled": coded_tot * 8.0 / modelled_bits if modelled_bits else None,
+        "n_esc": n_esc_tot,
         "plan_ms": plan_ms,
         "workspace_bytes": ws_bytes,
+        "memory": pm,
         "roofline": roof,
         "kernels": kern,
         "cpu_baseline": None,

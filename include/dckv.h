@@ -114,14 +114,26 @@ int dckv_plan_tables(const float *base_step, const float *laplace_scale, int32_t
                      uint16_t *freq_out, int32_t *c_active, uint32_t *crc);
 
 /* Builds a plan on the current HIP device, synchronously: host tables, an
- * upload of about 1 MB, and the embedding-mean table (below), which the plan
- * allocates (vocab * n_coef * 4 bytes: 256 MiB for a 32,768-token vocabulary)
- * and computes with one GEMM on the null stream.  *out receives the handle;
+ * upload of about 1.6 MB, and the embedding-mean table (below): vocab * n_coef
+ * * 4 bytes (256 MiB for a 32,768-token vocabulary), computed with one GEMM on
+ * the null stream, or shared with a live plan that has the same one
+ * (dckv_plan_memory).  *out receives the handle;
  * free with dckv_plan_free.  Returns DCKV_EUNSUPPORTED for shapes the kernels
  * do not support (vocab above 2^19 - 1 among them: the encoder addresses the
  * mean table with 32-bit byte offsets), DCKV_ENOMEM when an allocation fails. */
 int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **out);
 int dckv_plan_free(dckv_plan_t *plan);
+
+/* Device memory a plan holds (host outputs, any pointer may be NULL):
+ * *table_bytes, its own block of steps and integer tables (about 1.6 MB);
+ * *mean_table_bytes, the embedding-mean table it uses (vocab * n_coef * 4);
+ * *mean_table_users, how many live plans share that table.  Plans made on the
+ * same device from the same embedding and mean_head arrays, the same vocab
+ * and the same set of active components (so, the same column order) share
+ * one table: dckv_plan builds it for the first and the last dckv_plan_free
+ * releases it. */
+int dckv_plan_memory(const dckv_plan_t *plan, uint64_t *table_bytes, uint64_t *mean_table_bytes,
+                     int32_t *mean_table_users);
 
 /* Host copies of the plan's tables (any pointer may be NULL). */
 int dckv_plan_info(const dckv_plan_t *plan, float *step_out, uint8_t *active_out,
@@ -236,6 +248,25 @@ int dckv_decode_heads(const dckv_plan_t *plan, const uint8_t *stream, uint64_t s
 int dckv_unrope(const dckv_plan_t *plan, const uint16_t *rows_in, int64_t T, uint16_t *rows_out, void *hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * dckv_encode_postrope: dckv_encode of a cache whose keys already carry RoPE
+ * (the form an attention layer keeps them in).  DCKV digest, "How it works",
+ * first paragraph: the codec works on keys without their rotary embedding.
+ * rows [T][D] bf16 at positions 0..T-1, key heads rotated at angle t w_d.
+ * The call first rotates the key heads back into a key copy in the workspace
+ * (the arithmetic of dckv_unrope: fp64, no fused products, one rounding to
+ * bf16), then encodes with its key k-tiles from that copy and its value
+ * k-tiles from rows, so the stream equals dckv_encode's of
+ * dckv_unrope(rows) byte for byte.  The caller's rows are not modified.
+ * Other arguments and errors as dckv_encode; the workspace must hold
+ * dckv_bytes_postrope() bytes (the encode's part of dckv_bytes() plus
+ * T * n_layers * n_kv_heads * head_dim * 2 bytes for the key copy).
+ * --------------------------------------------------------------------------*/
+int dckv_bytes_postrope(const dckv_plan_t *plan, int64_t T, uint64_t *workspace_bytes);
+int dckv_encode_postrope(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *token_ids,
+                         int64_t T, uint8_t *stream, uint64_t capacity, uint64_t *stream_bytes,
+                         int32_t *status, void *workspace, uint64_t workspace_bytes, void *hip_stream);
+
+/* ---------------------------------------------------------------------------
  * Batches of independent requests in one call (DCKV digest, "How it works":
  * every request is coded on its own; "Limits": the pages code one request at a
  * time, so a batch is our extension).
@@ -253,11 +284,16 @@ int dckv_unrope(const dckv_plan_t *plan, const uint16_t *rows_in, int64_t T, uin
  *   status       (device) int32 per request, as for dckv_encode / dckv_decode
  * Every request is checked before anything is enqueued: an argument error in
  * any request returns its code (dckv_last_error names the request) and
- * enqueues nothing.  The requests then run in array order on hip_stream and
- * share one workspace of dckv_bytes_batch() bytes (the largest request's
- * need); the workspace is owned by the caller and must not be used by other
- * work on other streams meanwhile.  Each request's results equal those of the
- * single-request call.
+ * enqueues nothing.  The requests share one workspace of dckv_bytes_batch()
+ * bytes, the sum of their dckv_bytes() needs (each rounded up to 256 bytes):
+ * each request gets its own slice, so the stream stages of all requests (kept
+ * rows, rANS, group offsets and header, packing; on decode the parse and
+ * rANS) run in the same launches, up to 16 requests per launch, while each
+ * request's transform stages (the GEMMs and the dequantisation) run in their
+ * own launches, each of which fills the GPU.  Everything is enqueued on
+ * hip_stream; the workspace is owned by the caller and must not be used by
+ * other work on other streams meanwhile.  Each request's results equal those
+ * of the single-request call.
  * --------------------------------------------------------------------------*/
 typedef struct dckv_req {
   const dckv_plan_t *plan;

@@ -25,7 +25,8 @@ VIEW_SYMBOLS, VIEW_YHAT_B, VIEW_H_B = 0, 1, 2
 
 # every symbol include/dckv.h declares
 EXPORTS = ("dckv_plan_tables", "dckv_plan", "dckv_plan_free", "dckv_plan_info", "dckv_plan_mean_table",
-           "dckv_bytes", "dckv_encode", "dckv_encode_noalloc",
+           "dckv_plan_memory",
+           "dckv_bytes", "dckv_encode", "dckv_encode_noalloc", "dckv_bytes_postrope", "dckv_encode_postrope",
            "dckv_decode", "dckv_decode_heads", "dckv_unrope", "dckv_bytes_batch", "dckv_encode_batch", "dckv_decode_batch", "dckv_entropy_encode",
            "dckv_entropy_decode", "dckv_workspace_view", "dckv_profile_enable", "dckv_profile_only", "dckv_profile_reset",
            "dckv_profile_read", "dckv_fit_bytes", "dckv_fit", "dckv_rate_bytes", "dckv_rate_forward",
@@ -69,9 +70,12 @@ def _load():
         "dckv_plan_free": [P],
         "dckv_plan_info": [P, P, P, P, P, P],
         "dckv_plan_mean_table": [P, P, P, P],
+        "dckv_plan_memory": [P, P, P, P],
         "dckv_bytes": [P, I64, P, P],
         "dckv_encode": [P, P, P, I64, P, U64, P, P, P, U64, P],
         "dckv_encode_noalloc": [P, P, P, I64, P, U64, P, P, P],
+        "dckv_bytes_postrope": [P, I64, P],
+        "dckv_encode_postrope": [P, P, P, I64, P, U64, P, P, P, U64, P],
         "dckv_decode": [P, P, U64, P, I64, P, P, P, U64, P],
         "dckv_decode_heads": [P, P, U64, P, I64, P, P, P, U64, P],
         "dckv_unrope": [P, P, I64, P, P],
@@ -249,6 +253,13 @@ def dckv_plan_info(plan: Plan) -> dict:
     return dict(step=step, active=active.astype(bool), freq=freq[:ca.value], c_active=ca.value, crc=crc.value)
 
 
+def dckv_plan_memory(plan: Plan) -> dict:
+    """Device bytes the plan holds and how many plans share its mean table."""
+    tb, mb, users = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_int32()
+    _check(_lib.dckv_plan_memory(plan.handle, ctypes.byref(tb), ctypes.byref(mb), ctypes.byref(users)))
+    return dict(table_bytes=tb.value, mean_table_bytes=mb.value, mean_table_users=users.value)
+
+
 def dckv_plan_mean_table(plan: Plan):
     """(device address of the table, rows, col_component[n_coef]): the plan's
     embedding-mean table, fp32 [rows][n_coef]."""
@@ -310,6 +321,22 @@ def dckv_encode_noalloc(plan: Plan, rows, token_ids, stream_buf, stream_bytes, s
     rows = _as_bits(rows)
     _check(_lib.dckv_encode_noalloc(plan.handle, _ptr(rows), _ptr(token_ids), T, _ptr(stream_buf),
                                     stream_buf.numel(), _ptr(stream_bytes), _ptr(status), _stream_handle(stream)))
+
+
+def dckv_bytes_postrope(plan: Plan, T: int) -> int:
+    """Workspace bytes of dckv_encode_postrope for a request of T tokens."""
+    v = ctypes.c_uint64()
+    _check(_lib.dckv_bytes_postrope(plan.handle, int(T), ctypes.byref(v)))
+    return v.value
+
+
+def dckv_encode_postrope(plan: Plan, rows, token_ids, stream_buf, stream_bytes, status, ws, stream=None):
+    """Enqueue an encode of post-RoPE rows [T][D] (keys rotated back inside)."""
+    T = int(rows.shape[0])
+    rows = _as_bits(rows)
+    _check(_lib.dckv_encode_postrope(plan.handle, _ptr(rows), _ptr(token_ids), T, _ptr(stream_buf),
+                                     stream_buf.numel(), _ptr(stream_bytes), _ptr(status), _ptr(ws), ws.numel(),
+                                     _stream_handle(stream)))
 
 
 def dckv_decode(plan: Plan, stream_buf, n_bytes: int, token_ids, rows_out, status, ws, stream=None):

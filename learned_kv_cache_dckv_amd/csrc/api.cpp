@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "dckv_internal.h"
 
@@ -66,13 +67,24 @@ int encode_checks(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *
   return DCKV_OK;
 }
 
-void encode_sequence(const EncodeArgs &a) {
-  launch_start_encode(a);
-  launch_analysis_gemm(a);
-  launch_encode_fixup(a);
-  launch_rans_encode(a);
-  launch_scan_header(a);
-  launch_pack(a);
+int batch_error(int rc, int32_t i, const char *what) {
+  char msg[160];
+  std::snprintf(msg, sizeof msg, "%s: request %d: %s", what, (int)i, dckv_last_error());
+  return set_error(rc, msg);
+}
+
+// The big transform GEMMs (analysis, synthesis) run per request: each launch
+// fills the chip on its own.  Every other stage runs over all n requests at
+// once, so the small kernels of short requests share their launches.
+void encode_sequence(const EncodeArgs *a, int n) {
+  launch_start_encode(a, n);
+  for (int i = 0; i < n; ++i) {
+    launch_analysis_gemm(a[i]);
+    launch_encode_fixup(a[i]);
+  }
+  launch_rans_encode(a, n);
+  launch_scan_header(a, n);
+  launch_pack(a, n);
 }
 
 int decode_checks(const dckv_plan_t *plan, const uint8_t *stream, uint64_t stream_bytes, const int32_t *token_ids,
@@ -87,18 +99,28 @@ int decode_checks(const dckv_plan_t *plan, const uint8_t *stream, uint64_t strea
   return DCKV_OK;
 }
 
-void decode_sequence(const DecodeArgs &a) {
-  launch_parse(a, true);
-  launch_rans_decode(a);
-  launch_dequant(a);
-  launch_w1_gemm(a);  // also RoPE on the kept rows
-  launch_synthesis_gemm(a);
+void decode_sequence(const DecodeArgs *a, int n) {
+  launch_parse(a, n, true);
+  launch_rans_decode(a, n);
+  launch_dequant(a, n);
+  launch_w1_gemm(a, n);  // also RoPE on the kept rows
+  for (int i = 0; i < n; ++i) launch_synthesis_gemm(a[i]);
 }
 
-int batch_error(int rc, int32_t i, const char *what) {
-  char msg[160];
-  std::snprintf(msg, sizeof msg, "%s: request %d: %s", what, (int)i, dckv_last_error());
-  return set_error(rc, msg);
+// Workspace slices of a batch: request i at offsets[i], each 256-byte aligned
+// and as large as dckv_bytes() reports for it.
+int batch_slices(const dckv_req *reqs, int32_t n, std::vector<uint64_t> &offsets, uint64_t &total) {
+  offsets.assign((size_t)std::max(n, 0), 0);
+  total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    uint64_t ws = 0;
+    const int rc = dckv_bytes(reqs[i].plan, reqs[i].T, nullptr, &ws);
+    if (rc) return batch_error(rc, i, "batch");
+    offsets[i] = total;
+    total += (ws + 255) & ~(uint64_t)255;
+  }
+  total = std::max<uint64_t>(total, 256);
+  return DCKV_OK;
 }
 
 }  // namespace
@@ -111,8 +133,9 @@ extern "C" int dckv_encode(const dckv_plan_t *plan, const uint16_t *rows, const 
   int rc = encode_checks(plan, rows, token_ids, T, stream, capacity, stream_bytes, status, workspace,
                          workspace_bytes, g, l);
   if (rc) return rc;
-  encode_sequence(EncodeArgs{plan, g, l, static_cast<uint8_t *>(workspace), rows, token_ids, stream, capacity,
-                             stream_bytes, status, static_cast<hipStream_t>(hip_stream)});
+  const EncodeArgs a{plan, g, l, static_cast<uint8_t *>(workspace), rows, token_ids, stream, capacity,
+                     stream_bytes, status, static_cast<hipStream_t>(hip_stream)};
+  encode_sequence(&a, 1);
   return after_launch("dckv_encode");
 }
 
@@ -124,8 +147,9 @@ extern "C" int dckv_decode(const dckv_plan_t *plan, const uint8_t *stream, uint6
   int rc = decode_checks(plan, stream, stream_bytes, token_ids, T, rows_out, status, workspace, workspace_bytes,
                          g, l);
   if (rc) return rc;
-  decode_sequence(DecodeArgs{plan, g, l, static_cast<uint8_t *>(workspace), stream, stream_bytes, token_ids,
-                             rows_out, status, static_cast<hipStream_t>(hip_stream)});
+  const DecodeArgs a{plan, g, l, static_cast<uint8_t *>(workspace), stream, stream_bytes, token_ids,
+                     rows_out, status, static_cast<hipStream_t>(hip_stream)};
+  decode_sequence(&a, 1);
   return after_launch("dckv_decode");
 }
 
@@ -147,64 +171,73 @@ extern "C" int dckv_decode_heads(const dckv_plan_t *plan, const uint8_t *stream,
   DecodeArgs a{plan, g, l, static_cast<uint8_t *>(workspace), stream, stream_bytes, token_ids, nullptr, status,
                static_cast<hipStream_t>(hip_stream)};
   a.heads = &h;
-  decode_sequence(a);
+  decode_sequence(&a, 1);
   return after_launch("dckv_decode_heads");
 }
 
 extern "C" int dckv_bytes_batch(const dckv_req *reqs, int32_t n, uint64_t *workspace_bytes) {
   if (n < 0 || (n > 0 && !reqs) || !workspace_bytes) return set_error(DCKV_EINVAL, "bytes_batch: bad argument");
-  uint64_t need = 256;
-  for (int32_t i = 0; i < n; ++i) {
-    uint64_t ws = 0;
-    const int rc = dckv_bytes(reqs[i].plan, reqs[i].T, nullptr, &ws);
-    if (rc) return batch_error(rc, i, "bytes_batch");
-    need = std::max(need, ws);
-  }
-  *workspace_bytes = need;
+  std::vector<uint64_t> off;
+  uint64_t total = 0;
+  const int rc = batch_slices(reqs, n, off, total);
+  if (rc) return rc;
+  *workspace_bytes = total;
   return DCKV_OK;
 }
 
 extern "C" int dckv_encode_batch(const dckv_req *reqs, int32_t n, void *workspace, uint64_t workspace_bytes,
                                  void *hip_stream) {
   if (n < 0 || (n > 0 && !reqs)) return set_error(DCKV_EINVAL, "encode_batch: bad argument");
+  std::vector<uint64_t> off;
+  uint64_t total = 0;
+  int rc = batch_slices(reqs, n, off, total);
+  if (rc) return rc;
+  if (!workspace || workspace_bytes < total)
+    return set_error(DCKV_ECAPACITY, "encode_batch: workspace smaller than dckv_bytes_batch() reports");
+  std::vector<EncodeArgs> args;
+  args.reserve(n);
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
   for (int32_t i = 0; i < n; ++i) {
     const dckv_req &r = reqs[i];
     Geometry g;
     Layout l;
-    const int rc = encode_checks(r.plan, r.rows, r.token_ids, r.T, r.stream, r.capacity, r.stream_bytes, r.status,
-                                 workspace, workspace_bytes, g, l);
+    rc = encode_checks(r.plan, r.rows, r.token_ids, r.T, r.stream, r.capacity, r.stream_bytes, r.status,
+                       ws + off[i], total - off[i], g, l);
     if (rc) return batch_error(rc, i, "encode_batch");
     if (i > 0 && r.plan->device != reqs[0].plan->device)
       return batch_error(DCKV_EINVAL, i, "encode_batch: plans on different devices");
+    args.push_back(EncodeArgs{r.plan, g, l, ws + off[i], r.rows, r.token_ids, r.stream, r.capacity, r.stream_bytes,
+                              r.status, static_cast<hipStream_t>(hip_stream)});
   }
-  for (int32_t i = 0; i < n; ++i) {
-    const dckv_req &r = reqs[i];
-    const Geometry g = geometry(r.plan, r.T);
-    encode_sequence(EncodeArgs{r.plan, g, layout(r.plan, g), static_cast<uint8_t *>(workspace), r.rows, r.token_ids,
-                               r.stream, r.capacity, r.stream_bytes, r.status, static_cast<hipStream_t>(hip_stream)});
-  }
+  if (n > 0) encode_sequence(args.data(), n);
   return after_launch("dckv_encode_batch");
 }
 
 extern "C" int dckv_decode_batch(const dckv_req *reqs, int32_t n, void *workspace, uint64_t workspace_bytes,
                                  void *hip_stream) {
   if (n < 0 || (n > 0 && !reqs)) return set_error(DCKV_EINVAL, "decode_batch: bad argument");
+  std::vector<uint64_t> off;
+  uint64_t total = 0;
+  int rc = batch_slices(reqs, n, off, total);
+  if (rc) return rc;
+  if (!workspace || workspace_bytes < total)
+    return set_error(DCKV_ECAPACITY, "decode_batch: workspace smaller than dckv_bytes_batch() reports");
+  std::vector<DecodeArgs> args;
+  args.reserve(n);
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
   for (int32_t i = 0; i < n; ++i) {
     const dckv_req &r = reqs[i];
     Geometry g;
     Layout l;
-    const int rc = decode_checks(r.plan, r.stream, r.capacity, r.token_ids, r.T, r.rows_out, r.status, workspace,
-                                 workspace_bytes, g, l);
+    rc = decode_checks(r.plan, r.stream, r.capacity, r.token_ids, r.T, r.rows_out, r.status, ws + off[i],
+                       total - off[i], g, l);
     if (rc) return batch_error(rc, i, "decode_batch");
     if (i > 0 && r.plan->device != reqs[0].plan->device)
       return batch_error(DCKV_EINVAL, i, "decode_batch: plans on different devices");
+    args.push_back(DecodeArgs{r.plan, g, l, ws + off[i], r.stream, r.capacity, r.token_ids, r.rows_out, r.status,
+                              static_cast<hipStream_t>(hip_stream)});
   }
-  for (int32_t i = 0; i < n; ++i) {
-    const dckv_req &r = reqs[i];
-    const Geometry g = geometry(r.plan, r.T);
-    decode_sequence(DecodeArgs{r.plan, g, layout(r.plan, g), static_cast<uint8_t *>(workspace), r.stream,
-                               r.capacity, r.token_ids, r.rows_out, r.status, static_cast<hipStream_t>(hip_stream)});
-  }
+  if (n > 0) decode_sequence(args.data(), n);
   return after_launch("dckv_decode_batch");
 }
 
@@ -225,12 +258,12 @@ extern "C" int dckv_entropy_encode(const dckv_plan_t *plan, int64_t T, const uin
   if (capacity < g.fixed_bytes) return set_error(DCKV_ECAPACITY, "capacity below the stream's fixed part");
   EncodeArgs a{plan, g, l, static_cast<uint8_t *>(workspace), rows, nullptr, stream, capacity,
                stream_bytes, status, static_cast<hipStream_t>(hip_stream)};
-  launch_start_encode(a);
+  launch_start_encode(&a, 1);
   launch_sym_to_tiled(a, sym);
   launch_load_esc(a, esc, n_esc);
-  launch_rans_encode(a);
-  launch_scan_header(a);
-  launch_pack(a);
+  launch_rans_encode(&a, 1);
+  launch_scan_header(&a, 1);
+  launch_pack(&a, 1);
   return after_launch("dckv_entropy_encode");
 }
 
@@ -246,8 +279,8 @@ extern "C" int dckv_entropy_decode(const dckv_plan_t *plan, const uint8_t *strea
   if (stream_bytes < g.fixed_bytes) return set_error(DCKV_ECORRUPT, "stream shorter than its fixed part");
   DecodeArgs a{plan, g, l, static_cast<uint8_t *>(workspace), stream, stream_bytes, nullptr, nullptr, status,
                static_cast<hipStream_t>(hip_stream)};
-  launch_parse(a, false);
-  launch_rans_decode(a);
+  launch_parse(&a, 1, false);
+  launch_rans_decode(&a, 1);
   launch_sym_from_tiled(a, sym_out, n_esc_out);
   return after_launch("dckv_entropy_decode");
 }
@@ -475,7 +508,51 @@ extern "C" int dckv_encode_noalloc(const dckv_plan_t *plan, const uint16_t *rows
   rc = encode_checks(plan, rows, token_ids, T, stream, capacity, stream_bytes, status, ws, kNoAllocScratchBytes, g,
                      l, /*encode_only=*/true);
   if (rc) return rc;
-  encode_sequence(EncodeArgs{plan, g, l, static_cast<uint8_t *>(ws), rows, token_ids, stream, capacity, stream_bytes,
-                             status, static_cast<hipStream_t>(hip_stream)});
+  const EncodeArgs a{plan, g, l, static_cast<uint8_t *>(ws), rows, token_ids, stream, capacity, stream_bytes,
+                     status, static_cast<hipStream_t>(hip_stream)};
+  encode_sequence(&a, 1);
   return after_launch("dckv_encode_noalloc");
+}
+
+// ---------------------------------------------------------------------------
+// Encode from a post-RoPE cache: the key heads are rotated back into a copy in
+// the workspace (fp64, one bf16 rounding, as dckv_unrope), then the usual
+// encode reads its key k-tiles and kept-row keys from that copy and its value
+// k-tiles from the caller's rows.
+// ---------------------------------------------------------------------------
+namespace {
+uint64_t postrope_keys_offset(const Layout &l) { return (l.enc_total + 255) & ~(uint64_t)255; }
+}  // namespace
+
+extern "C" int dckv_bytes_postrope(const dckv_plan_t *plan, int64_t T, uint64_t *workspace_bytes) {
+  uint64_t ws = 0;
+  const int rc = dckv_bytes(plan, T, nullptr, &ws);
+  if (rc) return rc;
+  if (!workspace_bytes) return set_error(DCKV_EINVAL, "bytes_postrope: null workspace_bytes");
+  const Layout l = layout(plan, geometry(plan, T));
+  *workspace_bytes = postrope_keys_offset(l) + (uint64_t)std::max<int64_t>(T, 1) * kKeyCols * 2;
+  return DCKV_OK;
+}
+
+extern "C" int dckv_encode_postrope(const dckv_plan_t *plan, const uint16_t *rows, const int32_t *token_ids,
+                                    int64_t T, uint8_t *stream, uint64_t capacity, uint64_t *stream_bytes,
+                                    int32_t *status, void *workspace, uint64_t workspace_bytes, void *hip_stream) {
+  uint64_t need = 0;
+  int rc = dckv_bytes_postrope(plan, T, &need);
+  if (rc) return rc;
+  if (workspace_bytes < need)
+    return set_error(DCKV_ECAPACITY, "encode_postrope: workspace smaller than dckv_bytes_postrope() reports");
+  Geometry g;
+  Layout l;
+  rc = encode_checks(plan, rows, token_ids, T, stream, capacity, stream_bytes, status, workspace, workspace_bytes, g,
+                     l, /*encode_only=*/true);
+  if (rc) return rc;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  uint16_t *keys = reinterpret_cast<uint16_t *>(ws + postrope_keys_offset(l));
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  launch_unrope_keys(plan, rows, keys, T, s);
+  EncodeArgs a{plan, g, l, ws, rows, token_ids, stream, capacity, stream_bytes, status, s};
+  a.keys = keys;
+  encode_sequence(&a, 1);
+  return after_launch("dckv_encode_postrope");
 }

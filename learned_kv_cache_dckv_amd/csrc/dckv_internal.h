@@ -47,6 +47,7 @@ constexpr int kHid = 256;
 constexpr int kEmb = 2048;
 constexpr int kHeadDim = 256;
 constexpr int kHalf = kHeadDim / 2;
+constexpr int kKeyCols = 6 * 2 * kHeadDim;  // the key heads of a row (n_layers * n_kv_heads * head_dim)
 
 // ---- plan ----------------------------------------------------------------
 struct PlanDev {
@@ -79,8 +80,11 @@ struct dckv_plan_s {
   dckv::PlanDev dev;
   void *dev_block = nullptr;  // one allocation holding every PlanDev array
   // embedding-mean table [vocab][C] fp32: column i of row v is
-  // sum_k E[v][k] H[perm[i]][k] (its own allocation)
+  // sum_k E[v][k] H[perm[i]][k].  Plans over the same device, E, H, vocab and
+  // column order share one reference-counted copy; mt_perm is that order.
   float *mtab = nullptr;
+  std::vector<int32_t> mt_perm;
+  uint64_t dev_bytes = 0;  // the plan's own device block
 };
 
 namespace dckv {
@@ -146,6 +150,9 @@ struct EncodeArgs {
   uint64_t *stream_bytes;
   int32_t *status;
   hipStream_t s;
+  // set (encode from a post-RoPE cache): the pre-RoPE key heads of every row,
+  // [T][kKeyCols]; rows then supplies only the value heads
+  const uint16_t *keys = nullptr;
 };
 
 // Decoded rows either as rows_out [T][D], or per attention layer: for layer
@@ -169,16 +176,66 @@ struct DecodeArgs {
   const KvHeads *heads = nullptr;  // set: the per-layer layout, rows_out unused
 };
 
+// The stream stages (kept rows, rANS, scan, pack, parse) take n requests at
+// once: their kernels run up to kLaunchBatch requests per launch, so the
+// requests of a batch share each launch (and its load balance).
+constexpr int kLaunchBatch = 16;
+
+// Parameters of up to kMax requests for one launch of a stage kernel:
+// request r owns workgroups [start[r], start[r + 1]) of a 1-D grid.
+template <class P, int kMax = kLaunchBatch>
+struct Batch {
+  int n;
+  uint32_t start[kMax + 1];
+  P r[kMax];
+};
+
+// The request that owns workgroup w (a wave-uniform scan of the starts).
+template <class P, int kMax>
+__device__ __forceinline__ int batch_req(const Batch<P, kMax> &B, uint32_t w) {
+  int r = 0;
+#pragma unroll
+  for (int i = 1; i < kMax; ++i) r = (i < B.n && w >= B.start[i]) ? i : r;
+  return r;
+}
+
+// Launches kern over requests 0..n-1 in launches of up to kMax: fill(i) gives
+// request i's parameters, count(i) its workgroups (0: none); lds, dynamic LDS
+// bytes per workgroup.
+template <class P, int kMax = kLaunchBatch, class Kern, class Fill, class Count>
+void launch_batched(Kern kern, const char *name, int n, hipStream_t s, unsigned threads, Fill fill, Count count,
+                    size_t lds = 0) {
+  if (lds > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+  for (int i0 = 0; i0 < n; i0 += kMax) {
+    Batch<P, kMax> B{};
+    B.n = n - i0 < kMax ? n - i0 : kMax;
+    uint32_t w = 0;
+    for (int r = 0; r < B.n; ++r) {
+      B.start[r] = w;
+      B.r[r] = fill(i0 + r);
+      w += count(i0 + r);
+    }
+    for (int r = B.n; r <= kMax; ++r) B.start[r] = w;
+    if (w == 0) continue;
+    KernelTimer tm(name, s);
+    hipLaunchKernelGGL(kern, dim3(w), dim3(threads), lds, s, B);
+  }
+}
+
 // misc.hip
-void launch_start_encode(const EncodeArgs &a);  // control words, status, kept rows
+void launch_start_encode(const EncodeArgs *a, int n);  // control words, status, kept rows
 void launch_unrope(const dckv_plan_t *p, const uint16_t *in, uint16_t *out, int64_t T, hipStream_t s);
+// the inverse RoPE of the key heads only, rows [T][D] -> keys [T][kKeyCols]
+void launch_unrope_keys(const dckv_plan_t *p, const uint16_t *in, uint16_t *keys, int64_t T, hipStream_t s);
 
 // rans.hip
-void launch_rans_encode(const EncodeArgs &a);
-void launch_scan_header(const EncodeArgs &a);
-void launch_pack(const EncodeArgs &a);
-void launch_parse(const DecodeArgs &a, bool with_rope);  // control words, status, parse, RoPE tables
-void launch_rans_decode(const DecodeArgs &a);
+void launch_rans_encode(const EncodeArgs *a, int n);
+void launch_scan_header(const EncodeArgs *a, int n);
+void launch_pack(const EncodeArgs *a, int n);
+void launch_parse(const DecodeArgs *a, int n, bool with_rope);  // control words, status, parse, RoPE tables
+void launch_rans_decode(const DecodeArgs *a, int n);
 void launch_load_esc(const EncodeArgs &a, const uint32_t *esc, uint32_t n_esc);
 void launch_sym_to_tiled(const EncodeArgs &a, const uint8_t *sym);
 void launch_sym_from_tiled(const DecodeArgs &a, uint8_t *sym_out, uint32_t *n_esc_out);
@@ -280,8 +337,8 @@ struct RateBwdArgs {
 void rate_bwd_sequence(const RateBwdArgs &a);
 void launch_analysis_gemm(const EncodeArgs &a);
 void launch_encode_fixup(const EncodeArgs &a);
-void launch_dequant(const DecodeArgs &a);
-void launch_w1_gemm(const DecodeArgs &a);
+void launch_dequant(const DecodeArgs *a, int n);
+void launch_w1_gemm(const DecodeArgs *a, int n);
 void launch_synthesis_gemm(const DecodeArgs &a);
 
 

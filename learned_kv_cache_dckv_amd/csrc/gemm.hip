@@ -53,6 +53,8 @@
 // registers and stores it during the next tile's main loop.
 #include <cmath>
 
+#include <vector>
+
 #include "dckv_internal.h"
 
 namespace dckv {
@@ -155,8 +157,12 @@ struct TileSrc {
   uint32_t soff, rb;
 };
 
+// kKV: the k-tiles alternate in runs of 8 (one layer's two key heads, then
+// its two value heads); key runs come from p0, a [rows][6 * 512] key copy,
+// value runs from p1 at their own columns (split unused).
+template <bool kKV = false>
 __device__ __forceinline__ TileSrc tile_src(const Operand &op, int kt, int KT) {
-  const bool s0 = kt < op.split;
+  const bool s0 = kKV ? ((kt >> 3) & 1) == 0 : kt < op.split;
   // base and range are wave-uniform: keep them in scalar registers
   const uint64_t b = reinterpret_cast<uint64_t>(s0 ? op.p0 : op.p1);
   // (readfirstlane returns int: zero-extend each half, never sign-extend)
@@ -166,7 +172,10 @@ __device__ __forceinline__ TileSrc tile_src(const Operand &op, int kt, int KT) {
   TileSrc t;
   t.r = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(bu), (short)0, nrec, 0x00020000);
   t.rb = s0 ? op.rb0 : op.rb1;
-  t.soff = (uint32_t)(s0 ? kt : kt - op.split) * kRowBytes;
+  if (kKV)
+    t.soff = (uint32_t)(s0 ? (kt >> 4) * 8 + (kt & 7) : kt) * kRowBytes;
+  else
+    t.soff = (uint32_t)(s0 ? kt : kt - op.split) * kRowBytes;
   return t;
 }
 
@@ -243,7 +252,7 @@ struct NoSide {
 // kPeel > 0: the first kPeel k-tiles are unrolled and call side(8 kt + i),
 // i = 0..7, spread over their third k-step (work with compile-time indices,
 // such as stores of registers held from a previous tile); needs KT >= kPeel.
-template <bool kPinAcc = true, int kPeel = 0, class S = NoSide>
+template <bool kPinAcc = true, int kPeel = 0, bool kKV = false, class S = NoSide>
 __device__ __forceinline__ void mainloop(const Operand &A, const Operand &B, int KT, f32x16 (&acc)[4][4],
                                          char *lds, S &&side = S()) {
   // the wave index in a scalar register: LDS destinations of the direct loads
@@ -255,13 +264,13 @@ __device__ __forceinline__ void mainloop(const Operand &A, const Operand &B, int
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
   {
-    const TileSrc a0 = tile_src(A, 0, KT), b0 = tile_src(B, 0, KT);
+    const TileSrc a0 = tile_src<kKV>(A, 0, KT), b0 = tile_src(B, 0, KT);
 #pragma unroll
     for (int i = 0; i < 8; ++i) load_rows(A, a0, i, lds, wave, lane);
 #pragma unroll
     for (int i = 0; i < 8; ++i) load_rows(B, b0, i, lds + kBM * kRowBytes, wave, lane);
   }
-  TileSrc ta = tile_src(A, 1, KT), tb = tile_src(B, 1, KT);
+  TileSrc ta = tile_src<kKV>(A, 1, KT), tb = tile_src(B, 1, KT);
 #pragma unroll
   for (int i = 0; i < 8; ++i) load_rows(A, ta, i, lds + kStageBytes, wave, lane);
   tile_barrier<8>();  // k-tile 0 has landed
@@ -275,7 +284,7 @@ __device__ __forceinline__ void mainloop(const Operand &A, const Operand &B, int
     kstep(acc, f1, f0, cur, 2, lane, wm, wn, sidek);
     kstep(acc, f0, f1, cur, 3, lane, wm, wn, none);
     tile_barrier<0>();
-    ta = tile_src(A, kt + 2, KT);
+    ta = tile_src<kKV>(A, kt + 2, KT);
     tb = tile_src(B, kt + 2, KT);
     kstep(acc, f1, f0, nxt, 0, lane, wm, wn, [&](int i) { load_rows(A, ta, i, cur, wave, lane); });
   };
@@ -452,6 +461,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_f32(GemmF32Pair PP) {
 // ---------------------------------------------------------------------------
 struct QuantP {
   const uint16_t *rows, *A;
+  const uint16_t *keys;  // set: key heads from this pre-RoPE key copy [T][6 * 512], value heads from rows
   const int32_t *act, *tok;
   const float *step, *nbr;
   const float *qcol;  // [C_a padded][4]: step, 1 / step (0 past C_a), a, 0 of each rank
@@ -518,6 +528,8 @@ __device__ __forceinline__ uint32_t pack_u8x4(float a, float b, float c, float d
   return __builtin_amdgcn_cvt_pk_u8_f32(d, 3, w);
 }
 
+// kKeys: the key heads come from P.keys (encode of a post-RoPE cache)
+template <bool kKeys>
 __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   if (wg_stop(P.status)) return;
@@ -526,7 +538,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   const int64_t m0 = (int64_t)mt * kBM;
   const int n0 = nt * kBN;
   Operand A, B;
-  set_sources(A, P.rows, kD * 2, P.rows, kD * 2, kD / kBK);
+  if (kKeys)
+    set_sources(A, P.keys, kKeyCols * 2, P.rows, kD * 2, 0);
+  else
+    set_sources(A, P.rows, kD * 2, P.rows, kD * 2, kD / kBK);
   set_sources(B, P.A, kD * 2, P.A, kD * 2, kD / kBK);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -553,7 +568,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
   for (int nb = 0; nb < 4; ++nb)
     qc[nb] = gload(reinterpret_cast<const f32x4 *>(P.qcol) + n0 + wn * 128 + nb * 32 + (threadIdx.x & 31));
   f32x16 acc[4][4];
-  mainloop(A, B, kD / kBK, acc, lds);
+  mainloop<true, 0, kKeys>(A, B, kD / kBK, acc, lds);
 
   // The epilogue works one 32x32 accumulator block at a time.  Each value
   // first takes a short path that assumes a coded row, an active rank, a
@@ -851,10 +866,15 @@ __device__ __forceinline__ int esc_search(const DeqP &P, int j, int r) {
 // yhat_{j+1})); rows past the end count as zero.  kDense: no dropped
 // component, so component = rank = table column.
 template <bool kDense>
-__global__ __launch_bounds__(kDeqThreads) void k_dequant(DeqP P) {
+__global__ __launch_bounds__(kDeqThreads) void k_dequant(const Batch<DeqP> Bt) {
+  const int ri = batch_req(Bt, blockIdx.x);
+  const DeqP &P = Bt.r[ri];
+  const uint32_t local = blockIdx.x - Bt.start[ri];
+  constexpr uint32_t kCols = kC / (4 * kDeqThreads);  // workgroups across a row's components
+  const uint32_t by = local % kCols, bx = local / kCols;
   if (gload(P.status) != 0) return;
-  const int c0 = (blockIdx.y * kDeqThreads + threadIdx.x) * 4;
-  const int j0 = blockIdx.x * kDeqRows;
+  const int c0 = (by * kDeqThreads + threadIdx.x) * 4;
+  const int j0 = bx * kDeqRows;
   const int N = (int)P.N;
   const size_t n_quads = (size_t)(P.N256 / 4);
   float st[4], a[4];
@@ -1021,11 +1041,16 @@ struct W1P {
 // 256-row tiles times 2 halves fill twice as many CUs as whole-K tiles; the
 // halves are added (one fp32 addition, so the order does not matter) by
 // k_w1_gelu.
-__global__ __launch_bounds__(kThreads, 1) void k_w1(W1P P) {
+constexpr int kW1Batch = 8;  // requests per launch of the W1 kernels (their parameters are large)
+
+__global__ __launch_bounds__(kThreads, 1) void k_w1(const Batch<W1P, kW1Batch> Bt) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int ri = batch_req(Bt, blockIdx.x);
+  const W1P &P = Bt.r[ri];
+  const uint32_t local = blockIdx.x - Bt.start[ri];
   if (wg_stop(P.status)) return;
   int mt, kh;
-  tile_of(blockIdx.x, P.n_mt * 2, 2, mt, kh);
+  tile_of((int)local, P.n_mt * 2, 2, mt, kh);
   const int64_t m0 = (int64_t)mt * kBM;
   Operand A, B;
   set_sources(A, P.yhat_b + kh * (kC / 2), kC * 2, P.yhat_b + kh * (kC / 2), kC * 2, kC / 2 / kBK);
@@ -1058,13 +1083,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_w1(W1P P) {
 // h_b = bf16(GELU(part0 + part1)), exact-erf GELU; 4 hidden units per thread.
 // Workgroups past the GELU ones apply RoPE to one kept row each (the RoPE
 // tables are written by the parse kernel, which runs first).
-__global__ __launch_bounds__(256) void k_w1_gelu(W1P P) {
+__global__ __launch_bounds__(256) void k_w1_gelu(const Batch<W1P, kW1Batch> Bt) {
+  const int ri = batch_req(Bt, blockIdx.x);
+  const W1P &P = Bt.r[ri];
+  const uint32_t local = blockIdx.x - Bt.start[ri];
   if (*P.status != 0) return;
-  if (blockIdx.x >= P.gelu_blocks) {
-    kept_rope_row(blockIdx.x - P.gelu_blocks, P.stream, P.rope_lo, P.rope_hi, P.out, P.head_n, P.tail_pos0);
+  if (local >= P.gelu_blocks) {
+    kept_rope_row(local - P.gelu_blocks, P.stream, P.rope_lo, P.rope_hi, P.out, P.head_n, P.tail_pos0);
     return;
   }
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (row, 4-unit group)
+  const int64_t i = (int64_t)local * blockDim.x + threadIdx.x;  // (row, 4-unit group)
   if (i >= P.N * (kHid / 4)) return;
   const size_t o = (size_t)i * 4;
   const f32x4 a = *reinterpret_cast<const f32x4 *>(P.part + o);
@@ -1323,6 +1351,7 @@ int build_mean_table(dckv_plan_t *p) {
 static QuantP quant_params(const EncodeArgs &a) {
   QuantP P;
   P.rows = a.rows;
+  P.keys = a.keys;
   P.A = a.p->A;
   P.act = a.p->dev.act;
   P.tok = a.tok;
@@ -1352,7 +1381,10 @@ static QuantP quant_params(const EncodeArgs &a) {
 void launch_analysis_gemm(const EncodeArgs &a) {
   if (a.g.N == 0 || a.p->C_a == 0) return;
   QuantP P = quant_params(a);
-  launch_gemm(k_analysis_quant, "analysis_gemm", P.n_mt * P.n_nt, P, a.s);
+  if (P.keys)
+    launch_gemm(k_analysis_quant<true>, "analysis_gemm", P.n_mt * P.n_nt, P, a.s);
+  else
+    launch_gemm(k_analysis_quant<false>, "analysis_gemm", P.n_mt * P.n_nt, P, a.s);
 }
 
 void launch_encode_fixup(const EncodeArgs &a) {
@@ -1365,58 +1397,82 @@ void launch_encode_fixup(const EncodeArgs &a) {
   hipLaunchKernelGGL(k_encode_fixup, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, a.s, P, n_fix);
 }
 
-void launch_dequant(const DecodeArgs &a) {
-  if (a.g.N == 0) return;
-  DeqP P;
-  P.mtab = a.p->mtab;
-  P.tok = a.tok;
-  P.rank = a.p->dev.rank;
-  P.colpos = a.p->dev.colpos;
-  P.step = a.p->dev.step;
-  P.nbr = a.p->dev.nbr;
-  P.sym32 = reinterpret_cast<const uint32_t *>(a.ws + a.l.sym);
-  P.stream = a.stream;
-  P.ws = a.ws;
-  P.esc_rows = reinterpret_cast<const uint32_t *>(a.ws + a.l.esc_rows);
-  P.yhat_b = reinterpret_cast<uint16_t *>(a.ws + a.l.yhat_b);
-  P.N = a.g.N;
-  P.N256 = a.g.N256;
-  P.Ca = a.p->C_a;
-  P.keep_head = a.p->keep_head;
-  P.vocab = a.p->vocab;
-  P.status = a.status;
-  const dim3 grid((unsigned)((a.g.N + kDeqRows - 1) / kDeqRows), kC / (4 * kDeqThreads));
-  KernelTimer tm("dequant", a.s);
-  if (a.p->C_a == kC)
-    hipLaunchKernelGGL(k_dequant<true>, grid, dim3(kDeqThreads), 0, a.s, P);
-  else
-    hipLaunchKernelGGL(k_dequant<false>, grid, dim3(kDeqThreads), 0, a.s, P);
+void launch_dequant(const DecodeArgs *args, int n) {
+  auto fill = [&](int i) {
+    const DecodeArgs &a = args[i];
+    DeqP P;
+    P.mtab = a.p->mtab;
+    P.tok = a.tok;
+    P.rank = a.p->dev.rank;
+    P.colpos = a.p->dev.colpos;
+    P.step = a.p->dev.step;
+    P.nbr = a.p->dev.nbr;
+    P.sym32 = reinterpret_cast<const uint32_t *>(a.ws + a.l.sym);
+    P.stream = a.stream;
+    P.ws = a.ws;
+    P.esc_rows = reinterpret_cast<const uint32_t *>(a.ws + a.l.esc_rows);
+    P.yhat_b = reinterpret_cast<uint16_t *>(a.ws + a.l.yhat_b);
+    P.N = a.g.N;
+    P.N256 = a.g.N256;
+    P.Ca = a.p->C_a;
+    P.keep_head = a.p->keep_head;
+    P.vocab = a.p->vocab;
+    P.status = a.status;
+    return P;
+  };
+  // requests without dropped components take the dense variant; the others
+  // (in their own launches) read symbols and means through rank and colpos
+  for (int dense = 1; dense >= 0; --dense) {
+    std::vector<int> idx;
+    for (int i = 0; i < n; ++i)
+      if (args[i].g.N > 0 && (args[i].p->C_a == kC) == (dense == 1)) idx.push_back(i);
+    if (idx.empty()) continue;
+    auto f = [&](int k) { return fill(idx[k]); };
+    auto count = [&](int k) {
+      const DecodeArgs &a = args[idx[k]];
+      return (uint32_t)(((a.g.N + kDeqRows - 1) / kDeqRows) * (kC / (4 * kDeqThreads)));
+    };
+    if (dense)
+      launch_batched<DeqP>(k_dequant<true>, "dequant", (int)idx.size(), args[0].s, kDeqThreads, f, count);
+    else
+      launch_batched<DeqP>(k_dequant<false>, "dequant", (int)idx.size(), args[0].s, kDeqThreads, f, count);
+  }
 }
 
-void launch_w1_gemm(const DecodeArgs &a) {
-  if (a.g.N == 0 && a.g.n_kept == 0) return;
-  W1P P;
-  P.yhat_b = reinterpret_cast<const uint16_t *>(a.ws + a.l.yhat_b);
-  P.W1 = a.p->W1;
-  P.part = reinterpret_cast<float *>(a.ws + a.l.w1_part);
-  P.h_b = reinterpret_cast<uint16_t *>(a.ws + a.l.h_b);
-  P.N = a.g.N;
-  P.NM = a.g.NM;
-  P.n_mt = (int)a.g.n_mtiles;
-  P.status = a.status;
-  P.stream = a.stream;
-  P.rope_lo = reinterpret_cast<const float2 *>(a.ws + a.l.rope_lo);
-  P.rope_hi = reinterpret_cast<const float2 *>(a.ws + a.l.rope_hi);
-  P.out = out_rows(a);
-  P.n_kept = a.g.n_kept;
-  P.head_n = std::min<int64_t>(a.p->keep_head, a.g.T);
-  P.tail_pos0 = a.p->keep_head + a.g.N;
-  // the linear codec (no correction) launches the kept rows only
-  P.gelu_blocks = a.p->W1 ? (unsigned)((a.g.N * (kHid / 4) + 255) / 256) : 0u;
-  if (P.gelu_blocks + a.g.n_kept == 0) return;
-  if (a.g.N && a.p->W1) launch_gemm(k_w1, "w1_gemm", P.n_mt * 2, P, a.s);
-  KernelTimer tm("w1_gelu", a.s);
-  hipLaunchKernelGGL(k_w1_gelu, dim3(P.gelu_blocks + (unsigned)a.g.n_kept), dim3(256), 0, a.s, P);
+void launch_w1_gemm(const DecodeArgs *args, int n) {
+  auto fill = [&](int i) {
+    const DecodeArgs &a = args[i];
+    W1P P;
+    P.yhat_b = reinterpret_cast<const uint16_t *>(a.ws + a.l.yhat_b);
+    P.W1 = a.p->W1;
+    P.part = reinterpret_cast<float *>(a.ws + a.l.w1_part);
+    P.h_b = reinterpret_cast<uint16_t *>(a.ws + a.l.h_b);
+    P.N = a.g.N;
+    P.NM = a.g.NM;
+    P.n_mt = (int)a.g.n_mtiles;
+    P.status = a.status;
+    P.stream = a.stream;
+    P.rope_lo = reinterpret_cast<const float2 *>(a.ws + a.l.rope_lo);
+    P.rope_hi = reinterpret_cast<const float2 *>(a.ws + a.l.rope_hi);
+    P.out = out_rows(a);
+    P.n_kept = a.g.n_kept;
+    P.head_n = std::min<int64_t>(a.p->keep_head, a.g.T);
+    P.tail_pos0 = a.p->keep_head + a.g.N;
+    // the linear codec (no correction) launches the kept rows only
+    P.gelu_blocks = a.p->W1 ? (unsigned)((a.g.N * (kHid / 4) + 255) / 256) : 0u;
+    return P;
+  };
+  auto gemm_count = [&](int i) {
+    const DecodeArgs &a = args[i];
+    return (a.g.N && a.p->W1) ? (uint32_t)(a.g.n_mtiles * 2) : 0u;
+  };
+  launch_batched<W1P, kW1Batch>(k_w1, "w1_gemm", n, args[0].s, kThreads, fill, gemm_count, kLdsBytes);
+  auto gelu_count = [&](int i) {
+    const DecodeArgs &a = args[i];
+    const unsigned gb = a.p->W1 ? (unsigned)((a.g.N * (kHid / 4) + 255) / 256) : 0u;
+    return gb + (uint32_t)a.g.n_kept;
+  };
+  launch_batched<W1P, kW1Batch>(k_w1_gelu, "w1_gelu", n, args[0].s, 256, fill, gelu_count);
 }
 
 void launch_synthesis_gemm(const DecodeArgs &a) {

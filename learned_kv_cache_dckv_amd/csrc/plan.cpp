@@ -150,6 +150,78 @@ extern "C" int dckv_plan_tables(const float *base_step, const float *laplace_sca
   return DCKV_OK;
 }
 
+// ---------------------------------------------------------------------------
+// shared embedding-mean tables
+// ---------------------------------------------------------------------------
+namespace {
+struct MtKey {
+  int device;
+  const void *E, *H;
+  int vocab;
+  std::vector<int32_t> perm;
+  bool operator<(const MtKey &o) const {
+    if (device != o.device) return device < o.device;
+    if (E != o.E) return E < o.E;
+    if (H != o.H) return H < o.H;
+    if (vocab != o.vocab) return vocab < o.vocab;
+    return perm < o.perm;
+  }
+};
+struct MtEntry {
+  float *ptr;
+  int users;
+};
+struct MtState {
+  std::mutex mu;
+  std::map<MtKey, MtEntry> tables;
+};
+MtState &mt_state() {
+  static MtState s;
+  return s;
+}
+MtKey mt_key(const dckv_plan_t *pl) { return MtKey{pl->device, pl->E, pl->H, pl->vocab, pl->mt_perm}; }
+
+// Sets pl->mtab: an existing table of the same key (one more user), or a new
+// one built by one GEMM (synchronous).  The lock is held while a table is
+// built, so two plans never build the same table.
+int acquire_mean_table(dckv_plan_t *pl, const std::vector<int32_t> &perm) {
+  pl->mt_perm = perm;
+  MtState &st = mt_state();
+  std::lock_guard<std::mutex> lk(st.mu);
+  const MtKey key = mt_key(pl);
+  auto it = st.tables.find(key);
+  if (it != st.tables.end()) {
+    it->second.users += 1;
+    pl->mtab = it->second.ptr;
+    return DCKV_OK;
+  }
+  void *mtab = nullptr;
+  if (hipMalloc(&mtab, (size_t)pl->vocab * pl->C * 4) != hipSuccess)
+    return set_error(DCKV_ENOMEM, "plan: hipMalloc of the embedding-mean table failed");
+  pl->mtab = static_cast<float *>(mtab);
+  const int rc = build_mean_table(pl);
+  if (rc) {
+    (void)hipFree(mtab);
+    pl->mtab = nullptr;
+    return rc;
+  }
+  st.tables.emplace(key, MtEntry{pl->mtab, 1});
+  return DCKV_OK;
+}
+
+// One user fewer; the last one frees the table (the plan's device is current).
+int release_mean_table(dckv_plan_t *pl) {
+  MtState &st = mt_state();
+  std::lock_guard<std::mutex> lk(st.mu);
+  auto it = st.tables.find(mt_key(pl));
+  if (it == st.tables.end()) return set_error(DCKV_EINVAL, "plan_free: mean table not registered");
+  if (--it->second.users > 0) return DCKV_OK;
+  const int rc = check_hip(hipFree(it->second.ptr), "plan_free");
+  st.tables.erase(it);
+  return rc;
+}
+}  // namespace
+
 extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **out) {
   if (!p || !out) return set_error(DCKV_EINVAL, "plan: null argument");
   *out = nullptr;
@@ -319,17 +391,11 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
   pl->dev.rcp = reinterpret_cast<float *>(b + o_rcp);
   pl->dev.bucket = reinterpret_cast<uint16_t *>(b + o_bucket);
   pl->dev.omega = reinterpret_cast<double *>(b + o_omega);
-  // the embedding-mean table: H E[v] for every token id, once per plan
-  void *mtab = nullptr;
-  if (hipMalloc(&mtab, (size_t)pl->vocab * C * 4) != hipSuccess) {
-    (void)hipFree(blk);
-    delete pl;
-    return set_error(DCKV_ENOMEM, "plan: hipMalloc of the embedding-mean table failed");
-  }
-  pl->mtab = static_cast<float *>(mtab);
-  rc = build_mean_table(pl);
+  pl->dev_bytes = off;
+  // the embedding-mean table: H E[v] for every token id, shared by the plans
+  // that have the same device, embedding, mean head and column order
+  rc = acquire_mean_table(pl, perm);
   if (rc) {
-    (void)hipFree(mtab);
     (void)hipFree(blk);
     delete pl;
     return rc;
@@ -347,13 +413,26 @@ extern "C" int dckv_plan_free(dckv_plan_t *plan) {
     (void)hipSetDevice(plan->device);
     rc = check_hip(hipFree(plan->dev_block), "plan_free");
     if (plan->mtab) {
-      const int rc2 = check_hip(hipFree(plan->mtab), "plan_free");
+      const int rc2 = release_mean_table(plan);
       if (rc == DCKV_OK) rc = rc2;
     }
     (void)hipSetDevice(cur);
   }
   delete plan;
   return rc;
+}
+
+extern "C" int dckv_plan_memory(const dckv_plan_t *plan, uint64_t *table_bytes, uint64_t *mean_table_bytes,
+                                int32_t *mean_table_users) {
+  if (!plan) return set_error(DCKV_EINVAL, "plan_memory: null plan");
+  if (table_bytes) *table_bytes = plan->dev_bytes;
+  if (mean_table_bytes) *mean_table_bytes = (uint64_t)plan->vocab * plan->C * 4;
+  if (mean_table_users) {
+    std::lock_guard<std::mutex> lk(mt_state().mu);
+    auto it = mt_state().tables.find(mt_key(plan));
+    *mean_table_users = it == mt_state().tables.end() ? 0 : it->second.users;
+  }
+  return DCKV_OK;
 }
 
 extern "C" int dckv_plan_info(const dckv_plan_t *plan, float *step_out, uint8_t *active_out,

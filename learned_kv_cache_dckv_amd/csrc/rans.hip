@@ -25,7 +25,6 @@
 namespace dckv {
 namespace {
 
-constexpr int kTabStride = 257;   // u32 per table row in LDS: spreads equal symbols over banks
 constexpr int kEncWaves = 16;     // groups (waves) per encoder workgroup, one component group
 constexpr int kDecWaves = 16;
 constexpr int kWordBuf = 1024;    // u16 words cached per decoder wave
@@ -40,9 +39,15 @@ __device__ __forceinline__ T gload(const T *p) {
   return *(const T __attribute__((address_space(1))) *)p;
 }
 
-// The tables of component group g into LDS: n rows of 256 u32 (LDS row stride
-// kTabStride), contiguous in the plan.  Every thread issues its 16-byte loads
-// before its first LDS write, so the copy costs one memory latency.
+// A 64 x 256 block of 32-bit table entries (components 64 g .. 64 g + 63 of a
+// plan table [C_a][256]) into LDS transposed, entry (e, lane) at e * 64 +
+// lane: a wave that reads one entry per lane, each lane its own component at
+// its own index, then touches bank lane % 32 from every lane (two lanes per
+// bank, the minimum), whatever the indices.  Columns past the group's n
+// components are zero.  Piece pc (16 bytes) is entries 4 (pc / 64) .. + 3 of
+// component pc % 64, so the 64 lanes of a wave write one LDS row each time,
+// on consecutive banks.  Every thread issues its loads before its first LDS
+// write, so the copy costs one memory latency.
 template <int kThreads>
 __device__ __forceinline__ void stage_tab(uint32_t *tab, const uint32_t *gtab, int g, int n) {
   constexpr int kPer = kLanes * 256 / 4 / kThreads;  // 16-byte pieces per thread
@@ -51,19 +56,18 @@ __device__ __forceinline__ void stage_tab(uint32_t *tab, const uint32_t *gtab, i
   u32x4 v[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int pc = threadIdx.x + i * kThreads;  // row pc / 64, entries 4 (pc % 64) ..
-    if ((pc >> 6) < n) v[i] = gload(src + pc);
+    const int pc = threadIdx.x + i * kThreads;
+    const int c = pc & 63, q = pc >> 6;
+    v[i] = c < n ? gload(src + c * 64 + q) : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int pc = threadIdx.x + i * kThreads;
-    if ((pc >> 6) < n) {
-      uint32_t *d = tab + (pc >> 6) * kTabStride + (pc & 63) * 4;
-      d[0] = v[i].x;
-      d[1] = v[i].y;
-      d[2] = v[i].z;
-      d[3] = v[i].w;
-    }
+    uint32_t *d = tab + (pc >> 6) * 4 * kLanes + (pc & 63);
+    d[0] = v[i].x;
+    d[kLanes] = v[i].y;
+    d[2 * kLanes] = v[i].z;
+    d[3 * kLanes] = v[i].w;
   }
 }
 
@@ -80,17 +84,24 @@ struct EncP {
   const int32_t *status;
 };
 
-__global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(EncP P) {
-  __shared__ uint32_t tab[kLanes * kTabStride];
-  __shared__ uint32_t rcpt[kLanes * kTabStride];  // fp32 bits of the scaled reciprocal of each f
-  const int g = blockIdx.y;
+// Workgroup w of a request codes component group g = w / nch of the blocks
+// 16 (w % nch) .. + 15 (one wave each), nch = ceil(n_blk / 16).
+__global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(const Batch<EncP> B) {
+  __shared__ uint32_t tab[256 * kLanes];   // [symbol][lane]: f | cum << 16
+  __shared__ uint32_t rcpt[256 * kLanes];  // [symbol][lane]: fp32 bits of the scaled reciprocal of f
+  const int ri = batch_req(B, blockIdx.x);
+  const EncP &P = B.r[ri];
+  const uint32_t nch_w = (uint32_t)((P.n_blk + kEncWaves - 1) / kEncWaves);
+  const uint32_t local = blockIdx.x - B.start[ri];
+  const int g = (int)(local / nch_w);
+  const int chunk = (int)(local - (uint32_t)g * nch_w);
   const int n = min(kLanes, P.Ca - kLanes * g);
   stage_tab<kEncWaves * 64>(tab, P.tab, g, n);
   stage_tab<kEncWaves * 64>(rcpt, reinterpret_cast<const uint32_t *>(P.rcp), g, n);
   __syncthreads();
   if (*P.status != 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t b = (int64_t)blockIdx.x * kEncWaves + wave;
+  const int64_t b = (int64_t)chunk * kEncWaves + wave;
   if (b >= P.n_blk) return;
   const int Lb = (int)min<int64_t>(kBlock, P.N - kBlock * b);
   const int64_t gid = b * P.G + g;
@@ -100,8 +111,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(EncP P) {
   // Escapes code as the identity: table entry 255 is f = 2^15, cum = 0, so
   // the state never emits and x / f * 2^15 + x % f = x.  Lanes past C_a code
   // escapes only, through lane 0's table row.
-  const uint32_t *mytab = tab + (lane_ok ? lane : 0) * kTabStride;
-  const float *myrcp = reinterpret_cast<const float *>(rcpt) + (lane_ok ? lane : 0) * kTabStride;
+  const uint32_t *mytab = tab + (lane_ok ? lane : 0);
+  const float *myrcp = reinterpret_cast<const float *>(rcpt) + (lane_ok ? lane : 0);
   uint32_t x = kL;
   uint32_t cnt = 0;
   // One coding step of symbol entry (e, rf) = (f | cum << 16, scaled 1/f).
@@ -139,7 +150,28 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(EncP P) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) w[u] = gload(sw + (size_t)(ch * 8 + u) * 64);
   };
+  // the four table entries of a quad's symbols; a quad's entries are read
+  // while the quad before it in coding order is coded, so a step never
+  // waits on LDS
+  uint32_t ec[4], en[4];
+  float rc[4], rn[4];
+  auto fetch = [&](uint32_t w, uint32_t (&e)[4], float (&rf)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t sy = (w >> (8 * k)) & 0xFFu;
+      e[k] = mytab[sy * kLanes];
+      rf[k] = myrcp[sy * kLanes];
+    }
+  };
   load_chunk(nch - 1, wn);
+  {
+    // the first quad coded: quad nq - 1, in the last chunk
+    uint32_t w0 = 0xFFFFFFFFu;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u == ((nq - 1) & 7)) w0 = lane_ok ? wn[u] : 0xFFFFFFFFu;
+    fetch(w0 | tail, ec, rc);
+  }
 #pragma unroll 1
   for (int ch = nch - 1; ch >= 0; --ch) {
 #pragma unroll
@@ -149,18 +181,19 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(EncP P) {
     for (int u = 7; u >= 0; --u) {
       const int qd = ch * 8 + u;
       if (qd >= nq) continue;
-      const uint32_t w = wq[u] | (qd == nq - 1 ? tail : 0u);
-      // the quad's four table entries are read before its first step
-      uint32_t e[4];
-      float rf[4];
+      // the next quad in coding order: u - 1 of this chunk, or quad 7 of
+      // the next chunk
+      if (u > 0)
+        fetch(wq[u - 1], en, rn);
+      else if (ch > 0)
+        fetch(lane_ok ? wn[7] : 0xFFFFFFFFu, en, rn);
 #pragma unroll
-      for (int k = 3; k >= 0; --k) {
-        const uint32_t s = (w >> (8 * k)) & 0xFFu;
-        e[k] = mytab[s];
-        rf[k] = myrcp[s];
+      for (int k = 3; k >= 0; --k) enc(ec[k], rc[k]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        ec[k] = en[k];
+        rc[k] = rn[k];
       }
-#pragma unroll
-      for (int k = 3; k >= 0; --k) enc(e[k], rf[k]);
     }
   }
   if (lane_ok) {
@@ -249,7 +282,9 @@ struct ScanP {
   float step_scale;
 };
 
-__global__ __launch_bounds__(1024) void k_scan_header(ScanP P) {
+// One workgroup per request.
+__global__ __launch_bounds__(1024) void k_scan_header(const Batch<ScanP> B) {
+  const ScanP &P = B.r[batch_req(B, blockIdx.x)];
   __shared__ uint64_t part[1024];
   __shared__ unsigned long long keys[kSortLds];
   const int t = threadIdx.x;
@@ -341,19 +376,23 @@ struct PackP {
   const int32_t *status;
 };
 
-__global__ __launch_bounds__(256) void k_pack(PackP P) {
+// A request's cnt workgroups take its groups (and escape records) in strides.
+__global__ __launch_bounds__(256) void k_pack(const Batch<PackP> B) {
+  const int ri = batch_req(B, blockIdx.x);
+  const PackP &P = B.r[ri];
+  const uint32_t local = blockIdx.x - B.start[ri], cnt = B.start[ri + 1] - B.start[ri];
   if (*P.status != 0) return;
   const Ctrl *ct = reinterpret_cast<const Ctrl *>(P.ws);
   const uint64_t rans_off = ct->rans_off, esc_off = ct->esc_off;
   const uint32_t n_esc = ct->n_esc;
-  for (int64_t gid = blockIdx.x; gid < P.n_groups; gid += gridDim.x) {
+  for (int64_t gid = local; gid < P.n_groups; gid += cnt) {
     const uint32_t W = P.gwords[gid];
     const uint16_t *src = P.scratch + (size_t)gid * (kLanes * (kBlock + 2));
     uint16_t *dst = reinterpret_cast<uint16_t *>(P.stream + rans_off) + P.goffs[gid];
     for (uint32_t k = threadIdx.x; k < W; k += blockDim.x) dst[k] = src[W - 1 - k];
   }
   uint32_t *e = reinterpret_cast<uint32_t *>(P.stream + esc_off);
-  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n_esc; i += gridDim.x * blockDim.x) {
+  for (uint32_t i = local * blockDim.x + threadIdx.x; i < n_esc; i += cnt * blockDim.x) {
     e[2 * i] = P.esc_sorted[2 * i];
     e[2 * i + 1] = P.esc_sorted[2 * i + 1];
   }
@@ -379,15 +418,20 @@ struct ParseP {
   uint32_t n_row_tiles;
 };
 
-__global__ __launch_bounds__(256) void k_parse(ParseP P) {
+// Workgroup 0 of a request checks its stream; the others (if any) build its
+// RoPE tables.
+__global__ __launch_bounds__(256) void k_parse(const Batch<ParseP> B) {
+  const int ri = batch_req(B, blockIdx.x);
+  const ParseP &P = B.r[ri];
+  const uint32_t local = blockIdx.x - B.start[ri], cnt = B.start[ri + 1] - B.start[ri];
   __shared__ int bad;
   __shared__ int plan_bad;
   __shared__ uint64_t s_esc_off, s_rans_off, s_rans_bytes;
   __shared__ uint32_t s_n_esc;
   const int t = threadIdx.x;
-  if (blockIdx.x > 0) {
+  if (local > 0) {
     const int64_t n = (256 + P.rope_hi_n) * kHalf;
-    for (int64_t i = (int64_t)(blockIdx.x - 1) * blockDim.x + t; i < n; i += (int64_t)(gridDim.x - 1) * blockDim.x) {
+    for (int64_t i = (int64_t)(local - 1) * blockDim.x + t; i < n; i += (int64_t)(cnt - 1) * blockDim.x) {
       const int64_t u = i / kHalf;
       const int k = (int)(i - u * kHalf);
       double ang;
@@ -528,24 +572,24 @@ __device__ __forceinline__ void decode_rows(uint32_t &x, uint32_t &ptr, uint32_t
     if (!kPlain) act = lane_ok && !((emask >> lane) & 1ull);
     const uint32_t slot = x & (kM - 1u);
     const uint32_t bi = slot >> kBucketShift;
-    const uint32_t be = mybkt[bi];
+    const uint32_t be = mybkt[bi * kLanes];
     const uint32_t split = be >> 8;
     uint32_t s = (be & 0xFFu) + ((slot & ((1u << kBucketShift) - 1u)) >= split ? 1u : 0u);
     const bool srch = act && split == kSplitSearch;
     if (__ballot(srch)) {
       // candidates lo .. the first symbol of the next bucket
       uint32_t lo = s, hi = s;
-      if (srch) hi = bi + 1 < (uint32_t)kBuckets ? (uint32_t)(mybkt[bi + 1] & 0xFFu) : (uint32_t)(kNSym - 1);
+      if (srch) hi = bi + 1 < (uint32_t)kBuckets ? (uint32_t)(mybkt[(bi + 1) * kLanes] & 0xFFu) : (uint32_t)(kNSym - 1);
       while (__ballot(lo < hi)) {
         const uint32_t mid = (lo + hi + 1) >> 1;
-        const bool up = (mytab[mid] >> 16) <= slot;
+        const bool up = (mytab[mid * kLanes] >> 16) <= slot;
         const bool open = lo < hi;
         lo = open && up ? mid : lo;
         hi = open && !up ? mid - 1 : hi;
       }
       s = lo;
     }
-    const uint32_t e = mytab[s];
+    const uint32_t e = mytab[s * kLanes];
     // f * (x >> 15) < 2^32: f <= 2^15 and x >> 15 < 2^17 (24-bit multiply)
     const uint32_t xd = __umul24(e & 0xFFFFu, x >> kPrecBits) + slot - (e >> 16);
     x = act ? xd : x;
@@ -590,27 +634,43 @@ __device__ __forceinline__ void decode_rows(uint32_t &x, uint32_t &ptr, uint32_t
   }
 }
 
-__global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
-  __shared__ uint32_t tab[kLanes * kTabStride];
-  __shared__ uint16_t bkt[kLanes * kBuckets];
+// Workgroup w of a request decodes component group g = w / nch of the blocks
+// 16 (w % nch) .. + 15 (one wave each), nch = ceil(n_blk / 16).
+__global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(const Batch<DecP> B) {
+  const int ri = batch_req(B, blockIdx.x);
+  const DecP &P = B.r[ri];
+  const uint32_t nch_w = (uint32_t)((P.n_blk + kDecWaves - 1) / kDecWaves);
+  const uint32_t local = blockIdx.x - B.start[ri];
+  const int g = (int)(local / nch_w);
+  const int chunk = (int)(local - (uint32_t)g * nch_w);
+  __shared__ uint32_t tab[256 * kLanes];        // [symbol][lane]: f | cum << 16
+  __shared__ uint16_t bkt[kBuckets * kLanes];    // [bucket][lane]: lo | split << 8
   __shared__ __attribute__((aligned(16))) uint16_t wbuf[kDecWaves][kWordBuf];
-  const int g = blockIdx.y;
   const int n = min(kLanes, P.Ca - kLanes * g);
   stage_tab<kDecWaves * 64>(tab, P.tab, g, n);
   {
-    // bucket rows: 512 bytes per lane, two 16-byte pieces per thread
+    // bucket rows (512 bytes per component, two 16-byte pieces per thread),
+    // transposed like the tables; columns past n are zero
     static_assert(kDecWaves * 64 * 2 * 16 == kLanes * kBuckets * 2, "two pieces per thread");
     const u32x4 *src = reinterpret_cast<const u32x4 *>(P.bucket + (size_t)kLanes * g * kBuckets);
     u32x4 v[2];
+    // piece pc: buckets 8 (pc / 64) .. + 7 of component pc % 64
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int pc = threadIdx.x + i * kDecWaves * 64;  // row pc / 32
-      if ((pc >> 5) < n) v[i] = gload(src + pc);
+      const int pc = threadIdx.x + i * kDecWaves * 64;
+      const int c = pc & 63, q = pc >> 6;
+      v[i] = c < n ? gload(src + c * 32 + q) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int pc = threadIdx.x + i * kDecWaves * 64;
-      if ((pc >> 5) < n) reinterpret_cast<u32x4 *>(bkt)[pc] = v[i];
+      uint16_t *d = bkt + (pc >> 6) * 8 * kLanes + (pc & 63);
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        d[(2 * j) * kLanes] = (uint16_t)(w[j] & 0xFFFFu);
+        d[(2 * j + 1) * kLanes] = (uint16_t)(w[j] >> 16);
+      }
     }
   }
   __syncthreads();
@@ -619,7 +679,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
   // and lanes that decode nothing at a step take the same path with their
   // results discarded
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int64_t b = (int64_t)blockIdx.x * kDecWaves + wave;
+  const int64_t b = (int64_t)chunk * kDecWaves + wave;
   if (b >= P.n_blk) return;
   const Ctrl *ct = reinterpret_cast<const Ctrl *>(P.ws);
   const int Lb = (int)min<int64_t>(kBlock, P.N - kBlock * b);
@@ -683,8 +743,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(DecP P) {
   uint32_t x = kL;
   if (lane_ok) x = (uint32_t)wb[2 * lane] | ((uint32_t)wb[2 * lane + 1] << 16);
   uint32_t ptr = 2u * (uint32_t)n;
-  const uint32_t *mytab = tab + lane * kTabStride;
-  const uint16_t *mybkt = bkt + lane * kBuckets;
+  const uint32_t *mytab = tab + lane;
+  const uint16_t *mybkt = bkt + lane;
   uint32_t *sout = P.sym32 + ((size_t)g * (P.N256 / 4) + (size_t)b * 64) * 64 + lane;
   if (!has_esc && n == kLanes)
     decode_rows<true>(x, ptr, base, W, Lb, lane, true, false, esc, mytab, mybkt, wb, wsrc, sout);
@@ -748,111 +808,134 @@ unsigned grid_for(int64_t work, int per_block = 256, unsigned cap = 8192) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-void launch_rans_encode(const EncodeArgs &a) {
-  if (a.g.n_groups == 0) return;
-  EncP P;
-  P.tab = a.p->dev.tab;
-  P.rcp = a.p->dev.rcp;
-  P.sym32 = reinterpret_cast<const uint32_t *>(a.ws + a.l.sym);
-  P.scratch = reinterpret_cast<uint16_t *>(a.ws + a.l.scratch);
-  P.gwords = reinterpret_cast<uint32_t *>(a.ws + a.l.gwords);
-  P.N = a.g.N;
-  P.N256 = a.g.N256;
-  P.n_blk = a.g.n_blk;
-  P.Ca = a.p->C_a;
-  P.G = a.p->G;
-  P.status = a.status;
-  dim3 grid((unsigned)((a.g.n_blk + kEncWaves - 1) / kEncWaves), (unsigned)a.p->G);
-  KernelTimer tm("rans_encode", a.s);
-  hipLaunchKernelGGL(k_rans_encode, grid, dim3(kEncWaves * 64), 0, a.s, P);
+void launch_rans_encode(const EncodeArgs *args, int n) {
+  auto fill = [&](int i) {
+    const EncodeArgs &a = args[i];
+    EncP P;
+    P.tab = a.p->dev.tab;
+    P.rcp = a.p->dev.rcp;
+    P.sym32 = reinterpret_cast<const uint32_t *>(a.ws + a.l.sym);
+    P.scratch = reinterpret_cast<uint16_t *>(a.ws + a.l.scratch);
+    P.gwords = reinterpret_cast<uint32_t *>(a.ws + a.l.gwords);
+    P.N = a.g.N;
+    P.N256 = a.g.N256;
+    P.n_blk = a.g.n_blk;
+    P.Ca = a.p->C_a;
+    P.G = a.p->G;
+    P.status = a.status;
+    return P;
+  };
+  auto count = [&](int i) {
+    const EncodeArgs &a = args[i];
+    return a.g.n_groups == 0 ? 0u : (uint32_t)(((a.g.n_blk + kEncWaves - 1) / kEncWaves) * a.p->G);
+  };
+  launch_batched<EncP>(k_rans_encode, "rans_encode", n, args[0].s, kEncWaves * 64, fill, count);
 }
 
-void launch_scan_header(const EncodeArgs &a) {
-  ScanP P;
-  P.esc_raw = reinterpret_cast<uint32_t *>(a.ws + a.l.esc_raw);
-  P.esc_sorted = reinterpret_cast<uint32_t *>(a.ws + a.l.esc_sorted);
-  P.gwords = reinterpret_cast<const uint32_t *>(a.ws + a.l.gwords);
-  P.goffs = reinterpret_cast<uint64_t *>(a.ws + a.l.goffs);
-  P.ws = a.ws;
-  P.stream = a.stream;
-  P.capacity = a.capacity;
-  P.stream_bytes = a.stream_bytes;
-  P.status = a.status;
-  P.n_groups = a.g.n_groups;
-  P.esc_cap = a.g.esc_cap;
-  P.kept_bytes = (uint64_t)a.g.n_kept * a.p->D * 2;
-  P.T = (uint32_t)a.g.T;
-  P.keep_head = (uint32_t)a.p->keep_head;
-  P.keep_tail = (uint32_t)a.p->keep_tail;
-  P.N = (uint32_t)a.g.N;
-  P.n_coef = (uint32_t)a.p->C;
-  P.Ca = (uint32_t)a.p->C_a;
-  P.crc = a.p->crc;
-  P.step_scale = a.p->step_scale;
-  KernelTimer tm("scan", a.s);
-  hipLaunchKernelGGL(k_scan_header, dim3(1), dim3(1024), 0, a.s, P);
+void launch_scan_header(const EncodeArgs *args, int n) {
+  auto fill = [&](int i) {
+    const EncodeArgs &a = args[i];
+    ScanP P;
+    P.esc_raw = reinterpret_cast<uint32_t *>(a.ws + a.l.esc_raw);
+    P.esc_sorted = reinterpret_cast<uint32_t *>(a.ws + a.l.esc_sorted);
+    P.gwords = reinterpret_cast<const uint32_t *>(a.ws + a.l.gwords);
+    P.goffs = reinterpret_cast<uint64_t *>(a.ws + a.l.goffs);
+    P.ws = a.ws;
+    P.stream = a.stream;
+    P.capacity = a.capacity;
+    P.stream_bytes = a.stream_bytes;
+    P.status = a.status;
+    P.n_groups = a.g.n_groups;
+    P.esc_cap = a.g.esc_cap;
+    P.kept_bytes = (uint64_t)a.g.n_kept * a.p->D * 2;
+    P.T = (uint32_t)a.g.T;
+    P.keep_head = (uint32_t)a.p->keep_head;
+    P.keep_tail = (uint32_t)a.p->keep_tail;
+    P.N = (uint32_t)a.g.N;
+    P.n_coef = (uint32_t)a.p->C;
+    P.Ca = (uint32_t)a.p->C_a;
+    P.crc = a.p->crc;
+    P.step_scale = a.p->step_scale;
+    return P;
+  };
+  launch_batched<ScanP>(k_scan_header, "scan", n, args[0].s, 1024, fill, [](int) { return 1u; });
 }
 
-void launch_pack(const EncodeArgs &a) {
-  PackP P;
-  P.scratch = reinterpret_cast<const uint16_t *>(a.ws + a.l.scratch);
-  P.gwords = reinterpret_cast<const uint32_t *>(a.ws + a.l.gwords);
-  P.goffs = reinterpret_cast<const uint64_t *>(a.ws + a.l.goffs);
-  P.esc_sorted = reinterpret_cast<const uint32_t *>(a.ws + a.l.esc_sorted);
-  P.ws = a.ws;
-  P.stream = a.stream;
-  P.n_groups = a.g.n_groups;
-  P.status = a.status;
-  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(a.g.n_groups, 65535));
-  KernelTimer tm("pack", a.s);
-  hipLaunchKernelGGL(k_pack, dim3(grid), dim3(256), 0, a.s, P);
+void launch_pack(const EncodeArgs *args, int n) {
+  auto fill = [&](int i) {
+    const EncodeArgs &a = args[i];
+    PackP P;
+    P.scratch = reinterpret_cast<const uint16_t *>(a.ws + a.l.scratch);
+    P.gwords = reinterpret_cast<const uint32_t *>(a.ws + a.l.gwords);
+    P.goffs = reinterpret_cast<const uint64_t *>(a.ws + a.l.goffs);
+    P.esc_sorted = reinterpret_cast<const uint32_t *>(a.ws + a.l.esc_sorted);
+    P.ws = a.ws;
+    P.stream = a.stream;
+    P.n_groups = a.g.n_groups;
+    P.status = a.status;
+    return P;
+  };
+  // one workgroup per group, at most 4,096 per request (at least one, for the
+  // escape records)
+  auto count = [&](int i) { return (uint32_t)std::max<int64_t>(1, std::min<int64_t>(args[i].g.n_groups, 4096)); };
+  launch_batched<PackP>(k_pack, "pack", n, args[0].s, 256, fill, count);
 }
 
-void launch_parse(const DecodeArgs &a, bool with_rope) {
-  ParseP P;
-  P.stream = a.stream;
-  P.size = a.stream_size;
-  P.ws = a.ws;
-  P.status = a.status;
-  P.T = (uint32_t)a.g.T;
-  P.keep_head = (uint32_t)a.p->keep_head;
-  P.keep_tail = (uint32_t)a.p->keep_tail;
-  P.N = (uint32_t)a.g.N;
-  P.n_coef = (uint32_t)a.p->C;
-  P.Ca = (uint32_t)a.p->C_a;
-  P.crc = a.p->crc;
-  P.n_groups = (uint32_t)a.g.n_groups;
-  P.kept_bytes = (uint64_t)a.g.n_kept * a.p->D * 2;
-  P.esc_rows = reinterpret_cast<uint32_t *>(a.ws + a.l.esc_rows);
-  P.n_row_tiles = (uint32_t)a.g.n_mtiles;
-  P.omega = a.p->dev.omega;
-  P.rope_lo = reinterpret_cast<float2 *>(a.ws + a.l.rope_lo);
-  P.rope_hi = reinterpret_cast<float2 *>(a.ws + a.l.rope_hi);
-  P.rope_hi_n = a.g.rope_hi;
-  const int64_t n_rope = with_rope ? (256 + a.g.rope_hi) * kHalf : 0;
-  const unsigned rope_blocks = (unsigned)std::min<int64_t>((n_rope + 255) / 256, 4096);
-  KernelTimer tm("parse", a.s);
-  hipLaunchKernelGGL(k_parse, dim3(1 + rope_blocks), dim3(256), 0, a.s, P);
+void launch_parse(const DecodeArgs *args, int n, bool with_rope) {
+  auto rope_blocks = [&](int i) {
+    const int64_t n_rope = with_rope ? (256 + args[i].g.rope_hi) * kHalf : 0;
+    return (uint32_t)std::min<int64_t>((n_rope + 255) / 256, 4096);
+  };
+  auto fill = [&](int i) {
+    const DecodeArgs &a = args[i];
+    ParseP P;
+    P.stream = a.stream;
+    P.size = a.stream_size;
+    P.ws = a.ws;
+    P.status = a.status;
+    P.T = (uint32_t)a.g.T;
+    P.keep_head = (uint32_t)a.p->keep_head;
+    P.keep_tail = (uint32_t)a.p->keep_tail;
+    P.N = (uint32_t)a.g.N;
+    P.n_coef = (uint32_t)a.p->C;
+    P.Ca = (uint32_t)a.p->C_a;
+    P.crc = a.p->crc;
+    P.n_groups = (uint32_t)a.g.n_groups;
+    P.kept_bytes = (uint64_t)a.g.n_kept * a.p->D * 2;
+    P.esc_rows = reinterpret_cast<uint32_t *>(a.ws + a.l.esc_rows);
+    P.n_row_tiles = (uint32_t)a.g.n_mtiles;
+    P.omega = a.p->dev.omega;
+    P.rope_lo = reinterpret_cast<float2 *>(a.ws + a.l.rope_lo);
+    P.rope_hi = reinterpret_cast<float2 *>(a.ws + a.l.rope_hi);
+    P.rope_hi_n = a.g.rope_hi;
+    return P;
+  };
+  launch_batched<ParseP>(k_parse, "parse", n, args[0].s, 256, fill, [&](int i) { return 1u + rope_blocks(i); });
 }
 
-void launch_rans_decode(const DecodeArgs &a) {
-  if (a.g.n_groups == 0) return;
-  DecP P;
-  P.tab = a.p->dev.tab;
-  P.bucket = a.p->dev.bucket;
-  P.stream = a.stream;
-  P.ws = a.ws;
-  P.esc_rows = reinterpret_cast<const uint32_t *>(a.ws + a.l.esc_rows);
-  P.sym32 = reinterpret_cast<uint32_t *>(a.ws + a.l.sym);
-  P.N = a.g.N;
-  P.N256 = a.g.N256;
-  P.n_blk = a.g.n_blk;
-  P.Ca = a.p->C_a;
-  P.G = a.p->G;
-  P.status = a.status;
-  dim3 grid((unsigned)((a.g.n_blk + kDecWaves - 1) / kDecWaves), (unsigned)a.p->G);
-  KernelTimer tm("rans_decode", a.s);
-  hipLaunchKernelGGL(k_rans_decode, grid, dim3(kDecWaves * 64), 0, a.s, P);
+void launch_rans_decode(const DecodeArgs *args, int n) {
+  auto fill = [&](int i) {
+    const DecodeArgs &a = args[i];
+    DecP P;
+    P.tab = a.p->dev.tab;
+    P.bucket = a.p->dev.bucket;
+    P.stream = a.stream;
+    P.ws = a.ws;
+    P.esc_rows = reinterpret_cast<const uint32_t *>(a.ws + a.l.esc_rows);
+    P.sym32 = reinterpret_cast<uint32_t *>(a.ws + a.l.sym);
+    P.N = a.g.N;
+    P.N256 = a.g.N256;
+    P.n_blk = a.g.n_blk;
+    P.Ca = a.p->C_a;
+    P.G = a.p->G;
+    P.status = a.status;
+    return P;
+  };
+  auto count = [&](int i) {
+    const DecodeArgs &a = args[i];
+    return a.g.n_groups == 0 ? 0u : (uint32_t)(((a.g.n_blk + kDecWaves - 1) / kDecWaves) * a.p->G);
+  };
+  launch_batched<DecP>(k_rans_decode, "rans_decode", n, args[0].s, kDecWaves * 64, fill, count);
 }
 
 void launch_sym_to_tiled(const EncodeArgs &a, const uint8_t *sym) {
