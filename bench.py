@@ -409,7 +409,10 @@ def _oracle_plan(w, g):
 
 def unrope_bench(cfg: int, steps: int) -> int:
     """The inverse RoPE over the workload's rows (a post-RoPE cache back to
-    pre-RoPE rows): HBM-bound, 2 x T x 12,288 bytes per call."""
+    pre-RoPE rows): HBM-bound, 2 x T x 12,288 bytes per call.  Then the encode
+    of a post-RoPE cache (the decode of the workload, which carries RoPE) three
+    ways: dckv_encode of pre-RoPE rows, dckv_unrope + dckv_encode, and
+    dckv_encode_postrope."""
     import torch
     import dckv_synth as synth
     import learned_kv_cache_dckv_amd as dk
@@ -418,21 +421,49 @@ def unrope_bench(cfg: int, steps: int) -> int:
     codec = dk.Codec(synth.world().params(), device=dev)
     plan = codec.plan(req.step_scale)
     src = torch.from_numpy(req.rows.view(np.int16)).to(dev)
+    tok = torch.from_numpy(req.token_ids.astype(np.int32)).to(dev)
     dst = torch.empty_like(src)
     dk.dckv_unrope(plan, src, dst)
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(s)
-    for _ in range(steps):
-        dk.dckv_unrope(plan, src, dst)
-    b.record(s)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        for _ in range(steps):
+            fn()
+        b.record(s)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    ms = timed(lambda: dk.dckv_unrope(plan, src, dst))
     nbytes = 2.0 * req.T * KV_BYTES_PER_TOKEN
     gbps = nbytes / (ms * 1e-3) / 1e9
+    # a post-RoPE cache: the decode of the workload's stream
+    max_bytes, ws_bytes = plan.bytes(req.T)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    buf = torch.empty(max_bytes, dtype=torch.uint8, device=dev)
+    nb = torch.zeros(1, dtype=torch.int64, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    post = torch.empty_like(src)
+    dk.dckv_encode(plan, src, tok, buf, nb, st, ws)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    dk.dckv_decode(plan, buf, int(nb.item()), tok, post, st, ws)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    ws_post = torch.empty(dk.dckv_bytes_postrope(plan, req.T), dtype=torch.uint8, device=dev)
+    enc_ms = timed(lambda: dk.dckv_encode(plan, src, tok, buf, nb, st, ws))
+    two_ms = timed(lambda: (dk.dckv_unrope(plan, post, dst), dk.dckv_encode(plan, dst, tok, buf, nb, st, ws)))
+    post_ms = timed(lambda: dk.dckv_encode_postrope(plan, post, tok, buf, nb, st, ws_post))
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
     print(json.dumps({"metric": "inverse RoPE of a post-RoPE cache (GB/s)", "workload": req.note, "T": req.T,
-                      "ms": ms, "GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS}))
+                      "ms": ms, "GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS,
+                      "encode_ms": enc_ms, "unrope_then_encode_ms": two_ms, "encode_postrope_ms": post_ms,
+                      "postrope_over_encode": post_ms / enc_ms}))
     return 0
 
 

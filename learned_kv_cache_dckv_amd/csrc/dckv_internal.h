@@ -265,7 +265,7 @@ void launch_gemm_f32(const GemmF32Args &args, hipStream_t s);
 void launch_gemm_f32_pair(const GemmF32Args &a, const GemmF32Args &b, hipStream_t s);
 
 // fit.hip: the closed-form fit of the conditional models
-constexpr int kFitChunks = 64;  // row chunks of the per-component sums
+constexpr int kFitChunks = 512;  // row chunks of the per-component sums
 struct FitLayout {
   int64_t n_pad = 0;  // n rounded up to 64 (the inner dimension of the Gram products)
   uint64_t Y = 0, M = 0, Yhi = 0, Ylo = 0, Et = 0, G = 0, R = 0, Hb = 0, tokc = 0, part = 0, dg = 0, linv = 0, total = 0;

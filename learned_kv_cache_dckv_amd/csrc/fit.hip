@@ -110,134 +110,259 @@ __global__ void k_fit_add_diag(float *G, float v, float *dg) {
   }
 }
 
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Unblocked Cholesky of diagonal block k (lower, in place; the block's upper
 // triangle is zeroed, so later kernels read it as L_kk), then its inverse
-// Linv (lower) into linv.  One wave: lane r holds row r in registers; column
-// c's entries of the other rows come by readlane.  A pivot below 1e-6 of its
-// diagonal entry before the factorisation sets EINVAL: the Gram matrix plus
-// ridge is not positive definite in fp32 (e.g. a zero ridge with fewer rows
-// than dimensions).
+// Linv (lower) into linv.  One wave; lane r works on row r of the block,
+// which sits in LDS (rows padded to 68 floats: the lanes' 16-byte accesses
+// of one column quad fall in distinct banks).  Column c: the pivot comes from
+// lane c, each lane below it forms L[r][c], and the column goes to
+// col[c][s] = L[s][c] for s > c (zero elsewhere); every lane then subtracts
+// L[r][c] col[c][s] from its row, four entries at a time from the quad that
+// holds column c + 1 (the zeros leave the entries up to c as they are).
+// Linv's column r is built by lane r in the same row: a column sweep
+// y_j = y_j / L[j][j], then y_i -= L[i][j] y_j for i > j, reading the same
+// col rows.  The column loops stay rolled, so the kernel is a few hundred
+// instructions.  A pivot below 1e-6 of its diagonal entry before the
+// factorisation sets EINVAL: the Gram matrix plus ridge is not positive
+// definite in fp32 (e.g. a zero ridge with fewer rows than dimensions).
+constexpr int kRowPad = kNB + 4;
 __global__ __launch_bounds__(64) void k_chol_diag(float *G, int k, const float *dg, float *linv, int32_t *status) {
-  __shared__ float l[kNB][kNB + 1];
+  __shared__ __attribute__((aligned(16))) float a[kNB][kRowPad];
+  __shared__ __attribute__((aligned(16))) float col[kNB][kNB];
   float *blk = G + (size_t)(k * kNB) * kEmb + k * kNB;
   const int r = threadIdx.x;
-  float x[kNB];
+  float4 *ar = reinterpret_cast<float4 *>(&a[r][0]);
 #pragma unroll
-  for (int s = 0; s < kNB; ++s) x[s] = blk[(size_t)r * kEmb + s];
+  for (int q = 0; q < kNB / 4; ++q) ar[q] = *reinterpret_cast<const float4 *>(blk + (size_t)r * kEmb + 4 * q);
+  const float dgr = dg[k * kNB + r];
   bool bad = false;
-#pragma unroll
+  float dinv = 0.f;  // lane r: 1 / L[r][r]
+#pragma unroll 1
   for (int c = 0; c < kNB; ++c) {
-    const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[c]), c));
-    bad = bad || !(piv > 1e-6f * dg[k * kNB + c]) || !isfinite(piv);
+    const float arc = a[r][c];
+    const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(arc), c));
+    const float dgc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dgr), c));
+    bad = bad || !(piv > 1e-6f * dgc) || !isfinite(piv);
     const float d = sqrtf(fmaxf(piv, 1e-30f));
-    x[c] = r == c ? d : x[c] / d;  // rows above c hold upper-triangle values: discarded
-    // x[s] -= L[r][c] L[s][c] for s > c (L[s][c] is lane s's x[c])
-#pragma unroll
-    for (int s = c + 1; s < kNB; ++s)
-      x[s] -= x[c] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[c]), s));
+    const float rd = 1.0f / d;
+    if (r == c) dinv = rd;
+    const float l = r > c ? arc * rd : 0.f;
+    a[r][c] = r == c ? d : l;
+    col[c][r] = l;
+    wave_lds_sync();
+    const float4 *cc = reinterpret_cast<const float4 *>(&col[c][0]);
+#pragma unroll 2
+    for (int q = (c + 1) >> 2; q < kNB / 4; ++q) {
+      const float4 u = cc[q];
+      float4 v = ar[q];
+      v.x -= l * u.x;
+      v.y -= l * u.y;
+      v.z -= l * u.z;
+      v.w -= l * u.w;
+      ar[q] = v;
+    }
   }
 #pragma unroll
-  for (int s = 0; s < kNB; ++s) {
-    const float v = s <= r ? x[s] : 0.f;
-    l[r][s] = v;
-    blk[(size_t)r * kEmb + s] = v;
+  for (int q = 0; q < kNB / 4; ++q) {
+    const float4 v = ar[q];
+    *reinterpret_cast<float4 *>(blk + (size_t)r * kEmb + 4 * q) =
+        make_float4(4 * q <= r ? v.x : 0.f, 4 * q + 1 <= r ? v.y : 0.f, 4 * q + 2 <= r ? v.z : 0.f,
+                    4 * q + 3 <= r ? v.w : 0.f);
   }
-  __syncthreads();
-  // Linv column r: L y = e_r by forward substitution (rows above r are 0)
-  float y[kNB];
+  // Linv column r (entries above r stay 0), in lane r's row
 #pragma unroll
-  for (int i = 0; i < kNB; ++i) {
-    float v = i == r ? 1.f : 0.f;
-#pragma unroll
-    for (int j = 0; j < i; ++j) v -= l[i][j] * y[j];
-    y[i] = i < r ? 0.f : v / l[i][i];
+  for (int q = 0; q < kNB / 4; ++q)
+    ar[q] = make_float4(4 * q == r ? 1.f : 0.f, 4 * q + 1 == r ? 1.f : 0.f, 4 * q + 2 == r ? 1.f : 0.f,
+                        4 * q + 3 == r ? 1.f : 0.f);
+#pragma unroll 1
+  for (int j = 0; j < kNB; ++j) {
+    const float yj = a[r][j] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dinv), j));
+    a[r][j] = yj;
+    const float4 *cc = reinterpret_cast<const float4 *>(&col[j][0]);
+#pragma unroll 2
+    for (int q = (j + 1) >> 2; q < kNB / 4; ++q) {
+      const float4 u = cc[q];
+      float4 v = ar[q];
+      v.x -= yj * u.x;
+      v.y -= yj * u.y;
+      v.z -= yj * u.z;
+      v.w -= yj * u.w;
+      ar[q] = v;
+    }
   }
   float *lv = linv + (size_t)k * kNB * kNB;
-#pragma unroll
-  for (int i = 0; i < kNB; ++i) lv[i * kNB + r] = y[i];
+#pragma unroll 4
+  for (int i = 0; i < kNB; ++i) lv[i * kNB + r] = a[r][i];
   if (r == 0 && bad) atomicCAS(status, 0, DCKV_EINVAL);
 }
 
-// One 64 x 64 tile: C = op(A) op(B) (kAcc false) or C -= op(A) op(B), with
-// op(A)(r, t) = A[r][t] (A[t][r] when kTA) and op(B)(t, s) = B[t][s] (B[s][t]
-// when kTB); row-major with the given leading dimensions.  Both operands are
-// read into LDS before C is written, so C may be one of them.
-template <bool kTA, bool kTB, bool kAcc>
-__device__ __forceinline__ void tile_op(float *C, int ldc, const float *A, int lda, const float *B, int ldb) {
-  __shared__ float sa[kNB][kNB + 1];  // sa[t][r]
-  __shared__ float sb[kNB][kNB + 1];  // sb[t][s]
-  const int tid = threadIdx.x;
-  for (int i = tid; i < kNB * kNB; i += 256) {
-    const int p = i / kNB, q = i % kNB;  // row p, column q of the stored matrix (coalesced in q)
-    const float av = A[(size_t)p * lda + q];
-    if (kTA) sa[p][q] = av; else sa[q][p] = av;
-    const float bv = B[(size_t)p * ldb + q];
-    if (kTB) sb[q][p] = bv; else sb[p][q] = bv;
+// 64 x 64 tile products on 256 threads.  Operands are staged in LDS as
+// P[t][r] = op(A)(r, t) and Q[t][s] = op(B)(t, s) (rows padded to 65 floats:
+// conflict-free transposed writes); thread (r0, s0) = (tid / 16 * 4,
+// tid % 16 * 4) accumulates the 4 x 4 block at rows r0.., columns s0..
+typedef float TileLds[kNB][kNB + 1];
+
+// s[p][q] = M[p][q] (kDirect) or s[q][p] = M[p][q], M row-major with leading
+// dimension ld (a multiple of 4, 16-byte aligned rows); 16-byte reads, four
+// per thread, coalesced along q.  A wave's 64 reads cover 4 rows x 16 quads,
+// so with rows padded to 65 floats the scalar LDS writes (p + q + e, mod 64)
+// fall in distinct banks either way.
+template <bool kDirect>
+__device__ __forceinline__ void stage(TileLds &s, const float *M, int ld) {
+  float4 v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int f = threadIdx.x + 256 * u, p = f >> 4, q = (f & 15) * 4;
+    v[u] = *reinterpret_cast<const float4 *>(M + (size_t)p * ld + q);
   }
-  __syncthreads();
-  const int r0 = (tid >> 4) * 4, s0 = (tid & 15) * 4;
-  float acc[4][4] = {};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int f = threadIdx.x + 256 * u, p = f >> 4, q = (f & 15) * 4;
+    const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (kDirect) s[p][q + i] = e[i]; else s[q + i][p] = e[i];
+    }
+  }
+}
+
+__device__ __forceinline__ void tile_mac(const TileLds &P, const TileLds &Q, float (&acc)[4][4]) {
+  const int r0 = (threadIdx.x >> 4) * 4, s0 = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
 #pragma unroll 8
   for (int t = 0; t < kNB; ++t) {
     float av[4], bv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      av[i] = sa[t][r0 + i];
-      bv[i] = sb[t][s0 + i];
+      av[i] = P[t][r0 + i];
+      bv[i] = Q[t][s0 + i];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
   }
+}
+
+// this thread's 4 x 4 block of a row-major tile, as four 16-byte rows
+__device__ __forceinline__ void load_block(const float *C, int ldc, float (&v)[4][4]) {
+  const int r0 = (threadIdx.x >> 4) * 4, s0 = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 w = *reinterpret_cast<const float4 *>(C + (size_t)(r0 + i) * ldc + s0);
+    v[i][0] = w.x;
+    v[i][1] = w.y;
+    v[i][2] = w.z;
+    v[i][3] = w.w;
+  }
+}
+
+__device__ __forceinline__ void store_block(float *C, int ldc, const float (&v)[4][4]) {
+  const int r0 = (threadIdx.x >> 4) * 4, s0 = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<float4 *>(C + (size_t)(r0 + i) * ldc + s0) = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
+}
+
+// C = op(A) op(B) (kAcc false) or C -= op(A) op(B), with op(A)(r, t) = A[r][t]
+// (A[t][r] when kTA) and op(B)(t, s) = B[t][s] (B[s][t] when kTB).  Both
+// operands are in LDS before C is written, so C may be one of them.  The
+// result stays in v for a caller that applies a second product.
+template <bool kTA, bool kTB, bool kAcc>
+__device__ __forceinline__ void tile_op(TileLds &P, TileLds &Q, float *C, int ldc, const float *A, int lda,
+                                        const float *B, int ldb, float (&v)[4][4]) {
+  if (kAcc) load_block(C, ldc, v);  // in flight while the operands are staged
+  stage<kTA>(P, A, lda);
+  stage<!kTB>(Q, B, ldb);
+  __syncthreads();
+  float acc[4][4];
+  tile_mac(P, Q, acc);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float &c = C[(size_t)(r0 + i) * ldc + s0 + j];
-      c = kAcc ? c - acc[i][j] : acc[i][j];
-    }
+    for (int j = 0; j < 4; ++j) v[i][j] = kAcc ? v[i][j] - acc[i][j] : acc[i][j];
+  store_block(C, ldc, v);
 }
 
-// Panel: L_ik = G_ik Linv_kk^T for the block rows i = k + 1 + blockIdx.x.
-__global__ __launch_bounds__(256) void k_chol_panel(float *G, const float *linv, int k) {
-  float *gik = G + (size_t)((k + 1 + blockIdx.x) * kNB) * kEmb + k * kNB;
-  tile_op<false, true, false>(gik, kEmb, gik, kEmb, linv + (size_t)k * kNB * kNB, kNB);
+// After diagonal block k (m = block rows below it): workgroups x < m form the
+// panel L_ik = G_ik Linv_kk^T (i = k + 1 + x); the next 32 take the forward
+// substitution's diagonal step on the right-hand sides X [kEmb][kC]:
+// X_k = Linv_kk X_k, one 64-column block each.
+__global__ __launch_bounds__(256) void k_chol_panel_fwd(float *G, float *X, const float *linv, int k, int m) {
+  __shared__ TileLds P, Q;
+  float v[4][4];
+  const float *lk = linv + (size_t)k * kNB * kNB;
+  if ((int)blockIdx.x < m) {
+    float *gik = G + (size_t)((k + 1 + blockIdx.x) * kNB) * kEmb + k * kNB;
+    tile_op<false, true, false>(P, Q, gik, kEmb, gik, kEmb, lk, kNB, v);
+  } else {
+    float *xk = X + (size_t)(k * kNB) * kC + (blockIdx.x - m) * kNB;
+    tile_op<false, false, false>(P, Q, xk, kC, lk, kNB, xk, kC, v);
+  }
 }
 
-// Cholesky trailing update after block k: G_ij -= L_ik L_jk^T for
-// k < j <= i; blockIdx = (i - k - 1, j - k - 1).
-__global__ __launch_bounds__(256) void k_chol_update(float *G, int k) {
-  const int i = k + 1 + blockIdx.x, j = k + 1 + blockIdx.y;
-  if (j > i) return;
-  tile_op<false, true, true>(G + (size_t)(i * kNB) * kEmb + j * kNB, kEmb, G + (size_t)(i * kNB) * kEmb + k * kNB,
-                           kEmb, G + (size_t)(j * kNB) * kEmb + k * kNB, kEmb);
+// The trailing update after panel k, with the forward substitution's update:
+// the first m (m + 1) / 2 workgroups take G_ij -= L_ik L_jk^T over the lower
+// triangle k < j <= i; the next 32 m take X_i -= L_ik X_k (i > k, one
+// 64-column block each).
+__global__ __launch_bounds__(256) void k_chol_update_fwd(float *G, float *X, int k, int m) {
+  __shared__ TileLds P, Q;
+  float v[4][4];
+  const int t = blockIdx.x, ntri = m * (m + 1) / 2;
+  if (t < ntri) {
+    int ii = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
+    while ((ii + 1) * (ii + 2) / 2 <= t) ++ii;
+    while (ii * (ii + 1) / 2 > t) --ii;
+    const int i = k + 1 + ii, j = k + 1 + (t - ii * (ii + 1) / 2);
+    tile_op<false, true, true>(P, Q, G + (size_t)(i * kNB) * kEmb + j * kNB, kEmb, G + (size_t)(i * kNB) * kEmb + k * kNB,
+                               kEmb, G + (size_t)(j * kNB) * kEmb + k * kNB, kEmb, v);
+  } else {
+    const int u = t - ntri, i = k + 1 + u / (kC / kNB), c0 = (u % (kC / kNB)) * kNB;
+    tile_op<false, false, true>(P, Q, X + (size_t)(i * kNB) * kC + c0, kC, G + (size_t)(i * kNB) * kEmb + k * kNB, kEmb,
+                                X + (size_t)(k * kNB) * kC + c0, kC, v);
+  }
 }
 
-// Right-hand sides X [kEmb][kC] (row-major): block row k times Linv_kk
-// (forward, X_k = L_kk^-1 X_k) or Linv_kk^T (backward, X_k = L_kk^-T X_k),
-// one 64-column block per workgroup.
-template <bool kFwd>
-__global__ __launch_bounds__(256) void k_solve_diag(float *X, const float *linv, int k) {
+// Backward substitution L^T X = Z, last block row: X_k = Linv_kk^T X_k.
+__global__ __launch_bounds__(256) void k_bwd_diag(float *X, const float *linv, int k) {
+  __shared__ TileLds P, Q;
+  float v[4][4];
   float *xk = X + (size_t)(k * kNB) * kC + blockIdx.x * kNB;
-  tile_op<!kFwd, false, false>(xk, kC, linv + (size_t)k * kNB * kNB, kNB, xk, kC);
+  tile_op<true, false, false>(P, Q, xk, kC, linv + (size_t)k * kNB * kNB, kNB, xk, kC, v);
 }
 
-// After block row k is solved: forward, X_i -= L_ik X_k for i > k; backward,
-// X_i -= L_ki^T X_k for i < k.  blockIdx = (block row index among those,
-// 64-column block of the right-hand sides).
-template <bool kFwd>
-__global__ __launch_bounds__(256) void k_solve_update(float *X, const float *G, int k) {
-  const int i = kFwd ? k + 1 + blockIdx.x : blockIdx.x;
-  const int c0 = blockIdx.y * kNB;
-  float *Ci = X + (size_t)(i * kNB) * kC + c0;
-  const float *Xk = X + (size_t)(k * kNB) * kC + c0;
-  if (kFwd)
-    tile_op<false, false, true>(Ci, kC, G + (size_t)(i * kNB) * kEmb + k * kNB, kEmb, Xk, kC);
-  else
-    tile_op<true, false, true>(Ci, kC, G + (size_t)(k * kNB) * kEmb + i * kNB, kEmb, Xk, kC);
+// Backward step k (X_k final): X_i -= L_ki^T X_k for i < k, blockIdx =
+// (i, 64-column block); the workgroups of row i = k - 1 then finish it,
+// X_{k-1} = Linv^T X_{k-1}, from the registers they hold.
+__global__ __launch_bounds__(256) void k_bwd_step(float *X, const float *G, const float *linv, int k) {
+  __shared__ TileLds P, Q;
+  float v[4][4];
+  const int i = blockIdx.x, c0 = blockIdx.y * kNB;
+  float *xi = X + (size_t)(i * kNB) * kC + c0;
+  tile_op<true, false, true>(P, Q, xi, kC, G + (size_t)(k * kNB) * kEmb + i * kNB, kEmb, X + (size_t)(k * kNB) * kC + c0,
+                             kC, v);
+  if (i != k - 1) return;
+  __syncthreads();  // every thread is done with P and Q
+  const int r0 = (threadIdx.x >> 4) * 4, s0 = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) Q[r0 + a][s0 + b] = v[a][b];
+  stage<true>(P, linv + (size_t)i * kNB * kNB, kNB);  // P[t][r] = Linv[t][r] = op(A)(r, t) of Linv^T
+  __syncthreads();
+  float acc[4][4];
+  tile_mac(P, Q, acc);
+  store_block(xi, kC, acc);
 }
-
 // H[c][e] = Ht[e][c] (fp32 out), Hb = bf16(H)
 __global__ void k_fit_h_out(const float *Ht, float *H, uint16_t *Hb, uint16_t *Hb2) {
   __shared__ float t[64][65];
@@ -287,21 +412,39 @@ __global__ void k_fit_ab_part(const float *Y, const float *M, int64_t n, int64_t
   }
 }
 
+// The chunk sums of 64 components per workgroup: wave w adds the chunks
+// i = w, w + 4, ... of its lane's component in order, then the four wave
+// sums are added in wave order (a fixed order, so the result does not vary
+// between runs).
 template <int kPhase>
-__global__ void k_fit_ab_reduce(const double *part, int chunks, int64_t n, float *out) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (kPhase == 0) {
-    double num = 0.0, den = 0.0;
-    for (int i = 0; i < chunks; ++i) {
-      num += part[((size_t)i * 2) * kC + c];
-      den += part[((size_t)i * 2 + 1) * kC + c];
+__global__ __launch_bounds__(256) void k_fit_ab_reduce(const double *part, int chunks, int64_t n, float *out) {
+  __shared__ double acc[2][4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
+  double s0 = 0.0, s1 = 0.0;
+#pragma unroll 4
+  for (int i = w; i < chunks; i += 4) {
+    if (kPhase == 0) {
+      s0 += part[((size_t)i * 2) * kC + c];
+      s1 += part[((size_t)i * 2 + 1) * kC + c];
+    } else {
+      s0 += part[(size_t)i * kC + c];
     }
-    out[c] = den > 0.0 ? (float)(num / den) : 0.f;
-  } else {
-    double sum = 0.0;
-    for (int i = 0; i < chunks; ++i) sum += part[(size_t)i * kC + c];
-    out[c] = (float)(sum / (double)n);
   }
+  acc[0][w][lane] = s0;
+  acc[1][w][lane] = s1;
+  __syncthreads();
+  if (w != 0) return;
+  double num = 0.0, den = 0.0;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    num += acc[0][v][lane];
+    den += acc[1][v][lane];
+  }
+  if (kPhase == 0)
+    out[c] = den > 0.0 ? (float)(num / den) : 0.f;
+  else
+    out[c] = (float)(num / (double)n);
 }
 
 }  // namespace
@@ -397,23 +540,19 @@ void fit_sequence(const FitArgs &a) {
   float *dg = reinterpret_cast<float *>(ws + l.dg);
   float *linv = reinterpret_cast<float *>(ws + l.linv);
   hipLaunchKernelGGL(k_fit_add_diag, dim3(kEmb / 256), dim3(256), 0, s, G, a.ridge * (float)n, dg);
+  // G = L L^T by blocks, with the forward substitution L Z = R riding along:
+  // per block k one diagonal launch, one panel launch (plus Z_k) and one
+  // trailing-update launch (plus R_i -= L_ik Z_k)
   for (int k = 0; k < kNBlk; ++k) {
     hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(64), 0, s, G, k, dg, linv, a.status);
     const int m = kNBlk - k - 1;
-    if (m > 0) {
-      hipLaunchKernelGGL(k_chol_panel, dim3(m), dim3(256), 0, s, G, linv, k);
-      hipLaunchKernelGGL(k_chol_update, dim3(m, m), dim3(256), 0, s, G, k);
-    }
+    hipLaunchKernelGGL(k_chol_panel_fwd, dim3(m + kC / kNB), dim3(256), 0, s, G, R, linv, k, m);
+    if (m > 0)
+      hipLaunchKernelGGL(k_chol_update_fwd, dim3(m * (m + 1) / 2 + m * (kC / kNB)), dim3(256), 0, s, G, R, k, m);
   }
-  for (int k = 0; k < kNBlk; ++k) {  // L Z = R
-    hipLaunchKernelGGL(k_solve_diag<true>, dim3(kC / kNB), dim3(256), 0, s, R, linv, k);
-    if (k + 1 < kNBlk)
-      hipLaunchKernelGGL(k_solve_update<true>, dim3(kNBlk - k - 1, kC / kNB), dim3(256), 0, s, R, G, k);
-  }
-  for (int k = kNBlk - 1; k >= 0; --k) {  // L^T H^T = Z
-    hipLaunchKernelGGL(k_solve_diag<false>, dim3(kC / kNB), dim3(256), 0, s, R, linv, k);
-    if (k > 0) hipLaunchKernelGGL(k_solve_update<false>, dim3(k, kC / kNB), dim3(256), 0, s, R, G, k);
-  }
+  // L^T H^T = Z: one launch per block row
+  hipLaunchKernelGGL(k_bwd_diag, dim3(kC / kNB), dim3(256), 0, s, R, linv, kNBlk - 1);
+  for (int k = kNBlk - 1; k > 0; --k) hipLaunchKernelGGL(k_bwd_step, dim3(k, kC / kNB), dim3(256), 0, s, R, G, linv, k);
   hipLaunchKernelGGL(k_fit_h_out, dim3(kC / 64, kEmb / 64), dim3(256), 0, s, R, a.H_out, Hb, a.Hb_out);
   // M = E[tok] bf16(H)^T
   g.a0 = g.a1 = a.E;
@@ -431,9 +570,9 @@ void fit_sequence(const FitArgs &a) {
   const int64_t per = ((n + kFitChunks - 1) / kFitChunks + 1) / 2 * 2;
   const int chunks = (int)((n + per - 1) / per);
   hipLaunchKernelGGL(k_fit_ab_part<0>, dim3(kC / 256, chunks), dim3(256), 0, s, Y, M, n, per, a.a_out, part);
-  hipLaunchKernelGGL(k_fit_ab_reduce<0>, dim3(kC / 256), dim3(256), 0, s, part, chunks, n, a.a_out);
+  hipLaunchKernelGGL(k_fit_ab_reduce<0>, dim3(kC / 64), dim3(256), 0, s, part, chunks, n, a.a_out);
   hipLaunchKernelGGL(k_fit_ab_part<1>, dim3(kC / 256, chunks), dim3(256), 0, s, Y, M, n, per, a.a_out, part);
-  hipLaunchKernelGGL(k_fit_ab_reduce<1>, dim3(kC / 256), dim3(256), 0, s, part, chunks, n, a.b_out);
+  hipLaunchKernelGGL(k_fit_ab_reduce<1>, dim3(kC / 64), dim3(256), 0, s, part, chunks, n, a.b_out);
 }
 
 }  // namespace dckv

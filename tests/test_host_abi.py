@@ -78,11 +78,11 @@ def test_fit_workspace_size_and_bounds():
     # per row: fp32 coefficients and means (16 KiB), two bf16 halves of the
     # coefficients and the gathered embeddings (12 KiB), the checked id; fixed:
     # Gram and right-hand sides (32 MiB), bf16 head (8 MiB), partial sums,
-    # the diagonal, the inverses of the 32 diagonal blocks
+    # (512 row chunks), the diagonal, the inverses of the 32 diagonal blocks
     n = 4096
     got = dk.dckv_fit_bytes(n)
     per_row = 2048 * 4 * 2 + 2048 * 2 * 3 + 4
-    fixed = 2048 * 2048 * 4 * 2 + 2048 * 2048 * 2 + 64 * 2 * 2048 * 8 + 2048 * 4 + 32 * 64 * 64 * 4
+    fixed = 2048 * 2048 * 4 * 2 + 2048 * 2048 * 2 + 512 * 2 * 2048 * 8 + 2048 * 4 + 32 * 64 * 64 * 4
     assert fixed + per_row * n <= got <= fixed + per_row * n + 12 * 256
 
 
