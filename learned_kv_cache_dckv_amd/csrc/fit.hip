@@ -118,87 +118,73 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Unblocked Cholesky of diagonal block k (lower, in place; the block's upper
 // triangle is zeroed, so later kernels read it as L_kk), then its inverse
-// Linv (lower) into linv.  One wave; lane r works on row r of the block,
-// which sits in LDS (rows padded to 68 floats: the lanes' 16-byte accesses
-// of one column quad fall in distinct banks).  Column c: the pivot comes from
-// lane c, each lane below it forms L[r][c], and the column goes to
-// col[c][s] = L[s][c] for s > c (zero elsewhere); every lane then subtracts
-// L[r][c] col[c][s] from its row, four entries at a time from the quad that
-// holds column c + 1 (the zeros leave the entries up to c as they are).
-// Linv's column r is built by lane r in the same row: a column sweep
-// y_j = y_j / L[j][j], then y_i -= L[i][j] y_j for i > j, reading the same
-// col rows.  The column loops stay rolled, so the kernel is a few hundred
-// instructions.  A pivot below 1e-6 of its diagonal entry before the
+// Linv (lower) into linv.  One wave; lane r holds row r of the block in
+// registers.  Column c: the pivot p comes from lane c, 1 / sqrt(p) from one
+// reciprocal square root (L[c][c] = p / sqrt(p)), every lane below c scales
+// its entry, and the column goes through LDS (col[c][s] = L[s][c] below the
+// diagonal, 0 elsewhere) so that each lane subtracts L[r][c] L[s][c] from
+// its entries s > c with broadcast reads (all lanes read one address).  Linv
+// is then built one column per lane by a column sweep over L: y[j] /= L[j][j],
+// then y[i] -= L[i][j] y[j] for i > j, reading L's columns from the same LDS
+// rows; its steps are independent across i, so no long dependent chain forms.
+// (A version with the block in LDS and rolled column loops, a few hundred
+// instructions long, measured slower: its per-column LDS round trips are
+// serial.)  A pivot below 1e-6 of its diagonal entry before the
 // factorisation sets EINVAL: the Gram matrix plus ridge is not positive
 // definite in fp32 (e.g. a zero ridge with fewer rows than dimensions).
-constexpr int kRowPad = kNB + 4;
 __global__ __launch_bounds__(64) void k_chol_diag(float *G, int k, const float *dg, float *linv, int32_t *status) {
-  __shared__ __attribute__((aligned(16))) float a[kNB][kRowPad];
   __shared__ __attribute__((aligned(16))) float col[kNB][kNB];
   float *blk = G + (size_t)(k * kNB) * kEmb + k * kNB;
   const int r = threadIdx.x;
-  float4 *ar = reinterpret_cast<float4 *>(&a[r][0]);
+  float x[kNB];
 #pragma unroll
-  for (int q = 0; q < kNB / 4; ++q) ar[q] = *reinterpret_cast<const float4 *>(blk + (size_t)r * kEmb + 4 * q);
+  for (int q = 0; q < kNB / 4; ++q) {
+    const float4 v = *reinterpret_cast<const float4 *>(blk + (size_t)r * kEmb + 4 * q);
+    x[4 * q] = v.x;
+    x[4 * q + 1] = v.y;
+    x[4 * q + 2] = v.z;
+    x[4 * q + 3] = v.w;
+  }
   const float dgr = dg[k * kNB + r];
   bool bad = false;
   float dinv = 0.f;  // lane r: 1 / L[r][r]
-#pragma unroll 1
+#pragma unroll
   for (int c = 0; c < kNB; ++c) {
-    const float arc = a[r][c];
-    const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(arc), c));
+    const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[c]), c));
     const float dgc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dgr), c));
     bad = bad || !(piv > 1e-6f * dgc) || !isfinite(piv);
-    const float d = sqrtf(fmaxf(piv, 1e-30f));
-    const float rd = 1.0f / d;
+    const float pc = fmaxf(piv, 1e-30f);
+    const float rd = __builtin_amdgcn_rsqf(pc);
     if (r == c) dinv = rd;
-    const float l = r > c ? arc * rd : 0.f;
-    a[r][c] = r == c ? d : l;
-    col[c][r] = l;
+    // rows above c hold upper-triangle values: set to 0, zeroed in the output
+    x[c] = r == c ? pc * rd : (r > c ? x[c] * rd : 0.f);
+    col[c][r] = r > c ? x[c] : 0.f;
     wave_lds_sync();
-    const float4 *cc = reinterpret_cast<const float4 *>(&col[c][0]);
-#pragma unroll 2
-    for (int q = (c + 1) >> 2; q < kNB / 4; ++q) {
-      const float4 u = cc[q];
-      float4 v = ar[q];
-      v.x -= l * u.x;
-      v.y -= l * u.y;
-      v.z -= l * u.z;
-      v.w -= l * u.w;
-      ar[q] = v;
-    }
+#pragma unroll
+    for (int s = c + 1; s < kNB; ++s) x[s] -= x[c] * col[c][s];
   }
 #pragma unroll
   for (int q = 0; q < kNB / 4; ++q) {
-    const float4 v = ar[q];
-    *reinterpret_cast<float4 *>(blk + (size_t)r * kEmb + 4 * q) =
-        make_float4(4 * q <= r ? v.x : 0.f, 4 * q + 1 <= r ? v.y : 0.f, 4 * q + 2 <= r ? v.z : 0.f,
-                    4 * q + 3 <= r ? v.w : 0.f);
+    float4 v;
+    v.x = 4 * q <= r ? x[4 * q] : 0.f;
+    v.y = 4 * q + 1 <= r ? x[4 * q + 1] : 0.f;
+    v.z = 4 * q + 2 <= r ? x[4 * q + 2] : 0.f;
+    v.w = 4 * q + 3 <= r ? x[4 * q + 3] : 0.f;
+    *reinterpret_cast<float4 *>(blk + (size_t)r * kEmb + 4 * q) = v;
   }
-  // Linv column r (entries above r stay 0), in lane r's row
+  // Linv column r: L y = e_r (entries above r stay 0)
+  float y[kNB];
 #pragma unroll
-  for (int q = 0; q < kNB / 4; ++q)
-    ar[q] = make_float4(4 * q == r ? 1.f : 0.f, 4 * q + 1 == r ? 1.f : 0.f, 4 * q + 2 == r ? 1.f : 0.f,
-                        4 * q + 3 == r ? 1.f : 0.f);
-#pragma unroll 1
+  for (int i = 0; i < kNB; ++i) y[i] = i == r ? 1.f : 0.f;
+#pragma unroll
   for (int j = 0; j < kNB; ++j) {
-    const float yj = a[r][j] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dinv), j));
-    a[r][j] = yj;
-    const float4 *cc = reinterpret_cast<const float4 *>(&col[j][0]);
-#pragma unroll 2
-    for (int q = (j + 1) >> 2; q < kNB / 4; ++q) {
-      const float4 u = cc[q];
-      float4 v = ar[q];
-      v.x -= yj * u.x;
-      v.y -= yj * u.y;
-      v.z -= yj * u.z;
-      v.w -= yj * u.w;
-      ar[q] = v;
-    }
+    y[j] *= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dinv), j));
+#pragma unroll
+    for (int i = j + 1; i < kNB; ++i) y[i] -= col[j][i] * y[j];
   }
   float *lv = linv + (size_t)k * kNB * kNB;
-#pragma unroll 4
-  for (int i = 0; i < kNB; ++i) lv[i * kNB + r] = a[r][i];
+#pragma unroll
+  for (int i = 0; i < kNB; ++i) lv[i * kNB + r] = y[i];
   if (r == 0 && bad) atomicCAS(status, 0, DCKV_EINVAL);
 }
 

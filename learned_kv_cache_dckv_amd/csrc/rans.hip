@@ -210,8 +210,9 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(const Batch<EncP
 // Escapes (codes beyond +-127, 64 bits each) are found out of order by the
 // quantiser tiles; the stream stores them by ascending flat index
 // j * C_a + rank, so the scan's workgroup first sorts the (usually few)
-// records with a bitonic network, in LDS up to kSortLds records, else in
-// place in global memory.
+// records: up to one record per thread by counting the smaller keys, beyond
+// that with a bitonic network, in LDS up to kSortLds records, else in place
+// in global memory.
 constexpr int kSortLds = 4096;
 
 __device__ __forceinline__ void bitonic(unsigned long long *a, uint32_t n_pow2) {
@@ -259,6 +260,19 @@ __device__ __forceinline__ void sort_escapes(const uint8_t *ws, uint32_t *esc_ra
     }
   }
   __syncthreads();
+  if (n <= blockDim.x) {
+    // the flat indices are distinct, so each record's place is the number of
+    // smaller keys: one pass, one thread per record, no barriers
+    if (threadIdx.x < n) {
+      const unsigned long long v = a[threadIdx.x];
+      const unsigned long long key = v >> 32;
+      uint32_t pos = 0;
+      for (uint32_t j = 0; j < n; ++j) pos += (a[j] >> 32) < key ? 1u : 0u;
+      esc_sorted[2 * pos] = (uint32_t)(v >> 32);
+      esc_sorted[2 * pos + 1] = (uint32_t)v;
+    }
+    return;
+  }
   bitonic(a, p2);
   for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
     const unsigned long long v = a[i];
@@ -283,38 +297,59 @@ struct ScanP {
 };
 
 // One workgroup per request.
+constexpr int kScanChunk = 4096;
 __global__ __launch_bounds__(1024) void k_scan_header(const Batch<ScanP> B) {
   const ScanP &P = B.r[batch_req(B, blockIdx.x)];
-  __shared__ uint64_t part[1024];
+  __shared__ uint64_t part[16];
+  __shared__ uint64_t sbuf[kScanChunk];
   __shared__ unsigned long long keys[kSortLds];
   const int t = threadIdx.x;
   if (*P.status == 0) sort_escapes(P.ws, P.esc_raw, P.esc_sorted, P.esc_cap, keys);
   __syncthreads();
+  // group word offsets: chunks of 4,096 groups go through LDS, so that the
+  // loads and stores are coalesced and each thread scans 4 consecutive sizes
   const int64_t ng = P.n_groups;
-  const int64_t per = (ng + 1023) / 1024;
-  const int64_t lo = min<int64_t>(ng, t * per), hi = min<int64_t>(ng, lo + per);
-  uint64_t s = 0;
-  for (int64_t i = lo; i < hi; ++i) s += P.gwords[i];
-  // inclusive scan: within each wave by shuffles, then the 16 wave totals
   const int lane = t & 63, wv = t >> 6;
-  uint64_t incl = s;
+  uint64_t carry = 0;
+  for (int64_t c0 = 0; c0 < ng; c0 += kScanChunk) {
+    const int64_t m = min<int64_t>(kScanChunk, ng - c0);
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t v = __shfl_up(incl, off);
-    if (lane >= off) incl += v;
+    for (int u = 0; u < kScanChunk / 1024; ++u) {
+      const int64_t i = t + 1024 * u;
+      sbuf[i] = i < m ? P.gwords[c0 + i] : 0u;
+    }
+    __syncthreads();
+    const uint64_t e0 = sbuf[4 * t], e1 = sbuf[4 * t + 1], e2 = sbuf[4 * t + 2], e3 = sbuf[4 * t + 3];
+    const uint64_t s = e0 + e1 + e2 + e3;
+    // inclusive scan: within each wave by shuffles, then the 16 wave totals
+    uint64_t incl = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint64_t v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) part[wv] = incl;
+    __syncthreads();
+    uint64_t before = 0, all = 0;
+    for (int w = 0; w < 16; ++w) {
+      if (w < wv) before += part[w];
+      all += part[w];
+    }
+    const uint64_t ex = carry + before + incl - s;
+    sbuf[4 * t] = ex;
+    sbuf[4 * t + 1] = ex + e0;
+    sbuf[4 * t + 2] = ex + e0 + e1;
+    sbuf[4 * t + 3] = ex + e0 + e1 + e2;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kScanChunk / 1024; ++u) {
+      const int64_t i = t + 1024 * u;
+      if (i < m) P.goffs[c0 + i] = sbuf[i];
+    }
+    carry += all;
+    __syncthreads();  // sbuf and part are reused by the next chunk
   }
-  if (lane == 63) part[wv] = incl;
-  __syncthreads();
-  uint64_t before = 0;
-  for (int w = 0; w < wv; ++w) before += part[w];
-  uint64_t all = 0;
-  for (int w = 0; w < 16; ++w) all += part[w];
-  uint64_t run = before + incl - s;
-  for (int64_t i = lo; i < hi; ++i) {
-    P.goffs[i] = run;
-    run += P.gwords[i];
-  }
-  const uint64_t total_words = all;
+  const uint64_t total_words = carry;
   if (t == 0) P.goffs[ng] = total_words;
   Ctrl *ct = ctrl_of(P.ws);
   const uint32_t n_esc = ct->n_esc;
@@ -376,7 +411,9 @@ struct PackP {
   const int32_t *status;
 };
 
-// A request's cnt workgroups take its groups (and escape records) in strides.
+// Workgroup b of a request copies group b, reversed, to its offset (256
+// words per pass, coalesced both ways); the request's workgroups also copy its
+// escape records, in strides.
 __global__ __launch_bounds__(256) void k_pack(const Batch<PackP> B) {
   const int ri = batch_req(B, blockIdx.x);
   const PackP &P = B.r[ri];
@@ -385,7 +422,8 @@ __global__ __launch_bounds__(256) void k_pack(const Batch<PackP> B) {
   const Ctrl *ct = reinterpret_cast<const Ctrl *>(P.ws);
   const uint64_t rans_off = ct->rans_off, esc_off = ct->esc_off;
   const uint32_t n_esc = ct->n_esc;
-  for (int64_t gid = local; gid < P.n_groups; gid += cnt) {
+  const int64_t gid = local;
+  if (gid < P.n_groups) {
     const uint32_t W = P.gwords[gid];
     const uint16_t *src = P.scratch + (size_t)gid * (kLanes * (kBlock + 2));
     uint16_t *dst = reinterpret_cast<uint16_t *>(P.stream + rans_off) + P.goffs[gid];
@@ -877,7 +915,7 @@ void launch_pack(const EncodeArgs *args, int n) {
   };
   // one workgroup per group, at most 4,096 per request (at least one, for the
   // escape records)
-  auto count = [&](int i) { return (uint32_t)std::max<int64_t>(1, std::min<int64_t>(args[i].g.n_groups, 4096)); };
+  auto count = [&](int i) { return (uint32_t)std::max<int64_t>(1, args[i].g.n_groups); };
   launch_batched<PackP>(k_pack, "pack", n, args[0].s, 256, fill, count);
 }
 
