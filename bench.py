@@ -105,12 +105,13 @@ def cpu_baseline(req_cfg: int, n_rows: int):
     ocodec.decode(enc.data, req.token_ids, params, p)
     t2 = time.perf_counter()
     model, blas = _host_info()
+    n = int(req.rows.shape[0])  # the positions the sample holds
     if synth.CONFIGS[req_cfg].get("n_requests"):
-        what = "request 0 of the batch (its first %d positions)" % req.T
-    elif req.T >= synth.CONFIGS[req_cfg]["T"]:
-        what = "the whole %d-token workload" % req.T
+        what = "request 0 of the batch (its first %d positions)" % n
+    elif n >= synth.CONFIGS[req_cfg]["T"]:
+        what = "the whole %d-token workload" % n
     else:
-        what = "first %d positions of the workload as one %d-token prompt" % (req.T, req.T)
+        what = "first %d positions of the workload as one %d-token prompt" % (n, n)
     return {"value": enc.N / (t2 - t0), "unit": "coded tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": "%s (%d coded), same seeds and step scale; encode %.2f s + decode %.2f s, numpy float64" % (
                 what, enc.N, t1 - t0, t2 - t1),

@@ -335,25 +335,9 @@ __device__ __forceinline__ int acc_row(int mb, int v, int lane) { return mb * 32
 // the constant part of acc_row(): row of register v of block mb without the lane term
 __device__ __forceinline__ constexpr int acc_crow(int mb, int v) { return mb * 32 + 8 * (v >> 2) + (v & 3); }
 
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-
 // ---------------------------------------------------------------------------
 // operand setup helpers
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int clamp_tok(const int32_t *tok, int64_t t, int vocab, int32_t *status) {
-  int v = tok[t];
-  if (v < 0 || v >= vocab) {
-    set_status(status, DCKV_EINVAL);
-    v = 0;
-  }
-  return v;
-}
-
 // tile row staged by this lane in load i (0..7), matching load_rows()
 __device__ __forceinline__ int staged_row(int i) { return (threadIdx.x >> 6) * 64 + i * 8 + ((threadIdx.x & 63) >> 3); }
 
