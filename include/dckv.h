@@ -387,7 +387,7 @@ int dckv_profile_read(const char *kernel, double *total_ms, int64_t *launches);
  * (E^T Y keeps 16 mantissa bits of Y) with a blocked Cholesky solve; a Gram
  * matrix plus ridge that is not positive definite, or a token id outside
  * [0, vocab), sets *status to DCKV_EINVAL.  The workspace (dckv_fit_bytes)
- * is about 28 KiB per calibration row plus 42 MiB.  2 <= n <= 2^18.
+ * is about 28 KiB per calibration row plus 57 MiB.  2 <= n <= 2^18.
  * --------------------------------------------------------------------------*/
 int dckv_fit_bytes(int64_t n, uint64_t *workspace_bytes);
 int dckv_fit(const dckv_params *p, const uint16_t *rows, const int32_t *token_ids, int64_t n, float ridge,
