@@ -261,13 +261,18 @@ __device__ __forceinline__ void sort_escapes(const uint8_t *ws, uint32_t *esc_ra
   }
   __syncthreads();
   if (n <= blockDim.x) {
-    // the flat indices are distinct, so each record's place is the number of
-    // smaller keys: one pass, one thread per record, no barriers
+    // each record's place is the number of records before it in (flat
+    // index, arrival) order (the flat indices of a valid encode are distinct;
+    // arrival order only keeps the places distinct whatever the input): one
+    // pass, one thread per record, no barriers
     if (threadIdx.x < n) {
       const unsigned long long v = a[threadIdx.x];
       const unsigned long long key = v >> 32;
       uint32_t pos = 0;
-      for (uint32_t j = 0; j < n; ++j) pos += (a[j] >> 32) < key ? 1u : 0u;
+      for (uint32_t j = 0; j < n; ++j) {
+        const unsigned long long kj = a[j] >> 32;
+        pos += (kj < key || (kj == key && j < threadIdx.x)) ? 1u : 0u;
+      }
       esc_sorted[2 * pos] = (uint32_t)(v >> 32);
       esc_sorted[2 * pos + 1] = (uint32_t)v;
     }
