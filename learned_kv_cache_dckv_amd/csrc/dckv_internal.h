@@ -22,8 +22,8 @@ constexpr int kBlock = 256;                 // tokens per substream block
 constexpr int kLanes = 64;                  // components per group (one wave)
 constexpr int kBuckets = 256;               // decode lookup buckets per table (128 slots each)
 constexpr int kBucketShift = kPrecBits - 8; // slot >> 7 -> bucket
-constexpr uint32_t kSplitPure = 1u << kBucketShift;  // bucket split: one symbol
-constexpr uint32_t kSplitSearch = 255;               // bucket split: three or more symbols
+constexpr uint32_t kSplitPure = kM;         // bucket split: one symbol (no slot reaches it)
+constexpr uint32_t kSplitSearch = 0xFFFFu;  // bucket split: three or more symbols
 constexpr int kHeaderBytes = 64;
 constexpr uint16_t kVersion = 1;
 
@@ -61,7 +61,7 @@ struct PlanDev {
   float *scale = nullptr;       // [C]   Laplace scale b of each component
   uint32_t *tab = nullptr;      // [C_a][256]  f | cum << 16
   float *rcp = nullptr;         // [C_a][256]  fp32(1/f (1 - 2^-21)), the encoder's quotient estimate
-  uint16_t *bucket = nullptr;   // [C_a][kBuckets] lo | split << 8 of each slot bucket (decoder)
+  uint32_t *bucket = nullptr;   // [C_a][kBuckets] lo | split << 16 of each slot bucket (decoder)
   double *omega = nullptr;      // [head_dim/2] RoPE frequencies
 };
 

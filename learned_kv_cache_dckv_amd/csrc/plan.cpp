@@ -295,7 +295,7 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
   }
   std::vector<uint32_t> tab((size_t)std::max(Ca, 1) * 256, 0);
   std::vector<float> rcp((size_t)std::max(Ca, 1) * 256, 0.f);
-  std::vector<uint16_t> bucket((size_t)std::max(Ca, 1) * kBuckets, 0);
+  std::vector<uint32_t> bucket((size_t)std::max(Ca, 1) * kBuckets, 0);
   for (int r = 0; r < Ca; ++r) {
     uint32_t cum = 0;
     const uint16_t *f = &h.freq[(size_t)r * kNSym];
@@ -316,9 +316,10 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
       rcp[(size_t)r * 256 + s] = (float)((1.0 / (double)fs) * (1.0 - std::ldexp(1.0, -21)));
     }
     // decoder buckets of 2^kBucketShift slots: lo = symbol of the bucket's
-    // first slot; split = offset (in the bucket) where symbol lo + 1 starts
-    // when the bucket holds exactly two symbols, kSplitPure when it holds
-    // one, kSplitSearch when it holds three or more
+    // first slot; split = the slot where symbol lo + 1 starts when the bucket
+    // holds exactly two symbols (so a slot's symbol is lo + (slot >= split)),
+    // kSplitPure (no slot reaches it) when it holds one, kSplitSearch when it
+    // holds three or more
     int s = 0;
     for (int b = 0; b < kBuckets; ++b) {
       const uint32_t first = (uint32_t)b << kBucketShift, last = first + (1u << kBucketShift) - 1u;
@@ -327,9 +328,9 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
       while (cumv[e + 1] <= last) ++e;
       uint32_t split;
       if (e == s) split = kSplitPure;
-      else if (e == s + 1) split = cumv[s + 1] - first;
+      else if (e == s + 1) split = cumv[s + 1];
       else split = kSplitSearch;
-      bucket[(size_t)r * kBuckets + b] = (uint16_t)(s | (split << 8));
+      bucket[(size_t)r * kBuckets + b] = (uint32_t)s | (split << 16);
     }
   }
   // quantiser constants of each rank: step, 1 / step (0 past C_a), neighbour weight
@@ -352,7 +353,7 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
   };
   const size_t o_step = take(C * 4), o_nbr = take(C * 4), o_rank = take(C * 4), o_act = take(Ca_pad * 4);
   const size_t o_perm = take(C * 4), o_colpos = take(C * 4), o_qcol = take(qcol.size() * 4), o_scale = take(C * 4);
-  const size_t o_tab = take(tab.size() * 4), o_rcp = take(rcp.size() * 4), o_bucket = take(bucket.size() * 2);
+  const size_t o_tab = take(tab.size() * 4), o_rcp = take(rcp.size() * 4), o_bucket = take(bucket.size() * 4);
   const size_t o_omega = take(kHalf * 8);
   void *blk = nullptr;
   if (hipMalloc(&blk, off) != hipSuccess) {
@@ -370,7 +371,7 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
   std::memcpy(&img[o_scale], p->laplace_scale, C * 4);
   std::memcpy(&img[o_tab], tab.data(), tab.size() * 4);
   std::memcpy(&img[o_rcp], rcp.data(), rcp.size() * 4);
-  std::memcpy(&img[o_bucket], bucket.data(), bucket.size() * 2);
+  std::memcpy(&img[o_bucket], bucket.data(), bucket.size() * 4);
   std::memcpy(&img[o_omega], omega.data(), kHalf * 8);
   if (hipMemcpy(blk, img.data(), off, hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(blk);
@@ -389,7 +390,7 @@ extern "C" int dckv_plan(const dckv_params *p, float step_scale, dckv_plan_t **o
   pl->dev.scale = reinterpret_cast<float *>(b + o_scale);
   pl->dev.tab = reinterpret_cast<uint32_t *>(b + o_tab);
   pl->dev.rcp = reinterpret_cast<float *>(b + o_rcp);
-  pl->dev.bucket = reinterpret_cast<uint16_t *>(b + o_bucket);
+  pl->dev.bucket = reinterpret_cast<uint32_t *>(b + o_bucket);
   pl->dev.omega = reinterpret_cast<double *>(b + o_omega);
   pl->dev_bytes = off;
   // the embedding-mean table: H E[v] for every token id, shared by the plans

@@ -32,6 +32,8 @@ constexpr int kWordBuf = 1024;    // u16 words cached per decoder wave
 __device__ __forceinline__ void set_status(int32_t *st, int code) { atomicCAS(st, 0, code); }
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // A load through a global (address space 1) pointer.
 template <class T>
@@ -58,7 +60,9 @@ __device__ __forceinline__ void stage_tab(uint32_t *tab, const uint32_t *gtab, i
   for (int i = 0; i < kPer; ++i) {
     const int pc = threadIdx.x + i * kThreads;
     const int c = pc & 63, q = pc >> 6;
-    v[i] = c < n ? gload(src + c * 64 + q) : u32x4{0u, 0u, 0u, 0u};
+    // every load is issued (columns past n read column 0) before any is used
+    v[i] = gload(src + (c < n ? c : 0) * 64 + q);
+    if (c >= n) v[i] = u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -84,11 +88,42 @@ struct EncP {
   const int32_t *status;
 };
 
+// The table entries and the reciprocals of components 64 g .. 64 g + 63 into
+// LDS as pairs (entry, reciprocal), pair (e, lane) at e * 64 + lane: a wave
+// reads every lane's pair with one 8-byte LDS read, and the bank depends on
+// the lane alone, as in stage_tab().  Columns past n are zero.
+template <int kThreads>
+__device__ __forceinline__ void stage_pairs(u32x2 *pr, const uint32_t *gtab, const uint32_t *grcp, int g, int n) {
+  constexpr int kPer = kLanes * 256 / 4 / kThreads;
+  static_assert(kPer * kThreads * 4 == kLanes * 256, "whole pieces");
+  const u32x4 *st = reinterpret_cast<const u32x4 *>(gtab + (size_t)kLanes * g * 256);
+  const u32x4 *sr = reinterpret_cast<const u32x4 *>(grcp + (size_t)kLanes * g * 256);
+  u32x4 a[kPer], b[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int pc = threadIdx.x + i * kThreads;
+    const int c = pc & 63, q = pc >> 6;
+    // every load is issued (columns past n read column 0) before any is used
+    const int cc = c < n ? c : 0;
+    a[i] = gload(st + cc * 64 + q);
+    b[i] = gload(sr + cc * 64 + q);
+    if (c >= n) a[i] = b[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int pc = threadIdx.x + i * kThreads;
+    u32x2 *d = pr + (pc >> 6) * 4 * kLanes + (pc & 63);
+    d[0] = u32x2{a[i].x, b[i].x};
+    d[kLanes] = u32x2{a[i].y, b[i].y};
+    d[2 * kLanes] = u32x2{a[i].z, b[i].z};
+    d[3 * kLanes] = u32x2{a[i].w, b[i].w};
+  }
+}
+
 // Workgroup w of a request codes component group g = w / nch of the blocks
 // 16 (w % nch) .. + 15 (one wave each), nch = ceil(n_blk / 16).
 __global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(const Batch<EncP> B) {
-  __shared__ uint32_t tab[256 * kLanes];   // [symbol][lane]: f | cum << 16
-  __shared__ uint32_t rcpt[256 * kLanes];  // [symbol][lane]: fp32 bits of the scaled reciprocal of f
+  __shared__ u32x2 pairs[256 * kLanes];  // [symbol][lane]: (f | cum << 16, fp32 bits of the scaled 1/f)
   const int ri = batch_req(B, blockIdx.x);
   const EncP &P = B.r[ri];
   const uint32_t nch_w = (uint32_t)((P.n_blk + kEncWaves - 1) / kEncWaves);
@@ -96,110 +131,112 @@ __global__ __launch_bounds__(kEncWaves * 64) void k_rans_encode(const Batch<EncP
   const int g = (int)(local / nch_w);
   const int chunk = (int)(local - (uint32_t)g * nch_w);
   const int n = min(kLanes, P.Ca - kLanes * g);
-  stage_tab<kEncWaves * 64>(tab, P.tab, g, n);
-  stage_tab<kEncWaves * 64>(rcpt, reinterpret_cast<const uint32_t *>(P.rcp), g, n);
+  stage_pairs<kEncWaves * 64>(pairs, P.tab, reinterpret_cast<const uint32_t *>(P.rcp), g, n);
   __syncthreads();
   if (*P.status != 0) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave's block, its length and quad count are wave-uniform (scalar
+  // registers, scalar branches)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t b = (int64_t)chunk * kEncWaves + wave;
   if (b >= P.n_blk) return;
   const int Lb = (int)min<int64_t>(kBlock, P.N - kBlock * b);
   const int64_t gid = b * P.G + g;
   const uint32_t *sw = P.sym32 + ((size_t)g * (P.N256 / 4) + (size_t)b * 64) * 64 + lane;
   uint16_t *out = P.scratch + (size_t)gid * (kLanes * (kBlock + 2));
+  // the group's words go through a buffer resource over its scratch slot; a
+  // lane that emits nothing stores to an offset past the range, which the
+  // hardware drops, so no step changes the execution mask
+  constexpr uint32_t kSlotWords = kLanes * (kBlock + 2), kSlotBytes = 2 * kSlotWords;
+  constexpr int kDrop = 1 << 30;
+  const rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(out, (short)0, (int)kSlotBytes, 0x00020000);
   const bool lane_ok = lane < n;
   // Escapes code as the identity: table entry 255 is f = 2^15, cum = 0, so
   // the state never emits and x / f * 2^15 + x % f = x.  Lanes past C_a code
   // escapes only, through lane 0's table row.
-  const uint32_t *mytab = tab + (lane_ok ? lane : 0);
-  const float *myrcp = reinterpret_cast<const float *>(rcpt) + (lane_ok ? lane : 0);
+  const u32x2 *mypair = pairs + (lane_ok ? lane : 0);
   uint32_t x = kL;
   uint32_t cnt = 0;
-  // One coding step of symbol entry (e, rf) = (f | cum << 16, scaled 1/f).
+  // One coding step of the pair (e, rf) = (f | cum << 16, scaled 1/f).
+  // The lanes whose state is >= f 2^17 first emit their low 16 bits.  The
+  // coder pushes a step's words in descending lane order and the stream holds
+  // the pushes reversed, so the slot is filled from its top down: the step's
+  // words go below those already there, in ascending lane order, and the
+  // group's words end up in stream order at the top of the slot.
   // q0 = trunc(fp32(x) rf) is floor(x / f) or one less (the reciprocal is
   // scaled down so that the fp32 roundings never push it above), so
   // x' = q M + (x - q f) + cum = (q0 << 15) + r0 + cum, plus M - f when
   // r0 = x - q0 f is still >= f.
-  auto enc = [&](uint32_t e, float rf) {
-    const uint32_t f = e & 0xFFFFu, c = e >> 16;
+  auto enc = [&](u32x2 te) {
+    const uint32_t e = te.x, f = e & 0xFFFFu;
+    const float rf = __uint_as_float(te.y);
     const bool emit = (x >> 17) >= f;  // x >= f 2^17 (f = 2^15 never emits)
     const uint64_t mask = __ballot(emit);
-    if (mask) {
-      // the emitting lanes write in descending lane order
-      const uint32_t tot = (uint32_t)__popcll(mask);
-      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-      if (emit) out[cnt + tot - 1u - below] = (uint16_t)(x & 0xFFFFu);
-      x = emit ? x >> 16 : x;
-      cnt += tot;
-    }
+    const uint32_t tot = (uint32_t)__popcll(mask);
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+    // all-ones on the emitting lanes, as a value (the selections below stay
+    // arithmetic: no branch and no change of the execution mask)
+    uint32_t sel = emit ? 0xFFFFFFFFu : 0u;
+    asm volatile("" : "+v"(sel));
+    const uint32_t voff = ((2u * (kSlotWords - cnt - tot) + 2u * below) & sel) | ((uint32_t)kDrop & ~sel);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)x, wr, (int)voff, 0, 0);
+    x >>= sel & 16u;
+    cnt += tot;
     const uint32_t q0 = (uint32_t)((float)x * rf);
     const uint32_t r0 = x - __umul24(q0, f);
-    const uint32_t xn = (q0 << kPrecBits) + r0 + c;
+    const uint32_t xn = (q0 << kPrecBits) + r0 + (e >> 16);
     x = xn + (r0 >= f ? kM - f : 0u);
   };
-  // symbol words in chunks of 8 quads, last chunk first; the words of the
-  // next chunk are loaded while this one is coded (every quad of the block
-  // is in the buffer; quads past the last are not coded)
+  // Quads (symbol words of four rows) are coded last to first, in chunks of
+  // eight whose words are loaded one chunk ahead.  Quads past the block's
+  // last code as escapes (the identity), as do the rows past the block in its
+  // last quad, so every chunk is whole and the loop has no per-lane branch.
   const int nq = (Lb + 3) >> 2;
   const int nch = (nq + 7) >> 3;
-  // rows past the block in its last quad code as escapes
   const uint32_t tail = (Lb & 3) ? 0xFFFFFFFFu << (8 * (Lb & 3)) : 0u;
   uint32_t wq[8], wn[8];
   auto load_chunk = [&](int ch, uint32_t (&w)[8]) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) w[u] = gload(sw + (size_t)(ch * 8 + u) * 64);
-  };
-  // the four table entries of a quad's symbols; a quad's entries are read
-  // while the quad before it in coding order is coded, so a step never
-  // waits on LDS
-  uint32_t ec[4], en[4];
-  float rc[4], rn[4];
-  auto fetch = [&](uint32_t w, uint32_t (&e)[4], float (&rf)[4]) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t sy = (w >> (8 * k)) & 0xFFu;
-      e[k] = mytab[sy * kLanes];
-      rf[k] = myrcp[sy * kLanes];
+    for (int u = 0; u < 8; ++u) {
+      const int qd = ch * 8 + u;
+      const uint32_t v = gload(sw + (size_t)qd * 64);
+      w[u] = !lane_ok || qd >= nq ? 0xFFFFFFFFu : (qd == nq - 1 ? v | tail : v);
     }
   };
-  load_chunk(nch - 1, wn);
-  {
-    // the first quad coded: quad nq - 1, in the last chunk
-    uint32_t w0 = 0xFFFFFFFFu;
+  // the four pairs of a quad's symbols; a quad's pairs are read while the
+  // quad before it in coding order is coded, so a step never waits on LDS
+  auto fetch = [&](uint32_t w, u32x2 (&t)[4]) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (u == ((nq - 1) & 7)) w0 = lane_ok ? wn[u] : 0xFFFFFFFFu;
-    fetch(w0 | tail, ec, rc);
-  }
+    for (int k = 0; k < 4; ++k) t[k] = mypair[((w >> (8 * k)) & 0xFFu) * kLanes];
+  };
+  u32x2 ec[4], en[4];
+  load_chunk(nch - 1, wn);
+  fetch(wn[7], ec);
 #pragma unroll 1
   for (int ch = nch - 1; ch >= 0; --ch) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) wq[u] = lane_ok ? wn[u] : 0xFFFFFFFFu;
+    for (int u = 0; u < 8; ++u) wq[u] = wn[u];
     if (ch > 0) load_chunk(ch - 1, wn);
 #pragma unroll
     for (int u = 7; u >= 0; --u) {
-      const int qd = ch * 8 + u;
-      if (qd >= nq) continue;
-      // the next quad in coding order: u - 1 of this chunk, or quad 7 of
-      // the next chunk
+      // the next quad in coding order: u - 1 of this chunk, or quad 7 of the
+      // next chunk
       if (u > 0)
-        fetch(wq[u - 1], en, rn);
+        fetch(wq[u - 1], en);
       else if (ch > 0)
-        fetch(lane_ok ? wn[7] : 0xFFFFFFFFu, en, rn);
+        fetch(wn[7], en);
 #pragma unroll
-      for (int k = 3; k >= 0; --k) enc(ec[k], rc[k]);
+      for (int k = 3; k >= 0; --k) enc(ec[k]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        ec[k] = en[k];
-        rc[k] = rn[k];
-      }
+      for (int k = 0; k < 4; ++k) ec[k] = en[k];
     }
   }
+  // the final states come first in the stream: lane l's low and high halves
+  // at words 2 l and 2 l + 1
   if (lane_ok) {
-    const uint32_t pos = cnt + 2u * (uint32_t)(n - 1 - lane);
-    out[pos] = (uint16_t)(x >> 16);
-    out[pos + 1] = (uint16_t)(x & 0xFFFFu);
+    const uint32_t pos = kSlotWords - cnt - 2u * (uint32_t)n + 2u * (uint32_t)lane;
+    out[pos] = (uint16_t)(x & 0xFFFFu);
+    out[pos + 1] = (uint16_t)(x >> 16);
   }
   if (lane == 0) P.gwords[gid] = cnt + 2u * (uint32_t)n;
 }
@@ -416,9 +453,9 @@ struct PackP {
   const int32_t *status;
 };
 
-// Workgroup b of a request copies group b, reversed, to its offset (256
-// words per pass, coalesced both ways); the request's workgroups also copy its
-// escape records, in strides.
+// Workgroup b of a request copies group b (the top W words of its slot) to
+// its offset (256 words per pass, coalesced both ways); the request's
+// workgroups also copy its escape records, in strides.
 __global__ __launch_bounds__(256) void k_pack(const Batch<PackP> B) {
   const int ri = batch_req(B, blockIdx.x);
   const PackP &P = B.r[ri];
@@ -430,9 +467,9 @@ __global__ __launch_bounds__(256) void k_pack(const Batch<PackP> B) {
   const int64_t gid = local;
   if (gid < P.n_groups) {
     const uint32_t W = P.gwords[gid];
-    const uint16_t *src = P.scratch + (size_t)gid * (kLanes * (kBlock + 2));
+    const uint16_t *src = P.scratch + (size_t)(gid + 1) * (kLanes * (kBlock + 2)) - W;
     uint16_t *dst = reinterpret_cast<uint16_t *>(P.stream + rans_off) + P.goffs[gid];
-    for (uint32_t k = threadIdx.x; k < W; k += blockDim.x) dst[k] = src[W - 1 - k];
+    for (uint32_t k = threadIdx.x; k < W; k += blockDim.x) dst[k] = src[k];
   }
   uint32_t *e = reinterpret_cast<uint32_t *>(P.stream + esc_off);
   for (uint32_t i = local * blockDim.x + threadIdx.x; i < n_esc; i += cnt * blockDim.x) {
@@ -571,7 +608,7 @@ __global__ __launch_bounds__(256) void k_parse(const Batch<ParseP> B) {
 // ---------------------------------------------------------------------------
 struct DecP {
   const uint32_t *tab;
-  const uint16_t *bucket;
+  const uint32_t *bucket;
   const uint8_t *stream;
   const uint8_t *ws;
   const uint32_t *esc_rows;  // [blocks][2]: index range of each block's escape records (from the parser)
@@ -580,6 +617,17 @@ struct DecP {
   int Ca, G;
   int32_t *status;
 };
+
+// The LDS address of a shared array, and a shared-memory object at an LDS
+// address.
+template <class T>
+__device__ __forceinline__ uint32_t lds_addr(T *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(3))) T *lds_at(uint32_t a) {
+  return (const __attribute__((address_space(3))) T *)(uintptr_t)a;
+}
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -596,31 +644,37 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int q) {
 // The symbols of one wave's rows: step i pops the symbol of row i from each
 // lane's state, then renormalises the lanes that need it with the next words
 // of the interleaved stream, in lane order.  The symbol of a slot comes from
-// its bucket: lo, or lo + 1 from the bucket's split offset on; only buckets of
+// its bucket: lo, or lo + 1 from the bucket's split slot on; only buckets of
 // three or more symbols take a binary search over the cumulative table (rare:
 // a wave enters it only while one of its lanes sits in such a bucket).
 // kPlain: every lane is a coded component and the block has no escapes, so no
 // lane is ever skipped; otherwise lane l of row 4 q + k is skipped when bit l
-// of lane q's esc[k] is set.  The word window is read modulo its size: a
-// valid stream never leaves it (it slides before it would), and a corrupt one
+// of lane q's esc[k] is set.  A step has no branch of its own: every lane
+// reads a word of the window and keeps it only if it renormalises.  The window
+// slides (before a quad) when the quad could read past it; it is read modulo
+// its size, so a corrupt stream reads words of the window, never past it, and
 // ends with ptr != W or a final state != L, which the caller reports.
-template <bool kPlain>
+template <bool kPlain, class Fill>
 __device__ __forceinline__ void decode_rows(uint32_t &x, uint32_t &ptr, uint32_t &base, uint32_t W, int Lb, int lane,
                                             bool lane_ok, bool has_esc, const uint64_t (&esc)[4],
-                                            const uint32_t *mytab, const uint16_t *mybkt, uint16_t *wb,
-                                            const uint16_t *wsrc, uint32_t *sout) {
+                                            const uint32_t *mytab, const uint32_t *mybkt, uint32_t bkt_lane, uint32_t wofs,
+                                            uint32_t *sout, Fill &&fill) {
   // emask: the row's escaped lanes (bit l set: lane l is skipped)
   auto step = [&](uint64_t emask) -> uint32_t {
     bool act = true;
     if (!kPlain) act = lane_ok && !((emask >> lane) & 1ull);
     const uint32_t slot = x & (kM - 1u);
-    const uint32_t bi = slot >> kBucketShift;
-    const uint32_t be = mybkt[bi * kLanes];
-    const uint32_t split = be >> 8;
-    uint32_t s = (be & 0xFFu) + ((slot & ((1u << kBucketShift) - 1u)) >= split ? 1u : 0u);
+    // bucket row (slot >> 7) of 256 bytes, this lane's word in it (the mask
+    // is kept apart from the shift-add, one instruction each)
+    uint32_t brow = x & 0x7F80u;
+    asm volatile("" : "+v"(brow));
+    const uint32_t be = *lds_at<uint32_t>((brow << 1) + bkt_lane);
+    const uint32_t split = be >> 16;
+    uint32_t s = (be & 0xFFu) + (slot >= split ? 1u : 0u);
     const bool srch = act && split == kSplitSearch;
-    if (__ballot(srch)) {
+    if (__builtin_expect(__ballot(srch) != 0ull, 0)) {
       // candidates lo .. the first symbol of the next bucket
+      const uint32_t bi = slot >> kBucketShift;
       uint32_t lo = s, hi = s;
       if (srch) hi = bi + 1 < (uint32_t)kBuckets ? (uint32_t)(mybkt[(bi + 1) * kLanes] & 0xFFu) : (uint32_t)(kNSym - 1);
       while (__ballot(lo < hi)) {
@@ -638,20 +692,13 @@ __device__ __forceinline__ void decode_rows(uint32_t &x, uint32_t &ptr, uint32_t
     x = act ? xd : x;
     const bool need = act && x < kL;
     const uint64_t mask = __ballot(need);
-    if (mask) {
-      const uint32_t cnt = (uint32_t)__popcll(mask);
-      if (ptr + cnt > base + kWordBuf && base + kWordBuf < W) {  // slide the window
-        base = ptr;
-        wave_sync_lds();
-        for (uint32_t k2 = lane; k2 < kWordBuf && base + k2 < W; k2 += 64) wb[k2] = wsrc[base + k2];
-        wave_sync_lds();
-      }
-      const uint32_t before = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-      const uint32_t wv = wb[(ptr - base + before) & (kWordBuf - 1u)];
-      x = need ? (x << 16) | wv : x;
-      ptr += cnt;
-    }
+    const uint32_t before = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+    // the word window is 2 KiB-aligned: its offset is ORed in
+    uint32_t wv = *lds_at<uint16_t>(((2u * (ptr - base) + 2u * before) & (2u * kWordBuf - 2u)) | wofs);
+    asm volatile("" : "+v"(wv));
+    x = need ? (x << 16) | wv : x;
+    ptr += (uint32_t)__popcll(mask);
     return act ? s : (uint32_t)kEsc;
   };
   // the escaped lanes of row 4 q + k (lane q's esc[k]; k is a constant at
@@ -659,9 +706,18 @@ __device__ __forceinline__ void decode_rows(uint32_t &x, uint32_t &ptr, uint32_t
   auto em = [&](int q, int k) -> uint64_t {
     return (!kPlain && has_esc) ? readlane64(esc[k], q) : 0ull;
   };
+  // a quad takes at most 4 * 64 words: slide the window to ptr first when
+  // they could reach past it (and the stream goes on past it)
+  auto slide = [&]() {
+    if (ptr + 4u * kLanes > base + kWordBuf && base + kWordBuf < W) {
+      base = ptr;
+      fill(base);
+    }
+  };
   const int nq = Lb >> 2;
 #pragma unroll 1
   for (int q = 0; q < nq; ++q) {
+    slide();
     uint32_t w = step(em(q, 0));
     w |= step(em(q, 1)) << 8;
     w |= step(em(q, 2)) << 16;
@@ -669,6 +725,7 @@ __device__ __forceinline__ void decode_rows(uint32_t &x, uint32_t &ptr, uint32_t
     if (kPlain || lane_ok) sout[(size_t)q * 64] = w;
   }
   if (Lb & 3) {  // the last, partial quad: rows past the block read as escapes
+    slide();
     uint32_t w = 0xFFFFFFFFu;
     if ((Lb & 3) > 0) w = (w & ~0xFFu) | step(em(nq, 0));
     if ((Lb & 3) > 1) w = (w & ~0xFF00u) | (step(em(nq, 1)) << 8);
@@ -687,35 +744,12 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(const Batch<DecP
   const int g = (int)(local / nch_w);
   const int chunk = (int)(local - (uint32_t)g * nch_w);
   __shared__ uint32_t tab[256 * kLanes];        // [symbol][lane]: f | cum << 16
-  __shared__ uint16_t bkt[kBuckets * kLanes];    // [bucket][lane]: lo | split << 8
-  __shared__ __attribute__((aligned(16))) uint16_t wbuf[kDecWaves][kWordBuf];
+  __shared__ uint32_t bkt[kBuckets * kLanes];    // [bucket][lane]: lo | split << 16
+  __shared__ __attribute__((aligned(2048))) uint16_t wbuf[kDecWaves][kWordBuf];
+  static_assert(kBuckets == 256, "bucket rows are staged like the tables");
   const int n = min(kLanes, P.Ca - kLanes * g);
   stage_tab<kDecWaves * 64>(tab, P.tab, g, n);
-  {
-    // bucket rows (512 bytes per component, two 16-byte pieces per thread),
-    // transposed like the tables; columns past n are zero
-    static_assert(kDecWaves * 64 * 2 * 16 == kLanes * kBuckets * 2, "two pieces per thread");
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(P.bucket + (size_t)kLanes * g * kBuckets);
-    u32x4 v[2];
-    // piece pc: buckets 8 (pc / 64) .. + 7 of component pc % 64
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int pc = threadIdx.x + i * kDecWaves * 64;
-      const int c = pc & 63, q = pc >> 6;
-      v[i] = c < n ? gload(src + c * 32 + q) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int pc = threadIdx.x + i * kDecWaves * 64;
-      uint16_t *d = bkt + (pc >> 6) * 8 * kLanes + (pc & 63);
-      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        d[(2 * j) * kLanes] = (uint16_t)(w[j] & 0xFFFFu);
-        d[(2 * j + 1) * kLanes] = (uint16_t)(w[j] >> 16);
-      }
-    }
-  }
+  stage_tab<kDecWaves * 64>(bkt, P.bucket, g, n);
   __syncthreads();
   if (*P.status != 0) return;
   // per-wave values are kept in scalar registers: the step loop is uniform,
@@ -737,6 +771,20 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(const Batch<DecP
     if (lane == 0) set_status(P.status, DCKV_ECORRUPT);
     return;
   }
+  // the group's words through a buffer resource of W words: loads past the
+  // end return zero, so a window fill issues all its loads at once
+  const rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(wsrc), (short)0, (int)(2u * W),
+                                                      0x00020000);
+  auto fill = [&](uint32_t from) {
+    uint16_t v[kWordBuf / 64];
+    wave_sync_lds();
+#pragma unroll
+    for (int i = 0; i < kWordBuf / 64; ++i)
+      v[i] = __builtin_amdgcn_raw_buffer_load_b16(wr, (int)(2u * (from + (uint32_t)lane + 64u * i)), 0, 0);
+#pragma unroll
+    for (int i = 0; i < kWordBuf / 64; ++i) wb[lane + 64 * i] = v[i];
+    wave_sync_lds();
+  };
   // escape positions of this group: a bitmap of the block's 256 rows, built
   // in the word buffer (2 KiB) and then held in registers, rows 4 l .. 4 l + 3
   // by lane l
@@ -763,36 +811,24 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(const Batch<DecP
       wave_sync_lds();
 #pragma unroll
       for (int k = 0; k < 4; ++k) esc[k] = eb[4 * lane + k];
-      wave_sync_lds();
     }
   }
-  // word window [base, base + kWordBuf); the first window's loads are all
-  // issued before the first LDS write
+  // word window [base, base + kWordBuf)
   uint32_t base = 0;
-  {
-    uint16_t v[kWordBuf / 64];
-#pragma unroll
-    for (int i = 0; i < kWordBuf / 64; ++i) {
-      const uint32_t k = (uint32_t)lane + 64u * i;
-      if (k < W) v[i] = gload(wsrc + k);
-    }
-#pragma unroll
-    for (int i = 0; i < kWordBuf / 64; ++i) {
-      const uint32_t k = (uint32_t)lane + 64u * i;
-      if (k < W) wb[k] = v[i];
-    }
-  }
-  wave_sync_lds();
+  fill(0);
   uint32_t x = kL;
   if (lane_ok) x = (uint32_t)wb[2 * lane] | ((uint32_t)wb[2 * lane + 1] << 16);
   uint32_t ptr = 2u * (uint32_t)n;
   const uint32_t *mytab = tab + lane;
-  const uint16_t *mybkt = bkt + lane;
+  const uint32_t *mybkt = bkt + lane;
+  const uint32_t bkt_lane = lds_addr(mybkt);
   uint32_t *sout = P.sym32 + ((size_t)g * (P.N256 / 4) + (size_t)b * 64) * 64 + lane;
+  uint32_t wofs = lds_addr(wb);
+  asm volatile("" : "+v"(wofs));  // in a VGPR: a window address is then one and-or
   if (!has_esc && n == kLanes)
-    decode_rows<true>(x, ptr, base, W, Lb, lane, true, false, esc, mytab, mybkt, wb, wsrc, sout);
+    decode_rows<true>(x, ptr, base, W, Lb, lane, true, false, esc, mytab, mybkt, bkt_lane, wofs, sout, fill);
   else
-    decode_rows<false>(x, ptr, base, W, Lb, lane, lane_ok, has_esc, esc, mytab, mybkt, wb, wsrc, sout);
+    decode_rows<false>(x, ptr, base, W, Lb, lane, lane_ok, has_esc, esc, mytab, mybkt, bkt_lane, wofs, sout, fill);
   const bool lane_bad = lane_ok && x != kL;
   if (__ballot(lane_bad) != 0ull || ptr != W) {
     if (lane == 0) set_status(P.status, DCKV_ECORRUPT);
