@@ -73,15 +73,13 @@ int batch_error(int rc, int32_t i, const char *what) {
   return set_error(rc, msg);
 }
 
-// The big transform GEMMs (analysis, synthesis) run per request: each launch
-// fills the chip on its own.  Every other stage runs over all n requests at
-// once, so the small kernels of short requests share their launches.
+// Every stage runs over all n requests at once: one launch sequence per
+// batch (up to kLaunchBatch requests per launch), so the tiles and groups of
+// all requests share each launch and its load balance.
 void encode_sequence(const EncodeArgs *a, int n) {
   launch_start_encode(a, n);
-  for (int i = 0; i < n; ++i) {
-    launch_analysis_gemm(a[i]);
-    launch_encode_fixup(a[i]);
-  }
+  launch_analysis_gemm(a, n);
+  launch_encode_fixup(a, n);
   launch_rans_encode(a, n);
   launch_scan_header(a, n);
   launch_pack(a, n);
@@ -104,7 +102,7 @@ void decode_sequence(const DecodeArgs *a, int n) {
   launch_rans_decode(a, n);
   launch_dequant(a, n);
   launch_w1_gemm(a, n);  // also RoPE on the kept rows
-  for (int i = 0; i < n; ++i) launch_synthesis_gemm(a[i]);
+  launch_synthesis_gemm(a, n);
 }
 
 // Workspace slices of a batch: request i at offsets[i], each 256-byte aligned

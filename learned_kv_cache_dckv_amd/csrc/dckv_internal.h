@@ -335,11 +335,11 @@ struct RateBwdArgs {
   hipStream_t s;
 };
 void rate_bwd_sequence(const RateBwdArgs &a);
-void launch_analysis_gemm(const EncodeArgs &a);
-void launch_encode_fixup(const EncodeArgs &a);
+void launch_analysis_gemm(const EncodeArgs *a, int n);
+void launch_encode_fixup(const EncodeArgs *a, int n);
 void launch_dequant(const DecodeArgs *a, int n);
 void launch_w1_gemm(const DecodeArgs *a, int n);
-void launch_synthesis_gemm(const DecodeArgs &a);
+void launch_synthesis_gemm(const DecodeArgs *a, int n);
 
 
 }  // namespace dckv

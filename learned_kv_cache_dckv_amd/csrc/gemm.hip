@@ -512,13 +512,20 @@ __device__ __forceinline__ uint32_t pack_u8x4(float a, float b, float c, float d
   return __builtin_amdgcn_cvt_pk_u8_f32(d, 3, w);
 }
 
-// kKeys: the key heads come from P.keys (encode of a post-RoPE cache)
+// kKeys: the key heads come from P.keys (encode of a post-RoPE cache).  One
+// launch covers the tiles of up to kLaunchBatch requests; a request's tile
+// count is padded to a multiple of 8 so that its tiles keep the XCD order of
+// tile_of() (the padding workgroups return at once).
 template <bool kKeys>
-__global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
+__global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(const Batch<QuantP> Bt) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int ri = batch_req(Bt, blockIdx.x);
+  const QuantP &P = Bt.r[ri];
+  const int local = (int)(blockIdx.x - Bt.start[ri]);
+  if (local >= P.n_mt * P.n_nt) return;
   if (wg_stop(P.status)) return;
   int mt, nt;
-  tile_of(blockIdx.x, P.n_mt * P.n_nt, P.n_nt, mt, nt);
+  tile_of(local, P.n_mt * P.n_nt, P.n_nt, mt, nt);
   const int64_t m0 = (int64_t)mt * kBM;
   const int n0 = nt * kBN;
   Operand A, B;
@@ -785,9 +792,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_analysis_quant(QuantP P) {
 
 
 // last odd row of every row tile whose right neighbour is in the next tile
-__global__ void k_encode_fixup(QuantP P, int64_t n_fix) {
+__global__ void k_encode_fixup(const Batch<QuantP> Bt) {
+  const int ri = batch_req(Bt, blockIdx.x);
+  const QuantP &P = Bt.r[ri];
   if (*P.status != 0) return;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n_fix = (P.N - 1) / kBM;  // tiles t with (t + 1) BM < N
+  const int64_t i = (int64_t)(blockIdx.x - Bt.start[ri]) * blockDim.x + threadIdx.x;
   if (i >= n_fix * P.Ca) return;
   const int64_t mt = i / P.Ca;
   const int r = (int)(i - mt * P.Ca);
@@ -1147,15 +1157,17 @@ constexpr int kSynPeel = kSynDefer / 8;    // k-tiles that store them, 8 each
 static_assert(kC / kBK >= kSynPeel, "synthesis main loop shorter than the store spread");
 
 // KT: k-tiles, 36 with the correction, 32 for the linear codec; kHeads: the
-// per-layer head matrices as the output
+// per-layer head matrices as the output.  The tiles of up to kLaunchBatch
+// requests form one sequence (each request's count padded to a multiple of 8,
+// which keeps tile_of()'s XCD order); a tile of a request whose status is set
+// is skipped, and the words held over from the tile before are still stored.
 template <int KT, bool kHeads>
-__global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
+__global__ __launch_bounds__(kThreads, 1) void k_synthesis(const Batch<SynP> Bt) {
   constexpr int kLd = kHeads ? kHeadDim : kD;
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  if (wg_stop(P.status)) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int total = P.n_mt * P.n_nt;
+  const int total = (int)Bt.start[Bt.n];
   uint32_t pend[kSynDefer];
   rsrc_t pr;          // the tile of the words
   uint32_t lb = 0u, sel = 0u;
@@ -1172,8 +1184,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_synthesis(SynP P) {
   };
 #pragma unroll 1
   for (int t = blockIdx.x; t < total; t += gridDim.x) {
+    const int ri = batch_req(Bt, (uint32_t)t);
+    const SynP &P = Bt.r[ri];
+    const int local = t - (int)Bt.start[ri];
+    if (local >= P.n_mt * P.n_nt || wg_stop(P.status)) continue;
     int mt, nt;
-    tile_of(t, total, P.n_nt, mt, nt);
+    tile_of(local, P.n_mt * P.n_nt, P.n_nt, mt, nt);
     const int64_t m0 = (int64_t)mt * kBM;
     const int head = nt;
     Operand A, B;
@@ -1362,23 +1378,42 @@ static QuantP quant_params(const EncodeArgs &a) {
   return P;
 }
 
-void launch_analysis_gemm(const EncodeArgs &a) {
-  if (a.g.N == 0 || a.p->C_a == 0) return;
-  QuantP P = quant_params(a);
-  if (P.keys)
-    launch_gemm(k_analysis_quant<true>, "analysis_gemm", P.n_mt * P.n_nt, P, a.s);
-  else
-    launch_gemm(k_analysis_quant<false>, "analysis_gemm", P.n_mt * P.n_nt, P, a.s);
+// a launch's parameters stay within the 4 KiB of kernel arguments
+static_assert(sizeof(Batch<QuantP>) <= 4096 && sizeof(Batch<SynP>) <= 4096, "kernel argument size");
+
+// tiles of one request's GEMM, padded to a multiple of 8 (see k_analysis_quant)
+static uint32_t padded_tiles(int64_t n_mt, int64_t n_nt) { return (uint32_t)((n_mt * n_nt + 7) / 8 * 8); }
+
+void launch_analysis_gemm(const EncodeArgs *args, int n) {
+  // requests with a key copy (post-RoPE encode) take the other variant
+  for (int keys = 0; keys < 2; ++keys) {
+    std::vector<int> idx;
+    for (int i = 0; i < n; ++i)
+      if ((args[i].keys != nullptr) == (keys == 1) && args[i].g.N > 0 && args[i].p->C_a > 0) idx.push_back(i);
+    if (idx.empty()) continue;
+    auto fill = [&](int k) { return quant_params(args[idx[k]]); };
+    auto count = [&](int k) {
+      const QuantP P = quant_params(args[idx[k]]);
+      return padded_tiles(P.n_mt, P.n_nt);
+    };
+    if (keys)
+      launch_batched<QuantP>(k_analysis_quant<true>, "analysis_gemm", (int)idx.size(), args[0].s, kThreads, fill,
+                             count, kLdsBytes);
+    else
+      launch_batched<QuantP>(k_analysis_quant<false>, "analysis_gemm", (int)idx.size(), args[0].s, kThreads, fill,
+                             count, kLdsBytes);
+  }
 }
 
-void launch_encode_fixup(const EncodeArgs &a) {
-  if (a.g.N == 0 || a.p->C_a == 0) return;
-  const int64_t n_fix = (a.g.N - 1) / kBM;  // tiles t with (t+1)*BM < N
-  if (n_fix <= 0) return;
-  QuantP P = quant_params(a);
-  const int64_t work = n_fix * a.p->C_a;
-  KernelTimer tm("fixup", a.s);
-  hipLaunchKernelGGL(k_encode_fixup, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, a.s, P, n_fix);
+void launch_encode_fixup(const EncodeArgs *args, int n) {
+  auto fill = [&](int i) { return quant_params(args[i]); };
+  auto count = [&](int i) {
+    const EncodeArgs &a = args[i];
+    if (a.g.N == 0 || a.p->C_a == 0) return 0u;
+    const int64_t n_fix = (a.g.N - 1) / kBM;  // tiles t with (t+1)*BM < N
+    return n_fix <= 0 ? 0u : (uint32_t)((n_fix * a.p->C_a + 255) / 256);
+  };
+  launch_batched<QuantP>(k_encode_fixup, "fixup", n, args[0].s, 256, fill, count);
 }
 
 void launch_dequant(const DecodeArgs *args, int n) {
@@ -1459,8 +1494,7 @@ void launch_w1_gemm(const DecodeArgs *args, int n) {
   launch_batched<W1P, kW1Batch>(k_w1_gelu, "w1_gelu", n, args[0].s, 256, fill, gelu_count);
 }
 
-void launch_synthesis_gemm(const DecodeArgs &a) {
-  if (a.g.N == 0) return;
+static SynP syn_params(const DecodeArgs &a) {
   SynP P;
   P.yhat_b = reinterpret_cast<const uint16_t *>(a.ws + a.l.yhat_b);
   P.h_b = reinterpret_cast<const uint16_t *>(a.ws + a.l.h_b);
@@ -1474,28 +1508,52 @@ void launch_synthesis_gemm(const DecodeArgs &a) {
   P.n_mt = (int)a.g.n_mtiles;
   P.n_nt = kD / kBN;
   P.status = a.status;
+  return P;
+}
+
+void launch_synthesis_gemm(const DecodeArgs *args, int n) {
   // persistent: one workgroup per CU at most
   static int n_cu = 0;
   if (n_cu == 0) {
-    int dev = 0, n = 0;
+    int dev = 0, c = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      n_cu = n;
+        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+      n_cu = c;
     else
       n_cu = 256;
   }
-  const int grid = std::min(P.n_mt * P.n_nt, n_cu);
   constexpr int kFull = (kC + kHid) / kBK, kLin = kC / kBK;
-  if (a.heads) {
-    if (a.p->W1)
-      launch_gemm(k_synthesis<kFull, true>, "synthesis_gemm", grid, P, a.s);
-    else
-      launch_gemm(k_synthesis<kLin, true>, "synthesis_gemm", grid, P, a.s);
-  } else {
-    if (a.p->W1)
-      launch_gemm(k_synthesis<kFull, false>, "synthesis_gemm", grid, P, a.s);
-    else
-      launch_gemm(k_synthesis<kLin, false>, "synthesis_gemm", grid, P, a.s);
+  // one sequence of launches per kernel variant: correction or linear codec,
+  // rows or head matrices
+  for (int var = 0; var < 4; ++var) {
+    const bool lin = var & 1, heads = var >> 1;
+    std::vector<int> idx;
+    for (int i = 0; i < n; ++i)
+      if (args[i].g.N > 0 && (args[i].p->W1 == nullptr) == lin && (args[i].heads != nullptr) == heads)
+        idx.push_back(i);
+    for (size_t i0 = 0; i0 < idx.size(); i0 += kLaunchBatch) {
+      Batch<SynP> B{};
+      B.n = (int)std::min<size_t>(kLaunchBatch, idx.size() - i0);
+      uint32_t w = 0;
+      for (int r = 0; r < B.n; ++r) {
+        B.start[r] = w;
+        B.r[r] = syn_params(args[idx[i0 + r]]);
+        w += padded_tiles(B.r[r].n_mt, B.r[r].n_nt);
+      }
+      for (int r = B.n; r <= kLaunchBatch; ++r) B.start[r] = w;
+      const int grid = std::min<int>((int)w, n_cu);
+      if (heads) {
+        if (lin)
+          launch_gemm(k_synthesis<kLin, true>, "synthesis_gemm", grid, B, args[0].s);
+        else
+          launch_gemm(k_synthesis<kFull, true>, "synthesis_gemm", grid, B, args[0].s);
+      } else {
+        if (lin)
+          launch_gemm(k_synthesis<kLin, false>, "synthesis_gemm", grid, B, args[0].s);
+        else
+          launch_gemm(k_synthesis<kFull, false>, "synthesis_gemm", grid, B, args[0].s);
+      }
+    }
   }
 }
 
