@@ -119,17 +119,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Unblocked Cholesky of diagonal block k (lower, in place; the block's upper
 // triangle is zeroed, so later kernels read it as L_kk), then its inverse
 // Linv (lower) into linv.  One wave; lane r holds row r of the block in
-// registers.  Column c: the pivot p comes from lane c, 1 / sqrt(p) from one
-// reciprocal square root (L[c][c] = p / sqrt(p)), every lane below c scales
-// its entry, and the column goes through LDS (col[c][s] = L[s][c] below the
-// diagonal, 0 elsewhere) so that each lane subtracts L[r][c] L[s][c] from
-// its entries s > c with broadcast reads (all lanes read one address).  Linv
-// is then built one column per lane by a column sweep over L: y[j] /= L[j][j],
-// then y[i] -= L[i][j] y[j] for i > j, reading L's columns from the same LDS
-// rows; its steps are independent across i, so no long dependent chain forms.
-// (A version with the block in LDS and rolled column loops, a few hundred
-// instructions long, measured slower: its per-column LDS round trips are
-// serial.)  A pivot below 1e-6 of its diagonal entry before the
+// registers (by symmetry also column r).  Column c: the pivot p comes from
+// lane c and each lane r > c updates its entries s > c by
+// A[r][s] -= (A[r][c] / p) A[s][c], with column c read back from LDS as
+// broadcasts one step ahead; then column c is scaled by 1 / sqrt(p) (one
+// reciprocal square root; L[c][c] = p / sqrt(p)).  L then
+// goes to LDS once (col[c][i] = L[i][c]) and Linv is built one column per
+// lane by a column sweep over L: y[j] /= L[j][j], then y[i] -= L[i][j] y[j]
+// for i > j, with L's column j read as 16-byte broadcasts (all lanes read one
+// address).  A pivot below 1e-6 of its diagonal entry before the
 // factorisation sets EINVAL: the Gram matrix plus ridge is not positive
 // definite in fp32 (e.g. a zero ridge with fewer rows than dimensions).
 __global__ __launch_bounds__(64) void k_chol_diag(float *G, int k, const float *dg, float *linv, int32_t *status) {
@@ -148,40 +146,83 @@ __global__ __launch_bounds__(64) void k_chol_diag(float *G, int k, const float *
   const float dgr = dg[k * kNB + r];
   bool bad = false;
   float dinv = 0.f;  // lane r: 1 / L[r][r]
-#pragma unroll
-  for (int c = 0; c < kNB; ++c) {
-    const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[c]), c));
-    const float dgc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dgr), c));
-    bad = bad || !(piv > 1e-6f * dgc) || !isfinite(piv);
-    const float pc = fmaxf(piv, 1e-30f);
-    const float rd = __builtin_amdgcn_rsqf(pc);
-    if (r == c) dinv = rd;
-    // rows above c hold upper-triangle values: set to 0, zeroed in the output
-    x[c] = r == c ? pc * rd : (r > c ? x[c] * rd : 0.f);
-    col[c][r] = r > c ? x[c] : 0.f;
-    wave_lds_sync();
-#pragma unroll
-    for (int s = c + 1; s < kNB; ++s) x[s] -= x[c] * col[c][s];
+  auto bcast = [](float v, int lane) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane)); };
+  // column c of the partly factorised block goes through LDS (col[c][s] =
+  // A[s][c], written by lane s) and comes back as 16-byte broadcasts; a
+  // wave's LDS accesses complete in order, so a read after a write sees it.
+  // Column c + 1 is updated and written first in step c and its reads are
+  // issued before the rest of step c's updates, which hide their latency.
+  float cv[kNB], nv[kNB];
+  // pieces from q0 on (the entries before are not needed)
+#define DCKV_READ_COL(c, v, q0)                                                      \
+  _Pragma("unroll") for (int q = (q0); q < kNB / 4; ++q) {                          \
+    const float4 t = *reinterpret_cast<const float4 *>(&col[(c)][4 * q]);            \
+    v[4 * q] = t.x;                                                                  \
+    v[4 * q + 1] = t.y;                                                              \
+    v[4 * q + 2] = t.z;                                                              \
+    v[4 * q + 3] = t.w;                                                              \
   }
+  // step c with column c in cur; column c + 1 is read into nxt.  Steps go in
+  // pairs so that the two buffers swap roles without copies.
+#define DCKV_FACTOR_STEP(c, cur, nxt)                                               \
+  {                                                                                \
+    const float piv = bcast(x[(c)], (c));                                          \
+    const float dgc = bcast(dgr, (c));                                             \
+    bad = bad || !(piv > 1e-6f * dgc) || !isfinite(piv);                           \
+    const float pc = fmaxf(piv, 1e-30f);                                           \
+    const float rd = __builtin_amdgcn_rsqf(pc);                                    \
+    const float l2 = r > (c) ? x[(c)] * (rd * rd) : 0.f;                           \
+    if ((c) + 1 < kNB) {                                                           \
+      x[(c) + 1] = fmaf(-l2, cur[(c) + 1], x[(c) + 1]);                            \
+      col[(c) + 1][r] = x[(c) + 1];                                                \
+      DCKV_READ_COL((c) + 1, nxt, ((c) + 2) / 4)                                   \
+    }                                                                              \
+    __builtin_amdgcn_sched_barrier(0);                                             \
+    _Pragma("unroll") for (int s2 = (c) + 2; s2 < kNB; ++s2) x[s2] = fmaf(-l2, cur[s2], x[s2]); \
+    if (r == (c)) dinv = rd;                                                       \
+    x[(c)] = r == (c) ? pc * rd : (r > (c) ? x[(c)] * rd : 0.f);                   \
+  }
+  // A[r][s] -= (A[r][c] / p) A[s][c] for s > c; lanes at or above c leave
+  // their row alone; rows above c hold upper-triangle values: set to 0,
+  // zeroed in the output
+  col[0][r] = x[0];
+  DCKV_READ_COL(0, cv, 0)
+#pragma unroll
+  for (int c = 0; c < kNB; c += 2) {
+    DCKV_FACTOR_STEP(c, cv, nv)
+    DCKV_FACTOR_STEP(c + 1, nv, cv)
+  }
+#undef DCKV_FACTOR_STEP
 #pragma unroll
   for (int q = 0; q < kNB / 4; ++q) {
-    float4 v;
-    v.x = 4 * q <= r ? x[4 * q] : 0.f;
-    v.y = 4 * q + 1 <= r ? x[4 * q + 1] : 0.f;
-    v.z = 4 * q + 2 <= r ? x[4 * q + 2] : 0.f;
-    v.w = 4 * q + 3 <= r ? x[4 * q + 3] : 0.f;
+    const float4 v = {x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
     *reinterpret_cast<float4 *>(blk + (size_t)r * kEmb + 4 * q) = v;
   }
-  // Linv column r: L y = e_r (entries above r stay 0)
+  // L to LDS, transposed: col[c][r] = L[r][c] (0 above the diagonal)
+#pragma unroll
+  for (int c = 0; c < kNB; ++c) col[c][r] = c == r ? 0.f : x[c];
+  wave_lds_sync();
+  // Linv column r: L y = e_r (entries above r stay 0).  Column j of L (row j
+  // of col) is read by all lanes at once, in 16-byte pieces, one column ahead
+  // of its use, so the reads never wait on the sweep.
   float y[kNB];
 #pragma unroll
   for (int i = 0; i < kNB; ++i) y[i] = i == r ? 1.f : 0.f;
-#pragma unroll
-  for (int j = 0; j < kNB; ++j) {
-    y[j] *= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dinv), j));
-#pragma unroll
-    for (int i = j + 1; i < kNB; ++i) y[i] -= col[j][i] * y[j];
+#define DCKV_SWEEP_STEP(j, cur, nxt)                                               \
+  {                                                                                \
+    if ((j) + 1 < kNB) DCKV_READ_COL((j) + 1, nxt, ((j) + 2) / 4)                  \
+    __builtin_amdgcn_sched_barrier(0);                                             \
+    y[(j)] *= bcast(dinv, (j));                                                    \
+    _Pragma("unroll") for (int i = (j) + 1; i < kNB; ++i) y[i] = fmaf(-cur[i], y[(j)], y[i]); \
   }
+  DCKV_READ_COL(0, cv, 0)
+#pragma unroll
+  for (int j = 0; j < kNB; j += 2) {
+    DCKV_SWEEP_STEP(j, cv, nv)
+    DCKV_SWEEP_STEP(j + 1, nv, cv)
+  }
+#undef DCKV_SWEEP_STEP
+#undef DCKV_READ_COL
   float *lv = linv + (size_t)k * kNB * kNB;
 #pragma unroll
   for (int i = 0; i < kNB; ++i) lv[i * kNB + r] = y[i];

@@ -1035,7 +1035,8 @@ struct W1P {
 // 256-row tiles times 2 halves fill twice as many CUs as whole-K tiles; the
 // halves are added (one fp32 addition, so the order does not matter) by
 // k_w1_gelu.
-constexpr int kW1Batch = 8;  // requests per launch of the W1 kernels (their parameters are large)
+constexpr int kW1Batch = kLaunchBatch;  // requests per launch of the W1 kernels
+static_assert(sizeof(Batch<W1P, kW1Batch>) <= 4096, "kernel argument size");
 
 __global__ __launch_bounds__(kThreads, 1) void k_w1(const Batch<W1P, kW1Batch> Bt) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
