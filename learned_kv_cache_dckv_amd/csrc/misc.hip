@@ -94,25 +94,47 @@ __global__ __launch_bounds__(256) void k_unrope(const uint16_t *in, uint16_t *ou
 // The same inverse rotation of the key heads only, into the key copy
 // kc [T][6 * 2 * head_dim] (layer l, head h at columns (l * 2 + h) * head_dim):
 // half the traffic of a whole-row pass; the value heads are read from the
-// caller's rows where they are.
+// caller's rows where they are.  Thread (row t, group g) takes frequencies
+// 8 g .. 8 g + 7 of every key head: one angle computation per frequency for
+// all 12 heads, and 16-byte loads and stores.  Same fp64 arithmetic as
+// k_unrope, so the copy's keys equal its output bit for bit.
 __global__ __launch_bounds__(256) void k_unrope_keys(const uint16_t *in, uint16_t *kc, int64_t T,
                                                      const double *omega) {
-  const int64_t t = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
-  const int d = threadIdx.x & 127;
+  const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int g = threadIdx.x & 15;
   if (t >= T) return;
-  double sn, cs;
-  sincos((double)t * omega[d], &sn, &cs);
+  double cs[8], sn[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sincos((double)t * omega[8 * g + e], &sn[e], &cs[e]);
   const uint16_t *src = in + (size_t)t * kD;
   uint16_t *dst = kc + (size_t)t * kKeyCols;
+  auto lanes = [](const uint4 &v, int e) -> uint32_t {
+    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+    return (e & 1) ? w >> 16 : w & 0xFFFFu;
+  };
 #pragma unroll
   for (int l = 0; l < 6; ++l)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int kb = (l * 4 + h) * kHeadDim, ob = (l * 2 + h) * kHeadDim;
-      const double p0 = (double)__uint_as_float((uint32_t)src[kb + d] << 16);
-      const double p1 = (double)__uint_as_float((uint32_t)src[kb + d + kHalf] << 16);
-      dst[ob + d] = bf16_of_f64(__dadd_rn(__dmul_rn(p0, cs), __dmul_rn(p1, sn)));
-      dst[ob + d + kHalf] = bf16_of_f64(__dsub_rn(__dmul_rn(p1, cs), __dmul_rn(p0, sn)));
+      const int kb = (l * 4 + h) * kHeadDim + 8 * g, ob = (l * 2 + h) * kHeadDim + 8 * g;
+      const uint4 a = *reinterpret_cast<const uint4 *>(src + kb);
+      const uint4 b = *reinterpret_cast<const uint4 *>(src + kb + kHalf);
+      uint32_t o0[4], o1[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        uint32_t r0[2], r1[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const double p0 = (double)__uint_as_float(lanes(a, e + u) << 16);
+          const double p1 = (double)__uint_as_float(lanes(b, e + u) << 16);
+          r0[u] = bf16_of_f64(__dadd_rn(__dmul_rn(p0, cs[e + u]), __dmul_rn(p1, sn[e + u])));
+          r1[u] = bf16_of_f64(__dsub_rn(__dmul_rn(p1, cs[e + u]), __dmul_rn(p0, sn[e + u])));
+        }
+        o0[e / 2] = r0[0] | (r0[1] << 16);
+        o1[e / 2] = r1[0] | (r1[1] << 16);
+      }
+      *reinterpret_cast<uint4 *>(dst + ob) = uint4{o0[0], o0[1], o0[2], o0[3]};
+      *reinterpret_cast<uint4 *>(dst + ob + kHalf) = uint4{o1[0], o1[1], o1[2], o1[3]};
     }
 }
 }  // namespace
@@ -140,7 +162,7 @@ void launch_start_encode(const EncodeArgs *args, int n) {
 void launch_unrope_keys(const dckv_plan_t *p, const uint16_t *in, uint16_t *kc, int64_t T, hipStream_t s) {
   if (T <= 0) return;
   KernelTimer tm("unrope_keys", s);
-  hipLaunchKernelGGL(k_unrope_keys, dim3((unsigned)((T + 1) / 2)), dim3(256), 0, s, in, kc, T, p->dev.omega);
+  hipLaunchKernelGGL(k_unrope_keys, dim3((unsigned)((T + 15) / 16)), dim3(256), 0, s, in, kc, T, p->dev.omega);
 }
 
 void launch_unrope(const dckv_plan_t *p, const uint16_t *in, uint16_t *out, int64_t T, hipStream_t s) {
