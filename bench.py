@@ -472,6 +472,84 @@ def unrope_bench(cfg: int, steps: int) -> int:
     return 0
 
 
+def paged_bench(cfg: int, steps: int, block_size: int) -> int:
+    """Encode from and decode into a paged attention cache (per-layer key and
+    value pools of block_size positions, the request's blocks shuffled in a
+    pool with spare blocks), against the contiguous calls on the same rows:
+    dckv_encode vs dckv_encode_paged (pre-RoPE and post-RoPE keys) and
+    dckv_decode vs dckv_decode_paged.  The paged calls move the request's
+    rows once more (a gather before the encode, a scatter after the decode)."""
+    import torch
+    import dckv_synth as synth
+    import learned_kv_cache_dckv_amd as dk
+    dev = torch.device("cuda:0")
+    req = synth.make_request(cfg)
+    T = req.T
+    codec = dk.Codec(synth.world().params(), device=dev)
+    plan = codec.plan(req.step_scale)
+    src = torch.from_numpy(req.rows.view(np.int16)).to(dev)
+    tok = torch.from_numpy(req.token_ids.astype(np.int32)).to(dev)
+    n_log = (T + block_size - 1) // block_size
+    n_blocks = n_log + 64
+    table_np = np.random.default_rng(7).permutation(n_blocks)[:n_log].astype(np.int32)
+    table = torch.from_numpy(table_np).to(dev)
+    t = np.arange(T)
+    phys = torch.from_numpy(table_np[t // block_size].astype(np.int64) * block_size + t % block_size).to(dev)
+    max_bytes, ws_bytes = plan.bytes(T)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_paged = torch.empty(dk.dckv_bytes_paged(plan, T), dtype=torch.uint8, device=dev)
+    buf = torch.empty(max_bytes, dtype=torch.uint8, device=dev)
+    nb = torch.zeros(1, dtype=torch.int64, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    rows_out = torch.empty_like(src)
+
+    def pools_of(rows):
+        pools = [torch.zeros((n_blocks * block_size, 2, 256), dtype=torch.int16, device=dev) for _ in range(12)]
+        r = rows.view(T, 12, 2, 256)
+        for i in range(12):
+            pools[i][phys] = r[:, i]
+        return [p.view(n_blocks, block_size, 2, 256) for p in pools]
+
+    dk.dckv_encode(plan, src, tok, buf, nb, st, ws)
+    torch.cuda.synchronize()
+    n_bytes = int(nb.item())
+    dk.dckv_decode(plan, buf, n_bytes, tok, rows_out, st, ws)
+    torch.cuda.synchronize()
+    pre_cache = dk.PagedKV(pools_of(src), table, block_size)
+    post_cache = dk.PagedKV(pools_of(rows_out), table, block_size)
+    out_cache = dk.PagedKV([torch.zeros_like(p) for p in pre_cache.pools], table, block_size)
+    stream_buf = buf.clone()
+    s = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        for _ in range(steps):
+            fn()
+        b.record(s)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    enc_ms = timed(lambda: dk.dckv_encode(plan, src, tok, buf, nb, st, ws))
+    enc_paged_ms = timed(lambda: dk.dckv_encode_paged(plan, pre_cache, False, tok, buf, nb, st, ws_paged))
+    assert int(st.item()) == 0 and int(nb.item()) == n_bytes
+    enc_paged_post_ms = timed(lambda: dk.dckv_encode_paged(plan, post_cache, True, tok, buf, nb, st, ws_paged))
+    assert int(st.item()) == 0
+    dec_ms = timed(lambda: dk.dckv_decode(plan, stream_buf, n_bytes, tok, rows_out, st, ws))
+    dec_paged_ms = timed(lambda: dk.dckv_decode_paged(plan, stream_buf, n_bytes, tok, out_cache, st, ws_paged))
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    print(json.dumps({"metric": "paged attention cache on either side of the codec (ms per call)",
+                      "workload": req.note, "T": T, "block_size": block_size, "n_blocks": n_blocks,
+                      "encode_ms": enc_ms, "encode_paged_ms": enc_paged_ms,
+                      "encode_paged_postrope_ms": enc_paged_post_ms, "decode_ms": dec_ms,
+                      "decode_paged_ms": dec_paged_ms, "encode_paged_over_encode": enc_paged_ms / enc_ms,
+                      "decode_paged_over_decode": dec_paged_ms / dec_ms}))
+    return 0
+
+
 def vendor_gemm(N: int, steps: int) -> int:
     """The vendor library's plain bf16 GEMMs (torch.matmul: hipBLASLt) on the
     codec's GEMM shapes, for comparison with the fused kernels' main loops.
@@ -523,6 +601,9 @@ def main(argv=None) -> int:
                     help="time the inverse RoPE over the workload's rows, then exit")
     ap.add_argument("--layout", choices=("rows", "heads"), default="rows",
                     help="heads: decode into the per-layer [n_kv_heads][T][head_dim] matrices")
+    ap.add_argument("--paged", type=int, default=0, metavar="BLOCK_SIZE",
+                    help="time the encode from and the decode into a paged attention cache of this block size, "
+                         "then exit")
     ap.add_argument("--training-rate", action="store_true",
                     help="time the training rate and its gradients on the workload (default: the 4,096-token "
                          "prompt), then exit")
@@ -535,6 +616,8 @@ def main(argv=None) -> int:
         return vendor_gemm(T - 132, args.steps)
     if args.unrope:
         return unrope_bench(args.config, args.steps)
+    if args.paged:
+        return paged_bench(args.config, args.steps, args.paged)
     if args.fit:
         return fit_bench(args.config, args.fit, args.steps, not args.no_cpu_baseline)
     if args.training_rate:

@@ -42,9 +42,10 @@
  *
  * Entry points, in the order below: plan (tables, creation, inspection,
  * mean table); sizing; encode; decode (rows, or the per-layer head
- * matrices); inverse RoPE of a post-RoPE cache; batches; the lossless stage
- * alone; workspace views and kernel timing; the closed-form fit of the
- * conditional models; the training rate and its gradients.
+ * matrices); inverse RoPE of a post-RoPE cache; a paged attention cache on
+ * either side; batches; the lossless stage alone; workspace views and kernel
+ * timing; the closed-form fit of the conditional models; the training rate and
+ * its gradients.
  */
 #ifndef DCKV_H
 #define DCKV_H
@@ -267,6 +268,49 @@ int dckv_encode_postrope(const dckv_plan_t *plan, const uint16_t *rows, const in
                          int32_t *status, void *workspace, uint64_t workspace_bytes, void *hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * A paged attention cache on either side of the codec (DCKV digest, "How it
+ * works", first paragraph: the codec takes the keys before RoPE and reapplies
+ * it after decoding; abstract page: the cache is stored or moved to reuse it).
+ * Serving engines keep the cache in fixed-size blocks: per layer l a key pool
+ * kv[2 l] and a value pool kv[2 l + 1], each bf16
+ * [n_blocks][block_size][n_kv_heads][head_dim] (16-byte aligned, device), and
+ * one block table per request: position t of the request lives at row
+ * block_table[t / block_size] * block_size + t % block_size of every pool.
+ * Row t of the codec is then, per layer, the position's key heads followed by
+ * its value heads (the dckv_params row order).  The struct is host memory; the
+ * block table (int32, ceil(T / block_size) entries) is device memory.
+ *
+ * dckv_encode_paged: dckv_encode of the request held in the pools.  post_rope
+ * != 0: the keys carry RoPE at their positions and are rotated back first with
+ * dckv_unrope's arithmetic, so the stream equals dckv_encode_postrope's of the
+ * gathered rows; post_rope = 0: the stream equals dckv_encode's of them.  The
+ * rows are gathered into the workspace (one read of the request's blocks).
+ * dckv_decode_paged: dckv_decode, then the decoded rows (keys post-RoPE) are
+ * written into the request's rows of the pools; no other row is touched.
+ * Both: the workspace must hold dckv_bytes_paged() bytes (dckv_bytes()'s
+ * workspace plus T * 12,288 bytes of rows, plus 256).  The block table is
+ * checked on the device before the pools are used: an entry outside
+ * [0, n_blocks) makes the call's status DCKV_EINVAL (encode: and *stream_bytes
+ * 0), and then nothing is read from (encode) or written to (decode) the pools.
+ * Other arguments, errors and asynchrony as dckv_encode / dckv_decode.
+ * --------------------------------------------------------------------------*/
+typedef struct dckv_paged_kv {
+  uint16_t *kv[12];             /* kv[2 l + kv]: layer l's key (kv = 0) or value (1) pool */
+  const int32_t *block_table;   /* (device) physical block of each of the request's blocks */
+  int32_t block_size;           /* positions per block, >= 1 */
+  int64_t n_blocks;             /* blocks in each pool, >= 1 */
+} dckv_paged_kv;
+
+int dckv_bytes_paged(const dckv_plan_t *plan, int64_t T, uint64_t *workspace_bytes);
+int dckv_encode_paged(const dckv_plan_t *plan, const dckv_paged_kv *cache, int32_t post_rope,
+                      const int32_t *token_ids, int64_t T, uint8_t *stream, uint64_t capacity,
+                      uint64_t *stream_bytes, int32_t *status, void *workspace, uint64_t workspace_bytes,
+                      void *hip_stream);
+int dckv_decode_paged(const dckv_plan_t *plan, const uint8_t *stream, uint64_t stream_bytes,
+                      const int32_t *token_ids, int64_t T, const dckv_paged_kv *cache, int32_t *status,
+                      void *workspace, uint64_t workspace_bytes, void *hip_stream);
+
+/* ---------------------------------------------------------------------------
  * Batches of independent requests in one call (DCKV digest, "How it works":
  * every request is coded on its own; "Limits": the pages code one request at a
  * time, so a batch is our extension).
@@ -286,11 +330,10 @@ int dckv_encode_postrope(const dckv_plan_t *plan, const uint16_t *rows, const in
  * any request returns its code (dckv_last_error names the request) and
  * enqueues nothing.  The requests share one workspace of dckv_bytes_batch()
  * bytes, the sum of their dckv_bytes() needs (each rounded up to 256 bytes):
- * each request gets its own slice, so the stream stages of all requests (kept
- * rows, rANS, group offsets and header, packing; on decode the parse and
- * rANS) run in the same launches, up to 16 requests per launch, while each
- * request's transform stages (the GEMMs and the dequantisation) run in their
- * own launches, each of which fills the GPU.  Everything is enqueued on
+ * each request gets its own slice, and every stage runs in one launch over up
+ * to 16 requests (the transform GEMMs over all the requests' tiles, the stream
+ * stages over all their groups), so a batch is one launch sequence.
+ * Everything is enqueued on
  * hip_stream; the workspace is owned by the caller and must not be used by
  * other work on other streams meanwhile.  Each request's results equal those
  * of the single-request call.

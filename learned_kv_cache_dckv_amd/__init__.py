@@ -27,7 +27,8 @@ VIEW_SYMBOLS, VIEW_YHAT_B, VIEW_H_B = 0, 1, 2
 EXPORTS = ("dckv_plan_tables", "dckv_plan", "dckv_plan_free", "dckv_plan_info", "dckv_plan_mean_table",
            "dckv_plan_memory",
            "dckv_bytes", "dckv_encode", "dckv_encode_noalloc", "dckv_bytes_postrope", "dckv_encode_postrope",
-           "dckv_decode", "dckv_decode_heads", "dckv_unrope", "dckv_bytes_batch", "dckv_encode_batch", "dckv_decode_batch", "dckv_entropy_encode",
+           "dckv_decode", "dckv_decode_heads", "dckv_unrope", "dckv_bytes_paged", "dckv_encode_paged",
+           "dckv_decode_paged", "dckv_bytes_batch", "dckv_encode_batch", "dckv_decode_batch", "dckv_entropy_encode",
            "dckv_entropy_decode", "dckv_workspace_view", "dckv_profile_enable", "dckv_profile_only", "dckv_profile_reset",
            "dckv_profile_read", "dckv_fit_bytes", "dckv_fit", "dckv_rate_bytes", "dckv_rate_forward",
            "dckv_rate_backward_bytes", "dckv_rate_backward", "dckv_last_error")
@@ -48,6 +49,11 @@ class _Params(ctypes.Structure):
                 ("w2", ctypes.c_void_p), ("embedding", ctypes.c_void_p), ("mean_head", ctypes.c_void_p),
                 ("nbr_weight", ctypes.c_void_p), ("laplace_scale", ctypes.c_void_p),
                 ("base_step", ctypes.c_void_p)]
+
+
+class _PagedKV(ctypes.Structure):
+    _fields_ = [("kv", ctypes.c_void_p * 12), ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int32),
+                ("n_blocks", ctypes.c_int64)]
 
 
 class _Req(ctypes.Structure):
@@ -79,6 +85,9 @@ def _load():
         "dckv_decode": [P, P, U64, P, I64, P, P, P, U64, P],
         "dckv_decode_heads": [P, P, U64, P, I64, P, P, P, U64, P],
         "dckv_unrope": [P, P, I64, P, P],
+        "dckv_bytes_paged": [P, I64, P],
+        "dckv_encode_paged": [P, P, I32, P, I64, P, U64, P, P, P, U64, P],
+        "dckv_decode_paged": [P, P, U64, P, I64, P, P, P, U64, P],
         "dckv_bytes_batch": [P, I32, P],
         "dckv_encode_batch": [P, I32, P, U64, P],
         "dckv_decode_batch": [P, I32, P, U64, P],
@@ -337,6 +346,53 @@ def dckv_encode_postrope(plan: Plan, rows, token_ids, stream_buf, stream_bytes, 
     _check(_lib.dckv_encode_postrope(plan.handle, _ptr(rows), _ptr(token_ids), T, _ptr(stream_buf),
                                      stream_buf.numel(), _ptr(stream_bytes), _ptr(status), _ptr(ws), ws.numel(),
                                      _stream_handle(stream)))
+
+
+class PagedKV:
+    """A paged attention cache: pools[2 l + kv] (layer l, kv = 0 keys, 1 values) are device
+    tensors [n_blocks][block_size][n_kv_heads][head_dim] (bf16 or int16 bits); block_table is
+    a device int32 tensor of the request's physical blocks."""
+
+    def __init__(self, pools, block_table, block_size: int):
+        assert len(pools) == 12
+        self.pools = [_as_bits(t) for t in pools]
+        self.block_table = block_table
+        self.block_size = int(block_size)
+        self.n_blocks = int(self.pools[0].shape[0])
+
+    def c_struct(self) -> _PagedKV:
+        c = _PagedKV()
+        for i, t in enumerate(self.pools):
+            c.kv[i] = _ptr(t)
+        c.block_table = _ptr(self.block_table)
+        c.block_size = self.block_size
+        c.n_blocks = self.n_blocks
+        return c
+
+
+def dckv_bytes_paged(plan: Plan, T: int) -> int:
+    """Workspace bytes of dckv_encode_paged / dckv_decode_paged for T tokens."""
+    v = ctypes.c_uint64()
+    _check(_lib.dckv_bytes_paged(plan.handle, int(T), ctypes.byref(v)))
+    return v.value
+
+
+def dckv_encode_paged(plan: Plan, cache: PagedKV, post_rope: bool, token_ids, stream_buf, stream_bytes, status,
+                      ws, stream=None):
+    """Enqueue an encode of the request held in a paged cache."""
+    T = int(token_ids.shape[0])
+    c = cache.c_struct()
+    _check(_lib.dckv_encode_paged(plan.handle, ctypes.byref(c), 1 if post_rope else 0, _ptr(token_ids), T,
+                                  _ptr(stream_buf), stream_buf.numel(), _ptr(stream_bytes), _ptr(status), _ptr(ws),
+                                  ws.numel(), _stream_handle(stream)))
+
+
+def dckv_decode_paged(plan: Plan, stream_buf, n_bytes: int, token_ids, cache: PagedKV, status, ws, stream=None):
+    """Enqueue a decode into the request's rows of a paged cache."""
+    T = int(token_ids.shape[0])
+    c = cache.c_struct()
+    _check(_lib.dckv_decode_paged(plan.handle, _ptr(stream_buf), int(n_bytes), _ptr(token_ids), T, ctypes.byref(c),
+                                  _ptr(status), _ptr(ws), ws.numel(), _stream_handle(stream)))
 
 
 def dckv_decode(plan: Plan, stream_buf, n_bytes: int, token_ids, rows_out, status, ws, stream=None):

@@ -554,3 +554,110 @@ extern "C" int dckv_encode_postrope(const dckv_plan_t *plan, const uint16_t *row
   encode_sequence(&a, 1);
   return after_launch("dckv_encode_postrope");
 }
+
+// ---------------------------------------------------------------------------
+// A paged attention cache on either side of the codec: encode gathers the
+// request's rows from the pools (rotating the keys back when they carry RoPE)
+// into the workspace and encodes them; decode decodes into the workspace and
+// scatters the rows into the pools.  The block table is checked on the device
+// first: an entry outside [0, n_blocks) makes the call's status EINVAL and
+// nothing is read from (encode) or written to (decode) the pools.
+// ---------------------------------------------------------------------------
+namespace {
+// workspace of a paged call: the codec's workspace, the rows, one status word
+uint64_t paged_rows_offset(const Layout &l) { return (l.total + 255) & ~(uint64_t)255; }
+uint64_t paged_pre_offset(const Layout &l, int64_t T) {
+  return paged_rows_offset(l) + (((uint64_t)std::max<int64_t>(T, 1) * kD * 2 + 255) & ~(uint64_t)255);
+}
+
+int paged_from(const dckv_paged_kv *c, int64_t T, PagedKV &kv, const char *what) {
+  char msg[160];
+  if (!c) {
+    std::snprintf(msg, sizeof msg, "%s: null cache", what);
+    return set_error(DCKV_EINVAL, msg);
+  }
+  if (c->block_size < 1 || c->n_blocks < 1 || (T > 0 && !c->block_table) || !aligned(c->block_table, 4)) {
+    std::snprintf(msg, sizeof msg, "%s: block_size and n_blocks must be >= 1 and block_table a device int32 array",
+                  what);
+    return set_error(DCKV_EINVAL, msg);
+  }
+  for (int i = 0; i < 12; ++i) {
+    kv.p[i] = c->kv[i];
+    if (T > 0 && (!kv.p[i] || !aligned(kv.p[i], 16))) {
+      std::snprintf(msg, sizeof msg, "%s: every pool must be a 16-byte aligned device pointer", what);
+      return set_error(DCKV_EINVAL, msg);
+    }
+  }
+  kv.table = c->block_table;
+  kv.bs = c->block_size;
+  kv.n_blocks = c->n_blocks;
+  return DCKV_OK;
+}
+}  // namespace
+
+extern "C" int dckv_bytes_paged(const dckv_plan_t *plan, int64_t T, uint64_t *workspace_bytes) {
+  uint64_t ws = 0;
+  const int rc = dckv_bytes(plan, T, nullptr, &ws);
+  if (rc) return rc;
+  if (!workspace_bytes) return set_error(DCKV_EINVAL, "bytes_paged: null workspace_bytes");
+  const Layout l = layout(plan, geometry(plan, T));
+  *workspace_bytes = paged_pre_offset(l, T) + 256;
+  return DCKV_OK;
+}
+
+extern "C" int dckv_encode_paged(const dckv_plan_t *plan, const dckv_paged_kv *cache, int32_t post_rope,
+                                 const int32_t *token_ids, int64_t T, uint8_t *stream, uint64_t capacity,
+                                 uint64_t *stream_bytes, int32_t *status, void *workspace, uint64_t workspace_bytes,
+                                 void *hip_stream) {
+  uint64_t need = 0;
+  int rc = dckv_bytes_paged(plan, T, &need);
+  if (rc) return rc;
+  if (workspace_bytes < need)
+    return set_error(DCKV_ECAPACITY, "encode_paged: workspace smaller than dckv_bytes_paged() reports");
+  PagedKV kv;
+  rc = paged_from(cache, T, kv, "encode_paged");
+  if (rc) return rc;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  const Layout l0 = layout(plan, geometry(plan, T));
+  uint16_t *rows = reinterpret_cast<uint16_t *>(ws + paged_rows_offset(l0));
+  int32_t *pre = reinterpret_cast<int32_t *>(ws + paged_pre_offset(l0, T));
+  Geometry g;
+  Layout l;
+  rc = encode_checks(plan, rows, token_ids, T, stream, capacity, stream_bytes, status, workspace, workspace_bytes, g,
+                     l);
+  if (rc) return rc;
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  launch_paged_check(kv, T, pre, true, s);
+  launch_paged_gather(plan, kv, post_rope != 0, T, rows, pre, s);
+  EncodeArgs a{plan, g, l, ws, rows, token_ids, stream, capacity, stream_bytes, status, s};
+  a.pre = pre;
+  encode_sequence(&a, 1);
+  return after_launch("dckv_encode_paged");
+}
+
+extern "C" int dckv_decode_paged(const dckv_plan_t *plan, const uint8_t *stream, uint64_t stream_bytes,
+                                 const int32_t *token_ids, int64_t T, const dckv_paged_kv *cache, int32_t *status,
+                                 void *workspace, uint64_t workspace_bytes, void *hip_stream) {
+  uint64_t need = 0;
+  int rc = dckv_bytes_paged(plan, T, &need);
+  if (rc) return rc;
+  if (workspace_bytes < need)
+    return set_error(DCKV_ECAPACITY, "decode_paged: workspace smaller than dckv_bytes_paged() reports");
+  PagedKV kv;
+  rc = paged_from(cache, T, kv, "decode_paged");
+  if (rc) return rc;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  const Layout l0 = layout(plan, geometry(plan, T));
+  uint16_t *rows = reinterpret_cast<uint16_t *>(ws + paged_rows_offset(l0));
+  Geometry g;
+  Layout l;
+  rc = decode_checks(plan, stream, stream_bytes, token_ids, T, rows, status, workspace, workspace_bytes, g, l);
+  if (rc) return rc;
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const DecodeArgs a{plan, g, l, ws, stream, stream_bytes, token_ids, rows, status, s};
+  decode_sequence(&a, 1);
+  // after the decode: its parse clears the status first
+  launch_paged_check(kv, T, status, false, s);
+  launch_paged_scatter(kv, T, rows, status, s);
+  return after_launch("dckv_decode_paged");
+}

@@ -153,6 +153,9 @@ struct EncodeArgs {
   // set (encode from a post-RoPE cache): the pre-RoPE key heads of every row,
   // [T][kKeyCols]; rows then supplies only the value heads
   const uint16_t *keys = nullptr;
+  // set: the call's status starts as *pre (a check run before the encode)
+  // instead of 0
+  const int32_t *pre = nullptr;
 };
 
 // Decoded rows either as rows_out [T][D], or per attention layer: for layer
@@ -224,8 +227,27 @@ void launch_batched(Kern kern, const char *name, int n, hipStream_t s, unsigned 
   }
 }
 
+// A paged attention cache: per layer l, a key (kv = 0) and a value (kv = 1)
+// pool p[2 l + kv] of [n_blocks][block_size][n_kv_heads][head_dim] bf16;
+// position t of a request is row table[t / bs] * bs + t % bs of every pool.
+struct PagedKV {
+  uint16_t *p[12];
+  const int32_t *table;
+  int32_t bs;
+  int64_t n_blocks;
+};
+
 // misc.hip
 void launch_start_encode(const EncodeArgs *a, int n);  // control words, status, kept rows
+// status := EINVAL when an entry of the first ceil(T / bs) of the block table
+// is outside [0, n_blocks); clear_first: set it to 0 before (else only set)
+void launch_paged_check(const PagedKV &kv, int64_t T, int32_t *status, bool clear_first, hipStream_t s);
+// rows [T][D] <- the paged cache (post_rope: keys rotated back, as dckv_unrope);
+// nothing is read when *pre is not 0
+void launch_paged_gather(const dckv_plan_t *p, const PagedKV &kv, bool post_rope, int64_t T, uint16_t *rows,
+                         const int32_t *pre, hipStream_t s);
+// the paged cache <- rows [T][D]; nothing is written when *status is not 0
+void launch_paged_scatter(const PagedKV &kv, int64_t T, const uint16_t *rows, const int32_t *status, hipStream_t s);
 void launch_unrope(const dckv_plan_t *p, const uint16_t *in, uint16_t *out, int64_t T, hipStream_t s);
 // the inverse RoPE of the key heads only, rows [T][D] -> keys [T][kKeyCols]
 void launch_unrope_keys(const dckv_plan_t *p, const uint16_t *in, uint16_t *keys, int64_t T, hipStream_t s);

@@ -16,6 +16,7 @@ namespace {
 struct StartP {
   uint8_t *ws;
   int32_t *status;
+  const int32_t *pre;  // set: the status starts as *pre
   uint64_t *stream_bytes;
   const uint16_t *rows;
   const uint16_t *keys;  // set: the key heads of every row come from this key copy [T][kKeyCols]
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(256) void k_start_encode(const Batch<StartP> B) {
     ct->total_bytes = 0;
     ct->rans_bytes = 0;
     ct->esc_off = ct->rans_off = ct->offs_off = 0;
-    *P.status = 0;
+    *P.status = P.pre ? *P.pre : 0;
     *P.stream_bytes = 0;
   }
   if (k >= P.n_kept) return;
@@ -137,6 +138,93 @@ __global__ __launch_bounds__(256) void k_unrope_keys(const uint16_t *in, uint16_
       *reinterpret_cast<uint4 *>(dst + ob + kHalf) = uint4{o1[0], o1[1], o1[2], o1[3]};
     }
 }
+// ---------------------------------------------------------------------------
+// Paged attention cache (the layout serving engines keep the cache in): per
+// layer a key and a value pool of [n_blocks][block_size][n_kv_heads][head_dim]
+// bf16 and one block table for the request.  Position t is row
+// table[t / bs] * bs + t % bs of every pool; its 6,144-dim codec row is, per
+// layer l, the key heads then the value heads.
+// ---------------------------------------------------------------------------
+
+// Every entry of the request's block table in [0, n_blocks), else EINVAL.
+// One workgroup: thread 0 clears the word first when asked, the others wait.
+__global__ __launch_bounds__(256) void k_paged_check(const int32_t *table, int64_t n_logical, int64_t n_blocks,
+                                                     int32_t *status, int clear_first) {
+  if (clear_first) {
+    if (threadIdx.x == 0) *status = 0;
+    __syncthreads();
+  }
+  for (int64_t i = threadIdx.x; i < n_logical; i += blockDim.x) {
+    const int64_t b = table[i];
+    if (b < 0 || b >= n_blocks) atomicCAS(status, 0, DCKV_EINVAL);
+  }
+}
+
+// row t (thread group of 16 per row) from the pools; thread g takes the
+// 16-byte pieces 8 g .. 8 g + 7 of each half of every head, so a key pair
+// (d, d + 128) is one thread's (the inverse rotation as k_unrope_keys)
+__global__ __launch_bounds__(256) void k_paged_gather(PagedKV kv, int post_rope, int64_t T, const double *omega,
+                                                      uint16_t *rows, const int32_t *pre) {
+  const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int g = threadIdx.x & 15;
+  if (t >= T || *pre != 0) return;
+  const int64_t prow = (int64_t)kv.table[t / kv.bs] * kv.bs + t % kv.bs;
+  double cs[8], sn[8];
+  if (post_rope) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sincos((double)t * omega[8 * g + e], &sn[e], &cs[e]);
+  }
+  uint16_t *dst = rows + (size_t)t * kD;
+  auto half = [](const uint4 &v, int e) -> uint32_t {
+    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+    return (e & 1) ? w >> 16 : w & 0xFFFFu;
+  };
+#pragma unroll
+  for (int l = 0; l < 6; ++l)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const size_t so = ((size_t)prow * 2 + h) * kHeadDim + 8 * g;
+      const uint16_t *ks = kv.p[2 * l] + so, *vs = kv.p[2 * l + 1] + so;
+      const int kb = (l * 4 + h) * kHeadDim + 8 * g, vb = (l * 4 + 2 + h) * kHeadDim + 8 * g;
+      const uint4 a = *reinterpret_cast<const uint4 *>(ks), b = *reinterpret_cast<const uint4 *>(ks + kHalf);
+      *reinterpret_cast<uint4 *>(dst + vb) = *reinterpret_cast<const uint4 *>(vs);
+      *reinterpret_cast<uint4 *>(dst + vb + kHalf) = *reinterpret_cast<const uint4 *>(vs + kHalf);
+      if (!post_rope) {
+        *reinterpret_cast<uint4 *>(dst + kb) = a;
+        *reinterpret_cast<uint4 *>(dst + kb + kHalf) = b;
+        continue;
+      }
+      uint32_t o0[4], o1[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        uint32_t r0[2], r1[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const double p0 = (double)__uint_as_float(half(a, e + u) << 16);
+          const double p1 = (double)__uint_as_float(half(b, e + u) << 16);
+          r0[u] = bf16_of_f64(__dadd_rn(__dmul_rn(p0, cs[e + u]), __dmul_rn(p1, sn[e + u])));
+          r1[u] = bf16_of_f64(__dsub_rn(__dmul_rn(p1, cs[e + u]), __dmul_rn(p0, sn[e + u])));
+        }
+        o0[e / 2] = r0[0] | (r0[1] << 16);
+        o1[e / 2] = r1[0] | (r1[1] << 16);
+      }
+      *reinterpret_cast<uint4 *>(dst + kb) = uint4{o0[0], o0[1], o0[2], o0[3]};
+      *reinterpret_cast<uint4 *>(dst + kb + kHalf) = uint4{o1[0], o1[1], o1[2], o1[3]};
+    }
+}
+
+// the pools from rows: thread (t, 16-byte piece i) of a row's 768 pieces
+__global__ __launch_bounds__(256) void k_paged_scatter(PagedKV kv, int64_t T, const uint16_t *rows,
+                                                       const int32_t *status) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * (kD / 8) || *status != 0) return;
+  const int64_t t = i / (kD / 8);
+  const int c = (int)(i - t * (kD / 8)) * 8;  // column of the piece
+  const int l = c / 1024, w = c % 1024, kvi = w / 512, h = (w % 512) / kHeadDim, d = w % kHeadDim;
+  const int64_t prow = (int64_t)kv.table[t / kv.bs] * kv.bs + t % kv.bs;
+  *reinterpret_cast<uint4 *>(kv.p[2 * l + kvi] + ((size_t)prow * 2 + h) * kHeadDim + d) =
+      *reinterpret_cast<const uint4 *>(rows + (size_t)t * kD + c);
+}
 }  // namespace
 
 void launch_start_encode(const EncodeArgs *args, int n) {
@@ -145,6 +233,7 @@ void launch_start_encode(const EncodeArgs *args, int n) {
     StartP P;
     P.ws = a.ws;
     P.status = a.status;
+    P.pre = a.pre;
     P.stream_bytes = a.stream_bytes;
     P.rows = a.rows;
     P.keys = a.keys;
@@ -168,5 +257,25 @@ void launch_unrope_keys(const dckv_plan_t *p, const uint16_t *in, uint16_t *kc, 
 void launch_unrope(const dckv_plan_t *p, const uint16_t *in, uint16_t *out, int64_t T, hipStream_t s) {
   if (T == 0) return;
   hipLaunchKernelGGL(k_unrope, dim3((unsigned)((T + 1) / 2)), dim3(256), 0, s, in, out, T, p->dev.omega);
+}
+void launch_paged_check(const PagedKV &kv, int64_t T, int32_t *status, bool clear_first, hipStream_t s) {
+  const int64_t n_logical = T > 0 ? (T + kv.bs - 1) / kv.bs : 0;
+  hipLaunchKernelGGL(k_paged_check, dim3(1), dim3(256), 0, s, kv.table, n_logical, kv.n_blocks, status,
+                     clear_first ? 1 : 0);
+}
+
+void launch_paged_gather(const dckv_plan_t *p, const PagedKV &kv, bool post_rope, int64_t T, uint16_t *rows,
+                         const int32_t *pre, hipStream_t s) {
+  if (T <= 0) return;
+  KernelTimer tm("paged_gather", s);
+  hipLaunchKernelGGL(k_paged_gather, dim3((unsigned)((T + 15) / 16)), dim3(256), 0, s, kv, post_rope ? 1 : 0, T,
+                     p->dev.omega, rows, pre);
+}
+
+void launch_paged_scatter(const PagedKV &kv, int64_t T, const uint16_t *rows, const int32_t *status, hipStream_t s) {
+  if (T <= 0) return;
+  KernelTimer tm("paged_scatter", s);
+  const int64_t n = T * (kD / 8);
+  hipLaunchKernelGGL(k_paged_scatter, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, kv, T, rows, status);
 }
 }  // namespace dckv
