@@ -117,7 +117,7 @@ static_assert(sizeof(Ctrl) == 256, "ctrl block is 256 bytes");
 
 struct Layout {
   uint64_t ctrl, sym, esc_raw, esc_sorted, halo_a, halo_b, scratch, gwords, goffs;
-  uint64_t yhat_b, h_b, w1_part, rope_lo, rope_hi, esc_rows, total;
+  uint64_t yhat_b, h_b, w1_part, rope_lo, rope_hi, esc_rows, dhalo, total;
   uint64_t enc_total;  // end of what the encode kernels touch (total covers decode too)
 };
 
@@ -251,6 +251,13 @@ void launch_paged_scatter(const PagedKV &kv, int64_t T, const uint16_t *rows, co
 void launch_unrope(const dckv_plan_t *p, const uint16_t *in, uint16_t *out, int64_t T, hipStream_t s);
 // the inverse RoPE of the key heads only, rows [T][D] -> keys [T][kKeyCols]
 void launch_unrope_keys(const dckv_plan_t *p, const uint16_t *in, uint16_t *keys, int64_t T, hipStream_t s);
+
+// The rANS decoder also dequantises (writes yhat_b) for a request whose plan
+// codes every component (a full decode: token ids given); k_dequant then
+// skips it.
+inline bool dequant_fused(const DecodeArgs &a) {
+  return a.g.N > 0 && a.tok != nullptr && a.p->C_a == a.p->C && a.p->C == kC;
+}
 
 // rans.hip
 void launch_rans_encode(const EncodeArgs *a, int n);

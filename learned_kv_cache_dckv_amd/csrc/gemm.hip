@@ -1440,12 +1440,13 @@ void launch_dequant(const DecodeArgs *args, int n) {
     P.status = a.status;
     return P;
   };
-  // requests without dropped components take the dense variant; the others
+  // requests whose rANS decode dequantised them already are skipped; the
+  // others without dropped components take the dense variant; the others
   // (in their own launches) read symbols and means through rank and colpos
   for (int dense = 1; dense >= 0; --dense) {
     std::vector<int> idx;
     for (int i = 0; i < n; ++i)
-      if (args[i].g.N > 0 && (args[i].p->C_a == kC) == (dense == 1)) idx.push_back(i);
+      if (args[i].g.N > 0 && (args[i].p->C_a == kC) == (dense == 1) && !dequant_fused(args[i])) idx.push_back(i);
     if (idx.empty()) continue;
     auto f = [&](int k) { return fill(idx[k]); };
     auto count = [&](int k) {

@@ -509,6 +509,7 @@ Layout dckv::layout(const dckv_plan_t *p, const Geometry &g) {
   off = shared_end;
   l.yhat_b = take((uint64_t)g.NM * p->C * 2);
   l.esc_rows = take((uint64_t)g.n_mtiles * 2 * 4);
+  l.dhalo = take(2ull * g.n_mtiles * p->C * 4);  // fused dequantisation: left neighbours, first rows
   l.h_b = take((uint64_t)g.NM * p->hidden * 2);
   l.w1_part = take(2ull * g.NM * p->hidden * 4);
   l.rope_lo = take(256ull * kHalf * 8);

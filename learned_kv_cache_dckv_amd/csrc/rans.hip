@@ -20,6 +20,8 @@
 // lanes, words taken by ascending lane (ballot plus a popcount of the lower
 // lanes).  A group is valid only if every lane ends at L and every word was
 // consumed.
+#include <type_traits>
+
 #include "dckv_internal.h"
 
 namespace dckv {
@@ -609,6 +611,16 @@ __global__ __launch_bounds__(256) void k_parse(const Batch<ParseP> B) {
 struct DecP {
   const uint32_t *tab;
   const uint32_t *bucket;
+  // fused dequantisation (a plan without dropped components): the decoder
+  // writes yhat_b itself; the odd row that ends each block but the last is
+  // finished by k_dequant_fix from the four halo arrays [n_blk][C]
+  int fuse;
+  const float *mtab;         // [vocab][C] embedding means
+  const int32_t *tok;
+  const float *step, *nbr;
+  uint16_t *yhat_b;          // [NM][C]
+  float *hm, *hq, *hl, *hr;  // the pending row's mean and code, its left neighbour; each block's first yhat
+  int keep_head, vocab;
   const uint8_t *stream;
   const uint8_t *ws;
   const uint32_t *esc_rows;  // [blocks][2]: index range of each block's escape records (from the parser)
@@ -654,11 +666,17 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int q) {
 // slides (before a quad) when the quad could read past it; it is read modulo
 // its size, so a corrupt stream reads words of the window, never past it, and
 // ends with ptr != W or a final state != L, which the caller reports.
-template <bool kPlain, class Fill>
+// quad.template run<PH>(q, s0, s1, s2, s3, rows) takes the symbols of rows
+// 4 q .. 4 q + rows - 1 (rows past the block read as escapes);
+// quad.template pre<PH>(q) runs before the quad's steps (prefetches).  PH is
+// q mod 3 for whole quads, a constant at every call: the quad loop is unrolled
+// by three, so a functor can rotate three buffers without copying them.  The
+// partial quad runs with PH = 0 after quad.to_phase0(q mod 3).
+template <bool kPlain, class Fill, class Quad>
 __device__ __forceinline__ void decode_rows(uint32_t &x, uint32_t &ptr, uint32_t &base, uint32_t W, int Lb, int lane,
                                             bool lane_ok, bool has_esc, const uint64_t (&esc)[4],
                                             const uint32_t *mytab, const uint32_t *mybkt, uint32_t bkt_lane, uint32_t wofs,
-                                            uint32_t *sout, Fill &&fill) {
+                                            Fill &&fill, Quad &&quad) {
   // emask: the row's escaped lanes (bit l set: lane l is skipped)
   auto step = [&](uint64_t emask) -> uint32_t {
     bool act = true;
@@ -714,25 +732,146 @@ __device__ __forceinline__ void decode_rows(uint32_t &x, uint32_t &ptr, uint32_t
       fill(base);
     }
   };
+  auto whole = [&](int q, auto ph) __attribute__((always_inline)) {
+    constexpr int PH = decltype(ph)::value;
+    slide();
+    quad.template pre<PH>(q);
+    const uint32_t s0 = step(em(q, 0)), s1 = step(em(q, 1)), s2 = step(em(q, 2)), s3 = step(em(q, 3));
+    quad.template run<PH>(q, s0, s1, s2, s3, 4);
+  };
+  // the last, partial quad: rows past the block read as escapes
+  auto part = [&](int q, int r, auto ph) __attribute__((always_inline)) {
+    constexpr int PH = decltype(ph)::value;
+    slide();
+    quad.template pre<PH>(q);
+    const uint32_t s0 = step(em(q, 0));
+    const uint32_t s1 = r > 1 ? step(em(q, 1)) : (uint32_t)kEsc;
+    const uint32_t s2 = r > 2 ? step(em(q, 2)) : (uint32_t)kEsc;
+    quad.template run<PH>(q, s0, s1, s2, (uint32_t)kEsc, r);
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
   const int nq = Lb >> 2;
+  int q = 0;
 #pragma unroll 1
-  for (int q = 0; q < nq; ++q) {
-    slide();
-    uint32_t w = step(em(q, 0));
-    w |= step(em(q, 1)) << 8;
-    w |= step(em(q, 2)) << 16;
-    w |= step(em(q, 3)) << 24;
-    if (kPlain || lane_ok) sout[(size_t)q * 64] = w;
+  for (; q + 3 <= nq; q += 3) {
+    whole(q, P0{});
+    whole(q + 1, P1{});
+    whole(q + 2, P2{});
   }
-  if (Lb & 3) {  // the last, partial quad: rows past the block read as escapes
-    slide();
-    uint32_t w = 0xFFFFFFFFu;
-    if ((Lb & 3) > 0) w = (w & ~0xFFu) | step(em(nq, 0));
-    if ((Lb & 3) > 1) w = (w & ~0xFF00u) | (step(em(nq, 1)) << 8);
-    if ((Lb & 3) > 2) w = (w & ~0xFF0000u) | (step(em(nq, 2)) << 16);
-    if (kPlain || lane_ok) sout[(size_t)nq * 64] = w;
+  // at most two whole quads left (phases 0 and 1), then the partial one
+  if (q < nq) whole(q, P0{});
+  if (q + 1 < nq) whole(q + 1, P1{});
+  if (Lb & 3) {
+    // the partial quad's phase is nq - q (0, 1 or 2): its buffer moves to
+    // phase 0 by value (a buffer index that is not a constant would put the
+    // functor in scratch memory)
+    quad.to_phase0(nq - q);
+    part(nq, Lb & 3, P0{});
   }
 }
+
+// The decoder's per-quad work on symbols only: the symbol words.
+struct SymOnly {
+  uint32_t *sout;
+  bool ok;
+  __device__ __forceinline__ void to_phase0(int) {}
+  template <int PH>
+  __device__ __forceinline__ void pre(int) {}
+  template <int PH>
+  __device__ __forceinline__ void run(int q, uint32_t s0, uint32_t s1, uint32_t s2, uint32_t s3, int) {
+    if (ok) sout[(size_t)q * 64] = s0 | (s1 << 8) | (s2 << 16) | (s3 << 24);
+  }
+};
+
+// The decoder's per-quad work with the dequantisation fused (see
+// k_rans_decode).
+struct Fused {
+  const float *mcol;  // mtab + c
+  uint16_t *ycol;     // yhat_b + c
+  uint32_t *sout;
+  uint32_t tk[4];     // token ids of rows 4 l .. 4 l + 3 (lane l)
+  const uint32_t *erec;
+  uint32_t elo, ehi;
+  int32_t *status;
+  int64_t j0, N, n_blk, b;
+  int Ca, c;
+  float st, a;
+  float m[3][4];      // means of quad q in m[q mod 3] (loaded two quads ahead)
+  float yl, mp, qp;   // the pending odd row: left neighbour, mean, code
+  __device__ __forceinline__ float mean(int qq, int k) const {
+    const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)tk[k], qq);
+    return gload(mcol + (size_t)id * kC);
+  }
+  // quads 0 and 1 before the loop; quad q + 2 at quad q (buffer (q + 2) mod 3)
+  __device__ __forceinline__ void prime() {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      m[0][k] = mean(0, k);
+      m[1][k] = mean(1, k);
+    }
+  }
+  __device__ __forceinline__ void to_phase0(int ph) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float v0 = m[0][k], v1 = m[1][k], v2 = m[2][k];
+      // values, not addresses: a select of addresses is a dynamic index
+      asm volatile("" : "+v"(v0), "+v"(v1), "+v"(v2));
+      m[0][k] = ph == 0 ? v0 : ph == 1 ? v1 : v2;
+    }
+  }
+  template <int PH>
+  __device__ __forceinline__ void pre(int q) {
+    constexpr int B2 = (PH + 2) % 3;
+    if (q + 2 < kLanes) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m[B2][k] = mean(q + 2, k);
+    }
+  }
+  // the code of escaped row j: its record among the block's (ascending flat)
+  __device__ __forceinline__ float esc_code(int64_t j) const {
+    const uint32_t flat = (uint32_t)j * (uint32_t)Ca + (uint32_t)c;
+    uint32_t lo = elo, hi = ehi;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (gload(erec + 2 * mid) < flat) lo = mid + 1; else hi = mid;
+    }
+    if (lo < ehi && gload(erec + 2 * lo) == flat) return (float)(int)gload(erec + 2 * lo + 1);
+    set_status(status, DCKV_ECORRUPT);
+    return 0.f;
+  }
+  __device__ __forceinline__ void put(int64_t j, float y) { ycol[(size_t)j * kC] = __builtin_bit_cast(uint16_t, (__bf16)y); }
+  template <int PH>
+  __device__ __forceinline__ void run(int q, uint32_t s0, uint32_t s1, uint32_t s2, uint32_t s3, int rows) {
+    const float(&mq)[4] = m[PH];
+    sout[(size_t)q * 64] = s0 | (s1 << 8) | (s2 << 16) | (s3 << 24);
+    const int64_t j = j0 + 4 * q;
+    const uint32_t sy[4] = {s0, s1, s2, s3};
+    float qv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      qv[k] = (float)((int)sy[k] - 127);
+      const bool e = sy[k] == (uint32_t)kEsc && k < rows;
+      if (__builtin_expect(__ballot(e) != 0ull, 0))
+        if (e) qv[k] = esc_code(j + k);
+    }
+    const float y0 = mq[0] + qv[0] * st;
+    if (q > 0) put(j - 1, mp + a * (yl + y0) + qp * st);
+    else if (b > 0) hr_store(y0);
+    put(j, y0);
+    if (rows > 1) {
+      const float y2 = rows > 2 ? mq[2] + qv[2] * st : 0.f;
+      put(j + 1, mq[1] + a * (y0 + y2) + qv[1] * st);
+      if (rows > 2) put(j + 2, y2);
+      yl = y2;
+    }
+    mp = mq[3];
+    qp = qv[3];
+  }
+  float *hr_ptr;
+  __device__ __forceinline__ void hr_store(float y0) { *hr_ptr = y0; }
+};
 
 // Workgroup w of a request decodes component group g = w / nch of the blocks
 // 16 (w % nch) .. + 15 (one wave each), nch = ceil(n_blk / 16).
@@ -825,14 +964,103 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(const Batch<DecP
   uint32_t *sout = P.sym32 + ((size_t)g * (P.N256 / 4) + (size_t)b * 64) * 64 + lane;
   uint32_t wofs = lds_addr(wb);
   asm volatile("" : "+v"(wofs));  // in a VGPR: a window address is then one and-or
-  if (!has_esc && n == kLanes)
-    decode_rows<true>(x, ptr, base, W, Lb, lane, true, false, esc, mytab, mybkt, bkt_lane, wofs, sout, fill);
-  else
-    decode_rows<false>(x, ptr, base, W, Lb, lane, lane_ok, has_esc, esc, mytab, mybkt, bkt_lane, wofs, sout, fill);
+  if (!P.fuse) {
+    if (!has_esc && n == kLanes)
+      decode_rows<true>(x, ptr, base, W, Lb, lane, true, false, esc, mytab, mybkt, bkt_lane, wofs, fill,
+                        SymOnly{sout, true});
+    else
+      decode_rows<false>(x, ptr, base, W, Lb, lane, lane_ok, has_esc, esc, mytab, mybkt, bkt_lane, wofs, fill,
+                         SymOnly{sout, lane_ok});
+  } else {
+    // Fused dequantisation (every component coded: lane = component = mean
+    // table column c).  Row j of the block: yhat = mu + q step on even rows;
+    // an odd row waits for the next even one, mu + a (yhat_{j-1} + yhat_{j+1})
+    // + q step; the odd row past the request's end takes 0 on the right.  The
+    // block's last odd row, unless it is the request's last, goes to the halo
+    // (mean, code, left neighbour) with each block's first yhat, for
+    // k_dequant_fix.  Means: lane l holds the token ids of rows 4 l .. 4 l + 3
+    // (ids out of range set EINVAL and read as 0); a quad's means are loaded
+    // two quads ahead.  Escaped codes come from the block's records.
+    const int c = kLanes * g + lane;
+    const int64_t j0 = (int64_t)kBlock * b;
+    uint32_t tk[4];
+    {
+      bool badtok = false;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int64_t j = j0 + 4 * lane + k;
+        int v = j < P.N ? gload(P.tok + P.keep_head + j) : 0;
+        if (v < 0 || v >= P.vocab) {
+          badtok = true;
+          v = 0;
+        }
+        tk[k] = (uint32_t)v;
+      }
+      if (__ballot(badtok) != 0ull && lane == 0) set_status(P.status, DCKV_EINVAL);
+    }
+    const uint32_t *erec = reinterpret_cast<const uint32_t *>(P.stream + ct->esc_off);
+    const uint32_t elo = __builtin_amdgcn_readfirstlane(gload(P.esc_rows + 2 * b));
+    const uint32_t ehi = __builtin_amdgcn_readfirstlane(gload(P.esc_rows + 2 * b + 1));
+    Fused fz;
+    fz.mcol = P.mtab + c;
+    fz.ycol = P.yhat_b + c;
+    fz.sout = sout;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) fz.tk[k] = tk[k];
+    fz.erec = erec;
+    fz.elo = elo;
+    fz.ehi = ehi;
+    fz.status = P.status;
+    fz.j0 = j0;
+    fz.N = P.N;
+    fz.n_blk = P.n_blk;
+    fz.b = b;
+    fz.Ca = P.Ca;
+    fz.c = c;
+    fz.st = gload(P.step + c);
+    fz.a = gload(P.nbr + c);
+    fz.yl = fz.mp = fz.qp = 0.f;
+    fz.hr_ptr = P.hr + (size_t)b * kC + c;
+    fz.prime();
+    if (!has_esc)
+      decode_rows<true>(x, ptr, base, W, Lb, lane, true, false, esc, mytab, mybkt, bkt_lane, wofs, fill, fz);
+    else
+      decode_rows<false>(x, ptr, base, W, Lb, lane, true, has_esc, esc, mytab, mybkt, bkt_lane, wofs, fill, fz);
+    // the block's last row, when odd (whole quads): the request's last takes
+    // 0 on the right, any other goes to the halo
+    if ((Lb & 3) == 0) {
+      const int64_t jl = j0 + Lb - 1;
+      if (jl == P.N - 1)
+        fz.put(jl, fz.mp + fz.a * (fz.yl + 0.f) + fz.qp * fz.st);
+      else {
+        const size_t h = (size_t)b * kC + c;
+        P.hm[h] = fz.mp;
+        P.hq[h] = fz.qp;
+        P.hl[h] = fz.yl;
+      }
+    }
+  }
   const bool lane_bad = lane_ok && x != kL;
   if (__ballot(lane_bad) != 0ull || ptr != W) {
     if (lane == 0) set_status(P.status, DCKV_ECORRUPT);
   }
+}
+
+// The odd row that ends each block but the last, after the fused decode:
+// mu + a (yhat_{j-1} + yhat_{j+1}) + q step from the halo (the same
+// expression as the rows decoded in place).  Thread (block b, component c).
+__global__ __launch_bounds__(256) void k_dequant_fix(const Batch<DecP> B) {
+  const int ri = batch_req(B, blockIdx.x);
+  const DecP &P = B.r[ri];
+  if (*P.status != 0) return;
+  const int64_t i = (int64_t)(blockIdx.x - B.start[ri]) * blockDim.x + threadIdx.x;
+  if (i >= (P.n_blk - 1) * (int64_t)kC) return;
+  const int64_t b = i / kC;
+  const int c = (int)(i - b * kC);
+  const size_t h = (size_t)b * kC + c;
+  const float st = P.step[c], a = P.nbr[c];
+  const float y = P.hm[h] + a * (P.hl[h] + P.hr[h + kC]) + P.hq[h] * st;
+  P.yhat_b[(size_t)(kBlock * b + kBlock - 1) * kC + c] = __builtin_bit_cast(uint16_t, (__bf16)y);
 }
 
 // ---------------------------------------------------------------------------
@@ -995,9 +1223,21 @@ void launch_parse(const DecodeArgs *args, int n, bool with_rope) {
 void launch_rans_decode(const DecodeArgs *args, int n) {
   auto fill = [&](int i) {
     const DecodeArgs &a = args[i];
-    DecP P;
+    DecP P{};
     P.tab = a.p->dev.tab;
     P.bucket = a.p->dev.bucket;
+    P.fuse = dequant_fused(a) ? 1 : 0;
+    P.mtab = a.p->mtab;
+    P.tok = a.tok;
+    P.step = a.p->dev.step;
+    P.nbr = a.p->dev.nbr;
+    P.yhat_b = reinterpret_cast<uint16_t *>(a.ws + a.l.yhat_b);
+    P.hm = reinterpret_cast<float *>(a.ws + a.l.halo_a);
+    P.hq = reinterpret_cast<float *>(a.ws + a.l.halo_b);
+    P.hl = reinterpret_cast<float *>(a.ws + a.l.dhalo);
+    P.hr = reinterpret_cast<float *>(a.ws + a.l.dhalo) + (size_t)a.g.n_mtiles * a.p->C;
+    P.keep_head = a.p->keep_head;
+    P.vocab = a.p->vocab;
     P.stream = a.stream;
     P.ws = a.ws;
     P.esc_rows = reinterpret_cast<const uint32_t *>(a.ws + a.l.esc_rows);
@@ -1015,6 +1255,13 @@ void launch_rans_decode(const DecodeArgs *args, int n) {
     return a.g.n_groups == 0 ? 0u : (uint32_t)(((a.g.n_blk + kDecWaves - 1) / kDecWaves) * a.p->G);
   };
   launch_batched<DecP>(k_rans_decode, "rans_decode", n, args[0].s, kDecWaves * 64, fill, count);
+  // the odd rows that end the blocks of the fused requests
+  auto fix_count = [&](int i) {
+    const DecodeArgs &a = args[i];
+    if (!dequant_fused(a) || a.g.n_blk < 2) return 0u;
+    return (uint32_t)(((a.g.n_blk - 1) * (int64_t)a.p->C + 255) / 256);
+  };
+  launch_batched<DecP>(k_dequant_fix, "dequant_fix", n, args[0].s, 256, fill, fix_count);
 }
 
 void launch_sym_to_tiled(const EncodeArgs &a, const uint8_t *sym) {
