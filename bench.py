@@ -50,8 +50,12 @@ PEAK_HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_work(name: str, N: int, Ca: int, rans_bytes: int):
-    """(bound, algorithmic units per launch, unit) of each timed kernel."""
+def kernel_work(name: str, N: int, Ca: int, rans_bytes: int, fused: bool = False):
+    """(bound, algorithmic units per launch, unit) of each timed kernel.
+
+    fused: the decoder dequantises as it decodes (every component coded), so
+    it reads each row's means and writes its bf16 output instead of symbols.
+    """
     if name == "analysis_gemm":
         return "mfma", 2.0 * N * Ca * 6144, "flop"
     if name == "dequant":
@@ -61,6 +65,8 @@ def kernel_work(name: str, N: int, Ca: int, rans_bytes: int):
         return "mfma", 2.0 * N * 256 * 2048, "flop"
     if name == "synthesis_gemm":
         return "mfma", 2.0 * N * 6144 * (2048 + 256), "flop"
+    if name == "rans_decode" and fused:
+        return "hbm", float(N * (2048 * 4 + 2048 * 2) + rans_bytes), "byte"
     if name in ("rans_encode", "rans_decode"):
         return "hbm", float(N * Ca + rans_bytes), "byte"
     return None, 0.0, None
@@ -743,7 +749,7 @@ def codec_bench(args) -> int:
 
     s = torch.cuda.current_stream()
     names = ("start", "analysis_gemm", "fixup", "rans_encode", "scan", "pack", "parse", "rans_decode",
-             "dequant", "w1_gemm", "w1_gelu", "synthesis_gemm")
+             "dequant", "dequant_fix", "w1_gemm", "w1_gelu", "synthesis_gemm")
 
     def profiled(k, only=None):
         # k steps with kernel events (of one kernel, or of all); returns the
@@ -827,7 +833,7 @@ def codec_bench(args) -> int:
     # launches per step (a transform launch covers one request, a stream-stage
     # launch all of them)
     def work(name, v):
-        b_, u_, un_ = kernel_work(name, N_tot, Ca, rans_tot)
+        b_, u_, un_ = kernel_work(name, N_tot, Ca, rans_tot, fused="dequant" not in kern)
         per = v.get("launches_per_step") or 1.0
         return b_, u_ / per, un_
 

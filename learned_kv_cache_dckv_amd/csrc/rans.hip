@@ -790,7 +790,6 @@ struct SymOnly {
 struct Fused {
   const float *mcol;  // mtab + c
   uint16_t *ycol;     // yhat_b + c
-  uint32_t *sout;
   uint32_t tk[4];     // token ids of rows 4 l .. 4 l + 3 (lane l)
   const uint32_t *erec;
   uint32_t elo, ehi;
@@ -845,7 +844,6 @@ struct Fused {
   template <int PH>
   __device__ __forceinline__ void run(int q, uint32_t s0, uint32_t s1, uint32_t s2, uint32_t s3, int rows) {
     const float(&mq)[4] = m[PH];
-    sout[(size_t)q * 64] = s0 | (s1 << 8) | (s2 << 16) | (s3 << 24);
     const int64_t j = j0 + 4 * q;
     const uint32_t sy[4] = {s0, s1, s2, s3};
     float qv[4];
@@ -980,7 +978,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(const Batch<DecP
     // (mean, code, left neighbour) with each block's first yhat, for
     // k_dequant_fix.  Means: lane l holds the token ids of rows 4 l .. 4 l + 3
     // (ids out of range set EINVAL and read as 0); a quad's means are loaded
-    // two quads ahead.  Escaped codes come from the block's records.
+    // two quads ahead.  Escaped codes come from the block's records.  The
+    // symbols themselves are not stored: nothing after this reads them.
     const int c = kLanes * g + lane;
     const int64_t j0 = (int64_t)kBlock * b;
     uint32_t tk[4];
@@ -1004,7 +1003,6 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_rans_decode(const Batch<DecP
     Fused fz;
     fz.mcol = P.mtab + c;
     fz.ycol = P.yhat_b + c;
-    fz.sout = sout;
 #pragma unroll
     for (int k = 0; k < 4; ++k) fz.tk[k] = tk[k];
     fz.erec = erec;
