@@ -851,7 +851,8 @@ def codec_bench(args) -> int:
     roof["kernel"] = dom
     roof["traffic"] = None
     T0 = R[0]["T"]
-    if os.path.exists(TRAFFIC_FILE) and not batch:
+    # the counters were taken on the default codec and layout of one request
+    if os.path.exists(TRAFFIC_FILE) and not batch and args.codec == "dckv" and args.layout == "rows":
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         ent = tr.get(dom)

@@ -122,7 +122,7 @@ def test_codec_matches_oracle_on_workloads(cfg):
     _run_case(req.rows, req.token_ids, req.step_scale)
 
 
-@pytest.mark.parametrize("T", [0, 1, 100, 132, 133, 134, 135, 136, 259, 260, 261, 389, 517])
+@pytest.mark.parametrize("T", [0, 1, 100, 132, 133, 134, 135, 136, 259, 260, 261, 388, 389, 517, 645])
 def test_codec_edge_lengths(T):
     rows, tok = synth.random_rows(T, seed=1000 + T)
     _run_case(rows, tok, synth.step_scale_for(220.0))
@@ -206,6 +206,9 @@ def test_codec_status_codes():
     with pytest.raises(dk.DckvError):
         dk.encode(plan, gu.rows_dev(rows), gu.to_dev(tok.astype(np.int32)), capacity=1000)
     data, st = gu.gpu_encode(plan, rows, tok)
+    gu.say("decode with an out-of-range token id")
+    _, st = gu.gpu_decode(plan, data, tk)
+    assert st == dk.EINVAL
     gu.say("decode with the wrong plan / corrupt header")
     other = gu.device_codec().plan(synth.step_scale_for(120.0))
     _, st = gu.gpu_decode(other, data, tok)
