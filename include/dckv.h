@@ -383,7 +383,11 @@ int dckv_entropy_decode(const dckv_plan_t *plan, const uint8_t *stream, uint64_t
 /* ---------------------------------------------------------------------------
  * Introspection of the workspace after a call (for tests and tools).
  * Valid until the workspace is reused.  which:
- *   DCKV_VIEW_SYMBOLS  u8 symbols of the last encode/decode, group-tiled:
+ *   DCKV_VIEW_SYMBOLS  u8 symbols of the last encode, or of the last decode with
+ *                      a plan that drops components (a decode with every
+ *                      component coded dequantises inside the rANS decoder
+ *                      and leaves this view unwritten; dckv_entropy_decode
+ *                      returns the symbols), group-tiled:
  *                      [G][N256/4][64][4], N256 = 256 * ceil(N/256);
  *                      symbol (j, rank r) at ((r/64)*(N256/4) + j/4)*256 + (r%64)*4 + j%4
  *   DCKV_VIEW_YHAT_B   bf16 [N][n_coef] decoded coefficients (row stride n_coef)

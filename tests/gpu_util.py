@@ -78,6 +78,21 @@ def gpu_decode(plan, data: bytes, tok, ws=None):
     return out.view(torch.int16).cpu().numpy().view(np.uint16), st
 
 
+def gpu_entropy_decode(plan, data: bytes, T: int, N: int, Ca: int, ws=None):
+    """Symbols [N][C_a] of a stream from the GPU's rANS decoder alone
+    (dckv_entropy_decode), the escape count and the status."""
+    import torch
+    buf = to_dev(np.frombuffer(data, np.uint8).copy())
+    sym = torch.full((max(N * Ca, 1),), 7, dtype=torch.uint8, device="cuda:0")
+    ne = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    if ws is None:
+        ws = dk().workspace(plan, T)
+    dk().dckv_entropy_decode(plan, buf, len(data), T, sym, ne, st, ws)
+    torch.cuda.synchronize()
+    return sym[:N * Ca].cpu().numpy().reshape(N, Ca), int(ne.item()), int(st.item())
+
+
 def read_view(ws, plan, T, which):
     """Bytes of one workspace view (after a call that filled it)."""
     off, nb, rs = dk().dckv_workspace_view(plan, T, which)

@@ -33,17 +33,7 @@ def _entropy_encode(plan, T, sym, flat, qe, rows_bits):
 
 
 def _entropy_decode(plan, data, T, N, Ca):
-    import torch
-    dk = gu.dk()
-    dev = "cuda:0"
-    buf = gu.to_dev(np.frombuffer(data, np.uint8).copy())
-    sym = torch.full((max(N * Ca, 1),), 7, dtype=torch.uint8, device=dev)
-    ne = torch.zeros(1, dtype=torch.int32, device=dev)
-    st = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = dk.workspace(plan, T)
-    dk.dckv_entropy_decode(plan, buf, len(data), T, sym, ne, st, ws)
-    torch.cuda.synchronize()
-    return sym[:N * Ca].cpu().numpy().reshape(N, Ca), int(ne.item()), int(st.item())
+    return gu.gpu_entropy_decode(plan, data, T, N, Ca)
 
 
 @pytest.fixture(scope="module")
