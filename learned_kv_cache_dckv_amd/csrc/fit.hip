@@ -130,8 +130,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 // address).  A pivot below 1e-6 of its diagonal entry before the
 // factorisation sets EINVAL: the Gram matrix plus ridge is not positive
 // definite in fp32 (e.g. a zero ridge with fewer rows than dimensions).
-__global__ __launch_bounds__(64) void k_chol_diag(float *G, int k, const float *dg, float *linv, int32_t *status) {
-  __shared__ __attribute__((aligned(16))) float col[kNB][kNB];
+// Run by the first wave of a workgroup (lane r = threadIdx.x); col is 16 KiB
+// of 16-byte aligned LDS.
+__device__ __forceinline__ void chol_diag_wave(float *G, int k, const float *dg, float *linv, int32_t *status,
+                                               float (*col)[kNB]) {
   float *blk = G + (size_t)(k * kNB) * kEmb + k * kNB;
   const int r = threadIdx.x;
   float x[kNB];
@@ -227,6 +229,13 @@ __global__ __launch_bounds__(64) void k_chol_diag(float *G, int k, const float *
 #pragma unroll
   for (int i = 0; i < kNB; ++i) lv[i * kNB + r] = y[i];
   if (r == 0 && bad) atomicCAS(status, 0, DCKV_EINVAL);
+}
+
+// The first diagonal block (the later ones are factorised inside the trailing
+// update that finishes them).
+__global__ __launch_bounds__(64) void k_chol_diag(float *G, int k, const float *dg, float *linv, int32_t *status) {
+  __shared__ __attribute__((aligned(16))) float col[kNB][kNB];
+  chol_diag_wave(G, k, dg, linv, status, col);
 }
 
 // 64 x 64 tile products on 256 threads.  Operands are staged in LDS as
@@ -340,9 +349,14 @@ __global__ __launch_bounds__(256) void k_chol_panel_fwd(float *G, float *X, cons
 // The trailing update after panel k, with the forward substitution's update:
 // the first m (m + 1) / 2 workgroups take G_ij -= L_ik L_jk^T over the lower
 // triangle k < j <= i; the next 32 m take X_i -= L_ik X_k (i > k, one
-// 64-column block each).
-__global__ __launch_bounds__(256) void k_chol_update_fwd(float *G, float *X, int k, int m) {
-  __shared__ TileLds P, Q;
+// 64-column block each).  Workgroup 0 updates diagonal block k + 1, which is
+// then final, and its first wave factorises it (chol_diag_wave) while the
+// other workgroups finish the update: the factorisation of one block no
+// longer runs alone on the chip between two launches.  Two workgroups per CU
+// leave the factorisation its registers.
+__global__ __launch_bounds__(256, 2) void k_chol_update_fwd(float *G, float *X, int k, int m, const float *dg,
+                                                            float *linv, int32_t *status) {
+  __shared__ __attribute__((aligned(16))) TileLds P, Q;
   float v[4][4];
   const int t = blockIdx.x, ntri = m * (m + 1) / 2;
   if (t < ntri) {
@@ -352,6 +366,12 @@ __global__ __launch_bounds__(256) void k_chol_update_fwd(float *G, float *X, int
     const int i = k + 1 + ii, j = k + 1 + (t - ii * (ii + 1) / 2);
     tile_op<false, true, true>(P, Q, G + (size_t)(i * kNB) * kEmb + j * kNB, kEmb, G + (size_t)(i * kNB) * kEmb + k * kNB,
                                kEmb, G + (size_t)(j * kNB) * kEmb + k * kNB, kEmb, v);
+    if (t == 0) {
+      // the block's stores are visible to the workgroup and P is free
+      __syncthreads();
+      static_assert(sizeof(TileLds) >= kNB * kNB * sizeof(float), "column buffer inside P");
+      if (threadIdx.x < kNB) chol_diag_wave(G, k + 1, dg, linv, status, reinterpret_cast<float (*)[kNB]>(&P[0][0]));
+    }
   } else {
     const int u = t - ntri, i = k + 1 + u / (kC / kNB), c0 = (u % (kC / kNB)) * kNB;
     tile_op<false, false, true>(P, Q, X + (size_t)(i * kNB) * kC + c0, kC, G + (size_t)(i * kNB) * kEmb + k * kNB, kEmb,
@@ -568,14 +588,16 @@ void fit_sequence(const FitArgs &a) {
   float *linv = reinterpret_cast<float *>(ws + l.linv);
   hipLaunchKernelGGL(k_fit_add_diag, dim3(kEmb / 256), dim3(256), 0, s, G, a.ridge * (float)n, dg);
   // G = L L^T by blocks, with the forward substitution L Z = R riding along:
-  // per block k one diagonal launch, one panel launch (plus Z_k) and one
-  // trailing-update launch (plus R_i -= L_ik Z_k)
+  // the first diagonal block, then per block k one panel launch (plus Z_k)
+  // and one trailing-update launch (plus R_i -= L_ik Z_k) that also
+  // factorises diagonal block k + 1
+  hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(64), 0, s, G, 0, dg, linv, a.status);
   for (int k = 0; k < kNBlk; ++k) {
-    hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(64), 0, s, G, k, dg, linv, a.status);
     const int m = kNBlk - k - 1;
     hipLaunchKernelGGL(k_chol_panel_fwd, dim3(m + kC / kNB), dim3(256), 0, s, G, R, linv, k, m);
     if (m > 0)
-      hipLaunchKernelGGL(k_chol_update_fwd, dim3(m * (m + 1) / 2 + m * (kC / kNB)), dim3(256), 0, s, G, R, k, m);
+      hipLaunchKernelGGL(k_chol_update_fwd, dim3(m * (m + 1) / 2 + m * (kC / kNB)), dim3(256), 0, s, G, R, k, m,
+                         (const float *)dg, linv, a.status);
   }
   // L^T H^T = Z: one launch per block row
   hipLaunchKernelGGL(k_bwd_diag, dim3(kC / kNB), dim3(256), 0, s, R, linv, kNBlk - 1);
