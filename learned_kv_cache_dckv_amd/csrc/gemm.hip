@@ -989,26 +989,39 @@ static OutRows out_rows(const DecodeArgs &a) {
   return o;
 }
 
-// kept row k: RoPE on the key columns of the verbatim row in the stream
+// kept row k: RoPE on the key columns of the verbatim row in the stream.
+// Thread t takes the pair (d, d + 128), d = t % 128, of heads 2 j + t / 128,
+// j < 24 / 2 (even j: a layer's key heads, odd j: its value heads); every load
+// is issued before the first store.  256 threads.
+constexpr int kKeptThreads = 256;
 __device__ __forceinline__ void kept_rope_row(int64_t k, const uint8_t *stream, const float2 *lo, const float2 *hi,
                                               const OutRows &out, int64_t head_n, int64_t tail_pos0) {
+  constexpr int kJ = kD / 2 / kKeptThreads;
+  static_assert(kD / 2 % kKeptThreads == 0 && kKeptThreads == 2 * kHalf, "kept-row thread layout");
   const int64_t pos = k < head_n ? k : tail_pos0 + (k - head_n);
   const uint16_t *src = reinterpret_cast<const uint16_t *>(stream + kHeaderBytes) + (size_t)k * kD;
-  for (int i = threadIdx.x; i < kD / 2; i += blockDim.x) {
-    // i enumerates (head, d) with d < 128: the pair (d, d + 128) of every head
-    const int head = i / kHalf, d = i % kHalf;
-    const int base = head * kHeadDim;
-    uint16_t *dst = out.at(pos, head);
-    const float x0 = bf2f(src[base + d]), x1 = bf2f(src[base + d + kHalf]);
-    if ((head & 3) < 2) {
-      const float2 a = lo[(size_t)(pos & 255) * kHalf + d], b = hi[(size_t)(pos >> 8) * kHalf + d];
-      const float cs = b.x * a.x - b.y * a.y;
-      const float sn = b.y * a.x + b.x * a.y;
-      dst[d] = f2bf(x0 * cs - x1 * sn);
-      dst[d + kHalf] = f2bf(x1 * cs + x0 * sn);
+  const int d = threadIdx.x & (kHalf - 1), hsub = threadIdx.x >> 7;
+  uint16_t x0[kJ], x1[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int base = (2 * j + hsub) * kHeadDim;
+    x0[j] = src[base + d];
+    x1[j] = src[base + d + kHalf];
+  }
+  // the angle pos * w_d, the same for every key head
+  const float2 a = lo[(size_t)(pos & 255) * kHalf + d], b = hi[(size_t)(pos >> 8) * kHalf + d];
+  const float cs = b.x * a.x - b.y * a.y;
+  const float sn = b.y * a.x + b.x * a.y;
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    uint16_t *dst = out.at(pos, 2 * j + hsub);
+    if ((j & 1) == 0) {
+      const float v0 = bf2f(x0[j]), v1 = bf2f(x1[j]);
+      dst[d] = f2bf(v0 * cs - v1 * sn);
+      dst[d + kHalf] = f2bf(v1 * cs + v0 * sn);
     } else {
-      dst[d] = src[base + d];
-      dst[d + kHalf] = src[base + d + kHalf];
+      dst[d] = x0[j];
+      dst[d + kHalf] = x1[j];
     }
   }
 }
@@ -1023,12 +1036,11 @@ struct W1P {
   int64_t N, NM;
   int n_mt;
   int32_t *status;
-  // kept rows, RoPE'd by the GELU kernel's last n_kept workgroups
+  // kept rows, RoPE'd by the GELU kernel's first n_kept workgroups
   const uint8_t *stream;
   const float2 *rope_lo, *rope_hi;
   OutRows out;
   int64_t n_kept, head_n, tail_pos0;
-  unsigned gelu_blocks;
 };
 
 // W1 yhat_b as two half-K products (coefficients [0, 1024) and [1024, 2048)):
@@ -1076,18 +1088,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_w1(const Batch<W1P, kW1Batch> B
 }
 
 // h_b = bf16(GELU(part0 + part1)), exact-erf GELU; 4 hidden units per thread.
-// Workgroups past the GELU ones apply RoPE to one kept row each (the RoPE
-// tables are written by the parse kernel, which runs first).
-__global__ __launch_bounds__(256) void k_w1_gelu(const Batch<W1P, kW1Batch> Bt) {
+// The first n_kept workgroups apply RoPE to one kept row each (the RoPE tables
+// are written by the parse kernel, which runs first); they come first so that
+// their loads overlap the GELU workgroups rather than trail them.
+__global__ __launch_bounds__(kKeptThreads) void k_w1_gelu(const Batch<W1P, kW1Batch> Bt) {
   const int ri = batch_req(Bt, blockIdx.x);
   const W1P &P = Bt.r[ri];
   const uint32_t local = blockIdx.x - Bt.start[ri];
   if (*P.status != 0) return;
-  if (local >= P.gelu_blocks) {
-    kept_rope_row(local - P.gelu_blocks, P.stream, P.rope_lo, P.rope_hi, P.out, P.head_n, P.tail_pos0);
+  if (local < P.n_kept) {
+    kept_rope_row(local, P.stream, P.rope_lo, P.rope_hi, P.out, P.head_n, P.tail_pos0);
     return;
   }
-  const int64_t i = (int64_t)local * blockDim.x + threadIdx.x;  // (row, 4-unit group)
+  const int64_t i = (int64_t)(local - P.n_kept) * blockDim.x + threadIdx.x;  // (row, 4-unit group)
   if (i >= P.N * (kHid / 4)) return;
   const size_t o = (size_t)i * 4;
   const f32x4 a = *reinterpret_cast<const f32x4 *>(P.part + o);
@@ -1479,8 +1492,6 @@ void launch_w1_gemm(const DecodeArgs *args, int n) {
     P.n_kept = a.g.n_kept;
     P.head_n = std::min<int64_t>(a.p->keep_head, a.g.T);
     P.tail_pos0 = a.p->keep_head + a.g.N;
-    // the linear codec (no correction) launches the kept rows only
-    P.gelu_blocks = a.p->W1 ? (unsigned)((a.g.N * (kHid / 4) + 255) / 256) : 0u;
     return P;
   };
   auto gemm_count = [&](int i) {
@@ -1488,12 +1499,13 @@ void launch_w1_gemm(const DecodeArgs *args, int n) {
     return (a.g.N && a.p->W1) ? (uint32_t)(a.g.n_mtiles * 2) : 0u;
   };
   launch_batched<W1P, kW1Batch>(k_w1, "w1_gemm", n, args[0].s, kThreads, fill, gemm_count, kLdsBytes);
+  // the linear codec (no correction) launches the kept rows only
   auto gelu_count = [&](int i) {
     const DecodeArgs &a = args[i];
     const unsigned gb = a.p->W1 ? (unsigned)((a.g.N * (kHid / 4) + 255) / 256) : 0u;
     return gb + (uint32_t)a.g.n_kept;
   };
-  launch_batched<W1P, kW1Batch>(k_w1_gelu, "w1_gelu", n, args[0].s, 256, fill, gelu_count);
+  launch_batched<W1P, kW1Batch>(k_w1_gelu, "w1_gelu", n, args[0].s, kKeptThreads, fill, gelu_count);
 }
 
 static SynP syn_params(const DecodeArgs &a) {
