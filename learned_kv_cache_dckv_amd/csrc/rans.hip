@@ -545,7 +545,12 @@ __global__ __launch_bounds__(256) void k_parse(const Batch<ParseP> B) {
   if (t == 0) {
     bad = 0;
     plan_bad = 0;
-    const uint32_t *h = reinterpret_cast<const uint32_t *>(P.stream);
+    uint32_t h[kHeaderBytes / 4];
+    if (P.size >= (uint64_t)kHeaderBytes) {
+      // all header words in flight at once
+#pragma unroll
+      for (int i = 0; i < kHeaderBytes / 4; ++i) h[i] = reinterpret_cast<const uint32_t *>(P.stream)[i];
+    }
     if (P.size < (uint64_t)kHeaderBytes || h[0] != 0x564B4344u ||
         h[1] != ((uint32_t)kVersion | ((uint32_t)kHeaderBytes << 16))) {
       bad = 1;
@@ -571,9 +576,17 @@ __global__ __launch_bounds__(256) void k_parse(const Batch<ParseP> B) {
   if (!bad && !plan_bad) {
     const uint32_t *offs = reinterpret_cast<const uint32_t *>(P.stream + kHeaderBytes + P.kept_bytes);
     int my_bad = 0;
-    for (uint32_t i = t; i < P.n_groups; i += blockDim.x) {
-      const uint32_t a = offs[i], b2 = offs[i + 1];
-      if (b2 < a || (a & 1) || (b2 & 1)) my_bad = 1;
+    // thread t checks the offsets of groups [16 t, 16 t + 16) of each pass:
+    // 17 loads issued together (indices clamped to the last entry, which
+    // exists), then the 16 pairs inside the request
+    constexpr uint32_t kOffRun = 16;
+    for (uint32_t g0 = t * kOffRun; g0 < P.n_groups; g0 += blockDim.x * kOffRun) {
+      uint32_t o[kOffRun + 1];
+#pragma unroll
+      for (uint32_t j = 0; j <= kOffRun; ++j) o[j] = offs[min(g0 + j, P.n_groups)];
+#pragma unroll
+      for (uint32_t j = 0; j < kOffRun; ++j)
+        if (g0 + j < P.n_groups && (o[j + 1] < o[j] || (o[j] & 1) || (o[j + 1] & 1))) my_bad = 1;
     }
     if (t == 0 && (offs[0] != 0 || (uint64_t)offs[P.n_groups] != s_rans_bytes)) my_bad = 1;
     const uint32_t *esc = reinterpret_cast<const uint32_t *>(P.stream + s_esc_off);
