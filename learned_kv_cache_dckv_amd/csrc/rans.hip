@@ -462,16 +462,35 @@ __global__ __launch_bounds__(256) void k_pack(const Batch<PackP> B) {
   const int ri = batch_req(B, blockIdx.x);
   const PackP &P = B.r[ri];
   const uint32_t local = blockIdx.x - B.start[ri], cnt = B.start[ri + 1] - B.start[ri];
-  if (*P.status != 0) return;
+  // the status, the control words and the group's size and offset are read
+  // together (all lie in the workspace whatever the status)
   const Ctrl *ct = reinterpret_cast<const Ctrl *>(P.ws);
+  const int64_t gid = local;
+  const bool has_group = gid < P.n_groups;
+  const int32_t st = *P.status;
   const uint64_t rans_off = ct->rans_off, esc_off = ct->esc_off;
   const uint32_t n_esc = ct->n_esc;
-  const int64_t gid = local;
-  if (gid < P.n_groups) {
-    const uint32_t W = P.gwords[gid];
+  const uint32_t W = has_group ? P.gwords[gid] : 0u;
+  const uint64_t goff = has_group ? P.goffs[gid] : 0u;
+  if (st != 0) return;
+  if (has_group) {
     const uint16_t *src = P.scratch + (size_t)(gid + 1) * (kLanes * (kBlock + 2)) - W;
-    uint16_t *dst = reinterpret_cast<uint16_t *>(P.stream + rans_off) + P.goffs[gid];
-    for (uint32_t k = threadIdx.x; k < W; k += blockDim.x) dst[k] = src[k];
+    uint16_t *dst = reinterpret_cast<uint16_t *>(P.stream + rans_off) + goff;
+    // four words per thread per pass, loaded before any is stored
+    constexpr uint32_t kU = 4;
+    for (uint32_t k0 = threadIdx.x; k0 < W; k0 += kU * blockDim.x) {
+      uint16_t v[kU];
+#pragma unroll
+      for (uint32_t u = 0; u < kU; ++u) {
+        const uint32_t k = k0 + u * blockDim.x;
+        if (k < W) v[u] = src[k];
+      }
+#pragma unroll
+      for (uint32_t u = 0; u < kU; ++u) {
+        const uint32_t k = k0 + u * blockDim.x;
+        if (k < W) dst[k] = v[u];
+      }
+    }
   }
   uint32_t *e = reinterpret_cast<uint32_t *>(P.stream + esc_off);
   for (uint32_t i = local * blockDim.x + threadIdx.x; i < n_esc; i += cnt * blockDim.x) {
